@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+* top-M:        numpy's stable lexsort (library routine), bit-exact;
+* GRU step:     torch.nn.GRUCell in float64 (library routine), plus a closed
+                form that exposes the bf16 rounding of the recurrent operand;
+* distribution: torch.log_softmax + numpy.lexsort; sum of probabilities = 1;
+* tree:         exhaustive enumeration of the candidate tree (tests/bruteforce.py),
+                exact branch-and-bound on the tiny workload, and a search over
+                all prefix-closed node sets on very small trees;
+* closed forms / special cases: M = 1 chain, n = 1 argmax, L = 1 sorted list,
+                zero correction == factorized (DDTree) tree, a hand-derived
+                example under tests/golden/;
+* metamorphic:  vocabulary relabeling, batch independence.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as S
+from bruteforce import (Scorer, as_f64, best_n_branch_and_bound, best_n_bruteforce,
+                        factorized_tree, prefix_closed_subsets_best, topm_table, tree_arrays)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def small_cfg(**kw):
+    cfg = dict(B=1, V=50, L=4, E=6, H=5, M=4, n=8, dtype="f32", alpha=1.1, T=0.0)
+    cfg.update(kw)
+    return cfg
+
+
+def assert_tree_equal(res, ref, n, atol=1e-10):
+    tok, par, dep, sc = ref
+    np.testing.assert_array_equal(res["tokens"], tok)
+    np.testing.assert_array_equal(res["parents"], par)
+    np.testing.assert_array_equal(res["depths"], dep)
+    fin = np.isfinite(sc)
+    np.testing.assert_allclose(res["scores"][fin], sc[fin], atol=atol, rtol=0)
+    assert np.all(np.isneginf(res["scores"][~fin]))
+
+
+# ---------------------------------------------------------------- top-M ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,M", [(1000, 8), (257, 64), (64, 64), (5, 1), (3000, 17)])
+def test_topm_matches_stable_lexsort(dtype, V, M):
+    rng = np.random.default_rng(V * 31 + M)
+    x = (rng.normal(0, 2, V)).astype(np.float32)
+    x = np.round(x * 4) / 4  # many exact ties
+    row = S.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    idx, val = oracle.topm_row(row, M)
+    vals = as_f64(row)
+    ref = np.lexsort((np.arange(V), -vals))[:M]
+    np.testing.assert_array_equal(idx, ref)
+    np.testing.assert_array_equal(val, vals[ref])
+
+
+def test_topm_all_equal_takes_lowest_ids():
+    row = np.full(100, -3.5, np.float32)
+    idx, _ = oracle.topm_row(row, 10)
+    np.testing.assert_array_equal(idx, np.arange(10))
+
+
+def test_topm_bf16_zipf_row():
+    cfg = S.CONFIGS["qwen3_4b_single"]
+    base = S.make_base(1, 1, cfg["V"], cfg["alpha"], "bf16", seed=3)[0, 0]
+    idx, val = oracle.topm_row(base, 64)
+    vals = as_f64(base)
+    ref = np.argsort(-vals, kind="stable")[:64]
+    np.testing.assert_array_equal(idx, ref)
+    assert len(np.unique(val)) < 64  # the workload really has bf16 ties in the top-64
+
+
+# ------------------------------------------------------------ GRU step -----
+
+def _gru_inputs(E, H, dtype, seed):
+    cfg = small_cfg(V=7, E=E, H=H, dtype=dtype)
+    inp = S.make_inputs(cfg, seed=seed, variant="strong")
+    return inp
+
+
+def _torch_cell(inp):
+    E, H = inp["w_ih"].shape[1], inp["w_hh"].shape[1]
+    cell = torch.nn.GRUCell(E, H).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(as_f64(inp["w_ih"])))
+        cell.weight_hh.copy_(torch.from_numpy(as_f64(inp["w_hh"])))
+        cell.bias_ih.copy_(torch.from_numpy(as_f64(inp["b_ih"])))
+        cell.bias_hh.copy_(torch.from_numpy(as_f64(inp["b_hh"])))
+    return cell
+
+
+@pytest.mark.parametrize("E,H", [(6, 5), (32, 32), (40, 17)])
+def test_gru_f32_matches_torch_grucell(E, H):
+    inp = _gru_inputs(E, H, "f32", seed=E + H)
+    cell = _torch_cell(inp)
+    rng = np.random.default_rng(0)
+    for tok in range(inp["emb"].shape[0]):
+        h = rng.uniform(-1, 1, H)
+        got = oracle.gru(inp["emb"], tok, h, inp["w_ih"], inp["w_hh"], inp["b_ih"], inp["b_hh"])
+        with torch.no_grad():
+            ref = cell(torch.from_numpy(as_f64(inp["emb"][tok]))[None], torch.from_numpy(h)[None])[0]
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-13)
+
+
+def test_gru_null_biases_are_zero():
+    inp = _gru_inputs(6, 5, "f32", seed=1)
+    h = np.linspace(-0.5, 0.5, 5)
+    z = np.zeros_like(inp["b_ih"])
+    a = oracle.gru(inp["emb"], 2, h, inp["w_ih"], inp["w_hh"], None, None)
+    b = oracle.gru(inp["emb"], 2, h, inp["w_ih"], inp["w_hh"], z, z)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_gru_bf16_representable_state_matches_torch_grucell():
+    inp = _gru_inputs(16, 8, "bf16", seed=5)
+    cell = _torch_cell(inp)
+    rng = np.random.default_rng(1)
+    h32 = rng.uniform(-1, 1, 8).astype(np.float32)
+    h = as_f64(S.f32_to_bf16_bits(h32))  # exactly bf16-representable
+    for tok in range(7):
+        got = oracle.gru(inp["emb"], tok, h, inp["w_ih"], inp["w_hh"], inp["b_ih"], inp["b_hh"])
+        with torch.no_grad():
+            ref = cell(torch.from_numpy(as_f64(inp["emb"][tok]))[None], torch.from_numpy(h)[None])[0]
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-13)
+
+
+def test_gru_bf16_rounds_only_the_recurrent_operand():
+    """Closed form: with W_ih = 0, zero biases, reset/update rows of W_hh = 0 and
+    the new-gate rows of W_hh = identity, r = u = 1/2 and
+    h' = tanh(hb / 2) / 2 + h / 2, so hb = 2 atanh(2 h' - h) must equal torch's
+    bf16 rounding of fp32(h), while the blend uses the unrounded h."""
+    H, E = 16, 4
+    zero = lambda *s: S.f32_to_bf16_bits(np.zeros(s, np.float32))
+    w_hh = np.zeros((3 * H, H), np.float32)
+    w_hh[2 * H:] = np.eye(H, dtype=np.float32)
+    emb = zero(3, E)
+    rng = np.random.default_rng(7)
+    h = rng.uniform(-0.9, 0.9, H)
+    h[0] = 1.0 + 2.0 ** -8          # a bf16 tie: rounds to even (1.0)
+    h[1] = 1.0 + 3 * 2.0 ** -8      # a bf16 tie: rounds to even (1 + 2^-6)
+    out = oracle.gru(emb, 1, h, zero(3 * H, E), S.f32_to_bf16_bits(w_hh), zero(3 * H), zero(3 * H))
+    hb = 2.0 * np.arctanh(2.0 * out - h)
+    ref = torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_allclose(hb, ref, rtol=0, atol=1e-12)
+    assert ref[0] == 1.0 and ref[1] == 1.0 + 2.0 ** -6
+
+
+# ------------------------------------------------- children distribution ---
+
+@pytest.mark.parametrize("T", [0.0, 0.5, 1.0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dist_matches_torch_log_softmax(T, dtype):
+    cfg = small_cfg(V=300, H=24, M=16, dtype=dtype)
+    inp = S.make_inputs(cfg, seed=11, variant="strong")
+    idx, val = topm_table(inp["base"][0], cfg["M"])
+    rng = np.random.default_rng(2)
+    h = rng.normal(0, 1, cfg["H"])
+    tok, lp = oracle.dist(idx[2], val[2], inp["C"], h, T)
+    z = torch.from_numpy(val[2]) + torch.from_numpy(as_f64(inp["C"]))[torch.from_numpy(idx[2])] @ torch.from_numpy(h)
+    if T > 0:
+        z = z / T
+    ref = torch.log_softmax(z, 0).numpy()
+    order = np.lexsort((idx[2], -ref))
+    np.testing.assert_array_equal(tok, idx[2][order])
+    np.testing.assert_allclose(lp, ref[order], rtol=0, atol=1e-13)
+    assert abs(np.exp(lp).sum() - 1.0) < 1e-13
+    assert np.all(lp <= 0)
+
+
+def test_dist_ties_go_to_lower_token():
+    V, H, M = 10, 3, 6
+    Cm = np.zeros((V, H), np.float32)
+    idx = np.array([9, 4, 7, 1, 3, 2], np.int32)
+    val = np.array([1.0, 1.0, 0.5, 1.0, 0.5, -2.0])
+    tok, lp = oracle.dist(idx, val, Cm, np.ones(H), 0.0)
+    np.testing.assert_array_equal(tok, [1, 4, 9, 3, 7, 2])
+    np.testing.assert_allclose(np.exp(lp).sum(), 1.0, atol=1e-15)
+
+
+# ------------------------------------------------------ trees: brute force -
+
+def _oracle_tree(inp, cfg, b=0):
+    return oracle.build_request(inp, b, cfg["M"], cfg["n"], cfg["T"])
+
+
+@pytest.mark.parametrize("L,M,n,T,seed", [
+    (4, 4, 8, 0.0, 0), (4, 8, 16, 0.0, 1), (3, 5, 20, 0.5, 2), (6, 3, 12, 0.0, 3),
+    (2, 6, 5, 1.0, 4), (4, 3, 40, 0.0, 5),
+])
+def test_tree_equals_bruteforce_top_n(L, M, n, T, seed):
+    cfg = small_cfg(L=L, M=M, n=n, T=T, V=40, E=8, H=6)
+    inp = S.make_inputs(cfg, seed=seed, variant="strong")
+    sc = Scorer(inp, 0, M, T)
+    nodes = best_n_bruteforce(sc, n)
+    res = _oracle_tree(inp, cfg)
+    assert res["count"] == len(nodes)
+    assert_tree_equal(res, tree_arrays(nodes, n), n)
+
+
+@pytest.mark.parametrize("variant", ["default", "strong"])
+def test_tiny_workload_equals_branch_and_bound(variant):
+    cfg = S.CONFIGS["tiny"]
+    inp = S.make_inputs(cfg, seed=0, variant=variant)
+    sc = Scorer(inp, 0, cfg["M"], cfg["T"])
+    nodes = best_n_branch_and_bound(sc, cfg["n"])
+    res = _oracle_tree(inp, cfg)
+    assert res["count"] == cfg["n"]
+    assert_tree_equal(res, tree_arrays(nodes, cfg["n"]), cfg["n"])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tree_maximizes_over_all_prefix_closed_sets(seed):
+    cfg = small_cfg(L=3, M=3, n=4, V=12, E=4, H=3)
+    inp = S.make_inputs(cfg, seed=seed, variant="strong")
+    sc = Scorer(inp, 0, 3, 0.0)
+    best_p, best_s, _ = prefix_closed_subsets_best(sc, 4)
+    res = _oracle_tree(inp, cfg)
+    s = res["scores"][1:]
+    assert abs(np.exp(s).sum() - best_p) < 1e-12
+    assert abs(s.sum() - best_s) < 1e-12
+
+
+# ------------------------------------------ closed forms / special cases ---
+
+def test_zero_correction_equals_factorized_tree():
+    for name, over in [("tiny", {}), ("tiny", dict(T=0.5, M=6)), ("tiny", dict(n=40, L=5))]:
+        cfg = S.with_config(name, **over)
+        inp = S.make_inputs(cfg, seed=4, variant="zero_c")
+        res = _oracle_tree(inp, cfg)
+        ref = factorized_tree(inp["base"][0], cfg["M"], cfg["n"], cfg["T"])
+        assert_tree_equal(res, ref, cfg["n"], atol=1e-12)
+
+
+def test_zero_correction_bf16_ties_equal_factorized_tree():
+    cfg = S.with_config("tiny", dtype="bf16", V=2000, M=32, n=40, L=6, alpha=2.0)
+    inp = S.make_inputs(cfg, seed=9, variant="zero_c")
+    res = _oracle_tree(inp, cfg)
+    ref = factorized_tree(inp["base"][0], cfg["M"], cfg["n"], cfg["T"])
+    assert_tree_equal(res, ref, cfg["n"], atol=1e-12)
+
+
+def test_zero_gru_weights_equal_factorized_tree():
+    cfg = S.with_config("tiny")
+    inp = S.make_inputs(cfg, seed=6)
+    for k in ("w_ih", "w_hh", "b_ih", "b_hh"):
+        inp[k] = np.zeros_like(inp[k])
+    res = _oracle_tree(inp, cfg)  # h stays 0 -> correction is 0
+    ref = factorized_tree(inp["base"][0], cfg["M"], cfg["n"], cfg["T"])
+    assert_tree_equal(res, ref, cfg["n"], atol=1e-12)
+
+
+def test_m1_is_a_chain_of_top1_tokens():
+    cfg = S.with_config("tiny", M=1, n=16, L=8)
+    inp = S.make_inputs(cfg, seed=2, variant="strong")
+    res = _oracle_tree(inp, cfg)
+    idx, _ = topm_table(inp["base"][0], 1)
+    assert res["count"] == 8  # min(n, L): the tree runs out of candidates
+    np.testing.assert_array_equal(res["tokens"][1:9], idx[:, 0])
+    np.testing.assert_array_equal(res["parents"][1:9], np.arange(8))
+    np.testing.assert_array_equal(res["depths"][1:9], np.arange(1, 9))
+    assert np.all(res["scores"][:9] == 0.0)
+    assert np.all(res["tokens"][9:] == -1) and np.all(np.isneginf(res["scores"][9:]))
+    assert res["mask"][9:].sum() == 0
+
+
+def test_n1_is_the_argmax_of_the_first_corrected_slice():
+    cfg = S.with_config("tiny", n=1)
+    inp = S.make_inputs(cfg, seed=8, variant="strong")
+    res = _oracle_tree(inp, cfg)
+    idx, val = topm_table(inp["base"][0], cfg["M"])
+    z = val[0] + as_f64(inp["C"])[idx[0]] @ inp["h0"][0].astype(np.float64)
+    j = np.lexsort((idx[0], -z))[0]
+    assert res["tokens"][1] == idx[0][j]
+    ref = z[j] - (z.max() + np.log(np.exp(z - z.max()).sum()))
+    assert abs(res["scores"][1] - ref) < 1e-12
+
+
+def test_l1_is_the_sorted_root_list():
+    cfg = S.with_config("tiny", L=1, n=5, M=8)
+    inp = S.make_inputs(cfg, seed=3, variant="strong")
+    res = _oracle_tree(inp, cfg)
+    sc = Scorer(inp, 0, cfg["M"], 0.0)
+    toks, lps = sc.children(sc.h0, 0)
+    np.testing.assert_array_equal(res["tokens"][1:], toks[:5])
+    np.testing.assert_allclose(res["scores"][1:], lps[:5], atol=1e-12)
+    assert np.all(res["parents"][1:] == 0) and np.all(res["depths"][1:] == 1)
+
+
+@pytest.mark.parametrize("fixture", ["hand_factorized.json", "hand_depth_tie.json"])
+def test_hand_derived_example(fixture):
+    """tests/golden/hand_*.json: 4-token, 2-position examples whose trees are
+    derived by hand from the definitions (derivations are in the files)."""
+    with open(os.path.join(GOLDEN, fixture)) as f:
+        g = json.load(f)
+    base = np.array(g["base"], np.float32)[None]
+    V, E, H = base.shape[2], 2, 2
+    inp = dict(base=base, emb=np.zeros((V, E), np.float32), w_ih=np.zeros((3 * H, E), np.float32),
+               w_hh=np.zeros((3 * H, H), np.float32), b_ih=None, b_hh=None,
+               C=np.zeros((V, H), np.float32), h0=None)
+    res = oracle.build_request(inp, 0, g["M"], g["n"], 0.0)
+    np.testing.assert_array_equal(res["tokens"], g["tokens"])
+    np.testing.assert_array_equal(res["parents"], g["parents"])
+    np.testing.assert_array_equal(res["depths"], g["depths"])
+    ref = [eval(s, {"log": math.log, "exp": math.exp}) for s in g["scores_closed_form"]]
+    np.testing.assert_allclose(res["scores"], ref, atol=1e-15)
+    np.testing.assert_array_equal(res["mask"], g["mask"])
+
+
+# ---------------------------------------------------------- structure -----
+
+def _check_structure(res, n, L):
+    cnt = res["count"]
+    par, dep, sc = res["parents"], res["depths"], res["scores"]
+    for v in range(1, cnt + 1):
+        q = par[v]
+        assert 0 <= q < v                         # prefix-closed, parents first
+        assert dep[v] == dep[q] + 1 and dep[v] <= L
+        assert sc[v] <= sc[q]
+    anc = np.zeros((n + 1, n + 1), np.uint8)
+    for i in range(cnt + 1):
+        j = i
+        while j >= 0:
+            anc[i, j] = 1
+            j = par[j] if j > 0 else -1
+    np.testing.assert_array_equal(res["mask"], anc)
+    # pop order is the total order: non-increasing scores
+    assert np.all(np.diff(sc[1:cnt + 1]) <= 0)
+
+
+@pytest.mark.parametrize("name,variant", [("tiny", "default"), ("tiny", "strong")])
+def test_structure_invariants(name, variant):
+    cfg = S.CONFIGS[name]
+    inp = S.make_inputs(cfg, seed=12, variant=variant)
+    _check_structure(_oracle_tree(inp, cfg), cfg["n"], cfg["L"])
+
+
+# ---------------------------------------------------------- metamorphic ---
+
+def test_vocabulary_relabeling_maps_tokens():
+    cfg = S.with_config("tiny", V=600)
+    inp = S.make_inputs(cfg, seed=13, variant="strong")
+    perm = np.random.default_rng(0).permutation(cfg["V"])  # old id t -> new id perm[t]
+    inv = np.argsort(perm)
+    inp2 = dict(inp)
+    inp2["base"] = inp["base"][:, :, inv]
+    inp2["emb"] = inp["emb"][inv]
+    inp2["C"] = inp["C"][inv]
+    a, b = _oracle_tree(inp, cfg), _oracle_tree(inp2, cfg)
+    assert a["flags"] == 0 and b["flags"] == 0  # continuous fp32 draws: no near ties
+    np.testing.assert_array_equal(b["tokens"][1:], perm[a["tokens"][1:]])
+    np.testing.assert_array_equal(a["parents"], b["parents"])
+    np.testing.assert_allclose(a["scores"], b["scores"], atol=1e-12)
+
+
+def test_request_independent_of_batch():
+    cfg = S.with_config("tiny", B=4)
+    full = S.make_inputs(cfg, seed=14, variant="strong")
+    one = S.make_inputs(cfg, seed=14, variant="strong", requests=[2])
+    a = oracle.build_request(full, 2, cfg["M"], cfg["n"])
+    b = oracle.build_request(one, 0, cfg["M"], cfg["n"])
+    for k in ("tokens", "parents", "depths", "scores", "mask"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_score_paths_rescoring_agrees_with_tree():
+    cfg = S.CONFIGS["tiny"]
+    inp = S.make_inputs(cfg, seed=15, variant="strong")
+    res = _oracle_tree(inp, cfg)
+    paths = []
+    for v in range(1, res["count"] + 1):
+        p, j = [], v
+        while j > 0:
+            p.append(int(res["tokens"][j]))
+            j = res["parents"][j]
+        paths.append(p[::-1])
+    s = oracle.score_paths(inp, 0, cfg["M"], paths, cfg["T"])
+    np.testing.assert_array_equal(s, res["scores"][1:])
+
+
+def test_near_tie_gap_is_reported():
+    # two depth-1 candidates 1e-7 apart: a near tie that the flag must catch
+    base = np.array([[0.0, -1e-7, -3.0, -4.0]], np.float32)
+    V, E, H = 4, 2, 2
+    inp = dict(base=base[None], emb=np.zeros((V, E), np.float32), w_ih=np.zeros((3 * H, E), np.float32),
+               w_hh=np.zeros((3 * H, H), np.float32), b_ih=None, b_hh=None,
+               C=np.zeros((V, H), np.float32), h0=None)
+    res = oracle.build_request(inp, 0, 3, 2, 0.0, eps=1e-5)
+    assert res["flags"] & 1
+    assert 0 < res["min_gap"] < 1e-5
+    res = oracle.build_request(inp, 0, 3, 2, 0.0, eps=1e-8)
+    assert res["flags"] == 0
