@@ -1,0 +1,13 @@
+"""MI355X-native conditional draft-tree builder (DominoTree) -- Python binding.
+
+A thin ctypes layer over ``libdtree.so`` (the C ABI in ``include/dtree.h``).
+It only checks and marshals arguments: every step of the method runs in the
+library's HIP kernels.  PyTorch provides device memory and the current stream.
+There is no CPU fallback: if the library is missing, importing the binding's
+entry points raises.
+"""
+from ._lib import (  # noqa: F401
+    DT_BF16, DT_F32, Builder, DtreeError, dt_build, dt_correct, dt_create, dt_destroy,
+    dt_gru_step, dt_last_error, dt_status_string, dt_timing_enable, dt_timing_read, dt_topm,
+    dt_workspace_bytes, lib_path, load_library,
+)

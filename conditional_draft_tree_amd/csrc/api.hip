@@ -1,0 +1,389 @@
+// api.hip -- the C ABI declared in include/dtree.h: argument checks, the
+// workspace plan and the launch sequence of one build.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dtree.h"
+#include "dt_launch.h"
+
+namespace {
+
+using dt::u64;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+thread_local char g_create_error[512] = "";
+
+struct Layout {
+    size_t partial, tidx, tval, hstate, gates, gru_tok, gru_par, child_tok, child_lp, queue, qsize;
+    size_t total;
+};
+
+struct Marker {
+    char tag;  // 'S' start, 'T' top-M select, 'M' top-M merge, 'G' gate contraction,
+               // 'N' node step, 'E' end of a level-1 call
+    hipEvent_t ev;
+};
+
+}  // namespace
+
+struct dt_handle {
+    dt_config cfg;
+    int nseg;    // top-M segments per row
+    int ksplit;  // K slices of the gate contraction
+    Layout lay;
+    std::string err;
+    // timing
+    int tlevel = 0;
+    int tcapacity = 0;
+    std::vector<std::vector<Marker>> calls;
+    std::vector<hipEvent_t> pool;
+    size_t pool_used = 0;
+};
+
+namespace {
+
+dt_status fail(dt_handle* h, dt_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (h)
+        h->err = buf;
+    else
+        snprintf(g_create_error, sizeof g_create_error, "%s", buf);
+    return s;
+}
+
+dt_status hip_fail(dt_handle* h, hipError_t e, const char* what) {
+    return fail(h, DT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
+    Layout l{};
+    const size_t B = c.B, L = c.L, M = c.M, S = (size_t)c.n + 1, H = c.H;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    l.partial = take(B * L * (size_t)nseg * 64 * sizeof(u64));
+    l.tidx = take(B * L * M * 4);
+    l.tval = take(B * L * M * 4);
+    l.hstate = take(B * S * H * 4);
+    l.gates = take((size_t)ksplit * B * 4 * H * 4);
+    l.gru_tok = take(B * 4);
+    l.gru_par = take(B * 4);
+    l.child_tok = take(B * S * 64 * 4);
+    l.child_lp = take(B * S * 64 * 4);
+    l.queue = take(B * 64 * sizeof(u64));
+    l.qsize = take(B * 4);
+    l.total = off;
+    return l;
+}
+
+bool misaligned(const void* p) { return p && ((uintptr_t)p % 16) != 0; }
+
+dt_status check_ws(dt_handle* h, void* ws, size_t bytes) {
+    if (h->lay.total == 0) return DT_OK;
+    if (!ws) return fail(h, DT_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", h->lay.total);
+    if (bytes < h->lay.total)
+        return fail(h, DT_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", bytes, h->lay.total);
+    if ((uintptr_t)ws % kAlign)
+        return fail(h, DT_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    return DT_OK;
+}
+
+hipEvent_t take_event(dt_handle* h) {
+    if (h->pool_used == h->pool.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        h->pool.push_back(e);
+    }
+    return h->pool[h->pool_used++];
+}
+
+// Record a timing marker of the current call (level >= need).
+hipError_t mark(dt_handle* h, std::vector<Marker>* call, int need, char tag, hipStream_t st) {
+    if (!call || h->tlevel < need) return hipSuccess;
+    hipEvent_t e = take_event(h);
+    if (!e) return hipErrorOutOfMemory;
+    call->push_back({tag, e});
+    return hipEventRecord(e, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dt_status_string(dt_status s) {
+    switch (s) {
+        case DT_OK: return "ok";
+        case DT_ERR_INVALID_ARG: return "invalid argument";
+        case DT_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DT_ERR_WORKSPACE: return "workspace missing or too small";
+        case DT_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* dt_last_error(const dt_handle* h) { return h ? h->err.c_str() : g_create_error; }
+
+dt_status dt_create(const dt_config* cfg, dt_handle** out) {
+    if (!out) return fail(nullptr, DT_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg) return fail(nullptr, DT_ERR_INVALID_ARG, "cfg is NULL");
+    const dt_config c = *cfg;
+    if (c.dtype != DT_F32 && c.dtype != DT_BF16)
+        return fail(nullptr, DT_ERR_INVALID_ARG, "dtype %d is neither DT_F32 nor DT_BF16", (int)c.dtype);
+    if (c.B < 0 || c.L < 1 || c.V < 1 || c.E < 1 || c.H < 1 || c.M < 1 || c.n < 1)
+        return fail(nullptr, DT_ERR_INVALID_ARG,
+                    "sizes must be positive (B >= 0): B=%d L=%d V=%d E=%d H=%d M=%d n=%d", c.B, c.L,
+                    c.V, c.E, c.H, c.M, c.n);
+    if (c.M > c.V) return fail(nullptr, DT_ERR_INVALID_ARG, "M=%d exceeds V=%d", c.M, c.V);
+    if (!(c.temperature >= 0.f) || !(c.near_tie_eps >= 0.f))
+        return fail(nullptr, DT_ERR_INVALID_ARG, "temperature and near_tie_eps must be >= 0");
+    if (c.M > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "M=%d > 64 (one candidate per lane)", c.M);
+    if (c.n > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "n=%d > 64 (queue of one wave)", c.n);
+    if (c.L > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "L=%d > 64", c.L);
+    if (c.H > 4096) return fail(nullptr, DT_ERR_UNSUPPORTED, "H=%d > 4096", c.H);
+    if (c.dtype == DT_BF16 && (c.E % 32 || c.H % 32))
+        return fail(nullptr, DT_ERR_UNSUPPORTED, "bf16 needs E %% 32 == 0 and H %% 32 == 0 (E=%d H=%d)",
+                    c.E, c.H);
+    if (c.dtype == DT_F32 && (c.E % 4 || c.H % 4))
+        return fail(nullptr, DT_ERR_UNSUPPORTED, "f32 needs E %% 4 == 0 and H %% 4 == 0 (E=%d H=%d)",
+                    c.E, c.H);
+    if ((long long)c.B * c.L * c.V > (1ll << 40))
+        return fail(nullptr, DT_ERR_UNSUPPORTED, "B*L*V too large");
+    dt_handle* h = new dt_handle();
+    h->cfg = c;
+    h->nseg = dt::topm_segments(c.B * c.L, c.V);
+    h->ksplit = dt::gru_ksplit(c.B, c.E, c.H, (int)c.dtype);
+    h->lay = plan_layout(c, h->nseg, h->ksplit);
+    *out = h;
+    return DT_OK;
+}
+
+void dt_destroy(dt_handle* h) {
+    if (!h) return;
+    for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+    delete h;
+}
+
+size_t dt_workspace_bytes(const dt_handle* h) { return h ? h->lay.total : 0; }
+
+dt_status dt_timing_enable(dt_handle* h, int level, int capacity) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    if (level < 0 || level > 2 || capacity < 0)
+        return fail(h, DT_ERR_INVALID_ARG, "timing level must be 0..2 and capacity >= 0");
+    h->calls.clear();
+    h->pool_used = 0;
+    h->tlevel = level;
+    h->tcapacity = level ? capacity : 0;
+    return DT_OK;
+}
+
+dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out) {
+    if (!h || !n_out || (max > 0 && !ms)) return h ? fail(h, DT_ERR_INVALID_ARG, "null output") : DT_ERR_INVALID_ARG;
+    if (stage < 0 || stage > 5) return fail(h, DT_ERR_INVALID_ARG, "stage must be 0..5");
+    int n = 0;
+    for (const auto& call : h->calls) {
+        float sum = 0.f;
+        bool any = false;
+        for (size_t i = 1; i < call.size(); ++i) {
+            const char tag = call[i].tag;
+            bool hit = (stage == 0 && tag == 'T') || (stage == 1 && tag == 'M') ||
+                       (stage == 2 && tag == 'G') || (stage == 3 && tag == 'N') ||
+                       (stage == 5 && tag == 'G');
+            if (!hit) continue;
+            float t = 0.f;
+            hipError_t e = hipEventElapsedTime(&t, call[i - 1].ev, call[i].ev);
+            if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
+            if (stage == 5) {
+                if (n < max) ms[n] = t;
+                ++n;
+            } else {
+                sum += t;
+                any = true;
+            }
+        }
+        if (stage == 4 && call.size() >= 2) {
+            float t = 0.f;
+            hipError_t e = hipEventElapsedTime(&t, call.front().ev, call.back().ev);
+            if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
+            sum = t;
+            any = true;
+        }
+        if (stage != 5 && any) {
+            if (n < max) ms[n] = sum;
+            ++n;
+        }
+    }
+    *n_out = n;
+    return DT_OK;
+}
+
+dt_status dt_topm(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int32_t* idx, float* val,
+                  void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (c.B == 0) return DT_OK;
+    if (!base || !idx || !val) return fail(h, DT_ERR_INVALID_ARG, "dt_topm: null pointer");
+    if (misaligned(base) || misaligned(idx) || misaligned(val))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_topm: buffers must be 16-byte aligned");
+    dt_status s = check_ws(h, ws, ws_bytes);
+    if (s) return s;
+    hipError_t e = dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg,
+                                   (u64*)((char*)ws + h->lay.partial), c.M, idx, val,
+                                   (hipStream_t)stream, nullptr);
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_topm launch");
+}
+
+dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, const float* h_in,
+                      const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
+                      float* h_out, void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (c.B == 0) return DT_OK;
+    if (!x || !h_in || !W_ih || !W_hh || !h_out)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_gru_step: null pointer");
+    if (misaligned(x) || misaligned(h_in) || misaligned(W_ih) || misaligned(W_hh) || misaligned(h_out))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_gru_step: buffers must be 16-byte aligned");
+    if ((const void*)h_out == (const void*)h_in)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_gru_step: h_out must not alias h");
+    dt_status s = check_ws(h, ws, ws_bytes);
+    if (s) return s;
+    dt::GruGemmArgs g{};
+    g.x = x;
+    g.xtok = nullptr;
+    g.h = h_in;
+    g.hsel = nullptr;
+    g.hstride = (size_t)c.H;
+    g.W_ih = W_ih;
+    g.W_hh = W_hh;
+    g.gates = (float*)((char*)ws + h->lay.gates);
+    g.B = c.B;
+    g.E = c.E;
+    g.H = c.H;
+    g.ksplit = h->ksplit;
+    g.dtype = (int)c.dtype;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = dt::launch_gru_gemm(g, st);
+    if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step contraction launch");
+    e = dt::launch_gru_finalize(g.gates, g.ksplit, b_ih, b_hh, h_in, h_out, c.B, c.H, (int)c.dtype, st);
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_gru_step update launch");
+}
+
+dt_status dt_correct(dt_handle* h, const int32_t* idx, const float* val, const void* C,
+                     const float* h_in, const int32_t* pos, int32_t* tok_sorted, float* logp_sorted,
+                     void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (c.B == 0) return DT_OK;
+    if (!idx || !val || !C || !h_in || !pos || !tok_sorted || !logp_sorted)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_correct: null pointer");
+    if (misaligned(C) || misaligned(h_in))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_correct: C and h must be 16-byte aligned");
+    hipError_t e = dt::launch_correct(idx, val, C, h_in, pos, tok_sorted, logp_sorted, c.B, c.L, c.H,
+                                      c.M, (int)c.dtype, c.temperature, (hipStream_t)stream);
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_correct launch");
+}
+
+dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, const void* emb,
+                   const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
+                   const void* C, const float* h0, int32_t* tokens, int32_t* parents, int32_t* depths,
+                   float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (c.B == 0) return DT_OK;
+    if (!base || !emb || !W_ih || !W_hh || !C || !tokens || !parents || !depths || !scores || !mask ||
+        !count || !flags)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_build: null pointer (only b_ih, b_hh, h0 may be NULL)");
+    if (misaligned(base) || misaligned(emb) || misaligned(W_ih) || misaligned(W_hh) || misaligned(C) ||
+        misaligned(h0) || misaligned(b_ih) || misaligned(b_hh))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_build: matrices must be 16-byte aligned");
+    dt_status s = check_ws(h, ws, ws_bytes);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    char* w = (char*)ws;
+    const Layout& L = h->lay;
+
+    std::vector<Marker>* call = nullptr;
+    if (h->tlevel > 0 && (int)h->calls.size() < h->tcapacity) {
+        h->calls.emplace_back();
+        call = &h->calls.back();
+    }
+    hipError_t e;
+#define DT_TRY(expr, what)                                 \
+    do {                                                   \
+        e = (expr);                                        \
+        if (e != hipSuccess) return hip_fail(h, e, what);  \
+    } while (0)
+
+    DT_TRY(mark(h, call, 1, 'S', st), "timing event");
+    hipEvent_t ev_mid = nullptr;
+    if (call) {
+        ev_mid = take_event(h);
+        if (!ev_mid) return hip_fail(h, hipErrorOutOfMemory, "timing event");
+    }
+    int32_t* tidx = (int32_t*)(w + L.tidx);
+    float* tval = (float*)(w + L.tval);
+    DT_TRY(dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg, (u64*)(w + L.partial), c.M,
+                           tidx, tval, st, ev_mid),
+           "top-M launch");
+    if (call) call->push_back({'T', ev_mid});
+    DT_TRY(mark(h, call, 1, 'M', st), "timing event");
+
+    dt::NodeArgs a{};
+    a.B = c.B; a.L = c.L; a.V = c.V; a.E = c.E; a.H = c.H; a.M = c.M; a.n = c.n;
+    a.dtype = (int)c.dtype;
+    a.temp = c.temperature;
+    a.eps = c.near_tie_eps;
+    a.C = C; a.b_ih = b_ih; a.b_hh = b_hh; a.h0 = h0;
+    a.tidx = tidx; a.tval = tval;
+    a.hstate = (float*)(w + L.hstate);
+    a.gates = (float*)(w + L.gates);
+    a.ksplit = h->ksplit;
+    a.gru_tok = (int32_t*)(w + L.gru_tok);
+    a.gru_par = (int32_t*)(w + L.gru_par);
+    a.child_tok = (int32_t*)(w + L.child_tok);
+    a.child_lp = (float*)(w + L.child_lp);
+    a.queue = (u64*)(w + L.queue);
+    a.qsize = (int32_t*)(w + L.qsize);
+    a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
+    a.mask = mask; a.count = count; a.flags = flags;
+
+    dt::GruGemmArgs g{};
+    g.x = emb;
+    g.xtok = a.gru_tok;
+    g.h = a.hstate;
+    g.hsel = a.gru_par;
+    g.hstride = (size_t)(c.n + 1) * c.H;
+    g.W_ih = W_ih;
+    g.W_hh = W_hh;
+    g.gates = a.gates;
+    g.B = c.B; g.E = c.E; g.H = c.H;
+    g.ksplit = h->ksplit;
+    g.dtype = (int)c.dtype;
+
+    DT_TRY(dt::launch_node_step(a, 0, st), "node step launch");
+    DT_TRY(mark(h, call, 2, 'N', st), "timing event");
+    for (int step = 1; step < c.n; ++step) {
+        DT_TRY(dt::launch_gru_gemm(g, st), "gate contraction launch");
+        DT_TRY(mark(h, call, 2, 'G', st), "timing event");
+        DT_TRY(dt::launch_node_step(a, step, st), "node step launch");
+        DT_TRY(mark(h, call, 2, 'N', st), "timing event");
+    }
+    DT_TRY(mark(h, call, 1, 'E', st), "timing event");
+#undef DT_TRY
+    return DT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+/*
+ * dtree.h -- C ABI of the MI355X (gfx950) conditional draft-tree builder.
+ *
+ * The library builds DominoTree's conditional best-first draft trees on the
+ * GPU.  Sources, cited by site and section (arXiv:2607.08642, three pages):
+ *   [captcha] "DominoTree: Conditional Tree-Structured Drafting with Domino for
+ *             Speculative Decoding", blog.captcha.la research summary;
+ *   [zhichai] zhichai.top post on the same paper;
+ *   [gist]    gist.science explainer of the same paper (French).
+ *
+ * Conventions for every entry point below:
+ *  - Pointers named as device buffers are device pointers (e.g. from
+ *    torch.empty(..., device="cuda")).  They are BORROWED: the caller owns
+ *    them and keeps them alive until the work enqueued on `stream` is done.
+ *    Every matrix and table must be 16-byte aligned.
+ *  - Layouts are row-major and dense.  "dtype" tensors have the handle's
+ *    dt_config.dtype: IEEE binary32 (DT_F32) or bfloat16 (DT_BF16, stored as
+ *    16-bit patterns).  Hidden states and all scores are binary32.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work; none of them synchronizes.
+ *  - Argument errors return DT_ERR_INVALID_ARG / DT_ERR_UNSUPPORTED /
+ *    DT_ERR_WORKSPACE before anything is enqueued; dt_last_error() then holds
+ *    a message.  A failed launch returns DT_ERR_HIP.  Faults inside the
+ *    kernels surface as HIP errors at the caller's next synchronization.
+ *  - A handle is not thread-safe: one host thread at a time.  Overlapping
+ *    calls that share a workspace race; give concurrent calls their own
+ *    workspace.
+ *  - Base logits must be finite (no NaN, no infinities).
+ */
+#ifndef DTREE_H
+#define DTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DT_OK = 0,
+    DT_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned buffer      */
+    DT_ERR_UNSUPPORTED = -2, /* valid request outside what this build supports */
+    DT_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+    DT_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed      */
+} dt_status;
+
+typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
+
+/* Problem sizes, fixed at handle creation.
+ *   B  requests per call (independent trees)          B >= 0
+ *   L  block length = positions of base logits = max tree depth, 1..64
+ *   V  vocabulary size                                 V >= 1, V < 2^31
+ *   E  embedding width fed to the GRU                  bf16: multiple of 32; f32: multiple of 4
+ *   H  GRU hidden width                                bf16: multiple of 32; f32: multiple of 4; <= 4096
+ *   M  candidate width (top-M per position)            1..64, M <= V
+ *   n  node budget: non-root nodes per tree            1..64
+ *   temperature  0 = unscaled; > 0 divides the corrected logits before the
+ *                log-softmax ([captcha] "Methodology -- deep read": runs at
+ *                T in {0, 0.5, 1.0})
+ *   near_tie_eps decisions closer than this are flagged (e.g. 1e-5)         */
+typedef struct {
+    int32_t B, L, V, E, H, M, n;
+    float temperature;
+    dt_dtype dtype;
+    float near_tie_eps;
+} dt_config;
+
+typedef struct dt_handle dt_handle; /* opaque: configuration, launch plan, timing events */
+
+/* Validate `cfg` and create a handle.  Host only: no HIP call is made, so it
+ * works without a GPU.  On error *out is NULL and the message is available
+ * from dt_last_error(NULL). */
+dt_status dt_create(const dt_config *cfg, dt_handle **out);
+void dt_destroy(dt_handle *h);
+
+/* Device workspace bytes dt_build needs for this handle (caller allocates,
+ * 256-byte aligned).  dt_topm and dt_gru_step need no more than this. */
+size_t dt_workspace_bytes(const dt_handle *h);
+
+const char *dt_status_string(dt_status s);
+/* Last error message of `h` (or of the last failed dt_create when h is NULL). */
+const char *dt_last_error(const dt_handle *h);
+
+/*
+ * dt_build -- one speculative round's draft trees for B requests.
+ *
+ * The whole method runs on the device, with no host round trip:
+ *  1. top-M marginal candidates per request and block position ([captcha]
+ *     "Methodology -- deep read": per-node correction restricted to the
+ *     marginal top-M tokens; [gist] "Composants clés -- Restriction de
+ *     candidats (Top-M)");
+ *  2. best-first expansion keyed by cumulative conditional log-prob until n
+ *     nodes or the maximum depth L ([captcha] "Methodology -- deep read";
+ *     [gist] "Composants clés -- Tas de recherche de premier choix à score
+ *     conditionnel"); expanding node v advances the GRU hidden state by one
+ *     step with v's token (gate order reset, update, new; both biases), then
+ *     scores v's children over the top-M slice of block position depth(v):
+ *     z_j = base[pos, idx_j] + C[idx_j] . h_v, z /= T when T > 0, log-softmax
+ *     over the M-slice; children ranked by (log-prob desc, token id asc);
+ *  3. the prefix-closed tree and its ancestor-only attention mask ([captcha]
+ *     "Methodology -- deep read"; [gist] "Vérification").
+ * Queue order: (score desc, depth asc, parent slot asc, sibling rank asc).
+ * In DT_BF16 the GRU's W_hh product takes bf16(h) (round to nearest even);
+ * everything else uses the binary32 state.
+ *
+ * Inputs (device, dtype unless noted):
+ *   base_logits [B, L, V]   per-position base logits of each request
+ *   emb         [V, E]      token embeddings (GRU input)
+ *   W_ih [3H, E], W_hh [3H, H]; b_ih, b_hh [3H] or NULL (= zero)
+ *   C           [V, H]      correction matrix
+ *   h0          [B, H] binary32, or NULL (= zeros): hidden state at the root
+ * Outputs (device; n+1 slots per request, slot 0 = root, slots in pop order):
+ *   tokens  [B, n+1] int32   root -1; unused slots -1
+ *   parents [B, n+1] int32   root -1; unused slots -1
+ *   depths  [B, n+1] int32   root 0;  unused slots -1
+ *   scores  [B, n+1] binary32 cumulative conditional log-prob; root 0; unused -inf
+ *   mask    [B, n+1, n+1] uint8  mask[i][j] = 1 iff j == i or j is an ancestor
+ *                                of i; rows of unused slots are 0
+ *   count   [B] int32   non-root nodes built (< n only if the candidate tree
+ *                       is smaller than n)
+ *   flags   [B] uint32  bit 0: some pop beat the best remaining candidate by
+ *                       a positive margin below near_tie_eps
+ * workspace: device buffer of at least dt_workspace_bytes(h) bytes.
+ */
+dt_status dt_build(dt_handle *h, void *workspace, size_t ws_bytes, const void *base_logits,
+                   const void *emb, const void *W_ih, const void *W_hh, const void *b_ih,
+                   const void *b_hh, const void *C, const float *h0, int32_t *tokens,
+                   int32_t *parents, int32_t *depths, float *scores, uint8_t *mask,
+                   int32_t *count, uint32_t *flags, void *stream);
+
+/*
+ * dt_topm -- step 1 alone: per (request, position) row of base_logits
+ * [B, L, V] (dtype), the M largest values ordered by (value desc, token id
+ * asc).  Outputs idx [B, L, M] int32 and val [B, L, M] binary32 (exact input
+ * values).  ([captcha] "Methodology -- deep read": the builder precomputes
+ * the top-M marginal tokens per depth.)  Uses the workspace.
+ */
+dt_status dt_topm(dt_handle *h, void *workspace, size_t ws_bytes, const void *base_logits,
+                  int32_t *idx, float *val, void *stream);
+
+/*
+ * dt_gru_step -- the GRU update alone, batched over B rows: h_out[b] =
+ * GRUCell(x[b], h[b]) with x [B, E] (dtype), h [B, H] binary32, weights as in
+ * dt_build, h_out [B, H] binary32.  ([captcha] "Methodology -- deep read": the
+ * GRU hidden state is passed and updated along each candidate path.)  In
+ * DT_BF16 the gate contraction runs on bf16 matrix cores with binary32
+ * accumulation.  Uses the workspace.  h_out must not alias h.
+ */
+dt_status dt_gru_step(dt_handle *h, void *workspace, size_t ws_bytes, const void *x,
+                      const float *h_in, const void *W_ih, const void *W_hh, const void *b_ih,
+                      const void *b_hh, float *h_out, void *stream);
+
+/*
+ * dt_correct -- the conditional children distribution alone, one node per
+ * request: with idx/val the top-M tables [B, L, M] (as from dt_topm), pos [B]
+ * int32 the block position of each node's children (0..L-1), h [B, H]
+ * binary32 the node's hidden state and C [V, H] (dtype): z_j = val[b, pos, j]
+ * + C[idx[b, pos, j]] . h[b], z /= T when T > 0, log-softmax over the
+ * M-slice, children ranked by (log-prob desc, token id asc) into
+ * tok_sorted [B, M] int32 and logp_sorted [B, M] binary32.  ([captcha]
+ * "Methodology -- deep read": rows of the correction matrices and base logits
+ * of the top-M candidates are fetched; [gist] "Composants clés -- Restriction
+ * de candidats (Top-M)".)  Needs no workspace.
+ */
+dt_status dt_correct(dt_handle *h, const int32_t *idx, const float *val, const void *C,
+                     const float *h_in, const int32_t *pos, int32_t *tok_sorted,
+                     float *logp_sorted, void *stream);
+
+/*
+ * Stage timing for benchmarks.  dt_timing_enable(h, level, capacity) makes
+ * the next `capacity` dt_build calls record HIP events on their stream:
+ * level 1 around the top-M kernels only, level 2 around every kernel; level
+ * 0 turns timing off and drops recorded events.  After the stream is
+ * synchronized, dt_timing_read(h, stage, ms, max, n_out) returns per-call
+ * durations in milliseconds, oldest first:
+ *   stage 0  top-M select kernel (one launch per call)
+ *   stage 1  top-M merge kernel
+ *   stage 2  GRU gate contractions of the call, summed   (level 2)
+ *   stage 3  node (correction + queue) kernels, summed    (level 2)
+ *   stage 4  the whole call
+ *   stage 5  GRU gate contraction, every launch separately (level 2)
+ * Timing calls are host-side and need the handle's device to be current.
+ */
+dt_status dt_timing_enable(dt_handle *h, int level, int capacity);
+dt_status dt_timing_read(dt_handle *h, int stage, float *ms, int max, int *n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTREE_H */

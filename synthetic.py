@@ -165,3 +165,19 @@ def with_config(name: str, **over) -> dict:
     cfg = dict(CONFIGS[name])
     cfg.update(over)
     return cfg
+
+
+def to_torch(inp: dict, device) -> dict:
+    """The same inputs as torch tensors on `device` (uint16 bf16 patterns become
+    torch.bfloat16; None stays None)."""
+    import torch
+
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            out[k] = None
+        elif v.dtype == np.uint16:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(device)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+    return out

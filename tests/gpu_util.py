@@ -1,0 +1,88 @@
+"""Helpers of the GPU parity tests: run the library, compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+SCORE_TOL = 1e-4  # absolute, binary32 node scores vs the double-precision oracle
+
+
+def run_build(bld, t: dict):
+    import torch
+    out = bld.build(t["base"], t["emb"], t["w_ih"], t["w_hh"], t.get("b_ih"), t.get("b_hh"),
+                    t["C"], t.get("h0"))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def ancestor_mask(parents: np.ndarray, count: int) -> np.ndarray:
+    S = parents.shape[0]
+    m = np.zeros((S, S), np.uint8)
+    for i in range(count + 1):
+        j = i
+        while j >= 0:
+            m[i, j] = 1
+            j = parents[j] if j > 0 else -1
+    return m
+
+
+def check_valid_tree(got: dict, b: int, n: int, L: int):
+    """Properties every output must have, whatever the ties."""
+    cnt = int(got["count"][b])
+    tok, par, dep, sc = got["tokens"][b], got["parents"][b], got["depths"][b], got["scores"][b]
+    assert 0 <= cnt <= n
+    assert tok[0] == -1 and par[0] == -1 and dep[0] == 0 and sc[0] == 0.0
+    for v in range(1, cnt + 1):
+        q = par[v]
+        assert 0 <= q < v, (b, v, q)
+        assert dep[v] == dep[q] + 1 and 1 <= dep[v] <= L
+        assert sc[v] <= sc[q]
+        assert tok[v] >= 0
+    assert np.all(np.diff(sc[1:cnt + 1]) <= 0), "pop order must be by non-increasing score"
+    assert np.all(tok[cnt + 1:] == -1) and np.all(par[cnt + 1:] == -1)
+    assert np.all(dep[cnt + 1:] == -1) and np.all(np.isneginf(sc[cnt + 1:]))
+    np.testing.assert_array_equal(got["mask"][b], ancestor_mask(par, cnt))
+
+
+def paths_of(got: dict, b: int):
+    cnt = int(got["count"][b])
+    tok, par = got["tokens"][b], got["parents"][b]
+    out = []
+    for v in range(1, cnt + 1):
+        p, j = [], v
+        while j > 0:
+            p.append(int(tok[j]))
+            j = par[j]
+        out.append(p[::-1])
+    return out
+
+
+def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg: dict,
+                    eps: float = 1e-5) -> str:
+    """Compare request b_got of a GPU result with the oracle's tree `ref` of
+    request b_inp of `inp`.  Returns "exact" or "flagged"."""
+    n, L = cfg["n"], cfg["L"]
+    check_valid_tree(got, b_got, n, L)
+    assert int(got["count"][b_got]) == ref["count"]
+    gflag = int(got["flags"][b_got]) & 1
+    if ref["min_gap"] > 2 * eps:
+        assert gflag == 0, f"GPU flags a near tie the oracle puts at {ref['min_gap']:.3g}"
+    if ref["min_gap"] < eps / 2:
+        assert gflag == 1, f"GPU misses a near tie of {ref['min_gap']:.3g}"
+    cnt = ref["count"]
+    if ref["flags"] == 0:
+        for k in ("tokens", "parents", "depths", "mask"):
+            np.testing.assert_array_equal(got[k][b_got], ref[k], err_msg=k)
+        err = np.abs(got["scores"][b_got][:cnt + 1] - ref["scores"][:cnt + 1]).max()
+        assert err <= SCORE_TOL, f"score error {err}"
+        return "exact"
+    # A decision was closer than eps: several trees are correct.  What is
+    # unique is the multiset of the best scores; every GPU node must carry its
+    # own conditional score.
+    gs = got["scores"][b_got][1:cnt + 1].astype(np.float64)
+    rs = oracle.score_paths(inp, b_inp, cfg["M"], paths_of(got, b_got), cfg["T"])
+    assert np.all(np.isfinite(rs)), "GPU node outside the top-M candidate tree"
+    assert np.abs(gs - rs).max() <= SCORE_TOL
+    assert np.abs(np.sort(gs) - np.sort(ref["scores"][1:cnt + 1])).max() <= SCORE_TOL
+    return "flagged"

@@ -1,0 +1,123 @@
+"""The C ABI library, without a GPU: it loads, exports every symbol declared
+in include/dtree.h, and rejects bad arguments before enqueuing anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import conditional_draft_tree_amd as dtree
+from conditional_draft_tree_amd._lib import dt_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dtree.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dt_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("dt_create", "dt_destroy", "dt_workspace_bytes", "dt_build", "dt_topm",
+                 "dt_gru_step", "dt_correct", "dt_last_error", "dt_status_string",
+                 "dt_timing_enable", "dt_timing_read"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dtree.load_library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_library_is_built_for_gfx950():
+    with open(dtree.lib_path(), "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+
+
+def make(**kw):
+    cfg = dict(B=2, L=4, V=100, E=32, H=32, M=8, n=6, temperature=0.0, dtype=dtree.DT_BF16,
+               near_tie_eps=1e-5)
+    cfg.update(kw)
+    return dtree.dt_create(**cfg)
+
+
+def test_create_valid_and_workspace():
+    h = make()
+    assert dtree.dt_workspace_bytes(h) > 0
+    dtree.dt_destroy(h)
+    h = make(B=0)
+    dtree.dt_destroy(h)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), "INVALID_ARG"), (dict(V=0), "INVALID_ARG"), (dict(M=0), "INVALID_ARG"),
+    (dict(n=0), "INVALID_ARG"), (dict(B=-1), "INVALID_ARG"), (dict(M=101), "INVALID_ARG"),
+    (dict(temperature=-1.0), "INVALID_ARG"), (dict(dtype=7), "INVALID_ARG"),
+    (dict(M=65, V=1000), "UNSUPPORTED"), (dict(n=65), "UNSUPPORTED"), (dict(L=65), "UNSUPPORTED"),
+    (dict(E=48), "UNSUPPORTED"), (dict(H=24), "UNSUPPORTED"), (dict(H=48), "UNSUPPORTED"), (dict(H=8192), "UNSUPPORTED"),
+    (dict(dtype=dtree.DT_F32, E=6), "UNSUPPORTED"),
+])
+def test_create_rejects(kw, code):
+    with pytest.raises(ValueError, match=code):
+        make(**kw)
+    assert dtree.dt_last_error(None)  # message available without a handle
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert dtree.dt_status_string(s)
+
+
+def _raw_build(lib, h, ws, nbytes, ptr, **override):
+    args = dict(base=ptr, emb=ptr, w_ih=ptr, w_hh=ptr, b_ih=None, b_hh=None, C=ptr, h0=None,
+                tokens=ptr, parents=ptr, depths=ptr, scores=ptr, mask=ptr, count=ptr, flags=ptr)
+    args.update(override)
+    vals = [C.c_void_p(v) if v is not None else None for v in args.values()]
+    return lib.dt_build(h, C.c_void_p(ws) if ws else None, nbytes, *vals, None)
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only machines")
+def test_build_argument_errors_before_any_launch():
+    lib = dtree.load_library()
+    h = make()
+    need = dtree.dt_workspace_bytes(h)
+    fake = 0x10000  # never dereferenced: every call below fails validation
+    assert _raw_build(lib, h, fake, need, fake, C=None) == -1
+    assert "null" in dtree.dt_last_error(h)
+    assert _raw_build(lib, h, fake, need, fake, emb=fake + 4) == -1
+    assert "aligned" in dtree.dt_last_error(h)
+    assert _raw_build(lib, h, None, need, fake) == -3
+    assert _raw_build(lib, h, fake, need - 1, fake) == -3
+    assert _raw_build(lib, h, fake + 16, need, fake) == -3  # workspace alignment
+    dtree.dt_destroy(h)
+
+
+def test_empty_batch_is_a_noop():
+    lib = dtree.load_library()
+    h = make(B=0)
+    # B = 0: nothing to do, every pointer may be NULL
+    assert lib.dt_build(h, None, 0, *([None] * 15), None) == 0
+    assert lib.dt_topm(h, None, 0, None, None, None, None) == 0
+    dtree.dt_destroy(h)
+
+
+def test_timing_argument_checks():
+    lib = dtree.load_library()
+    h = make()
+    assert lib.dt_timing_enable(h, 3, 10) == -1
+    assert lib.dt_timing_enable(h, 1, -1) == -1
+    assert lib.dt_timing_enable(h, 0, 0) == 0
+    n = C.c_int(0)
+    assert lib.dt_timing_read(h, 9, None, 0, C.byref(n)) == -1
+    assert lib.dt_timing_read(h, 0, None, 0, C.byref(n)) == 0 and n.value == 0
+    dtree.dt_destroy(h)

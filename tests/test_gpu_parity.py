@@ -1,0 +1,222 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: top-M index sets and values bit-exact; tree topology (tokens, parents,
+depths, order, mask, count) bit-exact for every request whose decisions all
+clear the near-tie threshold; node scores within 1e-4 absolute.  Requests
+with a near tie are checked for validity and for the multiset of scores.
+Workloads: the named configurations at their real sizes (sampled requests
+where the oracle would be slow), plus edge cases.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+from gpu_util import SCORE_TOL, check_valid_tree, compare_request, run_build
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import conditional_draft_tree_amd as dtree  # noqa: E402
+
+DEV = torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=3)
+def inputs(name, variant="default", over=()):
+    cfg = S.with_config(name, **dict(over))
+    inp = S.make_inputs(cfg, seed=0, variant=variant)
+    return cfg, inp
+
+
+def builder(cfg, eps=1e-5):
+    return dtree.Builder(cfg["B"], cfg["L"], cfg["V"], cfg["E"], cfg["H"], cfg["M"], cfg["n"],
+                         cfg["T"], cfg["dtype"], eps, device=DEV)
+
+
+def build_and_compare(cfg, inp, requests=None, threads=8):
+    B = cfg["B"]
+    reqs = list(range(B)) if requests is None else list(requests)
+    say(f"  build B={B} V={cfg['V']} L={cfg['L']} E={cfg['E']} H={cfg['H']} M={cfg['M']} "
+        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']}")
+    bld = builder(cfg)
+    got = run_build(bld, S.to_torch(inp, DEV))
+    for b in range(B):
+        check_valid_tree(got, b, cfg["n"], cfg["L"])
+    refs = oracle.build_batch(inp, cfg["M"], cfg["n"], cfg["T"], requests=reqs, threads=threads)
+    kinds = [compare_request(got, b, r, inp, b, cfg) for b, r in zip(reqs, refs)]
+    bld.close()
+    say(f"  compared {len(reqs)} requests: {kinds.count('exact')} exact, "
+        f"{kinds.count('flagged')} near-tie")
+    return got, refs, kinds
+
+
+# ------------------------------------------------------------------ top-M --
+
+@pytest.mark.parametrize("dtype,V,M,L,B", [
+    ("f32", 1000, 8, 8, 1), ("bf16", 1000, 8, 8, 2), ("f32", 37, 37, 3, 2),
+    ("bf16", 5003, 64, 4, 3), ("bf16", 64, 64, 2, 1), ("f32", 131, 1, 5, 4),
+    ("bf16", 151936, 64, 16, 2),
+])
+def test_topm_bit_exact(dtype, V, M, L, B):
+    cfg = dict(B=B, V=V, L=L, E=32, H=32, M=M, n=4, dtype=dtype, alpha=1.1, T=0.0)
+    base = S.make_base(B, L, V, 1.1, dtype, seed=V + M)
+    # coarsen to force exact ties at and around the M boundary
+    if dtype == "bf16":
+        base = S.f32_to_bf16_bits(np.round(S.bf16_bits_to_f32(base) * 2) / 2)
+    else:
+        base = (np.round(base * 4) / 4).astype(np.float32)
+    bld = builder(cfg)
+    idx, val = bld.topm(S.to_torch({"b": base}, DEV)["b"])
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for b in range(B):
+        for p in range(L):
+            ri, rv = oracle.topm_row(base[b, p], M)
+            np.testing.assert_array_equal(idx[b, p], ri)
+            np.testing.assert_array_equal(val[b, p].astype(np.float64), rv)
+    bld.close()
+
+
+def test_topm_full_batch_sampled_rows():
+    cfg, inp = inputs("qwen3_4b_batched")
+    bld = builder(cfg)
+    idx, val = bld.topm(S.to_torch({"b": inp["base"]}, DEV)["b"])
+    torch.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    rng = np.random.default_rng(0)
+    for _ in range(24):
+        b, p = int(rng.integers(cfg["B"])), int(rng.integers(cfg["L"]))
+        ri, rv = oracle.topm_row(inp["base"][b, p], cfg["M"])
+        np.testing.assert_array_equal(idx[b, p], ri)
+        np.testing.assert_array_equal(val[b, p].astype(np.float64), rv)
+    # every row: sorted by (value desc, id asc), values read back exactly
+    v = val.reshape(-1, cfg["M"])
+    i = idx.reshape(-1, cfg["M"])
+    assert np.all((v[:, :-1] > v[:, 1:]) | ((v[:, :-1] == v[:, 1:]) & (i[:, :-1] < i[:, 1:])))
+    base = S.bf16_bits_to_f32(inp["base"]).reshape(-1, cfg["V"])
+    np.testing.assert_array_equal(np.take_along_axis(base, i.astype(np.int64), 1), v)
+    bld.close()
+
+
+# --------------------------------------------------------------- GRU step --
+
+@pytest.mark.parametrize("dtype,B,E,H", [("f32", 3, 32, 32), ("bf16", 64, 2560, 1024),
+                                         ("bf16", 70, 64, 96), ("bf16", 5, 4096, 1024)])
+def test_gru_step_matches_oracle(dtype, B, E, H):
+    cfg = dict(B=B, V=97, L=2, E=E, H=H, M=4, n=2, dtype=dtype, alpha=1.1, T=0.0)
+    inp = S.make_inputs(cfg, seed=B + E, variant="strong")
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, cfg["V"], B)
+    x = inp["emb"][rows]
+    h = rng.uniform(-1, 1, (B, H)).astype(np.float32)
+    t = S.to_torch(dict(x=x, h=h, w_ih=inp["w_ih"], w_hh=inp["w_hh"], b_ih=inp["b_ih"],
+                        b_hh=inp["b_hh"]), DEV)
+    bld = builder(cfg)
+    out = bld.gru_step(t["x"], t["h"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(B):
+        ref = oracle.gru(x, b, h[b].astype(np.float64), inp["w_ih"], inp["w_hh"], inp["b_ih"],
+                         inp["b_hh"])
+        np.testing.assert_allclose(out[b], ref, rtol=0, atol=2e-5)
+    bld.close()
+
+
+# -------------------------------------------------------- children scores --
+
+@pytest.mark.parametrize("dtype,T", [("bf16", 0.0), ("bf16", 1.0), ("f32", 0.5)])
+def test_correct_matches_oracle(dtype, T):
+    cfg = dict(B=16, V=3000, L=4, E=32, H=256 if dtype == "bf16" else 64, M=64, n=4, dtype=dtype,
+               alpha=1.1, T=T)
+    inp = S.make_inputs(cfg, seed=7, variant="strong")
+    rng = np.random.default_rng(2)
+    h = rng.normal(0, 0.5, (cfg["B"], cfg["H"])).astype(np.float32)
+    pos = rng.integers(0, cfg["L"], cfg["B"]).astype(np.int32)
+    bld = builder(cfg)
+    t = S.to_torch(dict(base=inp["base"], C=inp["C"], h=h, pos=pos), DEV)
+    idx, val = bld.topm(t["base"])
+    tok, lp = bld.correct(idx, val, t["C"], t["h"], t["pos"])
+    torch.cuda.synchronize()
+    tok, lp, idx, val = (a.cpu().numpy() for a in (tok, lp, idx, val))
+    for b in range(cfg["B"]):
+        rt, rl = oracle.dist(idx[b, pos[b]], val[b, pos[b]].astype(np.float64), inp["C"],
+                             h[b].astype(np.float64), T)
+        np.testing.assert_allclose(lp[b], rl, rtol=0, atol=1e-5)
+        gaps = np.diff(rl)
+        tie_free = np.all((gaps == 0) | (np.abs(gaps) > 1e-5))
+        if tie_free:
+            np.testing.assert_array_equal(tok[b], rt)
+        else:
+            assert sorted(tok[b]) == sorted(rt)
+    bld.close()
+
+
+# ------------------------------------------------------------ whole build --
+
+@pytest.mark.parametrize("variant,over", [
+    ("default", ()), ("strong", ()), ("zero_c", ()), ("strong", (("T", 0.5),)),
+    ("strong", (("M", 1),)), ("strong", (("n", 1),)), ("strong", (("L", 1), ("n", 5))),
+    ("strong", (("B", 5),)), ("strong", (("V", 37), ("M", 8))), ("strong", (("n", 64), ("L", 8))),
+])
+def test_build_tiny(variant, over):
+    cfg = S.with_config("tiny", **dict(over))
+    inp = S.make_inputs(cfg, seed=3, variant=variant)
+    got, refs, kinds = build_and_compare(cfg, inp)
+    if cfg["M"] == 1:
+        assert got["count"][0] == min(cfg["n"], cfg["L"])
+
+
+@pytest.mark.parametrize("variant", ["strong", "zero_c"])
+def test_build_bf16_ragged(variant):
+    # several GEMM row blocks with a ragged tail (70 = 64 + 6), V not a multiple
+    # of 8 (scalar top-M path), n = 64 (queue of one full wave)
+    cfg = dict(B=70, V=5003, L=16, E=256, H=128, M=64, n=64, dtype="bf16", alpha=1.5, T=0.0)
+    inp = S.make_inputs(cfg, seed=5, variant=variant)
+    build_and_compare(cfg, inp, requests=range(0, 70, 3))
+
+
+def test_build_qwen3_4b_single():
+    cfg, inp = inputs("qwen3_4b_single")
+    build_and_compare(cfg, inp)
+
+
+def test_build_qwen3_4b_batched_and_rerun_identical():
+    cfg, inp = inputs("qwen3_4b_batched")
+    got, _, _ = build_and_compare(cfg, inp, requests=[0, 1, 17, 33, 50, 63])
+    bld = builder(cfg)
+    again = run_build(bld, S.to_torch(inp, DEV))
+    bld.close()
+    for k in got:
+        np.testing.assert_array_equal(got[k], again[k], err_msg=f"rerun differs in {k}")
+
+
+def test_build_qwen3_4b_batched_strong_correction():
+    cfg, inp = inputs("qwen3_4b_batched", "strong")
+    build_and_compare(cfg, inp, requests=[2, 31, 60])
+
+
+def test_build_qwen3_8b():
+    cfg, inp = inputs("qwen3_8b")
+    build_and_compare(cfg, inp, requests=[0, 13, 31])
+
+
+def test_build_stress_and_zero_correction_ablation():
+    cfg, inp = inputs("stress")
+    got, _, _ = build_and_compare(cfg, inp, requests=[0, 100, 255])
+    # peaked logits drive chains to the maximum depth
+    assert got["depths"].max() == cfg["L"]
+    z = dict(inp)
+    z["C"] = np.zeros_like(inp["C"])
+    build_and_compare(cfg, z, requests=[0, 128, 255])
