@@ -233,10 +233,11 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, int
             if (lane == qs) q = key;
             ++qs;
         }
-        // near tie: the popped key vs the best one left
-        if (qs > 0) {
-            const float gap = psc - qk_score(wave_max_u64(q));
-            if (gap > 0.f && gap < a.eps) flag |= 1u;
+        // near tie: the popped score vs every candidate left (binary32 gaps;
+        // an exact tie is broken by the queue order and not flagged)
+        {
+            const float gap = psc - qk_score(q);
+            if (__ballot(lane < qs && gap > 0.f && gap < a.eps)) flag |= 1u;
         }
         const int v = step + 1;
         new_cnt = v;

@@ -119,8 +119,9 @@ const char *dt_last_error(const dt_handle *h);
  *                                of i; rows of unused slots are 0
  *   count   [B] int32   non-root nodes built (< n only if the candidate tree
  *                       is smaller than n)
- *   flags   [B] uint32  bit 0: some pop beat the best remaining candidate by
- *                       a positive margin below near_tie_eps
+ *   flags   [B] uint32  bit 0: some pop beat a candidate left in the queue by
+ *                       a positive binary32 margin below near_tie_eps (exact
+ *                       ties are broken by the queue order, not flagged)
  * workspace: device buffer of at least dt_workspace_bytes(h) bytes.
  */
 dt_status dt_build(dt_handle *h, void *workspace, size_t ws_bytes, const void *base_logits,

@@ -52,9 +52,15 @@
  *   - ties: children are ranked by (log-prob desc, token id asc); queue
  *     entries by (score desc, depth asc, parent pop index asc, sibling rank
  *     asc), a total order;
- *   - near ties: the smallest positive score gap between a popped entry and
- *     the best entry left in the queue right after it is reported, and a
- *     flag is raised when it is below eps;
+ *   - near ties: at each pop, every candidate left in the queue whose score
+ *     is within eps of the popped one is a near tie, unless both scores are
+ *     sums of the identical sequence of log-prob terms (exact zeros
+ *     dropped), which every floating-point evaluation ties exactly; the
+ *     smallest such gap (0 included) is reported and a flag is raised when
+ *     it is below eps.  Losslessness only holds up to floating-point
+ *     tie-breaking ([captcha] "Threat model"; [gist] "Résultats
+ *     expérimentaux -- Absence de perte"): mathematically equal scores
+ *     reached through different additions are such tie-breaks;
  *   - in the bf16 configuration the GRU's recurrent matrix product takes the
  *     hidden state rounded to bf16 (round to nearest even from its fp32
  *     value), as a bf16 matrix unit must; everything else uses the unrounded
@@ -247,6 +253,34 @@ typedef struct {
     int rank;     /* its rank among the parent's sorted children */
 } qent_t;
 
+/* Log-prob terms along the path of a candidate (parent q, rank r): the
+ * parent's path terms, then the candidate's own log-prob; exact zeros are
+ * dropped because adding 0 never changes a floating-point sum. */
+static int path_terms(const double *plp, const int *plen, const double *clp, int L, int M,
+                      const qent_t *c, double *out)
+{
+    int k = 0;
+    for (int i = 0; i < plen[c->parent]; ++i) {
+        double t = plp[(size_t)c->parent * L + i];
+        if (t != 0.0) out[k++] = t;
+    }
+    double t = clp[(size_t)c->parent * M + c->rank];
+    if (t != 0.0) out[k++] = t;
+    return k;
+}
+
+/* 1 when the two candidates' scores add the identical sequence of terms */
+static int same_terms(const double *plp, const int *plen, const double *clp, int L, int M,
+                      const qent_t *a, const qent_t *b, double *wa, double *wb)
+{
+    int na = path_terms(plp, plen, clp, L, M, a, wa);
+    int nb = path_terms(plp, plen, clp, L, M, b, wb);
+    if (na != nb) return 0;
+    for (int i = 0; i < na; ++i)
+        if (wa[i] != wb[i]) return 0;
+    return 1;
+}
+
 /* 1 when a comes before b in the queue's total order */
 static int q_before(const qent_t *a, const qent_t *b)
 {
@@ -303,7 +337,7 @@ static qent_t q_pop(queue_t *q)
  * Outputs (n+1 tree slots; slot 0 is the root):
  *   tokens/parents/depths [n+1] int32, scores [n+1] double, mask [(n+1)^2],
  *   count (non-root nodes built), flags (bit 0: a near tie below eps),
- *   min_gap (smallest positive gap seen, +inf if none),
+ *   min_gap (smallest near-tie gap seen, +inf if none below eps),
  *   topm_idx/topm_val [L,M] (optional, may be NULL).
  */
 int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int dtype, double eps,
@@ -325,8 +359,12 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
     double *hs = (double *)malloc((size_t)S * H * sizeof *hs);
     int32_t *ctok = (int32_t *)malloc((size_t)S * M * sizeof *ctok);
     double *clp = (double *)malloc((size_t)S * M * sizeof *clp);
+    double *plp = (double *)malloc((size_t)S * L * sizeof *plp); /* path terms per slot */
+    int *plen = (int *)malloc((size_t)S * sizeof *plen);
+    double *wa = (double *)malloc((size_t)(L + 1) * sizeof *wa);
+    double *wb = (double *)malloc((size_t)(L + 1) * sizeof *wb);
     queue_t q = {(qent_t *)malloc((size_t)(2 * S + 2) * sizeof(qent_t)), 0};
-    if (!tidx || !tval || !hs || !ctok || !clp || !q.e) goto done;
+    if (!tidx || !tval || !hs || !ctok || !clp || !plp || !plen || !wa || !wb || !q.e) goto done;
 
     /* 1. top-M marginal candidates per block position */
     const size_t esz = (dtype == OR_F32) ? 4 : 2;
@@ -348,6 +386,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
      * depth 1 and take their tokens from block position 0 */
     depths[0] = 0;
     scores[0] = 0.0;
+    plen[0] = 0;
     for (int k = 0; k < H; ++k) hs[k] = h0 ? (double)h0[k] : 0.0;
     rc = oracle_dist(tidx, tval, M, C, dtype, H, hs, T, ctok, clp);
     if (rc) goto done;
@@ -361,14 +400,20 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
         parents[v] = c.parent;
         depths[v] = c.depth;
         scores[v] = c.score;
+        plen[v] = plen[c.parent] + 1;
+        for (int i = 0; i < plen[c.parent]; ++i)
+            plp[(size_t)v * L + i] = plp[(size_t)c.parent * L + i];
+        plp[(size_t)v * L + plen[c.parent]] = clp[(size_t)c.parent * M + c.rank];
         /* the popped node's next-ranked sibling becomes a candidate */
         if (c.rank + 1 < M)
             q_push(&q, (qent_t){scores[c.parent] + clp[(size_t)c.parent * M + c.rank + 1], c.depth,
                                 c.parent, c.rank + 1});
-        /* near-tie bookkeeping: gap to the best remaining candidate */
-        if (q.size > 0) {
-            double gap = c.score - q.e[0].score;
-            if (gap > 0.0 && gap < *min_gap) *min_gap = gap;
+        /* near-tie bookkeeping: gaps to the candidates left in the queue */
+        for (int i = 0; i < q.size; ++i) {
+            double gap = c.score - q.e[i].score;
+            if (gap >= eps || gap >= *min_gap) continue;
+            if (gap == 0.0 && same_terms(plp, plen, clp, L, M, &c, &q.e[i], wa, wb)) continue;
+            *min_gap = gap;
         }
         /* expand: GRU step with the realized token, then score its children
          * at block position depth(v).  Nodes at the maximum depth have no
@@ -396,7 +441,8 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
     if (topm_val) memcpy(topm_val, tval, (size_t)L * M * sizeof *tval);
     rc = OR_OK;
 done:
-    free(tidx); free(tval); free(hs); free(ctok); free(clp); free(q.e);
+    free(tidx); free(tval); free(hs); free(ctok); free(clp); free(plp); free(plen); free(wa);
+    free(wb); free(q.e);
     return rc;
 }
 

@@ -310,6 +310,26 @@ def test_hand_derived_example(fixture):
     ref = [eval(s, {"log": math.log, "exp": math.exp}) for s in g["scores_closed_form"]]
     np.testing.assert_allclose(res["scores"], ref, atol=1e-15)
     np.testing.assert_array_equal(res["mask"], g["mask"])
+    # their exact ties add the same terms: every precision ties them, no flag
+    assert res["flags"] == 0
+
+
+def _zero_model_inputs(base):
+    base = np.asarray(base, np.float32)[None]
+    V, E, H = base.shape[2], 2, 2
+    return dict(base=base, emb=np.zeros((V, E), np.float32), w_ih=np.zeros((3 * H, E), np.float32),
+                w_hh=np.zeros((3 * H, H), np.float32), b_ih=None, b_hh=None,
+                C=np.zeros((V, H), np.float32), h0=None)
+
+
+def test_equal_scores_from_different_terms_are_near_ties():
+    """Paths (token 0, token 1) and (token 1, token 0) over two positions with
+    the same logits have mathematically equal scores built from different
+    additions; floating point may break that tie either way, so it is flagged
+    even when double precision happens to give an exact tie."""
+    inp = _zero_model_inputs([[1.0, 0.5, -9.0, -9.0], [1.0, 0.5, -9.0, -9.0]])
+    res = oracle.build_request(inp, 0, 2, 4, 0.0, eps=1e-5)
+    assert res["flags"] & 1 and res["min_gap"] < 1e-12
 
 
 # ---------------------------------------------------------- structure -----
@@ -395,3 +415,17 @@ def test_near_tie_gap_is_reported():
     assert 0 < res["min_gap"] < 1e-5
     res = oracle.build_request(inp, 0, 3, 2, 0.0, eps=1e-8)
     assert res["flags"] == 0
+
+
+def test_near_tie_behind_an_exact_structural_tie_is_found():
+    """After the second pop the queue holds the popped node's sibling (an exact
+    tie adding the same terms: no flag) and, 1e-6 lower, the root's second
+    child (different terms: a near tie).  Every candidate within eps counts,
+    not only the best one."""
+    import math as _m
+    v1 = np.float32(1.0 - _m.log(2.0) - 1e-6)
+    inp = _zero_model_inputs([[1.0, v1, -9.0, -9.0], [0.0, 0.0, -9.0, -9.0]])
+    res = oracle.build_request(inp, 0, 2, 2, 0.0, eps=1e-5)
+    np.testing.assert_array_equal(res["tokens"], [-1, 0, 0])
+    np.testing.assert_array_equal(res["depths"], [0, 1, 2])
+    assert res["flags"] & 1 and 5e-7 < res["min_gap"] < 2e-6
