@@ -61,10 +61,8 @@
  *     tie-breaking ([captcha] "Threat model"; [gist] "Résultats
  *     expérimentaux -- Absence de perte"): mathematically equal scores
  *     reached through different additions are such tie-breaks;
- *   - in the bf16 configuration the GRU's recurrent matrix product takes the
- *     hidden state rounded to bf16 (round to nearest even from its fp32
- *     value), as a bf16 matrix unit must; everything else uses the unrounded
- *     state.
+ *   - the hidden state is a real-valued state: it is never rounded to the
+ *     storage type of the weights (the pages fix no precision for it).
  *
  * Arithmetic is double precision throughout; fp32 and bf16 inputs are
  * widened exactly.
@@ -91,23 +89,6 @@ static double load_elem(const void *p, int dtype, size_t i)
     uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
-    return (double)f;
-}
-
-/* Round a hidden-state value the way the bf16 matrix unit receives it: first
- * to binary32 (the state's storage type), then to bf16 with round to nearest,
- * ties to even.  Hidden states are finite (|h| <= 1 by construction). */
-static double to_bf16_operand(double h)
-{
-    float f = (float)h;
-    uint32_t u;
-    memcpy(&u, &f, sizeof u);
-    uint32_t lower = u & 0xFFFFu;
-    uint32_t upper = u >> 16;
-    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
-        upper += 1u;
-    u = upper << 16;
-    memcpy(&f, &u, sizeof f);
     return (double)f;
 }
 
@@ -158,11 +139,8 @@ int oracle_gru(const void *xmat, int64_t xrow, int dtype, const double *h,
 {
     if (!xmat || !h || !W_ih || !W_hh || !h_out || E < 1 || H < 1 || xrow < 0)
         return OR_EINVAL;
-    double *hb = (double *)malloc((size_t)H * sizeof *hb);
     double *x = (double *)malloc((size_t)E * sizeof *x);
-    if (!hb || !x) { free(hb); free(x); return OR_ENOMEM; }
-    for (int k = 0; k < H; ++k)
-        hb[k] = (dtype == OR_BF16) ? to_bf16_operand(h[k]) : h[k];
+    if (!x) return OR_ENOMEM;
     for (int k = 0; k < E; ++k)
         x[k] = load_elem(xmat, dtype, (size_t)xrow * (size_t)E + (size_t)k);
 
@@ -175,7 +153,7 @@ int oracle_gru(const void *xmat, int64_t xrow, int dtype, const double *h,
                 si += load_elem(W_ih, dtype, row * (size_t)E + (size_t)k) * x[k];
             double sh = b_hh ? load_elem(b_hh, dtype, row) : 0.0;
             for (int k = 0; k < H; ++k)
-                sh += load_elem(W_hh, dtype, row * (size_t)H + (size_t)k) * hb[k];
+                sh += load_elem(W_hh, dtype, row * (size_t)H + (size_t)k) * h[k];
             gi[g] = si;
             gh[g] = sh;
         }
@@ -184,7 +162,6 @@ int oracle_gru(const void *xmat, int64_t xrow, int dtype, const double *h,
         double c = tanh(gi[2] + r * gh[2]);
         h_out[o] = (1.0 - u) * c + u * h[o];
     }
-    free(hb);
     free(x);
     return OR_OK;
 }
