@@ -20,7 +20,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 thread_local char g_create_error[512] = "";
 
 struct Layout {
-    size_t partial, tidx, tval, hstate, gates, gru_tok, gru_par, child_tok, child_lp, queue, qsize;
+    size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue,
+        qsize;
     size_t total;
 };
 
@@ -35,7 +36,8 @@ struct Marker {
 struct dt_handle {
     dt_config cfg;
     int nseg;    // top-M segments per row
-    int ksplit;  // K slices of the gate contraction
+    int ksplit;  // K ranges of the gate contraction
+    dt::NodeLds lds;
     Layout lay;
     std::string err;
     // timing
@@ -78,7 +80,8 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.tidx = take(B * L * M * 4);
     l.tval = take(B * L * M * 4);
     l.hstate = take(B * S * H * 4);
-    l.gates = take((size_t)ksplit * B * 4 * H * 4);
+    l.hsplit = take(c.dtype == DT_BF16 ? B * S * 3 * H * 2 : 0);
+    l.gpart = take((size_t)ksplit * B * dt::kGateSlotsHost * H * 4);
     l.gru_tok = take(B * 4);
     l.gru_par = take(B * 4);
     l.child_tok = take(B * S * 64 * 4);
@@ -162,10 +165,16 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
                     c.E, c.H);
     if ((long long)c.B * c.L * c.V > (1ll << 40))
         return fail(nullptr, DT_ERR_UNSUPPORTED, "B*L*V too large");
+    const dt::NodeLds lds = dt::node_lds_plan(c.L, c.M, c.n, c.H);
+    if (lds.bytes > 65536)
+        return fail(nullptr, DT_ERR_UNSUPPORTED,
+                    "per-request state needs %zu bytes of LDS (> 64 KiB): lower L*M, n or H",
+                    lds.bytes);
     dt_handle* h = new dt_handle();
     h->cfg = c;
     h->nseg = dt::topm_segments(c.B * c.L, c.V);
     h->ksplit = dt::gru_ksplit(c.B, c.E, c.H, (int)c.dtype);
+    h->lds = lds;
     h->lay = plan_layout(c, h->nseg, h->ksplit);
     *out = h;
     return DT_OK;
@@ -260,24 +269,29 @@ dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, co
         return fail(h, DT_ERR_INVALID_ARG, "dt_gru_step: h_out must not alias h");
     dt_status s = check_ws(h, ws, ws_bytes);
     if (s) return s;
-    dt::GruGemmArgs g{};
+    hipStream_t st = (hipStream_t)stream;
+    char* w = (char*)ws;
+    dt::GruGatesArgs g{};
     g.x = x;
     g.xtok = nullptr;
-    g.h = h_in;
+    g.hsplit = (uint16_t*)(w + h->lay.hsplit);
+    g.hf = h_in;
+    g.hrows = 1;
     g.hsel = nullptr;
-    g.hstride = (size_t)c.H;
     g.W_ih = W_ih;
     g.W_hh = W_hh;
-    g.gates = (float*)((char*)ws + h->lay.gates);
+    g.partial = (float*)(w + h->lay.gpart);
     g.B = c.B;
     g.E = c.E;
     g.H = c.H;
     g.ksplit = h->ksplit;
     g.dtype = (int)c.dtype;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = dt::launch_gru_gemm(g, st);
+    hipError_t e = hipSuccess;
+    if (c.dtype == DT_BF16) e = dt::launch_split(h_in, (uint16_t*)g.hsplit, c.B, c.H, st);
+    if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step split launch");
+    e = dt::launch_gru_gates(g, st);
     if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step contraction launch");
-    e = dt::launch_gru_finalize(g.gates, g.ksplit, b_ih, b_hh, h_in, h_out, c.B, c.H, (int)c.dtype, st);
+    e = dt::launch_finalize(g.partial, g.ksplit, b_ih, b_hh, h_out, c.B, c.H, (int)c.dtype, st);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_gru_step update launch");
 }
 
@@ -346,10 +360,12 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.dtype = (int)c.dtype;
     a.temp = c.temperature;
     a.eps = c.near_tie_eps;
-    a.C = C; a.b_ih = b_ih; a.b_hh = b_hh; a.h0 = h0;
+    a.C = C; a.h0 = h0;
     a.tidx = tidx; a.tval = tval;
+    a.b_ih = b_ih; a.b_hh = b_hh;
     a.hstate = (float*)(w + L.hstate);
-    a.gates = (float*)(w + L.gates);
+    a.hsplit = c.dtype == DT_BF16 ? (uint16_t*)(w + L.hsplit) : nullptr;
+    a.partial = (const float*)(w + L.gpart);
     a.ksplit = h->ksplit;
     a.gru_tok = (int32_t*)(w + L.gru_tok);
     a.gru_par = (int32_t*)(w + L.gru_par);
@@ -360,25 +376,26 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
     a.mask = mask; a.count = count; a.flags = flags;
 
-    dt::GruGemmArgs g{};
+    dt::GruGatesArgs g{};
     g.x = emb;
     g.xtok = a.gru_tok;
-    g.h = a.hstate;
+    g.hsplit = a.hsplit;
+    g.hf = a.hstate;
+    g.hrows = c.n + 1;
     g.hsel = a.gru_par;
-    g.hstride = (size_t)(c.n + 1) * c.H;
     g.W_ih = W_ih;
     g.W_hh = W_hh;
-    g.gates = a.gates;
+    g.partial = (float*)(w + L.gpart);
     g.B = c.B; g.E = c.E; g.H = c.H;
     g.ksplit = h->ksplit;
     g.dtype = (int)c.dtype;
 
-    DT_TRY(dt::launch_node_step(a, 0, st), "node step launch");
+    DT_TRY(dt::launch_node_step(a, h->lds, 0, st), "node step launch");
     DT_TRY(mark(h, call, 2, 'N', st), "timing event");
     for (int step = 1; step < c.n; ++step) {
-        DT_TRY(dt::launch_gru_gemm(g, st), "gate contraction launch");
+        DT_TRY(dt::launch_gru_gates(g, st), "GRU contraction launch");
         DT_TRY(mark(h, call, 2, 'G', st), "timing event");
-        DT_TRY(dt::launch_node_step(a, step, st), "node step launch");
+        DT_TRY(dt::launch_node_step(a, h->lds, step, st), "node step launch");
         DT_TRY(mark(h, call, 2, 'N', st), "timing event");
     }
     DT_TRY(mark(h, call, 1, 'E', st), "timing event");

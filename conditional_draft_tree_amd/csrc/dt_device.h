@@ -146,28 +146,49 @@ __device__ __forceinline__ float load_param(const void* p, int dtype, size_t i) 
     return dtype == 1 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
 
-// GRU elementwise update of hidden unit k of row b from the K-split partial
-// gate sums (layout of GruGemmArgs::gates), the biases and the previous state:
-// reset r, update u, candidate c; h' = (1 - u) c + u h.
-__device__ __forceinline__ float gru_unit_update(const float* gates, int ksplit, int B, int b,
-                                                 int H, int k, const void* b_ih, const void* b_hh,
-                                                 int dtype, float hprev) {
-    float pr = 0.f, pz = 0.f, px = 0.f, ph = 0.f;
-    for (int s = 0; s < ksplit; ++s) {
-        const float* g = gates + ((size_t)(s * B + b) * 4) * H + k;
-        pr += g[0];
-        pz += g[H];
-        px += g[2 * H];
-        ph += g[3 * H];
-    }
-    pr += load_param(b_ih, dtype, k) + load_param(b_hh, dtype, k);
-    pz += load_param(b_ih, dtype, H + k) + load_param(b_hh, dtype, H + k);
-    px += load_param(b_ih, dtype, 2 * H + k);
-    ph += load_param(b_hh, dtype, 2 * H + k);
-    float r = 1.f / (1.f + expf(-pr));
-    float u = 1.f / (1.f + expf(-pz));
-    float c = tanhf(px + r * ph);
+// GRU elementwise update of hidden unit k from its gate sums (bias not yet
+// added): reset r, update u, candidate c; h' = (1 - u) c + u h.
+__device__ __forceinline__ float gru_cell(float sr, float sz, float snx, float snh, const void* b_ih,
+                                          const void* b_hh, int dtype, int H, int k, float hprev) {
+    sr += load_param(b_ih, dtype, k) + load_param(b_hh, dtype, k);
+    sz += load_param(b_ih, dtype, H + k) + load_param(b_hh, dtype, H + k);
+    snx += load_param(b_ih, dtype, 2 * H + k);
+    snh += load_param(b_hh, dtype, 2 * H + k);
+    const float r = 1.f / (1.f + expf(-sr));
+    const float u = 1.f / (1.f + expf(-sz));
+    const float c = tanhf(snx + r * snh);
     return (1.f - u) * c + u * hprev;
+}
+
+// Partial-sum buffer of the gate contraction: [ksplit][B][kGateSlots][H],
+// slots 0 reset, 1 update, 2 candidate (x part), 3 candidate (h part), 4 the
+// previous state (K range 0 only).
+constexpr int kGateSlots = 5;
+
+// New state of (row b, unit k): the K-range partials added in K order.
+__device__ __forceinline__ float gru_from_partials(const float* partial, int ksplit, int B, int b,
+                                                   int H, int k, const void* b_ih, const void* b_hh,
+                                                   int dtype) {
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ksplit; ++s) {
+        const float* p = partial + ((size_t)(s * B + b) * kGateSlots) * H + k;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) t[g] += p[(size_t)g * H];
+    }
+    const float hprev = partial[((size_t)b * kGateSlots + 4) * H + k];
+    return gru_cell(t[0], t[1], t[2], t[3], b_ih, b_hh, dtype, H, k, hprev);
+}
+
+// x = p[0] + p[1] + p[2] exactly, each part a bf16 (bits returned): every
+// subtraction below is exact, and the last remainder has at most 8
+// significant bits.
+__device__ __forceinline__ void split3_bf16(float x, uint32_t p[3]) {
+    float r = x;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        p[s] = f32_to_bf16_rne(r);
+        r = r - bf16_to_f32(p[s]);
+    }
 }
 
 }  // namespace dt

@@ -17,30 +17,36 @@ int topm_segments(int rows, int V);
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial, int M,
                        int32_t* idx, float* val, hipStream_t stream, hipEvent_t ev_mid);
 
-// ---- GRU gate contraction (gru.hip) ----------------------------------------
-// Partial gate sums for every row b < B, written as
-//   gates[((s * B + b) * 4 + g) * H + j],  g = 0 reset, 1 update, 2 new (x
-// part), 3 new (h part), s < ksplit (K-split slices, summed by the consumer).
-// Row b's GRU input x is x + xrow(b) * E with xrow(b) = xtok ? xtok[b] : b;
-// a negative xtok[b] marks an idle row (its gates are not needed).  Row b's
-// hidden state is h + b * hstride + (hsel ? hsel[b] : 0) * H.
-struct GruGemmArgs {
+// ---- GRU gate contraction (gru.hip) -----------------------------------------
+// For every row b < B: x = x + xrow(b) * E with xrow(b) = xtok ? xtok[b] : b
+// (a negative xtok[b] marks an idle row); its state is number
+// state_index(b) = b * hrows + (hsel ? hsel[b] : 0) of `hsplit` (bf16, [3][H]
+// per state: its exact three-part split; bf16 path) or `hf` (binary32, [H]
+// per state; binary32 path).  Writes the K-range partial sums and the
+// previous state to `partial` ([ksplit][B][kGateSlots][H], see dt_device.h).
+struct GruGatesArgs {
     const void* x;
     const int32_t* xtok;
-    const float* h;
+    const uint16_t* hsplit;
+    const float* hf;
+    int hrows;
     const int32_t* hsel;
-    size_t hstride;
     const void* W_ih;
     const void* W_hh;
-    float* gates;
+    float* partial;
     int B, E, H, ksplit, dtype;
 };
+__device__ __forceinline__ size_t state_index(const GruGatesArgs& a, int b) {
+    return (size_t)b * a.hrows + (size_t)(a.hsel ? a.hsel[b] : 0);
+}
 int gru_ksplit(int B, int E, int H, int dtype);
-hipError_t launch_gru_gemm(const GruGemmArgs& a, hipStream_t stream);
-// h_out[b] = GRU elementwise update from the gate sums, biases and h[b].
-hipError_t launch_gru_finalize(const float* gates, int ksplit, const void* b_ih, const void* b_hh,
-                               const float* h, float* h_out, int B, int H, int dtype,
-                               hipStream_t stream);
+constexpr int kGateSlotsHost = 5;  // == kGateSlots (dt_device.h)
+hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream);
+// h [B, H] -> [B, 3, H] exact bf16 parts
+hipError_t launch_split(const float* h, uint16_t* parts, int B, int H, hipStream_t stream);
+// h_out [B, H] from the partial sums
+hipError_t launch_finalize(const float* partial, int ksplit, const void* b_ih, const void* b_hh,
+                           float* h_out, int B, int H, int dtype, hipStream_t stream);
 
 // ---- expansion (expand.hip) -------------------------------------------------
 struct NodeArgs {
@@ -50,17 +56,18 @@ struct NodeArgs {
     float eps;
     // inputs
     const void* C;
-    const void* b_ih;
-    const void* b_hh;
     const float* h0;
     const int32_t* tidx;  // [B, L, M] top-M tables
     const float* tval;
     // workspace
-    float* hstate;       // [B, n+1, H] hidden state per tree slot
-    float* gates;        // GRU partial gate sums (see GruGemmArgs)
+    const void* b_ih;
+    const void* b_hh;
+    float* hstate;       // [B, n+1, H] hidden state per tree slot (binary32)
+    uint16_t* hsplit;    // [B, n+1, 3, H] its exact bf16 parts (bf16 path)
+    const float* partial;  // gate partial sums of the preceding contraction
     int ksplit;
-    int32_t* gru_tok;    // [B] token to feed, -1 = idle row
-    int32_t* gru_par;    // [B] parent slot whose state is advanced
+    int32_t* gru_tok;    // [B] token of the slot to advance next, -1 = idle row
+    int32_t* gru_par;    // [B] its parent slot (whose state is advanced)
     int32_t* child_tok;  // [B, n+1, 64] sorted children per slot
     float* child_lp;     // [B, n+1, 64]
     u64* queue;          // [B, 64] candidate keys, 0 = empty
@@ -74,7 +81,13 @@ struct NodeArgs {
     int32_t* count;
     uint32_t* flags;
 };
-hipError_t launch_node_step(const NodeArgs& a, int step, hipStream_t stream);
+// Word offsets of the node kernel's dynamic LDS arrays.
+struct NodeLds {
+    size_t hs, zs, sc, par, tidx, tval, ctok, clp;
+    size_t bytes;
+};
+NodeLds node_lds_plan(int L, int M, int n, int H);
+hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream);
 
 // Conditional children distribution of one node per row (dt_correct).
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,

@@ -11,16 +11,17 @@
 // deep read"), normalized by a log-softmax over the M-slice.
 //
 // Step s (s = 0 .. n-1) of request b:
-//   1. finish the GRU update of tree slot s from the gate sums of the
-//      preceding contraction (slot 0, the root, takes h0 instead);
-//   2. score slot s's children: z_j = val_j + C[idx_j] . h, z /= T, log-softmax,
+//   1. slot s's hidden state (written by the preceding GRU step; the root
+//      takes h0), the top-M table, the sorted children of slots < s and the
+//      tree so far are loaded into LDS in one round trip;
+//   2. slot s's children: z_j = val_j + C[idx_j] . h, z /= T, log-softmax,
 //      bitonic sort by (log-prob desc, token asc) across one wave;
 //   3. push slot s's best child; pop the best candidate as slot s+1 and push
 //      its next-ranked sibling (lazy sibling push: the queue then holds at
 //      most n entries, one per lane of a wave);
-//   4. stage slot s+1's GRU input for the next contraction;
+//   4. stage slot s+1 for the next GRU step;
 //   5. after the last step, emit the ancestor-only mask.
-// The queue key orders (score desc, depth asc, parent slot asc, rank asc).
+// Queue key: (score desc, depth asc, parent slot asc, rank asc).
 #include "dt_device.h"
 #include "dt_launch.h"
 
@@ -29,6 +30,7 @@ namespace dt {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNodeThreads = 256;
 constexpr int kRowsPerWave = kMaxM / (kNodeThreads / kWave);  // 16
@@ -58,12 +60,13 @@ template <> struct Row<bf16_t> {
 };
 
 // z[j] = val[j] + C[idx[j]] . h for j < M (all four waves; 16 rows each).
-// h is in LDS; z goes to LDS.  Every lane keeps its 16 rows' loads in flight.
+// h is in LDS; z goes to LDS.  Two K chunks of all 16 rows are in flight per
+// lane (H = 1024 bf16 rows are covered in one round trip).
 template <typename T>
-__device__ void correction_logits(const T* __restrict__ C, const int32_t* __restrict__ idx,
-                                  const float* __restrict__ val, int M, int H, const float* hs,
-                                  float* z) {
+__device__ void correction_logits(const T* __restrict__ C, const int32_t* idx, const float* val,
+                                  int M, int H, const float* hs, float* z) {
     constexpr int P = Row<T>::kPerVec;
+    constexpr int kStep = kWave * P;
     const int wave = threadIdx.x / kWave, lane = lane_id();
     int tok[kRowsPerWave];
     float acc[kRowsPerWave];
@@ -73,20 +76,28 @@ __device__ void correction_logits(const T* __restrict__ C, const int32_t* __rest
         tok[jj] = j < M ? idx[j] : -1;
         acc[jj] = 0.f;
     }
-    for (int k0 = 0; k0 < H; k0 += kWave * P) {
-        const int k = k0 + lane * P;
-        const bool kok = k < H;
-        u32x4 v[kRowsPerWave];
+    for (int k0 = 0; k0 < H; k0 += 2 * kStep) {
+        const int ka = k0 + lane * P, kb = ka + kStep;
+        const bool oka = ka < H, okb = kb < H;
+        u32x4 va[kRowsPerWave], vb[kRowsPerWave];
 #pragma unroll
-        for (int jj = 0; jj < kRowsPerWave; ++jj)
-            v[jj] = (kok && tok[jj] >= 0)
-                        ? *reinterpret_cast<const u32x4*>(C + (size_t)tok[jj] * H + k)
-                        : u32x4{0u, 0u, 0u, 0u};
-        float hv[P];
+        for (int jj = 0; jj < kRowsPerWave; ++jj) {
+            const T* row = C + (size_t)(tok[jj] < 0 ? 0 : tok[jj]) * H;
+            const bool on = tok[jj] >= 0;
+            va[jj] = (on && oka) ? *reinterpret_cast<const u32x4*>(row + ka) : u32x4{0u, 0u, 0u, 0u};
+            vb[jj] = (on && okb) ? *reinterpret_cast<const u32x4*>(row + kb) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float ha[P], hb[P];
 #pragma unroll
-        for (int i = 0; i < P; ++i) hv[i] = kok ? hs[k + i] : 0.f;
+        for (int i = 0; i < P; ++i) {
+            ha[i] = oka ? hs[ka + i] : 0.f;
+            hb[i] = okb ? hs[kb + i] : 0.f;
+        }
 #pragma unroll
-        for (int jj = 0; jj < kRowsPerWave; ++jj) acc[jj] += Row<T>::dot(v[jj], hv);
+        for (int jj = 0; jj < kRowsPerWave; ++jj) {
+            acc[jj] += Row<T>::dot(va[jj], ha);
+            acc[jj] += Row<T>::dot(vb[jj], hb);
+        }
     }
 #pragma unroll
     for (int jj = 0; jj < kRowsPerWave; ++jj) {
@@ -115,53 +126,127 @@ __device__ u64 sorted_children(const float* z, const int32_t* idx, int M, float 
 __device__ __forceinline__ float child_lp_of(u64 k) { return f32_unord((uint32_t)(k >> 32)); }
 __device__ __forceinline__ int child_tok_of(u64 k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 
+}  // namespace
+
+// Dynamic LDS layout of the node kernel (floats / ints, 16-byte aligned).
+NodeLds node_lds_plan(int L, int M, int n, int H) {
+    NodeLds p{};
+    size_t off = 0;
+    auto take = [&](size_t words) {
+        size_t at = off;
+        off += (words + 3) / 4 * 4;
+        return at;
+    };
+    p.hs = take(H);
+    p.zs = take(kMaxM);
+    p.sc = take(kMaxN + 1);
+    p.par = take(kMaxN + 1);
+    p.tidx = take((size_t)L * M);
+    p.tval = take((size_t)L * M);
+    p.ctok = take((size_t)n * kMaxM);
+    p.clp = take((size_t)n * kMaxM);
+    p.bytes = off * 4;
+    return p;
+}
+
+namespace {
+
 template <typename T>
-__global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, int step) {
-    __shared__ float hs[kMaxH];
-    __shared__ float zs[kMaxM];
-    __shared__ int spar[kMaxN + 1];
+__global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
+    extern __shared__ float lds[];
+    float* hs = lds + lp.hs;
+    float* zs = lds + lp.zs;
+    float* s_sc = lds + lp.sc;
+    int* s_par = (int*)(lds + lp.par);
+    int32_t* s_tidx = (int32_t*)(lds + lp.tidx);
+    float* s_tval = lds + lp.tval;
+    int32_t* s_ctok = (int32_t*)(lds + lp.ctok);
+    float* s_clp = lds + lp.clp;
 
     const int b = blockIdx.x;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int S = a.n + 1;
     const size_t slot0 = (size_t)b * S;
-    const int cnt = step == 0 ? 0 : a.count[b];
-    // Slot `step` is expanded when it exists (every earlier pop succeeded)
-    // and was staged for expansion (depth < L).
-    const bool expand = step == 0 || (cnt == step && a.gru_tok[b] >= 0);
-    const int depth = step == 0 ? 0 : (expand ? a.depths[slot0 + step] : 0);
+    const int LM = a.L * a.M;
 
-    // ---- 1. hidden state of slot `step`
+    // ---- 1. one round trip: state, table, children of earlier slots, tree
+    const int cnt = step == 0 ? 0 : a.count[b];
+    const bool expand = step == 0 || (cnt == step && a.gru_tok[b] >= 0);
+    const int depth = step == 0 ? 0 : a.depths[slot0 + step];
     if (expand) {
+        // slot `step`'s state: h0 at the root, else the GRU cell applied to the
+        // K-range partial sums (added in K order) of the preceding contraction
         float* hdst = a.hstate + (slot0 + step) * a.H;
-        if (step == 0) {
-            for (int k = threadIdx.x; k < a.H; k += kNodeThreads) {
-                const float v = a.h0 ? a.h0[(size_t)b * a.H + k] : 0.f;
-                hs[k] = v;
-                hdst[k] = v;
+        uint16_t* pdst = a.hsplit ? a.hsplit + (slot0 + step) * 3 * (size_t)a.H : nullptr;
+        for (int k4 = threadIdx.x * 4; k4 < a.H; k4 += kNodeThreads * 4) {
+            float hv[4];
+            if (step == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = a.h0 ? a.h0[(size_t)b * a.H + k4 + e] : 0.f;
+            } else {
+                f32x4 t[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                              f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 8
+                for (int s = 0; s < a.ksplit; ++s) {
+                    const float* p = a.partial + ((size_t)(s * a.B + b) * kGateSlots) * a.H + k4;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) t[g] += *reinterpret_cast<const f32x4*>(p + (size_t)g * a.H);
+                }
+                const f32x4 hp = *reinterpret_cast<const f32x4*>(
+                    a.partial + ((size_t)b * kGateSlots + 4) * a.H + k4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hv[e] = gru_cell(t[0][e], t[1][e], t[2][e], t[3][e], a.b_ih, a.b_hh, a.dtype, a.H,
+                                     k4 + e, hp[e]);
             }
-        } else {
-            const float* hprev = a.hstate + (slot0 + a.gru_par[b]) * a.H;
-            for (int k = threadIdx.x; k < a.H; k += kNodeThreads) {
-                const float v = gru_unit_update(a.gates, a.ksplit, a.B, b, a.H, k, a.b_ih, a.b_hh,
-                                                a.dtype, hprev[k]);
-                hs[k] = v;
-                hdst[k] = v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hs[k4 + e] = hv[e];
+                hdst[k4 + e] = hv[e];
+                if (pdst) {
+                    uint32_t parts[3];
+                    split3_bf16(hv[e], parts);
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) pdst[(size_t)q * a.H + k4 + e] = (uint16_t)parts[q];
+                }
             }
         }
+        const int32_t* ti = a.tidx + (size_t)b * LM;
+        const float* tv = a.tval + (size_t)b * LM;
+        for (int i = threadIdx.x; i < LM; i += kNodeThreads) {
+            s_tidx[i] = ti[i];
+            s_tval[i] = tv[i];
+        }
+    }
+    const int nkid = step * kMaxM;  // children lists of slots 0 .. step-1
+    for (int i = threadIdx.x; i < nkid; i += kNodeThreads) {
+        s_ctok[i] = a.child_tok[slot0 * kMaxM + i];
+        s_clp[i] = a.child_lp[slot0 * kMaxM + i];
+    }
+    for (int i = threadIdx.x; i <= step; i += kNodeThreads) {
+        s_sc[i] = i == 0 ? 0.f : a.scores[slot0 + i];
+        s_par[i] = i == 0 ? -1 : a.parents[slot0 + i];
+    }
+    u64 q = 0ull;
+    int qs = 0;
+    uint32_t flag = 0u;
+    if (step > 0 && wave == 0) {
+        q = a.queue[(size_t)b * kWave + lane];
+        qs = a.qsize[b];
+        flag = a.flags[b];
     }
     __syncthreads();
 
     // ---- 2. children of slot `step` (block position = its depth)
-    const size_t trow = ((size_t)b * a.L + depth) * a.M;
     if (expand)
-        correction_logits<T>((const T*)a.C, a.tidx + trow, a.tval + trow, a.M, a.H, hs, zs);
+        correction_logits<T>((const T*)a.C, s_tidx + depth * a.M, s_tval + depth * a.M, a.M, a.H,
+                             hs, zs);
     __syncthreads();
     if (wave != 0) return;
 
     u64 kids = 0ull;  // lane r: rank-r child of slot `step`
     if (expand) {
-        kids = sorted_children(zs, a.tidx + trow, a.M, a.temp);
+        kids = sorted_children(zs, s_tidx + depth * a.M, a.M, a.temp);
         const size_t crow = (slot0 + step) * kMaxM;
         if (lane < a.M) {
             a.child_tok[crow + lane] = child_tok_of(kids);
@@ -170,12 +255,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, int
     }
 
     // ---- 3. queue: push slot `step`'s best child, pop, push the sibling
-    u64 q;
-    int qs;
     if (step == 0) {
-        q = 0ull;
-        qs = 0;
-        // root slot and empty slots
         for (int i = lane; i < S; i += kWave) {
             if (i == 0) {
                 a.tokens[slot0] = -1;
@@ -189,24 +269,19 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, int
                 a.scores[slot0 + i] = -INFINITY;
             }
         }
-    } else {
-        q = a.queue[(size_t)b * kWave + lane];
-        qs = a.qsize[b];
     }
-    const float score_step = step == 0 ? 0.f : a.scores[slot0 + step];
+    const float score_step = s_sc[step];
     if (expand) {
         const u64 best = shfl_u64(kids, 0);
         const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
         if (lane == qs) q = key;
         ++qs;
     }
-    uint32_t flag = step == 0 ? 0u : a.flags[b];
     int new_cnt = cnt;
     int v_par = -1;
     if (cnt == step && qs > 0) {
         const u64 top = wave_max_u64(q);
-        const u64 hold = __ballot(q == top);
-        const int holder = (int)__builtin_ctzll(hold);
+        const int holder = (int)__builtin_ctzll(__ballot(q == top));
         const u64 last = shfl_u64(q, qs - 1);
         if (lane == holder) q = last;
         if (lane == qs - 1) q = 0ull;
@@ -214,22 +289,18 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, int
 
         const int pd = qk_depth(top), pp = qk_parent(top), pr = qk_rank(top);
         const float psc = qk_score(top);
-        // the popped candidate's token and its next sibling's log-prob
-        int ptok;
-        float sib_lp = 0.f;
         const bool has_sib = pr + 1 < a.M;
+        int ptok;
+        float sib_lp;
         if (pp == step) {  // a child of the slot expanded just now: in registers
             ptok = child_tok_of(shfl_u64(kids, pr));
-            const float l = child_lp_of(shfl_u64(kids, min(pr + 1, kWave - 1)));
-            if (has_sib) sib_lp = l;
+            sib_lp = child_lp_of(shfl_u64(kids, min(pr + 1, kWave - 1)));
         } else {
-            const size_t crow = (slot0 + pp) * kMaxM;
-            ptok = a.child_tok[crow + pr];
-            if (has_sib) sib_lp = a.child_lp[crow + pr + 1];
+            ptok = s_ctok[pp * kMaxM + pr];
+            sib_lp = s_clp[pp * kMaxM + min(pr + 1, kMaxM - 1)];
         }
         if (has_sib) {
-            const float par_score = pp == 0 ? 0.f : (pp == step ? score_step : a.scores[slot0 + pp]);
-            const u64 key = queue_key(par_score + sib_lp, pd, pp, pr + 1);
+            const u64 key = queue_key(s_sc[pp] + sib_lp, pd, pp, pr + 1);
             if (lane == qs) q = key;
             ++qs;
         }
@@ -264,22 +335,15 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, int
 
     // ---- 5. ancestor-only mask after the last step
     if (step == a.n - 1) {
-        for (int i = lane; i < S; i += kWave) {
-            int p;
-            if (i == 0) p = -1;
-            else if (i == step + 1 && new_cnt == step + 1) p = v_par;
-            else if (i <= new_cnt) p = a.parents[slot0 + i];
-            else p = -2;  // unused slot
-            spar[i] = p;
-        }
+        if (lane == 0 && new_cnt == step + 1) s_par[step + 1] = v_par;
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
         for (int i = lane; i < S; i += kWave) {
             uint8_t* row = a.mask + ((size_t)b * S + i) * S;
             u64 bits_lo = 0ull;  // slots 0..63
             bool bit64 = false;  // slot 64 (only when n = 64)
-            if (spar[i] != -2) {
-                for (int j = i; j >= 0; j = j == 0 ? -1 : spar[j]) {
+            if (i <= new_cnt) {
+                for (int j = i; j >= 0; j = j == 0 ? -1 : s_par[j]) {
                     if (j < 64) bits_lo |= 1ull << j;
                     else bit64 = true;
                 }
@@ -298,14 +362,20 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
                                                                float temp) {
     __shared__ float hs[kMaxH];
     __shared__ float zs[kMaxM];
+    __shared__ int32_t si[kMaxM];
+    __shared__ float sv[kMaxM];
     const int b = blockIdx.x;
     for (int k = threadIdx.x; k < H; k += kNodeThreads) hs[k] = h[(size_t)b * H + k];
-    __syncthreads();
     const size_t trow = ((size_t)b * L + pos[b]) * M;
-    correction_logits<T>(C, tidx + trow, tval + trow, M, H, hs, zs);
+    if (threadIdx.x < M) {
+        si[threadIdx.x] = tidx[trow + threadIdx.x];
+        sv[threadIdx.x] = tval[trow + threadIdx.x];
+    }
+    __syncthreads();
+    correction_logits<T>(C, si, sv, M, H, hs, zs);
     __syncthreads();
     if (threadIdx.x >= kWave) return;
-    const u64 kids = sorted_children(zs, tidx + trow, M, temp);
+    const u64 kids = sorted_children(zs, si, M, temp);
     const int lane = lane_id();
     if (lane < M) {
         tok_out[(size_t)b * M + lane] = child_tok_of(kids);
@@ -315,12 +385,12 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
 
 }  // namespace
 
-hipError_t launch_node_step(const NodeArgs& a, int step, hipStream_t stream) {
+hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     if (a.dtype == 1)
-        node_step_kernel<bf16_t><<<a.B, kNodeThreads, 0, stream>>>(a, step);
+        node_step_kernel<bf16_t><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step);
     else
-        node_step_kernel<float><<<a.B, kNodeThreads, 0, stream>>>(a, step);
+        node_step_kernel<float><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step);
     return hipGetLastError();
 }
 

@@ -58,7 +58,9 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *   temperature  0 = unscaled; > 0 divides the corrected logits before the
  *                log-softmax ([captcha] "Methodology -- deep read": runs at
  *                T in {0, 0.5, 1.0})
- *   near_tie_eps decisions closer than this are flagged (e.g. 1e-5)         */
+ *   near_tie_eps decisions closer than this are flagged (e.g. 1e-5)
+ * A request's expansion state lives in one workgroup's LDS: configurations with
+ * 4 H + 8 L M + 512 n bytes (plus ~0.8 KiB) above 64 KiB are DT_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t B, L, V, E, H, M, n;
     float temperature;

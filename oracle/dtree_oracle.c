@@ -56,8 +56,8 @@
  *     is within eps of the popped one is a near tie, unless both scores are
  *     sums of the identical sequence of log-prob terms (exact zeros
  *     dropped), which every floating-point evaluation ties exactly; the
- *     smallest such gap (0 included) is reported and a flag is raised when
- *     it is below eps.  Losslessness only holds up to floating-point
+ *     smallest gap to a candidate not tied that way (0 included) is reported,
+ *     and a flag is raised when it is below eps.  Losslessness only holds up to floating-point
  *     tie-breaking ([captcha] "Threat model"; [gist] "Résultats
  *     expérimentaux -- Absence de perte"): mathematically equal scores
  *     reached through different additions are such tie-breaks;
@@ -314,7 +314,8 @@ static qent_t q_pop(queue_t *q)
  * Outputs (n+1 tree slots; slot 0 is the root):
  *   tokens/parents/depths [n+1] int32, scores [n+1] double, mask [(n+1)^2],
  *   count (non-root nodes built), flags (bit 0: a near tie below eps),
- *   min_gap (smallest near-tie gap seen, +inf if none below eps),
+ *   min_gap (smallest gap between a popped candidate and one left in the
+ *   queue, structural exact ties excluded; +inf if the queue was always empty),
  *   topm_idx/topm_val [L,M] (optional, may be NULL).
  */
 int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int dtype, double eps,
@@ -388,7 +389,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
         /* near-tie bookkeeping: gaps to the candidates left in the queue */
         for (int i = 0; i < q.size; ++i) {
             double gap = c.score - q.e[i].score;
-            if (gap >= eps || gap >= *min_gap) continue;
+            if (gap >= *min_gap) continue;
             if (gap == 0.0 && same_terms(plp, plen, clp, L, M, &c, &q.e[i], wa, wb)) continue;
             *min_gap = gap;
         }

@@ -45,17 +45,27 @@ def builder(cfg, eps=1e-5):
                          cfg["T"], cfg["dtype"], eps, device=DEV)
 
 
-def build_and_compare(cfg, inp, requests=None, threads=8):
+# The "strong" variant (h0 ~ N(0, 1), C scaled by 10) makes corrected logits
+# of magnitude ~10: a binary32 dot product of H such terms carries an error of
+# about sqrt(H) * ulp(10) / 2 ~ 3e-5 per child log-prob (H = 1024), and a
+# node's score adds up to L of them.  Decisions closer than 2e-4 are then not
+# reproducible between binary32 and the double-precision oracle, and scores
+# agree to ~5e-4.  The named workloads (default variant) use 1e-5 / 1e-4.
+STRONG = dict(eps=2e-4, tol=5e-4)
+
+
+def build_and_compare(cfg, inp, requests=None, threads=8, eps=1e-5, tol=SCORE_TOL):
     B = cfg["B"]
     reqs = list(range(B)) if requests is None else list(requests)
     say(f"  build B={B} V={cfg['V']} L={cfg['L']} E={cfg['E']} H={cfg['H']} M={cfg['M']} "
-        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']}")
-    bld = builder(cfg)
+        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']} eps={eps}")
+    bld = builder(cfg, eps)
     got = run_build(bld, S.to_torch(inp, DEV))
     for b in range(B):
         check_valid_tree(got, b, cfg["n"], cfg["L"])
-    refs = oracle.build_batch(inp, cfg["M"], cfg["n"], cfg["T"], requests=reqs, threads=threads)
-    kinds = [compare_request(got, b, r, inp, b, cfg) for b, r in zip(reqs, refs)]
+    refs = oracle.build_batch(inp, cfg["M"], cfg["n"], cfg["T"], eps=eps, requests=reqs,
+                              threads=threads)
+    kinds = [compare_request(got, b, r, inp, b, cfg, eps, tol) for b, r in zip(reqs, refs)]
     bld.close()
     say(f"  compared {len(reqs)} requests: {kinds.count('exact')} exact, "
         f"{kinds.count('flagged')} near-tie")
@@ -173,7 +183,7 @@ def test_correct_matches_oracle(dtype, T):
 def test_build_tiny(variant, over):
     cfg = S.with_config("tiny", **dict(over))
     inp = S.make_inputs(cfg, seed=3, variant=variant)
-    got, refs, kinds = build_and_compare(cfg, inp)
+    got, refs, kinds = build_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
     if cfg["M"] == 1:
         assert got["count"][0] == min(cfg["n"], cfg["L"])
 
@@ -184,7 +194,8 @@ def test_build_bf16_ragged(variant):
     # of 8 (scalar top-M path), n = 64 (queue of one full wave)
     cfg = dict(B=70, V=5003, L=16, E=256, H=128, M=64, n=64, dtype="bf16", alpha=1.5, T=0.0)
     inp = S.make_inputs(cfg, seed=5, variant=variant)
-    build_and_compare(cfg, inp, requests=range(0, 70, 3))
+    build_and_compare(cfg, inp, requests=range(0, 70, 3),
+                      **(STRONG if variant == "strong" else {}))
 
 
 def test_build_qwen3_4b_single():
@@ -204,7 +215,7 @@ def test_build_qwen3_4b_batched_and_rerun_identical():
 
 def test_build_qwen3_4b_batched_strong_correction():
     cfg, inp = inputs("qwen3_4b_batched", "strong")
-    build_and_compare(cfg, inp, requests=[2, 31, 60])
+    build_and_compare(cfg, inp, requests=[2, 31, 60], **STRONG)
 
 
 def test_build_qwen3_8b():
