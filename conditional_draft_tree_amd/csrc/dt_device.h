@@ -67,73 +67,135 @@ __device__ __forceinline__ u64 child_key(float lp, int tok) {
 }
 
 // ------------------------------------------------------------ wave ops ----
+// Cross-lane exchanges run on the VALU: DPP quad permutes and row shifts for
+// lane distances 1..8, the gfx950 permlane swaps for 16 and 32 (no LDS
+// traffic, no waits).  Lane semantics (checked on the device): row_shl:n
+// reads lane i+n, row_shr:n reads lane i-n within a 16-lane row;
+// permlane16_swap(v, v) = {row-even copies, row-odd copies} and
+// permlane32_swap(v, v) = {lower-half copies, upper-half copies}.
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
-__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int m) {
-    return (u64)__shfl_xor((unsigned long long)v, m, kWave);
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    const int lane = lane_id();
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (J == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+        return (lane & 4) ? dn : up;
+    } else if constexpr (J == 8) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x108, 0xF, 0xF, false);
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+        return (lane & 8) ? dn : up;
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
 }
-__device__ __forceinline__ u64 shfl_u64(u64 v, int src) {
-    return (u64)__shfl((unsigned long long)v, src, kWave);
+template <int J> __device__ __forceinline__ float xor_lane_f(float v) {
+    return __uint_as_float(xor_lane<J>(__float_as_uint(v)));
+}
+template <int J> __device__ __forceinline__ u64 xor_lane_u64(u64 v) {
+    return ((u64)xor_lane<J>((uint32_t)(v >> 32)) << 32) | (u64)xor_lane<J>((uint32_t)v);
+}
+__device__ __forceinline__ u64 xor_lane_u64(u64 v, int j) {
+    switch (j) {
+        case 1: return xor_lane_u64<1>(v);
+        case 2: return xor_lane_u64<2>(v);
+        case 4: return xor_lane_u64<4>(v);
+        case 8: return xor_lane_u64<8>(v);
+        case 16: return xor_lane_u64<16>(v);
+        default: return xor_lane_u64<32>(v);
+    }
 }
 
-// Sum over the 64 lanes; the butterfly order is fixed, so the result is
-// reproducible and identical in every lane.
+// Value of lane `src` (wave-uniform index) in every lane.
+__device__ __forceinline__ u64 bcast_u64(u64 v, int src) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    return ((u64)hi << 32) | lo;
+}
+
+// Butterfly sum over the 64 lanes: the order is fixed and, addition being
+// commutative, every lane ends with the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    v += xor_lane_f<32>(v);
+    v += xor_lane_f<16>(v);
+    v += xor_lane_f<8>(v);
+    v += xor_lane_f<4>(v);
+    v += xor_lane_f<2>(v);
+    v += xor_lane_f<1>(v);
     return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    v = fmaxf(v, xor_lane_f<32>(v));
+    v = fmaxf(v, xor_lane_f<16>(v));
+    v = fmaxf(v, xor_lane_f<8>(v));
+    v = fmaxf(v, xor_lane_f<4>(v));
+    v = fmaxf(v, xor_lane_f<2>(v));
+    v = fmaxf(v, xor_lane_f<1>(v));
     return v;
 }
+__device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
+__device__ __forceinline__ u64 umin64(u64 a, u64 b) { return a > b ? b : a; }
 __device__ __forceinline__ u64 wave_max_u64(u64 v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        u64 o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
+    v = umax64(v, xor_lane_u64<32>(v));
+    v = umax64(v, xor_lane_u64<16>(v));
+    v = umax64(v, xor_lane_u64<8>(v));
+    v = umax64(v, xor_lane_u64<4>(v));
+    v = umax64(v, xor_lane_u64<2>(v));
+    v = umax64(v, xor_lane_u64<1>(v));
     return v;
 }
 
-// Bitonic sort of one key per lane into descending lane order.
-__device__ __forceinline__ u64 wave_sort_desc(u64 key) {
+// One compare-exchange stage of a bitonic network at lane distance J:
+// the lower lane of each pair keeps the larger key when `desc`.
+template <int J>
+__device__ __forceinline__ u64 bitonic_stage(u64 key, bool desc) {
+    const u64 o = xor_lane_u64<J>(key);
+    const bool lower = (lane_id() & J) == 0;
+    return (lower == desc) ? umax64(key, o) : umin64(key, o);
+}
+
+// Bitonic sort of one key per lane into descending lane order (ascending
+// when `ascending`).
+__device__ __forceinline__ u64 wave_sort(u64 key, bool ascending) {
     const int lane = lane_id();
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            u64 o = shfl_xor_u64(key, j);
-            bool desc = (lane & k) == 0;
-            bool lower = (lane & j) == 0;
-            u64 mx = o > key ? o : key, mn = o > key ? key : o;
-            key = (lower == desc) ? mx : mn;
-        }
-    }
+#define DT_STAGE(K, J) key = bitonic_stage<J>(key, (((lane & K) == 0) != ascending))
+    DT_STAGE(2, 1);
+    DT_STAGE(4, 2); DT_STAGE(4, 1);
+    DT_STAGE(8, 4); DT_STAGE(8, 2); DT_STAGE(8, 1);
+    DT_STAGE(16, 8); DT_STAGE(16, 4); DT_STAGE(16, 2); DT_STAGE(16, 1);
+    DT_STAGE(32, 16); DT_STAGE(32, 8); DT_STAGE(32, 4); DT_STAGE(32, 2); DT_STAGE(32, 1);
+    DT_STAGE(64, 32); DT_STAGE(64, 16); DT_STAGE(64, 8); DT_STAGE(64, 4); DT_STAGE(64, 2); DT_STAGE(64, 1);
+#undef DT_STAGE
     return key;
 }
+__device__ __forceinline__ u64 wave_sort_desc(u64 key) { return wave_sort(key, false); }
 
 // Finish a bitonic sequence into descending lane order.
 __device__ __forceinline__ u64 wave_bitonic_merge_desc(u64 key) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int j = kWave >> 1; j > 0; j >>= 1) {
-        u64 o = shfl_xor_u64(key, j);
-        bool lower = (lane & j) == 0;
-        u64 mx = o > key ? o : key, mn = o > key ? key : o;
-        key = lower ? mx : mn;
-    }
+    key = bitonic_stage<32>(key, true);
+    key = bitonic_stage<16>(key, true);
+    key = bitonic_stage<8>(key, true);
+    key = bitonic_stage<4>(key, true);
+    key = bitonic_stage<2>(key, true);
+    key = bitonic_stage<1>(key, true);
     return key;
 }
 
-// `list` and `other` are each sorted descending across the wave; returns the
-// 64 largest keys of both, sorted descending.
-__device__ __forceinline__ u64 wave_merge_top64(u64 list, u64 other_sorted) {
-    u64 rev = shfl_u64(other_sorted, kWave - 1 - lane_id());
-    u64 m = rev > list ? rev : list;  // bitonic, holds the top 64
-    return wave_bitonic_merge_desc(m);
+// `list` sorted descending and `other_asc` sorted ascending across the wave:
+// the 64 largest keys of both, sorted descending.
+__device__ __forceinline__ u64 wave_merge_top64(u64 list, u64 other_asc) {
+    return wave_bitonic_merge_desc(umax64(list, other_asc));  // bitonic, holds the top 64
 }
 
 }  // namespace dt
@@ -149,21 +211,44 @@ __device__ __forceinline__ float load_param(const void* p, int dtype, size_t i) 
 // GRU elementwise update of hidden unit k from its gate sums (bias not yet
 // added): reset r, update u, candidate c; h' = (1 - u) c + u h.
 __device__ __forceinline__ float gru_cell(float sr, float sz, float snx, float snh, const void* b_ih,
-                                          const void* b_hh, int dtype, int H, int k, float hprev) {
-    sr += load_param(b_ih, dtype, k) + load_param(b_hh, dtype, k);
-    sz += load_param(b_ih, dtype, H + k) + load_param(b_hh, dtype, H + k);
-    snx += load_param(b_ih, dtype, 2 * H + k);
-    snh += load_param(b_hh, dtype, 2 * H + k);
-    const float r = 1.f / (1.f + expf(-sr));
-    const float u = 1.f / (1.f + expf(-sz));
-    const float c = tanhf(snx + r * snh);
+                                          const void* b_hh, int dtype, int H, int k, float hprev);
+
+// Four consecutive parameter elements [i, i+4) (zeros when p is NULL).
+typedef float dt_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ dt_f32x4 load_param4(const void* p, int dtype, size_t i) {
+    if (!p) return dt_f32x4{0.f, 0.f, 0.f, 0.f};
+    if (dtype == 1) {
+        const uint2 w = *reinterpret_cast<const uint2*>((const uint16_t*)p + i);
+        return dt_f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+    }
+    return *reinterpret_cast<const dt_f32x4*>((const float*)p + i);
+}
+
+// GRU cell with the biases already loaded (bi*: input biases, bh*: hidden).
+__device__ __forceinline__ float gru_cell_b(float sr, float sz, float snx, float snh, float bir,
+                                            float biz, float bin, float bhr, float bhz, float bhn,
+                                            float hprev) {
+    const float r = 1.f / (1.f + expf(-(sr + (bir + bhr))));
+    const float u = 1.f / (1.f + expf(-(sz + (biz + bhz))));
+    const float c = tanhf((snx + bin) + r * (snh + bhn));
     return (1.f - u) * c + u * hprev;
+}
+
+// GRU elementwise update of hidden unit k from its gate sums (biases not
+// yet added): reset r, update u, candidate c; h' = (1 - u) c + u h.
+__device__ __forceinline__ float gru_cell(float sr, float sz, float snx, float snh, const void* b_ih,
+                                          const void* b_hh, int dtype, int H, int k, float hprev) {
+    return gru_cell_b(sr, sz, snx, snh, load_param(b_ih, dtype, k), load_param(b_ih, dtype, H + k),
+                      load_param(b_ih, dtype, 2 * H + k), load_param(b_hh, dtype, k),
+                      load_param(b_hh, dtype, H + k), load_param(b_hh, dtype, 2 * H + k), hprev);
 }
 
 // Partial-sum buffer of the gate contraction: [ksplit][B][kGateSlots][H],
 // slots 0 reset, 1 update, 2 candidate (x part), 3 candidate (h part), 4 the
 // previous state (K range 0 only).
 constexpr int kGateSlots = 5;
+constexpr int kMaxKsplit = 6;  // K ranges of the gate contraction
 
 // New state of (row b, unit k): the K-range partials added in K order.
 __device__ __forceinline__ float gru_from_partials(const float* partial, int ksplit, int B, int b,

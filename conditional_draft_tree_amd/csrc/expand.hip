@@ -34,6 +34,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNodeThreads = 256;
 constexpr int kRowsPerWave = kMaxM / (kNodeThreads / kWave);  // 16
+// table entries (L*M) and child-list entries (step*64) staged per thread
+constexpr int kStage = 16;  // 16 * 256 = 4096 >= 64 * 64
+
+// Four consecutive elements as binary32.
+template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+template <> __device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+}
 
 template <typename T> struct Row;
 template <> struct Row<float> {
@@ -63,7 +76,7 @@ template <> struct Row<bf16_t> {
 // h is in LDS; z goes to LDS.  Two K chunks of all 16 rows are in flight per
 // lane (H = 1024 bf16 rows are covered in one round trip).
 template <typename T>
-__device__ void correction_logits(const T* __restrict__ C, const int32_t* idx, const float* val,
+__device__ __forceinline__ void correction_logits(const T* __restrict__ C, const int32_t* idx, const float* val,
                                   int M, int H, const float* hs, float* z) {
     constexpr int P = Row<T>::kPerVec;
     constexpr int kStep = kWave * P;
@@ -110,7 +123,7 @@ __device__ void correction_logits(const T* __restrict__ C, const int32_t* idx, c
 // Wave 0: temperature, log-softmax over the M-slice, children sorted by
 // (log-prob desc, token asc).  Lane r returns the rank-r child (key 0 when
 // r >= M).
-__device__ u64 sorted_children(const float* z, const int32_t* idx, int M, float temp) {
+__device__ __forceinline__ u64 sorted_children(const float* z, const int32_t* idx, int M, float temp) {
     const int lane = lane_id();
     const bool on = lane < M;
     float zz = on ? z[lane] : -INFINITY;
@@ -169,36 +182,89 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     const size_t slot0 = (size_t)b * S;
     const int LM = a.L * a.M;
 
-    // ---- 1. one round trip: state, table, children of earlier slots, tree
+    // ---- 1. one round trip: every load below is independent of the others;
+    // all are issued before the first use.
     const int cnt = step == 0 ? 0 : a.count[b];
-    const bool expand = step == 0 || (cnt == step && a.gru_tok[b] >= 0);
+    const int gtok = step == 0 ? 0 : a.gru_tok[b];
     const int depth = step == 0 ? 0 : a.depths[slot0 + step];
-    if (expand) {
-        // slot `step`'s state: h0 at the root, else the GRU cell applied to the
-        // K-range partial sums (added in K order) of the preceding contraction
-        float* hdst = a.hstate + (slot0 + step) * a.H;
-        uint16_t* pdst = a.hsplit ? a.hsplit + (slot0 + step) * 3 * (size_t)a.H : nullptr;
-        for (int k4 = threadIdx.x * 4; k4 < a.H; k4 += kNodeThreads * 4) {
-            float hv[4];
-            if (step == 0) {
+    u64 q = 0ull;
+    int qs = 0;
+    uint32_t flag = 0u;
+    if (step > 0 && wave == 0) {
+        q = a.queue[(size_t)b * kWave + lane];
+        qs = a.qsize[b];
+        flag = a.flags[b];
+    }
+    // top-M table of this request, children of slots 0 .. step-1, tree so far
+    int32_t r_ti[kStage];
+    float r_tv[kStage];
+    int32_t r_ct[kStage];
+    float r_cl[kStage];
+    const int32_t* ti = a.tidx + (size_t)b * LM;
+    const float* tv = a.tval + (size_t)b * LM;
+    const int nkid = step * kMaxM;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = a.h0 ? a.h0[(size_t)b * a.H + k4 + e] : 0.f;
-            } else {
-                f32x4 t[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
-                              f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-                for (int s = 0; s < a.ksplit; ++s) {
-                    const float* p = a.partial + ((size_t)(s * a.B + b) * kGateSlots) * a.H + k4;
+    for (int u = 0; u < kStage; ++u) {
+        const int i = threadIdx.x + u * kNodeThreads;
+        r_ti[u] = i < LM ? ti[i] : 0;
+        r_tv[u] = i < LM ? tv[i] : 0.f;
+        r_ct[u] = i < nkid ? a.child_tok[slot0 * kMaxM + i] : 0;
+        r_cl[u] = i < nkid ? a.child_lp[slot0 * kMaxM + i] : 0.f;
+    }
+    float r_sc = 0.f;
+    int r_par = -1;
+    if ((int)threadIdx.x <= step && threadIdx.x > 0) {
+        r_sc = a.scores[slot0 + threadIdx.x];
+        r_par = a.parents[slot0 + threadIdx.x];
+    }
+    // slot `step`'s state: h0 at the root, else the GRU cell applied to the
+    // K-range partial sums (added in K order) of the preceding contraction.
+    // Partials and biases are read whether or not the slot expands (they are
+    // always in bounds), so the expansion test does not delay them.
+    const bool expand = step == 0 || (cnt == step && gtok >= 0);
+    float* hdst = a.hstate + (slot0 + step) * a.H;
+    uint16_t* pdst = a.hsplit ? a.hsplit + (slot0 + step) * 3 * (size_t)a.H : nullptr;
+    for (int k4 = threadIdx.x * 4; k4 < a.H; k4 += kNodeThreads * 4) {
+        float hv[4];
+        if (step == 0) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) t[g] += *reinterpret_cast<const f32x4*>(p + (size_t)g * a.H);
+            for (int e = 0; e < 4; ++e) hv[e] = a.h0 ? a.h0[(size_t)b * a.H + k4 + e] : 0.f;
+        } else {
+            // branch-free: indices are clamped to valid slots, unused ones zeroed
+            f32x4 t[kMaxKsplit][4];
+#pragma unroll
+            for (int s = 0; s < kMaxKsplit; ++s) {
+                const int sc = min(s, a.ksplit - 1);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(
+                        a.partial + ((size_t)(sc * a.B + b) * kGateSlots + g) * a.H + k4);
+                    t[s][g] = s < a.ksplit ? v : f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                const f32x4 hp = *reinterpret_cast<const f32x4*>(
-                    a.partial + ((size_t)b * kGateSlots + 4) * a.H + k4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hv[e] = gru_cell(t[0][e], t[1][e], t[2][e], t[3][e], a.b_ih, a.b_hh, a.dtype, a.H,
-                                     k4 + e, hp[e]);
             }
+            const f32x4 hp = *reinterpret_cast<const f32x4*>(
+                a.partial + ((size_t)b * kGateSlots + 4) * a.H + k4);
+            f32x4 bias[6];
+#pragma unroll
+            for (int g = 0; g < 6; ++g) {
+                const void* bp = g < 3 ? a.b_ih : a.b_hh;
+                const T* src = bp ? (const T*)bp : (const T*)a.partial;  // any valid address
+                const f32x4 v = load4<T>(src + (size_t)(g % 3) * a.H + k4);
+                bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            f32x4 sum[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                sum[g] = t[0][g];
+#pragma unroll
+                for (int s = 1; s < kMaxKsplit; ++s) sum[g] += t[s][g];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                hv[e] = gru_cell_b(sum[0][e], sum[1][e], sum[2][e], sum[3][e], bias[0][e], bias[1][e],
+                                   bias[2][e], bias[3][e], bias[4][e], bias[5][e], hp[e]);
+        }
+        if (expand) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 hs[k4 + e] = hv[e];
@@ -207,33 +273,26 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                     uint32_t parts[3];
                     split3_bf16(hv[e], parts);
 #pragma unroll
-                    for (int q = 0; q < 3; ++q) pdst[(size_t)q * a.H + k4 + e] = (uint16_t)parts[q];
+                    for (int qq = 0; qq < 3; ++qq) pdst[(size_t)qq * a.H + k4 + e] = (uint16_t)parts[qq];
                 }
             }
         }
-        const int32_t* ti = a.tidx + (size_t)b * LM;
-        const float* tv = a.tval + (size_t)b * LM;
-        for (int i = threadIdx.x; i < LM; i += kNodeThreads) {
-            s_tidx[i] = ti[i];
-            s_tval[i] = tv[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+        const int i = threadIdx.x + u * kNodeThreads;
+        if (i < LM) {
+            s_tidx[i] = r_ti[u];
+            s_tval[i] = r_tv[u];
+        }
+        if (i < nkid) {
+            s_ctok[i] = r_ct[u];
+            s_clp[i] = r_cl[u];
         }
     }
-    const int nkid = step * kMaxM;  // children lists of slots 0 .. step-1
-    for (int i = threadIdx.x; i < nkid; i += kNodeThreads) {
-        s_ctok[i] = a.child_tok[slot0 * kMaxM + i];
-        s_clp[i] = a.child_lp[slot0 * kMaxM + i];
-    }
-    for (int i = threadIdx.x; i <= step; i += kNodeThreads) {
-        s_sc[i] = i == 0 ? 0.f : a.scores[slot0 + i];
-        s_par[i] = i == 0 ? -1 : a.parents[slot0 + i];
-    }
-    u64 q = 0ull;
-    int qs = 0;
-    uint32_t flag = 0u;
-    if (step > 0 && wave == 0) {
-        q = a.queue[(size_t)b * kWave + lane];
-        qs = a.qsize[b];
-        flag = a.flags[b];
+    if ((int)threadIdx.x <= step) {
+        s_sc[threadIdx.x] = threadIdx.x == 0 ? 0.f : r_sc;
+        s_par[threadIdx.x] = threadIdx.x == 0 ? -1 : r_par;
     }
     __syncthreads();
 
@@ -272,7 +331,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     const float score_step = s_sc[step];
     if (expand) {
-        const u64 best = shfl_u64(kids, 0);
+        const u64 best = bcast_u64(kids, 0);
         const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
         if (lane == qs) q = key;
         ++qs;
@@ -282,7 +341,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     if (cnt == step && qs > 0) {
         const u64 top = wave_max_u64(q);
         const int holder = (int)__builtin_ctzll(__ballot(q == top));
-        const u64 last = shfl_u64(q, qs - 1);
+        const u64 last = bcast_u64(q, qs - 1);
         if (lane == holder) q = last;
         if (lane == qs - 1) q = 0ull;
         --qs;
@@ -293,8 +352,8 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         int ptok;
         float sib_lp;
         if (pp == step) {  // a child of the slot expanded just now: in registers
-            ptok = child_tok_of(shfl_u64(kids, pr));
-            sib_lp = child_lp_of(shfl_u64(kids, min(pr + 1, kWave - 1)));
+            ptok = child_tok_of(bcast_u64(kids, pr));
+            sib_lp = child_lp_of(bcast_u64(kids, min(pr + 1, kWave - 1)));
         } else {
             ptok = s_ctok[pp * kMaxM + pr];
             sib_lp = s_clp[pp * kMaxM + min(pr + 1, kMaxM - 1)];

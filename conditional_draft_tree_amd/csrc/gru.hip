@@ -10,9 +10,9 @@
 // reset gate), hence four gate sums per output.
 //
 // bf16 path (v_mfma_f32_16x16x32_bf16, binary32 accumulation).  A workgroup
-// owns 16 hidden units x 64 rows x one of `ksplit` K ranges; its four waves
-// take a quarter of that range each, over all 64 rows, so every weight element
-// is loaded by exactly one wave.  The waves' sums meet in LDS in wave order and
+// owns 16 hidden units x 64 rows x one of `ksplit` K ranges; its eight waves
+// take disjoint chunk ranges over all 64 rows, so every weight element is
+// loaded by exactly one wave.  The waves' sums meet in LDS in wave order and
 // the workgroup writes its K-range partial sums; the consumer (the node step,
 // or gru_finalize) adds the `ksplit` partials in K order and applies the GRU
 // cell.  The binary32 state h is fed as the exact sum of three bf16 parts
@@ -30,7 +30,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kRowBlocks = 4;  // 4 x 16 rows per workgroup
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
@@ -41,13 +40,53 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kThreads) void gru_gates_bf16_kernel(GruGatesArgs a) {
-    __shared__ float red[kThreads / kWave - 1][kRowBlocks * 4 * 4][kWave];  // 48 KB
+// Work split.  K is cut into 32-wide chunks: nE chunks of the x part then
+// nH of the h part.  Each tile of 16 hidden units is covered by 8 * ksplit
+// waves (ksplit workgroups of 8 waves); the first WE waves take the x chunks,
+// the others the h chunks (three bf16 parts each, so three times the MFMAs),
+// WE chosen to balance the MFMA work.  A wave issues every load of its chunks
+// (weights and activations) before its first MFMA: one memory round trip.
+struct WaveSplit {
+    int WE;  // waves on the x part (the rest take the h part)
+};
+__host__ __device__ __forceinline__ WaveSplit wave_split(int nE, int nH, int W) {
+    int we = (int)(((long long)W * nE + (nE + 3 * nH) / 2) / max(1, nE + 3 * nH));
+    if (nE > 0) we = max(we, 1);
+    if (nH > 0) we = min(we, W - 1);
+    return WaveSplit{we};
+}
+// [begin, end) of the chunks of wave w (0 <= w < W)
+__host__ __device__ __forceinline__ void wave_chunks(int nE, int nH, int W, int w, int& cb, int& ce) {
+    const int we = wave_split(nE, nH, W).WE;
+    if (w < we) {
+        cb = (int)((long long)w * nE / we);
+        ce = (int)((long long)(w + 1) * nE / we);
+    } else {
+        const int wh = W - we, k = w - we;
+        cb = nE + (int)((long long)k * nH / wh);
+        ce = nE + (int)((long long)(k + 1) * nH / wh);
+    }
+}
+
+constexpr int kWaves8 = 8;
+constexpr int kMaxXChunks = 6;  // x chunks per wave and batch
+constexpr int kMaxHChunks = 2;  // h chunks per wave and batch
+
+__global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesArgs a) {
+    __shared__ float red[kWaves8][16][kWave];  // one row block of all waves: 32 KB
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const int ut = blockIdx.x, rg = blockIdx.y, ks = blockIdx.z;
     const int unit = ut * 16 + (lane & 15);
     const int kq = (lane >> 4) * 8;  // MFMA operand layout: lane l supplies row/column
                                      // l % 16 with K values 8 * (l / 16) .. + 8
+    const int nE = a.E / 32, nH = a.H / 32;
+    int cbeg, cend;
+    wave_chunks(nE, nH, kWaves8 * a.ksplit, ks * kWaves8 + wave, cbeg, cend);
+
+    const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
+    const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
+    const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     const size_t H3 = (size_t)3 * a.H;
     const bf16_t* xrow[kRowBlocks];
     const bf16_t* hrow[kRowBlocks];
@@ -55,15 +94,13 @@ __global__ __launch_bounds__(kThreads) void gru_gates_bf16_kernel(GruGatesArgs a
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r = rg * 64 + rb * 16 + (lane & 15);
-        int xr = -1;
-        if (r < a.B) xr = a.xtok ? a.xtok[r] : r;
+        const bool in = r < a.B;
+        const int xr = in ? (a.xtok ? a.xtok[r] : r) : -1;
+        const int hs = in && a.hsel ? a.hsel[r] : 0;
         xok[rb] = xr >= 0;  // rows past B and idle rows contribute zeros
         xrow[rb] = (const bf16_t*)a.x + (size_t)(xok[rb] ? xr : 0) * a.E;
-        hrow[rb] = a.hsplit + (xok[rb] ? state_index(a, r) * H3 : 0);
+        hrow[rb] = a.hsplit + (xok[rb] ? ((size_t)r * a.hrows + hs) * H3 : 0);
     }
-    const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
-    const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
-    const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;
 
     f32x4 acc[kRowBlocks][4];
 #pragma unroll
@@ -71,83 +108,101 @@ __global__ __launch_bounds__(kThreads) void gru_gates_bf16_kernel(GruGatesArgs a
 #pragma unroll
         for (int g = 0; g < 4; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nE = a.E / 32, nK = nE + a.H / 32;
-    const int c0 = ks * nK / a.ksplit, c1 = (ks + 1) * nK / a.ksplit;
-    const int w0 = c0 + wave * (c1 - c0) / 4, w1 = c0 + (wave + 1) * (c1 - c0) / 4;
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-
-#pragma unroll 2
-    for (int c = w0; c < min(w1, nE); ++c) {
-        const int k = c * 32 + kq;
-        const bf16x8 br = load_bf16x8(wi + k);
-        const bf16x8 bz = load_bf16x8(wi + gi + k);
-        const bf16x8 bn = load_bf16x8(wi + 2 * gi + k);
-        bf16x8 av[kRowBlocks];
+    if (cbeg < nE) {
+        // x part: batches of up to kMaxXChunks chunks, all loads of a batch at once
+        for (int cb = cbeg; cb < cend; cb += kMaxXChunks) {
+            const int n = min(kMaxXChunks, cend - cb);
+            bf16x8 w[kMaxXChunks][3], x[kMaxXChunks][kRowBlocks];
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) av[rb] = xok[rb] ? load_bf16x8(xrow[rb] + k) : zero;
+            for (int i = 0; i < kMaxXChunks; ++i) {
+                const int k = (cb + min(i, n - 1)) * 32 + kq;  // clamped: always in bounds
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            acc[rb][0] = mfma(av[rb], br, acc[rb][0]);
-            acc[rb][1] = mfma(av[rb], bz, acc[rb][1]);
-            acc[rb][2] = mfma(av[rb], bn, acc[rb][2]);
-        }
-    }
-#pragma unroll 2
-    for (int c = max(w0, nE); c < w1; ++c) {
-        const int k = (c - nE) * 32 + kq;
-        const bf16x8 br = load_bf16x8(wh + k);
-        const bf16x8 bz = load_bf16x8(wh + gh + k);
-        const bf16x8 bn = load_bf16x8(wh + 2 * gh + k);
-        bf16x8 p[kRowBlocks][3];
+                for (int g = 0; g < 3; ++g) w[i][g] = load_bf16x8(wi + g * gi + k);
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
-#pragma unroll
-            for (int s = 0; s < 3; ++s) p[rb][s] = xok[rb] ? load_bf16x8(hrow[rb] + s * a.H + k) : zero;
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
-#pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                acc[rb][0] = mfma(p[rb][s], br, acc[rb][0]);
-                acc[rb][1] = mfma(p[rb][s], bz, acc[rb][1]);
-                acc[rb][3] = mfma(p[rb][s], bn, acc[rb][3]);
+                for (int rb = 0; rb < kRowBlocks; ++rb) x[i][rb] = xok[rb] ? load_bf16x8(xrow[rb] + k) : zero;
             }
-    }
-
-    // the four waves' sums meet in wave 0, added in wave order
-    if (wave > 0) {
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
+            for (int i = 0; i < kMaxXChunks; ++i) {
+                if (i < n) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) red[wave - 1][(rb * 4 + g) * 4 + e][lane] = acc[rb][g][e];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // lane holds row rg*64 + rb*16 + (lane/16)*4 + e of hidden unit `unit`
-            const int row = rg * 64 + rb * 16 + (lane >> 4) * 4 + e;
-            if (row >= a.B) continue;
-            float* out = a.partial + ((size_t)(ks * a.B + row) * kGateSlots) * a.H + unit;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int i = (rb * 4 + g) * 4 + e;
-                out[(size_t)g * a.H] =
-                    ((acc[rb][g][e] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
-            }
-            if (ks == 0) {  // previous state of (row, unit), rebuilt exactly from its parts
-                const int xr = a.xtok ? a.xtok[row] : row;
-                float hp = 0.f;
-                if (xr >= 0) {
-                    const bf16_t* hs = a.hsplit + state_index(a, row) * H3 + unit;
-                    hp = (bf16_to_f32(hs[0]) + bf16_to_f32(hs[a.H])) + bf16_to_f32(hs[2 * a.H]);
+                    for (int rb = 0; rb < kRowBlocks; ++rb) {
+                        acc[rb][0] = mfma(x[i][rb], w[i][0], acc[rb][0]);
+                        acc[rb][1] = mfma(x[i][rb], w[i][1], acc[rb][1]);
+                        acc[rb][2] = mfma(x[i][rb], w[i][2], acc[rb][2]);
+                    }
                 }
-                out[(size_t)4 * a.H] = hp;
             }
         }
+    } else {
+        // h part (three exact bf16 parts per state element)
+        for (int cb = cbeg; cb < cend; cb += kMaxHChunks) {
+            const int n = min(kMaxHChunks, cend - cb);
+            bf16x8 w[kMaxHChunks][3], hp[kMaxHChunks][kRowBlocks][3];
+#pragma unroll
+            for (int i = 0; i < kMaxHChunks; ++i) {
+                const int k = (cb + min(i, n - 1) - nE) * 32 + kq;
+#pragma unroll
+                for (int g = 0; g < 3; ++g) w[i][g] = load_bf16x8(wh + g * gh + k);
+#pragma unroll
+                for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        hp[i][rb][q] = xok[rb] ? load_bf16x8(hrow[rb] + q * a.H + k) : zero;
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxHChunks; ++i) {
+                if (i < n) {
+#pragma unroll
+                    for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+                        for (int q = 0; q < 3; ++q) {
+                            acc[rb][0] = mfma(hp[i][rb][q], w[i][0], acc[rb][0]);
+                            acc[rb][1] = mfma(hp[i][rb][q], w[i][1], acc[rb][1]);
+                            acc[rb][3] = mfma(hp[i][rb][q], w[i][2], acc[rb][3]);
+                        }
+                }
+            }
+        }
+    }
+
+    // the 8 waves' sums, one row block at a time, added in wave order; all
+    // 512 threads write the workgroup's partial sums
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[wave][g * 4 + e][lane] = acc[rb][g][e];
+        __syncthreads();
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (i, lane) of 16 x 64
+            const int i = idx >> 6, ln = idx & 63;
+            float sum = red[0][i][ln];
+#pragma unroll
+            for (int w2 = 1; w2 < kWaves8; ++w2) sum += red[w2][i][ln];
+            const int g = i >> 2, e = i & 3;
+            const int row = rg * 64 + rb * 16 + (ln >> 4) * 4 + e;
+            if (row < a.B)
+                a.partial[((size_t)(ks * a.B + row) * kGateSlots + g) * a.H + ut * 16 + (ln & 15)] = sum;
+        }
+        __syncthreads();
+    }
+    if (ks == 0) {  // previous state of (row, unit), rebuilt exactly from its parts
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (row, unit) of 64 x 16
+            const int row = rg * 64 + (idx >> 4), u = ut * 16 + (idx & 15);
+            if (row >= a.B) continue;
+            const int xr = a.xtok ? a.xtok[row] : row;
+            float hpv = 0.f;
+            if (xr >= 0) {
+                const bf16_t* hs = a.hsplit + state_index(a, row) * H3 + u;
+                hpv = (bf16_to_f32(hs[0]) + bf16_to_f32(hs[a.H])) + bf16_to_f32(hs[2 * a.H]);
+            }
+            a.partial[((size_t)row * kGateSlots + 4) * a.H + u] = hpv;
+        }
+    }
 }
 
 // binary32 path (small configurations): one thread per (row, hidden unit),
@@ -209,17 +264,24 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* partial, int
 
 int gru_ksplit(int B, int E, int H, int dtype) {
     if (dtype != 1) return 1;
-    const int nK = (E + H) / 32;
+    // ~one workgroup per CU, and a single load batch per wave where possible
+    const int nE = E / 32, nH = H / 32;
     const int tiles = (H / 16) * ((B + 63) / 64);
-    int ks = (256 + tiles - 1) / max(tiles, 1);  // ~one workgroup per CU
-    return max(1, min(ks, max(1, nK / 8)));       // >= 2 chunks per wave
+    int best = kMaxKsplit;
+    for (int ks = 1; ks <= kMaxKsplit; ++ks) {
+        const int W = kWaves8 * ks, we = wave_split(nE, nH, W).WE;
+        const int xmax = nE ? (nE + we - 1) / we : 0, hmax = nH ? (nH + (W - we) - 1) / (W - we) : 0;
+        if (xmax <= kMaxXChunks && hmax <= kMaxHChunks && tiles * ks >= 192) return ks;
+        if (xmax <= kMaxXChunks && hmax <= kMaxHChunks) best = min(best, ks);
+    }
+    return best;
 }
 
 hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     if (a.dtype == 1) {
         dim3 grid(a.H / 16, (a.B + 63) / 64, a.ksplit);
-        gru_gates_bf16_kernel<<<grid, kThreads, 0, stream>>>(a);
+        gru_gates_bf16_kernel<<<grid, kWaves8 * kWave, 0, stream>>>(a);
     } else {
         dim3 grid((a.H + 63) / 64, a.B, 1);
         gru_gates_f32_kernel<<<grid, 64, 0, stream>>>(a);

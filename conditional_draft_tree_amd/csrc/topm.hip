@@ -84,10 +84,10 @@ __device__ __forceinline__ void publish(const WaveTop& w, uint32_t* s_thr) {
 __device__ __forceinline__ void fold_buffer(WaveTop& w, u64* buf, uint32_t* s_thr) {
     const int lane = lane_id();
     u64 x = lane < w.nbuf ? buf[lane] : 0ull;
-    x = wave_sort_desc(x);
+    x = wave_sort(x, /*ascending=*/true);
     w.list = wave_merge_top64(w.list, x);
     w.nbuf = 0;
-    set_thr(w, shfl_u64(w.list, kWave - 1));
+    set_thr(w, bcast_u64(w.list, kWave - 1));
     publish(w, s_thr);
 }
 
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
     if (wave == 0) {
         u64 l = w.list;
 #pragma unroll
-        for (int o = 1; o < kWaves; ++o) l = wave_merge_top64(l, sbuf[o][lane]);
+        for (int o = 1; o < kWaves; ++o) l = wave_merge_top64(l, sbuf[o][kWave - 1 - lane]);
         partial[((size_t)row * nseg + s) * kWave + lane] = l;
     }
 }
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kWave) void topm_merge_kernel(const u64* __restrict
     const int row = blockIdx.x, lane = lane_id();
     const u64* p = partial + (size_t)row * nseg * kWave;
     u64 l = p[lane];
-    for (int s = 1; s < nseg; ++s) l = wave_merge_top64(l, p[(size_t)s * kWave + lane]);
+    for (int s = 1; s < nseg; ++s) l = wave_merge_top64(l, p[(size_t)s * kWave + kWave - 1 - lane]);
     if (lane < M) {
         idx[(size_t)row * M + lane] = (int32_t)topm_key_id(l);
         val[(size_t)row * M + lane] = topm_key_val(l);
