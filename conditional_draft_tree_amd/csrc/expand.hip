@@ -184,17 +184,19 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
 
     // ---- 1. one round trip: every load below is independent of the others;
     // all are issued before the first use.
-    const int cnt = step == 0 ? 0 : a.count[b];
-    const int gtok = step == 0 ? 0 : a.gru_tok[b];
-    const int depth = step == 0 ? 0 : a.depths[slot0 + step];
-    u64 q = 0ull;
-    int qs = 0;
-    uint32_t flag = 0u;
-    if (step > 0 && wave == 0) {
-        q = a.queue[(size_t)b * kWave + lane];
-        qs = a.qsize[b];
-        flag = a.flags[b];
-    }
+    // per-request scalars: always-valid addresses, loaded unconditionally
+    // (at step 0 they hold stale values, replaced below) so that no load
+    // waits behind a branch on another
+    const int cnt_m = a.count[b], gtok_m = a.gru_tok[b], depth_m = a.depths[slot0 + step];
+    const int qs_m = a.qsize[b];
+    const uint32_t flag_m = a.flags[b];
+    const u64 q_m = a.queue[(size_t)b * kWave + lane];
+    const int cnt = step == 0 ? 0 : cnt_m;
+    const int gtok = step == 0 ? 0 : gtok_m;
+    const int depth = step == 0 ? 0 : depth_m;
+    u64 q = step == 0 ? 0ull : q_m;
+    int qs = step == 0 ? 0 : qs_m;
+    uint32_t flag = step == 0 ? 0u : flag_m;
     // top-M table of this request, children of slots 0 .. step-1, tree so far
     int32_t r_ti[kStage];
     float r_tv[kStage];
