@@ -28,6 +28,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# Per-source extra flags.  The top-M select only compares finite base logits
+# (the ABI requires them): without NaN semantics a float max is one
+# instruction instead of three (no quieting of its operands).
+FILE_FLAGS = {"topm.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
@@ -44,7 +48,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        _run([HIPCC, *FLAGS, "-c", src, "-o", obj])
+        _run([HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
         return obj
 
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:

@@ -170,9 +170,13 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
         return fail(nullptr, DT_ERR_UNSUPPORTED,
                     "per-request state needs %zu bytes of LDS (> 64 KiB): lower L*M, n or H",
                     lds.bytes);
+    const int nseg = dt::topm_segments(c.B * c.L, c.V);
+    const size_t seg_bytes = ((size_t)c.V + nseg - 1) / nseg * (c.dtype == DT_BF16 ? 2 : 4);
+    if (seg_bytes > (1u << 30))  // the select addresses a segment with 32-bit byte offsets
+        return fail(nullptr, DT_ERR_UNSUPPORTED, "top-M segment of %zu bytes exceeds 1 GiB", seg_bytes);
     dt_handle* h = new dt_handle();
     h->cfg = c;
-    h->nseg = dt::topm_segments(c.B * c.L, c.V);
+    h->nseg = nseg;
     h->ksplit = dt::gru_ksplit(c.B, c.E, c.H, (int)c.dtype);
     h->lds = lds;
     h->lay = plan_layout(c, h->nseg, h->ksplit);

@@ -118,6 +118,14 @@ __device__ __forceinline__ u64 xor_lane_u64(u64 v, int j) {
 }
 
 // Value of lane `src` (wave-uniform index) in every lane.
+// Lane i receives lane i-1's value; lane 0 receives 0 (DPP whole-wave shift
+// right by one lane).
+__device__ __forceinline__ u64 wave_shr1_u64(u64 v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x138, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x138, 0xF, 0xF, false);
+    return ((u64)hi << 32) | lo;
+}
+
 __device__ __forceinline__ u64 bcast_u64(u64 v, int src) {
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);

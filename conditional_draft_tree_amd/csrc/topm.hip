@@ -5,18 +5,25 @@
 // Restriction de candidats (Top-M)").  Order: value desc, token id asc.
 //
 // The select is HBM-bound: every row of V logits is streamed once, in
-// `nseg` segments of one 256-thread workgroup each.  Every wave keeps the 64
-// best (value, ~id) keys it has admitted, sorted across its lanes, and an
-// admission threshold: a key below it cannot be among the segment's 64 best.
-// Valid thresholds come from (a) the minimum of the 64 lane maxima of the
-// first vectors (64 distinct elements reach it), (b) the wave's own 64th best
-// key, and (c) the best value threshold any wave of the workgroup has
-// published in LDS (the segment's list merges all four waves).  The hot loop
-// is one max-reduction and one compare per 16-byte vector; a vector whose
-// maximum reaches the threshold is stashed in LDS, and stashed vectors are
-// evaluated 64 at a time (one per lane), which amortizes the wave-wide work of
-// admitting a key.  Admitted keys are folded into the list with a bitonic
-// sort + merge.  topm_merge folds a row's partial lists into its top M.
+// `nseg` segments of one 256-thread workgroup each, through buffer loads
+// software-pipelined over two register sets (one batch in flight while the
+// previous one is evaluated).  Every wave keeps the 64 best (value, ~id) keys
+// it has admitted, sorted across its lanes, and an admission threshold: a key
+// below it cannot be among the segment's 64 best.  Valid thresholds come from
+//   (a) the 64th largest of the 256 lane maxima of the first batch (64
+//       distinct elements reach it);
+//   (b) the wave's own 64th best key;
+//   (c) bounds the four waves share in LDS: the largest 64th best of any wave,
+//       and the smallest of the four waves' 16th best keys (together the
+//       waves hold 64 keys at or above it).
+// The hot loop is one conservative max-reduction and one compare per 16-byte
+// vector; a vector whose maximum reaches the threshold is stashed in LDS, and
+// stashed vectors are evaluated 64 at a time (one per lane), which amortizes
+// the wave-wide work of admitting a key.  Admitted keys are folded into the
+// list by insertion (few keys) or bitonic sort + merge.  topm_merge folds a
+// row's partial lists into its top M.
+#include <cfloat>
+
 #include "dt_device.h"
 #include "dt_launch.h"
 
@@ -26,8 +33,9 @@ namespace {
 
 constexpr int kTopmThreads = 256;
 constexpr int kWaves = kTopmThreads / kWave;
-constexpr int kUnroll = 8;   // 16-byte vectors in flight per lane
-constexpr int kStash = 128;  // stashed vectors per wave
+constexpr int kUnroll = 4;  // 16-byte vectors per lane per batch (two batches in flight)
+// stashed vectors per wave: fewer than 64 left over plus at most 64 per vector of a batch
+constexpr int kStash = kWave * (kUnroll + 1);
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,6 +49,9 @@ template <> struct Elem<float> {
         return fmaxf(fmaxf(__uint_as_float(v.x), __uint_as_float(v.y)),
                      fmaxf(__uint_as_float(v.z), __uint_as_float(v.w)));
     }
+    // binary32 elements are compared exactly
+    static constexpr float kSlack = 0.f;
+    __device__ static float vfilter(const u32x4& v) { return vmax(v); }
     __device__ static float scalar(const float* p) { return *p; }
 };
 template <> struct Elem<bf16_t> {
@@ -56,6 +67,20 @@ template <> struct Elem<bf16_t> {
         float d = fmaxf(__uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
         return fmaxf(fmaxf(a, b), fmaxf(c, d));
     }
+    // An upper bound on the element maximum within |value| / 128 of it, in 8
+    // operations instead of 12: a 32-bit word read as binary32 is its high
+    // bf16 element plus part of the low one's bits, i.e. the high element
+    // moved away from zero by less than 2^-7 of its magnitude.  Vectors are
+    // therefore compared with a threshold lowered by |threshold| / 64, which
+    // never rejects an element at or above the threshold.
+    static constexpr float kSlack = 1.f / 64.f;
+    __device__ static float vfilter(const u32x4& v) {
+        const float a = fmaxf(fmaxf(__uint_as_float(v.x), __uint_as_float(v.y)), __uint_as_float(v.z));
+        const float b = fmaxf(fmaxf(__uint_as_float(v.w), __uint_as_float(v.x << 16)),
+                              __uint_as_float(v.y << 16));
+        const float c = fmaxf(fmaxf(__uint_as_float(v.z << 16), __uint_as_float(v.w << 16)), a);
+        return fmaxf(b, c);
+    }
     __device__ static float scalar(const bf16_t* p) { return bf16_to_f32(*p); }
 };
 
@@ -66,6 +91,8 @@ struct WaveTop {
     u64 list;
     u64 thr;
     float thr_val;  // value part of thr (-inf while thr == 0)
+    float filt;     // vector filter bound: thr_val lowered by slack * |thr_val|, >= -FLT_MAX
+    float slack;
     int nbuf;
 };
 
@@ -73,26 +100,71 @@ __device__ __forceinline__ void set_thr(WaveTop& w, u64 t) {
     if (t > w.thr) {
         w.thr = t;
         w.thr_val = topm_key_val(t);
+        // finite, so that masked vectors (-inf) never pass
+        w.filt = fmaxf(w.slack > 0.f ? w.thr_val - fabsf(w.thr_val) * w.slack : w.thr_val, -FLT_MAX);
     }
 }
 
-// Publish the value part of the wave's threshold to the workgroup.
-__device__ __forceinline__ void publish(const WaveTop& w, uint32_t* s_thr) {
-    if (w.thr && lane_id() == 0) atomicMax(s_thr, (uint32_t)(w.thr >> 32));
+// Value bounds the waves of a workgroup share (order-preserving value bits,
+// 0 = none yet).  Both only rise.
+//   max64:  the largest 64th-best value of any wave's list;
+//   q16[w]: the 16th-best value of wave w's list.
+// Wave lists only improve, so wave w keeps holding 16 keys >= q16[w]: the four
+// waves together hold 64 keys >= min_w q16[w], and a key below that bound is
+// not among the workgroup's 64 best.  With each wave seeing a quarter of the
+// segment, this bound tracks the segment's own 64th best.
+struct SharedThr {
+    uint32_t max64;
+    uint32_t q16[kWaves];
+};
+
+__device__ __forceinline__ u64 shared_bound(const SharedThr* st) {
+    uint32_t q = __hip_atomic_load(&st->q16[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i)
+        q = min(q, __hip_atomic_load(&st->q16[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    const uint32_t m = __hip_atomic_load(&st->max64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return (u64)max(q, m) << 32;
 }
 
-__device__ __forceinline__ void fold_buffer(WaveTop& w, u64* buf, uint32_t* s_thr) {
+// Publish the wave's bounds to the workgroup.
+__device__ __forceinline__ void publish(const WaveTop& w, SharedThr* st) {
+    const uint32_t q = (uint32_t)(bcast_u64(w.list, 15) >> 32);
+    if (lane_id() == 0) {
+        if (w.thr) atomicMax(&st->max64, (uint32_t)(w.thr >> 32));
+        if (q) __hip_atomic_store(&st->q16[threadIdx.x / kWave], q, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+// Folds of at most this many keys insert them one at a time (a ballot and a
+// one-lane shift each); larger ones sort the buffer and merge it.
+constexpr int kInsertMax = 16;
+
+__device__ __forceinline__ void fold_buffer(WaveTop& w, u64* buf, SharedThr* st) {
     const int lane = lane_id();
-    u64 x = lane < w.nbuf ? buf[lane] : 0ull;
-    x = wave_sort(x, /*ascending=*/true);
-    w.list = wave_merge_top64(w.list, x);
+    if (w.nbuf <= kInsertMax) {
+        for (int i = 0; i < w.nbuf; ++i) {
+            const u64 k = buf[i];
+            // the list is descending and its keys differ from k (ids differ)
+            const int pos = __popcll(__ballot(w.list > k));
+            if (pos >= kWave) continue;
+            const u64 sh = wave_shr1_u64(w.list);
+            w.list = lane < pos ? w.list : (lane == pos ? k : sh);
+        }
+    } else {
+        u64 x = lane < w.nbuf ? buf[lane] : 0ull;
+        x = wave_sort(x, /*ascending=*/true);
+        w.list = wave_merge_top64(w.list, x);
+    }
     w.nbuf = 0;
     set_thr(w, bcast_u64(w.list, kWave - 1));
-    publish(w, s_thr);
+    publish(w, st);
+    set_thr(w, shared_bound(st));
 }
 
 // Offer one key per lane (valid only where `ok`); wave-uniform call.
-__device__ __forceinline__ void offer(WaveTop& w, u64* buf, uint32_t* s_thr, bool ok, u64 key) {
+__device__ __forceinline__ void offer(WaveTop& w, u64* buf, SharedThr* s_thr, bool ok, u64 key) {
     bool pass = ok && key >= w.thr;
     u64 m = __ballot(pass);
     if (m == 0) return;
@@ -115,36 +187,29 @@ __device__ __forceinline__ int prefix_count(u64 m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Evaluate the first min(nst, 64) stashed vectors (one per lane) element by
-// element, then move the rest down.
+// Evaluate the last min(nst, 64) stashed vectors (one per lane) element by
+// element.  The order in which admitted keys arrive does not change the
+// result.  One copy of this code serves the whole kernel (its element loop is
+// not unrolled), which keeps the kernel small enough for the instruction cache.
 template <typename T>
-__device__ __forceinline__ void drain_stash(WaveTop& w, u64* buf, uint32_t* s_thr, u32x4* svec,
-                                            int* sidx, int& nst, int lo) {
+__device__ __forceinline__ void drain_stash(WaveTop& w, u64* buf, SharedThr* s_thr, const u32x4* svec,
+                                            const int* sidx, int& nst, int lo) {
     constexpr int P = Elem<T>::kPerVec;
     const int lane = lane_id();
     const int take = min(nst, kWave);
+    const int from = nst - take;
     const bool on = lane < take;
-    const u32x4 v = on ? svec[lane] : u32x4{0u, 0u, 0u, 0u};
-    const int vi = on ? sidx[lane] : 0;
-    set_thr(w, (u64)__hip_atomic_load(s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) << 32);
-#pragma unroll
+    const u32x4 v = on ? svec[from + lane] : u32x4{0u, 0u, 0u, 0u};
+    const int vi = on ? sidx[from + lane] : 0;
+    set_thr(w, shared_bound(s_thr));
+#pragma unroll 1
     for (int i = 0; i < P; ++i) {
         const float x = Elem<T>::get(v, i);
         offer(w, buf, s_thr, on && x >= w.thr_val, topm_key(x, (uint32_t)(lo + vi * P + i)));
     }
-    const int rest = nst - take;
-    u32x4 mv = u32x4{0u, 0u, 0u, 0u};
-    int mi = 0;
-    if (lane < rest) {
-        mv = svec[kWave + lane];
-        mi = sidx[kWave + lane];
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (lane < rest) {
-        svec[lane] = mv;
-        sidx[lane] = mi;
-    }
-    nst = rest;
+    // fold now, so that the shared bounds follow every admitted key
+    if (w.nbuf) fold_buffer(w, buf, s_thr);
+    nst = from;
 }
 
 template <typename T, bool kVec>
@@ -154,57 +219,81 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
     __shared__ u64 sbuf[kWaves][kWave];
     __shared__ u32x4 svec[kWaves][kStash];
     __shared__ int sidx[kWaves][kStash];
-    __shared__ uint32_t s_thr;
+    __shared__ SharedThr s_thr;
     const int row = blockIdx.y, s = blockIdx.x;
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const T* rp = base + (size_t)row * (size_t)V;
     const int lo = s * seg;
     const int hi = min(V, lo + seg);
     u64* buf = sbuf[wave];
-    if (threadIdx.x == 0) s_thr = 0u;
+    if (threadIdx.x == 0) s_thr.max64 = 0u;
+    if (threadIdx.x < kWaves) s_thr.q16[threadIdx.x] = 0u;
     __syncthreads();
 
     WaveTop w;
     w.list = 0ull;
     w.thr = 0ull;
     w.thr_val = -INFINITY;
+    w.filt = -FLT_MAX;
+    w.slack = Elem<T>::kSlack;
     w.nbuf = 0;
     int nst = 0;
 
     int tail_lo = lo;
     if (kVec && hi > lo) {
         constexpr int P = Elem<T>::kPerVec;
+        constexpr int kBatch = kUnroll * kTopmThreads;
         const int nvec = (hi - lo) / P;
-        const u32x4* vp = reinterpret_cast<const u32x4*>(rp + lo);
-        bool first = true;
-        for (int v0 = 0; v0 < nvec; v0 += kUnroll * kTopmThreads) {
-            u32x4 vec[kUnroll];
-            float vm[kUnroll];
-            bool ok[kUnroll];
+        // Buffer loads over the segment's whole vectors: reads past its end
+        // return zeros (masked below), so the loop needs no address clamps.
+        // The logits are read once: the loads are non-temporal (cache policy
+        // bit 1), which keeps them from evicting, and writing back, what the
+        // memory-side cache holds.
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(rp + lo), (short)0, nvec * 16, 0x00020000);
+        const int voff = (int)threadIdx.x * 16;
+        auto load = [&](int vi0) {
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, vi0 * 16, 2));
+        };
+        // Initial bound from the exact maxima of the first batch.
+        auto init_bound = [&](const u32x4 (&vec)[kUnroll]) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int vi = v0 + u * kTopmThreads + (int)threadIdx.x;
-                ok[u] = vi < nvec;
-                vec[u] = ok[u] ? __builtin_nontemporal_load(vp + vi) : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int u = 0; u < kUnroll; ++u)
+                mx = fmaxf(mx, u * kTopmThreads + (int)threadIdx.x < nvec ? Elem<T>::vmax(vec[u]) : -INFINITY);
+            if (nvec >= kBatch) {
+                // Every lane of the workgroup holds a full first batch: the 64th
+                // largest of the 256 lane maxima is reached by 64 distinct
+                // elements, so no key below it is in the top 64.
+                const u64 k = wave_sort_desc((u64)f32_ord(mx) << 32);
+                buf[lane] = k;
+                __syncthreads();
+                u64 l = k;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) vm[u] = ok[u] ? Elem<T>::vmax(vec[u]) : -INFINITY;
-            if (first) {
+                for (int o = 1; o < kWaves; ++o)
+                    l = wave_merge_top64(l, sbuf[(wave + o) % kWaves][kWave - 1 - lane]);
+                __syncthreads();  // the key buffers are reused for admitted keys
+                set_thr(w, bcast_u64(l, kWave - 1));
+            } else if (__ballot((int)threadIdx.x < nvec) == ~0ull) {
                 // 64 distinct elements (one per lane) reach the smallest lane maximum
-                first = false;
-                float mx = vm[0];
+                set_thr(w, (u64)f32_ord(-wave_max(-mx)) << 32);
+                publish(w, &s_thr);
+            }
+        };
+        // Evaluate the batch of vectors v0 + u * 256 + thread (u < kUnroll).
+        auto process = [&](const u32x4 (&vec)[kUnroll], int v0) {
+            float vm[kUnroll];
+            set_thr(w, shared_bound(&s_thr));
 #pragma unroll
-                for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, vm[u]);
-                if (__ballot(v0 + (int)threadIdx.x < nvec) == ~0ull) {
-                    set_thr(w, (u64)f32_ord(-wave_max(-mx)) << 32);
-                    publish(w, &s_thr);
-                }
-            } else {
-                set_thr(w, (u64)__hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) << 32);
+            for (int u = 0; u < kUnroll; ++u) vm[u] = Elem<T>::vfilter(vec[u]);
+            if (v0 + kBatch > nvec) {  // last, partial batch
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (v0 + u * kTopmThreads + (int)threadIdx.x >= nvec) vm[u] = -INFINITY;
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const bool pass = ok[u] && vm[u] >= w.thr_val;
+                const bool pass = vm[u] >= w.filt;
                 const u64 m = __ballot(pass);
                 if (m == 0) continue;
                 if (pass) {
@@ -213,10 +302,30 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
                     sidx[wave][pos] = v0 + u * kTopmThreads + (int)threadIdx.x;
                 }
                 nst += __popcll(m);
-                if (nst >= kWave) drain_stash<T>(w, buf, &s_thr, svec[wave], sidx[wave], nst, lo);
             }
+            // fewer than 64 stay stashed between batches; none after the last
+            const bool last = v0 + kBatch >= nvec;
+            while (nst >= kWave || (last && nst > 0))
+                drain_stash<T>(w, buf, &s_thr, svec[wave], sidx[wave], nst, lo);
+        };
+        // Software pipeline over two register sets: the next batch is in
+        // flight while this one is evaluated, and no loaded register is
+        // copied (a copy would wait for its load).
+        u32x4 va[kUnroll], vb[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) va[u] = load(u * kTopmThreads);
+        for (int v0 = 0; v0 < nvec;) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) vb[u] = load(v0 + kBatch + u * kTopmThreads);
+            if (v0 == 0) init_bound(va);
+            process(va, v0);
+            v0 += kBatch;
+            if (v0 >= nvec) break;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) va[u] = load(v0 + kBatch + u * kTopmThreads);
+            process(vb, v0);
+            v0 += kBatch;
         }
-        while (nst > 0) drain_stash<T>(w, buf, &s_thr, svec[wave], sidx[wave], nst, lo);
         tail_lo = lo + nvec * P;
     }
     // scalar part: the row's tail, or everything when rows are not 16-byte aligned
