@@ -20,7 +20,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 thread_local char g_create_error[512] = "";
 
 struct Layout {
-    size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue,
+    size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
         qsize;
     size_t total;
 };
@@ -88,6 +88,8 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.child_lp = take(B * S * 64 * 4);
     l.queue = take(B * 64 * sizeof(u64));
     l.qsize = take(B * 4);
+    l.nidx = take(B * 64 * 4);
+    l.nval = take(B * 64 * 4);
     l.total = off;
     return l;
 }
@@ -377,6 +379,8 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.child_lp = (float*)(w + L.child_lp);
     a.queue = (u64*)(w + L.queue);
     a.qsize = (int32_t*)(w + L.qsize);
+    a.nidx = (int32_t*)(w + L.nidx);
+    a.nval = (float*)(w + L.nval);
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
     a.mask = mask; a.count = count; a.flags = flags;
 

@@ -72,6 +72,8 @@ struct NodeArgs {
     float* child_lp;     // [B, n+1, 64]
     u64* queue;          // [B, 64] candidate keys, 0 = empty
     int32_t* qsize;      // [B]
+    int32_t* nidx;       // [B, 64] candidate tokens of the slot expanded next
+    float* nval;         // [B, 64] their base logits
     // outputs
     int32_t* tokens;
     int32_t* parents;

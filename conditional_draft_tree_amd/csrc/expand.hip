@@ -164,7 +164,61 @@ NodeLds node_lds_plan(int L, int M, int n, int H) {
 
 namespace {
 
-template <typename T>
+// Row sums over the 64 lanes of a wave's 16 per-lane partial dots, reduced
+// in transposed form (each exchange halves the values a lane holds): lane l
+// ends with the sum of row (l >> 2) & 15, the same in the four lanes of a quad.
+// Lane semantics of the swaps with two operands A, B: permlane32_swap returns
+// {[A lower half, B lower half], [A upper half, B upper half]};
+// permlane16_swap returns {[A row0, B row0, A row2, B row2],
+// [A row1, B row1, A row3, B row3]} (rows of 16 lanes).
+__device__ __forceinline__ float wave_rowsum16(const float (&acc)[kRowsPerWave]) {
+    const int lane = lane_id();
+    float s8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // rows i + 8 * lane bit 5
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i + 8]),
+                                                        false, false);
+        s8[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // rows i + 4 * bit 4 + 8 * bit 5
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s8[i]), __float_as_uint(s8[i + 4]),
+                                                        false, false);
+        s4[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool b3 = lane & 8, b2 = lane & 4;
+    float s2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // rows i + 2 * bit 3 + 4 * bit 4 + 8 * bit 5
+        const float keep = b3 ? s4[i + 2] : s4[i];
+        const float send = b3 ? s4[i] : s4[i + 2];
+        s2[i] = keep + xor_lane_f<8>(send);
+    }
+    float v = (b2 ? s2[1] : s2[0]) + xor_lane_f<4>(b2 ? s2[0] : s2[1]);
+    v += xor_lane_f<2>(v);
+    v += xor_lane_f<1>(v);
+    return v;
+}
+
+// Wave 0: z = base logit + correction dot, temperature, log-softmax over the
+// M-slice, children sorted by (log-prob desc, token asc).  Lane j holds
+// candidate j's token, base logit and dot; lane r returns the rank-r child
+// (key 0 when r >= M).
+__device__ __forceinline__ u64 sorted_children_r(float val, float dot, int tok, int M, float temp) {
+    const int lane = lane_id();
+    const bool on = lane < M;
+    float zz = on ? val + dot : -INFINITY;
+    if (temp > 0.f) zz = zz / temp;
+    const float m = wave_max(zz);
+    const float e = on ? expf(zz - m) : 0.f;
+    const float ssum = wave_sum(e);
+    const float lp = (zz - m) - logf(ssum);
+    u64 key = on ? child_key(lp, tok) : 0ull;
+    return wave_sort_desc(key);
+}
+
+template <typename T, int KS>
 __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
     extern __shared__ float lds[];
     float* hs = lds + lp.hs;
@@ -175,29 +229,66 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     float* s_tval = lds + lp.tval;
     int32_t* s_ctok = (int32_t*)(lds + lp.ctok);
     float* s_clp = lds + lp.clp;
+    constexpr int P = Row<T>::kPerVec;       // elements per 16-byte vector
+    constexpr int kChunk = 2 * kWave * P;    // K elements of a gathered chunk
 
     const int b = blockIdx.x;
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int S = a.n + 1;
     const size_t slot0 = (size_t)b * S;
     const int LM = a.L * a.M;
+    const int H = a.H;
 
-    // ---- 1. one round trip: every load below is independent of the others;
-    // all are issued before the first use.
-    // per-request scalars: always-valid addresses, loaded unconditionally
-    // (at step 0 they hold stale values, replaced below) so that no load
-    // waits behind a branch on another
-    const int cnt_m = a.count[b], gtok_m = a.gru_tok[b], depth_m = a.depths[slot0 + step];
-    const int qs_m = a.qsize[b];
-    const uint32_t flag_m = a.flags[b];
+    // ---- 1. loads.  Round trip 1: the candidate list of the slot expanded
+    // now (the previous step left it in nidx/nval; the root takes block
+    // position 0 of the table), the gate partial sums, the queue.  Round
+    // trip 2, issued as soon as the candidate tokens arrive: the gathered
+    // rows of the correction matrix.  Every address is valid whatever the
+    // state (tokens clamped to the vocabulary), so no load waits on a test.
+    const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
+    const float* vp = step == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
+    const int jl = min(lane, a.M - 1);
+    const int my_tok = min(max(ip[jl], 0), a.V - 1);  // candidate `lane` (all waves)
+    const float my_val = vp[jl];
     const u64 q_m = a.queue[(size_t)b * kWave + lane];
-    const int cnt = step == 0 ? 0 : cnt_m;
-    const int gtok = step == 0 ? 0 : gtok_m;
-    const int depth = step == 0 ? 0 : depth_m;
-    u64 q = step == 0 ? 0ull : q_m;
-    int qs = step == 0 ? 0 : qs_m;
-    uint32_t flag = step == 0 ? 0u : flag_m;
+    // slot `step`'s state: the GRU cell on the K-range partial sums of the
+    // preceding contraction, added in K order (read at every step; the root
+    // takes h0 instead)
+    const int k4 = (int)threadIdx.x * 4;  // first of this thread's 4 state elements
+    const bool kin = k4 < H;
+    const int kc = kin ? k4 : 0;
+    f32x4 t[KS][4];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kc);
+    f32x4 hp = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)b * kGateSlots + 4) * H + kc);
+    f32x4 bias[6];
+#pragma unroll
+    for (int g = 0; g < 6; ++g) {
+        const void* bp = g < 3 ? a.b_ih : a.b_hh;
+        const T* src = bp ? (const T*)bp : (const T*)a.partial;  // any valid address
+        const f32x4 v = load4<T>(src + (size_t)(g % 3) * H + kc);
+        bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // round trip 2: chunk k0 of this wave's 16 rows, two vectors per lane and
+    // row (positions past H are clamped; their state elements are zero)
+    u32x4 cv[kRowsPerWave][2];
+    auto gather = [&](int k0) {
+        const int ka = min(k0 + lane * P, H - P), kb = min(k0 + (kWave + lane) * P, H - P);
+#pragma unroll
+        for (int jj = 0; jj < kRowsPerWave; ++jj) {
+            const int tk = __builtin_amdgcn_readlane(my_tok, wave * kRowsPerWave + jj);
+            const T* row = (const T*)a.C + (size_t)tk * H;
+            cv[jj][0] = *reinterpret_cast<const u32x4*>(row + ka);
+            cv[jj][1] = *reinterpret_cast<const u32x4*>(row + kb);
+        }
+    };
+    gather(0);
     // top-M table of this request, children of slots 0 .. step-1, tree so far
+    // (into registers now, into LDS after the state is computed)
     int32_t r_ti[kStage];
     float r_tv[kStage];
     int32_t r_ct[kStage];
@@ -219,63 +310,69 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         r_sc = a.scores[slot0 + threadIdx.x];
         r_par = a.parents[slot0 + threadIdx.x];
     }
-    // slot `step`'s state: h0 at the root, else the GRU cell applied to the
-    // K-range partial sums (added in K order) of the preceding contraction.
-    // Partials and biases are read whether or not the slot expands (they are
-    // always in bounds), so the expansion test does not delay them.
+    // per-request state (scalar loads)
+    const int cnt_m = a.count[b], gtok_m = a.gru_tok[b], depth_m = a.depths[slot0 + step];
+    const int qs_m = a.qsize[b];
+    const uint32_t flag_m = a.flags[b];
+    const int cnt = step == 0 ? 0 : cnt_m;
+    const int gtok = step == 0 ? 0 : gtok_m;
+    const int depth = step == 0 ? 0 : depth_m;
+    u64 q = step == 0 ? 0ull : q_m;
+    int qs = step == 0 ? 0 : qs_m;
+    uint32_t flag = step == 0 ? 0u : flag_m;
     const bool expand = step == 0 || (cnt == step && gtok >= 0);
-    float* hdst = a.hstate + (slot0 + step) * a.H;
-    uint16_t* pdst = a.hsplit ? a.hsplit + (slot0 + step) * 3 * (size_t)a.H : nullptr;
-    for (int k4 = threadIdx.x * 4; k4 < a.H; k4 += kNodeThreads * 4) {
-        float hv[4];
-        if (step == 0) {
+
+    // ---- 2. the state of slot `step`, 4 elements per thread and pass (the
+    // first pass's operands are already in flight)
+    for (int kb0 = 0; kb0 < H; kb0 += kNodeThreads * 4) {
+        const int kk = kb0 + k4;
+        if (kb0 > 0 && kk < H) {  // states wider than 1024
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = a.h0 ? a.h0[(size_t)b * a.H + k4 + e] : 0.f;
-        } else {
-            // branch-free: indices are clamped to valid slots, unused ones zeroed
-            f32x4 t[kMaxKsplit][4];
+            for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
-            for (int s = 0; s < kMaxKsplit; ++s) {
-                const int sc = min(s, a.ksplit - 1);
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(
-                        a.partial + ((size_t)(sc * a.B + b) * kGateSlots + g) * a.H + k4);
-                    t[s][g] = s < a.ksplit ? v : f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-            const f32x4 hp = *reinterpret_cast<const f32x4*>(
-                a.partial + ((size_t)b * kGateSlots + 4) * a.H + k4);
-            f32x4 bias[6];
+                for (int g = 0; g < 4; ++g)
+                    t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kk);
+            hp = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)b * kGateSlots + 4) * H + kk);
 #pragma unroll
             for (int g = 0; g < 6; ++g) {
                 const void* bp = g < 3 ? a.b_ih : a.b_hh;
-                const T* src = bp ? (const T*)bp : (const T*)a.partial;  // any valid address
-                const f32x4 v = load4<T>(src + (size_t)(g % 3) * a.H + k4);
-                bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+                if (bp) bias[g] = load4<T>((const T*)bp + (size_t)(g % 3) * H + kk);
             }
+        }
+        if (kk >= H) break;
+        float hv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (step == 0) {
+            if (a.h0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = a.h0[(size_t)b * H + kk + e];
+            }
+        } else {
             f32x4 sum[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 sum[g] = t[0][g];
 #pragma unroll
-                for (int s = 1; s < kMaxKsplit; ++s) sum[g] += t[s][g];
+                for (int s2 = 1; s2 < KS; ++s2) sum[g] += t[s2][g];
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 hv[e] = gru_cell_b(sum[0][e], sum[1][e], sum[2][e], sum[3][e], bias[0][e], bias[1][e],
                                    bias[2][e], bias[3][e], bias[4][e], bias[5][e], hp[e]);
         }
-        if (expand) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hs[k4 + e] = hv[e];
-                hdst[k4 + e] = hv[e];
-                if (pdst) {
+        for (int e = 0; e < 4; ++e) hs[kk + e] = hv[e];
+        if (expand) {
+            float* hdst = a.hstate + (slot0 + step) * H;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hdst[kk + e] = hv[e];
+            if (a.hsplit) {
+                uint16_t* pdst = a.hsplit + (slot0 + step) * 3 * (size_t)H;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
                     uint32_t parts[3];
                     split3_bf16(hv[e], parts);
 #pragma unroll
-                    for (int qq = 0; qq < 3; ++qq) pdst[(size_t)qq * a.H + k4 + e] = (uint16_t)parts[qq];
+                    for (int qq = 0; qq < 3; ++qq) pdst[(size_t)qq * H + kk + e] = (uint16_t)parts[qq];
                 }
             }
         }
@@ -298,16 +395,36 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     __syncthreads();
 
-    // ---- 2. children of slot `step` (block position = its depth)
-    if (expand)
-        correction_logits<T>((const T*)a.C, s_tidx + depth * a.M, s_tval + depth * a.M, a.M, a.H,
-                             hs, zs);
+    // ---- 3. correction dots of slot `step`'s children (block position = its
+    // depth): this wave's 16 rows, then a transposed reduction across lanes
+    if (expand) {
+        float acc[kRowsPerWave];
+#pragma unroll
+        for (int jj = 0; jj < kRowsPerWave; ++jj) acc[jj] = 0.f;
+        for (int k0 = 0; k0 < H; k0 += kChunk) {
+            if (k0 > 0) gather(k0);  // states wider than one chunk
+            const int ka = k0 + lane * P, kb = k0 + (kWave + lane) * P;
+            float ha[P], hb[P];  // zero past H (those lanes read a clamped row segment)
+#pragma unroll
+            for (int i2 = 0; i2 < P; ++i2) {
+                ha[i2] = ka < H ? hs[ka + i2] : 0.f;
+                hb[i2] = kb < H ? hs[kb + i2] : 0.f;
+            }
+#pragma unroll
+            for (int jj = 0; jj < kRowsPerWave; ++jj) {
+                acc[jj] += Row<T>::dot(cv[jj][0], ha);
+                acc[jj] += Row<T>::dot(cv[jj][1], hb);
+            }
+        }
+        const float d = wave_rowsum16(acc);
+        if ((lane & 3) == 0) zs[wave * kRowsPerWave + (lane >> 2)] = d;
+    }
     __syncthreads();
     if (wave != 0) return;
 
     u64 kids = 0ull;  // lane r: rank-r child of slot `step`
     if (expand) {
-        kids = sorted_children(zs, s_tidx + depth * a.M, a.M, a.temp);
+        kids = sorted_children_r(my_val, zs[lane], my_tok, a.M, a.temp);
         const size_t crow = (slot0 + step) * kMaxM;
         if (lane < a.M) {
             a.child_tok[crow + lane] = child_tok_of(kids);
@@ -383,6 +500,11 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
             a.gru_tok[b] = grow ? ptok : -1;
             a.gru_par[b] = pp;
         }
+        if (pd < a.L && v < a.n) {  // the next step expands v: hand over its candidates
+            const int jm = min(lane, a.M - 1);
+            a.nidx[(size_t)b * kWave + lane] = s_tidx[pd * a.M + jm];
+            a.nval[(size_t)b * kWave + lane] = s_tval[pd * a.M + jm];
+        }
     } else if (lane == 0) {
         a.gru_tok[b] = -1;
         a.gru_par[b] = 0;
@@ -446,13 +568,21 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
 
 }  // namespace
 
+template <typename T>
+hipError_t launch_node_t(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream) {
+    switch (a.ksplit) {
+#define DT_KS(K) \
+    case K: node_step_kernel<T, K><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step); break;
+        DT_KS(1) DT_KS(2) DT_KS(3) DT_KS(4) DT_KS(5) DT_KS(6)
+#undef DT_KS
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
-    if (a.dtype == 1)
-        node_step_kernel<bf16_t><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step);
-    else
-        node_step_kernel<float><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step);
-    return hipGetLastError();
+    return a.dtype == 1 ? launch_node_t<bf16_t>(a, lp, step, stream) : launch_node_t<float>(a, lp, step, stream);
 }
 
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,
