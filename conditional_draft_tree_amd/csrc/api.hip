@@ -21,7 +21,7 @@ thread_local char g_create_error[512] = "";
 
 struct Layout {
     size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
-        qsize;
+        rstate;
     size_t total;
 };
 
@@ -79,7 +79,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.partial = take(B * L * (size_t)nseg * 64 * sizeof(u64));
     l.tidx = take(B * L * M * 4);
     l.tval = take(B * L * M * 4);
-    l.hstate = take(B * S * H * 4);
+    l.hstate = take(c.dtype == DT_F32 ? B * S * H * 4 : 0);  // the bf16 path keeps bf16 parts only
     l.hsplit = take(c.dtype == DT_BF16 ? B * S * 3 * H * 2 : 0);
     l.gpart = take((size_t)ksplit * B * dt::kGateSlotsHost * H * 4);
     l.gru_tok = take(B * 4);
@@ -87,7 +87,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.child_tok = take(B * S * 64 * 4);
     l.child_lp = take(B * S * 64 * 4);
     l.queue = take(B * 64 * sizeof(u64));
-    l.qsize = take(B * 4);
+    l.rstate = take(B * dt::kStateWords * 4);
     l.nidx = take(B * 64 * 4);
     l.nval = take(B * 64 * 4);
     l.total = off;
@@ -369,7 +369,7 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.C = C; a.h0 = h0;
     a.tidx = tidx; a.tval = tval;
     a.b_ih = b_ih; a.b_hh = b_hh;
-    a.hstate = (float*)(w + L.hstate);
+    a.hstate = c.dtype == DT_F32 ? (float*)(w + L.hstate) : nullptr;
     a.hsplit = c.dtype == DT_BF16 ? (uint16_t*)(w + L.hsplit) : nullptr;
     a.partial = (const float*)(w + L.gpart);
     a.ksplit = h->ksplit;
@@ -378,7 +378,7 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.child_tok = (int32_t*)(w + L.child_tok);
     a.child_lp = (float*)(w + L.child_lp);
     a.queue = (u64*)(w + L.queue);
-    a.qsize = (int32_t*)(w + L.qsize);
+    a.rstate = (int32_t*)(w + L.rstate);
     a.nidx = (int32_t*)(w + L.nidx);
     a.nval = (float*)(w + L.nval);
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;

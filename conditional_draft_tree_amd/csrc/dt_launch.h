@@ -49,6 +49,7 @@ hipError_t launch_finalize(const float* partial, int ksplit, const void* b_ih, c
                            float* h_out, int B, int H, int dtype, hipStream_t stream);
 
 // ---- expansion (expand.hip) -------------------------------------------------
+constexpr int kStateWords = 8;
 struct NodeArgs {
     // problem
     int B, L, V, E, H, M, n, dtype;
@@ -71,7 +72,8 @@ struct NodeArgs {
     int32_t* child_tok;  // [B, n+1, 64] sorted children per slot
     float* child_lp;     // [B, n+1, 64]
     u64* queue;          // [B, 64] candidate keys, 0 = empty
-    int32_t* qsize;      // [B]
+    int32_t* rstate;     // [B, kStateWords] per-request state left for the next step:
+                         // count, next GRU token, queue size, flags, depth of the next slot
     int32_t* nidx;       // [B, 64] candidate tokens of the slot expanded next
     float* nval;         // [B, 64] their base logits
     // outputs

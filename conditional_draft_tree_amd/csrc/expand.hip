@@ -31,6 +31,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNodeThreads = 256;
 constexpr int kRowsPerWave = kMaxM / (kNodeThreads / kWave);  // 16
@@ -246,11 +247,6 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // trip 2, issued as soon as the candidate tokens arrive: the gathered
     // rows of the correction matrix.  Every address is valid whatever the
     // state (tokens clamped to the vocabulary), so no load waits on a test.
-    const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
-    const float* vp = step == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
-    const int jl = min(lane, a.M - 1);
-    const int my_tok = min(max(ip[jl], 0), a.V - 1);  // candidate `lane` (all waves)
-    const float my_val = vp[jl];
     const u64 q_m = a.queue[(size_t)b * kWave + lane];
     // slot `step`'s state: the GRU cell on the K-range partial sums of the
     // preceding contraction, added in K order (read at every step; the root
@@ -273,6 +269,14 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         const f32x4 v = load4<T>(src + (size_t)(g % 3) * H + kc);
         bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // (the scheduler keeps the loads above in flight before the candidate
+    // list is waited for)
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
+    const float* vp = step == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
+    const int jl = min(lane, a.M - 1);
+    const int my_tok = min(max(ip[jl], 0), a.V - 1);  // candidate `lane` (all waves)
+    const float my_val = vp[jl];
     // round trip 2: chunk k0 of this wave's 16 rows, two vectors per lane and
     // row (positions past H are clamped; their state elements are zero)
     u32x4 cv[kRowsPerWave][2];
@@ -288,21 +292,26 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     };
     gather(0);
     // top-M table of this request, children of slots 0 .. step-1, tree so far
-    // (into registers now, into LDS after the state is computed)
-    int32_t r_ti[kStage];
-    float r_tv[kStage];
-    int32_t r_ct[kStage];
-    float r_cl[kStage];
+    // (into registers now as 16-byte vectors, into LDS after the state is
+    // computed; a table whose rows are not a multiple of 4 entries long is
+    // staged element by element below)
+    constexpr int kStageV = kStage / 4;
+    const bool tvec = (LM & 3) == 0;
+    i32x4 r_ti[kStageV], r_ct[kStageV];
+    f32x4 r_tv[kStageV], r_cl[kStageV];
     const int32_t* ti = a.tidx + (size_t)b * LM;
     const float* tv = a.tval + (size_t)b * LM;
+    const int32_t* kt = a.child_tok + slot0 * kMaxM;
+    const float* kl = a.child_lp + slot0 * kMaxM;
     const int nkid = step * kMaxM;
 #pragma unroll
-    for (int u = 0; u < kStage; ++u) {
-        const int i = threadIdx.x + u * kNodeThreads;
-        r_ti[u] = i < LM ? ti[i] : 0;
-        r_tv[u] = i < LM ? tv[i] : 0.f;
-        r_ct[u] = i < nkid ? a.child_tok[slot0 * kMaxM + i] : 0;
-        r_cl[u] = i < nkid ? a.child_lp[slot0 * kMaxM + i] : 0.f;
+    for (int u = 0; u < kStageV; ++u) {
+        const int e = ((int)threadIdx.x + u * kNodeThreads) * 4;
+        const bool te = tvec && e < LM, ke = e < nkid;
+        r_ti[u] = te ? *reinterpret_cast<const i32x4*>(ti + e) : i32x4{0, 0, 0, 0};
+        r_tv[u] = te ? *reinterpret_cast<const f32x4*>(tv + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+        r_ct[u] = ke ? *reinterpret_cast<const i32x4*>(kt + e) : i32x4{0, 0, 0, 0};
+        r_cl[u] = ke ? *reinterpret_cast<const f32x4*>(kl + e) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float r_sc = 0.f;
     int r_par = -1;
@@ -310,16 +319,15 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         r_sc = a.scores[slot0 + threadIdx.x];
         r_par = a.parents[slot0 + threadIdx.x];
     }
-    // per-request state (scalar loads)
-    const int cnt_m = a.count[b], gtok_m = a.gru_tok[b], depth_m = a.depths[slot0 + step];
-    const int qs_m = a.qsize[b];
-    const uint32_t flag_m = a.flags[b];
-    const int cnt = step == 0 ? 0 : cnt_m;
-    const int gtok = step == 0 ? 0 : gtok_m;
-    const int depth = step == 0 ? 0 : depth_m;
+    // per-request state left by the previous step (one record)
+    const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
+    const int rs_depth = a.rstate[(size_t)b * kStateWords + 4];
+    const int cnt = step == 0 ? 0 : rs0[0];
+    const int gtok = step == 0 ? 0 : rs0[1];
+    int qs = step == 0 ? 0 : rs0[2];
+    uint32_t flag = step == 0 ? 0u : (uint32_t)rs0[3];
+    const int depth = step == 0 ? 0 : rs_depth;
     u64 q = step == 0 ? 0ull : q_m;
-    int qs = step == 0 ? 0 : qs_m;
-    uint32_t flag = step == 0 ? 0u : flag_m;
     const bool expand = step == 0 || (cnt == step && gtok >= 0);
 
     // ---- 2. the state of slot `step`, 4 elements per thread and pass (the
@@ -359,34 +367,38 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                 hv[e] = gru_cell_b(sum[0][e], sum[1][e], sum[2][e], sum[3][e], bias[0][e], bias[1][e],
                                    bias[2][e], bias[3][e], bias[4][e], bias[5][e], hp[e]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hs[kk + e] = hv[e];
+        *reinterpret_cast<f32x4*>(hs + kk) = f32x4{hv[0], hv[1], hv[2], hv[3]};
         if (expand) {
-            float* hdst = a.hstate + (slot0 + step) * H;
+            if (a.hstate)  // binary32 state (read by the binary32 contraction)
+                *reinterpret_cast<f32x4*>(a.hstate + (slot0 + step) * H + kk) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+            if (a.hsplit) {  // its exact bf16 parts (read by the bf16 contraction)
+                uint32_t parts[4][3];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hdst[kk + e] = hv[e];
-            if (a.hsplit) {
-                uint16_t* pdst = a.hsplit + (slot0 + step) * 3 * (size_t)H;
+                for (int e = 0; e < 4; ++e) split3_bf16(hv[e], parts[e]);
+                uint16_t* pdst = a.hsplit + (slot0 + step) * 3 * (size_t)H + kk;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t parts[3];
-                    split3_bf16(hv[e], parts);
-#pragma unroll
-                    for (int qq = 0; qq < 3; ++qq) pdst[(size_t)qq * H + kk + e] = (uint16_t)parts[qq];
-                }
+                for (int qq = 0; qq < 3; ++qq)
+                    *reinterpret_cast<uint2*>(pdst + (size_t)qq * H) =
+                        uint2{parts[0][qq] | (parts[1][qq] << 16), parts[2][qq] | (parts[3][qq] << 16)};
             }
         }
     }
 #pragma unroll
-    for (int u = 0; u < kStage; ++u) {
-        const int i = threadIdx.x + u * kNodeThreads;
-        if (i < LM) {
-            s_tidx[i] = r_ti[u];
-            s_tval[i] = r_tv[u];
+    for (int u = 0; u < kStageV; ++u) {
+        const int e = ((int)threadIdx.x + u * kNodeThreads) * 4;
+        if (tvec && e < LM) {
+            *reinterpret_cast<i32x4*>(s_tidx + e) = r_ti[u];
+            *reinterpret_cast<f32x4*>(s_tval + e) = r_tv[u];
         }
-        if (i < nkid) {
-            s_ctok[i] = r_ct[u];
-            s_clp[i] = r_cl[u];
+        if (e < nkid) {
+            *reinterpret_cast<i32x4*>(s_ctok + e) = r_ct[u];
+            *reinterpret_cast<f32x4*>(s_clp + e) = r_cl[u];
+        }
+    }
+    if (!tvec) {
+        for (int e = threadIdx.x; e < LM; e += kNodeThreads) {
+            s_tidx[e] = ti[e];
+            s_tval[e] = tv[e];
         }
     }
     if ((int)threadIdx.x <= step) {
@@ -457,6 +469,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     int new_cnt = cnt;
     int v_par = -1;
+    int next_depth = 0, next_tok = -1;
     if (cnt == step && qs > 0) {
         const u64 top = wave_max_u64(q);
         const int holder = (int)__builtin_ctzll(__ballot(q == top));
@@ -491,6 +504,8 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         const int v = step + 1;
         new_cnt = v;
         v_par = pp;
+        next_depth = pd;
+        next_tok = pd < a.L && v < a.n ? ptok : -1;
         if (lane == 0) {
             a.tokens[slot0 + v] = ptok;
             a.parents[slot0 + v] = pp;
@@ -511,7 +526,9 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     a.queue[(size_t)b * kWave + lane] = q;
     if (lane == 0) {
-        a.qsize[b] = qs;
+        int32_t* rs = a.rstate + (size_t)b * kStateWords;
+        *reinterpret_cast<i32x4*>(rs) = i32x4{new_cnt, next_tok, qs, (int)flag};
+        *reinterpret_cast<i32x4*>(rs + 4) = i32x4{next_depth, 0, 0, 0};
         a.count[b] = new_cnt;
         a.flags[b] = flag;
     }
