@@ -32,13 +32,32 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16
 MFMA_FP32_PEAK_TFS = 157.3
 
 
+def topm_traffic():
+    """HBM bytes per top-M select launch from the committed counter summary,
+    or None when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", "topm_select_qwen3_4b_batched_pmc.md")).read()
+    except OSError:
+        return None
+    m = re.search(r"topm_traffic_bytes=(\d+) source_sha256=([0-9a-f]{64})", text)
+    if not m:
+        return None
+    h = hashlib.sha256()
+    for f in ("topm.hip", "dt_device.h"):
+        with open(os.path.join(ROOT, "conditional_draft_tree_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(m.group(1)) if h.hexdigest() == m.group(2) else None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="qwen3_4b_batched")
-    p.add_argument("--cpu-requests", type=int, default=32,
+    p.add_argument("--cpu-requests", type=int, default=64,
                    help="requests in the CPU oracle sample (0 = skip)")
     p.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, cpu count)")
     p.add_argument("--stage-steps", type=int, default=10, help="steps of the per-kernel timing pass")
@@ -158,7 +177,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": topm_traffic() if args.config == "qwen3_4b_batched" else None,
             "algorithmic_bytes_per_launch": topm_bytes,
             "mean_launch_ms": round(sel_mean, 5),
             "launches": len(sel_ms),
