@@ -21,7 +21,7 @@ thread_local char g_create_error[512] = "";
 
 struct Layout {
     size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
-        rstate;
+        rstate, xpack, hpack;
     size_t total;
 };
 
@@ -89,6 +89,8 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.queue = take(B * 64 * sizeof(u64));
     l.rstate = take(B * dt::kStateWords * 4);
     l.nidx = take(B * 64 * 4);
+    l.xpack = take(c.dtype == DT_BF16 ? (size_t)dt::pack_rows(c.B) * c.E * 2 : 0);
+    l.hpack = take(c.dtype == DT_BF16 ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
     l.nval = take(B * 64 * 4);
     l.total = off;
     return l;
@@ -278,9 +280,10 @@ dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, co
     hipStream_t st = (hipStream_t)stream;
     char* w = (char*)ws;
     dt::GruGatesArgs g{};
+    g.xpack = (uint16_t*)(w + h->lay.xpack);
+    g.hpack = (uint16_t*)(w + h->lay.hpack);
     g.x = x;
     g.xtok = nullptr;
-    g.hsplit = (uint16_t*)(w + h->lay.hsplit);
     g.hf = h_in;
     g.hrows = 1;
     g.hsel = nullptr;
@@ -293,8 +296,9 @@ dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, co
     g.ksplit = h->ksplit;
     g.dtype = (int)c.dtype;
     hipError_t e = hipSuccess;
-    if (c.dtype == DT_BF16) e = dt::launch_split(h_in, (uint16_t*)g.hsplit, c.B, c.H, st);
-    if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step split launch");
+    if (c.dtype == DT_BF16)
+        e = dt::launch_pack((const uint16_t*)x, h_in, (uint16_t*)g.xpack, (uint16_t*)g.hpack, c.B, c.E, c.H, st);
+    if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step packing launch");
     e = dt::launch_gru_gates(g, st);
     if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step contraction launch");
     e = dt::launch_finalize(g.partial, g.ksplit, b_ih, b_hh, h_out, c.B, c.H, (int)c.dtype, st);
@@ -381,13 +385,17 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.rstate = (int32_t*)(w + L.rstate);
     a.nidx = (int32_t*)(w + L.nidx);
     a.nval = (float*)(w + L.nval);
+    a.emb = emb;
+    a.xpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.xpack) : nullptr;
+    a.hpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.hpack) : nullptr;
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
     a.mask = mask; a.count = count; a.flags = flags;
 
     dt::GruGatesArgs g{};
+    g.xpack = a.xpack;
+    g.hpack = a.hpack;
     g.x = emb;
     g.xtok = a.gru_tok;
-    g.hsplit = a.hsplit;
     g.hf = a.hstate;
     g.hrows = c.n + 1;
     g.hsel = a.gru_par;

@@ -18,16 +18,19 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
                        int32_t* idx, float* val, hipStream_t stream, hipEvent_t ev_mid);
 
 // ---- GRU gate contraction (gru.hip) -----------------------------------------
-// For every row b < B: x = x + xrow(b) * E with xrow(b) = xtok ? xtok[b] : b
-// (a negative xtok[b] marks an idle row); its state is number
-// state_index(b) = b * hrows + (hsel ? hsel[b] : 0) of `hsplit` (bf16, [3][H]
-// per state: its exact three-part split; bf16 path) or `hf` (binary32, [H]
-// per state; binary32 path).  Writes the K-range partial sums and the
-// previous state to `partial` ([ksplit][B][kGateSlots][H], see dt_device.h).
+// bf16 path: the activations come packed for the MFMA operands (see
+// pack_index_x / pack_index_h): row b's embedding in `xpack` and the exact
+// three-part bf16 split of its previous state in `hpack` (idle rows are
+// zero).  binary32 path: row b reads x + xrow(b) * E with xrow(b) = xtok ?
+// xtok[b] : b (a negative xtok[b] marks an idle row) and state number
+// b * hrows + (hsel ? hsel[b] : 0) of `hf` ([H] per state).  Both write the
+// K-range partial sums and the previous state to `partial`
+// ([ksplit][B][kGateSlots][H], see dt_device.h).
 struct GruGatesArgs {
+    const uint16_t* xpack;
+    const uint16_t* hpack;
     const void* x;
     const int32_t* xtok;
-    const uint16_t* hsplit;
     const float* hf;
     int hrows;
     const int32_t* hsel;
@@ -36,14 +39,27 @@ struct GruGatesArgs {
     float* partial;
     int B, E, H, ksplit, dtype;
 };
+// Packed activations (bf16 elements).  Rows are grouped in blocks of 16 (the
+// MFMA operand rows); a block's K range is cut into 32-wide chunks; one chunk
+// of one block is 16 rows x 32 elements = 1 KB, contiguous, so a wave loads an
+// operand tile with one contiguous 1 KB read.  Row blocks are allocated for
+// B rounded up to 64 rows.
+__host__ __device__ inline size_t pack_index_x(int b, int k, int E) {
+    return ((size_t)((b >> 4) * (E >> 5) + (k >> 5)) * 16 + (b & 15)) * 32 + (k & 31);
+}
+__host__ __device__ inline size_t pack_index_h(int b, int part, int k, int H) {
+    return ((size_t)(((b >> 4) * 3 + part) * (H >> 5) + (k >> 5)) * 16 + (b & 15)) * 32 + (k & 31);
+}
+inline int pack_rows(int B) { return (B + 63) / 64 * 64; }
 __device__ __forceinline__ size_t state_index(const GruGatesArgs& a, int b) {
     return (size_t)b * a.hrows + (size_t)(a.hsel ? a.hsel[b] : 0);
 }
 int gru_ksplit(int B, int E, int H, int dtype);
 constexpr int kGateSlotsHost = 5;  // == kGateSlots (dt_device.h)
 hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream);
-// h [B, H] -> [B, 3, H] exact bf16 parts
-hipError_t launch_split(const float* h, uint16_t* parts, int B, int H, hipStream_t stream);
+// x [B, E] bf16 and h [B, H] binary32 -> packed activations (rows B .. pack_rows(B) zero)
+hipError_t launch_pack(const uint16_t* x, const float* h, uint16_t* xpack, uint16_t* hpack, int B, int E,
+                       int H, hipStream_t stream);
 // h_out [B, H] from the partial sums
 hipError_t launch_finalize(const float* partial, int ksplit, const void* b_ih, const void* b_hh,
                            float* h_out, int B, int H, int dtype, hipStream_t stream);
@@ -76,6 +92,9 @@ struct NodeArgs {
                          // count, next GRU token, queue size, flags, depth of the next slot
     int32_t* nidx;       // [B, 64] candidate tokens of the slot expanded next
     float* nval;         // [B, 64] their base logits
+    const void* emb;     // [V, E] token embeddings
+    uint16_t* xpack;     // packed activations of the next contraction (bf16 path; see
+    uint16_t* hpack;     // pack_index_x / pack_index_h), NULL on the binary32 path
     // outputs
     int32_t* tokens;
     int32_t* parents;

@@ -203,10 +203,10 @@ __device__ __forceinline__ float wave_rowsum16(const float (&acc)[kRowsPerWave])
 }
 
 // Wave 0: z = base logit + correction dot, temperature, log-softmax over the
-// M-slice, children sorted by (log-prob desc, token asc).  Lane j holds
-// candidate j's token, base logit and dot; lane r returns the rank-r child
-// (key 0 when r >= M).
-__device__ __forceinline__ u64 sorted_children_r(float val, float dot, int tok, int M, float temp) {
+// M-slice; lane j holds candidate j's token, base logit and dot and returns
+// its child key (log-prob desc, token asc; 0 when j >= M).  Sorted across
+// the wave, lane r holds the rank-r child.
+__device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M, float temp) {
     const int lane = lane_id();
     const bool on = lane < M;
     float zz = on ? val + dot : -INFINITY;
@@ -215,8 +215,7 @@ __device__ __forceinline__ u64 sorted_children_r(float val, float dot, int tok, 
     const float e = on ? expf(zz - m) : 0.f;
     const float ssum = wave_sum(e);
     const float lp = (zz - m) - logf(ssum);
-    u64 key = on ? child_key(lp, tok) : 0ull;
-    return wave_sort_desc(key);
+    return on ? child_key(lp, tok) : 0ull;
 }
 
 template <typename T, int KS>
@@ -432,19 +431,108 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         if ((lane & 3) == 0) zs[wave * kRowsPerWave + (lane >> 2)] = d;
     }
     __syncthreads();
-    if (wave != 0) return;
+    // ---- 3. queue.  Wave 0 first takes the pop decision, which needs only the
+    // best child of slot `step` (the largest child key), then hands the
+    // popped node to waves 1-3, which pack the next contraction's activations
+    // while wave 0 sorts the children and updates the queue.
+    __shared__ int s_dec[2];  // next GRU token (-1 = idle row), parent slot of the popped node
+    const float score_step = s_sc[step];
+    u64 ckey = 0ull, best = 0ull, top = 0ull;
+    int new_cnt = cnt;
+    int v_par = -1, pd = 0, pr = 0, ptok = -1;
+    int next_depth = 0, next_tok = -1;
+    float psc = 0.f;
+    const bool pop = wave == 0 && cnt == step && (qs > 0 || expand);
+    if (wave == 0) {
+        if (expand) {
+            ckey = child_keys_r(my_val, zs[lane], my_tok, a.M, a.temp);
+            best = wave_max_u64(ckey);  // the rank-0 child
+            const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
+            if (lane == qs) q = key;
+            ++qs;
+        }
+        if (pop) {
+            top = wave_max_u64(q);
+            pd = qk_depth(top);
+            v_par = qk_parent(top);
+            pr = qk_rank(top);
+            psc = qk_score(top);
+            // a child of slot `step` in the queue is its rank-0 child, pushed just now
+            ptok = v_par == step ? child_tok_of(best) : s_ctok[v_par * kMaxM + pr];
+            const int v = step + 1;
+            new_cnt = v;
+            next_depth = pd;
+            next_tok = pd < a.L && v < a.n ? ptok : -1;
+        }
+        if (lane == 0) {
+            s_dec[0] = next_tok;
+            s_dec[1] = v_par;
+        }
+    }
+    __syncthreads();
 
+    if (wave != 0) {
+        // ---- 4. row b's activations of the next contraction, packed for its
+        // MFMA operands: the popped node's token embedding (wave 1) and its
+        // parent's state in three exact bf16 parts (waves 2-3); zeros for an
+        // idle row.  The parent is slot `step` (state in LDS) or an older slot
+        // (parts in hsplit).
+        if (a.xpack && step + 1 < a.n) {
+            const int ntok = s_dec[0], par = s_dec[1];
+            const bool grow = ntok >= 0;
+            if (wave == 1) {
+                const int nxc = a.E >> 5;
+                for (int c = lane; c < nxc; c += kWave) {
+                    u32x4 v[4] = {};
+                    if (grow) {
+                        const bf16_t* src = (const bf16_t*)a.emb + (size_t)ntok * a.E + c * 32;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const u32x4*>(src + 8 * e);
+                    }
+                    uint16_t* dst = a.xpack + pack_index_x(b, c * 32, a.E);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(dst + 8 * e) = v[e];
+                }
+            } else {
+                const int nhc = H >> 5;
+                for (int it = (wave - 2) * kWave + lane; it < 3 * nhc; it += 2 * kWave) {
+                    const int qq = it / nhc, c = it - qq * nhc;
+                    uint32_t w[16] = {};  // 32 elements of part qq, two per word
+                    if (grow && par == step) {
+#pragma unroll
+                        for (int e = 0; e < 32; ++e) {
+                            uint32_t p3[3];
+                            split3_bf16(hs[c * 32 + e], p3);
+                            w[e >> 1] |= (qq == 0 ? p3[0] : qq == 1 ? p3[1] : p3[2]) << (16 * (e & 1));
+                        }
+                    } else if (grow) {
+                        const uint16_t* src = a.hsplit + ((slot0 + par) * 3 + qq) * (size_t)H + c * 32;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const u32x4 t4 = *reinterpret_cast<const u32x4*>(src + 8 * e);
+                            w[4 * e] = t4.x; w[4 * e + 1] = t4.y; w[4 * e + 2] = t4.z; w[4 * e + 3] = t4.w;
+                        }
+                    }
+                    uint16_t* dst = a.hpack + pack_index_h(b, qq, c * 32, H);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        *reinterpret_cast<u32x4*>(dst + 8 * e) = u32x4{w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]};
+                }
+            }
+        }
+        return;
+    }
+
+    // wave 0: slot `step`'s sorted children
     u64 kids = 0ull;  // lane r: rank-r child of slot `step`
     if (expand) {
-        kids = sorted_children_r(my_val, zs[lane], my_tok, a.M, a.temp);
+        kids = wave_sort_desc(ckey);
         const size_t crow = (slot0 + step) * kMaxM;
         if (lane < a.M) {
             a.child_tok[crow + lane] = child_tok_of(kids);
             a.child_lp[crow + lane] = child_lp_of(kids);
         }
     }
-
-    // ---- 3. queue: push slot `step`'s best child, pop, push the sibling
     if (step == 0) {
         for (int i = lane; i < S; i += kWave) {
             if (i == 0) {
@@ -460,38 +548,18 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
             }
         }
     }
-    const float score_step = s_sc[step];
-    if (expand) {
-        const u64 best = bcast_u64(kids, 0);
-        const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
-        if (lane == qs) q = key;
-        ++qs;
-    }
-    int new_cnt = cnt;
-    int v_par = -1;
-    int next_depth = 0, next_tok = -1;
-    if (cnt == step && qs > 0) {
-        const u64 top = wave_max_u64(q);
+    if (pop) {
+        // remove the popped entry, push its next-ranked sibling
         const int holder = (int)__builtin_ctzll(__ballot(q == top));
         const u64 last = bcast_u64(q, qs - 1);
         if (lane == holder) q = last;
         if (lane == qs - 1) q = 0ull;
         --qs;
-
-        const int pd = qk_depth(top), pp = qk_parent(top), pr = qk_rank(top);
-        const float psc = qk_score(top);
         const bool has_sib = pr + 1 < a.M;
-        int ptok;
-        float sib_lp;
-        if (pp == step) {  // a child of the slot expanded just now: in registers
-            ptok = child_tok_of(bcast_u64(kids, pr));
-            sib_lp = child_lp_of(bcast_u64(kids, min(pr + 1, kWave - 1)));
-        } else {
-            ptok = s_ctok[pp * kMaxM + pr];
-            sib_lp = s_clp[pp * kMaxM + min(pr + 1, kMaxM - 1)];
-        }
+        const float sib_lp = v_par == step ? child_lp_of(bcast_u64(kids, min(pr + 1, kWave - 1)))
+                                           : s_clp[v_par * kMaxM + min(pr + 1, kMaxM - 1)];
         if (has_sib) {
-            const u64 key = queue_key(s_sc[pp] + sib_lp, pd, pp, pr + 1);
+            const u64 key = queue_key(s_sc[v_par] + sib_lp, pd, v_par, pr + 1);
             if (lane == qs) q = key;
             ++qs;
         }
@@ -502,20 +570,15 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
             if (__ballot(lane < qs && gap > 0.f && gap < a.eps)) flag |= 1u;
         }
         const int v = step + 1;
-        new_cnt = v;
-        v_par = pp;
-        next_depth = pd;
-        next_tok = pd < a.L && v < a.n ? ptok : -1;
         if (lane == 0) {
             a.tokens[slot0 + v] = ptok;
-            a.parents[slot0 + v] = pp;
+            a.parents[slot0 + v] = v_par;
             a.depths[slot0 + v] = pd;
             a.scores[slot0 + v] = psc;
-            const bool grow = pd < a.L && v < a.n;
-            a.gru_tok[b] = grow ? ptok : -1;
-            a.gru_par[b] = pp;
+            a.gru_tok[b] = next_tok;
+            a.gru_par[b] = v_par;
         }
-        if (pd < a.L && v < a.n) {  // the next step expands v: hand over its candidates
+        if (next_tok >= 0) {  // the next step expands v: hand over its candidates
             const int jm = min(lane, a.M - 1);
             a.nidx[(size_t)b * kWave + lane] = s_tidx[pd * a.M + jm];
             a.nval[(size_t)b * kWave + lane] = s_tval[pd * a.M + jm];

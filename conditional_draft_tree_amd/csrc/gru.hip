@@ -86,21 +86,19 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
     const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
     const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
     const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    const size_t H3 = (size_t)3 * a.H;
-    const bf16_t* xrow[kRowBlocks];
-    const bf16_t* hrow[kRowBlocks];
-    bool xok[kRowBlocks];
+    // packed activations: lane l reads row l % 16 of its row block at K offset
+    // 8 * (l / 16) of a chunk; a wave's read is one contiguous 1 KB block.
+    // Rows past B read the last row (their sums are not stored).
+    const bf16_t* xblk[kRowBlocks];
+    const bf16_t* hblk[kRowBlocks];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rg * 64 + rb * 16 + (lane & 15);
-        const bool in = r < a.B;
-        const int xr = in ? (a.xtok ? a.xtok[r] : r) : -1;
-        const int hs = in && a.hsel ? a.hsel[r] : 0;
-        xok[rb] = xr >= 0;  // rows past B and idle rows contribute zeros
-        xrow[rb] = (const bf16_t*)a.x + (size_t)(xok[rb] ? xr : 0) * a.E;
-        hrow[rb] = a.hsplit + (xok[rb] ? ((size_t)r * a.hrows + hs) * H3 : 0);
+        const int r = min(rg * 64 + rb * 16 + (lane & 15), a.B - 1);
+        xblk[rb] = (const bf16_t*)a.xpack + pack_index_x(r, 0, a.E) + kq;
+        hblk[rb] = (const bf16_t*)a.hpack + pack_index_h(r, 0, 0, a.H) + kq;
     }
+    const size_t xstep = 16 * 32;                  // one chunk of one block
+    const size_t hpart = (size_t)nH * 16 * 32;     // one part of one block
 
     f32x4 acc[kRowBlocks][4];
 #pragma unroll
@@ -118,8 +116,9 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                 const int k = (cb + min(i, n - 1)) * 32 + kq;  // clamped: always in bounds
 #pragma unroll
                 for (int g = 0; g < 3; ++g) w[i][g] = load_bf16x8(wi + g * gi + k);
+                const size_t c = (size_t)(cb + min(i, n - 1));
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) x[i][rb] = xok[rb] ? load_bf16x8(xrow[rb] + k) : zero;
+                for (int rb = 0; rb < kRowBlocks; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
             }
 #pragma unroll
             for (int i = 0; i < kMaxXChunks; ++i) {
@@ -143,11 +142,12 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                 const int k = (cb + min(i, n - 1) - nE) * 32 + kq;
 #pragma unroll
                 for (int g = 0; g < 3; ++g) w[i][g] = load_bf16x8(wh + g * gh + k);
+                const size_t c = (size_t)(cb + min(i, n - 1) - nE);
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
                     for (int q = 0; q < 3; ++q)
-                        hp[i][rb][q] = xok[rb] ? load_bf16x8(hrow[rb] + q * a.H + k) : zero;
+                        hp[i][rb][q] = load_bf16x8(hblk[rb] + q * hpart + c * xstep);
             }
 #pragma unroll
             for (int i = 0; i < kMaxHChunks; ++i) {
@@ -194,12 +194,9 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
             const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (row, unit) of 64 x 16
             const int row = rg * 64 + (idx >> 4), u = ut * 16 + (idx & 15);
             if (row >= a.B) continue;
-            const int xr = a.xtok ? a.xtok[row] : row;
-            float hpv = 0.f;
-            if (xr >= 0) {
-                const bf16_t* hs = a.hsplit + state_index(a, row) * H3 + u;
-                hpv = (bf16_to_f32(hs[0]) + bf16_to_f32(hs[a.H])) + bf16_to_f32(hs[2 * a.H]);
-            }
+            const bf16_t* hs = (const bf16_t*)a.hpack + pack_index_h(row, 0, u, a.H);
+            const size_t hpart = (size_t)nH * 16 * 32;
+            const float hpv = (bf16_to_f32(hs[0]) + bf16_to_f32(hs[hpart])) + bf16_to_f32(hs[2 * hpart]);
             a.partial[((size_t)row * kGateSlots + 4) * a.H + u] = hpv;
         }
     }
@@ -241,13 +238,18 @@ __global__ __launch_bounds__(64) void gru_gates_f32_kernel(GruGatesArgs a) {
     out[(size_t)4 * a.H] = h[j];
 }
 
-// h [B, H] binary32 -> its exact three-part bf16 split [B, 3, H].
-__global__ __launch_bounds__(256) void split_kernel(const float* h, bf16_t* parts, int B, int H) {
+// x [B, E] bf16 and h [B, H] binary32 -> packed activations; rows B .. of the
+// last 64-row group are zero.
+__global__ __launch_bounds__(256) void pack_kernel(const bf16_t* x, const float* h, bf16_t* xpack,
+                                                   bf16_t* hpack, int B, int E, int H) {
     const int b = blockIdx.x;
+    const bool in = b < B;
+    for (int k = threadIdx.x; k < E; k += blockDim.x)
+        xpack[pack_index_x(b, k, E)] = in ? x[(size_t)b * E + k] : (bf16_t)0;
     for (int k = threadIdx.x; k < H; k += blockDim.x) {
-        uint32_t p[3];
-        split3_bf16(h[(size_t)b * H + k], p);
-        for (int s = 0; s < 3; ++s) parts[((size_t)b * 3 + s) * H + k] = (bf16_t)p[s];
+        uint32_t p[3] = {0u, 0u, 0u};
+        if (in) split3_bf16(h[(size_t)b * H + k], p);
+        for (int s = 0; s < 3; ++s) hpack[pack_index_h(b, s, k, H)] = (bf16_t)p[s];
     }
 }
 
@@ -289,9 +291,10 @@ hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_split(const float* h, bf16_t* parts, int B, int H, hipStream_t stream) {
+hipError_t launch_pack(const uint16_t* x, const float* h, uint16_t* xpack, uint16_t* hpack, int B, int E,
+                       int H, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    split_kernel<<<B, 256, 0, stream>>>(h, parts, B, H);
+    pack_kernel<<<pack_rows(B), 256, 0, stream>>>((const bf16_t*)x, h, (bf16_t*)xpack, (bf16_t*)hpack, B, E, H);
     return hipGetLastError();
 }
 
