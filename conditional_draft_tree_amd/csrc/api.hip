@@ -301,7 +301,7 @@ dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, co
     if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step packing launch");
     e = dt::launch_gru_gates(g, st);
     if (e != hipSuccess) return hip_fail(h, e, "dt_gru_step contraction launch");
-    e = dt::launch_finalize(g.partial, g.ksplit, b_ih, b_hh, h_out, c.B, c.H, (int)c.dtype, st);
+    e = dt::launch_finalize(g.partial, g.ksplit, b_ih, b_hh, h_in, h_out, c.B, c.H, (int)c.dtype, st);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_gru_step update launch");
 }
 

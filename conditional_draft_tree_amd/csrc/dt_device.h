@@ -253,22 +253,20 @@ __device__ __forceinline__ float gru_cell(float sr, float sz, float snx, float s
 }
 
 // Partial-sum buffer of the gate contraction: [ksplit][B][kGateSlots][H],
-// slots 0 reset, 1 update, 2 candidate (x part), 3 candidate (h part), 4 the
-// previous state (K range 0 only).
-constexpr int kGateSlots = 5;
+// slots 0 reset, 1 update, 2 candidate (x part), 3 candidate (h part).
+constexpr int kGateSlots = 4;
 constexpr int kMaxKsplit = 6;  // K ranges of the gate contraction
 
 // New state of (row b, unit k): the K-range partials added in K order.
 __device__ __forceinline__ float gru_from_partials(const float* partial, int ksplit, int B, int b,
                                                    int H, int k, const void* b_ih, const void* b_hh,
-                                                   int dtype) {
+                                                   int dtype, float hprev) {
     float t[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < ksplit; ++s) {
         const float* p = partial + ((size_t)(s * B + b) * kGateSlots) * H + k;
 #pragma unroll
         for (int g = 0; g < 4; ++g) t[g] += p[(size_t)g * H];
     }
-    const float hprev = partial[((size_t)b * kGateSlots + 4) * H + k];
     return gru_cell(t[0], t[1], t[2], t[3], b_ih, b_hh, dtype, H, k, hprev);
 }
 

@@ -24,8 +24,8 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
 // zero).  binary32 path: row b reads x + xrow(b) * E with xrow(b) = xtok ?
 // xtok[b] : b (a negative xtok[b] marks an idle row) and state number
 // b * hrows + (hsel ? hsel[b] : 0) of `hf` ([H] per state).  Both write the
-// K-range partial sums and the previous state to `partial`
-// ([ksplit][B][kGateSlots][H], see dt_device.h).
+// K-range partial sums to `partial` ([ksplit][B][kGateSlots][H], see
+// dt_device.h); the consumer supplies the previous state itself.
 struct GruGatesArgs {
     const uint16_t* xpack;
     const uint16_t* hpack;
@@ -55,14 +55,14 @@ __device__ __forceinline__ size_t state_index(const GruGatesArgs& a, int b) {
     return (size_t)b * a.hrows + (size_t)(a.hsel ? a.hsel[b] : 0);
 }
 int gru_ksplit(int B, int E, int H, int dtype);
-constexpr int kGateSlotsHost = 5;  // == kGateSlots (dt_device.h)
+constexpr int kGateSlotsHost = 4;  // == kGateSlots (dt_device.h)
 hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream);
 // x [B, E] bf16 and h [B, H] binary32 -> packed activations (rows B .. pack_rows(B) zero)
 hipError_t launch_pack(const uint16_t* x, const float* h, uint16_t* xpack, uint16_t* hpack, int B, int E,
                        int H, hipStream_t stream);
-// h_out [B, H] from the partial sums
+// h_out [B, H] from the partial sums and the previous state h [B, H]
 hipError_t launch_finalize(const float* partial, int ksplit, const void* b_ih, const void* b_hh,
-                           float* h_out, int B, int H, int dtype, hipStream_t stream);
+                           const float* h, float* h_out, int B, int H, int dtype, hipStream_t stream);
 
 // ---- expansion (expand.hip) -------------------------------------------------
 constexpr int kStateWords = 8;

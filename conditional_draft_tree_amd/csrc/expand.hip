@@ -259,7 +259,6 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kc);
-    f32x4 hp = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)b * kGateSlots + 4) * H + kc);
     f32x4 bias[6];
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
@@ -320,7 +319,25 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     // per-request state left by the previous step (one record)
     const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
-    const int rs_depth = a.rstate[(size_t)b * kStateWords + 4];
+    const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
+    const int rs_depth = rs1[0];
+    // the parent's state (the GRU's previous state), exact: binary32, or the sum
+    // of its three bf16 parts
+    const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
+    auto parent_state = [&](int kk) {
+        if (a.hsplit) {
+            const uint16_t* src = a.hsplit + ((slot0 + par) * 3) * (size_t)H + kk;
+            const uint2 p0 = *reinterpret_cast<const uint2*>(src);
+            const uint2 p1 = *reinterpret_cast<const uint2*>(src + H);
+            const uint2 p2 = *reinterpret_cast<const uint2*>(src + 2 * (size_t)H);
+            auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+            auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+            return f32x4{(lo(p0.x) + lo(p1.x)) + lo(p2.x), (hi(p0.x) + hi(p1.x)) + hi(p2.x),
+                         (lo(p0.y) + lo(p1.y)) + lo(p2.y), (hi(p0.y) + hi(p1.y)) + hi(p2.y)};
+        }
+        return *reinterpret_cast<const f32x4*>(a.hstate + (slot0 + par) * H + kk);
+    };
+    f32x4 hp = parent_state(kc);
     const int cnt = step == 0 ? 0 : rs0[0];
     const int gtok = step == 0 ? 0 : rs0[1];
     int qs = step == 0 ? 0 : rs0[2];
@@ -339,7 +356,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
                     t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kk);
-            hp = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)b * kGateSlots + 4) * H + kk);
+            hp = parent_state(kk);
 #pragma unroll
             for (int g = 0; g < 6; ++g) {
                 const void* bp = g < 3 ? a.b_ih : a.b_hh;
@@ -478,7 +495,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         // idle row.  The parent is slot `step` (state in LDS) or an older slot
         // (parts in hsplit).
         if (a.xpack && step + 1 < a.n) {
-            const int ntok = s_dec[0], par = s_dec[1];
+            const int ntok = s_dec[0], vpar = s_dec[1];
             const bool grow = ntok >= 0;
             if (wave == 1) {
                 const int nxc = a.E >> 5;
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                 for (int it = (wave - 2) * kWave + lane; it < 3 * nhc; it += 2 * kWave) {
                     const int qq = it / nhc, c = it - qq * nhc;
                     uint32_t w[16] = {};  // 32 elements of part qq, two per word
-                    if (grow && par == step) {
+                    if (grow && vpar == step) {
 #pragma unroll
                         for (int e = 0; e < 32; ++e) {
                             uint32_t p3[3];
@@ -506,7 +523,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                             w[e >> 1] |= (qq == 0 ? p3[0] : qq == 1 ? p3[1] : p3[2]) << (16 * (e & 1));
                         }
                     } else if (grow) {
-                        const uint16_t* src = a.hsplit + ((slot0 + par) * 3 + qq) * (size_t)H + c * 32;
+                        const uint16_t* src = a.hsplit + ((slot0 + vpar) * 3 + qq) * (size_t)H + c * 32;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const u32x4 t4 = *reinterpret_cast<const u32x4*>(src + 8 * e);
@@ -591,7 +608,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     if (lane == 0) {
         int32_t* rs = a.rstate + (size_t)b * kStateWords;
         *reinterpret_cast<i32x4*>(rs) = i32x4{new_cnt, next_tok, qs, (int)flag};
-        *reinterpret_cast<i32x4*>(rs + 4) = i32x4{next_depth, 0, 0, 0};
+        *reinterpret_cast<i32x4*>(rs + 4) = i32x4{next_depth, v_par < 0 ? 0 : v_par, 0, 0};
         a.count[b] = new_cnt;
         a.flags[b] = flag;
     }

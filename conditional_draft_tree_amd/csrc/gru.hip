@@ -188,18 +188,6 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
         }
         __syncthreads();
     }
-    if (ks == 0) {  // previous state of (row, unit), rebuilt exactly from its parts
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (row, unit) of 64 x 16
-            const int row = rg * 64 + (idx >> 4), u = ut * 16 + (idx & 15);
-            if (row >= a.B) continue;
-            const bf16_t* hs = (const bf16_t*)a.hpack + pack_index_h(row, 0, u, a.H);
-            const size_t hpart = (size_t)nH * 16 * 32;
-            const float hpv = (bf16_to_f32(hs[0]) + bf16_to_f32(hs[hpart])) + bf16_to_f32(hs[2 * hpart]);
-            a.partial[((size_t)row * kGateSlots + 4) * a.H + u] = hpv;
-        }
-    }
 }
 
 // binary32 path (small configurations): one thread per (row, hidden unit),
@@ -235,7 +223,6 @@ __global__ __launch_bounds__(64) void gru_gates_f32_kernel(GruGatesArgs a) {
     out[(size_t)a.H] = iz + hz;
     out[(size_t)2 * a.H] = in;
     out[(size_t)3 * a.H] = hn;
-    out[(size_t)4 * a.H] = h[j];
 }
 
 // x [B, E] bf16 and h [B, H] binary32 -> packed activations; rows B .. of the
@@ -253,13 +240,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* x, const float*
     }
 }
 
-// h_out[b] = GRU cell from the K-range partial sums of row b.
+// h_out[b] = GRU cell from the K-range partial sums of row b and its state h[b].
 __global__ __launch_bounds__(256) void finalize_kernel(const float* partial, int ksplit,
-                                                       const void* b_ih, const void* b_hh,
+                                                       const void* b_ih, const void* b_hh, const float* h,
                                                        float* h_out, int B, int H, int dtype) {
     const int b = blockIdx.x;
     for (int k = threadIdx.x; k < H; k += blockDim.x)
-        h_out[(size_t)b * H + k] = gru_from_partials(partial, ksplit, B, b, H, k, b_ih, b_hh, dtype);
+        h_out[(size_t)b * H + k] =
+            gru_from_partials(partial, ksplit, B, b, H, k, b_ih, b_hh, dtype, h[(size_t)b * H + k]);
 }
 
 }  // namespace
@@ -299,9 +287,9 @@ hipError_t launch_pack(const uint16_t* x, const float* h, uint16_t* xpack, uint1
 }
 
 hipError_t launch_finalize(const float* partial, int ksplit, const void* b_ih, const void* b_hh,
-                           float* h_out, int B, int H, int dtype, hipStream_t stream) {
+                           const float* h, float* h_out, int B, int H, int dtype, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    finalize_kernel<<<B, 256, 0, stream>>>(partial, ksplit, b_ih, b_hh, h_out, B, H, dtype);
+    finalize_kernel<<<B, 256, 0, stream>>>(partial, ksplit, b_ih, b_hh, h, h_out, B, H, dtype);
     return hipGetLastError();
 }
 
