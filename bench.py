@@ -142,6 +142,17 @@ def main():
     peak_mfma = MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS
     gemm_tfs = gemm_flop / (gemm_each * 1e-3) / 1e12
 
+    # ---- the factorized (marginal) scoring mode on the same logits (extra key)
+    mout = bld.build_marginal(t["base"])
+    for _ in range(3):
+        bld.build_marginal(t["base"], out=mout)
+    torch.cuda.synchronize()
+    m0 = time.perf_counter()
+    for _ in range(args.stage_steps):
+        bld.build_marginal(t["base"], out=mout)
+    torch.cuda.synchronize()
+    marg_us = (time.perf_counter() - m0) * 1e6 / max(args.stage_steps, 1)
+
     if args.copy_calib:  # a plain copy of known size, for counter scaling
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -197,6 +208,8 @@ def main():
         "topm_merge_ms_mean": round(float(np.mean(merge_ms)), 5),
         "call_ms_events_mean": round(float(np.mean(call_ms)), 5),
         "latency_per_request_us": round(ms_per_step * 1e3, 1),
+        "marginal_mode": {"us_per_round": round(marg_us, 1),
+                          "tree_builds_per_s": round(B / (marg_us * 1e-6), 1)},
     }
 
     # ---- CPU baseline: the oracle as it stands, one request per thread

@@ -56,13 +56,16 @@ def load_library():
         # tokens, parents, depths, scores, mask, count, flags, stream
         lib.dt_build.argtypes = [H, vp, C.c_size_t] + [vp] * 7 + [f32p] + [i32p] * 3 + [
             f32p, vp, i32p, vp, vp]
+        # handle, workspace, bytes, base, tokens, parents, depths, scores, mask, count, flags, stream
+        lib.dt_build_marginal.argtypes = [H, vp, C.c_size_t, vp] + [i32p] * 3 + [f32p, vp, i32p, vp, vp]
         lib.dt_topm.argtypes = [H, vp, C.c_size_t, vp, i32p, f32p, vp]
         lib.dt_gru_step.argtypes = [H, vp, C.c_size_t, vp, f32p, vp, vp, vp, vp, f32p, vp]
         lib.dt_correct.argtypes = [H, i32p, f32p, vp, f32p, i32p, i32p, f32p, vp]
         lib.dt_timing_enable.argtypes = [H, C.c_int, C.c_int]
         lib.dt_timing_read.argtypes = [H, C.c_int, C.POINTER(C.c_float), C.c_int,
                                        C.POINTER(C.c_int)]
-        for f in (lib.dt_create, lib.dt_build, lib.dt_topm, lib.dt_gru_step, lib.dt_correct,
+        for f in (lib.dt_create, lib.dt_build, lib.dt_build_marginal, lib.dt_topm, lib.dt_gru_step,
+                  lib.dt_correct,
                   lib.dt_timing_enable, lib.dt_timing_read):
             f.restype = C.c_int
         _lib = lib
@@ -122,6 +125,14 @@ def dt_build(handle, workspace, base, emb, w_ih, w_hh, b_ih, b_hh, Cmat, h0, tok
                         _p(base), _p(emb), _p(w_ih), _p(w_hh), _p(b_ih), _p(b_hh), _p(Cmat), _p(h0),
                         _p(tokens), _p(parents), _p(depths), _p(scores), _p(mask), _p(count),
                         _p(flags), _stream(stream)), handle)
+
+
+def dt_build_marginal(handle, workspace, base, tokens, parents, depths, scores, mask, count, flags,
+                      stream=None):
+    lib = load_library()
+    _check(lib.dt_build_marginal(handle, _p(workspace), workspace.numel() if workspace is not None else 0,
+                                 _p(base), _p(tokens), _p(parents), _p(depths), _p(scores), _p(mask),
+                                 _p(count), _p(flags), _stream(stream)), handle)
 
 
 def dt_topm(handle, workspace, base, idx, val, stream=None):
@@ -227,6 +238,29 @@ class Builder:
         dt_build(self.handle, self.workspace, base, emb, w_ih, w_hh, b_ih, b_hh, Cmat, h0,
                  out["tokens"], out["parents"], out["depths"], out["scores"], out["mask"],
                  out["count"], out["flags"], stream)
+        return out
+
+    def _outputs(self):
+        import torch
+        B, S = self.cfg["B"], self.cfg["n"] + 1
+        dev = self.device
+        return dict(tokens=torch.empty((B, S), dtype=torch.int32, device=dev),
+                    parents=torch.empty((B, S), dtype=torch.int32, device=dev),
+                    depths=torch.empty((B, S), dtype=torch.int32, device=dev),
+                    scores=torch.empty((B, S), dtype=torch.float32, device=dev),
+                    mask=torch.empty((B, S, S), dtype=torch.uint8, device=dev),
+                    count=torch.empty((B,), dtype=torch.int32, device=dev),
+                    flags=torch.empty((B,), dtype=torch.int32, device=dev))
+
+    def build_marginal(self, base, out=None, stream=None):
+        """The factorized (marginal) scoring mode: dt_build with no GRU and no
+        correction."""
+        c = self.cfg
+        self._chk("base", base, (c["B"], c["L"], c["V"]))
+        if out is None:
+            out = self._outputs()
+        dt_build_marginal(self.handle, self.workspace, base, out["tokens"], out["parents"], out["depths"],
+                          out["scores"], out["mask"], out["count"], out["flags"], stream)
         return out
 
     def topm(self, base, stream=None):

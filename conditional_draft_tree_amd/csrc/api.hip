@@ -320,15 +320,19 @@ dt_status dt_correct(dt_handle* h, const int32_t* idx, const float* val, const v
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_correct launch");
 }
 
-dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, const void* emb,
+}  // extern "C"
+
+namespace {
+dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, const void* base, const void* emb,
                    const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
                    const void* C, const float* h0, int32_t* tokens, int32_t* parents, int32_t* depths,
                    float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream) {
     if (!h) return DT_ERR_INVALID_ARG;
     const dt_config& c = h->cfg;
     if (c.B == 0) return DT_OK;
-    if (!base || !emb || !W_ih || !W_hh || !C || !tokens || !parents || !depths || !scores || !mask ||
-        !count || !flags)
+    if (!base || !tokens || !parents || !depths || !scores || !mask || !count || !flags)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_build: null pointer");
+    if (!marginal && (!emb || !W_ih || !W_hh || !C))
         return fail(h, DT_ERR_INVALID_ARG, "dt_build: null pointer (only b_ih, b_hh, h0 may be NULL)");
     if (misaligned(base) || misaligned(emb) || misaligned(W_ih) || misaligned(W_hh) || misaligned(C) ||
         misaligned(h0) || misaligned(b_ih) || misaligned(b_hh))
@@ -368,6 +372,7 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     dt::NodeArgs a{};
     a.B = c.B; a.L = c.L; a.V = c.V; a.E = c.E; a.H = c.H; a.M = c.M; a.n = c.n;
     a.dtype = (int)c.dtype;
+    a.marginal = marginal ? 1 : 0;
     a.temp = c.temperature;
     a.eps = c.near_tie_eps;
     a.C = C; a.h0 = h0;
@@ -386,8 +391,8 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     a.nidx = (int32_t*)(w + L.nidx);
     a.nval = (float*)(w + L.nval);
     a.emb = emb;
-    a.xpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.xpack) : nullptr;
-    a.hpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.hpack) : nullptr;
+    a.xpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.xpack) : nullptr;
+    a.hpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.hpack) : nullptr;
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
     a.mask = mask; a.count = count; a.flags = flags;
 
@@ -409,14 +414,34 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
     DT_TRY(dt::launch_node_step(a, h->lds, 0, st), "node step launch");
     DT_TRY(mark(h, call, 2, 'N', st), "timing event");
     for (int step = 1; step < c.n; ++step) {
-        DT_TRY(dt::launch_gru_gates(g, st), "GRU contraction launch");
-        DT_TRY(mark(h, call, 2, 'G', st), "timing event");
+        if (!marginal) {
+            DT_TRY(dt::launch_gru_gates(g, st), "GRU contraction launch");
+            DT_TRY(mark(h, call, 2, 'G', st), "timing event");
+        }
         DT_TRY(dt::launch_node_step(a, h->lds, step, st), "node step launch");
         DT_TRY(mark(h, call, 2, 'N', st), "timing event");
     }
     DT_TRY(mark(h, call, 1, 'E', st), "timing event");
 #undef DT_TRY
     return DT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, const void* emb,
+                   const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
+                   const void* C, const float* h0, int32_t* tokens, int32_t* parents, int32_t* depths,
+                   float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream) {
+    return build_impl(false, h, ws, ws_bytes, base, emb, W_ih, W_hh, b_ih, b_hh, C, h0, tokens, parents,
+                      depths, scores, mask, count, flags, stream);
+}
+
+dt_status dt_build_marginal(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int32_t* tokens,
+                            int32_t* parents, int32_t* depths, float* scores, uint8_t* mask,
+                            int32_t* count, uint32_t* flags, void* stream) {
+    return build_impl(true, h, ws, ws_bytes, base, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, tokens, parents, depths, scores, mask, count, flags, stream);
 }
 
 }  // extern "C"

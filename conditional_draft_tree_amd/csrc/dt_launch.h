@@ -69,6 +69,7 @@ constexpr int kStateWords = 8;
 struct NodeArgs {
     // problem
     int B, L, V, E, H, M, n, dtype;
+    int marginal;  // 1: factorized scores (no GRU, no correction)
     float temp;  // T > 0 divides the corrected logits; 0 = unscaled
     float eps;
     // inputs

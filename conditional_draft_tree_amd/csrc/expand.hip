@@ -218,7 +218,10 @@ __device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M
     return on ? child_key(lp, tok) : 0ull;
 }
 
-template <typename T, int KS>
+// MARG: factorized (marginal) scoring: the children distribution of every node
+// is the log-softmax of the base logits over its M-slice (no GRU state, no
+// correction).
+template <typename T, int KS, bool MARG>
 __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
     extern __shared__ float lds[];
     float* hs = lds + lp.hs;
@@ -254,18 +257,20 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     const bool kin = k4 < H;
     const int kc = kin ? k4 : 0;
     f32x4 t[KS][4];
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kc);
     f32x4 bias[6];
+    if constexpr (!MARG) {
 #pragma unroll
-    for (int g = 0; g < 6; ++g) {
-        const void* bp = g < 3 ? a.b_ih : a.b_hh;
-        const T* src = bp ? (const T*)bp : (const T*)a.partial;  // any valid address
-        const f32x4 v = load4<T>(src + (size_t)(g % 3) * H + kc);
-        bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kc);
+#pragma unroll
+        for (int g = 0; g < 6; ++g) {
+            const void* bp = g < 3 ? a.b_ih : a.b_hh;
+            const T* src = bp ? (const T*)bp : (const T*)a.partial;  // any valid address
+            const f32x4 v = load4<T>(src + (size_t)(g % 3) * H + kc);
+            bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     // (the scheduler keeps the loads above in flight before the candidate
     // list is waited for)
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
             cv[jj][1] = *reinterpret_cast<const u32x4*>(row + kb);
         }
     };
-    gather(0);
+    if constexpr (!MARG) gather(0);
     // top-M table of this request, children of slots 0 .. step-1, tree so far
     // (into registers now as 16-byte vectors, into LDS after the state is
     // computed; a table whose rows are not a multiple of 4 entries long is
@@ -337,7 +342,8 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         }
         return *reinterpret_cast<const f32x4*>(a.hstate + (slot0 + par) * H + kk);
     };
-    f32x4 hp = parent_state(kc);
+    f32x4 hp = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!MARG) hp = parent_state(kc);
     const int cnt = step == 0 ? 0 : rs0[0];
     const int gtok = step == 0 ? 0 : rs0[1];
     int qs = step == 0 ? 0 : rs0[2];
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
 
     // ---- 2. the state of slot `step`, 4 elements per thread and pass (the
     // first pass's operands are already in flight)
-    for (int kb0 = 0; kb0 < H; kb0 += kNodeThreads * 4) {
+    for (int kb0 = 0; kb0 < (MARG ? 0 : H); kb0 += kNodeThreads * 4) {
         const int kk = kb0 + k4;
         if (kb0 > 0 && kk < H) {  // states wider than 1024
 #pragma unroll
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
 
     // ---- 3. correction dots of slot `step`'s children (block position = its
     // depth): this wave's 16 rows, then a transposed reduction across lanes
-    if (expand) {
+    if (!MARG && expand) {
         float acc[kRowsPerWave];
 #pragma unroll
         for (int jj = 0; jj < kRowsPerWave; ++jj) acc[jj] = 0.f;
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     const bool pop = wave == 0 && cnt == step && (qs > 0 || expand);
     if (wave == 0) {
         if (expand) {
-            ckey = child_keys_r(my_val, zs[lane], my_tok, a.M, a.temp);
+            ckey = child_keys_r(my_val, MARG ? 0.f : zs[lane], my_tok, a.M, a.temp);
             best = wave_max_u64(ckey);  // the rank-0 child
             const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
             if (lane == qs) q = key;
@@ -667,9 +673,13 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
 
 template <typename T>
 hipError_t launch_node_t(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream) {
+    if (a.marginal) {
+        node_step_kernel<T, 1, true><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step);
+        return hipGetLastError();
+    }
     switch (a.ksplit) {
 #define DT_KS(K) \
-    case K: node_step_kernel<T, K><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step); break;
+    case K: node_step_kernel<T, K, false><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step); break;
         DT_KS(1) DT_KS(2) DT_KS(3) DT_KS(4) DT_KS(5) DT_KS(6)
 #undef DT_KS
         default: return hipErrorInvalidValue;

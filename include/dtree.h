@@ -103,8 +103,9 @@ const char *dt_last_error(const dt_handle *h);
  *  3. the prefix-closed tree and its ancestor-only attention mask ([captcha]
  *     "Methodology -- deep read"; [gist] "Vérification").
  * Queue order: (score desc, depth asc, parent slot asc, sibling rank asc).
- * In DT_BF16 the GRU's W_hh product takes bf16(h) (round to nearest even);
- * everything else uses the binary32 state.
+ * The hidden state is kept in binary32; in DT_BF16 the GRU's W_hh product
+ * takes it as the exact sum of three bf16 parts (bf16 MFMA with binary32
+ * accumulation), so the state is never rounded to bf16.
  *
  * Inputs (device, dtype unless noted):
  *   base_logits [B, L, V]   per-position base logits of each request
@@ -131,6 +132,20 @@ dt_status dt_build(dt_handle *h, void *workspace, size_t ws_bytes, const void *b
                    const void *b_hh, const void *C, const float *h0, int32_t *tokens,
                    int32_t *parents, int32_t *depths, float *scores, uint8_t *mask,
                    int32_t *count, uint32_t *flags, void *stream);
+
+/*
+ * dt_build_marginal -- the same best-first builder with DDTree's factorized
+ * scores: every node's children distribution is the log-softmax of the base
+ * logits over the top-M slice of its block position (no GRU, no
+ * correction), so a node's score is the sum of its tokens' marginal
+ * log-probs ([zhichai] "DominoTree 的破局": DDTree's marginal scoring
+ * function; [captcha] "Key findings": the marginal-scoring ablation).  The
+ * result equals dt_build with C = 0.  Same handle, workspace, outputs,
+ * temperature, tie orders and near-tie flags as dt_build; no GRU inputs.
+ */
+dt_status dt_build_marginal(dt_handle *h, void *workspace, size_t ws_bytes, const void *base_logits,
+                            int32_t *tokens, int32_t *parents, int32_t *depths, float *scores,
+                            uint8_t *mask, int32_t *count, uint32_t *flags, void *stream);
 
 /*
  * dt_topm -- step 1 alone: per (request, position) row of base_logits

@@ -102,11 +102,28 @@ def test_build_argument_errors_before_any_launch():
     dtree.dt_destroy(h)
 
 
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only machines")
+def test_build_marginal_argument_errors_before_any_launch():
+    lib = dtree.load_library()
+    h = make()
+    need = dtree.dt_workspace_bytes(h)
+    fake = C.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    outs = [fake] * 7
+    # no GRU inputs are needed; the logits and the outputs are
+    assert lib.dt_build_marginal(h, fake, need, None, *outs, None) == -1
+    assert "null" in dtree.dt_last_error(h)
+    assert lib.dt_build_marginal(h, fake, need, C.c_void_p(0x10004), *outs, None) == -1
+    assert "aligned" in dtree.dt_last_error(h)
+    assert lib.dt_build_marginal(h, None, need, fake, *outs, None) == -3
+    dtree.dt_destroy(h)
+
+
 def test_empty_batch_is_a_noop():
     lib = dtree.load_library()
     h = make(B=0)
     # B = 0: nothing to do, every pointer may be NULL
     assert lib.dt_build(h, None, 0, *([None] * 15), None) == 0
+    assert lib.dt_build_marginal(h, None, 0, *([None] * 8), None) == 0
     assert lib.dt_topm(h, None, 0, None, None, None, None) == 0
     dtree.dt_destroy(h)
 

@@ -230,3 +230,51 @@ def test_build_stress_and_zero_correction_ablation():
     z = dict(inp)
     z["C"] = np.zeros_like(inp["C"])
     build_and_compare(cfg, z, requests=[0, 128, 255])
+
+
+# ------------------------------------------------- factorized (marginal) --
+
+def marginal_and_compare(cfg, inp, requests, eps=1e-5, tol=SCORE_TOL):
+    """dt_build_marginal against the oracle with the correction zeroed (the
+    factorized tree; the oracle's zero-correction result is pinned to an
+    independent factorized builder on the CPU)."""
+    bld = builder(cfg, eps)
+    t = S.to_torch(inp, DEV)
+    out = bld.build_marginal(t["base"])
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    bld.close()
+    z = dict(inp)
+    z["C"] = np.zeros_like(inp["C"])
+    refs = oracle.build_batch(z, cfg["M"], cfg["n"], cfg["T"], eps=eps, requests=list(requests),
+                              threads=8)
+    kinds = [compare_request(got, b, r, z, b, cfg, eps, tol) for b, r in zip(requests, refs)]
+    say(f"  marginal: {kinds.count('exact')} exact, {kinds.count('flagged')} near-tie")
+    return got
+
+
+@pytest.mark.parametrize("over", [(), (("T", 0.5),), (("M", 1),), (("L", 1), ("n", 5)),
+                                  (("n", 64), ("L", 8))])
+def test_marginal_tiny(over):
+    cfg = S.with_config("tiny", **dict(over))
+    inp = S.make_inputs(cfg, seed=11)
+    marginal_and_compare(cfg, inp, requests=[0])
+
+
+def test_marginal_bf16_ragged():
+    cfg = dict(B=70, V=5003, L=16, E=256, H=128, M=64, n=64, dtype="bf16", alpha=1.5, T=0.0)
+    inp = S.make_inputs(cfg, seed=6)
+    marginal_and_compare(cfg, inp, requests=range(0, 70, 5))
+
+
+def test_marginal_qwen3_4b_batched_equals_zero_correction_build():
+    # the factorized mode must reproduce dt_build with C = 0 bit for bit
+    cfg, inp = inputs("qwen3_4b_batched")
+    got = marginal_and_compare(cfg, inp, requests=[0, 21, 42, 63])
+    z = dict(inp)
+    z["C"] = np.zeros_like(inp["C"])
+    bld = builder(cfg)
+    full = run_build(bld, S.to_torch(z, DEV))
+    bld.close()
+    for k in got:
+        np.testing.assert_array_equal(got[k], full[k], err_msg=f"marginal mode differs from C = 0 in {k}")
