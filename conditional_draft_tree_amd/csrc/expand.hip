@@ -275,11 +275,36 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // (the scheduler keeps the loads above in flight before the candidate
     // list is waited for)
     __builtin_amdgcn_sched_barrier(0);
+    // per-request state left by the previous step (one record)
+    const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
+    const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
+    const int rs_depth = rs1[0];
+    // the parent's state (the GRU's previous state), exact: binary32, or the sum
+    // of its three bf16 parts
+    const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
+    auto parent_state = [&](int kk) {
+        if (a.hsplit) {
+            const uint16_t* src = a.hsplit + ((slot0 + par) * 3) * (size_t)H + kk;
+            const uint2 p0 = *reinterpret_cast<const uint2*>(src);
+            const uint2 p1 = *reinterpret_cast<const uint2*>(src + H);
+            const uint2 p2 = *reinterpret_cast<const uint2*>(src + 2 * (size_t)H);
+            auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+            auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+            return f32x4{(lo(p0.x) + lo(p1.x)) + lo(p2.x), (hi(p0.x) + hi(p1.x)) + hi(p2.x),
+                         (lo(p0.y) + lo(p1.y)) + lo(p2.y), (hi(p0.y) + hi(p1.y)) + hi(p2.y)};
+        }
+        return *reinterpret_cast<const f32x4*>(a.hstate + (slot0 + par) * H + kk);
+    };
     const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
     const float* vp = step == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
     const int jl = min(lane, a.M - 1);
     const int my_tok = min(max(ip[jl], 0), a.V - 1);  // candidate `lane` (all waves)
     const float my_val = vp[jl];
+    // the parent's state is loaded before the gathers: loads complete in
+    // order, and the GRU cell must not wait for the gathers
+    f32x4 hp = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!MARG) hp = parent_state(kc);
+    __builtin_amdgcn_sched_barrier(0);
     // round trip 2: chunk k0 of this wave's 16 rows, two vectors per lane and
     // row (positions past H are clamped; their state elements are zero)
     u32x4 cv[kRowsPerWave][2];
@@ -322,28 +347,6 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         r_sc = a.scores[slot0 + threadIdx.x];
         r_par = a.parents[slot0 + threadIdx.x];
     }
-    // per-request state left by the previous step (one record)
-    const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
-    const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
-    const int rs_depth = rs1[0];
-    // the parent's state (the GRU's previous state), exact: binary32, or the sum
-    // of its three bf16 parts
-    const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
-    auto parent_state = [&](int kk) {
-        if (a.hsplit) {
-            const uint16_t* src = a.hsplit + ((slot0 + par) * 3) * (size_t)H + kk;
-            const uint2 p0 = *reinterpret_cast<const uint2*>(src);
-            const uint2 p1 = *reinterpret_cast<const uint2*>(src + H);
-            const uint2 p2 = *reinterpret_cast<const uint2*>(src + 2 * (size_t)H);
-            auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
-            auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
-            return f32x4{(lo(p0.x) + lo(p1.x)) + lo(p2.x), (hi(p0.x) + hi(p1.x)) + hi(p2.x),
-                         (lo(p0.y) + lo(p1.y)) + lo(p2.y), (hi(p0.y) + hi(p1.y)) + hi(p2.y)};
-        }
-        return *reinterpret_cast<const f32x4*>(a.hstate + (slot0 + par) * H + kk);
-    };
-    f32x4 hp = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (!MARG) hp = parent_state(kc);
     const int cnt = step == 0 ? 0 : rs0[0];
     const int gtok = step == 0 ? 0 : rs0[1];
     int qs = step == 0 ? 0 : rs0[2];
