@@ -21,7 +21,7 @@ thread_local char g_create_error[512] = "";
 
 struct Layout {
     size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
-        rstate, xpack, hpack;
+        rstate, xpack, hpack, hprev;
     size_t total;
 };
 
@@ -91,6 +91,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.nidx = take(B * 64 * 4);
     l.xpack = take(c.dtype == DT_BF16 ? (size_t)dt::pack_rows(c.B) * c.E * 2 : 0);
     l.hpack = take(c.dtype == DT_BF16 ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
+    l.hprev = take(c.dtype == DT_BF16 ? B * H * 4 : 0);
     l.nval = take(B * 64 * 4);
     l.total = off;
     return l;
@@ -393,6 +394,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     a.emb = emb;
     a.xpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.xpack) : nullptr;
     a.hpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.hpack) : nullptr;
+    a.hprev = c.dtype == DT_BF16 && !marginal ? (float*)(w + L.hprev) : nullptr;
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
     a.mask = mask; a.count = count; a.flags = flags;
 

@@ -96,6 +96,7 @@ struct NodeArgs {
     const void* emb;     // [V, E] token embeddings
     uint16_t* xpack;     // packed activations of the next contraction (bf16 path; see
     uint16_t* hpack;     // pack_index_x / pack_index_h), NULL on the binary32 path
+    float* hprev;        // [B, H] the next expanded slot's parent state (bf16 path), or NULL
     // outputs
     int32_t* tokens;
     int32_t* parents;

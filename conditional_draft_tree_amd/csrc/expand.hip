@@ -283,16 +283,8 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // of its three bf16 parts
     const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
     auto parent_state = [&](int kk) {
-        if (a.hsplit) {
-            const uint16_t* src = a.hsplit + ((slot0 + par) * 3) * (size_t)H + kk;
-            const uint2 p0 = *reinterpret_cast<const uint2*>(src);
-            const uint2 p1 = *reinterpret_cast<const uint2*>(src + H);
-            const uint2 p2 = *reinterpret_cast<const uint2*>(src + 2 * (size_t)H);
-            auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
-            auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
-            return f32x4{(lo(p0.x) + lo(p1.x)) + lo(p2.x), (hi(p0.x) + hi(p1.x)) + hi(p2.x),
-                         (lo(p0.y) + lo(p1.y)) + lo(p2.y), (hi(p0.y) + hi(p1.y)) + hi(p2.y)};
-        }
+        if (a.hprev)  // left by the previous step (bf16 path)
+            return *reinterpret_cast<const f32x4*>(a.hprev + (size_t)b * H + kk);
         return *reinterpret_cast<const f32x4*>(a.hstate + (slot0 + par) * H + kk);
     };
     const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
@@ -521,28 +513,51 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                 }
             } else {
                 const int nhc = H >> 5;
-                for (int it = (wave - 2) * kWave + lane; it < 3 * nhc; it += 2 * kWave) {
-                    const int qq = it / nhc, c = it - qq * nhc;
-                    uint32_t w[16] = {};  // 32 elements of part qq, two per word
+                for (int c = (wave - 2) * kWave + lane; c < nhc; c += 2 * kWave) {
+                    uint32_t w[3][16] = {};  // 32 elements of each part, two per word
+                    float hv[32];
                     if (grow && vpar == step) {
 #pragma unroll
                         for (int e = 0; e < 32; ++e) {
+                            hv[e] = hs[c * 32 + e];
                             uint32_t p3[3];
-                            split3_bf16(hs[c * 32 + e], p3);
-                            w[e >> 1] |= (qq == 0 ? p3[0] : qq == 1 ? p3[1] : p3[2]) << (16 * (e & 1));
+                            split3_bf16(hv[e], p3);
+#pragma unroll
+                            for (int qq = 0; qq < 3; ++qq) w[qq][e >> 1] |= p3[qq] << (16 * (e & 1));
                         }
                     } else if (grow) {
-                        const uint16_t* src = a.hsplit + ((slot0 + vpar) * 3 + qq) * (size_t)H + c * 32;
+                        const uint16_t* src = a.hsplit + ((slot0 + vpar) * 3) * (size_t)H + c * 32;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const u32x4 t4 = *reinterpret_cast<const u32x4*>(src + 8 * e);
-                            w[4 * e] = t4.x; w[4 * e + 1] = t4.y; w[4 * e + 2] = t4.z; w[4 * e + 3] = t4.w;
+                        for (int qq = 0; qq < 3; ++qq)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const u32x4 t4 = *reinterpret_cast<const u32x4*>(src + (size_t)qq * H + 8 * e);
+                                w[qq][4 * e] = t4.x; w[qq][4 * e + 1] = t4.y; w[qq][4 * e + 2] = t4.z; w[qq][4 * e + 3] = t4.w;
+                            }
+#pragma unroll
+                        for (int e = 0; e < 32; ++e) {  // the exact binary32 state
+                            const int sh = 16 * (e & 1);
+                            const float p0 = __uint_as_float(((w[0][e >> 1] >> sh) & 0xFFFFu) << 16);
+                            const float p1 = __uint_as_float(((w[1][e >> 1] >> sh) & 0xFFFFu) << 16);
+                            const float p2 = __uint_as_float(((w[2][e >> 1] >> sh) & 0xFFFFu) << 16);
+                            hv[e] = (p0 + p1) + p2;
                         }
-                    }
-                    uint16_t* dst = a.hpack + pack_index_h(b, qq, c * 32, H);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        *reinterpret_cast<u32x4*>(dst + 8 * e) = u32x4{w[4 * e], w[4 * e + 1], w[4 * e + 2], w[4 * e + 3]};
+                        for (int e = 0; e < 32; ++e) hv[e] = 0.f;
+                    }
+#pragma unroll
+                    for (int qq = 0; qq < 3; ++qq) {
+                        uint16_t* dst = a.hpack + pack_index_h(b, qq, c * 32, H);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            *reinterpret_cast<u32x4*>(dst + 8 * e) =
+                                u32x4{w[qq][4 * e], w[qq][4 * e + 1], w[qq][4 * e + 2], w[qq][4 * e + 3]};
+                    }
+                    float* hdst = a.hprev + (size_t)b * H + c * 32;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        *reinterpret_cast<f32x4*>(hdst + 4 * e) = f32x4{hv[4 * e], hv[4 * e + 1], hv[4 * e + 2], hv[4 * e + 3]};
                 }
             }
         }

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
     const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
     const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
     const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     // packed activations: lane l reads row l % 16 of its row block at K offset
     // 8 * (l / 16) of a chunk; a wave's read is one contiguous 1 KB block.
     // Rows past B read the last row (their sums are not stored).
@@ -115,20 +116,25 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
             for (int i = 0; i < kMaxXChunks; ++i) {
                 const int k = (cb + min(i, n - 1)) * 32 + kq;  // clamped: always in bounds
 #pragma unroll
-                for (int g = 0; g < 3; ++g) w[i][g] = load_bf16x8(wi + g * gi + k);
+                for (int g = 0; g < 3; ++g) {  // chunks past n: zero weights (no branch, see below)
+                    const bf16x8 v = load_bf16x8(wi + g * gi + k);
+                    w[i][g] = i < n ? v : zero;
+                }
                 const size_t c = (size_t)(cb + min(i, n - 1));
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
             }
+            // MFMAs for every chunk slot, unconditionally, and no scheduling
+            // across this point: loads sunk next to their MFMAs would wait
+            // one by one (loads complete in order)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kMaxXChunks; ++i) {
-                if (i < n) {
 #pragma unroll
-                    for (int rb = 0; rb < kRowBlocks; ++rb) {
-                        acc[rb][0] = mfma(x[i][rb], w[i][0], acc[rb][0]);
-                        acc[rb][1] = mfma(x[i][rb], w[i][1], acc[rb][1]);
-                        acc[rb][2] = mfma(x[i][rb], w[i][2], acc[rb][2]);
-                    }
+                for (int rb = 0; rb < kRowBlocks; ++rb) {
+                    acc[rb][0] = mfma(x[i][rb], w[i][0], acc[rb][0]);
+                    acc[rb][1] = mfma(x[i][rb], w[i][1], acc[rb][1]);
+                    acc[rb][2] = mfma(x[i][rb], w[i][2], acc[rb][2]);
                 }
             }
         }
@@ -141,7 +147,10 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
             for (int i = 0; i < kMaxHChunks; ++i) {
                 const int k = (cb + min(i, n - 1) - nE) * 32 + kq;
 #pragma unroll
-                for (int g = 0; g < 3; ++g) w[i][g] = load_bf16x8(wh + g * gh + k);
+                for (int g = 0; g < 3; ++g) {
+                    const bf16x8 v = load_bf16x8(wh + g * gh + k);
+                    w[i][g] = i < n ? v : zero;
+                }
                 const size_t c = (size_t)(cb + min(i, n - 1) - nE);
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; ++rb)
@@ -149,18 +158,17 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                     for (int q = 0; q < 3; ++q)
                         hp[i][rb][q] = load_bf16x8(hblk[rb] + q * hpart + c * xstep);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < kMaxHChunks; ++i) {
-                if (i < n) {
 #pragma unroll
-                    for (int rb = 0; rb < kRowBlocks; ++rb)
+                for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
-                        for (int q = 0; q < 3; ++q) {
-                            acc[rb][0] = mfma(hp[i][rb][q], w[i][0], acc[rb][0]);
-                            acc[rb][1] = mfma(hp[i][rb][q], w[i][1], acc[rb][1]);
-                            acc[rb][3] = mfma(hp[i][rb][q], w[i][2], acc[rb][3]);
-                        }
-                }
+                    for (int q = 0; q < 3; ++q) {
+                        acc[rb][0] = mfma(hp[i][rb][q], w[i][0], acc[rb][0]);
+                        acc[rb][1] = mfma(hp[i][rb][q], w[i][1], acc[rb][1]);
+                        acc[rb][3] = mfma(hp[i][rb][q], w[i][2], acc[rb][3]);
+                    }
             }
         }
     }
