@@ -296,6 +296,15 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // order, and the GRU cell must not wait for the gathers
     f32x4 hp = {0.f, 0.f, 0.f, 0.f};
     if constexpr (!MARG) hp = parent_state(kc);
+    // the root's state h0 (first pass), loaded at every step from a valid
+    // address: a load inside a branch would make the code after the branch
+    // wait for every outstanding load, the gathers included
+    f32x4 h0v = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!MARG) {
+        const float* h0p = a.h0 ? a.h0 + (size_t)b * H : a.partial;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(h0p + kc);
+        h0v = a.h0 ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     __builtin_amdgcn_sched_barrier(0);
     // round trip 2: chunk k0 of this wave's 16 rows, two vectors per lane and
     // row (positions past H are clamped; their state elements are zero)
@@ -367,7 +376,10 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         if (kk >= H) break;
         float hv[4] = {0.f, 0.f, 0.f, 0.f};
         if (step == 0) {
-            if (a.h0) {
+            if (kb0 == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = h0v[e];
+            } else if (a.h0) {  // states wider than 1024
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hv[e] = a.h0[(size_t)b * H + kk + e];
             }
