@@ -20,8 +20,8 @@
 // vector; a vector whose maximum reaches the threshold is stashed in LDS, and
 // stashed vectors are evaluated 64 at a time (one per lane), which amortizes
 // the wave-wide work of admitting a key.  Admitted keys are folded into the
-// list by insertion (few keys) or bitonic sort + merge.  topm_merge folds a
-// row's partial lists into its top M.
+// list by insertion (few keys) or bitonic sort + merge.  With several segments
+// per row, topm_merge folds a row's partial lists into its top M.
 #include <cfloat>
 
 #include "dt_device.h"
@@ -212,10 +212,14 @@ __device__ __forceinline__ void drain_stash(WaveTop& w, u64* buf, SharedThr* s_t
     nst = from;
 }
 
+// With one segment per row the workgroup's list is the row's: it then writes
+// the top M (idx, val) directly and no merge kernel runs.
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __restrict__ base, int V,
                                                                     int nseg, int seg,
-                                                                    u64* __restrict__ partial) {
+                                                                    u64* __restrict__ partial, int M,
+                                                                    int32_t* __restrict__ idx,
+                                                                    float* __restrict__ val) {
     __shared__ u64 sbuf[kWaves][kWave];
     __shared__ u32x4 svec[kWaves][kStash];
     __shared__ int sidx[kWaves][kStash];
@@ -345,7 +349,14 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
         u64 l = w.list;
 #pragma unroll
         for (int o = 1; o < kWaves; ++o) l = wave_merge_top64(l, sbuf[o][kWave - 1 - lane]);
-        partial[((size_t)row * nseg + s) * kWave + lane] = l;
+        if (nseg == 1) {
+            if (lane < M) {
+                idx[(size_t)row * M + lane] = (int32_t)topm_key_id(l);
+                val[(size_t)row * M + lane] = topm_key_val(l);
+            }
+        } else {
+            partial[((size_t)row * nseg + s) * kWave + lane] = l;
+        }
     }
 }
 
@@ -385,14 +396,14 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
     dim3 grid(nseg, rows);
     if (dtype == 1) {
         if (vec)
-            topm_partial_kernel<bf16_t, true><<<grid, kTopmThreads, 0, stream>>>((const bf16_t*)base, V, nseg, seg, partial);
+            topm_partial_kernel<bf16_t, true><<<grid, kTopmThreads, 0, stream>>>((const bf16_t*)base, V, nseg, seg, partial, M, idx, val);
         else
-            topm_partial_kernel<bf16_t, false><<<grid, kTopmThreads, 0, stream>>>((const bf16_t*)base, V, nseg, seg, partial);
+            topm_partial_kernel<bf16_t, false><<<grid, kTopmThreads, 0, stream>>>((const bf16_t*)base, V, nseg, seg, partial, M, idx, val);
     } else {
         if (vec)
-            topm_partial_kernel<float, true><<<grid, kTopmThreads, 0, stream>>>((const float*)base, V, nseg, seg, partial);
+            topm_partial_kernel<float, true><<<grid, kTopmThreads, 0, stream>>>((const float*)base, V, nseg, seg, partial, M, idx, val);
         else
-            topm_partial_kernel<float, false><<<grid, kTopmThreads, 0, stream>>>((const float*)base, V, nseg, seg, partial);
+            topm_partial_kernel<float, false><<<grid, kTopmThreads, 0, stream>>>((const float*)base, V, nseg, seg, partial, M, idx, val);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -400,7 +411,7 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
         e = hipEventRecord(ev_mid, stream);
         if (e != hipSuccess) return e;
     }
-    topm_merge_kernel<<<rows, kWave, 0, stream>>>(partial, nseg, M, idx, val);
+    if (nseg > 1) topm_merge_kernel<<<rows, kWave, 0, stream>>>(partial, nseg, M, idx, val);
     return hipGetLastError();
 }
 
