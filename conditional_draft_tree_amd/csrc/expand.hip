@@ -466,6 +466,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // popped node to waves 1-3, which pack the next contraction's activations
     // while wave 0 sorts the children and updates the queue.
     __shared__ int s_dec[2];  // next GRU token (-1 = idle row), parent slot of the popped node
+    __shared__ u64 s_keys[kWave];  // child keys of slot `step`, unsorted
     const float score_step = s_sc[step];
     u64 ckey = 0ull, best = 0ull, top = 0ull;
     int new_cnt = cnt;
@@ -476,6 +477,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     if (wave == 0) {
         if (expand) {
             ckey = child_keys_r(my_val, MARG ? 0.f : zs[lane], my_tok, a.M, a.temp);
+            s_keys[lane] = ckey;
             best = wave_max_u64(ckey);  // the rank-0 child
             const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
             if (lane == qs) q = key;
@@ -501,11 +503,24 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     __syncthreads();
 
+    if (wave == 3) {
+        // slot `step`'s children sorted by (log-prob desc, token asc), kept
+        // for the sibling pushes of later steps
+        if (expand) {
+            const u64 kids = wave_sort_desc(s_keys[lane]);
+            const size_t crow = (slot0 + step) * kMaxM;
+            if (lane < a.M) {
+                a.child_tok[crow + lane] = child_tok_of(kids);
+                a.child_lp[crow + lane] = child_lp_of(kids);
+            }
+        }
+        return;
+    }
     if (wave != 0) {
         // ---- 4. row b's activations of the next contraction, packed for its
         // MFMA operands: the popped node's token embedding (wave 1) and its
-        // parent's state in three exact bf16 parts (waves 2-3); zeros for an
-        // idle row.  The parent is slot `step` (state in LDS) or an older slot
+        // parent's state in three exact bf16 parts (wave 2); zeros for an idle
+        // row.  The parent is slot `step` (state in LDS) or an older slot
         // (parts in hsplit).
         if (a.xpack && step + 1 < a.n) {
             const int ntok = s_dec[0], vpar = s_dec[1];
@@ -525,7 +540,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                 }
             } else {
                 const int nhc = H >> 5;
-                for (int c = (wave - 2) * kWave + lane; c < nhc; c += 2 * kWave) {
+                for (int c = lane; c < nhc; c += kWave) {
                     uint32_t w[3][16] = {};  // 32 elements of each part, two per word
                     float hv[32];
                     if (grow && vpar == step) {
@@ -576,16 +591,9 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         return;
     }
 
-    // wave 0: slot `step`'s sorted children
-    u64 kids = 0ull;  // lane r: rank-r child of slot `step`
-    if (expand) {
-        kids = wave_sort_desc(ckey);
-        const size_t crow = (slot0 + step) * kMaxM;
-        if (lane < a.M) {
-            a.child_tok[crow + lane] = child_tok_of(kids);
-            a.child_lp[crow + lane] = child_lp_of(kids);
-        }
-    }
+    // wave 0: the rank-1 child of slot `step` (the sibling pushed when its
+    // rank-0 child is popped): the largest key below the rank-0 child's
+    const u64 second = expand ? wave_max_u64(ckey == best ? 0ull : ckey) : 0ull;
     if (step == 0) {
         for (int i = lane; i < S; i += kWave) {
             if (i == 0) {
@@ -609,7 +617,8 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         if (lane == qs - 1) q = 0ull;
         --qs;
         const bool has_sib = pr + 1 < a.M;
-        const float sib_lp = v_par == step ? child_lp_of(bcast_u64(kids, min(pr + 1, kWave - 1)))
+        // a child of slot `step` popped now is its rank-0 child (pr == 0)
+        const float sib_lp = v_par == step ? child_lp_of(second)
                                            : s_clp[v_par * kMaxM + min(pr + 1, kMaxM - 1)];
         if (has_sib) {
             const u64 key = queue_key(s_sc[v_par] + sib_lp, pd, v_par, pr + 1);
