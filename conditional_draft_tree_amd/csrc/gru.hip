@@ -73,7 +73,8 @@ constexpr int kMaxXChunks = 6;  // x chunks per wave and batch
 constexpr int kMaxHChunks = 2;  // h chunks per wave and batch
 
 __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesArgs a) {
-    __shared__ float red[kWaves8][16][kWave];  // one row block of all waves: 32 KB
+    // every wave's sums of the workgroup's 64 x 16 outputs x 4 gates: 128 KB
+    __shared__ f32x4 red[kWaves8][kRowBlocks * 4][kWave];
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const int ut = blockIdx.x, rg = blockIdx.y, ks = blockIdx.z;
     const int unit = ut * 16 + (lane & 15);
@@ -173,28 +174,27 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
         }
     }
 
-    // the 8 waves' sums, one row block at a time, added in wave order; all
-    // 512 threads write the workgroup's partial sums
+    // the 8 waves' sums added in wave order (one LDS round trip); all 512
+    // threads write the workgroup's partial sums
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 4; ++g) red[wave][rb * 4 + g][lane] = acc[rb][g];
+    __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave][g * 4 + e][lane] = acc[rb][g][e];
-        __syncthreads();
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (rb, g, lane) of 4 x 4 x 64
+        const int sl = idx >> 6, ln = idx & 63;
+        f32x4 sum = red[0][sl][ln];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (i, lane) of 16 x 64
-            const int i = idx >> 6, ln = idx & 63;
-            float sum = red[0][i][ln];
+        for (int w2 = 1; w2 < kWaves8; ++w2) sum += red[w2][sl][ln];
+        const int rb = sl >> 2, g = sl & 3;
 #pragma unroll
-            for (int w2 = 1; w2 < kWaves8; ++w2) sum += red[w2][i][ln];
-            const int g = i >> 2, e = i & 3;
+        for (int e = 0; e < 4; ++e) {  // MFMA output rows 4 * (lane / 16) + e
             const int row = rg * 64 + rb * 16 + (ln >> 4) * 4 + e;
             if (row < a.B)
-                a.partial[((size_t)(ks * a.B + row) * kGateSlots + g) * a.H + ut * 16 + (ln & 15)] = sum;
+                a.partial[((size_t)(ks * a.B + row) * kGateSlots + g) * a.H + ut * 16 + (ln & 15)] = sum[e];
         }
-        __syncthreads();
     }
 }
 
