@@ -9,8 +9,9 @@ resident in HBM.  Prints ONE JSON line:
 
   value       tree builds per second (B * K / wall time of the K timed steps)
   roofline    the top-M select kernel (the dominant HBM stream): algorithmic
-              bytes per launch / its mean launch time from HIP events recorded
-              on the library's stream during the timed steps, against 8 TB/s
+              bytes per launch / its mean kernel duration from the HIP events
+              that each launch records on the library's stream (begin and end
+              of the kernel itself) during the timed steps, against 8 TB/s
   cpu_baseline the CPU oracle on a bounded sample of requests of the same
               workload, on the host's cores
 Extra keys: per-stage times (a separate pass with per-kernel events), the GRU

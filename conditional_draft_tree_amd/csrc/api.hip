@@ -26,8 +26,10 @@ struct Layout {
 };
 
 struct Marker {
-    char tag;  // 'S' start, 'T' top-M select, 'M' top-M merge, 'G' gate contraction,
-               // 'N' node step, 'E' end of a level-1 call
+    // 'K'/'T' begin/end of the top-M select kernel, 'M' after the top-M merge,
+    // 'g'/'G' begin/end of a gate contraction, 'n'/'N' of a node step, 'E'
+    // end of the call.  A stage's time is the span from the preceding marker.
+    char tag;
     hipEvent_t ev;
 };
 
@@ -125,6 +127,22 @@ hipError_t mark(dt_handle* h, std::vector<Marker>* call, int need, char tag, hip
     if (!e) return hipErrorOutOfMemory;
     call->push_back({tag, e});
     return hipEventRecord(e, st);
+}
+
+// Begin/end markers (tags t0, t1) of the next kernel of the current call
+// (level >= need): `ev` receives two events that the launch itself records.
+// Below the level, `ev` is cleared and the launch is untimed.
+hipError_t kernel_marks(dt_handle* h, std::vector<Marker>* call, int need, char t0, char t1,
+                        dt::LaunchEvents* ev) {
+    *ev = dt::LaunchEvents{};
+    if (!call || h->tlevel < need) return hipSuccess;
+    hipEvent_t e0 = take_event(h), e1 = take_event(h);
+    if (!e0 || !e1) return hipErrorOutOfMemory;
+    call->push_back({t0, e0});
+    call->push_back({t1, e1});
+    ev->start = e0;
+    ev->stop = e1;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -260,7 +278,7 @@ dt_status dt_topm(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int
     if (s) return s;
     hipError_t e = dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg,
                                    (u64*)((char*)ws + h->lay.partial), c.M, idx, val,
-                                   (hipStream_t)stream, nullptr);
+                                   (hipStream_t)stream);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_topm launch");
 }
 
@@ -356,18 +374,13 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         if (e != hipSuccess) return hip_fail(h, e, what);  \
     } while (0)
 
-    DT_TRY(mark(h, call, 1, 'S', st), "timing event");
-    hipEvent_t ev_mid = nullptr;
-    if (call) {
-        ev_mid = take_event(h);
-        if (!ev_mid) return hip_fail(h, hipErrorOutOfMemory, "timing event");
-    }
     int32_t* tidx = (int32_t*)(w + L.tidx);
     float* tval = (float*)(w + L.tval);
+    dt::LaunchEvents ev{};
+    DT_TRY(kernel_marks(h, call, 1, 'K', 'T', &ev), "timing event");
     DT_TRY(dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg, (u64*)(w + L.partial), c.M,
-                           tidx, tval, st, ev_mid),
+                           tidx, tval, st, ev),
            "top-M launch");
-    if (call) call->push_back({'T', ev_mid});
     DT_TRY(mark(h, call, 1, 'M', st), "timing event");
 
     dt::NodeArgs a{};
@@ -413,15 +426,15 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     g.ksplit = h->ksplit;
     g.dtype = (int)c.dtype;
 
-    DT_TRY(dt::launch_node_step(a, h->lds, 0, st), "node step launch");
-    DT_TRY(mark(h, call, 2, 'N', st), "timing event");
+    DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
+    DT_TRY(dt::launch_node_step(a, h->lds, 0, st, ev), "node step launch");
     for (int step = 1; step < c.n; ++step) {
         if (!marginal) {
-            DT_TRY(dt::launch_gru_gates(g, st), "GRU contraction launch");
-            DT_TRY(mark(h, call, 2, 'G', st), "timing event");
+            DT_TRY(kernel_marks(h, call, 2, 'g', 'G', &ev), "timing event");
+            DT_TRY(dt::launch_gru_gates(g, st, ev), "GRU contraction launch");
         }
-        DT_TRY(dt::launch_node_step(a, h->lds, step, st), "node step launch");
-        DT_TRY(mark(h, call, 2, 'N', st), "timing event");
+        DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
+        DT_TRY(dt::launch_node_step(a, h->lds, step, st, ev), "node step launch");
     }
     DT_TRY(mark(h, call, 1, 'E', st), "timing event");
 #undef DT_TRY

@@ -2,6 +2,7 @@
 // per-call argument block of the expansion.  Internal; not part of the C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,12 +11,30 @@ namespace dt {
 
 typedef unsigned long long u64;
 
+// Optional timing of one launch: when `start` is set, the two events take the
+// kernel's own begin and end times (hipExtLaunchKernel), so their difference
+// is the kernel's duration without the dispatch gap.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+template <typename T> struct same_type { using type = T; };
+template <typename... P>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, unsigned shm, hipStream_t s,
+                         LaunchEvents ev, typename same_type<P>::type... args) {
+    if (!ev.start) {
+        hipLaunchKernelGGL(k, grid, block, shm, s, args...);
+        return hipGetLastError();
+    }
+    void* argv[] = {(void*)&args...};
+    return hipExtLaunchKernel((const void*)k, grid, block, argv, shm, s, ev.start, ev.stop, 0);
+}
+
 // ---- top-M select (topm.hip) ----------------------------------------------
 int topm_segments(int rows, int V);
 // rows = B*L rows of V logits; partial: rows*nseg*64 keys of scratch.
-// ev_mid (optional) is recorded between the select and the merge kernel.
+// ev (optional) times the select kernel alone (not the merge).
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial, int M,
-                       int32_t* idx, float* val, hipStream_t stream, hipEvent_t ev_mid);
+                       int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev = {});
 
 // ---- GRU gate contraction (gru.hip) -----------------------------------------
 // bf16 path: the activations come packed for the MFMA operands (see
@@ -56,7 +75,7 @@ __device__ __forceinline__ size_t state_index(const GruGatesArgs& a, int b) {
 }
 int gru_ksplit(int B, int E, int H, int dtype);
 constexpr int kGateSlotsHost = 4;  // == kGateSlots (dt_device.h)
-hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream);
+hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream, LaunchEvents ev = {});
 // x [B, E] bf16 and h [B, H] binary32 -> packed activations (rows B .. pack_rows(B) zero)
 hipError_t launch_pack(const uint16_t* x, const float* h, uint16_t* xpack, uint16_t* hpack, int B, int E,
                        int H, hipStream_t stream);
@@ -112,7 +131,8 @@ struct NodeLds {
     size_t bytes;
 };
 NodeLds node_lds_plan(int L, int M, int n, int H);
-hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream);
+hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream,
+                            LaunchEvents ev = {});
 
 // Conditional children distribution of one node per row (dt_correct).
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,

@@ -711,24 +711,25 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
 }  // namespace
 
 template <typename T>
-hipError_t launch_node_t(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream) {
-    if (a.marginal) {
-        node_step_kernel<T, 1, true><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step);
-        return hipGetLastError();
-    }
+hipError_t launch_node_t(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream,
+                         LaunchEvents ev) {
+    const dim3 grid(a.B), block(kNodeThreads);
+    const unsigned shm = (unsigned)lp.bytes;
+    if (a.marginal) return launch_kernel(node_step_kernel<T, 1, true>, grid, block, shm, stream, ev, a, lp, step);
     switch (a.ksplit) {
 #define DT_KS(K) \
-    case K: node_step_kernel<T, K, false><<<a.B, kNodeThreads, lp.bytes, stream>>>(a, lp, step); break;
+    case K: return launch_kernel(node_step_kernel<T, K, false>, grid, block, shm, stream, ev, a, lp, step);
         DT_KS(1) DT_KS(2) DT_KS(3) DT_KS(4) DT_KS(5) DT_KS(6)
 #undef DT_KS
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
-hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream) {
+hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream,
+                            LaunchEvents ev) {
     if (a.B == 0) return hipSuccess;
-    return a.dtype == 1 ? launch_node_t<bf16_t>(a, lp, step, stream) : launch_node_t<float>(a, lp, step, stream);
+    return a.dtype == 1 ? launch_node_t<bf16_t>(a, lp, step, stream, ev)
+                        : launch_node_t<float>(a, lp, step, stream, ev);
 }
 
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,

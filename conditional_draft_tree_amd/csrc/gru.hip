@@ -275,16 +275,12 @@ int gru_ksplit(int B, int E, int H, int dtype) {
     return best;
 }
 
-hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream) {
+hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream, LaunchEvents ev) {
     if (a.B == 0) return hipSuccess;
-    if (a.dtype == 1) {
-        dim3 grid(a.H / 16, (a.B + 63) / 64, a.ksplit);
-        gru_gates_bf16_kernel<<<grid, kWaves8 * kWave, 0, stream>>>(a);
-    } else {
-        dim3 grid((a.H + 63) / 64, a.B, 1);
-        gru_gates_f32_kernel<<<grid, 64, 0, stream>>>(a);
-    }
-    return hipGetLastError();
+    if (a.dtype == 1)
+        return launch_kernel(gru_gates_bf16_kernel, dim3(a.H / 16, (a.B + 63) / 64, a.ksplit),
+                             dim3(kWaves8 * kWave), 0, stream, ev, a);
+    return launch_kernel(gru_gates_f32_kernel, dim3((a.H + 63) / 64, a.B, 1), dim3(64), 0, stream, ev, a);
 }
 
 hipError_t launch_pack(const uint16_t* x, const float* h, uint16_t* xpack, uint16_t* hpack, int B, int E,

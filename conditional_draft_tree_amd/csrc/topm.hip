@@ -386,31 +386,24 @@ int topm_segments(int rows, int V) {
 }
 
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial,
-                       int M, int32_t* idx, float* val, hipStream_t stream, hipEvent_t ev_mid) {
+                       int M, int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev) {
     if (rows == 0) return hipSuccess;
     const size_t esz = dtype == 1 ? 2 : 4;
     const int per_vec = 16 / (int)esz;
     int seg = (V + nseg - 1) / nseg;
     seg = (seg + per_vec - 1) / per_vec * per_vec;  // segments start on vector boundaries
     const bool vec = ((uintptr_t)base % 16 == 0) && ((size_t)V * esz % 16 == 0);
-    dim3 grid(nseg, rows);
-    if (dtype == 1) {
-        if (vec)
-            topm_partial_kernel<bf16_t, true><<<grid, kTopmThreads, 0, stream>>>((const bf16_t*)base, V, nseg, seg, partial, M, idx, val);
-        else
-            topm_partial_kernel<bf16_t, false><<<grid, kTopmThreads, 0, stream>>>((const bf16_t*)base, V, nseg, seg, partial, M, idx, val);
-    } else {
-        if (vec)
-            topm_partial_kernel<float, true><<<grid, kTopmThreads, 0, stream>>>((const float*)base, V, nseg, seg, partial, M, idx, val);
-        else
-            topm_partial_kernel<float, false><<<grid, kTopmThreads, 0, stream>>>((const float*)base, V, nseg, seg, partial, M, idx, val);
-    }
-    hipError_t e = hipGetLastError();
+    const dim3 grid(nseg, rows), block(kTopmThreads);
+    hipError_t e;
+    if (dtype == 1)
+        e = launch_kernel(vec ? topm_partial_kernel<bf16_t, true> : topm_partial_kernel<bf16_t, false>,
+                          grid, block, 0, stream, ev, (const bf16_t*)base, V, nseg, seg, partial, M,
+                          idx, val);
+    else
+        e = launch_kernel(vec ? topm_partial_kernel<float, true> : topm_partial_kernel<float, false>,
+                          grid, block, 0, stream, ev, (const float*)base, V, nseg, seg, partial, M,
+                          idx, val);
     if (e != hipSuccess) return e;
-    if (ev_mid) {
-        e = hipEventRecord(ev_mid, stream);
-        if (e != hipSuccess) return e;
-    }
     if (nseg > 1) topm_merge_kernel<<<rows, kWave, 0, stream>>>(partial, nseg, M, idx, val);
     return hipGetLastError();
 }

@@ -188,12 +188,14 @@ dt_status dt_correct(dt_handle *h, const int32_t *idx, const float *val, const v
 /*
  * Stage timing for benchmarks.  dt_timing_enable(h, level, capacity) makes
  * the next `capacity` dt_build calls record HIP events on their stream:
- * level 1 around the top-M kernels only, level 2 around every kernel; level
- * 0 turns timing off and drops recorded events.  After the stream is
- * synchronized, dt_timing_read(h, stage, ms, max, n_out) returns per-call
- * durations in milliseconds, oldest first:
+ * level 1 on the top-M select kernel only, level 2 on every kernel; level 0
+ * turns timing off and drops recorded events.  A kernel's events are taken
+ * by its launch (hipExtLaunchKernel), so they span the kernel alone, not the
+ * dispatch gap before it.  After the stream is synchronized,
+ * dt_timing_read(h, stage, ms, max, n_out) returns per-call durations in
+ * milliseconds, oldest first:
  *   stage 0  top-M select kernel (one launch per call)
- *   stage 1  top-M merge kernel
+ *   stage 1  top-M merge kernel, with the gap before it (0 with one segment)
  *   stage 2  GRU gate contractions of the call, summed   (level 2)
  *   stage 3  node (correction + queue) kernels, summed    (level 2)
  *   stage 4  the whole call
