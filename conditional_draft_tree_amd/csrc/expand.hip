@@ -33,10 +33,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kNodeThreads = 256;
-constexpr int kRowsPerWave = kMaxM / (kNodeThreads / kWave);  // 16
-// table entries (L*M) and child-list entries (step*64) staged per thread
-constexpr int kStage = 16;  // 16 * 256 = 4096 >= 64 * 64
+// dt_correct's kernel: 4 waves, 16 gathered rows each
+constexpr int kCorrThreads = 256;
+constexpr int kCorrRows = kMaxM / (kCorrThreads / kWave);  // 16
+
+// Threads of the node kernel: 16 waves for the conditional step (its 64
+// gathered rows and its state spread over 16 waves, so that a wave waits for
+// 4 rows, not 16: the gathers land about twice as fast), 4 for the
+// factorized step (no state, no gathers).
+template <bool MARG> constexpr int node_threads() { return MARG ? 256 : 1024; }
 
 // Four consecutive elements as binary32.
 template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
@@ -47,6 +52,13 @@ template <> __device__ __forceinline__ f32x4 load4<bf16_t>(const bf16_t* p) {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
     return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+}
+
+// One element as binary32.
+template <typename T> __device__ __forceinline__ float load1(const T* p);
+template <> __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load1<bf16_t>(const bf16_t* p) {
+    return __uint_as_float((uint32_t)*p << 16);
 }
 
 template <typename T> struct Row;
@@ -82,20 +94,20 @@ __device__ __forceinline__ void correction_logits(const T* __restrict__ C, const
     constexpr int P = Row<T>::kPerVec;
     constexpr int kStep = kWave * P;
     const int wave = threadIdx.x / kWave, lane = lane_id();
-    int tok[kRowsPerWave];
-    float acc[kRowsPerWave];
+    int tok[kCorrRows];
+    float acc[kCorrRows];
 #pragma unroll
-    for (int jj = 0; jj < kRowsPerWave; ++jj) {
-        const int j = wave * kRowsPerWave + jj;
+    for (int jj = 0; jj < kCorrRows; ++jj) {
+        const int j = wave * kCorrRows + jj;
         tok[jj] = j < M ? idx[j] : -1;
         acc[jj] = 0.f;
     }
     for (int k0 = 0; k0 < H; k0 += 2 * kStep) {
         const int ka = k0 + lane * P, kb = ka + kStep;
         const bool oka = ka < H, okb = kb < H;
-        u32x4 va[kRowsPerWave], vb[kRowsPerWave];
+        u32x4 va[kCorrRows], vb[kCorrRows];
 #pragma unroll
-        for (int jj = 0; jj < kRowsPerWave; ++jj) {
+        for (int jj = 0; jj < kCorrRows; ++jj) {
             const T* row = C + (size_t)(tok[jj] < 0 ? 0 : tok[jj]) * H;
             const bool on = tok[jj] >= 0;
             va[jj] = (on && oka) ? *reinterpret_cast<const u32x4*>(row + ka) : u32x4{0u, 0u, 0u, 0u};
@@ -108,15 +120,15 @@ __device__ __forceinline__ void correction_logits(const T* __restrict__ C, const
             hb[i] = okb ? hs[kb + i] : 0.f;
         }
 #pragma unroll
-        for (int jj = 0; jj < kRowsPerWave; ++jj) {
+        for (int jj = 0; jj < kCorrRows; ++jj) {
             acc[jj] += Row<T>::dot(va[jj], ha);
             acc[jj] += Row<T>::dot(vb[jj], hb);
         }
     }
 #pragma unroll
-    for (int jj = 0; jj < kRowsPerWave; ++jj) {
+    for (int jj = 0; jj < kCorrRows; ++jj) {
         const float d = wave_sum(acc[jj]);
-        const int j = wave * kRowsPerWave + jj;
+        const int j = wave * kCorrRows + jj;
         if (lane == 0 && j < M) z[j] = val[j] + d;
     }
 }
@@ -165,38 +177,26 @@ NodeLds node_lds_plan(int L, int M, int n, int H) {
 
 namespace {
 
-// Row sums over the 64 lanes of a wave's 16 per-lane partial dots, reduced
+// Row sums over the 64 lanes of a wave's 4 per-lane partial dots, reduced
 // in transposed form (each exchange halves the values a lane holds): lane l
-// ends with the sum of row (l >> 2) & 15, the same in the four lanes of a quad.
+// ends with the sum of row l / 16, the same in the 16 lanes of a row.
 // Lane semantics of the swaps with two operands A, B: permlane32_swap returns
 // {[A lower half, B lower half], [A upper half, B upper half]};
 // permlane16_swap returns {[A row0, B row0, A row2, B row2],
 // [A row1, B row1, A row3, B row3]} (rows of 16 lanes).
-__device__ __forceinline__ float wave_rowsum16(const float (&acc)[kRowsPerWave]) {
-    const int lane = lane_id();
-    float s8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {  // rows i + 8 * lane bit 5
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i + 8]),
-                                                        false, false);
-        s8[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    float s4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // rows i + 4 * bit 4 + 8 * bit 5
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s8[i]), __float_as_uint(s8[i + 4]),
-                                                        false, false);
-        s4[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    const bool b3 = lane & 8, b2 = lane & 4;
+__device__ __forceinline__ float wave_rowsum4(const float (&acc)[4]) {
     float s2[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // rows i + 2 * bit 3 + 4 * bit 4 + 8 * bit 5
-        const float keep = b3 ? s4[i + 2] : s4[i];
-        const float send = b3 ? s4[i] : s4[i + 2];
-        s2[i] = keep + xor_lane_f<8>(send);
+    for (int i = 0; i < 2; ++i) {  // rows i + 2 * lane bit 5
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i + 2]),
+                                                        false, false);
+        s2[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    float v = (b2 ? s2[1] : s2[0]) + xor_lane_f<4>(b2 ? s2[0] : s2[1]);
+    // rows bit 4 + 2 * bit 5
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2[0]), __float_as_uint(s2[1]), false, false);
+    float v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    v += xor_lane_f<8>(v);
+    v += xor_lane_f<4>(v);
     v += xor_lane_f<2>(v);
     v += xor_lane_f<1>(v);
     return v;
@@ -222,7 +222,11 @@ __device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M
 // is the log-softmax of the base logits over its M-slice (no GRU state, no
 // correction).
 template <typename T, int KS, bool MARG>
-__global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
+__global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
+    constexpr int NT = node_threads<MARG>();
+    constexpr int NW = NT / kWave;
+    constexpr int RW = kMaxM / NW;                    // gathered rows per wave
+    constexpr int kStageV = kMaxM * kMaxN / (4 * NT);  // 16-byte vectors of table / child list per thread
     extern __shared__ float lds[];
     float* hs = lds + lp.hs;
     float* zs = lds + lp.zs;
@@ -253,23 +257,22 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // slot `step`'s state: the GRU cell on the K-range partial sums of the
     // preceding contraction, added in K order (read at every step; the root
     // takes h0 instead)
-    const int k4 = (int)threadIdx.x * 4;  // first of this thread's 4 state elements
-    const bool kin = k4 < H;
-    const int kc = kin ? k4 : 0;
-    f32x4 t[KS][4];
-    f32x4 bias[6];
+    const int k1 = (int)threadIdx.x;  // this thread's state element
+    const int kc = k1 < H ? k1 : 0;
+    float t[KS][4];
+    float bias[6];
     if constexpr (!MARG) {
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kc);
+                t[s2][g] = a.partial[((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kc];
 #pragma unroll
         for (int g = 0; g < 6; ++g) {
             const void* bp = g < 3 ? a.b_ih : a.b_hh;
             const T* src = bp ? (const T*)bp : (const T*)a.partial;  // any valid address
-            const f32x4 v = load4<T>(src + (size_t)(g % 3) * H + kc);
-            bias[g] = bp ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+            const float v = load1<T>(src + (size_t)(g % 3) * H + kc);
+            bias[g] = bp ? v : 0.f;
         }
     }
     // (the scheduler keeps the loads above in flight before the candidate
@@ -284,8 +287,8 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
     auto parent_state = [&](int kk) {
         if (a.hprev)  // left by the previous step (bf16 path)
-            return *reinterpret_cast<const f32x4*>(a.hprev + (size_t)b * H + kk);
-        return *reinterpret_cast<const f32x4*>(a.hstate + (slot0 + par) * H + kk);
+            return a.hprev[(size_t)b * H + kk];
+        return a.hstate[(slot0 + par) * H + kk];
     };
     const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
     const float* vp = step == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
@@ -294,26 +297,26 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     const float my_val = vp[jl];
     // the parent's state is loaded before the gathers: loads complete in
     // order, and the GRU cell must not wait for the gathers
-    f32x4 hp = {0.f, 0.f, 0.f, 0.f};
+    float hp = 0.f;
     if constexpr (!MARG) hp = parent_state(kc);
     // the root's state h0 (first pass), loaded at every step from a valid
     // address: a load inside a branch would make the code after the branch
     // wait for every outstanding load, the gathers included
-    f32x4 h0v = {0.f, 0.f, 0.f, 0.f};
+    float h0v = 0.f;
     if constexpr (!MARG) {
         const float* h0p = a.h0 ? a.h0 + (size_t)b * H : a.partial;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(h0p + kc);
-        h0v = a.h0 ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+        const float v = h0p[kc];
+        h0v = a.h0 ? v : 0.f;
     }
     __builtin_amdgcn_sched_barrier(0);
-    // round trip 2: chunk k0 of this wave's 16 rows, two vectors per lane and
+    // round trip 2: chunk k0 of this wave's RW rows, two vectors per lane and
     // row (positions past H are clamped; their state elements are zero)
-    u32x4 cv[kRowsPerWave][2];
+    u32x4 cv[RW][2];
     auto gather = [&](int k0) {
         const int ka = min(k0 + lane * P, H - P), kb = min(k0 + (kWave + lane) * P, H - P);
 #pragma unroll
-        for (int jj = 0; jj < kRowsPerWave; ++jj) {
-            const int tk = __builtin_amdgcn_readlane(my_tok, wave * kRowsPerWave + jj);
+        for (int jj = 0; jj < RW; ++jj) {
+            const int tk = __builtin_amdgcn_readlane(my_tok, wave * RW + jj);
             const T* row = (const T*)a.C + (size_t)tk * H;
             cv[jj][0] = *reinterpret_cast<const u32x4*>(row + ka);
             cv[jj][1] = *reinterpret_cast<const u32x4*>(row + kb);
@@ -324,7 +327,6 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     // (into registers now as 16-byte vectors, into LDS after the state is
     // computed; a table whose rows are not a multiple of 4 entries long is
     // staged element by element below)
-    constexpr int kStageV = kStage / 4;
     const bool tvec = (LM & 3) == 0;
     i32x4 r_ti[kStageV], r_ct[kStageV];
     f32x4 r_tv[kStageV], r_cl[kStageV];
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     const int nkid = step * kMaxM;
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
-        const int e = ((int)threadIdx.x + u * kNodeThreads) * 4;
+        const int e = ((int)threadIdx.x + u * NT) * 4;
         const bool te = tvec && e < LM, ke = e < nkid;
         r_ti[u] = te ? *reinterpret_cast<const i32x4*>(ti + e) : i32x4{0, 0, 0, 0};
         r_tv[u] = te ? *reinterpret_cast<const f32x4*>(tv + e) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -356,65 +358,55 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     u64 q = step == 0 ? 0ull : q_m;
     const bool expand = step == 0 || (cnt == step && gtok >= 0);
 
-    // ---- 2. the state of slot `step`, 4 elements per thread and pass (the
+    // ---- 2. the state of slot `step`, one element per thread and pass (the
     // first pass's operands are already in flight)
-    for (int kb0 = 0; kb0 < (MARG ? 0 : H); kb0 += kNodeThreads * 4) {
-        const int kk = kb0 + k4;
-        if (kb0 > 0 && kk < H) {  // states wider than 1024
+    for (int kb0 = 0; kb0 < (MARG ? 0 : H); kb0 += NT) {
+        const int kk = kb0 + k1;
+        if (kb0 > 0 && kk < H) {  // states wider than NT
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    t[s2][g] = *reinterpret_cast<const f32x4*>(a.partial + ((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kk);
+                    t[s2][g] = a.partial[((size_t)(s2 * a.B + b) * kGateSlots + g) * H + kk];
             hp = parent_state(kk);
 #pragma unroll
             for (int g = 0; g < 6; ++g) {
                 const void* bp = g < 3 ? a.b_ih : a.b_hh;
-                if (bp) bias[g] = load4<T>((const T*)bp + (size_t)(g % 3) * H + kk);
+                if (bp) bias[g] = load1<T>((const T*)bp + (size_t)(g % 3) * H + kk);
             }
         }
         if (kk >= H) break;
-        float hv[4] = {0.f, 0.f, 0.f, 0.f};
+        float hv = 0.f;
         if (step == 0) {
-            if (kb0 == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = h0v[e];
-            } else if (a.h0) {  // states wider than 1024
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hv[e] = a.h0[(size_t)b * H + kk + e];
-            }
+            if (kb0 == 0) hv = h0v;
+            else if (a.h0) hv = a.h0[(size_t)b * H + kk];  // states wider than NT
         } else {
-            f32x4 sum[4];
+            float sum[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 sum[g] = t[0][g];
 #pragma unroll
                 for (int s2 = 1; s2 < KS; ++s2) sum[g] += t[s2][g];
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                hv[e] = gru_cell_b(sum[0][e], sum[1][e], sum[2][e], sum[3][e], bias[0][e], bias[1][e],
-                                   bias[2][e], bias[3][e], bias[4][e], bias[5][e], hp[e]);
+            hv = gru_cell_b(sum[0], sum[1], sum[2], sum[3], bias[0], bias[1], bias[2], bias[3], bias[4],
+                            bias[5], hp);
         }
-        *reinterpret_cast<f32x4*>(hs + kk) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+        hs[kk] = hv;
         if (expand) {
             if (a.hstate)  // binary32 state (read by the binary32 contraction)
-                *reinterpret_cast<f32x4*>(a.hstate + (slot0 + step) * H + kk) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+                a.hstate[(slot0 + step) * H + kk] = hv;
             if (a.hsplit) {  // its exact bf16 parts (read by the bf16 contraction)
-                uint32_t parts[4][3];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) split3_bf16(hv[e], parts[e]);
+                uint32_t parts[3];
+                split3_bf16(hv, parts);
                 uint16_t* pdst = a.hsplit + (slot0 + step) * 3 * (size_t)H + kk;
 #pragma unroll
-                for (int qq = 0; qq < 3; ++qq)
-                    *reinterpret_cast<uint2*>(pdst + (size_t)qq * H) =
-                        uint2{parts[0][qq] | (parts[1][qq] << 16), parts[2][qq] | (parts[3][qq] << 16)};
+                for (int qq = 0; qq < 3; ++qq) pdst[(size_t)qq * H] = (uint16_t)parts[qq];
             }
         }
     }
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
-        const int e = ((int)threadIdx.x + u * kNodeThreads) * 4;
+        const int e = ((int)threadIdx.x + u * NT) * 4;
         if (tvec && e < LM) {
             *reinterpret_cast<i32x4*>(s_tidx + e) = r_ti[u];
             *reinterpret_cast<f32x4*>(s_tval + e) = r_tv[u];
@@ -425,7 +417,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
         }
     }
     if (!tvec) {
-        for (int e = threadIdx.x; e < LM; e += kNodeThreads) {
+        for (int e = threadIdx.x; e < LM; e += NT) {
             s_tidx[e] = ti[e];
             s_tval[e] = tv[e];
         }
@@ -437,34 +429,37 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     __syncthreads();
 
     // ---- 3. correction dots of slot `step`'s children (block position = its
-    // depth): this wave's 16 rows, then a transposed reduction across lanes
-    if (!MARG && expand) {
-        float acc[kRowsPerWave];
+    // depth): this wave's RW rows, then a transposed reduction across lanes
+    if constexpr (!MARG) {
+        if (expand) {
+            float acc[RW];
 #pragma unroll
-        for (int jj = 0; jj < kRowsPerWave; ++jj) acc[jj] = 0.f;
-        for (int k0 = 0; k0 < H; k0 += kChunk) {
-            if (k0 > 0) gather(k0);  // states wider than one chunk
-            const int ka = k0 + lane * P, kb = k0 + (kWave + lane) * P;
-            float ha[P], hb[P];  // zero past H (those lanes read a clamped row segment)
+            for (int jj = 0; jj < RW; ++jj) acc[jj] = 0.f;
+            for (int k0 = 0; k0 < H; k0 += kChunk) {
+                if (k0 > 0) gather(k0);  // states wider than one chunk
+                const int ka = k0 + lane * P, kb = k0 + (kWave + lane) * P;
+                float ha[P], hb[P];  // zero past H (those lanes read a clamped row segment)
 #pragma unroll
-            for (int i2 = 0; i2 < P; ++i2) {
-                ha[i2] = ka < H ? hs[ka + i2] : 0.f;
-                hb[i2] = kb < H ? hs[kb + i2] : 0.f;
+                for (int i2 = 0; i2 < P; ++i2) {
+                    ha[i2] = ka < H ? hs[ka + i2] : 0.f;
+                    hb[i2] = kb < H ? hs[kb + i2] : 0.f;
+                }
+#pragma unroll
+                for (int jj = 0; jj < RW; ++jj) {
+                    acc[jj] += Row<T>::dot(cv[jj][0], ha);
+                    acc[jj] += Row<T>::dot(cv[jj][1], hb);
+                }
             }
-#pragma unroll
-            for (int jj = 0; jj < kRowsPerWave; ++jj) {
-                acc[jj] += Row<T>::dot(cv[jj][0], ha);
-                acc[jj] += Row<T>::dot(cv[jj][1], hb);
-            }
+            static_assert(RW == 4, "the row reduction takes 4 rows per wave");
+            const float d = wave_rowsum4(acc);
+            if ((lane & 15) == 0) zs[wave * RW + (lane >> 4)] = d;
         }
-        const float d = wave_rowsum16(acc);
-        if ((lane & 3) == 0) zs[wave * kRowsPerWave + (lane >> 2)] = d;
     }
     __syncthreads();
     // ---- 3. queue.  Wave 0 first takes the pop decision, which needs only the
     // best child of slot `step` (the largest child key), then hands the
-    // popped node to waves 1-3, which pack the next contraction's activations
-    // while wave 0 sorts the children and updates the queue.
+    // popped node to the other waves: wave 1 sorts the children, the rest
+    // pack the next contraction's activations, while wave 0 updates the queue.
     __shared__ int s_dec[2];  // next GRU token (-1 = idle row), parent slot of the popped node
     __shared__ u64 s_keys[kWave];  // child keys of slot `step`, unsorted
     const float score_step = s_sc[step];
@@ -503,7 +498,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     __syncthreads();
 
-    if (wave == 3) {
+    if (wave == 1) {
         // slot `step`'s children sorted by (log-prob desc, token asc), kept
         // for the sibling pushes of later steps
         if (expand) {
@@ -518,51 +513,46 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
     }
     if (wave != 0) {
         // ---- 4. row b's activations of the next contraction, packed for its
-        // MFMA operands: the popped node's token embedding (wave 1) and its
-        // parent's state in three exact bf16 parts (wave 2); zeros for an idle
-        // row.  The parent is slot `step` (state in LDS) or an older slot
-        // (parts in hsplit).
+        // MFMA operands, 8 elements per lane: the popped node's token
+        // embedding (waves kXw0 ..) and its parent's state in three exact bf16
+        // parts plus binary32 (waves kHw0 ..); zeros for an idle row.  The
+        // parent is slot `step` (state in LDS) or an older slot (parts in
+        // hsplit).
+        constexpr int kXw0 = 2, kXwN = (NW - kXw0 + 1) / 2, kHw0 = kXw0 + kXwN, kHwN = NW - kHw0;
         if (a.xpack && step + 1 < a.n) {
             const int ntok = s_dec[0], vpar = s_dec[1];
             const bool grow = ntok >= 0;
-            if (wave == 1) {
-                const int nxc = a.E >> 5;
-                for (int c = lane; c < nxc; c += kWave) {
-                    u32x4 v[4] = {};
-                    if (grow) {
-                        const bf16_t* src = (const bf16_t*)a.emb + (size_t)ntok * a.E + c * 32;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const u32x4*>(src + 8 * e);
-                    }
-                    uint16_t* dst = a.xpack + pack_index_x(b, c * 32, a.E);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(dst + 8 * e) = v[e];
+            if (wave < kHw0) {
+                const int nv = a.E >> 3;
+                for (int i = (wave - kXw0) * kWave + lane; i < nv; i += kXwN * kWave) {
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (grow) v = *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + (size_t)ntok * a.E + i * 8);
+                    *reinterpret_cast<u32x4*>(a.xpack + pack_index_x(b, i * 8, a.E)) = v;
                 }
             } else {
-                const int nhc = H >> 5;
-                for (int c = lane; c < nhc; c += kWave) {
-                    uint32_t w[3][16] = {};  // 32 elements of each part, two per word
-                    float hv[32];
+                const int nv = H >> 3;
+                for (int i = (wave - kHw0) * kWave + lane; i < nv; i += kHwN * kWave) {
+                    const int k = i * 8;
+                    uint32_t w[3][4] = {};  // 8 elements of each part, two per word
+                    float hv[8];
                     if (grow && vpar == step) {
 #pragma unroll
-                        for (int e = 0; e < 32; ++e) {
-                            hv[e] = hs[c * 32 + e];
+                        for (int e = 0; e < 8; ++e) {
+                            hv[e] = hs[k + e];
                             uint32_t p3[3];
                             split3_bf16(hv[e], p3);
 #pragma unroll
                             for (int qq = 0; qq < 3; ++qq) w[qq][e >> 1] |= p3[qq] << (16 * (e & 1));
                         }
                     } else if (grow) {
-                        const uint16_t* src = a.hsplit + ((slot0 + vpar) * 3) * (size_t)H + c * 32;
+                        const uint16_t* src = a.hsplit + ((slot0 + vpar) * 3) * (size_t)H + k;
 #pragma unroll
-                        for (int qq = 0; qq < 3; ++qq)
+                        for (int qq = 0; qq < 3; ++qq) {
+                            const u32x4 t4 = *reinterpret_cast<const u32x4*>(src + (size_t)qq * H);
+                            w[qq][0] = t4.x; w[qq][1] = t4.y; w[qq][2] = t4.z; w[qq][3] = t4.w;
+                        }
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const u32x4 t4 = *reinterpret_cast<const u32x4*>(src + (size_t)qq * H + 8 * e);
-                                w[qq][4 * e] = t4.x; w[qq][4 * e + 1] = t4.y; w[qq][4 * e + 2] = t4.z; w[qq][4 * e + 3] = t4.w;
-                            }
-#pragma unroll
-                        for (int e = 0; e < 32; ++e) {  // the exact binary32 state
+                        for (int e = 0; e < 8; ++e) {  // the exact binary32 state
                             const int sh = 16 * (e & 1);
                             const float p0 = __uint_as_float(((w[0][e >> 1] >> sh) & 0xFFFFu) << 16);
                             const float p1 = __uint_as_float(((w[1][e >> 1] >> sh) & 0xFFFFu) << 16);
@@ -571,20 +561,15 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
                         }
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 32; ++e) hv[e] = 0.f;
+                        for (int e = 0; e < 8; ++e) hv[e] = 0.f;
                     }
 #pragma unroll
-                    for (int qq = 0; qq < 3; ++qq) {
-                        uint16_t* dst = a.hpack + pack_index_h(b, qq, c * 32, H);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            *reinterpret_cast<u32x4*>(dst + 8 * e) =
-                                u32x4{w[qq][4 * e], w[qq][4 * e + 1], w[qq][4 * e + 2], w[qq][4 * e + 3]};
-                    }
-                    float* hdst = a.hprev + (size_t)b * H + c * 32;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        *reinterpret_cast<f32x4*>(hdst + 4 * e) = f32x4{hv[4 * e], hv[4 * e + 1], hv[4 * e + 2], hv[4 * e + 3]};
+                    for (int qq = 0; qq < 3; ++qq)
+                        *reinterpret_cast<u32x4*>(a.hpack + pack_index_h(b, qq, k, H)) =
+                            u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]};
+                    float* hdst = a.hprev + (size_t)b * H + k;
+                    *reinterpret_cast<f32x4*>(hdst) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+                    *reinterpret_cast<f32x4*>(hdst + 4) = f32x4{hv[4], hv[5], hv[6], hv[7]};
                 }
             }
         }
@@ -680,7 +665,7 @@ __global__ __launch_bounds__(kNodeThreads) void node_step_kernel(NodeArgs a, Nod
 }
 
 template <typename T>
-__global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* tidx, const float* tval,
+__global__ __launch_bounds__(kCorrThreads) void correct_kernel(const int32_t* tidx, const float* tval,
                                                                const T* C, const float* h,
                                                                const int32_t* pos, int32_t* tok_out,
                                                                float* lp_out, int L, int H, int M,
@@ -690,7 +675,7 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
     __shared__ int32_t si[kMaxM];
     __shared__ float sv[kMaxM];
     const int b = blockIdx.x;
-    for (int k = threadIdx.x; k < H; k += kNodeThreads) hs[k] = h[(size_t)b * H + k];
+    for (int k = threadIdx.x; k < H; k += kCorrThreads) hs[k] = h[(size_t)b * H + k];
     const size_t trow = ((size_t)b * L + pos[b]) * M;
     if (threadIdx.x < M) {
         si[threadIdx.x] = tidx[trow + threadIdx.x];
@@ -713,9 +698,11 @@ __global__ __launch_bounds__(kNodeThreads) void correct_kernel(const int32_t* ti
 template <typename T>
 hipError_t launch_node_t(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream,
                          LaunchEvents ev) {
-    const dim3 grid(a.B), block(kNodeThreads);
+    const dim3 grid(a.B), block(node_threads<false>());
     const unsigned shm = (unsigned)lp.bytes;
-    if (a.marginal) return launch_kernel(node_step_kernel<T, 1, true>, grid, block, shm, stream, ev, a, lp, step);
+    if (a.marginal)
+        return launch_kernel(node_step_kernel<T, 1, true>, grid, dim3(node_threads<true>()), shm, stream, ev, a,
+                             lp, step);
     switch (a.ksplit) {
 #define DT_KS(K) \
     case K: return launch_kernel(node_step_kernel<T, K, false>, grid, block, shm, stream, ev, a, lp, step);
@@ -737,10 +724,10 @@ hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C,
                           int H, int M, int dtype, float temp, hipStream_t stream) {
     if (B == 0) return hipSuccess;
     if (dtype == 1)
-        correct_kernel<bf16_t><<<B, kNodeThreads, 0, stream>>>(tidx, tval, (const bf16_t*)C, h, pos,
+        correct_kernel<bf16_t><<<B, kCorrThreads, 0, stream>>>(tidx, tval, (const bf16_t*)C, h, pos,
                                                                tok_sorted, lp_sorted, L, H, M, temp);
     else
-        correct_kernel<float><<<B, kNodeThreads, 0, stream>>>(tidx, tval, (const float*)C, h, pos,
+        correct_kernel<float><<<B, kCorrThreads, 0, stream>>>(tidx, tval, (const float*)C, h, pos,
                                                               tok_sorted, lp_sorted, L, H, M, temp);
     return hipGetLastError();
 }
