@@ -57,6 +57,7 @@ struct GruGatesArgs {
     const void* W_hh;
     float* partial;
     int B, E, H, ksplit, dtype;
+    int xwaves;  // bf16 path: waves per workgroup on the x part (set by the launcher)
 };
 // Packed activations (bf16 elements).  Rows are grouped in blocks of 16 (the
 // MFMA operand rows); a block's K range is cut into 32-wide chunks; one chunk

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
     // state (tokens clamped to the vocabulary), so no load waits on a test.
     const u64 q_m = a.queue[(size_t)b * kWave + lane];
     // slot `step`'s state: the GRU cell on the K-range partial sums of the
-    // preceding contraction, added in K order (read at every step; the root
+    // preceding contraction, added in K-range order (read at every step; the root
     // takes h0 instead)
     const int k1 = (int)threadIdx.x;  // this thread's state element
     const int kc = k1 < H ? k1 : 0;

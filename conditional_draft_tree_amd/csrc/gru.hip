@@ -40,37 +40,50 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Work split.  K is cut into 32-wide chunks: nE chunks of the x part then
-// nH of the h part.  Each tile of 16 hidden units is covered by 8 * ksplit
-// waves (ksplit workgroups of 8 waves); the first WE waves take the x chunks,
-// the others the h chunks (three bf16 parts each, so three times the MFMAs),
-// WE chosen to balance the MFMA work.  A wave issues every load of its chunks
-// (weights and activations) before its first MFMA: one memory round trip.
-struct WaveSplit {
-    int WE;  // waves on the x part (the rest take the h part)
-};
-__host__ __device__ __forceinline__ WaveSplit wave_split(int nE, int nH, int W) {
-    int we = (int)(((long long)W * nE + (nE + 3 * nH) / 2) / max(1, nE + 3 * nH));
-    if (nE > 0) we = max(we, 1);
-    if (nH > 0) we = min(we, W - 1);
-    return WaveSplit{we};
-}
-// [begin, end) of the chunks of wave w (0 <= w < W)
-__host__ __device__ __forceinline__ void wave_chunks(int nE, int nH, int W, int w, int& cb, int& ce) {
-    const int we = wave_split(nE, nH, W).WE;
-    if (w < we) {
-        cb = (int)((long long)w * nE / we);
-        ce = (int)((long long)(w + 1) * nE / we);
-    } else {
-        const int wh = W - we, k = w - we;
-        cb = nE + (int)((long long)k * nH / wh);
-        ce = nE + (int)((long long)(k + 1) * nH / wh);
-    }
-}
-
 constexpr int kWaves8 = 8;
 constexpr int kMaxXChunks = 6;  // x chunks per wave and batch
 constexpr int kMaxHChunks = 2;  // h chunks per wave and batch
+constexpr int kXChunkLoads = 3 + kRowBlocks;      // 16-byte loads per lane of an x chunk
+constexpr int kHChunkLoads = 3 + 3 * kRowBlocks;  // of an h chunk (three activation parts)
+
+// Work split.  K is cut into 32-wide chunks: nE chunks of the x part then
+// nH of the h part (three bf16 parts each, so three times the MFMAs and the
+// activation loads).  Each tile of 16 hidden units is covered by ksplit
+// workgroups of 8 waves; in every workgroup the first WX waves take x chunks
+// and the others h chunks, so that every workgroup loads about the same
+// bytes (the bytes a CU loads set the contraction's time).  WX minimizes
+// the larger per-wave load of the two kinds.  A wave issues every load of
+// its chunks (weights and activations) before its first MFMA: one memory
+// round trip.
+inline int x_waves(int nE, int nH, int ksplit) {
+    if (nH == 0) return kWaves8;
+    if (nE == 0) return 0;
+    int best = 1;
+    long long best_cost = -1;
+    for (int wx = 1; wx < kWaves8; ++wx) {
+        const int nx = ksplit * wx, nh = ksplit * (kWaves8 - wx);
+        const long long cost = max((long long)((nE + nx - 1) / nx) * kXChunkLoads,
+                                   (long long)((nH + nh - 1) / nh) * kHChunkLoads);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = wx;
+        }
+    }
+    return best;
+}
+// [begin, end) of the chunks of wave w (0 <= w < 8) of K range ks, with wx
+// x waves per workgroup
+__device__ __forceinline__ void wave_chunks(int nE, int nH, int ksplit, int wx, int ks, int w, int& cb, int& ce) {
+    if (w < wx) {
+        const int n = ksplit * wx, i = ks * wx + w;
+        cb = (int)((long long)i * nE / n);
+        ce = (int)((long long)(i + 1) * nE / n);
+    } else {
+        const int n = ksplit * (kWaves8 - wx), i = ks * (kWaves8 - wx) + (w - wx);
+        cb = nE + (int)((long long)i * nH / n);
+        ce = nE + (int)((long long)(i + 1) * nH / n);
+    }
+}
 
 __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesArgs a) {
     // every wave's sums of the workgroup's 64 x 16 outputs x 4 gates: 128 KB
@@ -82,7 +95,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                                      // l % 16 with K values 8 * (l / 16) .. + 8
     const int nE = a.E / 32, nH = a.H / 32;
     int cbeg, cend;
-    wave_chunks(nE, nH, kWaves8 * a.ksplit, ks * kWaves8 + wave, cbeg, cend);
+    wave_chunks(nE, nH, a.ksplit, a.xwaves, ks, wave, cbeg, cend);
 
     const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
     const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
@@ -267,8 +280,8 @@ int gru_ksplit(int B, int E, int H, int dtype) {
     const int tiles = (H / 16) * ((B + 63) / 64);
     int best = kMaxKsplit;
     for (int ks = 1; ks <= kMaxKsplit; ++ks) {
-        const int W = kWaves8 * ks, we = wave_split(nE, nH, W).WE;
-        const int xmax = nE ? (nE + we - 1) / we : 0, hmax = nH ? (nH + (W - we) - 1) / (W - we) : 0;
+        const int wx = x_waves(nE, nH, ks), nx = ks * wx, nh = ks * (kWaves8 - wx);
+        const int xmax = nE ? (nE + nx - 1) / nx : 0, hmax = nH ? (nH + nh - 1) / nh : 0;
         if (xmax <= kMaxXChunks && hmax <= kMaxHChunks && tiles * ks >= 192) return ks;
         if (xmax <= kMaxXChunks && hmax <= kMaxHChunks) best = min(best, ks);
     }
@@ -277,9 +290,12 @@ int gru_ksplit(int B, int E, int H, int dtype) {
 
 hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream, LaunchEvents ev) {
     if (a.B == 0) return hipSuccess;
-    if (a.dtype == 1)
+    if (a.dtype == 1) {
+        GruGatesArgs b = a;
+        b.xwaves = x_waves(a.E / 32, a.H / 32, a.ksplit);
         return launch_kernel(gru_gates_bf16_kernel, dim3(a.H / 16, (a.B + 63) / 64, a.ksplit),
-                             dim3(kWaves8 * kWave), 0, stream, ev, a);
+                             dim3(kWaves8 * kWave), 0, stream, ev, b);
+    }
     return launch_kernel(gru_gates_f32_kernel, dim3((a.H + 63) / 64, a.B, 1), dim3(64), 0, stream, ev, a);
 }
 
