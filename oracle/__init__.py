@@ -58,8 +58,10 @@ def _load():
                  f64p, i32p, f64p])
             lib.oracle_score_paths.argtypes = (
                 [C.c_int] * 5 + [C.c_double, C.c_int] + [vp] * 8 + [C.c_int, i32p, i32p, f64p])
+            lib.oracle_accept_greedy.argtypes = [C.c_int, C.c_int, i32p, i32p, i32p, i32p, i32p,
+                                                 i32p]
             for f in (lib.oracle_topm_row, lib.oracle_gru, lib.oracle_dist,
-                      lib.oracle_build_request, lib.oracle_score_paths):
+                      lib.oracle_build_request, lib.oracle_score_paths, lib.oracle_accept_greedy):
                 f.restype = C.c_int
             _lib = lib
     return _lib
@@ -185,3 +187,23 @@ def score_paths(inp: dict, b: int, M: int, paths, T: float = 0.0) -> np.ndarray:
         _ptr(h0b), P, _ptr(arr, C.c_int32), _ptr(lens, C.c_int32), _ptr(out, C.c_double))
     _check(rc, "oracle_score_paths")
     return out[:P]
+
+
+def accept_greedy(tokens, parents, count: int, target) -> dict:
+    """Greedy acceptance walk of one request's tree (slots 0..n): the accepted
+    slots in order (``path``, length ``accepted``), and the target's bonus token."""
+    tok = np.ascontiguousarray(tokens, np.int32)
+    par = np.ascontiguousarray(parents, np.int32)
+    tgt = np.ascontiguousarray(target, np.int32)
+    n = tok.shape[0] - 1
+    if par.shape != tok.shape or tgt.shape != tok.shape:
+        raise ValueError("tokens, parents and target must all have n + 1 entries")
+    path = np.empty(n + 1, np.int32)
+    acc = np.zeros(1, np.int32)
+    bonus = np.zeros(1, np.int32)
+    rc = _load().oracle_accept_greedy(n, int(count), _ptr(tok, C.c_int32), _ptr(par, C.c_int32),
+                                      _ptr(tgt, C.c_int32), _ptr(path, C.c_int32),
+                                      _ptr(acc, C.c_int32), _ptr(bonus, C.c_int32))
+    _check(rc, "oracle_accept_greedy")
+    k = int(acc[0])
+    return {"path": path[:k].copy(), "accepted": k, "bonus": int(bonus[0])}

@@ -36,7 +36,13 @@
  *      "Composants clés -- Tas de recherche de premier choix à score
  *      conditionnel");
  *   5. the prefix-closed tree and its ancestor-only attention mask
- *      ([captcha] "Methodology -- deep read"; [gist] "Vérification").
+ *      ([captcha] "Methodology -- deep read"; [gist] "Vérification");
+ *   6. after verification at temperature 0, the accepted path: the target's
+ *      greedy token at each node decides which child, if any, is accepted
+ *      next ([captcha] "Methodology -- deep read": the longest accepted
+ *      root-to-leaf path of one target forward pass; [gist] "Résultats
+ *      expérimentaux -- Absence de perte": the output equals serial greedy
+ *      decoding).
  *
  * Readings of points the pages leave open (each is also listed in the
  * design notes):
@@ -478,4 +484,48 @@ int oracle_score_paths(int V, int L, int E, int H, int M, double T, int dtype, c
 done:
     free(tidx); free(tval); free(h); free(h2); free(ctok); free(clp);
     return rc;
+}
+
+/*
+ * Greedy (temperature 0) acceptance of one request's verified tree.
+ *
+ * The tree is the builder's output: slots 0..count, slot 0 the root,
+ * tokens[i] and parents[i] for i >= 1.  target[i] is the target model's
+ * greedy next token after the prefix that ends at node i (slot 0: after the
+ * context alone).  Serial greedy decoding emits target[0]; it agrees with
+ * the draft exactly when some child of the root carries that token, and so
+ * on down the tree ([gist] "Résultats expérimentaux -- Absence de perte";
+ * [captcha] "Methodology -- deep read": the longest accepted root-to-leaf
+ * path is verified in one forward pass).  Starting from the root, the walk
+ * moves to the child of the current node whose token equals the target's
+ * token at the current node (children of one node carry distinct tokens;
+ * were two equal, the lower slot is taken) and stops at a node with no such
+ * child.
+ *
+ * Outputs: path[0 .. accepted) the accepted slots in order, the rest of
+ * path[0 .. n] set to -1; *accepted the number of accepted draft tokens;
+ * *bonus the target's token at the last accepted node (the round emits
+ * accepted + 1 tokens).  The walk takes at most n steps, so a malformed
+ * tree cannot make it loop.
+ */
+int oracle_accept_greedy(int n, int count, const int32_t *tokens, const int32_t *parents,
+                         const int32_t *target, int32_t *path, int32_t *accepted, int32_t *bonus)
+{
+    if (n < 1 || !tokens || !parents || !target || !path || !accepted || !bonus) return OR_EINVAL;
+    if (count < 0) count = 0;
+    if (count > n) count = n;
+    for (int i = 0; i <= n; ++i) path[i] = -1;
+    int u = 0, k = 0;
+    while (k < n) {
+        int next = -1;
+        for (int c = 1; c <= count; ++c) {
+            if (parents[c] == u && tokens[c] == target[u]) { next = c; break; }
+        }
+        if (next < 0) break;
+        path[k++] = next;
+        u = next;
+    }
+    *accepted = k;
+    *bonus = target[u];
+    return OR_OK;
 }

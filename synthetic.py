@@ -19,6 +19,12 @@ datasets, which are not available):
   and, for bf16 configurations, rounded to bf16 with round-to-nearest-even.
   bf16 arrays are carried as ``uint16`` bit patterns.
 
+* greedy target tokens ``[B, n+1]`` for the acceptance walk (the target
+  model's argmax after each tree node, which needs the target model): for
+  every slot of a given tree, with probability ``p_follow`` the token of one
+  of that node's children drawn uniformly, otherwise a token drawn uniformly
+  from the vocabulary (slots past ``count``: -1).
+
 Seeds: ``numpy.random.default_rng(SeedSequence([seed, tensor_id, b + 1]))`` for
 per-request tensors (positions drawn in order from that stream); shared
 matrices are drawn in blocks of 8192 rows, block i from
@@ -50,7 +56,8 @@ CONFIGS = {
                    alpha=2.0, T=0.0),
 }
 
-_TID = {"base": 1, "emb": 2, "w_ih": 3, "w_hh": 4, "b_ih": 5, "b_hh": 6, "C": 7, "h0": 8}
+_TID = {"base": 1, "emb": 2, "w_ih": 3, "w_hh": 4, "b_ih": 5, "b_hh": 6, "C": 7, "h0": 8,
+        "target": 9}
 
 
 def _rng(seed: int, name: str, b: int | None):
@@ -180,4 +187,31 @@ def to_torch(inp: dict, device) -> dict:
             out[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(device)
         else:
             out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+    return out
+
+
+def make_greedy_targets(tokens: np.ndarray, parents: np.ndarray, count: np.ndarray, V: int,
+                        p_follow: float, seed: int = 0) -> np.ndarray:
+    """Synthetic greedy target tokens ``[B, n+1]`` int32 for trees ``tokens`` /
+    ``parents`` ``[B, n+1]`` with ``count[b]`` nodes: slot i takes one of node
+    i's child tokens (uniformly) with probability ``p_follow``, else a uniform
+    vocabulary token; slots past ``count[b]`` hold -1."""
+    tokens = np.asarray(tokens)
+    parents = np.asarray(parents)
+    B, S = tokens.shape
+    out = np.full((B, S), -1, np.int32)
+    for b in range(B):
+        rng = _rng(seed, "target", b)
+        c = int(count[b])
+        kids = [[] for _ in range(S)]
+        for j in range(1, c + 1):
+            if 0 <= parents[b, j] < S:
+                kids[int(parents[b, j])].append(int(tokens[b, j]))
+        for i in range(c + 1):
+            follow = rng.random() < p_follow
+            pick = rng.integers(0, 1 << 30)
+            if follow and kids[i]:
+                out[b, i] = kids[i][pick % len(kids[i])]
+            else:
+                out[b, i] = pick % V
     return out

@@ -10,7 +10,10 @@
 * closed forms / special cases: M = 1 chain, n = 1 argmax, L = 1 sorted list,
                 zero correction == factorized (DDTree) tree, a hand-derived
                 example under tests/golden/;
-* metamorphic:  vocabulary relabeling, batch independence.
+* metamorphic:  vocabulary relabeling, batch independence;
+* acceptance walk: hand-derived cases (tests/golden/hand_accept.json), and the
+                accepted path recomputed as the set of nodes whose every root-path
+                edge matches the target, on random trees and on oracle trees.
 """
 import json
 import math
@@ -408,3 +411,108 @@ def test_near_tie_behind_an_exact_structural_tie_is_found():
     np.testing.assert_array_equal(res["tokens"], [-1, 0, 0])
     np.testing.assert_array_equal(res["depths"], [0, 1, 2])
     assert res["flags"] & 1 and 5e-7 < res["min_gap"] < 2e-6
+
+
+# ---- greedy acceptance walk -------------------------------------------------
+
+def _accept_by_matched_set(tokens, parents, count, target):
+    """The accepted path from its definition as a set: node c is accepted iff
+    every edge (p -> child) on its root path has token(child) == target(p).
+    Accepted nodes form one chain (siblings carry distinct tokens); its
+    deepest node ends the walk."""
+    S = len(tokens)
+    acc = {0}
+    changed = True
+    while changed:  # fixed point, no assumption on slot order
+        changed = False
+        for c in range(1, min(count, S - 1) + 1):
+            if c not in acc and parents[c] in acc and tokens[c] == target[parents[c]]:
+                acc.add(c)
+                changed = True
+    depth = {0: 0}
+    def d(c):
+        if c not in depth:
+            depth[c] = d(parents[c]) + 1
+        return depth[c]
+    end = max(acc, key=d)
+    chain = []
+    c = end
+    while c != 0:
+        chain.append(c)
+        c = parents[c]
+    return chain[::-1], int(target[end])
+
+
+def test_accept_hand_derived_cases():
+    g = json.load(open(os.path.join(GOLDEN, "hand_accept.json")))
+    tok, par = g["tree"]["tokens"], g["tree"]["parents"]
+    for case in g["cases"]:
+        r = oracle.accept_greedy(tok, par, case["count"], case["target"])
+        assert r["path"].tolist() == case["path"], case["why"]
+        assert r["accepted"] == len(case["path"])
+        assert r["bonus"] == case["bonus"], case["why"]
+
+
+def _random_tree(rng, n, V, fanout_tokens=6):
+    """A random prefix-closed tree in pop order (parent slot < child slot),
+    siblings with distinct tokens drawn from a small alphabet so that
+    matches are frequent."""
+    tokens = [-1]
+    parents = [-1]
+    kids = {0: set()}
+    for c in range(1, n + 1):
+        for _ in range(100):
+            p = int(rng.integers(0, c))
+            t = int(rng.integers(0, fanout_tokens))
+            if t not in kids[p]:
+                break
+        else:
+            p, t = c - 1, 0
+        kids[p].add(t)
+        kids[c] = set()
+        tokens.append(t)
+        parents.append(p)
+    return np.array(tokens, np.int32), np.array(parents, np.int32)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_equals_matched_set_on_random_trees(seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(50):
+        n = int(rng.integers(1, 20))
+        tok, par = _random_tree(rng, n, 6)
+        count = int(rng.integers(0, n + 1))
+        target = rng.integers(0, 6, size=n + 1).astype(np.int32)
+        r = oracle.accept_greedy(tok, par, count, target)
+        path, bonus = _accept_by_matched_set(tok.tolist(), par.tolist(), count, target.tolist())
+        assert r["path"].tolist() == path
+        assert r["bonus"] == bonus
+
+
+def test_accept_on_oracle_trees_with_synthetic_targets():
+    cfg = S.CONFIGS["tiny"]
+    inp = S.make_inputs(cfg, seed=3)
+    res = oracle.build_request(inp, 0, cfg["M"], cfg["n"])
+    tok, par, cnt = res["tokens"], res["parents"], res["count"]
+    for p_follow in (0.0, 0.5, 1.0):
+        tgt = S.make_greedy_targets(tok[None], par[None], np.array([cnt]), cfg["V"], p_follow, seed=1)[0]
+        r = oracle.accept_greedy(tok, par, cnt, tgt)
+        path, bonus = _accept_by_matched_set(tok.tolist(), par.tolist(), cnt, tgt.tolist())
+        assert r["path"].tolist() == path and r["bonus"] == bonus
+        if p_follow == 1.0:  # every node follows a child while it has one: the walk ends at a leaf
+            end = path[-1] if path else 0
+            assert all(par[c] != end for c in range(1, cnt + 1))
+
+
+def test_accept_special_cases():
+    tok = np.array([-1, 4, 5, 6], np.int32)
+    par = np.array([-1, 0, 1, 2], np.int32)  # a chain
+    # count 0: only the root; bonus is the target's first token
+    r = oracle.accept_greedy(tok, par, 0, [4, 5, 6, 9])
+    assert r["accepted"] == 0 and r["bonus"] == 4
+    # the whole chain accepted: tau = n + 1 tokens in the round
+    r = oracle.accept_greedy(tok, par, 3, [4, 5, 6, 9])
+    assert r["path"].tolist() == [1, 2, 3] and r["bonus"] == 9
+    # a mismatch in the middle stops the walk there
+    r = oracle.accept_greedy(tok, par, 3, [4, 7, 6, 9])
+    assert r["path"].tolist() == [1] and r["bonus"] == 7
