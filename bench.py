@@ -154,6 +154,22 @@ def main():
     torch.cuda.synchronize()
     marg_us = (time.perf_counter() - m0) * 1e6 / max(args.stage_steps, 1)
 
+    # ---- the greedy acceptance walk on the timed trees (extra key): synthetic
+    # greedy target tokens that follow one of a node's children with
+    # probability 0.8
+    tree_cpu = {k: out[k].cpu().numpy() for k in ("tokens", "parents", "count")}
+    tgt = torch.from_numpy(S.make_greedy_targets(tree_cpu["tokens"], tree_cpu["parents"],
+                                                 tree_cpu["count"], V, 0.8, seed=0)).to(dev)
+    acc = bld.accept_greedy(out, tgt)
+    torch.cuda.synchronize()
+    dtree.dt_timing_enable(bld.handle, 1, args.stage_steps)
+    for _ in range(args.stage_steps):
+        bld.accept_greedy(out, tgt, out=acc)
+    torch.cuda.synchronize()
+    acc_us = float(np.mean(dtree.dt_timing_read(bld.handle, 6))) * 1e3 if args.stage_steps else float("nan")
+    dtree.dt_timing_enable(bld.handle, 0, 0)
+    tau = float((acc["accepted"].float() + 1).mean())
+
     if args.copy_calib:  # a plain copy of known size, for counter scaling
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -211,6 +227,9 @@ def main():
         "latency_per_request_us": round(ms_per_step * 1e3, 1),
         "marginal_mode": {"us_per_round": round(marg_us, 1),
                           "tree_builds_per_s": round(B / (marg_us * 1e-6), 1)},
+        "acceptance_walk": {"kernel_us": round(acc_us, 2), "requests": B,
+                            "mean_tokens_per_round_synthetic_targets": round(tau, 3),
+                            "target_follow_probability": 0.8},
     }
 
     # ---- CPU baseline: the oracle as it stands, one request per thread

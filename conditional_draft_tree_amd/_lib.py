@@ -61,11 +61,12 @@ def load_library():
         lib.dt_topm.argtypes = [H, vp, C.c_size_t, vp, i32p, f32p, vp]
         lib.dt_gru_step.argtypes = [H, vp, C.c_size_t, vp, f32p, vp, vp, vp, vp, f32p, vp]
         lib.dt_correct.argtypes = [H, i32p, f32p, vp, f32p, i32p, i32p, f32p, vp]
+        lib.dt_accept_greedy.argtypes = [H] + [i32p] * 7 + [vp]
         lib.dt_timing_enable.argtypes = [H, C.c_int, C.c_int]
         lib.dt_timing_read.argtypes = [H, C.c_int, C.POINTER(C.c_float), C.c_int,
                                        C.POINTER(C.c_int)]
         for f in (lib.dt_create, lib.dt_build, lib.dt_build_marginal, lib.dt_topm, lib.dt_gru_step,
-                  lib.dt_correct,
+                  lib.dt_correct, lib.dt_accept_greedy,
                   lib.dt_timing_enable, lib.dt_timing_read):
             f.restype = C.c_int
         _lib = lib
@@ -152,6 +153,12 @@ def dt_correct(handle, idx, val, Cmat, h, pos, tok_sorted, logp_sorted, stream=N
     lib = load_library()
     _check(lib.dt_correct(handle, _p(idx), _p(val), _p(Cmat), _p(h), _p(pos), _p(tok_sorted),
                           _p(logp_sorted), _stream(stream)), handle)
+
+
+def dt_accept_greedy(handle, tokens, parents, count, target, path, accepted, bonus, stream=None):
+    lib = load_library()
+    _check(lib.dt_accept_greedy(handle, _p(tokens), _p(parents), _p(count), _p(target), _p(path),
+                                _p(accepted), _p(bonus), _stream(stream)), handle)
 
 
 def dt_timing_enable(handle, level: int, capacity: int):
@@ -299,3 +306,22 @@ class Builder:
         lp = torch.empty((B, M), dtype=torch.float32, device=self.device)
         dt_correct(self.handle, idx, val, Cmat, h, pos, tok, lp, stream)
         return tok, lp
+
+    def accept_greedy(self, tree, target, out=None, stream=None):
+        """Greedy acceptance walk of the trees in ``tree`` (dt_build's outputs:
+        tokens, parents, count) against the target's greedy tokens ``target``
+        [B, n+1] int32.  Returns dict(path [B, n+1], accepted [B], bonus [B])
+        (``out``, if given, is filled and returned)."""
+        import torch
+        B, S = self.cfg["B"], self.cfg["n"] + 1
+        self._chk("tokens", tree["tokens"], (B, S), dtype=torch.int32)
+        self._chk("parents", tree["parents"], (B, S), dtype=torch.int32)
+        self._chk("count", tree["count"], (B,), dtype=torch.int32)
+        self._chk("target", target, (B, S), dtype=torch.int32)
+        dev = self.device
+        res = out if out is not None else dict(path=torch.empty((B, S), dtype=torch.int32, device=dev),
+                                               accepted=torch.empty((B,), dtype=torch.int32, device=dev),
+                                               bonus=torch.empty((B,), dtype=torch.int32, device=dev))
+        dt_accept_greedy(self.handle, tree["tokens"], tree["parents"], tree["count"], target, res["path"],
+                         res["accepted"], res["bonus"], stream)
+        return res

@@ -28,7 +28,8 @@ struct Layout {
 struct Marker {
     // 'K'/'T' begin/end of the top-M select kernel, 'M' after the top-M merge,
     // 'g'/'G' begin/end of a gate contraction, 'n'/'N' of a node step, 'E'
-    // end of the call.  A stage's time is the span from the preceding marker.
+    // end of the call; 'a'/'A' begin/end of a dt_accept_greedy kernel.  A
+    // stage's time is the span from the preceding marker.
     char tag;
     hipEvent_t ev;
 };
@@ -228,7 +229,7 @@ dt_status dt_timing_enable(dt_handle* h, int level, int capacity) {
 
 dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out) {
     if (!h || !n_out || (max > 0 && !ms)) return h ? fail(h, DT_ERR_INVALID_ARG, "null output") : DT_ERR_INVALID_ARG;
-    if (stage < 0 || stage > 5) return fail(h, DT_ERR_INVALID_ARG, "stage must be 0..5");
+    if (stage < 0 || stage > 6) return fail(h, DT_ERR_INVALID_ARG, "stage must be 0..6");
     int n = 0;
     for (const auto& call : h->calls) {
         float sum = 0.f;
@@ -237,7 +238,7 @@ dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out
             const char tag = call[i].tag;
             bool hit = (stage == 0 && tag == 'T') || (stage == 1 && tag == 'M') ||
                        (stage == 2 && tag == 'G') || (stage == 3 && tag == 'N') ||
-                       (stage == 5 && tag == 'G');
+                       (stage == 5 && tag == 'G') || (stage == 6 && tag == 'A');
             if (!hit) continue;
             float t = 0.f;
             hipError_t e = hipEventElapsedTime(&t, call[i - 1].ev, call[i].ev);
@@ -337,6 +338,27 @@ dt_status dt_correct(dt_handle* h, const int32_t* idx, const float* val, const v
     hipError_t e = dt::launch_correct(idx, val, C, h_in, pos, tok_sorted, logp_sorted, c.B, c.L, c.H,
                                       c.M, (int)c.dtype, c.temperature, (hipStream_t)stream);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_correct launch");
+}
+
+dt_status dt_accept_greedy(dt_handle* h, const int32_t* tokens, const int32_t* parents, const int32_t* count,
+                           const int32_t* target, int32_t* path, int32_t* accepted, int32_t* bonus,
+                           void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (c.B == 0) return DT_OK;
+    if (!tokens || !parents || !count || !target || !path || !accepted || !bonus)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_accept_greedy: null pointer");
+    std::vector<Marker>* call = nullptr;
+    if (h->tlevel > 0 && (int)h->calls.size() < h->tcapacity) {
+        h->calls.emplace_back();
+        call = &h->calls.back();
+    }
+    dt::LaunchEvents ev{};
+    hipError_t e = kernel_marks(h, call, 1, 'a', 'A', &ev);
+    if (e != hipSuccess) return hip_fail(h, e, "timing event");
+    e = dt::launch_accept_greedy(tokens, parents, count, target, c.B, c.n, path, accepted, bonus,
+                                 (hipStream_t)stream, ev);
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_accept_greedy launch");
 }
 
 }  // extern "C"

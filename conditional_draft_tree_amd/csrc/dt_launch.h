@@ -140,4 +140,11 @@ hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C,
                           const int32_t* pos, int32_t* tok_sorted, float* lp_sorted, int B, int L,
                           int H, int M, int dtype, float temp, hipStream_t stream);
 
+// ---- greedy acceptance walk (accept.hip) --------------------------------------
+// trees [B, n+1] as dt_build writes them, target [B, n+1] -> path [B, n+1],
+// accepted [B], bonus [B]
+hipError_t launch_accept_greedy(const int32_t* tokens, const int32_t* parents, const int32_t* count,
+                                const int32_t* target, int B, int n, int32_t* path, int32_t* accepted,
+                                int32_t* bonus, hipStream_t stream, LaunchEvents ev = {});
+
 }  // namespace dt

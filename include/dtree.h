@@ -186,8 +186,41 @@ dt_status dt_correct(dt_handle *h, const int32_t *idx, const float *val, const v
                      float *logp_sorted, void *stream);
 
 /*
+ * dt_accept_greedy -- greedy (temperature 0) acceptance of B verified trees.
+ *
+ * After one target forward pass over the tree (ancestor-only mask), serial
+ * greedy decoding agrees with the draft along one root path: at the current
+ * node, first the root, the target's greedy token selects the child carrying
+ * it, and the walk stops at a node with no such child; the target's token
+ * there is also emitted, so a round yields accepted + 1 tokens
+ * ([captcha] "Methodology -- deep read": the longest accepted root-to-leaf
+ * path of one verification pass; [gist] "Résultats expérimentaux -- Absence
+ * de perte": lossless against serial greedy decoding).
+ *
+ *   tokens, parents [B, n+1] int32, count [B] int32: a tree as dt_build
+ *                   writes it (slot 0 = root; slots 1..count are nodes;
+ *                   count is clamped to [0, n]).  Children of one node
+ *                   should carry distinct tokens; if two match, the lower
+ *                   slot is taken.
+ *   target [B, n+1] int32: target[b][i] = the target model's greedy token
+ *                   after the prefix that ends at node i (slot 0: after the
+ *                   context); slots past count are not read.
+ *   path   [B, n+1] int32 (out): the accepted slots in order, then -1.
+ *   accepted [B] int32 (out): number of accepted draft tokens (0..n).
+ *   bonus    [B] int32 (out): the target's token at the last accepted node.
+ *
+ * Device pointers, borrowed; asynchronous on `stream`; B = 0 is a no-op.
+ * Errors: DT_ERR_INVALID_ARG for a null pointer (before any launch),
+ * DT_ERR_HIP if the launch fails.  Uses no workspace.
+ */
+dt_status dt_accept_greedy(dt_handle *h, const int32_t *tokens, const int32_t *parents,
+                           const int32_t *count, const int32_t *target, int32_t *path,
+                           int32_t *accepted, int32_t *bonus, void *stream);
+
+/*
  * Stage timing for benchmarks.  dt_timing_enable(h, level, capacity) makes
- * the next `capacity` dt_build calls record HIP events on their stream:
+ * the next `capacity` dt_build (or dt_accept_greedy) calls record HIP events
+ * on their stream:
  * level 1 on the top-M select kernel only, level 2 on every kernel; level 0
  * turns timing off and drops recorded events.  A kernel's events are taken
  * by its launch (hipExtLaunchKernel), so they span the kernel alone, not the
@@ -200,6 +233,7 @@ dt_status dt_correct(dt_handle *h, const int32_t *idx, const float *val, const v
  *   stage 3  node (correction + queue) kernels, summed    (level 2)
  *   stage 4  the whole call
  *   stage 5  GRU gate contraction, every launch separately (level 2)
+ *   stage 6  the dt_accept_greedy kernel (one launch per call)
  * Timing calls are host-side and need the handle's device to be current.
  */
 dt_status dt_timing_enable(dt_handle *h, int level, int capacity);

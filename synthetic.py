@@ -21,9 +21,14 @@ datasets, which are not available):
 
 * greedy target tokens ``[B, n+1]`` for the acceptance walk (the target
   model's argmax after each tree node, which needs the target model): for
-  every slot of a given tree, with probability ``p_follow`` the token of one
-  of that node's children drawn uniformly, otherwise a token drawn uniformly
-  from the vocabulary (slots past ``count``: -1).
+  every slot of a given tree, with probability ``p_follow`` the token of that
+  node's earliest child (lowest slot: the draft's own first choice there),
+  otherwise a token drawn uniformly from the vocabulary (slots past
+  ``count``: -1);
+* random trees ``[B, n+1]`` in the builder's output format (for the acceptance
+  walk on its own): slot c > 0 gets a parent drawn uniformly from slots < c
+  and a token drawn from a small alphabet, distinct among siblings; the node
+  count is drawn uniformly from 0..n, or is n.
 
 Seeds: ``numpy.random.default_rng(SeedSequence([seed, tensor_id, b + 1]))`` for
 per-request tensors (positions drawn in order from that stream); shared
@@ -57,7 +62,7 @@ CONFIGS = {
 }
 
 _TID = {"base": 1, "emb": 2, "w_ih": 3, "w_hh": 4, "b_ih": 5, "b_hh": 6, "C": 7, "h0": 8,
-        "target": 9}
+        "target": 9, "tree": 10}
 
 
 def _rng(seed: int, name: str, b: int | None):
@@ -193,8 +198,8 @@ def to_torch(inp: dict, device) -> dict:
 def make_greedy_targets(tokens: np.ndarray, parents: np.ndarray, count: np.ndarray, V: int,
                         p_follow: float, seed: int = 0) -> np.ndarray:
     """Synthetic greedy target tokens ``[B, n+1]`` int32 for trees ``tokens`` /
-    ``parents`` ``[B, n+1]`` with ``count[b]`` nodes: slot i takes one of node
-    i's child tokens (uniformly) with probability ``p_follow``, else a uniform
+    ``parents`` ``[B, n+1]`` with ``count[b]`` nodes: slot i takes the token of
+    node i's earliest child with probability ``p_follow``, else a uniform
     vocabulary token; slots past ``count[b]`` hold -1."""
     tokens = np.asarray(tokens)
     parents = np.asarray(parents)
@@ -211,7 +216,39 @@ def make_greedy_targets(tokens: np.ndarray, parents: np.ndarray, count: np.ndarr
             follow = rng.random() < p_follow
             pick = rng.integers(0, 1 << 30)
             if follow and kids[i]:
-                out[b, i] = kids[i][pick % len(kids[i])]
+                out[b, i] = kids[i][0]
             else:
                 out[b, i] = pick % V
     return out
+
+
+def make_random_trees(B: int, n: int, V: int, seed: int = 0, alphabet: int = 6,
+                      full: bool = False):
+    """Random prefix-closed trees in pop order: (tokens, parents) [B, n+1] int32
+    and count [B] int32.  Tokens come from an alphabet of ``alphabet`` ids
+    spread over the vocabulary, distinct among the children of one node."""
+    alphabet = max(1, min(alphabet, V))
+    step = max(1, V // alphabet)
+    tok = np.full((B, n + 1), -1, np.int32)
+    par = np.full((B, n + 1), -1, np.int32)
+    cnt = np.zeros(B, np.int32)
+    for b in range(B):
+        rng = _rng(seed, "tree", b)
+        kids = {0: set()}
+        for c in range(1, n + 1):
+            p, t = c - 1, None
+            for _ in range(64):
+                p = int(rng.integers(0, c))
+                a = int(rng.integers(0, alphabet))
+                if a not in kids[p]:
+                    t = a
+                    break
+            if t is None:  # every draw collided: hang the node under its predecessor
+                p = c - 1
+                t = int(rng.integers(0, alphabet))
+            kids[p].add(t)
+            kids[c] = set()
+            tok[b, c] = t * step
+            par[b, c] = p
+        cnt[b] = n if full else int(rng.integers(0, n + 1))
+    return tok, par, cnt

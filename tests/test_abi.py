@@ -118,6 +118,19 @@ def test_build_marginal_argument_errors_before_any_launch():
     dtree.dt_destroy(h)
 
 
+def test_accept_greedy_null_pointer_before_any_launch():
+    lib = dtree.load_library()
+    h = make()
+    fake = C.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    for i in range(7):
+        args = [fake] * 7
+        args[i] = None
+        assert lib.dt_accept_greedy(h, *args, None) == -1
+        assert "null" in dtree.dt_last_error(h)
+    assert lib.dt_accept_greedy(None, *([fake] * 7), None) == -1
+    dtree.dt_destroy(h)
+
+
 def test_empty_batch_is_a_noop():
     lib = dtree.load_library()
     h = make(B=0)
@@ -125,6 +138,7 @@ def test_empty_batch_is_a_noop():
     assert lib.dt_build(h, None, 0, *([None] * 15), None) == 0
     assert lib.dt_build_marginal(h, None, 0, *([None] * 8), None) == 0
     assert lib.dt_topm(h, None, 0, None, None, None, None) == 0
+    assert lib.dt_accept_greedy(h, *([None] * 7), None) == 0
     dtree.dt_destroy(h)
 
 
@@ -136,5 +150,7 @@ def test_timing_argument_checks():
     assert lib.dt_timing_enable(h, 0, 0) == 0
     n = C.c_int(0)
     assert lib.dt_timing_read(h, 9, None, 0, C.byref(n)) == -1
+    assert lib.dt_timing_read(h, 7, None, 0, C.byref(n)) == -1
     assert lib.dt_timing_read(h, 0, None, 0, C.byref(n)) == 0 and n.value == 0
+    assert lib.dt_timing_read(h, 6, None, 0, C.byref(n)) == 0 and n.value == 0
     dtree.dt_destroy(h)

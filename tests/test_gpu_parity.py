@@ -5,9 +5,12 @@ depths, order, mask, count) bit-exact for every request whose decisions all
 clear the near-tie threshold; node scores within 1e-4 absolute.  Requests
 with a near tie are checked for validity and for the multiset of scores.
 Workloads: the named configurations at their real sizes (sampled requests
-where the oracle would be slow), plus edge cases.
+where the oracle would be slow), plus edge cases.  The greedy acceptance walk
+(integer work) is bit-exact on every request.
 """
 import functools
+import json
+import os
 import sys
 
 import numpy as np
@@ -278,3 +281,81 @@ def test_marginal_qwen3_4b_batched_equals_zero_correction_build():
     bld.close()
     for k in got:
         np.testing.assert_array_equal(got[k], full[k], err_msg=f"marginal mode differs from C = 0 in {k}")
+
+
+# ---- greedy acceptance walk --------------------------------------------------
+
+def accept_and_compare(tok, par, cnt, tgt):
+    """dt_accept_greedy on the given trees and targets against the oracle walk,
+    every request, bit-exact."""
+    B, S1 = tok.shape
+    n = S1 - 1
+    say(f"  accept B={B} n={n}")
+    bld = dtree.Builder(B, 8, 1000, 32, 32, 8, n, 0.0, "f32", device=DEV)  # the walk uses B and n
+    tree = {"tokens": torch.from_numpy(np.ascontiguousarray(tok)).to(DEV),
+            "parents": torch.from_numpy(np.ascontiguousarray(par)).to(DEV),
+            "count": torch.from_numpy(np.ascontiguousarray(cnt)).to(DEV)}
+    res = bld.accept_greedy(tree, torch.from_numpy(np.ascontiguousarray(tgt)).to(DEV))
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in res.items()}
+    bld.close()
+    for b in range(B):
+        r = oracle.accept_greedy(tok[b], par[b], int(cnt[b]), tgt[b])
+        want = np.full(S1, -1, np.int32)
+        want[:r["accepted"]] = r["path"]
+        np.testing.assert_array_equal(got["path"][b], want, err_msg=f"path of request {b}")
+        assert got["accepted"][b] == r["accepted"], b
+        assert got["bonus"][b] == r["bonus"], b
+    return got
+
+
+def test_accept_hand_derived_cases():
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "hand_accept.json")))
+    cases = g["cases"]
+    B = len(cases)
+    tok = np.array([g["tree"]["tokens"]] * B, np.int32)
+    par = np.array([g["tree"]["parents"]] * B, np.int32)
+    cnt = np.array([c["count"] for c in cases], np.int32)
+    tgt = np.array([c["target"] for c in cases], np.int32)
+    got = accept_and_compare(tok, par, cnt, tgt)
+    for b, c in enumerate(cases):
+        assert got["path"][b][:len(c["path"])].tolist() == c["path"], c["why"]
+        assert got["bonus"][b] == c["bonus"], c["why"]
+
+
+@pytest.mark.parametrize("B,n,p_follow,full", [(1, 1, 1.0, True), (64, 16, 0.3, False),
+                                                (64, 16, 0.9, True), (70, 64, 0.8, False),
+                                                (3, 64, 1.0, True)])
+def test_accept_random_trees(B, n, p_follow, full):
+    V = 151936
+    tok, par, cnt = S.make_random_trees(B, n, V, seed=B * 100 + n, full=full)
+    tgt = S.make_greedy_targets(tok, par, cnt, V, p_follow, seed=n)
+    accept_and_compare(tok, par, cnt, tgt)
+
+
+def test_accept_full_chain_of_64():
+    # a chain of n = 64 nodes all accepted: path entries 0..63 are slots 1..64, entry 64 stays -1
+    n, B = 64, 2
+    tok = np.tile(np.arange(-1, n, dtype=np.int32) * 3, (B, 1))
+    tok[:, 0] = -1
+    par = np.tile(np.arange(-1, n, dtype=np.int32), (B, 1))
+    cnt = np.array([n, n - 1], np.int32)
+    tgt = np.zeros((B, n + 1), np.int32)
+    tgt[:, :n] = tok[:, 1:]
+    tgt[:, n] = 7
+    got = accept_and_compare(tok, par, cnt, tgt)
+    assert got["accepted"].tolist() == [64, 63]
+    assert got["bonus"].tolist() == [7, tgt[1, 63]]
+
+
+def test_accept_on_oracle_built_trees():
+    cfg = S.with_config("tiny", B=4)
+    inp = S.make_inputs(cfg, seed=5)
+    trees = oracle.build_batch(inp, cfg["M"], cfg["n"])
+    tok = np.stack([t["tokens"] for t in trees]).astype(np.int32)
+    par = np.stack([t["parents"] for t in trees]).astype(np.int32)
+    cnt = np.array([t["count"] for t in trees], np.int32)
+    for p_follow in (0.0, 0.6, 1.0):
+        tgt = S.make_greedy_targets(tok, par, cnt, cfg["V"], p_follow, seed=2)
+        accept_and_compare(tok, par, cnt, tgt)
