@@ -51,16 +51,17 @@ def _load():
             lib.oracle_gru.argtypes = [vp, C.c_int64, C.c_int, f64p, vp, vp, vp, vp, C.c_int,
                                        C.c_int, f64p]
             lib.oracle_dist.argtypes = [i32p, f64p, C.c_int, vp, C.c_int, C.c_int, f64p,
-                                        C.c_double, i32p, f64p]
+                                        C.c_double, C.c_double, i32p, f64p]
+            lib.oracle_tail_lse.argtypes = [vp, C.c_int, C.c_int, C.c_int, C.c_double, i32p, f64p]
             lib.oracle_build_request.argtypes = (
                 [C.c_int] * 6 + [C.c_double, C.c_int, C.c_double] + [vp] * 8 +
                 [i32p, i32p, i32p, f64p, C.POINTER(C.c_uint8), i32p, C.POINTER(C.c_uint32),
-                 f64p, i32p, f64p])
+                 f64p, i32p, f64p, C.c_int, f64p])
             lib.oracle_score_paths.argtypes = (
-                [C.c_int] * 5 + [C.c_double, C.c_int] + [vp] * 8 + [C.c_int, i32p, i32p, f64p])
+                [C.c_int] * 5 + [C.c_double, C.c_int] + [vp] * 8 + [C.c_int, i32p, i32p, f64p, C.c_int])
             lib.oracle_accept_greedy.argtypes = [C.c_int, C.c_int, i32p, i32p, i32p, i32p, i32p,
                                                  i32p]
-            for f in (lib.oracle_topm_row, lib.oracle_gru, lib.oracle_dist,
+            for f in (lib.oracle_topm_row, lib.oracle_gru, lib.oracle_dist, lib.oracle_tail_lse,
                       lib.oracle_build_request, lib.oracle_score_paths, lib.oracle_accept_greedy):
                 f.restype = C.c_int
             _lib = lib
@@ -109,8 +110,22 @@ def gru(xmat: np.ndarray, xrow: int, h: np.ndarray, w_ih, w_hh, b_ih=None, b_hh=
     return out
 
 
-def dist(idx: np.ndarray, val: np.ndarray, Cmat: np.ndarray, h: np.ndarray, T: float = 0.0):
-    """Sorted children (tok int32 [M], logp float64 [M]) of a node with state h."""
+def tail_lse(row: np.ndarray, M: int, T: float = 0.0) -> float:
+    """log sum of exp(x / T) (T = 1 when T = 0) over the row's logits outside its
+    top M (the full-vocabulary mode's tail); -inf when M = V."""
+    row = np.ascontiguousarray(row)
+    idx, _ = topm_row(row, M)
+    out = np.zeros(1, np.float64)
+    _check(_load().oracle_tail_lse(_ptr(row), _dt(row), row.shape[0], M, float(T), _ptr(idx, C.c_int32),
+                                   _ptr(out, C.c_double)), "oracle_tail_lse")
+    return float(out[0])
+
+
+def dist(idx: np.ndarray, val: np.ndarray, Cmat: np.ndarray, h: np.ndarray, T: float = 0.0,
+         tail: float = -np.inf):
+    """Sorted children (tok int32 [M], logp float64 [M]) of a node with state h;
+    ``tail`` (the row's tail_lse) adds the rest of the vocabulary to the
+    normalizer (-inf: normalized over the M-slice)."""
     idx = np.ascontiguousarray(idx, np.int32)
     val = np.ascontiguousarray(val, np.float64)
     h = np.ascontiguousarray(h, np.float64)
@@ -118,15 +133,17 @@ def dist(idx: np.ndarray, val: np.ndarray, Cmat: np.ndarray, h: np.ndarray, T: f
     tok = np.empty(M, np.int32)
     lp = np.empty(M, np.float64)
     _check(_load().oracle_dist(_ptr(idx, C.c_int32), _ptr(val, C.c_double), M, _ptr(Cmat), _dt(Cmat),
-                               H, _ptr(h, C.c_double), float(T), _ptr(tok, C.c_int32),
+                               H, _ptr(h, C.c_double), float(T), float(tail), _ptr(tok, C.c_int32),
                                _ptr(lp, C.c_double)), "oracle_dist")
     return tok, lp
 
 
-def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float = 1e-5) -> dict:
+def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float = 1e-5,
+                  full_vocab: bool = False) -> dict:
     """Tree of request b.  ``inp`` holds numpy arrays: base [B,L,V], emb [V,E],
     w_ih [3H,E], w_hh [3H,H], b_ih/b_hh [3H] (or None), C [V,H], h0 [B,H] float32
-    (or None)."""
+    (or None).  ``full_vocab``: normalize children over the whole vocabulary
+    (corrected top-M plus the uncorrected tail; ``tail`` [L] is returned)."""
     base = np.ascontiguousarray(inp["base"][b])
     L, V = base.shape
     E, H = inp["w_ih"].shape[1], inp["w_hh"].shape[1]
@@ -135,7 +152,8 @@ def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float 
                depths=np.empty(S, np.int32), scores=np.empty(S, np.float64),
                mask=np.empty((S, S), np.uint8), count=np.zeros(1, np.int32),
                flags=np.zeros(1, np.uint32), min_gap=np.zeros(1, np.float64),
-               topm_idx=np.empty((L, M), np.int32), topm_val=np.empty((L, M), np.float64))
+               topm_idx=np.empty((L, M), np.int32), topm_val=np.empty((L, M), np.float64),
+               tail=np.empty(L, np.float64))
     h0 = inp.get("h0")
     h0b = None if h0 is None else np.ascontiguousarray(h0[b], np.float32)
     rc = _load().oracle_build_request(
@@ -146,7 +164,8 @@ def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float 
         _ptr(out["depths"], C.c_int32), _ptr(out["scores"], C.c_double),
         _ptr(out["mask"], C.c_uint8), _ptr(out["count"], C.c_int32),
         _ptr(out["flags"], C.c_uint32), _ptr(out["min_gap"], C.c_double),
-        _ptr(out["topm_idx"], C.c_int32), _ptr(out["topm_val"], C.c_double))
+        _ptr(out["topm_idx"], C.c_int32), _ptr(out["topm_val"], C.c_double), int(bool(full_vocab)),
+        _ptr(out["tail"], C.c_double))
     _check(rc, "oracle_build_request")
     out["count"] = int(out["count"][0])
     out["flags"] = int(out["flags"][0])
@@ -155,19 +174,19 @@ def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float 
 
 
 def build_batch(inp: dict, M: int, n: int, T: float = 0.0, eps: float = 1e-5,
-                requests=None, threads: int = 1) -> list:
+                requests=None, threads: int = 1, full_vocab: bool = False) -> list:
     """Trees of several requests; each request is one single-threaded oracle
     call, spread over ``threads`` worker threads (the C call drops the GIL)."""
     B = inp["base"].shape[0]
     reqs = list(range(B)) if requests is None else list(requests)
     _load()
     if threads <= 1:
-        return [build_request(inp, b, M, n, T, eps) for b in reqs]
+        return [build_request(inp, b, M, n, T, eps, full_vocab) for b in reqs]
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        return list(ex.map(lambda b: build_request(inp, b, M, n, T, eps), reqs))
+        return list(ex.map(lambda b: build_request(inp, b, M, n, T, eps, full_vocab), reqs))
 
 
-def score_paths(inp: dict, b: int, M: int, paths, T: float = 0.0) -> np.ndarray:
+def score_paths(inp: dict, b: int, M: int, paths, T: float = 0.0, full_vocab: bool = False) -> np.ndarray:
     """Conditional score of each token path (list of token lists) of request b."""
     base = np.ascontiguousarray(inp["base"][b])
     L, V = base.shape
@@ -184,7 +203,8 @@ def score_paths(inp: dict, b: int, M: int, paths, T: float = 0.0) -> np.ndarray:
     rc = _load().oracle_score_paths(
         V, L, E, H, M, float(T), _dt(base), _ptr(base), _ptr(inp["emb"]), _ptr(inp["w_ih"]),
         _ptr(inp["w_hh"]), _ptr(inp.get("b_ih")), _ptr(inp.get("b_hh")), _ptr(inp["C"]),
-        _ptr(h0b), P, _ptr(arr, C.c_int32), _ptr(lens, C.c_int32), _ptr(out, C.c_double))
+        _ptr(h0b), P, _ptr(arr, C.c_int32), _ptr(lens, C.c_int32), _ptr(out, C.c_double),
+        int(bool(full_vocab)))
     _check(rc, "oracle_score_paths")
     return out[:P]
 

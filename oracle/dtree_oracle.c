@@ -68,7 +68,17 @@
  *     expérimentaux -- Absence de perte"): mathematically equal scores
  *     reached through different additions are such tie-breaks;
  *   - the hidden state is a real-valued state: it is never rounded to the
- *     storage type of the weights (the pages fix no precision for it).
+ *     storage type of the weights (the pages fix no precision for it);
+ *   - full-vocabulary normalization (an optional mode): the pages say the
+ *     per-node correction is restricted to the top-M candidates and that
+ *     the restriction leaves the tree shape unchanged ([captcha] "Key
+ *     findings", "Methodology -- deep read"), but not over which tokens the
+ *     softmax runs.  In this mode a node's children are normalized over the
+ *     whole vocabulary: the corrected top-M logits plus the uncorrected
+ *     logits of every other token (the tail), i.e. the normalizer adds
+ *     exp(tail_lse) with tail_lse = log sum over v outside the top-M of
+ *     exp(base_v / T) (T = 1 when T = 0).  The default mode normalizes over
+ *     the M-slice only.
  *
  * Arithmetic is double precision throughout; fp32 and bf16 inputs are
  * widened exactly.
@@ -132,6 +142,34 @@ int oracle_topm_row(const void *row, int dtype, int V, int M, int32_t *idx, doub
     return OR_OK;
 }
 
+/* Log of the summed exponentials of the row's logits outside its top-M set
+ * idx[0..M), each divided by T when T > 0 (full-vocabulary normalization);
+ * -inf when the top-M set is the whole row. */
+int oracle_tail_lse(const void *row, int dtype, int V, int M, double T, const int32_t *idx, double *out)
+{
+    if (!row || !idx || !out || V < 1 || M < 1 || M > V || T < 0.0) return OR_EINVAL;
+    unsigned char *in_top = (unsigned char *)calloc((size_t)V, 1);
+    if (!in_top) return OR_ENOMEM;
+    for (int j = 0; j < M; ++j) {
+        if (idx[j] < 0 || idx[j] >= V) { free(in_top); return OR_EINVAL; }
+        in_top[idx[j]] = 1;
+    }
+    const double scale = T > 0.0 ? 1.0 / T : 1.0;
+    double mx = -INFINITY;
+    for (int t = 0; t < V; ++t)
+        if (!in_top[t]) {
+            double x = load_elem(row, dtype, (size_t)t) * scale;
+            if (x > mx) mx = x;
+        }
+    double sum = 0.0;
+    if (mx > -INFINITY)
+        for (int t = 0; t < V; ++t)
+            if (!in_top[t]) sum += exp(load_elem(row, dtype, (size_t)t) * scale - mx);
+    *out = sum > 0.0 ? mx + log(sum) : -INFINITY;
+    free(in_top);
+    return OR_OK;
+}
+
 /* ---- 2. one GRU step ------------------------------------------------------ */
 
 static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -188,10 +226,12 @@ static int child_cmp(const void *a, const void *b)
     return (x->tok > y->tok) - (x->tok < y->tok);
 }
 
-/* z_j = val_j + C[idx_j] . h ; z /= T if T > 0 ; log-softmax over j < M ;
- * children sorted by (log-prob desc, token asc). */
+/* z_j = val_j + C[idx_j] . h ; z /= T if T > 0 ; log-softmax over j < M,
+ * with exp(tail) added to the normalizer (tail = -inf: the M-slice alone;
+ * else the full-vocabulary mode's tail_lse of the node's row) ; children
+ * sorted by (log-prob desc, token asc). */
 int oracle_dist(const int32_t *idx, const double *val, int M, const void *C, int dtype,
-                int H, const double *h, double T, int32_t *tok_sorted, double *lp_sorted)
+                int H, const double *h, double T, double tail, int32_t *tok_sorted, double *lp_sorted)
 {
     if (!idx || !val || !C || !h || !tok_sorted || !lp_sorted || M < 1 || H < 1 || T < 0.0)
         return OR_EINVAL;
@@ -209,9 +249,11 @@ int oracle_dist(const int32_t *idx, const double *val, int M, const void *C, int
     double m = z[0];
     for (int j = 1; j < M; ++j)
         if (z[j] > m) m = z[j];
+    if (tail > m) m = tail;
     double s = 0.0;
     for (int j = 0; j < M; ++j)
         s += exp(z[j] - m);
+    if (tail > -INFINITY) s += exp(tail - m);
     double ls = log(s);
     for (int j = 0; j < M; ++j) {
         ch[j].lp = (z[j] - m) - ls;
@@ -322,14 +364,18 @@ static qent_t q_pop(queue_t *q)
  *   count (non-root nodes built), flags (bit 0: a near tie below eps),
  *   min_gap (smallest gap between a popped candidate and one left in the
  *   queue, structural exact ties excluded; +inf if the queue was always empty),
- *   topm_idx/topm_val [L,M] (optional, may be NULL).
+ *   topm_idx/topm_val [L,M] (optional, may be NULL);
+ *   full_vocab  0: children normalized over the M-slice; 1: over the whole
+ *               vocabulary (corrected top-M plus the uncorrected tail);
+ *   tail_out [L] (optional): the per-position tail_lse (-inf in the
+ *               M-slice mode).
  */
 int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int dtype, double eps,
                          const void *base, const void *emb, const void *W_ih, const void *W_hh,
                          const void *b_ih, const void *b_hh, const void *C, const float *h0,
                          int32_t *tokens, int32_t *parents, int32_t *depths, double *scores,
                          uint8_t *mask, int32_t *count, uint32_t *flags, double *min_gap,
-                         int32_t *topm_idx, double *topm_val)
+                         int32_t *topm_idx, double *topm_val, int full_vocab, double *tail_out)
 {
     if (V < 1 || L < 1 || E < 1 || H < 1 || M < 1 || M > V || n < 1 || T < 0.0 ||
         (dtype != OR_F32 && dtype != OR_BF16) || !base || !emb || !W_ih || !W_hh || !C ||
@@ -347,8 +393,9 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
     int *plen = (int *)malloc((size_t)S * sizeof *plen);
     double *wa = (double *)malloc((size_t)(L + 1) * sizeof *wa);
     double *wb = (double *)malloc((size_t)(L + 1) * sizeof *wb);
+    double *tail = (double *)malloc((size_t)L * sizeof *tail);
     queue_t q = {(qent_t *)malloc((size_t)(2 * S + 2) * sizeof(qent_t)), 0};
-    if (!tidx || !tval || !hs || !ctok || !clp || !plp || !plen || !wa || !wb || !q.e) goto done;
+    if (!tidx || !tval || !hs || !ctok || !clp || !plp || !plen || !wa || !wb || !tail || !q.e) goto done;
 
     /* 1. top-M marginal candidates per block position */
     const size_t esz = (dtype == OR_F32) ? 4 : 2;
@@ -356,6 +403,11 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
         const char *row = (const char *)base + (size_t)p * (size_t)V * esz;
         rc = oracle_topm_row(row, dtype, V, M, tidx + (size_t)p * M, tval + (size_t)p * M);
         if (rc) goto done;
+        tail[p] = -INFINITY;
+        if (full_vocab) {
+            rc = oracle_tail_lse(row, dtype, V, M, T, tidx + (size_t)p * M, tail + p);
+            if (rc) goto done;
+        }
     }
 
     /* empty tree */
@@ -372,7 +424,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
     scores[0] = 0.0;
     plen[0] = 0;
     for (int k = 0; k < H; ++k) hs[k] = h0 ? (double)h0[k] : 0.0;
-    rc = oracle_dist(tidx, tval, M, C, dtype, H, hs, T, ctok, clp);
+    rc = oracle_dist(tidx, tval, M, C, dtype, H, hs, T, tail[0], ctok, clp);
     if (rc) goto done;
     q_push(&q, (qent_t){0.0 + clp[0], 1, 0, 0});
 
@@ -408,7 +460,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
                             E, H, hv);
             if (rc) goto done;
             rc = oracle_dist(tidx + (size_t)c.depth * M, tval + (size_t)c.depth * M, M, C, dtype, H,
-                             hv, T, ctok + (size_t)v * M, clp + (size_t)v * M);
+                             hv, T, tail[c.depth], ctok + (size_t)v * M, clp + (size_t)v * M);
             if (rc) goto done;
             q_push(&q, (qent_t){scores[v] + clp[(size_t)v * M], c.depth + 1, v, 0});
         }
@@ -423,10 +475,11 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
 
     if (topm_idx) memcpy(topm_idx, tidx, (size_t)L * M * sizeof *tidx);
     if (topm_val) memcpy(topm_val, tval, (size_t)L * M * sizeof *tval);
+    if (tail_out) memcpy(tail_out, tail, (size_t)L * sizeof *tail);
     rc = OR_OK;
 done:
     free(tidx); free(tval); free(hs); free(ctok); free(clp); free(plp); free(plen); free(wa);
-    free(wb); free(q.e);
+    free(wb); free(tail); free(q.e);
     return rc;
 }
 
@@ -439,7 +492,7 @@ done:
 int oracle_score_paths(int V, int L, int E, int H, int M, double T, int dtype, const void *base,
                        const void *emb, const void *W_ih, const void *W_hh, const void *b_ih,
                        const void *b_hh, const void *C, const float *h0, int npaths,
-                       const int32_t *paths, const int32_t *len, double *out)
+                       const int32_t *paths, const int32_t *len, double *out, int full_vocab)
 {
     if (V < 1 || L < 1 || E < 1 || H < 1 || M < 1 || M > V || npaths < 0 || T < 0.0 || !base ||
         !emb || !W_ih || !W_hh || !C || (npaths > 0 && (!paths || !len || !out)))
@@ -451,12 +504,18 @@ int oracle_score_paths(int V, int L, int E, int H, int M, double T, int dtype, c
     double *h2 = (double *)malloc((size_t)H * sizeof *h2);
     int32_t *ctok = (int32_t *)malloc((size_t)M * sizeof *ctok);
     double *clp = (double *)malloc((size_t)M * sizeof *clp);
-    if (!tidx || !tval || !h || !h2 || !ctok || !clp) goto done;
+    double *tail = (double *)malloc((size_t)L * sizeof *tail);
+    if (!tidx || !tval || !h || !h2 || !ctok || !clp || !tail) goto done;
     const size_t esz = (dtype == OR_F32) ? 4 : 2;
     for (int p = 0; p < L; ++p) {
-        rc = oracle_topm_row((const char *)base + (size_t)p * V * esz, dtype, V, M,
-                             tidx + (size_t)p * M, tval + (size_t)p * M);
+        const char *row = (const char *)base + (size_t)p * V * esz;
+        rc = oracle_topm_row(row, dtype, V, M, tidx + (size_t)p * M, tval + (size_t)p * M);
         if (rc) goto done;
+        tail[p] = -INFINITY;
+        if (full_vocab) {
+            rc = oracle_tail_lse(row, dtype, V, M, T, tidx + (size_t)p * M, tail + p);
+            if (rc) goto done;
+        }
     }
     for (int i = 0; i < npaths; ++i) {
         int d = len[i];
@@ -465,7 +524,8 @@ int oracle_score_paths(int V, int L, int E, int H, int M, double T, int dtype, c
         double s = 0.0;
         for (int p = 0; p < d; ++p) {
             int32_t tok = paths[(size_t)i * L + p];
-            rc = oracle_dist(tidx + (size_t)p * M, tval + (size_t)p * M, M, C, dtype, H, h, T, ctok, clp);
+            rc = oracle_dist(tidx + (size_t)p * M, tval + (size_t)p * M, M, C, dtype, H, h, T, tail[p], ctok,
+                             clp);
             if (rc) goto done;
             int r = -1;
             for (int j = 0; j < M; ++j)
@@ -482,7 +542,7 @@ int oracle_score_paths(int V, int L, int E, int H, int M, double T, int dtype, c
     }
     rc = OR_OK;
 done:
-    free(tidx); free(tval); free(h); free(h2); free(ctok); free(clp);
+    free(tidx); free(tval); free(h); free(h2); free(ctok); free(clp); free(tail);
     return rc;
 }
 

@@ -44,10 +44,18 @@ def topm_table(base_req: np.ndarray, M: int):
 class Scorer:
     """Conditional child distributions via torch library routines (float64)."""
 
-    def __init__(self, inp: dict, b: int, M: int, T: float):
+    def __init__(self, inp: dict, b: int, M: int, T: float, full_vocab: bool = False):
         self.idx, self.val = topm_table(inp["base"][b], M)
         self.L = self.idx.shape[0]
         self.T = T
+        # full-vocabulary normalization: every row's logits outside its top M
+        # (uncorrected) join the softmax
+        self.full_vocab = full_vocab
+        if full_vocab:
+            rows = as_f64(inp["base"][b])
+            keep = np.ones(rows.shape, bool)
+            np.put_along_axis(keep, self.idx, False, axis=1)
+            self.tail_logits = [torch.from_numpy(rows[p][keep[p]]) for p in range(self.L)]
         self.emb = torch.from_numpy(as_f64(inp["emb"]))
         self.C = torch.from_numpy(as_f64(inp["C"]))
         H, E = inp["w_hh"].shape[1], inp["w_ih"].shape[1]
@@ -70,7 +78,11 @@ class Scorer:
         z = torch.from_numpy(self.val[pos]) + self.C[torch.from_numpy(idx)] @ h
         if self.T > 0:
             z = z / self.T
-        lp = torch.log_softmax(z, dim=0).numpy()
+        if self.full_vocab:
+            tail = self.tail_logits[pos] / (self.T if self.T > 0 else 1.0)
+            lp = (z - torch.logsumexp(torch.cat([z, tail]), dim=0)).numpy()
+        else:
+            lp = torch.log_softmax(z, dim=0).numpy()
         order = np.lexsort((idx, -lp))
         return idx[order], lp[order]
 

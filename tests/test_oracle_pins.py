@@ -13,7 +13,11 @@
 * metamorphic:  vocabulary relabeling, batch independence;
 * acceptance walk: hand-derived cases (tests/golden/hand_accept.json), and the
                 accepted path recomputed as the set of nodes whose every root-path
-                edge matches the target, on random trees and on oracle trees.
+                edge matches the target, on random trees and on oracle trees;
+* full-vocabulary mode: tail vs scipy's logsumexp over the non-top-M logits;
+                C = 0 children vs torch.log_softmax of the whole row; trees vs
+                brute force and branch-and-bound with a torch scorer that adds
+                the tail to its softmax; M = V reduces to the M-slice mode.
 """
 import json
 import math
@@ -516,3 +520,89 @@ def test_accept_special_cases():
     # a mismatch in the middle stops the walk there
     r = oracle.accept_greedy(tok, par, 3, [4, 7, 6, 9])
     assert r["path"].tolist() == [1] and r["bonus"] == 7
+
+
+# ---- full-vocabulary normalization (optional mode) -----------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,M,T", [(1000, 8, 0.0), (257, 64, 0.5), (3000, 17, 1.0), (70, 1, 2.0)])
+def test_tail_lse_matches_scipy_logsumexp(dtype, V, M, T):
+    from scipy.special import logsumexp
+    cfg = small_cfg(V=V, L=1, dtype=dtype, alpha=1.1)
+    row = S.make_inputs(cfg, seed=V + M)["base"][0, 0]
+    x = as_f64(row)
+    top = np.lexsort((np.arange(V), -x))[:M]  # numpy's ordering, not the oracle's
+    keep = np.ones(V, bool)
+    keep[top] = False
+    want = logsumexp(x[keep] / (T if T > 0 else 1.0))
+    assert oracle.tail_lse(row, M, T) == pytest.approx(want, abs=1e-12, rel=1e-13)
+
+
+def test_tail_is_empty_when_m_equals_v():
+    row = np.linspace(-3, 2, 11).astype(np.float32)
+    assert oracle.tail_lse(row, 11) == -np.inf
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_full_vocab_zero_correction_is_the_full_log_softmax(T):
+    # with C = 0 the corrected logits are the base logits: the children's
+    # log-probs are the log-softmax of the whole row, read at the top-M tokens
+    cfg = small_cfg(V=500, L=1, M=12, H=7)
+    inp = S.make_inputs(cfg, seed=4)
+    row = inp["base"][0, 0]
+    idx, val = oracle.topm_row(row, cfg["M"])
+    tok, lp = oracle.dist(idx, val, np.zeros_like(inp["C"]), np.ones(cfg["H"]), T,
+                          tail=oracle.tail_lse(row, cfg["M"], T))
+    full = torch.log_softmax(torch.from_numpy(as_f64(row)) / (T if T > 0 else 1.0), dim=0).numpy()
+    np.testing.assert_allclose(lp, full[tok], atol=1e-12)
+    # and the M-slice mode differs from it by the slice's total mass
+    _, lp_slice = oracle.dist(idx, val, np.zeros_like(inp["C"]), np.ones(cfg["H"]), T)
+    assert np.all(lp < lp_slice)
+
+
+@pytest.mark.parametrize("L,M,n,T,seed", [
+    (4, 4, 8, 0.0, 0), (3, 5, 20, 0.5, 2), (6, 3, 12, 0.0, 3), (4, 3, 40, 1.0, 5),
+])
+def test_full_vocab_tree_equals_bruteforce_top_n(L, M, n, T, seed):
+    cfg = small_cfg(L=L, M=M, n=n, T=T, V=40, E=8, H=6)
+    inp = S.make_inputs(cfg, seed=seed, variant="strong")
+    sc = Scorer(inp, 0, M, T, full_vocab=True)
+    nodes = best_n_bruteforce(sc, n)
+    res = oracle.build_request(inp, 0, M, n, T, full_vocab=True)
+    assert res["count"] == len(nodes)
+    assert_tree_equal(res, tree_arrays(nodes, n), n)
+
+
+def test_full_vocab_tiny_equals_branch_and_bound():
+    cfg = S.CONFIGS["tiny"]
+    inp = S.make_inputs(cfg, seed=0, variant="strong")
+    sc = Scorer(inp, 0, cfg["M"], cfg["T"], full_vocab=True)
+    nodes = best_n_branch_and_bound(sc, cfg["n"])
+    res = oracle.build_request(inp, 0, cfg["M"], cfg["n"], cfg["T"], full_vocab=True)
+    assert res["count"] == cfg["n"]
+    assert_tree_equal(res, tree_arrays(nodes, cfg["n"]), cfg["n"])
+
+
+def test_full_vocab_with_m_equal_v_is_the_slice_mode():
+    cfg = small_cfg(V=9, M=9, L=3, n=10)
+    inp = S.make_inputs(cfg, seed=8, variant="strong")
+    a = oracle.build_request(inp, 0, 9, 10, full_vocab=True)
+    b = oracle.build_request(inp, 0, 9, 10)
+    assert np.all(a["tail"] == -np.inf)
+    for k in ("tokens", "parents", "depths", "scores"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_full_vocab_rescoring_agrees_with_tree():
+    cfg = S.CONFIGS["tiny"]
+    inp = S.make_inputs(cfg, seed=1)
+    res = oracle.build_request(inp, 0, cfg["M"], cfg["n"], full_vocab=True)
+    paths = []
+    for v in range(1, res["count"] + 1):
+        p, j = [], v
+        while j > 0:
+            p.append(int(res["tokens"][j]))
+            j = res["parents"][j]
+        paths.append(p[::-1])
+    sc = oracle.score_paths(inp, 0, cfg["M"], paths, full_vocab=True)
+    np.testing.assert_allclose(sc, res["scores"][1:res["count"] + 1], atol=1e-12)
