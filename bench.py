@@ -154,6 +154,25 @@ def main():
     torch.cuda.synchronize()
     marg_us = (time.perf_counter() - m0) * 1e6 / max(args.stage_steps, 1)
 
+    # ---- the full-vocabulary normalization mode (extra key): same inputs; the
+    # top-M select also sums the tail mass; how many trees keep their shape
+    fbld = dtree.Builder(B, L, V, E, H, M, n, cfg["T"], cfg["dtype"], 1e-5, device=dev, full_vocab=True)
+    fout = fbld.build(t["base"], t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"], t["h0"])
+    for _ in range(3):
+        fbld.build(t["base"], t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"], t["h0"], out=fout)
+    torch.cuda.synchronize()
+    dtree.dt_timing_enable(fbld.handle, 1, args.stage_steps)
+    f0 = time.perf_counter()
+    for _ in range(args.stage_steps):
+        fbld.build(t["base"], t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"], t["h0"], out=fout)
+    torch.cuda.synchronize()
+    fv_us = (time.perf_counter() - f0) * 1e6 / max(args.stage_steps, 1)
+    fv_sel = float(np.mean(dtree.dt_timing_read(fbld.handle, 0))) if args.stage_steps else float("nan")
+    dtree.dt_timing_enable(fbld.handle, 0, 0)
+    same_shape = float(((fout["tokens"] == out["tokens"]).all(dim=1) &
+                        (fout["parents"] == out["parents"]).all(dim=1)).float().mean())
+    fbld.close()
+
     # ---- the greedy acceptance walk on the timed trees (extra key): synthetic
     # greedy target tokens that follow one of a node's children with
     # probability 0.8
@@ -227,6 +246,11 @@ def main():
         "latency_per_request_us": round(ms_per_step * 1e3, 1),
         "marginal_mode": {"us_per_round": round(marg_us, 1),
                           "tree_builds_per_s": round(B / (marg_us * 1e-6), 1)},
+        "full_vocab_mode": {"us_per_round": round(fv_us, 1),
+                            "tree_builds_per_s": round(B / (fv_us * 1e-6), 1),
+                            "topm_select_with_tail_us": round(fv_sel * 1e3, 2),
+                            "topm_select_with_tail_gbs": round(topm_bytes / (fv_sel * 1e-3) / 1e9, 1),
+                            "trees_same_shape_as_top_m_softmax": round(same_shape, 4)},
         "acceptance_walk": {"kernel_us": round(acc_us, 2), "requests": B,
                             "mean_tokens_per_round_synthetic_targets": round(tau, 3),
                             "target_follow_probability": 0.8},

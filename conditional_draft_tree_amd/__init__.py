@@ -9,6 +9,6 @@ entry points raises.
 from ._lib import (  # noqa: F401
     DT_BF16, DT_F32, Builder, DtreeError, dt_accept_greedy, dt_build, dt_build_marginal, dt_correct,
     dt_create, dt_destroy,
-    dt_gru_step, dt_last_error, dt_status_string, dt_timing_enable, dt_timing_read, dt_topm,
+    dt_gru_step, dt_last_error, dt_status_string, dt_timing_enable, dt_timing_read, dt_topm, dt_topm_tail,
     dt_workspace_bytes, lib_path, load_library,
 )

@@ -24,7 +24,7 @@ class DtreeError(RuntimeError):
 class dt_config(C.Structure):
     _fields_ = [("B", C.c_int32), ("L", C.c_int32), ("V", C.c_int32), ("E", C.c_int32),
                 ("H", C.c_int32), ("M", C.c_int32), ("n", C.c_int32), ("temperature", C.c_float),
-                ("dtype", C.c_int), ("near_tie_eps", C.c_float)]
+                ("dtype", C.c_int), ("near_tie_eps", C.c_float), ("full_vocab", C.c_int32)]
 
 
 def lib_path() -> str:
@@ -59,13 +59,15 @@ def load_library():
         # handle, workspace, bytes, base, tokens, parents, depths, scores, mask, count, flags, stream
         lib.dt_build_marginal.argtypes = [H, vp, C.c_size_t, vp] + [i32p] * 3 + [f32p, vp, i32p, vp, vp]
         lib.dt_topm.argtypes = [H, vp, C.c_size_t, vp, i32p, f32p, vp]
+        lib.dt_topm_tail.argtypes = [H, vp, C.c_size_t, vp, i32p, f32p, f32p, vp]
         lib.dt_gru_step.argtypes = [H, vp, C.c_size_t, vp, f32p, vp, vp, vp, vp, f32p, vp]
         lib.dt_correct.argtypes = [H, i32p, f32p, vp, f32p, i32p, i32p, f32p, vp]
         lib.dt_accept_greedy.argtypes = [H] + [i32p] * 7 + [vp]
         lib.dt_timing_enable.argtypes = [H, C.c_int, C.c_int]
         lib.dt_timing_read.argtypes = [H, C.c_int, C.POINTER(C.c_float), C.c_int,
                                        C.POINTER(C.c_int)]
-        for f in (lib.dt_create, lib.dt_build, lib.dt_build_marginal, lib.dt_topm, lib.dt_gru_step,
+        for f in (lib.dt_create, lib.dt_build, lib.dt_build_marginal, lib.dt_topm, lib.dt_topm_tail,
+                  lib.dt_gru_step,
                   lib.dt_correct, lib.dt_accept_greedy,
                   lib.dt_timing_enable, lib.dt_timing_read):
             f.restype = C.c_int
@@ -92,10 +94,11 @@ def dt_last_error(handle=None) -> str:
     return load_library().dt_last_error(handle).decode(errors="replace")
 
 
-def dt_create(B, L, V, E, H, M, n, temperature=0.0, dtype=DT_BF16, near_tie_eps=1e-5):
+def dt_create(B, L, V, E, H, M, n, temperature=0.0, dtype=DT_BF16, near_tie_eps=1e-5, full_vocab=False):
     """Returns an opaque handle (host only; no GPU needed)."""
     lib = load_library()
-    cfg = dt_config(B, L, V, E, H, M, n, float(temperature), int(dtype), float(near_tie_eps))
+    cfg = dt_config(B, L, V, E, H, M, n, float(temperature), int(dtype), float(near_tie_eps),
+                    int(bool(full_vocab)))
     h = C.c_void_p()
     _check(lib.dt_create(C.byref(cfg), C.byref(h)), None)
     return h
@@ -142,6 +145,12 @@ def dt_topm(handle, workspace, base, idx, val, stream=None):
                        _p(base), _p(idx), _p(val), _stream(stream)), handle)
 
 
+def dt_topm_tail(handle, workspace, base, idx, val, tail, stream=None):
+    lib = load_library()
+    _check(lib.dt_topm_tail(handle, _p(workspace), workspace.numel() if workspace is not None else 0,
+                            _p(base), _p(idx), _p(val), _p(tail), _stream(stream)), handle)
+
+
 def dt_gru_step(handle, workspace, x, h, w_ih, w_hh, b_ih, b_hh, h_out, stream=None):
     lib = load_library()
     _check(lib.dt_gru_step(handle, _p(workspace), workspace.numel() if workspace is not None else 0,
@@ -182,14 +191,14 @@ class Builder:
     """
 
     def __init__(self, B, L, V, E, H, M, n, temperature=0.0, dtype="bf16", near_tie_eps=1e-5,
-                 device=None):
+                 device=None, full_vocab=False):
         import torch
         self.cfg = dict(B=B, L=L, V=V, E=E, H=H, M=M, n=n, temperature=float(temperature),
-                        near_tie_eps=float(near_tie_eps))
+                        near_tie_eps=float(near_tie_eps), full_vocab=bool(full_vocab))
         self.dtype_name = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.handle = dt_create(B, L, V, E, H, M, n, temperature,
-                                DT_BF16 if dtype == "bf16" else DT_F32, near_tie_eps)
+                                DT_BF16 if dtype == "bf16" else DT_F32, near_tie_eps, full_vocab)
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         nbytes = dt_workspace_bytes(self.handle)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
@@ -278,6 +287,18 @@ class Builder:
         val = torch.empty((c["B"], c["L"], c["M"]), dtype=torch.float32, device=self.device)
         dt_topm(self.handle, self.workspace, base, idx, val, stream)
         return idx, val
+
+    def topm_tail(self, base, stream=None):
+        """Top-M tables and each row's tail_lse [B, L] (log sum of exp(x / T)
+        over the logits outside the row's top M)."""
+        import torch
+        c = self.cfg
+        self._chk("base", base, (c["B"], c["L"], c["V"]))
+        idx = torch.empty((c["B"], c["L"], c["M"]), dtype=torch.int32, device=self.device)
+        val = torch.empty((c["B"], c["L"], c["M"]), dtype=torch.float32, device=self.device)
+        tail = torch.empty((c["B"], c["L"]), dtype=torch.float32, device=self.device)
+        dt_topm_tail(self.handle, self.workspace, base, idx, val, tail, stream)
+        return idx, val, tail
 
     def gru_step(self, x, h, w_ih, w_hh, b_ih=None, b_hh=None, stream=None):
         import torch

@@ -21,7 +21,7 @@ thread_local char g_create_error[512] = "";
 
 struct Layout {
     size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
-        rstate, xpack, hpack, hprev;
+        rstate, xpack, hpack, hprev, tail, tail_part;
     size_t total;
 };
 
@@ -70,6 +70,12 @@ dt_status hip_fail(dt_handle* h, hipError_t e, const char* what) {
     return fail(h, DT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// log2(e) / T (T = 1 when the temperature is 0): the top-M select sums
+// 2^(x * this) for the full-vocabulary tail
+float tail_scale(const dt_config& c) {
+    return 1.4426950408889634f / (c.temperature > 0.f ? c.temperature : 1.f);
+}
+
 Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     Layout l{};
     const size_t B = c.B, L = c.L, M = c.M, S = (size_t)c.n + 1, H = c.H;
@@ -96,6 +102,8 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.hpack = take(c.dtype == DT_BF16 ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
     l.hprev = take(c.dtype == DT_BF16 ? B * H * 4 : 0);
     l.nval = take(B * 64 * 4);
+    l.tail = take(B * L * 4);                          // full-vocabulary mode: tail_lse per row
+    l.tail_part = take(B * L * (size_t)nseg * 2 * 4);  // its per-segment (m, s) sums
     l.total = off;
     return l;
 }
@@ -177,6 +185,8 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     if (c.M > c.V) return fail(nullptr, DT_ERR_INVALID_ARG, "M=%d exceeds V=%d", c.M, c.V);
     if (!(c.temperature >= 0.f) || !(c.near_tie_eps >= 0.f))
         return fail(nullptr, DT_ERR_INVALID_ARG, "temperature and near_tie_eps must be >= 0");
+    if (c.full_vocab != 0 && c.full_vocab != 1)
+        return fail(nullptr, DT_ERR_INVALID_ARG, "full_vocab must be 0 or 1 (got %d)", (int)c.full_vocab);
     if (c.M > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "M=%d > 64 (one candidate per lane)", c.M);
     if (c.n > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "n=%d > 64 (queue of one wave)", c.n);
     if (c.L > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "L=%d > 64", c.L);
@@ -281,6 +291,23 @@ dt_status dt_topm(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int
                                    (u64*)((char*)ws + h->lay.partial), c.M, idx, val,
                                    (hipStream_t)stream);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_topm launch");
+}
+
+dt_status dt_topm_tail(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int32_t* idx, float* val,
+                       float* tail, void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (c.B == 0) return DT_OK;
+    if (!base || !idx || !val || !tail) return fail(h, DT_ERR_INVALID_ARG, "dt_topm_tail: null pointer");
+    if (misaligned(base) || misaligned(idx) || misaligned(val))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_topm_tail: buffers must be 16-byte aligned");
+    dt_status s = check_ws(h, ws, ws_bytes);
+    if (s) return s;
+    hipError_t e = dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg,
+                                   (u64*)((char*)ws + h->lay.partial), c.M, idx, val, (hipStream_t)stream,
+                                   dt::LaunchEvents{}, tail_scale(c), tail,
+                                   (float*)((char*)ws + h->lay.tail_part));
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_topm_tail launch");
 }
 
 dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, const float* h_in,
@@ -400,8 +427,9 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     float* tval = (float*)(w + L.tval);
     dt::LaunchEvents ev{};
     DT_TRY(kernel_marks(h, call, 1, 'K', 'T', &ev), "timing event");
+    float* tail = c.full_vocab ? (float*)(w + L.tail) : nullptr;
     DT_TRY(dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg, (u64*)(w + L.partial), c.M,
-                           tidx, tval, st, ev),
+                           tidx, tval, st, ev, tail_scale(c), tail, (float*)(w + L.tail_part)),
            "top-M launch");
     DT_TRY(mark(h, call, 1, 'M', st), "timing event");
 
@@ -430,6 +458,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     a.xpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.xpack) : nullptr;
     a.hpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.hpack) : nullptr;
     a.hprev = c.dtype == DT_BF16 && !marginal ? (float*)(w + L.hprev) : nullptr;
+    a.tail = tail;
     a.tokens = tokens; a.parents = parents; a.depths = depths; a.scores = scores;
     a.mask = mask; a.count = count; a.flags = flags;
 

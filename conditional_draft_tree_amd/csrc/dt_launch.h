@@ -32,9 +32,14 @@ hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, unsigned shm, h
 // ---- top-M select (topm.hip) ----------------------------------------------
 int topm_segments(int rows, int V);
 // rows = B*L rows of V logits; partial: rows*nseg*64 keys of scratch.
-// ev (optional) times the select kernel alone (not the merge).
+// ev (optional) times the select kernel alone (not the merge).  With
+// tail_out (full-vocabulary mode) tail_out[row] also receives log sum of
+// exp(x / T) over the row's logits outside its top M (-inf if none), with
+// tail_c = log2(e) / T (T = 1 when T = 0); tail_part is rows*nseg*2 floats
+// of scratch.
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial, int M,
-                       int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev = {});
+                       int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev = {},
+                       float tail_c = 0.f, float* tail_out = nullptr, float* tail_part = nullptr);
 
 // ---- GRU gate contraction (gru.hip) -----------------------------------------
 // bf16 path: the activations come packed for the MFMA operands (see
@@ -117,6 +122,7 @@ struct NodeArgs {
     uint16_t* xpack;     // packed activations of the next contraction (bf16 path; see
     uint16_t* hpack;     // pack_index_x / pack_index_h), NULL on the binary32 path
     float* hprev;        // [B, H] the next expanded slot's parent state (bf16 path), or NULL
+    const float* tail;   // [B, L] full-vocabulary mode: each row's tail_lse; NULL = M-slice softmax
     // outputs
     int32_t* tokens;
     int32_t* parents;

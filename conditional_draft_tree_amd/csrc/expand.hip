@@ -203,17 +203,19 @@ __device__ __forceinline__ float wave_rowsum4(const float (&acc)[4]) {
 }
 
 // Wave 0: z = base logit + correction dot, temperature, log-softmax over the
-// M-slice; lane j holds candidate j's token, base logit and dot and returns
-// its child key (log-prob desc, token asc; 0 when j >= M).  Sorted across
-// the wave, lane r holds the rank-r child.
-__device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M, float temp) {
+// M-slice, or over the whole vocabulary when `tz` (the row's tail_lse: the
+// uncorrected logits outside the top M, same temperature) is finite; lane j
+// holds candidate j's token, base logit and dot and returns its child key
+// (log-prob desc, token asc; 0 when j >= M).  Sorted across the wave, lane r
+// holds the rank-r child.
+__device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M, float temp, float tz) {
     const int lane = lane_id();
     const bool on = lane < M;
     float zz = on ? val + dot : -INFINITY;
     if (temp > 0.f) zz = zz / temp;
-    const float m = wave_max(zz);
+    const float m = fmaxf(wave_max(zz), tz);
     const float e = on ? expf(zz - m) : 0.f;
-    const float ssum = wave_sum(e);
+    const float ssum = wave_sum(e) + (tz > -INFINITY ? expf(tz - m) : 0.f);
     const float lp = (zz - m) - logf(ssum);
     return on ? child_key(lp, tok) : 0ull;
 }
@@ -282,6 +284,14 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
     const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
     const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
     const int rs_depth = rs1[0];
+    // full-vocabulary mode: the tails of this request's rows (lane p holds
+    // position p's), read from a valid address in either mode
+    float tail_l = -INFINITY;
+    {
+        const float* tp = a.tail ? a.tail + (size_t)b * a.L : a.tval;
+        const float v = tp[min(lane, a.L - 1)];
+        tail_l = a.tail ? v : -INFINITY;
+    }
     // the parent's state (the GRU's previous state), exact: binary32, or the sum
     // of its three bf16 parts
     const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
@@ -471,7 +481,9 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
     const bool pop = wave == 0 && cnt == step && (qs > 0 || expand);
     if (wave == 0) {
         if (expand) {
-            ckey = child_keys_r(my_val, MARG ? 0.f : zs[lane], my_tok, a.M, a.temp);
+            const float tz = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(tail_l), min(depth, a.L - 1)));
+            ckey = child_keys_r(my_val, MARG ? 0.f : zs[lane], my_tok, a.M, a.temp, tz);
             s_keys[lane] = ckey;
             best = wave_max_u64(ckey);  // the rank-0 child
             const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);

@@ -22,6 +22,16 @@
 // the wave-wide work of admitting a key.  Admitted keys are folded into the
 // list by insertion (few keys) or bitonic sort + merge.  With several segments
 // per row, topm_merge folds a row's partial lists into its top M.
+//
+// Full-vocabulary mode (TAIL): the same pass also sums exp(x / T) (T = 1 when
+// T = 0) over the row's logits outside its top M, the tail that the
+// full-vocabulary softmax adds to a node's normalizer.  Every element of the
+// row is counted exactly once: those of vectors the filter rejects, stashed
+// elements below the threshold, admitted keys that later drop out of a list
+// (insertion, merge), keys that lose the final merges, and list entries past
+// M.  Per lane the sum is held as s * 2^m with y = x * log2(e) / T; elements
+// of rejected vectors lie below the threshold, so with m kept at least the
+// threshold they add 2^(y - m) <= 1 without a compare.
 #include <cfloat>
 
 #include "dt_device.h"
@@ -96,6 +106,50 @@ struct WaveTop {
     int nbuf;
 };
 
+// Per-lane tail sum: sum of 2^(y - m) over the values added, y = x * c.
+struct TailAcc {
+    float m;  // -FLT_MAX while empty (2^(y - m) of any finite y is then 0)
+    float s;
+    float c;  // log2(e) / T
+};
+__device__ __forceinline__ void tail_add(TailAcc& t, float x) {  // any value
+    const float y = x * t.c;
+    if (y > t.m) {
+        t.s = t.s * __builtin_amdgcn_exp2f(t.m - y) + 1.f;
+        t.m = y;
+    } else {
+        t.s += __builtin_amdgcn_exp2f(y - t.m);
+    }
+}
+// x * c <= m: no compare
+__device__ __forceinline__ void tail_add_below(TailAcc& t, float x) {
+    t.s += __builtin_amdgcn_exp2f(fmaf(x, t.c, -t.m));
+}
+// Keep m at or above the threshold's y (raised 8 above it, so that it moves
+// only when the threshold has risen by 8 since).
+__device__ __forceinline__ void tail_cover(TailAcc& t, float thr_val) {
+    const float ty = thr_val * t.c;
+    if (ty > t.m) {
+        const float nm = ty + 8.f;
+        t.s *= __builtin_amdgcn_exp2f(t.m - nm);
+        t.m = nm;
+    }
+}
+// (m, s) of a whole wave: the largest m and the rescaled sum (wave-uniform)
+__device__ __forceinline__ void tail_wave_total(const TailAcc& t, float& M, float& S) {
+    M = wave_max(t.m);
+    S = wave_sum(t.s * __builtin_amdgcn_exp2f(t.m - M));
+}
+__device__ __forceinline__ void tail_join(float& M, float& S, float m2, float s2) {
+    const float nm = fmaxf(M, m2);
+    S = S * __builtin_amdgcn_exp2f(M - nm) + s2 * __builtin_amdgcn_exp2f(m2 - nm);
+    M = nm;
+}
+// natural log of the tail, sum of exp(x / T) = 2^M * S; -inf when nothing was added
+__device__ __forceinline__ float tail_lse(float M, float S) {
+    return S > 0.f ? (M + __log2f(S)) * 0.6931471805599453f : -INFINITY;
+}
+
 __device__ __forceinline__ void set_thr(WaveTop& w, u64 t) {
     if (t > w.thr) {
         w.thr = t;
@@ -141,40 +195,55 @@ __device__ __forceinline__ void publish(const WaveTop& w, SharedThr* st) {
 // one-lane shift each); larger ones sort the buffer and merge it.
 constexpr int kInsertMax = 16;
 
-__device__ __forceinline__ void fold_buffer(WaveTop& w, u64* buf, SharedThr* st) {
+template <bool TAIL>
+__device__ __forceinline__ void fold_buffer(WaveTop& w, TailAcc& ta, u64* buf, SharedThr* st) {
     const int lane = lane_id();
     if (w.nbuf <= kInsertMax) {
         for (int i = 0; i < w.nbuf; ++i) {
             const u64 k = buf[i];
             // the list is descending and its keys differ from k (ids differ)
             const int pos = __popcll(__ballot(w.list > k));
-            if (pos >= kWave) continue;
+            if (pos >= kWave) {
+                if (TAIL && lane == 0) tail_add(ta, topm_key_val(k));  // k drops out at once
+                continue;
+            }
+            if (TAIL && lane == kWave - 1 && w.list) tail_add(ta, topm_key_val(w.list));  // shifted out
             const u64 sh = wave_shr1_u64(w.list);
             w.list = lane < pos ? w.list : (lane == pos ? k : sh);
         }
     } else {
         u64 x = lane < w.nbuf ? buf[lane] : 0ull;
         x = wave_sort(x, /*ascending=*/true);
+        if (TAIL) {  // the 64 smaller of the 128 keys drop out
+            const u64 lost = umin64(w.list, x);
+            if (lost) tail_add(ta, topm_key_val(lost));
+        }
         w.list = wave_merge_top64(w.list, x);
     }
     w.nbuf = 0;
     set_thr(w, bcast_u64(w.list, kWave - 1));
     publish(w, st);
     set_thr(w, shared_bound(st));
+    if (TAIL) tail_cover(ta, w.thr_val);
 }
 
 // Offer one key per lane (valid only where `ok`); wave-uniform call.
-__device__ __forceinline__ void offer(WaveTop& w, u64* buf, SharedThr* s_thr, bool ok, u64 key) {
+template <bool TAIL>
+__device__ __forceinline__ void offer(WaveTop& w, TailAcc& ta, u64* buf, SharedThr* s_thr, bool ok, u64 key) {
     bool pass = ok && key >= w.thr;
     u64 m = __ballot(pass);
-    if (m == 0) return;
+    if (m == 0) {
+        if (TAIL && ok) tail_add(ta, topm_key_val(key));
+        return;
+    }
     int cnt = __popcll(m);
     if (w.nbuf + cnt > kWave) {
-        fold_buffer(w, buf, s_thr);
+        fold_buffer<TAIL>(w, ta, buf, s_thr);
         pass = ok && key >= w.thr;
         m = __ballot(pass);
         cnt = __popcll(m);
     }
+    if (TAIL && ok && !pass) tail_add(ta, topm_key_val(key));
     if (pass) {
         const int pos = w.nbuf + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -191,9 +260,9 @@ __device__ __forceinline__ int prefix_count(u64 m) {
 // element.  The order in which admitted keys arrive does not change the
 // result.  One copy of this code serves the whole kernel (its element loop is
 // not unrolled), which keeps the kernel small enough for the instruction cache.
-template <typename T>
-__device__ __forceinline__ void drain_stash(WaveTop& w, u64* buf, SharedThr* s_thr, const u32x4* svec,
-                                            const int* sidx, int& nst, int lo) {
+template <typename T, bool TAIL>
+__device__ __forceinline__ void drain_stash(WaveTop& w, TailAcc& ta, u64* buf, SharedThr* s_thr,
+                                            const u32x4* svec, const int* sidx, int& nst, int lo) {
     constexpr int P = Elem<T>::kPerVec;
     const int lane = lane_id();
     const int take = min(nst, kWave);
@@ -205,25 +274,33 @@ __device__ __forceinline__ void drain_stash(WaveTop& w, u64* buf, SharedThr* s_t
 #pragma unroll 1
     for (int i = 0; i < P; ++i) {
         const float x = Elem<T>::get(v, i);
-        offer(w, buf, s_thr, on && x >= w.thr_val, topm_key(x, (uint32_t)(lo + vi * P + i)));
+        const bool cand = x >= w.thr_val;
+        if (TAIL && on && !cand) tail_add(ta, x);
+        offer<TAIL>(w, ta, buf, s_thr, on && cand, topm_key(x, (uint32_t)(lo + vi * P + i)));
     }
     // fold now, so that the shared bounds follow every admitted key
-    if (w.nbuf) fold_buffer(w, buf, s_thr);
+    if (w.nbuf) fold_buffer<TAIL>(w, ta, buf, s_thr);
     nst = from;
 }
 
 // With one segment per row the workgroup's list is the row's: it then writes
-// the top M (idx, val) directly and no merge kernel runs.
-template <typename T, bool kVec>
+// the top M (idx, val) directly (and with TAIL the row's tail_lse to
+// tail_out[row]) and no merge kernel runs; with several, each segment leaves
+// its list in `partial` (and its tail sum (m, s), list excluded, in
+// tail_part[row * nseg + segment]).
+template <typename T, bool kVec, bool TAIL>
 __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __restrict__ base, int V,
                                                                     int nseg, int seg,
                                                                     u64* __restrict__ partial, int M,
                                                                     int32_t* __restrict__ idx,
-                                                                    float* __restrict__ val) {
+                                                                    float* __restrict__ val, float tail_c,
+                                                                    float* __restrict__ tail_out,
+                                                                    float2* __restrict__ tail_part) {
     __shared__ u64 sbuf[kWaves][kWave];
     __shared__ u32x4 svec[kWaves][kStash];
     __shared__ int sidx[kWaves][kStash];
     __shared__ SharedThr s_thr;
+    __shared__ float2 s_tail[kWaves];
     const int row = blockIdx.y, s = blockIdx.x;
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const T* rp = base + (size_t)row * (size_t)V;
@@ -242,6 +319,7 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
     w.slack = Elem<T>::kSlack;
     w.nbuf = 0;
     int nst = 0;
+    TailAcc ta{-FLT_MAX, 0.f, tail_c};
 
     int tail_lo = lo;
     if (kVec && hi > lo) {
@@ -288,6 +366,7 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
         auto process = [&](const u32x4 (&vec)[kUnroll], int v0) {
             float vm[kUnroll];
             set_thr(w, shared_bound(&s_thr));
+            if (TAIL) tail_cover(ta, w.thr_val);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) vm[u] = Elem<T>::vfilter(vec[u]);
             if (v0 + kBatch > nvec) {  // last, partial batch
@@ -298,6 +377,11 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const bool pass = vm[u] >= w.filt;
+                if (TAIL && !pass && v0 + u * kTopmThreads + (int)threadIdx.x < nvec) {
+                    // every element lies below the threshold: tail
+#pragma unroll
+                    for (int i = 0; i < P; ++i) tail_add_below(ta, Elem<T>::get(vec[u], i));
+                }
                 const u64 m = __ballot(pass);
                 if (m == 0) continue;
                 if (pass) {
@@ -310,7 +394,7 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
             // fewer than 64 stay stashed between batches; none after the last
             const bool last = v0 + kBatch >= nvec;
             while (nst >= kWave || (last && nst > 0))
-                drain_stash<T>(w, buf, &s_thr, svec[wave], sidx[wave], nst, lo);
+                drain_stash<T, TAIL>(w, ta, buf, &s_thr, svec[wave], sidx[wave], nst, lo);
         };
         // Software pipeline over two register sets: the next batch is in
         // flight while this one is evaluated, and no loaded register is
@@ -337,40 +421,88 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
         const int e = e0 + (int)threadIdx.x;
         const bool ok = e < hi;
         const float x = ok ? Elem<T>::scalar(rp + e) : -INFINITY;
-        offer(w, buf, &s_thr, ok && x >= w.thr_val, topm_key(x, (uint32_t)e));
+        const bool cand = x >= w.thr_val;
+        if (TAIL && ok && !cand) tail_add(ta, x);
+        offer<TAIL>(w, ta, buf, &s_thr, ok && cand, topm_key(x, (uint32_t)e));
     }
-    if (w.nbuf) fold_buffer(w, buf, &s_thr);
+    if (w.nbuf) fold_buffer<TAIL>(w, ta, buf, &s_thr);
 
     // merge the workgroup's four wave lists (reusing the key buffers)
+    float tM = -FLT_MAX, tS = 0.f;
+    if (TAIL) {
+        tail_wave_total(ta, tM, tS);
+        if (lane == 0) s_tail[wave] = float2{tM, tS};
+    }
     __syncthreads();
     sbuf[wave][lane] = w.list;
     __syncthreads();
     if (wave == 0) {
         u64 l = w.list;
+        TailAcc tb{-FLT_MAX, 0.f, tail_c};  // keys losing the merge, list entries past M
 #pragma unroll
-        for (int o = 1; o < kWaves; ++o) l = wave_merge_top64(l, sbuf[o][kWave - 1 - lane]);
+        for (int o = 1; o < kWaves; ++o) {
+            const u64 other = sbuf[o][kWave - 1 - lane];
+            if (TAIL) {
+                const u64 lost = umin64(l, other);
+                if (lost) tail_add(tb, topm_key_val(lost));
+            }
+            l = wave_merge_top64(l, other);
+        }
+        if (TAIL && nseg == 1 && lane >= M && l) tail_add(tb, topm_key_val(l));
+        if (TAIL) {
+#pragma unroll
+            for (int o = 1; o < kWaves; ++o) tail_join(tM, tS, s_tail[o].x, s_tail[o].y);
+            float m2, s2;
+            tail_wave_total(tb, m2, s2);
+            tail_join(tM, tS, m2, s2);
+        }
         if (nseg == 1) {
             if (lane < M) {
                 idx[(size_t)row * M + lane] = (int32_t)topm_key_id(l);
                 val[(size_t)row * M + lane] = topm_key_val(l);
             }
+            if (TAIL && lane == 0) tail_out[row] = tail_lse(tM, tS);
         } else {
             partial[((size_t)row * nseg + s) * kWave + lane] = l;
+            if (TAIL && lane == 0) tail_part[(size_t)row * nseg + s] = float2{tM, tS};
         }
     }
 }
 
-// One wave per row: fold the row's `nseg` sorted partial lists, emit top M.
+// One wave per row: fold the row's `nseg` sorted partial lists, emit top M
+// (and with TAIL the row's tail_lse: the segments' sums plus the keys losing
+// this merge and the list entries past M).
+template <bool TAIL>
 __global__ __launch_bounds__(kWave) void topm_merge_kernel(const u64* __restrict__ partial, int nseg,
                                                            int M, int32_t* __restrict__ idx,
-                                                           float* __restrict__ val) {
+                                                           float* __restrict__ val, float tail_c,
+                                                           const float2* __restrict__ tail_part,
+                                                           float* __restrict__ tail_out) {
     const int row = blockIdx.x, lane = lane_id();
     const u64* p = partial + (size_t)row * nseg * kWave;
     u64 l = p[lane];
-    for (int s = 1; s < nseg; ++s) l = wave_merge_top64(l, p[(size_t)s * kWave + kWave - 1 - lane]);
+    TailAcc tb{-FLT_MAX, 0.f, tail_c};
+    for (int s = 1; s < nseg; ++s) {
+        const u64 other = p[(size_t)s * kWave + kWave - 1 - lane];
+        if (TAIL) {
+            const u64 lost = umin64(l, other);
+            if (lost) tail_add(tb, topm_key_val(lost));
+        }
+        l = wave_merge_top64(l, other);
+    }
     if (lane < M) {
         idx[(size_t)row * M + lane] = (int32_t)topm_key_id(l);
         val[(size_t)row * M + lane] = topm_key_val(l);
+    }
+    if (TAIL) {
+        if (lane >= M && l) tail_add(tb, topm_key_val(l));
+        float tM, tS;
+        tail_wave_total(tb, tM, tS);
+        for (int s = 0; s < nseg; ++s) {
+            const float2 ps = tail_part[(size_t)row * nseg + s];
+            tail_join(tM, tS, ps.x, ps.y);
+        }
+        if (lane == 0) tail_out[row] = tail_lse(tM, tS);
     }
 }
 
@@ -386,7 +518,8 @@ int topm_segments(int rows, int V) {
 }
 
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial,
-                       int M, int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev) {
+                       int M, int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev, float tail_c,
+                       float* tail_out, float* tail_part) {
     if (rows == 0) return hipSuccess;
     const size_t esz = dtype == 1 ? 2 : 4;
     const int per_vec = 16 / (int)esz;
@@ -394,17 +527,26 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
     seg = (seg + per_vec - 1) / per_vec * per_vec;  // segments start on vector boundaries
     const bool vec = ((uintptr_t)base % 16 == 0) && ((size_t)V * esz % 16 == 0);
     const dim3 grid(nseg, rows), block(kTopmThreads);
+    float2* tp = reinterpret_cast<float2*>(tail_part);
     hipError_t e;
-    if (dtype == 1)
-        e = launch_kernel(vec ? topm_partial_kernel<bf16_t, true> : topm_partial_kernel<bf16_t, false>,
-                          grid, block, 0, stream, ev, (const bf16_t*)base, V, nseg, seg, partial, M,
-                          idx, val);
-    else
-        e = launch_kernel(vec ? topm_partial_kernel<float, true> : topm_partial_kernel<float, false>,
-                          grid, block, 0, stream, ev, (const float*)base, V, nseg, seg, partial, M,
-                          idx, val);
+#define DT_TOPM(Ty, kV, TL) \
+    launch_kernel(topm_partial_kernel<Ty, kV, TL>, grid, block, 0, stream, ev, (const Ty*)base, V, nseg, seg, \
+                  partial, M, idx, val, tail_c, tail_out, tp)
+    if (tail_out) {
+        if (dtype == 1) e = vec ? DT_TOPM(bf16_t, true, true) : DT_TOPM(bf16_t, false, true);
+        else e = vec ? DT_TOPM(float, true, true) : DT_TOPM(float, false, true);
+    } else {
+        if (dtype == 1) e = vec ? DT_TOPM(bf16_t, true, false) : DT_TOPM(bf16_t, false, false);
+        else e = vec ? DT_TOPM(float, true, false) : DT_TOPM(float, false, false);
+    }
+#undef DT_TOPM
     if (e != hipSuccess) return e;
-    if (nseg > 1) topm_merge_kernel<<<rows, kWave, 0, stream>>>(partial, nseg, M, idx, val);
+    if (nseg > 1) {
+        if (tail_out)
+            topm_merge_kernel<true><<<rows, kWave, 0, stream>>>(partial, nseg, M, idx, val, tail_c, tp, tail_out);
+        else
+            topm_merge_kernel<false><<<rows, kWave, 0, stream>>>(partial, nseg, M, idx, val, 0.f, nullptr, nullptr);
+    }
     return hipGetLastError();
 }
 

@@ -59,6 +59,13 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *                log-softmax ([captcha] "Methodology -- deep read": runs at
  *                T in {0, 0.5, 1.0})
  *   near_tie_eps decisions closer than this are flagged (e.g. 1e-5)
+ *   full_vocab   0: a node's children are normalized over its top-M slice;
+ *                1: over the whole vocabulary, the corrected top-M logits
+ *                plus the uncorrected logits of every other token of the
+ *                row (the pages restrict the correction to the top M and
+ *                leave the softmax scope open: [captcha] "Key findings",
+ *                "Methodology -- deep read").  Applies to dt_build and
+ *                dt_build_marginal.
  * A request's expansion state lives in one workgroup's LDS: configurations with
  * 4 H + 8 L M + 512 n bytes (plus ~0.8 KiB) above 64 KiB are DT_ERR_UNSUPPORTED. */
 typedef struct {
@@ -66,6 +73,7 @@ typedef struct {
     float temperature;
     dt_dtype dtype;
     float near_tie_eps;
+    int32_t full_vocab;
 } dt_config;
 
 typedef struct dt_handle dt_handle; /* opaque: configuration, launch plan, timing events */
@@ -184,6 +192,20 @@ dt_status dt_gru_step(dt_handle *h, void *workspace, size_t ws_bytes, const void
 dt_status dt_correct(dt_handle *h, const int32_t *idx, const float *val, const void *C,
                      const float *h_in, const int32_t *pos, int32_t *tok_sorted,
                      float *logp_sorted, void *stream);
+
+/*
+ * dt_topm_tail -- dt_topm plus each row's tail mass: tail[b][p] = log of the
+ * sum of exp(x / T) (T = 1 when temperature = 0) over the logits x of row
+ * (b, p) outside its top M; -inf when M = V.  This is the extra term of the
+ * full-vocabulary normalizer (see dt_config.full_vocab), computed in the
+ * same single pass over the logits: every element outside the final top M
+ * is added exactly once.
+ *   base [B, L, V] dtype; idx [B, L, M] int32, val [B, L, M] binary32,
+ *   tail [B, L] binary32 (out).  Workspace as for dt_build.
+ * Errors as dt_topm.
+ */
+dt_status dt_topm_tail(dt_handle *h, void *workspace, size_t ws_bytes, const void *base, int32_t *idx,
+                       float *val, float *tail, void *stream);
 
 /*
  * dt_accept_greedy -- greedy (temperature 0) acceptance of B verified trees.

@@ -85,7 +85,8 @@ def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg
     # unique is the multiset of the best scores; every GPU node must carry its
     # own conditional score.
     gs = got["scores"][b_got][1:cnt + 1].astype(np.float64)
-    rs = oracle.score_paths(inp, b_inp, cfg["M"], paths_of(got, b_got), cfg["T"])
+    rs = oracle.score_paths(inp, b_inp, cfg["M"], paths_of(got, b_got), cfg["T"],
+                            full_vocab=cfg.get("full_vocab", False))
     assert np.all(np.isfinite(rs)), "GPU node outside the top-M candidate tree"
     assert np.abs(gs - rs).max() <= tol
     assert np.abs(np.sort(gs) - np.sort(ref["scores"][1:cnt + 1])).max() <= tol

@@ -118,6 +118,21 @@ def test_build_marginal_argument_errors_before_any_launch():
     dtree.dt_destroy(h)
 
 
+def test_full_vocab_flag_is_validated():
+    lib = dtree.load_library()
+    bad = dt_config(1, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_F32, 1e-5, 2)
+    out = C.c_void_p()
+    assert lib.dt_create(C.byref(bad), C.byref(out)) == -1 and not out.value
+    assert "full_vocab" in dtree.dt_last_error(None)
+    h = dtree.dt_create(1, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_F32, 1e-5, full_vocab=True)
+    fake = C.c_void_p(0x10000)
+    need = dtree.dt_workspace_bytes(h)
+    assert lib.dt_topm_tail(h, fake, need, fake, fake, fake, None, None) == -1
+    assert lib.dt_topm_tail(h, fake, need, C.c_void_p(0x10004), fake, fake, fake, None) == -1
+    assert lib.dt_topm_tail(h, None, need, fake, fake, fake, fake, None) == -3
+    dtree.dt_destroy(h)
+
+
 def test_accept_greedy_null_pointer_before_any_launch():
     lib = dtree.load_library()
     h = make()
@@ -139,6 +154,7 @@ def test_empty_batch_is_a_noop():
     assert lib.dt_build_marginal(h, None, 0, *([None] * 8), None) == 0
     assert lib.dt_topm(h, None, 0, None, None, None, None) == 0
     assert lib.dt_accept_greedy(h, *([None] * 7), None) == 0
+    assert lib.dt_topm_tail(h, None, 0, None, None, None, None, None) == 0
     dtree.dt_destroy(h)
 
 

@@ -45,7 +45,7 @@ def inputs(name, variant="default", over=()):
 
 def builder(cfg, eps=1e-5):
     return dtree.Builder(cfg["B"], cfg["L"], cfg["V"], cfg["E"], cfg["H"], cfg["M"], cfg["n"],
-                         cfg["T"], cfg["dtype"], eps, device=DEV)
+                         cfg["T"], cfg["dtype"], eps, device=DEV, full_vocab=cfg.get("full_vocab", False))
 
 
 # The "strong" variant (h0 ~ N(0, 1), C scaled by 10) makes corrected logits
@@ -61,13 +61,13 @@ def build_and_compare(cfg, inp, requests=None, threads=8, eps=1e-5, tol=SCORE_TO
     B = cfg["B"]
     reqs = list(range(B)) if requests is None else list(requests)
     say(f"  build B={B} V={cfg['V']} L={cfg['L']} E={cfg['E']} H={cfg['H']} M={cfg['M']} "
-        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']} eps={eps}")
+        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']} eps={eps} full_vocab={cfg.get('full_vocab', False)}")
     bld = builder(cfg, eps)
     got = run_build(bld, S.to_torch(inp, DEV))
     for b in range(B):
         check_valid_tree(got, b, cfg["n"], cfg["L"])
     refs = oracle.build_batch(inp, cfg["M"], cfg["n"], cfg["T"], eps=eps, requests=reqs,
-                              threads=threads)
+                              threads=threads, full_vocab=cfg.get("full_vocab", False))
     kinds = [compare_request(got, b, r, inp, b, cfg, eps, tol) for b, r in zip(reqs, refs)]
     bld.close()
     say(f"  compared {len(reqs)} requests: {kinds.count('exact')} exact, "
@@ -250,7 +250,7 @@ def marginal_and_compare(cfg, inp, requests, eps=1e-5, tol=SCORE_TOL):
     z = dict(inp)
     z["C"] = np.zeros_like(inp["C"])
     refs = oracle.build_batch(z, cfg["M"], cfg["n"], cfg["T"], eps=eps, requests=list(requests),
-                              threads=8)
+                              threads=8, full_vocab=cfg.get("full_vocab", False))
     kinds = [compare_request(got, b, r, z, b, cfg, eps, tol) for b, r in zip(requests, refs)]
     say(f"  marginal: {kinds.count('exact')} exact, {kinds.count('flagged')} near-tie")
     return got
@@ -359,3 +359,85 @@ def test_accept_on_oracle_built_trees():
     for p_follow in (0.0, 0.6, 1.0):
         tgt = S.make_greedy_targets(tok, par, cnt, cfg["V"], p_follow, seed=2)
         accept_and_compare(tok, par, cnt, tgt)
+
+
+# ---- full-vocabulary normalization ----------------------------------------------
+
+# binary32 tail: a sum of up to V terms <= 1 (relative error ~1e-6) taken to
+# log and rescaled: absolute error well below 1e-4 for the logit ranges here
+TAIL_TOL = 2e-5
+
+
+@pytest.mark.parametrize("dtype,V,M,L,B,T", [
+    ("f32", 1000, 8, 8, 1, 0.0), ("bf16", 1000, 8, 8, 2, 0.5), ("f32", 37, 37, 3, 2, 0.0),
+    ("bf16", 5003, 64, 4, 3, 1.0), ("f32", 131, 1, 5, 4, 2.0), ("bf16", 5003, 17, 16, 70, 0.0),
+    ("bf16", 151936, 64, 16, 2, 0.0),
+])
+def test_topm_tail_matches_oracle(dtype, V, M, L, B, T):
+    # small B*L rows split each row over several segments (merge kernel path)
+    cfg = dict(B=B, V=V, L=L, E=32, H=32, M=M, n=4, dtype=dtype, alpha=1.1, T=T)
+    base = S.make_base(B, L, V, 1.1, dtype, seed=V + M + B)
+    say(f"  topm_tail B={B} L={L} V={V} M={M} {dtype} T={T}")
+    bld = builder(cfg)
+    idx, val, tail = bld.topm_tail(S.to_torch({"b": base}, DEV)["b"])
+    torch.cuda.synchronize()
+    idx, val, tail = idx.cpu().numpy(), val.cpu().numpy(), tail.cpu().numpy()
+    bld.close()
+    rows = [(b, p) for b in range(B) for p in range(L)]
+    if len(rows) > 48:
+        rng = np.random.default_rng(0)
+        rows = [rows[i] for i in rng.choice(len(rows), 48, replace=False)]
+    for b, p in rows:
+        ri, rv = oracle.topm_row(base[b, p], M)
+        np.testing.assert_array_equal(idx[b, p], ri)
+        np.testing.assert_array_equal(val[b, p].astype(np.float64), rv)
+        want = oracle.tail_lse(base[b, p], M, T)
+        if want == -np.inf:
+            assert tail[b, p] == -np.inf
+        else:
+            assert abs(tail[b, p] - want) <= TAIL_TOL * max(1.0, abs(want)), (b, p, tail[b, p], want)
+
+
+def test_topm_tail_full_batch_sampled_rows():
+    cfg, inp = inputs("qwen3_4b_batched")
+    bld = builder(cfg)
+    idx, val, tail = bld.topm_tail(S.to_torch({"b": inp["base"]}, DEV)["b"])
+    torch.cuda.synchronize()
+    tail = tail.cpu().numpy()
+    bld.close()
+    rng = np.random.default_rng(3)
+    for _ in range(16):
+        b, p = int(rng.integers(cfg["B"])), int(rng.integers(cfg["L"]))
+        want = oracle.tail_lse(inp["base"][b, p], cfg["M"], cfg["T"])
+        assert abs(tail[b, p] - want) <= TAIL_TOL * max(1.0, abs(want)), (b, p, tail[b, p], want)
+
+
+@pytest.mark.parametrize("over,variant", [((), "default"), ((("T", 0.5),), "default"),
+                                          ((), "strong"), ((("M", 1),), "default"),
+                                          ((("n", 64), ("L", 8)), "default")])
+def test_full_vocab_tiny(over, variant):
+    cfg = S.with_config("tiny", full_vocab=True, **dict(over))
+    inp = S.make_inputs(cfg, seed=21, variant=variant)
+    kw = STRONG if variant == "strong" else {}
+    build_and_compare(cfg, inp, **kw)
+
+
+def test_full_vocab_bf16_ragged():
+    cfg = dict(B=70, V=5003, L=16, E=256, H=128, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0,
+               full_vocab=True)
+    inp = S.make_inputs(cfg, seed=9)
+    build_and_compare(cfg, inp, requests=range(0, 70, 7))
+
+
+def test_full_vocab_qwen3_4b_batched_sampled():
+    cfg, inp = inputs("qwen3_4b_batched")
+    cfg = dict(cfg, full_vocab=True)
+    build_and_compare(cfg, inp, requests=[0, 31, 63])
+
+
+def test_full_vocab_marginal_matches_oracle():
+    cfg = S.with_config("tiny", full_vocab=True, B=3)
+    inp = S.make_inputs(cfg, seed=13)
+    marginal_and_compare(cfg, inp, requests=[0, 1, 2])
+    cfg, inp = inputs("qwen3_4b_batched")
+    marginal_and_compare(dict(cfg, full_vocab=True), inp, requests=[5, 50])
