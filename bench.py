@@ -173,6 +173,35 @@ def main():
                         (fout["parents"] == out["parents"]).all(dim=1)).float().mean())
     fbld.close()
 
+    # ---- the 256-wide correction head (extra key): the same logits and
+    # embeddings, a 256-wide GRU state and C = W_2 [V, 256]
+    c256 = S.with_config("qwen3_4b_head256") if args.config == "qwen3_4b_batched" else None
+    h256 = None
+    if c256 is not None:
+        t256 = S.to_torch(S.make_inputs(c256, seed=0, skip=("base", "emb")), dev)
+        hb = dtree.Builder(B, L, V, E, c256["H"], M, n, c256["T"], c256["dtype"], 1e-5, device=dev)
+        hstep = lambda o=None: hb.build(t["base"], t["emb"], t256["w_ih"], t256["w_hh"], t256["b_ih"],
+                                        t256["b_hh"], t256["C"], t256["h0"], out=o)
+        hout = hstep()
+        for _ in range(3):
+            hstep(hout)
+        torch.cuda.synchronize()
+        h0t = time.perf_counter()
+        for _ in range(args.stage_steps):
+            hstep(hout)
+        torch.cuda.synchronize()
+        h_us = (time.perf_counter() - h0t) * 1e6 / max(args.stage_steps, 1)
+        dtree.dt_timing_enable(hb.handle, 2, 3)
+        for _ in range(3):
+            hstep(hout)
+        torch.cuda.synchronize()
+        h256 = {"workload": "qwen3_4b_head256: H=256, C [V, 256], otherwise as the main workload",
+                "us_per_round": round(h_us, 1), "tree_builds_per_s": round(B / (h_us * 1e-6), 1),
+                "gru_gemm_each_us": round(float(np.mean(dtree.dt_timing_read(hb.handle, 5))) * 1e3, 2),
+                "node_step_each_us": round(float(np.mean(dtree.dt_timing_read(hb.handle, 3))) * 1e3 / n, 2)}
+        hb.close()
+        del t256
+
     # ---- the greedy acceptance walk on the timed trees (extra key): synthetic
     # greedy target tokens that follow one of a node's children with
     # probability 0.8
@@ -251,6 +280,7 @@ def main():
                             "topm_select_with_tail_us": round(fv_sel * 1e3, 2),
                             "topm_select_with_tail_gbs": round(topm_bytes / (fv_sel * 1e-3) / 1e9, 1),
                             "trees_same_shape_as_top_m_softmax": round(same_shape, 4)},
+        "head256_mode": h256,
         "acceptance_walk": {"kernel_us": round(acc_us, 2), "requests": B,
                             "mean_tokens_per_round_synthetic_targets": round(tau, 3),
                             "target_follow_probability": 0.8},

@@ -56,6 +56,10 @@ CONFIGS = {
     # Qwen3-8B-shaped drafter, T = 1.0, flatter logits
     "qwen3_8b": dict(B=32, V=151936, L=16, E=4096, H=1024, M=64, n=16, dtype="bf16",
                      alpha=0.8, T=1.0),
+    # Qwen3-4B shapes with a 256-wide GRU state, so that the correction head
+    # C = W_2 is [V, 256] (the 256 x M slice the pages print)
+    "qwen3_4b_head256": dict(B=64, V=151936, L=16, E=2560, H=256, M=64, n=16, dtype="bf16",
+                             alpha=1.1, T=0.0),
     # large batch, large budget, peaked logits (long chains)
     "stress": dict(B=256, V=151936, L=16, E=2560, H=1024, M=64, n=64, dtype="bf16",
                    alpha=2.0, T=0.0),
@@ -141,20 +145,23 @@ def _normal(seed, name, shape, std, dtype):
     return out
 
 
-def make_inputs(cfg: dict, seed: int = 0, variant: str = "default", requests=None) -> dict:
+def make_inputs(cfg: dict, seed: int = 0, variant: str = "default", requests=None, skip=()) -> dict:
     """Inputs of a workload as numpy arrays.
 
     variant: "default"; "strong" (h0 ~ N(0,1) and C scaled by 10, to make the
     correction change trees); "zero_c" (C = 0: the factorized ablation).
     ``requests`` restricts the per-request tensors to those request ids
-    (their values equal those of the full batch).
+    (their values equal those of the full batch).  Tensors named in ``skip``
+    ("base", "emb") are not drawn (None): they depend on neither H nor the
+    variant, so a caller can reuse them from another workload of the same
+    B, L, V, E, alpha and seed.
     """
     B, V, L, E, H = cfg["B"], cfg["V"], cfg["L"], cfg["E"], cfg["H"]
     dt = cfg["dtype"]
     reqs = list(range(B)) if requests is None else list(requests)
     inp = {
-        "base": make_base(B, L, V, cfg["alpha"], dt, seed, reqs),
-        "emb": _normal(seed, "emb", (V, E), 1.0 / math.sqrt(E), dt),
+        "base": None if "base" in skip else make_base(B, L, V, cfg["alpha"], dt, seed, reqs),
+        "emb": None if "emb" in skip else _normal(seed, "emb", (V, E), 1.0 / math.sqrt(E), dt),
         "w_ih": _normal(seed, "w_ih", (3 * H, E), 1.0 / math.sqrt(E), dt),
         "w_hh": _normal(seed, "w_hh", (3 * H, H), 1.0 / math.sqrt(H), dt),
         "b_ih": _normal(seed, "b_ih", (3 * H,), 1.0 / math.sqrt(H), dt),

@@ -441,3 +441,17 @@ def test_full_vocab_marginal_matches_oracle():
     marginal_and_compare(cfg, inp, requests=[0, 1, 2])
     cfg, inp = inputs("qwen3_4b_batched")
     marginal_and_compare(dict(cfg, full_vocab=True), inp, requests=[5, 50])
+
+
+# ---- the 256-wide correction head ---------------------------------------------------
+
+def test_build_head256_sampled():
+    cfg, inp = inputs("qwen3_4b_head256")
+    build_and_compare(cfg, inp, requests=[0, 31, 63])
+
+
+@pytest.mark.parametrize("variant", ["default", "strong"])
+def test_build_head256_small(variant):
+    cfg = dict(B=9, V=5003, L=16, E=256, H=256, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0)
+    inp = S.make_inputs(cfg, seed=17, variant=variant)
+    build_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
