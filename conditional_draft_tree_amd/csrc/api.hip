@@ -21,7 +21,7 @@ thread_local char g_create_error[512] = "";
 
 struct Layout {
     size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
-        rstate, xpack, hpack, hprev, tail, tail_part;
+        rstate, xpack, hpack, hprev, tail, tail_part, wpack;
     size_t total;
 };
 
@@ -104,6 +104,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
     l.nval = take(B * 64 * 4);
     l.tail = take(B * L * 4);                          // full-vocabulary mode: tail_lse per row
     l.tail_part = take(B * L * (size_t)nseg * 2 * 4);  // its per-segment (m, s) sums
+    l.wpack = take(c.dtype == DT_BF16 ? (size_t)3 * H * (c.E + c.H) * 2 : 0);  // weights in operand tiles
     l.total = off;
     return l;
 }
@@ -476,11 +477,15 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     g.B = c.B; g.E = c.E; g.H = c.H;
     g.ksplit = h->ksplit;
     g.dtype = (int)c.dtype;
+    g.wpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.wpack) : nullptr;
 
     DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
     DT_TRY(dt::launch_node_step(a, h->lds, 0, st, ev), "node step launch");
     for (int step = 1; step < c.n; ++step) {
         if (!marginal) {
+            // the first contraction of the call leaves the weights in operand
+            // tiles; the later ones read that copy (contiguous 1 KB per wave load)
+            g.wmode = c.dtype == DT_BF16 ? (step == 1 ? 1 : 2) : 0;
             DT_TRY(kernel_marks(h, call, 2, 'g', 'G', &ev), "timing event");
             DT_TRY(dt::launch_gru_gates(g, st, ev), "GRU contraction launch");
         }

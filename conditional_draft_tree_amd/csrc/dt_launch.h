@@ -63,6 +63,11 @@ struct GruGatesArgs {
     float* partial;
     int B, E, H, ksplit, dtype;
     int xwaves;  // bf16 path: waves per workgroup on the x part (set by the launcher)
+    // bf16 path: the weights in MFMA operand tiles ([H/16][3][nE + nH][512],
+    // see pack_index_w).  wmode 0: read W_ih / W_hh; 1: read them and write
+    // this copy; 2: read this copy.
+    uint16_t* wpack;
+    int wmode;
 };
 // Packed activations (bf16 elements).  Rows are grouped in blocks of 16 (the
 // MFMA operand rows); a block's K range is cut into 32-wide chunks; one chunk
@@ -76,6 +81,12 @@ __host__ __device__ inline size_t pack_index_h(int b, int part, int k, int H) {
     return ((size_t)(((b >> 4) * 3 + part) * (H >> 5) + (k >> 5)) * 16 + (b & 15)) * 32 + (k & 31);
 }
 inline int pack_rows(int B) { return (B + 63) / 64 * 64; }
+// Packed weights: operand tile (unit tile ut of 16 hidden units, gate g, K
+// chunk c of nchunk = E/32 + H/32; x chunks first) is 512 contiguous bf16,
+// lane l's 8 elements (unit l % 16, K 8 * (l / 16) .. + 8 of the chunk) at l * 8.
+__host__ __device__ inline size_t pack_index_w(int ut, int g, int c, int nchunk) {
+    return ((size_t)(ut * 3 + g) * nchunk + c) * 512;
+}
 __device__ __forceinline__ size_t state_index(const GruGatesArgs& a, int b) {
     return (size_t)b * a.hrows + (size_t)(a.hsel ? a.hsel[b] : 0);
 }

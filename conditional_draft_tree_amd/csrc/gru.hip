@@ -85,6 +85,10 @@ __device__ __forceinline__ void wave_chunks(int nE, int nH, int ksplit, int wx, 
     }
 }
 
+// WM: weight source (0: W_ih / W_hh; 1: those, and write the packed copy; 2:
+// the packed copy), a template parameter so that each variant keeps one
+// address path and no dead store code.
+template <int WM>
 __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesArgs a) {
     // every wave's sums of the workgroup's 64 x 16 outputs x 4 gates: 128 KB
     __shared__ f32x4 red[kWaves8][kRowBlocks * 4][kWave];
@@ -99,7 +103,17 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
 
     const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
     const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
-    const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;
+    const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;  // one gate's rows
+    // packed weights: the 1 KB operand tile (16 units x 32 K) of unit tile ut,
+    // gate g and chunk c (x chunks, then h chunks) is contiguous; lane l's
+    // 16 bytes sit at l * 16 in it (see pack_index_w)
+    constexpr bool wread = WM == 2, wwrite = WM == 1;
+    const size_t wgate = (size_t)(nE + nH) * 512;  // one gate of one unit tile
+    // per-lane base and strides (gate, chunk) of the weight loads, either layout
+    const bf16_t* wpl = (const bf16_t*)a.wpack + pack_index_w(ut, 0, 0, nE + nH) + lane * 8;
+    const bf16_t* wxb = wread ? wpl : wi + kq;
+    const bf16_t* whb = wread ? wpl + (size_t)nE * 512 : wh + kq;
+    const size_t wxg = wread ? wgate : gi, whg = wread ? wgate : gh, wcs = wread ? 512 : 32;
     const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     // packed activations: lane l reads row l % 16 of its row block at K offset
     // 8 * (l / 16) of a chunk; a wave's read is one contiguous 1 KB block.
@@ -128,13 +142,12 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
             bf16x8 w[kMaxXChunks][3], x[kMaxXChunks][kRowBlocks];
 #pragma unroll
             for (int i = 0; i < kMaxXChunks; ++i) {
-                const int k = (cb + min(i, n - 1)) * 32 + kq;  // clamped: always in bounds
+                const size_t c = (size_t)(cb + min(i, n - 1));  // clamped: always in bounds
 #pragma unroll
                 for (int g = 0; g < 3; ++g) {  // chunks past n: zero weights (no branch, see below)
-                    const bf16x8 v = load_bf16x8(wi + g * gi + k);
+                    const bf16x8 v = load_bf16x8(wxb + g * wxg + c * wcs);
                     w[i][g] = i < n ? v : zero;
                 }
-                const size_t c = (size_t)(cb + min(i, n - 1));
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
             }
@@ -142,6 +155,15 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
             // across this point: loads sunk next to their MFMAs would wait
             // one by one (loads complete in order)
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (wwrite) {  // the round's first contraction leaves the packed copy
+#pragma unroll
+                for (int i = 0; i < kMaxXChunks; ++i)
+                    if (i < n)
+#pragma unroll
+                        for (int g = 0; g < 3; ++g)
+                            *reinterpret_cast<u32x4*>((bf16_t*)wpl + g * wgate + (size_t)(cb + i) * 512) =
+                                __builtin_bit_cast(u32x4, w[i][g]);
+            }
 #pragma unroll
             for (int i = 0; i < kMaxXChunks; ++i) {
 #pragma unroll
@@ -159,13 +181,12 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
             bf16x8 w[kMaxHChunks][3], hp[kMaxHChunks][kRowBlocks][3];
 #pragma unroll
             for (int i = 0; i < kMaxHChunks; ++i) {
-                const int k = (cb + min(i, n - 1) - nE) * 32 + kq;
+                const size_t c = (size_t)(cb + min(i, n - 1) - nE);
 #pragma unroll
                 for (int g = 0; g < 3; ++g) {
-                    const bf16x8 v = load_bf16x8(wh + g * gh + k);
+                    const bf16x8 v = load_bf16x8(whb + g * whg + c * wcs);
                     w[i][g] = i < n ? v : zero;
                 }
-                const size_t c = (size_t)(cb + min(i, n - 1) - nE);
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
@@ -173,6 +194,15 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                         hp[i][rb][q] = load_bf16x8(hblk[rb] + q * hpart + c * xstep);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (wwrite) {
+#pragma unroll
+                for (int i = 0; i < kMaxHChunks; ++i)
+                    if (i < n)
+#pragma unroll
+                        for (int g = 0; g < 3; ++g)
+                            *reinterpret_cast<u32x4*>((bf16_t*)wpl + g * wgate + (size_t)(cb + i) * 512) =
+                                __builtin_bit_cast(u32x4, w[i][g]);
+            }
 #pragma unroll
             for (int i = 0; i < kMaxHChunks; ++i) {
 #pragma unroll
@@ -293,8 +323,10 @@ hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream, LaunchEve
     if (a.dtype == 1) {
         GruGatesArgs b = a;
         b.xwaves = x_waves(a.E / 32, a.H / 32, a.ksplit);
-        return launch_kernel(gru_gates_bf16_kernel, dim3(a.H / 16, (a.B + 63) / 64, a.ksplit),
-                             dim3(kWaves8 * kWave), 0, stream, ev, b);
+        const dim3 grid(a.H / 16, (a.B + 63) / 64, a.ksplit), block(kWaves8 * kWave);
+        if (a.wpack && a.wmode == 2) return launch_kernel(gru_gates_bf16_kernel<2>, grid, block, 0, stream, ev, b);
+        if (a.wpack && a.wmode == 1) return launch_kernel(gru_gates_bf16_kernel<1>, grid, block, 0, stream, ev, b);
+        return launch_kernel(gru_gates_bf16_kernel<0>, grid, block, 0, stream, ev, b);
     }
     return launch_kernel(gru_gates_f32_kernel, dim3((a.H + 63) / 64, a.B, 1), dim3(64), 0, stream, ev, a);
 }
