@@ -202,6 +202,41 @@ def main():
         hb.close()
         del t256
 
+    # ---- the folded input projection (extra key): the [V, 3H] table of
+    # b_ih + W_ih . Emb[v] is computed once, then each step contracts W_hh . h only
+    folded = None
+    if esz == 2:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        table = bld.fold_input(t["emb"], t["w_ih"], t["b_ih"])
+        e1.record()
+        torch.cuda.synchronize()
+        fold_ms = e0.elapsed_time(e1)
+        fstep = lambda o=None: bld.build_folded(t["base"], table, t["w_hh"], t["b_hh"], t["C"], t["h0"], out=o)
+        fo = fstep()
+        for _ in range(3):
+            fstep(fo)
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for _ in range(args.stage_steps):
+            fstep(fo)
+        torch.cuda.synchronize()
+        fo_us = (time.perf_counter() - f0) * 1e6 / max(args.stage_steps, 1)
+        dtree.dt_timing_enable(bld.handle, 2, 3)
+        for _ in range(3):
+            fstep(fo)
+        torch.cuda.synchronize()
+        folded = {"us_per_round": round(fo_us, 1), "tree_builds_per_s": round(B / (fo_us * 1e-6), 1),
+                  "fold_once_ms": round(fold_ms, 2), "table_bytes": V * 3 * H * 4,
+                  "gru_gemm_each_us": round(float(np.mean(dtree.dt_timing_read(bld.handle, 5))) * 1e3, 2),
+                  "node_step_each_us": round(float(np.mean(dtree.dt_timing_read(bld.handle, 3))) * 1e3 / n, 2),
+                  "trees_equal_to_contracted": round(float(((fo["tokens"] == out["tokens"]).all(dim=1) &
+                                                            (fo["parents"] == out["parents"]).all(dim=1))
+                                                           .float().mean()), 4)}
+        dtree.dt_timing_enable(bld.handle, 0, 0)
+        del table
+
     # ---- the greedy acceptance walk on the timed trees (extra key): synthetic
     # greedy target tokens that follow one of a node's children with
     # probability 0.8
@@ -281,6 +316,7 @@ def main():
                             "topm_select_with_tail_gbs": round(topm_bytes / (fv_sel * 1e-3) / 1e9, 1),
                             "trees_same_shape_as_top_m_softmax": round(same_shape, 4)},
         "head256_mode": h256,
+        "folded_input_mode": folded,
         "acceptance_walk": {"kernel_us": round(acc_us, 2), "requests": B,
                             "mean_tokens_per_round_synthetic_targets": round(tau, 3),
                             "target_follow_probability": 0.8},

@@ -63,12 +63,17 @@ def load_library():
         lib.dt_gru_step.argtypes = [H, vp, C.c_size_t, vp, f32p, vp, vp, vp, vp, f32p, vp]
         lib.dt_correct.argtypes = [H, i32p, f32p, vp, f32p, i32p, i32p, f32p, vp]
         lib.dt_accept_greedy.argtypes = [H] + [i32p] * 7 + [vp]
+        lib.dt_fold_input.argtypes = [H, vp, vp, vp, f32p, vp]
+        # handle, workspace, bytes, base, table, W_hh, b_hh, C, h0, tokens, parents, depths,
+        # scores, mask, count, flags, stream
+        lib.dt_build_folded.argtypes = [H, vp, C.c_size_t, vp, f32p, vp, vp, vp, f32p] + [i32p] * 3 + [
+            f32p, vp, i32p, vp, vp]
         lib.dt_timing_enable.argtypes = [H, C.c_int, C.c_int]
         lib.dt_timing_read.argtypes = [H, C.c_int, C.POINTER(C.c_float), C.c_int,
                                        C.POINTER(C.c_int)]
         for f in (lib.dt_create, lib.dt_build, lib.dt_build_marginal, lib.dt_topm, lib.dt_topm_tail,
                   lib.dt_gru_step,
-                  lib.dt_correct, lib.dt_accept_greedy,
+                  lib.dt_correct, lib.dt_accept_greedy, lib.dt_fold_input, lib.dt_build_folded,
                   lib.dt_timing_enable, lib.dt_timing_read):
             f.restype = C.c_int
         _lib = lib
@@ -129,6 +134,19 @@ def dt_build(handle, workspace, base, emb, w_ih, w_hh, b_ih, b_hh, Cmat, h0, tok
                         _p(base), _p(emb), _p(w_ih), _p(w_hh), _p(b_ih), _p(b_hh), _p(Cmat), _p(h0),
                         _p(tokens), _p(parents), _p(depths), _p(scores), _p(mask), _p(count),
                         _p(flags), _stream(stream)), handle)
+
+
+def dt_fold_input(handle, emb, w_ih, b_ih, table, stream=None):
+    _check(load_library().dt_fold_input(handle, _p(emb), _p(w_ih), _p(b_ih), _p(table), _stream(stream)), handle)
+
+
+def dt_build_folded(handle, workspace, base, table, w_hh, b_hh, Cmat, h0, tokens, parents, depths, scores, mask,
+                    count, flags, stream=None):
+    lib = load_library()
+    _check(lib.dt_build_folded(handle, _p(workspace), workspace.numel() if workspace is not None else 0,
+                               _p(base), _p(table), _p(w_hh), _p(b_hh), _p(Cmat), _p(h0), _p(tokens),
+                               _p(parents), _p(depths), _p(scores), _p(mask), _p(count), _p(flags),
+                               _stream(stream)), handle)
 
 
 def dt_build_marginal(handle, workspace, base, tokens, parents, depths, scores, mask, count, flags,
@@ -267,6 +285,35 @@ class Builder:
                     mask=torch.empty((B, S, S), dtype=torch.uint8, device=dev),
                     count=torch.empty((B,), dtype=torch.int32, device=dev),
                     flags=torch.empty((B,), dtype=torch.int32, device=dev))
+
+    def fold_input(self, emb, w_ih, b_ih=None, stream=None):
+        """The folded input projection table [V, 3H] float32 (b_ih + W_ih . emb[v])."""
+        import torch
+        c = self.cfg
+        self._chk("emb", emb, (c["V"], c["E"]))
+        self._chk("w_ih", w_ih, (3 * c["H"], c["E"]))
+        self._chk("b_ih", b_ih, (3 * c["H"],), optional=True)
+        table = torch.empty((c["V"], 3 * c["H"]), dtype=torch.float32, device=self.device)
+        dt_fold_input(self.handle, emb, w_ih, b_ih, table, stream)
+        return table
+
+    def build_folded(self, base, table, w_hh, b_hh, Cmat, h0=None, out=None, stream=None):
+        """dt_build with the folded input projection ``table`` (from fold_input)."""
+        import torch
+        c = self.cfg
+        B, L, V, H = c["B"], c["L"], c["V"], c["H"]
+        self._chk("base", base, (B, L, V))
+        self._chk("table", table, (V, 3 * H), dtype=torch.float32)
+        self._chk("w_hh", w_hh, (3 * H, H))
+        self._chk("b_hh", b_hh, (3 * H,), optional=True)
+        self._chk("C", Cmat, (V, H))
+        self._chk("h0", h0, (B, H), dtype=torch.float32, optional=True)
+        if out is None:
+            out = self._outputs()
+        dt_build_folded(self.handle, self.workspace, base, table, w_hh, b_hh, Cmat, h0, out["tokens"],
+                        out["parents"], out["depths"], out["scores"], out["mask"], out["count"], out["flags"],
+                        stream)
+        return out
 
     def build_marginal(self, base, out=None, stream=None):
         """The factorized (marginal) scoring mode: dt_build with no GRU and no

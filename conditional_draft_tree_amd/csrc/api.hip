@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -39,7 +40,8 @@ struct Marker {
 struct dt_handle {
     dt_config cfg;
     int nseg;    // top-M segments per row
-    int ksplit;  // K ranges of the gate contraction
+    int ksplit;    // K ranges of the gate contraction
+    int ksplit_f;  // of its recurrent part alone (folded input projection)
     dt::NodeLds lds;
     Layout lay;
     std::string err;
@@ -76,7 +78,7 @@ float tail_scale(const dt_config& c) {
     return 1.4426950408889634f / (c.temperature > 0.f ? c.temperature : 1.f);
 }
 
-Layout plan_layout(const dt_config& c, int nseg, int ksplit) {
+Layout plan_layout(const dt_config& c, int nseg, int ksplit) {  // ksplit: the larger of the two
     Layout l{};
     const size_t B = c.B, L = c.L, M = c.M, S = (size_t)c.n + 1, H = c.H;
     size_t off = 0;
@@ -213,8 +215,9 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     h->cfg = c;
     h->nseg = nseg;
     h->ksplit = dt::gru_ksplit(c.B, c.E, c.H, (int)c.dtype);
+    h->ksplit_f = dt::gru_ksplit(c.B, 0, c.H, (int)c.dtype);
     h->lds = lds;
-    h->lay = plan_layout(c, h->nseg, h->ksplit);
+    h->lay = plan_layout(c, h->nseg, std::max(h->ksplit, h->ksplit_f));
     *out = h;
     return DT_OK;
 }
@@ -392,17 +395,24 @@ dt_status dt_accept_greedy(dt_handle* h, const int32_t* tokens, const int32_t* p
 }  // extern "C"
 
 namespace {
+// table: the folded input projection [V, 3H] (dt_build_folded; emb, W_ih and
+// b_ih are then unused), or NULL.
 dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, const void* base, const void* emb,
                    const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
                    const void* C, const float* h0, int32_t* tokens, int32_t* parents, int32_t* depths,
-                   float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream) {
+                   float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream,
+                   const float* table = nullptr) {
     if (!h) return DT_ERR_INVALID_ARG;
     const dt_config& c = h->cfg;
     if (c.B == 0) return DT_OK;
     if (!base || !tokens || !parents || !depths || !scores || !mask || !count || !flags)
         return fail(h, DT_ERR_INVALID_ARG, "dt_build: null pointer");
-    if (!marginal && (!emb || !W_ih || !W_hh || !C))
+    if (!marginal && !table && (!emb || !W_ih || !W_hh || !C))
         return fail(h, DT_ERR_INVALID_ARG, "dt_build: null pointer (only b_ih, b_hh, h0 may be NULL)");
+    if (table && (!W_hh || !C))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_build_folded: null pointer (only b_hh, h0 may be NULL)");
+    if (misaligned(table))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_build_folded: the table must be 16-byte aligned");
     if (misaligned(base) || misaligned(emb) || misaligned(W_ih) || misaligned(W_hh) || misaligned(C) ||
         misaligned(h0) || misaligned(b_ih) || misaligned(b_hh))
         return fail(h, DT_ERR_INVALID_ARG, "dt_build: matrices must be 16-byte aligned");
@@ -442,11 +452,13 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     a.eps = c.near_tie_eps;
     a.C = C; a.h0 = h0;
     a.tidx = tidx; a.tval = tval;
-    a.b_ih = b_ih; a.b_hh = b_hh;
+    a.b_ih = table ? nullptr : b_ih;  // folded into the table
+    a.b_hh = b_hh;
+    a.table = table;
     a.hstate = c.dtype == DT_F32 ? (float*)(w + L.hstate) : nullptr;
     a.hsplit = c.dtype == DT_BF16 ? (uint16_t*)(w + L.hsplit) : nullptr;
     a.partial = (const float*)(w + L.gpart);
-    a.ksplit = h->ksplit;
+    a.ksplit = table ? h->ksplit_f : h->ksplit;
     a.gru_tok = (int32_t*)(w + L.gru_tok);
     a.gru_par = (int32_t*)(w + L.gru_par);
     a.child_tok = (int32_t*)(w + L.child_tok);
@@ -456,7 +468,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     a.nidx = (int32_t*)(w + L.nidx);
     a.nval = (float*)(w + L.nval);
     a.emb = emb;
-    a.xpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.xpack) : nullptr;
+    a.xpack = c.dtype == DT_BF16 && !marginal && !table ? (uint16_t*)(w + L.xpack) : nullptr;
     a.hpack = c.dtype == DT_BF16 && !marginal ? (uint16_t*)(w + L.hpack) : nullptr;
     a.hprev = c.dtype == DT_BF16 && !marginal ? (float*)(w + L.hprev) : nullptr;
     a.tail = tail;
@@ -464,7 +476,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     a.mask = mask; a.count = count; a.flags = flags;
 
     dt::GruGatesArgs g{};
-    g.xpack = a.xpack;
+    g.xpack = table ? a.hpack : a.xpack;  // (no x part when folded)
     g.hpack = a.hpack;
     g.x = emb;
     g.xtok = a.gru_tok;
@@ -474,8 +486,8 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     g.W_ih = W_ih;
     g.W_hh = W_hh;
     g.partial = (float*)(w + L.gpart);
-    g.B = c.B; g.E = c.E; g.H = c.H;
-    g.ksplit = h->ksplit;
+    g.B = c.B; g.E = table ? 0 : c.E; g.H = c.H;  // folded: the recurrent part alone
+    g.ksplit = a.ksplit;
     g.dtype = (int)c.dtype;
     g.wpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.wpack) : nullptr;
 
@@ -506,6 +518,26 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
                    float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream) {
     return build_impl(false, h, ws, ws_bytes, base, emb, W_ih, W_hh, b_ih, b_hh, C, h0, tokens, parents,
                       depths, scores, mask, count, flags, stream);
+}
+
+dt_status dt_build_folded(dt_handle* h, void* ws, size_t ws_bytes, const void* base, const float* table,
+                          const void* W_hh, const void* b_hh, const void* C, const float* h0, int32_t* tokens,
+                          int32_t* parents, int32_t* depths, float* scores, uint8_t* mask, int32_t* count,
+                          uint32_t* flags, void* stream) {
+    if (h && !table) return fail(h, DT_ERR_INVALID_ARG, "dt_build_folded: null table");
+    return build_impl(false, h, ws, ws_bytes, base, nullptr, nullptr, W_hh, nullptr, b_hh, C, h0, tokens, parents,
+                      depths, scores, mask, count, flags, stream, table);
+}
+
+dt_status dt_fold_input(dt_handle* h, const void* emb, const void* W_ih, const void* b_ih, float* table,
+                        void* stream) {
+    if (!h) return DT_ERR_INVALID_ARG;
+    const dt_config& c = h->cfg;
+    if (!emb || !W_ih || !table) return fail(h, DT_ERR_INVALID_ARG, "dt_fold_input: null pointer");
+    if (misaligned(emb) || misaligned(W_ih) || misaligned(b_ih) || misaligned(table))
+        return fail(h, DT_ERR_INVALID_ARG, "dt_fold_input: buffers must be 16-byte aligned");
+    hipError_t e = dt::launch_fold(emb, W_ih, b_ih, table, c.V, c.E, c.H, (int)c.dtype, (hipStream_t)stream);
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_fold_input launch");
 }
 
 dt_status dt_build_marginal(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int32_t* tokens,

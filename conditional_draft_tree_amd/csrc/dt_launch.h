@@ -134,6 +134,7 @@ struct NodeArgs {
     uint16_t* hpack;     // pack_index_x / pack_index_h), NULL on the binary32 path
     float* hprev;        // [B, H] the next expanded slot's parent state (bf16 path), or NULL
     const float* tail;   // [B, L] full-vocabulary mode: each row's tail_lse; NULL = M-slice softmax
+    const float* table;  // [V, 3H] folded input projection (b_ih + W_ih . Emb[v]); NULL = contracted
     // outputs
     int32_t* tokens;
     int32_t* parents;
@@ -156,6 +157,11 @@ hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipS
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,
                           const int32_t* pos, int32_t* tok_sorted, float* lp_sorted, int B, int L,
                           int H, int M, int dtype, float temp, hipStream_t stream);
+
+// ---- folded input projection (fold.hip) ---------------------------------------
+// table [V, 3H] binary32 = b_ih + W_ih . Emb[v] for every token v
+hipError_t launch_fold(const void* emb, const void* W_ih, const void* b_ih, float* table, int V, int E, int H,
+                       int dtype, hipStream_t stream);
 
 // ---- greedy acceptance walk (accept.hip) --------------------------------------
 // trees [B, n+1] as dt_build writes them, target [B, n+1] -> path [B, n+1],

@@ -292,6 +292,19 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
         const float v = tp[min(lane, a.L - 1)];
         tail_l = a.tail ? v : -INFINITY;
     }
+    // folded input projection: the row of this slot's token (r, z, n parts of
+    // b_ih + W_ih . x for this thread's state element), from a valid address
+    // in either mode
+    float xg[3] = {0.f, 0.f, 0.f};
+    if constexpr (!MARG) {
+        const int xt = min(max(rs0[1], 0), a.V - 1);
+        const float* xp = a.table ? a.table + (size_t)xt * 3 * H : a.partial;
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+            const float v = xp[(size_t)g * H + kc];
+            xg[g] = a.table ? v : 0.f;
+        }
+    }
     // the parent's state (the GRU's previous state), exact: binary32, or the sum
     // of its three bf16 parts
     const int par = step == 0 ? 0 : min(max(rs1[1], 0), a.n);
@@ -384,6 +397,11 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
                 const void* bp = g < 3 ? a.b_ih : a.b_hh;
                 if (bp) bias[g] = load1<T>((const T*)bp + (size_t)(g % 3) * H + kk);
             }
+            if (a.table) {
+                const int xt = min(max(rs0[1], 0), a.V - 1);
+#pragma unroll
+                for (int g = 0; g < 3; ++g) xg[g] = a.table[((size_t)xt * 3 + g) * H + kk];
+            }
         }
         if (kk >= H) break;
         float hv = 0.f;
@@ -397,6 +415,11 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
                 sum[g] = t[0][g];
 #pragma unroll
                 for (int s2 = 1; s2 < KS; ++s2) sum[g] += t[s2][g];
+            }
+            if (a.table) {  // the x parts of r, z and the candidate (slot 2 holds none)
+                sum[0] += xg[0];
+                sum[1] += xg[1];
+                sum[2] += xg[2];
             }
             hv = gru_cell_b(sum[0], sum[1], sum[2], sum[3], bias[0], bias[1], bias[2], bias[3], bias[4],
                             bias[5], hp);
@@ -531,10 +554,11 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
         // parent is slot `step` (state in LDS) or an older slot (parts in
         // hsplit).
         constexpr int kXw0 = 2, kXwN = (NW - kXw0 + 1) / 2, kHw0 = kXw0 + kXwN, kHwN = NW - kHw0;
-        if (a.xpack && step + 1 < a.n) {
+        if (a.hpack && step + 1 < a.n) {
             const int ntok = s_dec[0], vpar = s_dec[1];
             const bool grow = ntok >= 0;
             if (wave < kHw0) {
+                if (!a.xpack) return;  // folded input projection: no x part to pack
                 const int nv = a.E >> 3;
                 for (int i = (wave - kXw0) * kWave + lane; i < nv; i += kXwN * kWave) {
                     u32x4 v = {0u, 0u, 0u, 0u};

@@ -194,6 +194,31 @@ dt_status dt_correct(dt_handle *h, const int32_t *idx, const float *val, const v
                      float *logp_sorted, void *stream);
 
 /*
+ * Folded input projection.  A node's GRU input is the embedding of its own
+ * token ([captcha] "Methodology -- deep read": the GRU state is advanced
+ * with the realized tokens of the path), so b_ih + W_ih . x takes one of V
+ * values, fixed by the model.
+ *
+ * dt_fold_input computes them once: table [V, 3H] binary32 (caller-owned,
+ * 16-byte aligned; 3 * 4 * H * V bytes, 1.9 GB at V = 151936, H = 1024),
+ * table[v][g H + u] = b_ih[g H + u] + sum_k W_ih[g H + u][k] * emb[v][k]
+ * (gate order r, z, n; b_ih may be NULL).  emb [V, E] and W_ih [3H, E] in
+ * the handle's dtype.  fp32 accumulation (bf16 products are exact).
+ *
+ * dt_build_folded is dt_build with that table in place of emb, W_ih and
+ * b_ih: each step's gate contraction covers the recurrent part W_hh . h
+ * alone and the node step adds the popped token's table row.  Same outputs
+ * as dt_build up to binary32 rounding order.  Errors as dt_build (a NULL
+ * table is DT_ERR_INVALID_ARG).
+ */
+dt_status dt_fold_input(dt_handle *h, const void *emb, const void *W_ih, const void *b_ih, float *table,
+                        void *stream);
+dt_status dt_build_folded(dt_handle *h, void *workspace, size_t ws_bytes, const void *base,
+                          const float *table, const void *W_hh, const void *b_hh, const void *C,
+                          const float *h0, int32_t *tokens, int32_t *parents, int32_t *depths,
+                          float *scores, uint8_t *mask, int32_t *count, uint32_t *flags, void *stream);
+
+/*
  * dt_topm_tail -- dt_topm plus each row's tail mass: tail[b][p] = log of the
  * sum of exp(x / T) (T = 1 when temperature = 0) over the logits x of row
  * (b, p) outside its top M; -inf when M = V.  This is the extra term of the

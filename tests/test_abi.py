@@ -133,6 +133,21 @@ def test_full_vocab_flag_is_validated():
     dtree.dt_destroy(h)
 
 
+def test_folded_entry_points_validate_before_any_launch():
+    lib = dtree.load_library()
+    h = make()
+    need = dtree.dt_workspace_bytes(h)
+    fake = C.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    assert lib.dt_fold_input(h, None, fake, None, fake, None) == -1
+    assert lib.dt_fold_input(h, fake, fake, None, C.c_void_p(0x10004), None) == -1
+    outs = [fake] * 7
+    assert lib.dt_build_folded(h, fake, need, fake, None, fake, None, fake, None, *outs, None) == -1
+    assert "table" in dtree.dt_last_error(h)
+    assert lib.dt_build_folded(h, fake, need, fake, fake, None, None, fake, None, *outs, None) == -1
+    assert lib.dt_build_folded(h, None, need, fake, fake, fake, None, fake, None, *outs, None) == -3
+    dtree.dt_destroy(h)
+
+
 def test_accept_greedy_null_pointer_before_any_launch():
     lib = dtree.load_library()
     h = make()
@@ -155,7 +170,12 @@ def test_empty_batch_is_a_noop():
     assert lib.dt_topm(h, None, 0, None, None, None, None) == 0
     assert lib.dt_accept_greedy(h, *([None] * 7), None) == 0
     assert lib.dt_topm_tail(h, None, 0, None, None, None, None, None) == 0
+    assert lib.dt_build_folded(h, None, 0, None, fake_table(), *([None] * 11), None) == 0
     dtree.dt_destroy(h)
+
+
+def fake_table():
+    return C.c_void_p(0x10000)  # B = 0: never dereferenced
 
 
 def test_timing_argument_checks():

@@ -455,3 +455,60 @@ def test_build_head256_small(variant):
     cfg = dict(B=9, V=5003, L=16, E=256, H=256, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0)
     inp = S.make_inputs(cfg, seed=17, variant=variant)
     build_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
+
+
+# ---- folded input projection ---------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,V,E,H", [("bf16", 1003, 256, 96), ("bf16", 4096, 2560, 64), ("f32", 100, 32, 32)])
+def test_fold_input_matches_float64(dtype, V, E, H):
+    cfg = dict(B=1, V=V, L=2, E=E, H=H, M=4, n=2, dtype=dtype, alpha=1.1, T=0.0)
+    inp = S.make_inputs(cfg, seed=V + E, skip=("base",))
+    bld = builder(cfg)
+    t = S.to_torch({k: inp[k] for k in ("emb", "w_ih", "b_ih")}, DEV)
+    table = bld.fold_input(t["emb"], t["w_ih"], t["b_ih"])
+    torch.cuda.synchronize()
+    got = table.cpu().numpy().astype(np.float64)
+    bld.close()
+    from bruteforce import as_f64
+    emb, w, b = as_f64(inp["emb"]), as_f64(inp["w_ih"]), as_f64(inp["b_ih"])
+    want = emb @ w.T + b
+    scale = np.abs(emb) @ np.abs(w).T + np.abs(b)
+    assert np.all(np.abs(got - want) <= 1e-5 * scale + 1e-7), np.max(np.abs(got - want) / (scale + 1e-30))
+
+
+def folded_and_compare(cfg, inp, requests=None, eps=1e-5, tol=SCORE_TOL):
+    """dt_build_folded against the oracle's standard tree (the same GRU)."""
+    B = cfg["B"]
+    reqs = list(range(B)) if requests is None else list(requests)
+    say(f"  folded build B={B} V={cfg['V']} E={cfg['E']} H={cfg['H']} {cfg['dtype']}")
+    bld = builder(cfg, eps)
+    t = S.to_torch(inp, DEV)
+    table = bld.fold_input(t["emb"], t["w_ih"], t["b_ih"])
+    out = bld.build_folded(t["base"], table, t["w_hh"], t["b_hh"], t["C"], t["h0"])
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    bld.close()
+    del table
+    refs = oracle.build_batch(inp, cfg["M"], cfg["n"], cfg["T"], eps=eps, requests=reqs, threads=8)
+    kinds = [compare_request(got, b, r, inp, b, cfg, eps, tol) for b, r in zip(reqs, refs)]
+    say(f"  folded: {kinds.count('exact')} exact, {kinds.count('flagged')} near-tie")
+    return got
+
+
+@pytest.mark.parametrize("over,variant", [((), "default"), ((("T", 0.5),), "default"), ((), "strong")])
+def test_folded_tiny(over, variant):
+    cfg = S.with_config("tiny", **dict(over))
+    inp = S.make_inputs(cfg, seed=31, variant=variant)
+    folded_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
+
+
+@pytest.mark.parametrize("variant", ["default", "strong"])
+def test_folded_bf16_ragged(variant):
+    cfg = dict(B=70, V=5003, L=16, E=256, H=128, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0)
+    inp = S.make_inputs(cfg, seed=12, variant=variant)
+    folded_and_compare(cfg, inp, requests=range(0, 70, 7), **(STRONG if variant == "strong" else {}))
+
+
+def test_folded_qwen3_4b_batched_sampled():
+    cfg, inp = inputs("qwen3_4b_batched")
+    folded_and_compare(cfg, inp, requests=[0, 31, 63])
