@@ -271,12 +271,23 @@ __device__ __forceinline__ void drain_stash(WaveTop& w, TailAcc& ta, u64* buf, S
     const u32x4 v = on ? svec[from + lane] : u32x4{0u, 0u, 0u, 0u};
     const int vi = on ? sidx[from + lane] : 0;
     set_thr(w, shared_bound(s_thr));
-#pragma unroll 1
+    // Elements at or above the bound as it stands (the others are out); a
+    // vector passed the filter through one or two of them, so the offers
+    // below take each lane's next pending element, lowest position first,
+    // for as many rounds as the fullest lane needs instead of P.
+    uint32_t pend = 0u;
+#pragma unroll
     for (int i = 0; i < P; ++i) {
         const float x = Elem<T>::get(v, i);
-        const bool cand = x >= w.thr_val;
-        if (TAIL && on && !cand) tail_add(ta, x);
-        offer<TAIL>(w, ta, buf, s_thr, on && cand, topm_key(x, (uint32_t)(lo + vi * P + i)));
+        if (on && x >= w.thr_val) pend |= 1u << i;
+        else if (TAIL && on) tail_add(ta, x);
+    }
+#pragma unroll 1
+    while (__ballot(pend != 0u)) {
+        const bool has = pend != 0u;
+        const int i = has ? __builtin_ctz(pend) : 0;
+        pend &= pend - 1u;
+        offer<TAIL>(w, ta, buf, s_thr, has, topm_key(Elem<T>::get(v, i), (uint32_t)(lo + vi * P + i)));
     }
     // fold now, so that the shared bounds follow every admitted key
     if (w.nbuf) fold_buffer<TAIL>(w, ta, buf, s_thr);
