@@ -412,6 +412,53 @@ def test_topm_tail_full_batch_sampled_rows():
         assert abs(tail[b, p] - want) <= TAIL_TOL * max(1.0, abs(want)), (b, p, tail[b, p], want)
 
 
+def adversarial_rows(order, V):
+    """Row shapes that stress the select's running threshold: ascending (every
+    vector beats the bound, all of its elements pending), descending (the first
+    batch holds the answer), all equal (every element ties, ids decide) and a
+    sawtooth (equal values recurring along the row)."""
+    up = np.linspace(-6.0, 6.0, V)
+    if order == "ascending":
+        return up
+    if order == "descending":
+        return up[::-1].copy()
+    if order == "equal":
+        return np.full(V, 0.25)
+    return np.resize(np.linspace(-1.0, 1.0, 1000), V)
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending", "equal", "sawtooth"])
+@pytest.mark.parametrize("dtype,B,L,V", [("bf16", 2, 2, 40000), ("f32", 2, 2, 40000), ("bf16", 64, 16, 16384)])
+def test_topm_adversarial_orders(order, dtype, B, L, V):
+    # (2, 2, 40000): each row over two segments and the merge kernel;
+    # (64, 16, 16384): 1024 rows, one workgroup per row
+    M, T = 64, 0.5
+    row = adversarial_rows(order, V)
+    base = np.stack([np.stack([row + 0.001 * (b * L + p) for p in range(L)]) for b in range(B)])
+    base = S.f32_to_bf16_bits(base.astype(np.float32)) if dtype == "bf16" else base.astype(np.float32)
+    cfg = dict(B=B, V=V, L=L, E=32, H=32, M=M, n=4, dtype=dtype, alpha=1.1, T=T)
+    say(f"  topm adversarial {order} B={B} L={L} V={V} {dtype}")
+    bld = builder(cfg)
+    t = S.to_torch({"b": base}, DEV)["b"]
+    idx, val = bld.topm(t)
+    idx2, val2, tail = bld.topm_tail(t)
+    torch.cuda.synchronize()
+    idx, val, idx2, val2, tail = (x.cpu().numpy() for x in (idx, val, idx2, val2, tail))
+    bld.close()
+    np.testing.assert_array_equal(idx, idx2)
+    np.testing.assert_array_equal(val, val2)
+    rows = [(b, p) for b in range(B) for p in range(L)]
+    if len(rows) > 24:
+        rng = np.random.default_rng(1)
+        rows = [rows[i] for i in rng.choice(len(rows), 24, replace=False)]
+    for b, p in rows:
+        ri, rv = oracle.topm_row(base[b, p], M)
+        np.testing.assert_array_equal(idx[b, p], ri)
+        np.testing.assert_array_equal(val[b, p].astype(np.float64), rv)
+        want = oracle.tail_lse(base[b, p], M, T)
+        assert abs(tail[b, p] - want) <= TAIL_TOL * max(1.0, abs(want)), (b, p, tail[b, p], want)
+
+
 @pytest.mark.parametrize("over,variant", [((), "default"), ((("T", 0.5),), "default"),
                                           ((), "strong"), ((("M", 1),), "default"),
                                           ((("n", 64), ("L", 8)), "default")])
