@@ -559,3 +559,55 @@ def test_folded_bf16_ragged(variant):
 def test_folded_qwen3_4b_batched_sampled():
     cfg, inp = inputs("qwen3_4b_batched")
     folded_and_compare(cfg, inp, requests=[0, 31, 63])
+
+
+# ------------------------------------------------ streams and graph replay --
+
+def test_build_side_stream_and_graph_replay():
+    # The library launches on the stream it is given and keeps no state in its
+    # workspace from one call to the next: a build on a side stream, and every
+    # replay of a captured build, equal the eager build bit for bit, with an
+    # eager build on other logits (which rewrites the whole workspace) and
+    # host synchronizations between the replays.
+    cfg, inp = inputs("qwen3_4b_batched")
+    t = S.to_torch(inp, DEV)
+    other = dict(t)
+    other["base"] = t["base"].flip(-1).contiguous()  # other logits, same shape
+    bld = builder(cfg)
+
+    def build(src, out=None):
+        return bld.build(src["base"], src["emb"], src["w_ih"], src["w_hh"], src["b_ih"], src["b_hh"],
+                         src["C"], src["h0"], out=out)
+
+    ref = {k: v.clone() for k, v in build(t).items()}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = build(t)
+    side.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), f"side-stream build differs in {k}"
+    out = {k: torch.empty_like(v) for k, v in ref.items()}
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        build(t, out)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        build(t, out)
+    torch.cuda.synchronize()
+    differs = False
+    for i in range(3):
+        eager = build(other)  # rewrites the workspace between replays
+        torch.cuda.synchronize()
+        differs = differs or not torch.equal(eager["tokens"], ref["tokens"])
+        for k in out:
+            out[k].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {i}")
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), f"replay {i} differs in {k}"
+    assert differs, "the interleaved build on other logits should give other trees"
+    del g
+    bld.close()
