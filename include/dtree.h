@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
     DT_OK = 0,
     DT_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned buffer      */
-    DT_ERR_UNSUPPORTED = -2, /* valid request outside what this build supports */
+    DT_ERR_UNSUPPORTED = -2, /* valid request outside what the library supports */
     DT_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
     DT_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed      */
 } dt_status;
