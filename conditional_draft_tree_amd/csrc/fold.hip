@@ -75,11 +75,12 @@ __global__ __launch_bounds__(256) void fold_bf16_kernel(const bf16_t* __restrict
     }
 }
 
-// binary32 inputs (small configurations): one thread per (token, output).
+// binary32 inputs (small configurations): one thread per (token, output);
+// tokens along the grid's x dimension, whose extent is not limited to 16 bits.
 __global__ __launch_bounds__(64) void fold_f32_kernel(const float* __restrict__ emb, const float* __restrict__ W,
                                                       const float* __restrict__ bias, float* __restrict__ table,
                                                       int V, int E, int N) {
-    const int v = blockIdx.y, j = blockIdx.x * 64 + (int)threadIdx.x;
+    const int v = blockIdx.x, j = blockIdx.y * 64 + (int)threadIdx.x;
     if (j >= N) return;
     float s = bias ? bias[j] : 0.f;
     for (int k = 0; k < E; ++k) s = fmaf(W[(size_t)j * E + k], emb[(size_t)v * E + k], s);
@@ -96,7 +97,7 @@ hipError_t launch_fold(const void* emb, const void* W_ih, const void* b_ih, floa
         return launch_kernel(fold_bf16_kernel, dim3((V + 63) / 64, (N + 63) / 64), dim3(256), 0, stream,
                              LaunchEvents{}, (const bf16_t*)emb, (const bf16_t*)W_ih, (const bf16_t*)b_ih, table,
                              V, E, N);
-    return launch_kernel(fold_f32_kernel, dim3((N + 63) / 64, V), dim3(64), 0, stream, LaunchEvents{},
+    return launch_kernel(fold_f32_kernel, dim3(V, (N + 63) / 64), dim3(64), 0, stream, LaunchEvents{},
                          (const float*)emb, (const float*)W_ih, (const float*)b_ih, table, V, E, N);
 }
 

@@ -506,7 +506,8 @@ def test_build_head256_small(variant):
 
 # ---- folded input projection ---------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,V,E,H", [("bf16", 1003, 256, 96), ("bf16", 4096, 2560, 64), ("f32", 100, 32, 32)])
+@pytest.mark.parametrize("dtype,V,E,H", [("bf16", 1003, 256, 96), ("bf16", 4096, 2560, 64), ("f32", 100, 32, 32),
+                                         ("f32", 70001, 8, 4)])
 def test_fold_input_matches_float64(dtype, V, E, H):
     cfg = dict(B=1, V=V, L=2, E=E, H=H, M=4, n=2, dtype=dtype, alpha=1.1, T=0.0)
     inp = S.make_inputs(cfg, seed=V + E, skip=("base",))
