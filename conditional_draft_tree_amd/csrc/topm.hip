@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
     __shared__ int sidx[kWaves][kStash];
     __shared__ SharedThr s_thr;
     __shared__ float2 s_tail[kWaves];
-    const int row = blockIdx.y, s = blockIdx.x;
+    const int row = blockIdx.x, s = blockIdx.y;  // rows along x: B * L is not limited to 16 bits
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const T* rp = base + (size_t)row * (size_t)V;
     const int lo = s * seg;
@@ -537,7 +537,7 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
     int seg = (V + nseg - 1) / nseg;
     seg = (seg + per_vec - 1) / per_vec * per_vec;  // segments start on vector boundaries
     const bool vec = ((uintptr_t)base % 16 == 0) && ((size_t)V * esz % 16 == 0);
-    const dim3 grid(nseg, rows), block(kTopmThreads);
+    const dim3 grid(rows, nseg), block(kTopmThreads);
     float2* tp = reinterpret_cast<float2*>(tail_part);
     hipError_t e;
 #define DT_TOPM(Ty, kV, TL) \
