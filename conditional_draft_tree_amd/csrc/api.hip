@@ -491,16 +491,20 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     g.dtype = (int)c.dtype;
     g.wpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.wpack) : nullptr;
 
+    if (marginal) {  // no contraction between the steps: one launch runs all n
+        DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
+        DT_TRY(dt::launch_marginal_build(a, h->lds, st, ev), "factorized expansion launch");
+        DT_TRY(mark(h, call, 1, 'E', st), "timing event");
+        return DT_OK;
+    }
     DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
     DT_TRY(dt::launch_node_step(a, h->lds, 0, st, ev), "node step launch");
     for (int step = 1; step < c.n; ++step) {
-        if (!marginal) {
-            // the first contraction of the call leaves the weights in operand
-            // tiles; the later ones read that copy (contiguous 1 KB per wave load)
-            g.wmode = c.dtype == DT_BF16 ? (step == 1 ? 1 : 2) : 0;
-            DT_TRY(kernel_marks(h, call, 2, 'g', 'G', &ev), "timing event");
-            DT_TRY(dt::launch_gru_gates(g, st, ev), "GRU contraction launch");
-        }
+        // the first contraction of the call leaves the weights in operand
+        // tiles; the later ones read that copy (contiguous 1 KB per wave load)
+        g.wmode = c.dtype == DT_BF16 ? (step == 1 ? 1 : 2) : 0;
+        DT_TRY(kernel_marks(h, call, 2, 'g', 'G', &ev), "timing event");
+        DT_TRY(dt::launch_gru_gates(g, st, ev), "GRU contraction launch");
         DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
         DT_TRY(dt::launch_node_step(a, h->lds, step, st, ev), "node step launch");
     }

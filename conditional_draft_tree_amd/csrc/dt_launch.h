@@ -152,6 +152,9 @@ struct NodeLds {
 NodeLds node_lds_plan(int L, int M, int n, int H);
 hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream,
                             LaunchEvents ev = {});
+// The factorized mode (a.marginal) expanded in one launch: steps 0 .. n-1 of
+// every request, one workgroup per request looping over them.
+hipError_t launch_marginal_build(const NodeArgs& a, const NodeLds& lp, hipStream_t stream, LaunchEvents ev = {});
 
 // Conditional children distribution of one node per row (dt_correct).
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,

@@ -220,11 +220,13 @@ __device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M
     return on ? child_key(lp, tok) : 0ull;
 }
 
-// MARG: factorized (marginal) scoring: the children distribution of every node
-// is the log-softmax of the base logits over its M-slice (no GRU state, no
-// correction).
+// One expansion step of request blockIdx.x, run by node_threads<MARG>()
+// threads.  MARG: factorized (marginal) scoring: the children distribution of
+// every node is the log-softmax of the base logits over its M-slice (no GRU
+// state, no correction).  Waves with no further part in the step return early;
+// the step has no workgroup barrier after the first such return.
 template <typename T, int KS, bool MARG>
-__global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
+__device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds& lp, int step) {
     constexpr int NT = node_threads<MARG>();
     constexpr int NW = NT / kWave;
     constexpr int RW = kMaxM / NW;                    // gathered rows per wave
@@ -700,6 +702,24 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
     }
 }
 
+template <typename T, int KS, bool MARG>
+__global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArgs a, NodeLds lp, int step) {
+    node_step_body<T, KS, MARG>(a, lp, step);
+}
+
+// The factorized mode's whole expansion in one launch: without the batched
+// contraction nothing ties the requests together between steps, so each
+// workgroup runs its request's n steps back to back.  The state a step leaves
+// in the workspace is read by the next after a workgroup barrier (all waves of
+// a workgroup share one CU, whose vector memory path keeps the order).
+template <typename T>
+__global__ __launch_bounds__(node_threads<true>()) void marginal_build_kernel(NodeArgs a, NodeLds lp) {
+    for (int step = 0; step < a.n; ++step) {
+        node_step_body<T, 1, true>(a, lp, step);
+        __syncthreads();
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kCorrThreads) void correct_kernel(const int32_t* tidx, const float* tval,
                                                                const T* C, const float* h,
@@ -753,6 +773,14 @@ hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipS
     if (a.B == 0) return hipSuccess;
     return a.dtype == 1 ? launch_node_t<bf16_t>(a, lp, step, stream, ev)
                         : launch_node_t<float>(a, lp, step, stream, ev);
+}
+
+hipError_t launch_marginal_build(const NodeArgs& a, const NodeLds& lp, hipStream_t stream, LaunchEvents ev) {
+    if (a.B == 0) return hipSuccess;
+    const dim3 grid(a.B), block(node_threads<true>());
+    const unsigned shm = (unsigned)lp.bytes;
+    return a.dtype == 1 ? launch_kernel(marginal_build_kernel<bf16_t>, grid, block, shm, stream, ev, a, lp)
+                        : launch_kernel(marginal_build_kernel<float>, grid, block, shm, stream, ev, a, lp);
 }
 
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,
