@@ -220,13 +220,31 @@ __device__ __forceinline__ u64 child_keys_r(float val, float dot, int tok, int M
     return on ? child_key(lp, tok) : 0ull;
 }
 
+// What one step hands the next when a workgroup runs all of its request's
+// steps (the factorized mode): kept in LDS instead of going through the
+// workspace.  The top-M table, child lists, scores and parents stay in the
+// node LDS arrays from step to step.
+constexpr int kMaxL = 64;  // positions per request (dt_create's limit)
+struct StepLds {
+    u64 q[kWave];             // queue, one entry per lane
+    int32_t rs[kStateWords];  // state record: count, next token, queue size, flags, next depth, parent
+    int32_t nidx[kWave];  // the next step's candidate list
+    float nval[kWave];
+    float tail[kMaxL];    // the rows' tails (full-vocabulary mode)
+};
+
 // One expansion step of request blockIdx.x, run by node_threads<MARG>()
 // threads.  MARG: factorized (marginal) scoring: the children distribution of
 // every node is the log-softmax of the base logits over its M-slice (no GRU
-// state, no correction).  Waves with no further part in the step return early;
-// the step has no workgroup barrier after the first such return.
-template <typename T, int KS, bool MARG>
-__device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds& lp, int step) {
+// state, no correction).  PERSIST (with MARG, all steps in one workgroup):
+// the state of the previous step comes from `ps` and the LDS arrays instead of
+// the workspace (the workspace and outputs are still written).  Waves with no
+// further part in the step return early; the step has no workgroup barrier
+// after the first such return.
+template <typename T, int KS, bool MARG, bool PERSIST = false>
+__device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds& lp, int step,
+                                               StepLds* ps = nullptr) {
+    static_assert(!PERSIST || MARG, "only the factorized mode runs its steps in one workgroup");
     constexpr int NT = node_threads<MARG>();
     constexpr int NW = NT / kWave;
     constexpr int RW = kMaxM / NW;                    // gathered rows per wave
@@ -257,7 +275,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     // trip 2, issued as soon as the candidate tokens arrive: the gathered
     // rows of the correction matrix.  Every address is valid whatever the
     // state (tokens clamped to the vocabulary), so no load waits on a test.
-    const u64 q_m = a.queue[(size_t)b * kWave + lane];
+    const u64 q_m = PERSIST ? (step == 0 ? 0ull : ps->q[lane]) : a.queue[(size_t)b * kWave + lane];
     // slot `step`'s state: the GRU cell on the K-range partial sums of the
     // preceding contraction, added in K-range order (read at every step; the root
     // takes h0 instead)
@@ -283,13 +301,17 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     // list is waited for)
     __builtin_amdgcn_sched_barrier(0);
     // per-request state left by the previous step (one record)
-    const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
-    const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
+    const i32x4 rs0 = PERSIST ? *reinterpret_cast<const i32x4*>(ps->rs)
+                              : *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
+    const i32x4 rs1 = PERSIST ? *reinterpret_cast<const i32x4*>(ps->rs + 4)
+                              : *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
     const int rs_depth = rs1[0];
     // full-vocabulary mode: the tails of this request's rows (lane p holds
     // position p's), read from a valid address in either mode
     float tail_l = -INFINITY;
-    {
+    if (PERSIST) {
+        tail_l = a.tail ? ps->tail[min(lane, a.L - 1)] : -INFINITY;
+    } else {
         const float* tp = a.tail ? a.tail + (size_t)b * a.L : a.tval;
         const float v = tp[min(lane, a.L - 1)];
         tail_l = a.tail ? v : -INFINITY;
@@ -318,8 +340,9 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     const int32_t* ip = step == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
     const float* vp = step == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
     const int jl = min(lane, a.M - 1);
-    const int my_tok = min(max(ip[jl], 0), a.V - 1);  // candidate `lane` (all waves)
-    const float my_val = vp[jl];
+    const bool from_ps = PERSIST && step > 0;
+    const int my_tok = min(max(from_ps ? ps->nidx[jl] : ip[jl], 0), a.V - 1);  // candidate `lane` (all waves)
+    const float my_val = from_ps ? ps->nval[jl] : vp[jl];
     // the parent's state is loaded before the gathers: loads complete in
     // order, and the GRU cell must not wait for the gathers
     float hp = 0.f;
@@ -363,7 +386,9 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
         const int e = ((int)threadIdx.x + u * NT) * 4;
-        const bool te = tvec && e < LM, ke = e < nkid;
+        // (with PERSIST the table is staged at step 0 only and the child lists
+        // never: the steps write them into LDS themselves)
+        const bool te = tvec && e < LM && (!PERSIST || step == 0), ke = !PERSIST && e < nkid;
         r_ti[u] = te ? *reinterpret_cast<const i32x4*>(ti + e) : i32x4{0, 0, 0, 0};
         r_tv[u] = te ? *reinterpret_cast<const f32x4*>(tv + e) : f32x4{0.f, 0.f, 0.f, 0.f};
         r_ct[u] = ke ? *reinterpret_cast<const i32x4*>(kt + e) : i32x4{0, 0, 0, 0};
@@ -371,7 +396,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     }
     float r_sc = 0.f;
     int r_par = -1;
-    if ((int)threadIdx.x <= step && threadIdx.x > 0) {
+    if (!PERSIST && (int)threadIdx.x <= step && threadIdx.x > 0) {
         r_sc = a.scores[slot0 + threadIdx.x];
         r_par = a.parents[slot0 + threadIdx.x];
     }
@@ -442,22 +467,22 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
         const int e = ((int)threadIdx.x + u * NT) * 4;
-        if (tvec && e < LM) {
+        if (tvec && e < LM && (!PERSIST || step == 0)) {
             *reinterpret_cast<i32x4*>(s_tidx + e) = r_ti[u];
             *reinterpret_cast<f32x4*>(s_tval + e) = r_tv[u];
         }
-        if (e < nkid) {
+        if (!PERSIST && e < nkid) {
             *reinterpret_cast<i32x4*>(s_ctok + e) = r_ct[u];
             *reinterpret_cast<f32x4*>(s_clp + e) = r_cl[u];
         }
     }
-    if (!tvec) {
+    if (!tvec && (!PERSIST || step == 0)) {
         for (int e = threadIdx.x; e < LM; e += NT) {
             s_tidx[e] = ti[e];
             s_tval[e] = tv[e];
         }
     }
-    if ((int)threadIdx.x <= step) {
+    if (PERSIST ? threadIdx.x == 0 && step == 0 : (int)threadIdx.x <= step) {
         s_sc[threadIdx.x] = threadIdx.x == 0 ? 0.f : r_sc;
         s_par[threadIdx.x] = threadIdx.x == 0 ? -1 : r_par;
     }
@@ -544,6 +569,10 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
             if (lane < a.M) {
                 a.child_tok[crow + lane] = child_tok_of(kids);
                 a.child_lp[crow + lane] = child_lp_of(kids);
+                if (PERSIST) {  // row `step` of the LDS child lists (wave 0 reads rows < step)
+                    s_ctok[step * kMaxM + lane] = child_tok_of(kids);
+                    s_clp[step * kMaxM + lane] = child_lp_of(kids);
+                }
             }
         }
         return;
@@ -662,11 +691,19 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
             a.scores[slot0 + v] = psc;
             a.gru_tok[b] = next_tok;
             a.gru_par[b] = v_par;
+            if (PERSIST) {  // slot v's score and parent for the later steps
+                s_sc[v] = psc;
+                s_par[v] = v_par;
+            }
         }
         if (next_tok >= 0) {  // the next step expands v: hand over its candidates
             const int jm = min(lane, a.M - 1);
             a.nidx[(size_t)b * kWave + lane] = s_tidx[pd * a.M + jm];
             a.nval[(size_t)b * kWave + lane] = s_tval[pd * a.M + jm];
+            if (PERSIST) {
+                ps->nidx[lane] = s_tidx[pd * a.M + jm];
+                ps->nval[lane] = s_tval[pd * a.M + jm];
+            }
         }
     } else if (lane == 0) {
         a.gru_tok[b] = -1;
@@ -679,6 +716,13 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
         *reinterpret_cast<i32x4*>(rs + 4) = i32x4{next_depth, v_par < 0 ? 0 : v_par, 0, 0};
         a.count[b] = new_cnt;
         a.flags[b] = flag;
+    }
+    if (PERSIST) {  // read by every wave at the start of the next step
+        ps->q[lane] = q;
+        if (lane == 0) {
+            *reinterpret_cast<i32x4*>(ps->rs) = i32x4{new_cnt, next_tok, qs, (int)flag};
+            *reinterpret_cast<i32x4*>(ps->rs + 4) = i32x4{next_depth, v_par < 0 ? 0 : v_par, 0, 0};
+        }
     }
 
     // ---- 5. ancestor-only mask after the last step
@@ -709,13 +753,16 @@ __global__ __launch_bounds__(node_threads<MARG>()) void node_step_kernel(NodeArg
 
 // The factorized mode's whole expansion in one launch: without the batched
 // contraction nothing ties the requests together between steps, so each
-// workgroup runs its request's n steps back to back.  The state a step leaves
-// in the workspace is read by the next after a workgroup barrier (all waves of
-// a workgroup share one CU, whose vector memory path keeps the order).
+// workgroup runs its request's n steps back to back, handing the queue, state
+// record and candidate list from step to step in LDS (and keeping the table,
+// child lists, scores and parents there), a workgroup barrier between steps.
 template <typename T>
 __global__ __launch_bounds__(node_threads<true>()) void marginal_build_kernel(NodeArgs a, NodeLds lp) {
+    __shared__ StepLds ps;
+    if (a.tail && (int)threadIdx.x < a.L) ps.tail[threadIdx.x] = a.tail[(size_t)blockIdx.x * a.L + threadIdx.x];
+    __syncthreads();
     for (int step = 0; step < a.n; ++step) {
-        node_step_body<T, 1, true>(a, lp, step);
+        node_step_body<T, 1, true, true>(a, lp, step, &ps);
         __syncthreads();
     }
 }
