@@ -305,7 +305,8 @@ def main():
             "mean_launch_ms": round(gemm_each, 5),
         },
         "stages_ms_mean": {k: round(float(np.mean(v)), 5) for k, v in st.items() if v},
-        "topm_merge_ms_mean": round(float(np.mean(merge_ms)), 5),
+        # (null: each row is one segment, so no merge kernel runs)
+        "topm_merge_ms_mean": round(float(np.mean(merge_ms)), 5) if merge_ms else None,
         "call_ms_events_mean": round(float(np.mean(call_ms)), 5),
         "latency_per_request_us": round(ms_per_step * 1e3, 1),
         "marginal_mode": {"us_per_round": round(marg_us, 1),

@@ -442,7 +442,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     DT_TRY(dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg, (u64*)(w + L.partial), c.M,
                            tidx, tval, st, ev, tail_scale(c), tail, (float*)(w + L.tail_part)),
            "top-M launch");
-    DT_TRY(mark(h, call, 1, 'M', st), "timing event");
+    if (h->nseg > 1) DT_TRY(mark(h, call, 1, 'M', st), "timing event");  // after the merge kernel
 
     dt::NodeArgs a{};
     a.B = c.B; a.L = c.L; a.V = c.V; a.E = c.E; a.H = c.H; a.M = c.M; a.n = c.n;

@@ -275,7 +275,8 @@ dt_status dt_accept_greedy(dt_handle *h, const int32_t *tokens, const int32_t *p
  * dt_timing_read(h, stage, ms, max, n_out) returns per-call durations in
  * milliseconds, oldest first:
  *   stage 0  top-M select kernel (one launch per call)
- *   stage 1  top-M merge kernel, with the gap before it (0 with one segment)
+ *   stage 1  top-M merge kernel, with the gap before it (no entries when
+ *            each row is one segment and no merge kernel runs)
  *   stage 2  GRU gate contractions of the call, summed   (level 2)
  *   stage 3  node (correction + queue) kernels, summed    (level 2)
  *   stage 4  the whole call
