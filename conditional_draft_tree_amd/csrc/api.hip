@@ -21,7 +21,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 thread_local char g_create_error[512] = "";
 
 struct Layout {
-    size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, queue, nidx, nval,
+    size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, ckey, queue, nidx, nval,
         rstate, xpack, hpack, hprev, tail, tail_part, wpack;
     size_t total;
 };
@@ -97,6 +97,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {  // ksplit: the l
     l.gru_par = take(B * 4);
     l.child_tok = take(B * S * 64 * 4);
     l.child_lp = take(B * S * 64 * 4);
+    l.ckey = take(B * S * 64 * sizeof(u64));
     l.queue = take(B * 64 * sizeof(u64));
     l.rstate = take(B * dt::kStateWords * 4);
     l.nidx = take(B * 64 * 4);
@@ -463,6 +464,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     a.gru_par = (int32_t*)(w + L.gru_par);
     a.child_tok = (int32_t*)(w + L.child_tok);
     a.child_lp = (float*)(w + L.child_lp);
+    a.ckey = (u64*)(w + L.ckey);
     a.queue = (u64*)(w + L.queue);
     a.rstate = (int32_t*)(w + L.rstate);
     a.nidx = (int32_t*)(w + L.nidx);

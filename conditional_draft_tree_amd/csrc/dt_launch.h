@@ -124,6 +124,7 @@ struct NodeArgs {
     int32_t* gru_par;    // [B] its parent slot (whose state is advanced)
     int32_t* child_tok;  // [B, n+1, 64] sorted children per slot
     float* child_lp;     // [B, n+1, 64]
+    u64* ckey;           // [B, n+1, 64] unsorted child keys, sorted by the next step
     u64* queue;          // [B, 64] candidate keys, 0 = empty
     int32_t* rstate;     // [B, kStateWords] per-request state left for the next step:
                          // count, next GRU token, queue size, flags, depth of the next slot

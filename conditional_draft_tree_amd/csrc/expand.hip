@@ -276,6 +276,11 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     // rows of the correction matrix.  Every address is valid whatever the
     // state (tokens clamped to the vocabulary), so no load waits on a test.
     const u64 q_m = PERSIST ? (step == 0 ? 0ull : ps->q[lane]) : a.queue[(size_t)b * kWave + lane];
+    // the child keys of slot step - 1, left unsorted by the step that expanded
+    // it (sorted below by wave 1; loaded by every wave, from a valid address).
+    // The factorized mode, with no gathers to hide a sort behind, sorts a
+    // slot's children in the step that expands it, beside the queue update.
+    const u64 prev_keys = MARG ? 0ull : a.ckey[(slot0 + (step > 0 ? step - 1 : 0)) * kMaxM + lane];
     // slot `step`'s state: the GRU cell on the K-range partial sums of the
     // preceding contraction, added in K-range order (read at every step; the root
     // takes h0 instead)
@@ -488,6 +493,21 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     }
     __syncthreads();
 
+    // Slot step - 1's children sorted by (log-prob desc, token asc), for the
+    // sibling pushes from this step on (no earlier step needs them): wave 1
+    // sorts them while the gathers are in flight, into the workspace and into
+    // the LDS row that the staging above filled with stale data.
+    if (!MARG && wave == 1 && step > 0) {
+        const u64 kids = wave_sort_desc(prev_keys);
+        const int r = step - 1;
+        if (lane < a.M) {
+            a.child_tok[(slot0 + r) * kMaxM + lane] = child_tok_of(kids);
+            a.child_lp[(slot0 + r) * kMaxM + lane] = child_lp_of(kids);
+            s_ctok[r * kMaxM + lane] = child_tok_of(kids);
+            s_clp[r * kMaxM + lane] = child_lp_of(kids);
+        }
+    }
+
     // ---- 3. correction dots of slot `step`'s children (block position = its
     // depth): this wave's RW rows, then a transposed reduction across lanes
     if constexpr (!MARG) {
@@ -517,11 +537,13 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     }
     __syncthreads();
     // ---- 3. queue.  Wave 0 first takes the pop decision, which needs only the
-    // best child of slot `step` (the largest child key), then hands the
-    // popped node to the other waves: wave 1 sorts the children, the rest
-    // pack the next contraction's activations, while wave 0 updates the queue.
+    // best child of slot `step` (the largest child key; the children are
+    // sorted by the next step, or by wave 1 after the decision in the
+    // factorized mode), then hands the popped node to the packing waves,
+    // which pack the next contraction's activations while wave 0 updates the
+    // queue.
     __shared__ int s_dec[2];  // next GRU token (-1 = idle row), parent slot of the popped node
-    __shared__ u64 s_keys[kWave];  // child keys of slot `step`, unsorted
+    __shared__ u64 s_keys[kWave];  // (factorized mode) child keys of slot `step`, unsorted
     const float score_step = s_sc[step];
     u64 ckey = 0ull, best = 0ull, top = 0ull;
     int new_cnt = cnt;
@@ -534,7 +556,8 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
             const float tz = __int_as_float(
                 __builtin_amdgcn_readlane(__float_as_int(tail_l), min(depth, a.L - 1)));
             ckey = child_keys_r(my_val, MARG ? 0.f : zs[lane], my_tok, a.M, a.temp, tz);
-            s_keys[lane] = ckey;
+            if (MARG) s_keys[lane] = ckey;  // sorted by wave 1 after the decision
+            else if (step + 1 < a.n) a.ckey[(slot0 + step) * kMaxM + lane] = ckey;  // sorted by the next step
             best = wave_max_u64(ckey);  // the rank-0 child
             const u64 key = queue_key(score_step + child_lp_of(best), depth + 1, step, 0);
             if (lane == qs) q = key;
@@ -561,9 +584,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     __syncthreads();
 
     if (wave == 1) {
-        // slot `step`'s children sorted by (log-prob desc, token asc), kept
-        // for the sibling pushes of later steps
-        if (expand) {
+        if (MARG && expand) {  // slot `step`'s children, sorted for the later steps
             const u64 kids = wave_sort_desc(s_keys[lane]);
             const size_t crow = (slot0 + step) * kMaxM;
             if (lane < a.M) {
@@ -575,7 +596,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
                 }
             }
         }
-        return;
+        return;  // (otherwise its sort came before the dots)
     }
     if (wave != 0) {
         // ---- 4. row b's activations of the next contraction, packed for its
