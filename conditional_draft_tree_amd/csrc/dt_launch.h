@@ -151,6 +151,7 @@ struct NodeLds {
     size_t bytes;
 };
 NodeLds node_lds_plan(int L, int M, int n, int H);
+// One expansion step of the standard or folded path (not the factorized mode).
 hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipStream_t stream,
                             LaunchEvents ev = {});
 // The factorized mode (a.marginal) expanded in one launch: steps 0 .. n-1 of

@@ -824,9 +824,7 @@ hipError_t launch_node_t(const NodeArgs& a, const NodeLds& lp, int step, hipStre
                          LaunchEvents ev) {
     const dim3 grid(a.B), block(node_threads<false>());
     const unsigned shm = (unsigned)lp.bytes;
-    if (a.marginal)
-        return launch_kernel(node_step_kernel<T, 1, true>, grid, dim3(node_threads<true>()), shm, stream, ev, a,
-                             lp, step);
+    if (a.marginal) return hipErrorInvalidValue;  // the factorized mode runs marginal_build_kernel
     switch (a.ksplit) {
 #define DT_KS(K) \
     case K: return launch_kernel(node_step_kernel<T, K, false>, grid, block, shm, stream, ev, a, lp, step);
