@@ -260,9 +260,34 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # ---- achievable HBM bandwidth on this machine: a plain device-to-device copy
+    # (bytes read + bytes written per second), the select's second reference
+    ca = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    cb = torch.empty_like(ca)
+    for _ in range(3):
+        cb.copy_(ca)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        cb.copy_(ca)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * ca.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del ca, cb
+
     # correctness guard on the timed output: valid trees
     cnt = out["count"].cpu().numpy()
     assert (cnt >= 1).all() and (cnt <= n).all()
+
+    # ---- the gathers of the node step: per launch, M rows of C and one
+    # embedding row per request; per round also the lower bound that reads
+    # each (request, depth) slice of C once (slots 0 .. min(count, n-1) are
+    # expanded, slot k from the slice of position depth(k))
+    node_each = float(np.mean(st["node_total"])) / n if st["node_total"] else float("nan")
+    gather_bytes = B * (M * H + E) * esz
+    dep = out["depths"].cpu().numpy()
+    uniq = sum(len(set(dep[b, :min(int(cnt[b]), n - 1) + 1].tolist())) for b in range(B))
+    gather_gbs = gather_bytes / (node_each * 1e-3) / 1e9
 
     res = {
         "metric": "tree builds/sec and us/round at B, n=16, M=64; % HBM peak (topM) and % MFMA (GRU)",
@@ -292,6 +317,22 @@ def main():
             "algorithmic_bytes_per_launch": topm_bytes,
             "mean_launch_ms": round(sel_mean, 5),
             "launches": len(sel_ms),
+            "achievable_copy_gbs": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved_gbs / copy_gbs, 4),
+        },
+        "roofline_gather": {
+            "kernel": "node_step_kernel (the gathers of one expansion step)",
+            "bound": "hbm",
+            "limited_by": "latency: a dependent round trip for the candidate tokens, then 64 random "
+                          "2 KiB rows per request",
+            "achieved": round(gather_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gather_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": gather_bytes,
+            "mean_launch_ms": round(node_each, 5),
+            "round_bytes": gather_bytes * n,
+            "round_bytes_unique_slices": uniq * M * H * esz + B * (n - 1) * E * esz,
         },
         "roofline_gru": {
             "kernel": "gru_gemm_bf16_kernel (one expansion step)",
