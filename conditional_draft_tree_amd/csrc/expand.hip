@@ -491,7 +491,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
         s_sc[threadIdx.x] = threadIdx.x == 0 ? 0.f : r_sc;
         s_par[threadIdx.x] = threadIdx.x == 0 ? -1 : r_par;
     }
-    __syncthreads();
+    if (!(PERSIST && step > 0)) __syncthreads();  // (later persistent steps stage nothing)
 
     // Slot step - 1's children sorted by (log-prob desc, token asc), for the
     // sibling pushes from this step on (no earlier step needs them): wave 1
@@ -535,7 +535,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
             if ((lane & 15) == 0) zs[wave * RW + (lane >> 4)] = d;
         }
     }
-    __syncthreads();
+    if constexpr (!MARG) __syncthreads();  // (the factorized mode has no dots to share)
     // ---- 3. queue.  Wave 0 first takes the pop decision, which needs only the
     // best child of slot `step` (the largest child key; the children are
     // sorted by the next step, or by wave 1 after the decision in the
