@@ -201,6 +201,16 @@ def test_build_bf16_ragged(variant):
                       **(STRONG if variant == "strong" else {}))
 
 
+@pytest.mark.parametrize("dtype,H,E,variant", [("bf16", 2048, 64, "strong"), ("bf16", 4096, 96, "default"),
+                                               ("f32", 1100, 36, "strong")])
+def test_build_wide_state(dtype, H, E, variant):
+    # states wider than the node step's 1024 threads (several passes of the GRU
+    # cell) and than one 1024-element gather chunk (several gather rounds)
+    cfg = dict(B=3, V=5003, L=4, E=E, H=H, M=16, n=8, dtype=dtype, alpha=1.5, T=0.0)
+    inp = S.make_inputs(cfg, seed=7, variant=variant)
+    build_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
+
+
 def test_build_qwen3_4b_single():
     cfg, inp = inputs("qwen3_4b_single")
     build_and_compare(cfg, inp)
@@ -555,6 +565,13 @@ def test_folded_bf16_ragged(variant):
     cfg = dict(B=70, V=5003, L=16, E=256, H=128, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0)
     inp = S.make_inputs(cfg, seed=12, variant=variant)
     folded_and_compare(cfg, inp, requests=range(0, 70, 7), **(STRONG if variant == "strong" else {}))
+
+
+def test_folded_wide_state():
+    # the folded table rows and the recurrent contraction for a state wider
+    # than the node step's 1024 threads
+    cfg = dict(B=3, V=5003, L=4, E=64, H=2048, M=16, n=8, dtype="bf16", alpha=1.5, T=0.0)
+    folded_and_compare(cfg, S.make_inputs(cfg, seed=8, variant="strong"), **STRONG)
 
 
 def test_folded_qwen3_4b_batched_sampled():
