@@ -149,11 +149,12 @@ def test_gru_step_matches_oracle(dtype, B, E, H):
 
 # -------------------------------------------------------- children scores --
 
-@pytest.mark.parametrize("dtype,T", [("bf16", 0.0), ("bf16", 1.0), ("f32", 0.5)])
-def test_correct_matches_oracle(dtype, T):
-    cfg = dict(B=16, V=3000, L=4, E=32, H=256 if dtype == "bf16" else 64, M=64, n=4, dtype=dtype,
-               alpha=1.1, T=T)
-    inp = S.make_inputs(cfg, seed=7, variant="strong")
+@pytest.mark.parametrize("dtype,T,H,M,variant", [("bf16", 0.0, 256, 64, "strong"), ("bf16", 1.0, 256, 64, "strong"),
+                                                 ("f32", 0.5, 64, 64, "strong"), ("bf16", 0.5, 4096, 17, "default")])
+def test_correct_matches_oracle(dtype, T, H, M, variant):
+    # (H = 4096: the widest state, several row passes; M = 17: a partial wave of candidates)
+    cfg = dict(B=16, V=3000, L=4, E=32, H=H, M=M, n=4, dtype=dtype, alpha=1.1, T=T)
+    inp = S.make_inputs(cfg, seed=7, variant=variant)
     rng = np.random.default_rng(2)
     h = rng.normal(0, 0.5, (cfg["B"], cfg["H"])).astype(np.float32)
     pos = rng.integers(0, cfg["L"], cfg["B"]).astype(np.int32)
