@@ -630,3 +630,21 @@ def test_build_side_stream_and_graph_replay():
     assert differs, "the interleaved build on other logits should give other trees"
     del g
     bld.close()
+
+
+# ------------------------------------------------------- the position limit --
+
+@pytest.mark.parametrize("mode", ["standard", "marginal", "full_vocab"])
+def test_build_max_positions(mode):
+    # L = 64 positions (the limit): depths up to n in the queue keys, the whole
+    # L x M table staged per step, every row's tail (full-vocabulary mode);
+    # very peaked logits (Zipf alpha = 6) grow chains n nodes deep
+    cfg = dict(B=5, V=4099, L=64, E=64, H=96, M=32, n=32, dtype="bf16", alpha=6.0, T=0.0,
+               full_vocab=mode == "full_vocab")
+    inp = S.make_inputs(cfg, seed=11)
+    if mode == "marginal":
+        got = marginal_and_compare(cfg, inp, requests=range(cfg["B"]))
+    else:
+        got, _, _ = build_and_compare(cfg, inp)
+    say(f"  deepest node: {int(got['depths'].max())}")
+    assert got["depths"].max() >= 24
