@@ -46,6 +46,12 @@ def make(**kw):
     return dtree.dt_create(**cfg)
 
 
+def test_create_accepts_the_limits():
+    # the largest shapes each limit allows (L = 64, M = 64 or n = 64, H = 4096)
+    for kw in (dict(L=64, M=32, n=32, V=1000), dict(M=64, n=64, V=1000), dict(H=4096), dict(L=64, V=1000)):
+        dtree.dt_destroy(make(**kw))
+
+
 def test_create_valid_and_workspace():
     h = make()
     assert dtree.dt_workspace_bytes(h) > 0
@@ -61,6 +67,8 @@ def test_create_valid_and_workspace():
     (dict(M=65, V=1000), "UNSUPPORTED"), (dict(n=65), "UNSUPPORTED"), (dict(L=65), "UNSUPPORTED"),
     (dict(E=48), "UNSUPPORTED"), (dict(H=24), "UNSUPPORTED"), (dict(H=48), "UNSUPPORTED"), (dict(H=8192), "UNSUPPORTED"),
     (dict(dtype=dtree.DT_F32, E=6), "UNSUPPORTED"),
+    # per-request state beyond 64 KiB of LDS: the L x M table and n x 64 child lists
+    (dict(L=64, M=64, n=64, V=1000), "UNSUPPORTED"),
 ])
 def test_create_rejects(kw, code):
     with pytest.raises(ValueError, match=code):
