@@ -71,7 +71,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(requests shard across GPUs with no exchange; see the design notes)",
+              "(the requests are independent: G GPUs would each take B/G of them, with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
