@@ -44,8 +44,7 @@
  *      expérimentaux -- Absence de perte": the output equals serial greedy
  *      decoding).
  *
- * Readings of points the pages leave open (each is also listed in the
- * design notes):
+ * Readings of points the pages leave open:
  *   - nodes at depth d take their tokens from block position d-1, so the
  *     maximum depth equals the block length L;
  *   - the GRU is the textbook cell with gate order (reset, update, new) and
