@@ -520,10 +520,12 @@ __global__ __launch_bounds__(kWave) void topm_merge_kernel(const u64* __restrict
 }  // namespace
 
 int topm_segments(int rows, int V) {
-    // >= ~1024 workgroups (4 per CU), segments of >= 16384 elements; fewer,
+    // >= ~512 workgroups (2 per CU), segments of >= 16384 elements; fewer,
     // longer segments admit fewer keys (a running top-64 of N elements admits
-    // about 64 ln(N / 64) of them per segment)
-    int want = (1024 + rows - 1) / max(rows, 1);
+    // about 64 ln(N / 64) of them per segment) and need no merge (measured on
+    // 151936-wide bf16 rows: at 512 rows one segment per row beats two, at
+    // 128 rows four beat eight)
+    int want = (512 + rows - 1) / max(rows, 1);
     int cap = max(1, V / 16384);
     return max(1, min(want, cap));
 }
