@@ -260,6 +260,31 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # ---- one request alone (extra key): request 0 of the same inputs built by
+    # a B = 1 handle; the pages quote their per-round build time for one request
+    # at n = 16, M = 64 (other hardware: context, not a target)
+    single = None
+    if args.config == "qwen3_4b_batched":
+        sb = dtree.Builder(1, L, V, E, H, M, n, cfg["T"], cfg["dtype"], 1e-5, device=dev)
+        s_base = t["base"][0:1].contiguous()
+        s_h0 = t["h0"][0:1].contiguous() if t["h0"] is not None else None
+        sstep = lambda o=None: sb.build(s_base, t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"],
+                                        s_h0, out=o)
+        sout = sstep()
+        for _ in range(3):
+            sstep(sout)
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for _ in range(max(args.stage_steps, 1)):
+            sstep(sout)
+        torch.cuda.synchronize()
+        s_us = (time.perf_counter() - s0) * 1e6 / max(args.stage_steps, 1)
+        same = bool((sout["tokens"][0] == out["tokens"][0]).all() and (sout["parents"][0] == out["parents"][0]).all())
+        sb.close()
+        single = {"workload": "qwen3_4b_single: request 0 of the inputs above, B = 1",
+                  "us_per_round": round(s_us, 1), "tree_equal_to_batched_request": same,
+                  "pages_per_round_ms_other_hardware": {"python_builder": 3.67, "cuda_graph_builder": 2.31}}
+
     # ---- achievable HBM bandwidth on this machine: a plain device-to-device copy
     # (bytes read + bytes written per second), the select's second reference
     ca = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
@@ -359,6 +384,7 @@ def main():
                             "trees_same_shape_as_top_m_softmax": round(same_shape, 4)},
         "head256_mode": h256,
         "folded_input_mode": folded,
+        "single_request": single,
         "acceptance_walk": {"kernel_us": round(acc_us, 2), "requests": B,
                             "mean_tokens_per_round_synthetic_targets": round(tau, 3),
                             "target_follow_probability": 0.8},
