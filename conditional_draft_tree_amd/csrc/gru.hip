@@ -30,7 +30,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowBlocks = 4;  // 4 x 16 rows per workgroup
+constexpr int kRowBlocks = 4;  // up to 4 x 16 rows per workgroup
+// 16-row blocks a workgroup covers: fewer when the batch is small, so that
+// no activation loads are spent on rows past B
+inline int row_blocks(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : kRowBlocks; }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -43,8 +46,10 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 constexpr int kWaves8 = 8;
 constexpr int kMaxXChunks = 6;  // x chunks per wave and batch
 constexpr int kMaxHChunks = 2;  // h chunks per wave and batch
-constexpr int kXChunkLoads = 3 + kRowBlocks;      // 16-byte loads per lane of an x chunk
-constexpr int kHChunkLoads = 3 + 3 * kRowBlocks;  // of an h chunk (three activation parts)
+// 16-byte loads per lane of an x chunk, and of an h chunk (three activation
+// parts), with rb row blocks
+constexpr int x_chunk_loads(int rb) { return 3 + rb; }
+constexpr int h_chunk_loads(int rb) { return 3 + 3 * rb; }
 
 // Work split.  K is cut into 32-wide chunks: nE chunks of the x part then
 // nH of the h part (three bf16 parts each, so three times the MFMAs and the
@@ -55,15 +60,15 @@ constexpr int kHChunkLoads = 3 + 3 * kRowBlocks;  // of an h chunk (three activa
 // the larger per-wave load of the two kinds.  A wave issues every load of
 // its chunks (weights and activations) before its first MFMA: one memory
 // round trip.
-inline int x_waves(int nE, int nH, int ksplit) {
+inline int x_waves(int nE, int nH, int ksplit, int rb) {
     if (nH == 0) return kWaves8;
     if (nE == 0) return 0;
     int best = 1;
     long long best_cost = -1;
     for (int wx = 1; wx < kWaves8; ++wx) {
         const int nx = ksplit * wx, nh = ksplit * (kWaves8 - wx);
-        const long long cost = max((long long)((nE + nx - 1) / nx) * kXChunkLoads,
-                                   (long long)((nH + nh - 1) / nh) * kHChunkLoads);
+        const long long cost = max((long long)((nE + nx - 1) / nx) * x_chunk_loads(rb),
+                                   (long long)((nH + nh - 1) / nh) * h_chunk_loads(rb));
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best = wx;
@@ -87,11 +92,12 @@ __device__ __forceinline__ void wave_chunks(int nE, int nH, int ksplit, int wx, 
 
 // WM: weight source (0: W_ih / W_hh; 1: those, and write the packed copy; 2:
 // the packed copy), a template parameter so that each variant keeps one
-// address path and no dead store code.
-template <int WM>
+// address path and no dead store code.  RB: 16-row blocks per workgroup.
+template <int WM, int RB>
 __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesArgs a) {
-    // every wave's sums of the workgroup's 64 x 16 outputs x 4 gates: 128 KB
-    __shared__ f32x4 red[kWaves8][kRowBlocks * 4][kWave];
+    // every wave's sums of the workgroup's (RB x 16) x 16 outputs x 4 gates
+    // (128 KB at RB = 4)
+    __shared__ f32x4 red[kWaves8][RB * 4][kWave];
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const int ut = blockIdx.x, rg = blockIdx.y, ks = blockIdx.z;
     const int unit = ut * 16 + (lane & 15);
@@ -118,10 +124,10 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
     // packed activations: lane l reads row l % 16 of its row block at K offset
     // 8 * (l / 16) of a chunk; a wave's read is one contiguous 1 KB block.
     // Rows past B read the last row (their sums are not stored).
-    const bf16_t* xblk[kRowBlocks];
-    const bf16_t* hblk[kRowBlocks];
+    const bf16_t* xblk[RB];
+    const bf16_t* hblk[RB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const int r = min(rg * 64 + rb * 16 + (lane & 15), a.B - 1);
         xblk[rb] = (const bf16_t*)a.xpack + pack_index_x(r, 0, a.E) + kq;
         hblk[rb] = (const bf16_t*)a.hpack + pack_index_h(r, 0, 0, a.H) + kq;
@@ -129,9 +135,9 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
     const size_t xstep = 16 * 32;                  // one chunk of one block
     const size_t hpart = (size_t)nH * 16 * 32;     // one part of one block
 
-    f32x4 acc[kRowBlocks][4];
+    f32x4 acc[RB][4];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
         // x part: batches of up to kMaxXChunks chunks, all loads of a batch at once
         for (int cb = cbeg; cb < cend; cb += kMaxXChunks) {
             const int n = min(kMaxXChunks, cend - cb);
-            bf16x8 w[kMaxXChunks][3], x[kMaxXChunks][kRowBlocks];
+            bf16x8 w[kMaxXChunks][3], x[kMaxXChunks][RB];
 #pragma unroll
             for (int i = 0; i < kMaxXChunks; ++i) {
                 const size_t c = (size_t)(cb + min(i, n - 1));  // clamped: always in bounds
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                     w[i][g] = i < n ? v : zero;
                 }
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
+                for (int rb = 0; rb < RB; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
             }
             // MFMAs for every chunk slot, unconditionally, and no scheduling
             // across this point: loads sunk next to their MFMAs would wait
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
 #pragma unroll
             for (int i = 0; i < kMaxXChunks; ++i) {
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) {
+                for (int rb = 0; rb < RB; ++rb) {
                     acc[rb][0] = mfma(x[i][rb], w[i][0], acc[rb][0]);
                     acc[rb][1] = mfma(x[i][rb], w[i][1], acc[rb][1]);
                     acc[rb][2] = mfma(x[i][rb], w[i][2], acc[rb][2]);
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
         // h part (three exact bf16 parts per state element)
         for (int cb = cbeg; cb < cend; cb += kMaxHChunks) {
             const int n = min(kMaxHChunks, cend - cb);
-            bf16x8 w[kMaxHChunks][3], hp[kMaxHChunks][kRowBlocks][3];
+            bf16x8 w[kMaxHChunks][3], hp[kMaxHChunks][RB][3];
 #pragma unroll
             for (int i = 0; i < kMaxHChunks; ++i) {
                 const size_t c = (size_t)(cb + min(i, n - 1) - nE);
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
                     w[i][g] = i < n ? v : zero;
                 }
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int q = 0; q < 3; ++q)
                         hp[i][rb][q] = load_bf16x8(hblk[rb] + q * hpart + c * xstep);
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
 #pragma unroll
             for (int i = 0; i < kMaxHChunks; ++i) {
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
                         acc[rb][0] = mfma(hp[i][rb][q], w[i][0], acc[rb][0]);
@@ -220,13 +226,14 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
     // the 8 waves' sums added in wave order (one LDS round trip); all 512
     // threads write the workgroup's partial sums
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) red[wave][rb * 4 + g][lane] = acc[rb][g];
     __syncthreads();
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-        const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (rb, g, lane) of 4 x 4 x 64
+        const int idx = (int)threadIdx.x + h2 * kWaves8 * kWave;  // (rb, g, lane) of RB x 4 x 64
+        if (idx >= RB * 4 * kWave) break;
         const int sl = idx >> 6, ln = idx & 63;
         f32x4 sum = red[0][sl][ln];
 #pragma unroll
@@ -306,11 +313,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* partial, int
 int gru_ksplit(int B, int E, int H, int dtype) {
     if (dtype != 1) return 1;
     // ~one workgroup per CU, and a single load batch per wave where possible
-    const int nE = E / 32, nH = H / 32;
+    const int nE = E / 32, nH = H / 32, rb = row_blocks(B);
     const int tiles = (H / 16) * ((B + 63) / 64);
     int best = kMaxKsplit;
     for (int ks = 1; ks <= kMaxKsplit; ++ks) {
-        const int wx = x_waves(nE, nH, ks), nx = ks * wx, nh = ks * (kWaves8 - wx);
+        const int wx = x_waves(nE, nH, ks, rb), nx = ks * wx, nh = ks * (kWaves8 - wx);
         const int xmax = nE ? (nE + nx - 1) / nx : 0, hmax = nH ? (nH + nh - 1) / nh : 0;
         if (xmax <= kMaxXChunks && hmax <= kMaxHChunks && tiles * ks >= 192) return ks;
         if (xmax <= kMaxXChunks && hmax <= kMaxHChunks) best = min(best, ks);
@@ -322,11 +329,16 @@ hipError_t launch_gru_gates(const GruGatesArgs& a, hipStream_t stream, LaunchEve
     if (a.B == 0) return hipSuccess;
     if (a.dtype == 1) {
         GruGatesArgs b = a;
-        b.xwaves = x_waves(a.E / 32, a.H / 32, a.ksplit);
+        const int rb = row_blocks(a.B);
+        b.xwaves = x_waves(a.E / 32, a.H / 32, a.ksplit, rb);
         const dim3 grid(a.H / 16, (a.B + 63) / 64, a.ksplit), block(kWaves8 * kWave);
-        if (a.wpack && a.wmode == 2) return launch_kernel(gru_gates_bf16_kernel<2>, grid, block, 0, stream, ev, b);
-        if (a.wpack && a.wmode == 1) return launch_kernel(gru_gates_bf16_kernel<1>, grid, block, 0, stream, ev, b);
-        return launch_kernel(gru_gates_bf16_kernel<0>, grid, block, 0, stream, ev, b);
+        const int wm = a.wpack ? (a.wmode == 2 ? 2 : a.wmode == 1 ? 1 : 0) : 0;
+#define DT_GATES(WM, RB) \
+    if (wm == WM && rb == RB) return launch_kernel(gru_gates_bf16_kernel<WM, RB>, grid, block, 0, stream, ev, b);
+        DT_GATES(2, 4) DT_GATES(1, 4) DT_GATES(0, 4) DT_GATES(2, 2) DT_GATES(1, 2) DT_GATES(0, 2)
+        DT_GATES(2, 1) DT_GATES(1, 1) DT_GATES(0, 1)
+#undef DT_GATES
+        return hipErrorInvalidValue;
     }
     return launch_kernel(gru_gates_f32_kernel, dim3((a.H + 63) / 64, a.B, 1), dim3(64), 0, stream, ev, a);
 }
