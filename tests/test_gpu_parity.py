@@ -126,7 +126,10 @@ def test_topm_full_batch_sampled_rows():
 # --------------------------------------------------------------- GRU step --
 
 @pytest.mark.parametrize("dtype,B,E,H", [("f32", 3, 32, 32), ("bf16", 64, 2560, 1024),
-                                         ("bf16", 70, 64, 96), ("bf16", 5, 4096, 1024), ("bf16", 3, 64, 4096)])
+                                         ("bf16", 70, 64, 96), ("bf16", 5, 4096, 1024), ("bf16", 3, 64, 4096),
+                                         # the contraction's row blocks follow B: 1 up to 16 rows, 2 up to 32
+                                         ("bf16", 16, 64, 96), ("bf16", 17, 64, 96), ("bf16", 20, 2560, 1024),
+                                         ("bf16", 33, 64, 96)])
 def test_gru_step_matches_oracle(dtype, B, E, H):
     cfg = dict(B=B, V=97, L=2, E=E, H=H, M=4, n=2, dtype=dtype, alpha=1.1, T=0.0)
     inp = S.make_inputs(cfg, seed=B + E, variant="strong")
