@@ -205,6 +205,16 @@ def test_build_bf16_ragged(variant):
                       **(STRONG if variant == "strong" else {}))
 
 
+@pytest.mark.parametrize("B", [16, 17, 32, 33])
+def test_build_bf16_row_blocks(B):
+    # whole builds at the contraction's row-block boundaries: one 16-row block
+    # per workgroup up to 16 rows, two up to 32, four above (ragged tails at
+    # 17 and 33)
+    cfg = dict(B=B, V=5003, L=16, E=256, H=128, M=64, n=16, dtype="bf16", alpha=1.5, T=0.0)
+    inp = S.make_inputs(cfg, seed=11, variant="strong")
+    build_and_compare(cfg, inp, requests=range(B), **STRONG)
+
+
 @pytest.mark.parametrize("dtype,H,E,variant", [("bf16", 2048, 64, "strong"), ("bf16", 4096, 96, "default"),
                                                ("f32", 1100, 36, "strong")])
 def test_build_wide_state(dtype, H, E, variant):
