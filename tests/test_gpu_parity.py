@@ -81,6 +81,8 @@ def build_and_compare(cfg, inp, requests=None, threads=8, eps=1e-5, tol=SCORE_TO
     ("f32", 1000, 8, 8, 1), ("bf16", 1000, 8, 8, 2), ("f32", 37, 37, 3, 2),
     ("bf16", 5003, 64, 4, 3), ("bf16", 64, 64, 2, 1), ("f32", 131, 1, 5, 4),
     ("bf16", 151936, 64, 16, 2),
+    # few rows of a long vocabulary: 64 segments per row (bf16), 36 (f32), one merge each
+    ("bf16", 1 << 20, 64, 1, 1), ("f32", 600000, 17, 2, 1),
 ])
 def test_topm_bit_exact(dtype, V, M, L, B):
     cfg = dict(B=B, V=V, L=L, E=32, H=32, M=M, n=4, dtype=dtype, alpha=1.1, T=0.0)
