@@ -56,7 +56,7 @@ def _load():
             lib.oracle_build_request.argtypes = (
                 [C.c_int] * 6 + [C.c_double, C.c_int, C.c_double] + [vp] * 8 +
                 [i32p, i32p, i32p, f64p, C.POINTER(C.c_uint8), i32p, C.POINTER(C.c_uint32),
-                 f64p, i32p, f64p, C.c_int, f64p])
+                 f64p, i32p, f64p, C.c_int, f64p, i32p])
             lib.oracle_score_paths.argtypes = (
                 [C.c_int] * 5 + [C.c_double, C.c_int] + [vp] * 8 + [C.c_int, i32p, i32p, f64p, C.c_int])
             lib.oracle_accept_greedy.argtypes = [C.c_int, C.c_int, i32p, i32p, i32p, i32p, i32p,
@@ -153,7 +153,7 @@ def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float 
                mask=np.empty((S, S), np.uint8), count=np.zeros(1, np.int32),
                flags=np.zeros(1, np.uint32), min_gap=np.zeros(1, np.float64),
                topm_idx=np.empty((L, M), np.int32), topm_val=np.empty((L, M), np.float64),
-               tail=np.empty(L, np.float64))
+               tail=np.empty(L, np.float64), first_flag=np.zeros(1, np.int32))
     h0 = inp.get("h0")
     h0b = None if h0 is None else np.ascontiguousarray(h0[b], np.float32)
     rc = _load().oracle_build_request(
@@ -165,11 +165,14 @@ def build_request(inp: dict, b: int, M: int, n: int, T: float = 0.0, eps: float 
         _ptr(out["mask"], C.c_uint8), _ptr(out["count"], C.c_int32),
         _ptr(out["flags"], C.c_uint32), _ptr(out["min_gap"], C.c_double),
         _ptr(out["topm_idx"], C.c_int32), _ptr(out["topm_val"], C.c_double), int(bool(full_vocab)),
-        _ptr(out["tail"], C.c_double))
+        _ptr(out["tail"], C.c_double), _ptr(out["first_flag"], C.c_int32))
     _check(rc, "oracle_build_request")
     out["count"] = int(out["count"][0])
     out["flags"] = int(out["flags"][0])
     out["min_gap"] = float(out["min_gap"][0])
+    # slot of the first pop decided by a margin below eps (0: none); slots
+    # before it were decided by margins of at least eps
+    out["first_flag"] = int(out["first_flag"][0])
     return out
 
 

@@ -363,6 +363,9 @@ static qent_t q_pop(queue_t *q)
  *   count (non-root nodes built), flags (bit 0: a near tie below eps),
  *   min_gap (smallest gap between a popped candidate and one left in the
  *   queue, structural exact ties excluded; +inf if the queue was always empty),
+ *   first_flag (optional, may be NULL): the slot created by the first pop
+ *   whose gap to a candidate left in the queue was below eps (0 when no pop
+ *   was), so slots 1 .. first_flag-1 were decided by margins of at least eps,
  *   topm_idx/topm_val [L,M] (optional, may be NULL);
  *   full_vocab  0: children normalized over the M-slice; 1: over the whole
  *               vocabulary (corrected top-M plus the uncorrected tail);
@@ -374,7 +377,8 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
                          const void *b_ih, const void *b_hh, const void *C, const float *h0,
                          int32_t *tokens, int32_t *parents, int32_t *depths, double *scores,
                          uint8_t *mask, int32_t *count, uint32_t *flags, double *min_gap,
-                         int32_t *topm_idx, double *topm_val, int full_vocab, double *tail_out)
+                         int32_t *topm_idx, double *topm_val, int full_vocab, double *tail_out,
+                         int32_t *first_flag)
 {
     if (V < 1 || L < 1 || E < 1 || H < 1 || M < 1 || M > V || n < 1 || T < 0.0 ||
         (dtype != OR_F32 && dtype != OR_BF16) || !base || !emb || !W_ih || !W_hh || !C ||
@@ -416,6 +420,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
     memset(mask, 0, (size_t)S * S);
     *flags = 0;
     *min_gap = INFINITY;
+    int first = 0;
 
     /* root: slot 0, depth 0, score 0, hidden state h0; its children sit at
      * depth 1 and take their tokens from block position 0 */
@@ -449,6 +454,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
             if (gap >= *min_gap) continue;
             if (gap == 0.0 && same_terms(plp, plen, clp, L, M, &c, &q.e[i], wa, wb)) continue;
             *min_gap = gap;
+            if (!first && gap < eps) first = v;
         }
         /* expand: GRU step with the realized token, then score its children
          * at block position depth(v).  Nodes at the maximum depth have no
@@ -466,6 +472,7 @@ int oracle_build_request(int V, int L, int E, int H, int M, int n, double T, int
     }
     *count = built;
     if (*min_gap < eps) *flags |= 1u;
+    if (first_flag) *first_flag = first;
 
     /* 5. ancestor-only mask: row i attends to itself and its ancestors */
     for (int i = 0; i <= built; ++i)

@@ -399,8 +399,10 @@ def test_near_tie_gap_is_reported():
     res = oracle.build_request(inp, 0, 3, 2, 0.0, eps=1e-5)
     assert res["flags"] & 1
     assert 0 < res["min_gap"] < 1e-5
+    # the first pop (slot 1) leaves its sibling 1e-7 below it in the queue
+    assert res["first_flag"] == 1
     res = oracle.build_request(inp, 0, 3, 2, 0.0, eps=1e-8)
-    assert res["flags"] == 0
+    assert res["flags"] == 0 and res["first_flag"] == 0
 
 
 def test_near_tie_behind_an_exact_structural_tie_is_found():
@@ -415,6 +417,8 @@ def test_near_tie_behind_an_exact_structural_tie_is_found():
     np.testing.assert_array_equal(res["tokens"], [-1, 0, 0])
     np.testing.assert_array_equal(res["depths"], [0, 1, 2])
     assert res["flags"] & 1 and 5e-7 < res["min_gap"] < 2e-6
+    # the first pop's gaps are 0.3 nats and more; the second pop is the near tie
+    assert res["first_flag"] == 2
 
 
 # ---- greedy acceptance walk -------------------------------------------------
