@@ -114,6 +114,15 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {  // ksplit: the l
 
 bool misaligned(const void* p) { return p && ((uintptr_t)p % 16) != 0; }
 
+// An error that earlier asynchronous HIP work left on this host thread (a
+// failed launch, an error reported since) is returned, and cleared, before
+// anything is enqueued, so that it is not blamed on a later call that
+// succeeds.  Called after argument validation, which makes no HIP call.
+dt_status pending_error(dt_handle* h) {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DT_OK : hip_fail(h, e, "HIP error pending from earlier asynchronous work");
+}
+
 dt_status check_ws(dt_handle* h, void* ws, size_t bytes) {
     if (h->lay.total == 0) return DT_OK;
     if (!ws) return fail(h, DT_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", h->lay.total);
@@ -163,7 +172,9 @@ hipError_t kernel_marks(dt_handle* h, std::vector<Marker>* call, int need, char 
 extern "C" {
 
 const char* dt_status_string(dt_status s) {
-    switch (s) {
+    int32_t v;  // any int from a C caller: read it as one (see dt_create)
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case DT_OK: return "ok";
         case DT_ERR_INVALID_ARG: return "invalid argument";
         case DT_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -179,9 +190,14 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     if (!out) return fail(nullptr, DT_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (!cfg) return fail(nullptr, DT_ERR_INVALID_ARG, "cfg is NULL");
+    // the dtype field arrives from C callers as any int: read it as one, since
+    // a value outside the enumerators is not a valid dt_dtype in C++
+    static_assert(sizeof(dt_dtype) == sizeof(int32_t), "dt_dtype is stored as a 32-bit int");
+    int32_t dtype_raw;
+    memcpy(&dtype_raw, &cfg->dtype, sizeof dtype_raw);
+    if (dtype_raw != (int32_t)DT_F32 && dtype_raw != (int32_t)DT_BF16)
+        return fail(nullptr, DT_ERR_INVALID_ARG, "dtype %d is neither DT_F32 nor DT_BF16", (int)dtype_raw);
     const dt_config c = *cfg;
-    if (c.dtype != DT_F32 && c.dtype != DT_BF16)
-        return fail(nullptr, DT_ERR_INVALID_ARG, "dtype %d is neither DT_F32 nor DT_BF16", (int)c.dtype);
     if (c.B < 0 || c.L < 1 || c.V < 1 || c.E < 1 || c.H < 1 || c.M < 1 || c.n < 1)
         return fail(nullptr, DT_ERR_INVALID_ARG,
                     "sizes must be positive (B >= 0): B=%d L=%d V=%d E=%d H=%d M=%d n=%d", c.B, c.L,
@@ -291,7 +307,7 @@ dt_status dt_topm(dt_handle* h, void* ws, size_t ws_bytes, const void* base, int
     if (misaligned(base) || misaligned(idx) || misaligned(val))
         return fail(h, DT_ERR_INVALID_ARG, "dt_topm: buffers must be 16-byte aligned");
     dt_status s = check_ws(h, ws, ws_bytes);
-    if (s) return s;
+    if (s || (s = pending_error(h))) return s;
     hipError_t e = dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg,
                                    (u64*)((char*)ws + h->lay.partial), c.M, idx, val,
                                    (hipStream_t)stream);
@@ -307,7 +323,7 @@ dt_status dt_topm_tail(dt_handle* h, void* ws, size_t ws_bytes, const void* base
     if (misaligned(base) || misaligned(idx) || misaligned(val))
         return fail(h, DT_ERR_INVALID_ARG, "dt_topm_tail: buffers must be 16-byte aligned");
     dt_status s = check_ws(h, ws, ws_bytes);
-    if (s) return s;
+    if (s || (s = pending_error(h))) return s;
     hipError_t e = dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg,
                                    (u64*)((char*)ws + h->lay.partial), c.M, idx, val, (hipStream_t)stream,
                                    dt::LaunchEvents{}, tail_scale(c), tail,
@@ -328,7 +344,7 @@ dt_status dt_gru_step(dt_handle* h, void* ws, size_t ws_bytes, const void* x, co
     if ((const void*)h_out == (const void*)h_in)
         return fail(h, DT_ERR_INVALID_ARG, "dt_gru_step: h_out must not alias h");
     dt_status s = check_ws(h, ws, ws_bytes);
-    if (s) return s;
+    if (s || (s = pending_error(h))) return s;
     hipStream_t st = (hipStream_t)stream;
     char* w = (char*)ws;
     dt::GruGatesArgs g{};
@@ -367,6 +383,7 @@ dt_status dt_correct(dt_handle* h, const int32_t* idx, const float* val, const v
         return fail(h, DT_ERR_INVALID_ARG, "dt_correct: null pointer");
     if (misaligned(C) || misaligned(h_in))
         return fail(h, DT_ERR_INVALID_ARG, "dt_correct: C and h must be 16-byte aligned");
+    if (dt_status s = pending_error(h)) return s;
     hipError_t e = dt::launch_correct(idx, val, C, h_in, pos, tok_sorted, logp_sorted, c.B, c.L, c.H,
                                       c.M, (int)c.dtype, c.temperature, (hipStream_t)stream);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_correct launch");
@@ -380,6 +397,7 @@ dt_status dt_accept_greedy(dt_handle* h, const int32_t* tokens, const int32_t* p
     if (c.B == 0) return DT_OK;
     if (!tokens || !parents || !count || !target || !path || !accepted || !bonus)
         return fail(h, DT_ERR_INVALID_ARG, "dt_accept_greedy: null pointer");
+    if (dt_status s = pending_error(h)) return s;
     std::vector<Marker>* call = nullptr;
     if (h->tlevel > 0 && (int)h->calls.size() < h->tcapacity) {
         h->calls.emplace_back();
@@ -418,7 +436,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         misaligned(h0) || misaligned(b_ih) || misaligned(b_hh))
         return fail(h, DT_ERR_INVALID_ARG, "dt_build: matrices must be 16-byte aligned");
     dt_status s = check_ws(h, ws, ws_bytes);
-    if (s) return s;
+    if (s || (s = pending_error(h))) return s;
     hipStream_t st = (hipStream_t)stream;
     char* w = (char*)ws;
     const Layout& L = h->lay;
@@ -542,6 +560,7 @@ dt_status dt_fold_input(dt_handle* h, const void* emb, const void* W_ih, const v
     if (!emb || !W_ih || !table) return fail(h, DT_ERR_INVALID_ARG, "dt_fold_input: null pointer");
     if (misaligned(emb) || misaligned(W_ih) || misaligned(b_ih) || misaligned(table))
         return fail(h, DT_ERR_INVALID_ARG, "dt_fold_input: buffers must be 16-byte aligned");
+    if (dt_status s = pending_error(h)) return s;
     hipError_t e = dt::launch_fold(emb, W_ih, b_ih, table, c.V, c.E, c.H, (int)c.dtype, (hipStream_t)stream);
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "dt_fold_input launch");
 }
