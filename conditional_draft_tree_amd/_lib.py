@@ -259,16 +259,8 @@ class Builder:
         self._chk("b_hh", b_hh, (3 * H,), optional=True)
         self._chk("C", Cmat, (V, H))
         self._chk("h0", h0, (B, H), dtype=torch.float32, optional=True)
-        S = n + 1
         if out is None:
-            dev = self.device
-            out = dict(tokens=torch.empty((B, S), dtype=torch.int32, device=dev),
-                       parents=torch.empty((B, S), dtype=torch.int32, device=dev),
-                       depths=torch.empty((B, S), dtype=torch.int32, device=dev),
-                       scores=torch.empty((B, S), dtype=torch.float32, device=dev),
-                       mask=torch.empty((B, S, S), dtype=torch.uint8, device=dev),
-                       count=torch.empty((B,), dtype=torch.int32, device=dev),
-                       flags=torch.empty((B,), dtype=torch.int32, device=dev))
+            out = self._outputs()
         dt_build(self.handle, self.workspace, base, emb, w_ih, w_hh, b_ih, b_hh, Cmat, h0,
                  out["tokens"], out["parents"], out["depths"], out["scores"], out["mask"],
                  out["count"], out["flags"], stream)
@@ -284,7 +276,7 @@ class Builder:
                     scores=torch.empty((B, S), dtype=torch.float32, device=dev),
                     mask=torch.empty((B, S, S), dtype=torch.uint8, device=dev),
                     count=torch.empty((B,), dtype=torch.int32, device=dev),
-                    flags=torch.empty((B,), dtype=torch.int32, device=dev))
+                    flags=torch.empty((B,), dtype=torch.uint32, device=dev))  # uint32 [B], as declared
 
     def fold_input(self, emb, w_ih, b_ih=None, stream=None):
         """The folded input projection table [V, 3H] float32 (b_ih + W_ih . emb[v])."""

@@ -80,8 +80,10 @@ template <> struct Elem<bf16_t> {
     // An upper bound on the element maximum within |value| / 128 of it, in 8
     // operations instead of 12: a 32-bit word read as binary32 is its high
     // bf16 element plus part of the low one's bits, i.e. the high element
-    // moved away from zero by less than 2^-7 of its magnitude.  Vectors are
-    // therefore compared with a threshold lowered by |threshold| / 64, which
+    // moved away from zero by less than 2^-7 of its magnitude, or, when the
+    // high element is a zero or a denormal, by less than 2^-133 (a -0.0 high
+    // element then reads as a negative denormal).  Vectors are therefore
+    // compared with a threshold lowered by |threshold| / 64 + FLT_MIN, which
     // never rejects an element at or above the threshold.
     static constexpr float kSlack = 1.f / 64.f;
     __device__ static float vfilter(const u32x4& v) {
@@ -101,7 +103,7 @@ struct WaveTop {
     u64 list;
     u64 thr;
     float thr_val;  // value part of thr (-inf while thr == 0)
-    float filt;     // vector filter bound: thr_val lowered by slack * |thr_val|, >= -FLT_MAX
+    float filt;     // vector filter bound: thr_val lowered by slack * |thr_val| (bf16: and FLT_MIN), >= -FLT_MAX
     float slack;
     int nbuf;
 };
@@ -154,8 +156,9 @@ __device__ __forceinline__ void set_thr(WaveTop& w, u64 t) {
     if (t > w.thr) {
         w.thr = t;
         w.thr_val = topm_key_val(t);
-        // finite, so that masked vectors (-inf) never pass
-        w.filt = fmaxf(w.slack > 0.f ? w.thr_val - fabsf(w.thr_val) * w.slack : w.thr_val, -FLT_MAX);
+        // finite, so that masked vectors (-inf) never pass; the bf16 slack
+        // also covers zero and denormal high elements (FLT_MIN)
+        w.filt = fmaxf(w.slack > 0.f ? w.thr_val - fabsf(w.thr_val) * w.slack - FLT_MIN : w.thr_val, -FLT_MAX);
     }
 }
 

@@ -20,8 +20,12 @@
  *    enqueue work; none of them synchronizes.
  *  - Argument errors return DT_ERR_INVALID_ARG / DT_ERR_UNSUPPORTED /
  *    DT_ERR_WORKSPACE before anything is enqueued; dt_last_error() then holds
- *    a message.  A failed launch returns DT_ERR_HIP.  Faults inside the
- *    kernels surface as HIP errors at the caller's next synchronization.
+ *    a message.  A failed launch returns DT_ERR_HIP.  An error that earlier
+ *    asynchronous HIP work left pending on the calling host thread (what
+ *    hipGetLastError reports) is returned as DT_ERR_HIP, and cleared, by the
+ *    next enqueueing call after its argument checks, before it enqueues
+ *    anything.  Faults inside the kernels surface as HIP errors at the
+ *    caller's next synchronization.
  *  - A handle is not thread-safe: one host thread at a time.  Overlapping
  *    calls that share a workspace race; give concurrent calls their own
  *    workspace.
@@ -132,7 +136,13 @@ const char *dt_last_error(const dt_handle *h);
  *                       is smaller than n)
  *   flags   [B] uint32  bit 0: some pop beat a candidate left in the queue by
  *                       a positive binary32 margin below near_tie_eps (exact
- *                       ties are broken by the queue order, not flagged)
+ *                       ties are broken by the queue order, not flagged).
+ *                       The popped node's next-ranked sibling is queued
+ *                       before the comparison, so two children closer than
+ *                       eps are such a pop, and the last pop's comparison
+ *                       covers the final node set: every decision whose
+ *                       outcome rounding could change sets this one bit.
+ *                       Other bits are 0.
  * workspace: device buffer of at least dt_workspace_bytes(h) bytes.
  */
 dt_status dt_build(dt_handle *h, void *workspace, size_t ws_bytes, const void *base_logits,
