@@ -43,6 +43,9 @@ def check_valid_tree(got: dict, b: int, n: int, L: int):
         assert dep[v] == dep[q] + 1 and 1 <= dep[v] <= L
         assert sc[v] <= sc[q]
         assert tok[v] >= 0
+    # every node is a distinct token path: no two slots share (parent, token)
+    pairs = set(zip(par[1:cnt + 1].tolist(), tok[1:cnt + 1].tolist()))
+    assert len(pairs) == cnt, f"request {b}: two slots share a (parent, token) pair"
     assert np.all(np.diff(sc[1:cnt + 1]) <= 0), "pop order must be by non-increasing score"
     assert np.all(tok[cnt + 1:] == -1) and np.all(par[cnt + 1:] == -1)
     assert np.all(dep[cnt + 1:] == -1) and np.all(np.isneginf(sc[cnt + 1:]))
@@ -63,9 +66,10 @@ def paths_of(got: dict, b: int):
 
 
 def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg: dict,
-                    eps: float = 1e-5, tol: float = SCORE_TOL) -> str:
+                    eps: float = 1e-5, tol: float = SCORE_TOL):
     """Compare request b_got of a GPU result with the oracle's tree `ref` of
-    request b_inp of `inp`.  Returns "exact" or "flagged"."""
+    request b_inp of `inp`.  Returns ("exact" or "flagged", the largest
+    |GPU score - oracle score| over the request's nodes)."""
     n, L = cfg["n"], cfg["L"]
     check_valid_tree(got, b_got, n, L)
     assert int(got["count"][b_got]) == ref["count"]
@@ -78,16 +82,23 @@ def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg
     if ref["flags"] == 0:
         for k in ("tokens", "parents", "depths", "mask"):
             np.testing.assert_array_equal(got[k][b_got], ref[k], err_msg=k)
-        err = np.abs(got["scores"][b_got][:cnt + 1] - ref["scores"][:cnt + 1]).max()
+        err = float(np.abs(got["scores"][b_got][:cnt + 1] - ref["scores"][:cnt + 1]).max())
         assert err <= tol, f"score error {err}"
-        return "exact"
-    # A decision was closer than eps: several trees are correct.  What is
-    # unique is the multiset of the best scores; every GPU node must carry its
-    # own conditional score.
+        return "exact", err
+    # A decision was closer than eps: several trees are correct.  The pops
+    # before the first such decision were decided by margins of at least eps,
+    # so those slots are unique; so is the multiset of the best scores, and
+    # every GPU node must carry its own conditional score.
+    k0 = ref["first_flag"]
+    assert 1 <= k0 <= cnt, k0
+    for k in ("tokens", "parents", "depths"):
+        np.testing.assert_array_equal(got[k][b_got][:k0], ref[k][:k0],
+                                      err_msg=f"{k} before the first near tie (slot {k0})")
     gs = got["scores"][b_got][1:cnt + 1].astype(np.float64)
     rs = oracle.score_paths(inp, b_inp, cfg["M"], paths_of(got, b_got), cfg["T"],
                             full_vocab=cfg.get("full_vocab", False))
     assert np.all(np.isfinite(rs)), "GPU node outside the top-M candidate tree"
-    assert np.abs(gs - rs).max() <= tol
+    err = float(np.abs(gs - rs).max())
+    assert err <= tol, f"score error {err}"
     assert np.abs(np.sort(gs) - np.sort(ref["scores"][1:cnt + 1])).max() <= tol
-    return "flagged"
+    return "flagged", err
