@@ -55,6 +55,38 @@ def topm_traffic():
     return int(m.group(1)) if h.hexdigest() == m.group(2) else None
 
 
+def gru_counters():
+    """(MFMA MOPs, MFMA busy SIMD-cycles) per benchmarked contraction launch from
+    the committed counter summary, or None when the contraction's sources have
+    changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", "gru_contraction_qwen3_4b_batched_mfma.md")).read()
+    except OSError:
+        return None
+    m = re.search(r"gru_mfma_mops_bf16=(\d+) gru_mfma_busy_cycles=(\d+) source_sha256=([0-9a-f]{64})", text)
+    if not m:
+        return None
+    h = hashlib.sha256()
+    for f in ("gru.hip", "dt_device.h", "dt_launch.h"):
+        with open(os.path.join(ROOT, "conditional_draft_tree_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return (int(m.group(1)), int(m.group(2))) if h.hexdigest() == m.group(3) else None
+
+
+def gru_counter_figures(mean_ms):
+    c = gru_counters()
+    if c is None or not mean_ms == mean_ms:
+        return None
+    mops, busy = c
+    issued = 512.0 * mops / (mean_ms * 1e-3) / 1e12
+    return {"mfma_mops_bf16_per_launch": mops, "issued_tflops": round(issued, 1),
+            "issued_frac_of_peak": round(issued / MFMA_BF16_PEAK_TFS, 4),
+            "mfma_busy_frac": round(busy / (mean_ms * 1e-3 * 2.4e9 * 1024), 4),
+            "source": "profiles/gru_contraction_qwen3_4b_batched_mfma.md"}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -427,6 +459,10 @@ def main():
             "hbm_frac_weights": round(gemm_weight_bytes / (gemm_each * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "flop_per_launch": gemm_flop,
             "mean_launch_ms": round(gemm_each, 5),
+            # from the committed rocprofv3 counters of the same launch shape:
+            # MFMA ops actually issued (512 flops per MOP) and MFMA busy cycles
+            # over the launch (1024 SIMDs at 2.4 GHz), at this run's mean time
+            "counters": gru_counter_figures(gemm_each) if args.config == "qwen3_4b_batched" else None,
         },
         "stages_ms_mean": {k: round(float(np.mean(v)), 5) for k, v in st.items() if v},
         # (null: each row is one segment, so no merge kernel runs)

@@ -41,3 +41,24 @@ def test_every_summary_names_its_command():
     for name in os.listdir(PROF):
         text = read(name)
         assert "rocprofv3" in text and "bench.py" in text, name
+
+
+def test_contraction_mfma_counters_match_the_kernel_structure():
+    # SQ_INSTS_VALU_MFMA_MOPS_BF16 of the benchmarked contraction (64 unit
+    # tiles x 4 K ranges, 8 waves: 4 on x chunks in one batch of 6 slots for
+    # 5 chunks, 4 on h chunks, 2 each, the state as 3 bf16 parts), 4 row
+    # blocks, 3 gates; one 16x16x32 MFMA is 16384 flops = 32 MOPs of 512
+    text = read("gru_contraction_qwen3_4b_batched_mfma.md")
+    m = re.search(r"gru_mfma_mops_bf16=(\d+) gru_mfma_busy_cycles=(\d+) source_sha256=[0-9a-f]{64}", text)
+    assert m
+    mops, busy = int(m.group(1)), int(m.group(2))
+    tiles, ks, rb, gates = 64, 4, 4, 3
+    x_mfma = tiles * ks * 4 * 6 * gates * rb
+    h_mfma = tiles * ks * 4 * 2 * 3 * gates * rb
+    assert mops == (x_mfma + h_mfma) * 32
+    # 16 busy cycles per MFMA on each of the SIMDs that issue it
+    assert busy == (x_mfma + h_mfma) * 16
+    shown = re.search(r"(\d+) MOPs = ([0-9.]+) GFLOP issued per launch, against ([0-9.]+) GFLOP algorithmic", text)
+    assert int(shown.group(1)) == mops
+    assert abs(float(shown.group(2)) - 512 * mops / 1e9) < 1e-3
+    assert abs(float(shown.group(3)) - 2 * 64 * 3 * 1024 * (2560 + 1024) / 1e9) < 1e-3
