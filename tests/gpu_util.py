@@ -69,7 +69,8 @@ def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg
                     eps: float = 1e-5, tol: float = SCORE_TOL):
     """Compare request b_got of a GPU result with the oracle's tree `ref` of
     request b_inp of `inp`.  Returns ("exact" or "flagged", the largest
-    |GPU score - oracle score| over the request's nodes)."""
+    |GPU score - oracle score| over the request's nodes, and that largest
+    error per node depth as a dict)."""
     n, L = cfg["n"], cfg["L"]
     check_valid_tree(got, b_got, n, L)
     assert int(got["count"][b_got]) == ref["count"]
@@ -82,9 +83,10 @@ def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg
     if ref["flags"] == 0:
         for k in ("tokens", "parents", "depths", "mask"):
             np.testing.assert_array_equal(got[k][b_got], ref[k], err_msg=k)
-        err = float(np.abs(got["scores"][b_got][:cnt + 1] - ref["scores"][:cnt + 1]).max())
+        e = np.abs(got["scores"][b_got][:cnt + 1] - ref["scores"][:cnt + 1])
+        err = float(e.max())
         assert err <= tol, f"score error {err}"
-        return "exact", err
+        return "exact", err, by_depth(e[1:], ref["depths"][1:cnt + 1])
     # A decision was closer than eps: several trees are correct.  The pops
     # before the first such decision were decided by margins of at least eps,
     # so those slots are unique; so is the multiset of the best scores, and
@@ -98,7 +100,15 @@ def compare_request(got: dict, b_got: int, ref: dict, inp: dict, b_inp: int, cfg
     rs = oracle.score_paths(inp, b_inp, cfg["M"], paths_of(got, b_got), cfg["T"],
                             full_vocab=cfg.get("full_vocab", False))
     assert np.all(np.isfinite(rs)), "GPU node outside the top-M candidate tree"
-    err = float(np.abs(gs - rs).max())
+    e = np.abs(gs - rs)
+    err = float(e.max())
     assert err <= tol, f"score error {err}"
     assert np.abs(np.sort(gs) - np.sort(ref["scores"][1:cnt + 1])).max() <= tol
-    return "flagged", err
+    return "flagged", err, by_depth(e, got["depths"][b_got][1:cnt + 1])
+
+
+def by_depth(err, depths) -> dict:
+    out = {}
+    for e, d in zip(err.tolist(), depths.tolist()):
+        out[int(d)] = max(out.get(int(d), 0.0), float(e))
+    return out
