@@ -8,6 +8,7 @@ entry points raises.
 """
 from ._lib import (  # noqa: F401
     DT_BF16, DT_F32, Builder, DtreeError, dt_accept_greedy, dt_build, dt_build_folded, dt_build_marginal,
+    dt_build_noalloc,
     dt_correct, dt_fold_input,
     dt_create, dt_destroy,
     dt_gru_step, dt_last_error, dt_status_string, dt_timing_enable, dt_timing_read, dt_topm, dt_topm_tail,

@@ -56,6 +56,9 @@ def load_library():
         # tokens, parents, depths, scores, mask, count, flags, stream
         lib.dt_build.argtypes = [H, vp, C.c_size_t] + [vp] * 7 + [f32p] + [i32p] * 3 + [
             f32p, vp, i32p, vp, vp]
+        # handle, base, emb, W_ih, W_hh, b_ih, b_hh, C, h0, tokens, parents, depths, scores, mask,
+        # count, flags, stream
+        lib.dt_build_noalloc.argtypes = [H] + [vp] * 7 + [f32p] + [i32p] * 3 + [f32p, vp, i32p, vp, vp]
         # handle, workspace, bytes, base, tokens, parents, depths, scores, mask, count, flags, stream
         lib.dt_build_marginal.argtypes = [H, vp, C.c_size_t, vp] + [i32p] * 3 + [f32p, vp, i32p, vp, vp]
         lib.dt_topm.argtypes = [H, vp, C.c_size_t, vp, i32p, f32p, vp]
@@ -71,7 +74,7 @@ def load_library():
         lib.dt_timing_enable.argtypes = [H, C.c_int, C.c_int]
         lib.dt_timing_read.argtypes = [H, C.c_int, C.POINTER(C.c_float), C.c_int,
                                        C.POINTER(C.c_int)]
-        for f in (lib.dt_create, lib.dt_build, lib.dt_build_marginal, lib.dt_topm, lib.dt_topm_tail,
+        for f in (lib.dt_create, lib.dt_build, lib.dt_build_noalloc, lib.dt_build_marginal, lib.dt_topm, lib.dt_topm_tail,
                   lib.dt_gru_step,
                   lib.dt_correct, lib.dt_accept_greedy, lib.dt_fold_input, lib.dt_build_folded,
                   lib.dt_timing_enable, lib.dt_timing_read):
@@ -134,6 +137,14 @@ def dt_build(handle, workspace, base, emb, w_ih, w_hh, b_ih, b_hh, Cmat, h0, tok
                         _p(base), _p(emb), _p(w_ih), _p(w_hh), _p(b_ih), _p(b_hh), _p(Cmat), _p(h0),
                         _p(tokens), _p(parents), _p(depths), _p(scores), _p(mask), _p(count),
                         _p(flags), _stream(stream)), handle)
+
+
+def dt_build_noalloc(handle, base, emb, w_ih, w_hh, b_ih, b_hh, Cmat, h0, tokens, parents, depths, scores, mask,
+                     count, flags, stream=None):
+    lib = load_library()
+    _check(lib.dt_build_noalloc(handle, _p(base), _p(emb), _p(w_ih), _p(w_hh), _p(b_ih), _p(b_hh), _p(Cmat),
+                                _p(h0), _p(tokens), _p(parents), _p(depths), _p(scores), _p(mask), _p(count),
+                                _p(flags), _stream(stream)), handle)
 
 
 def dt_fold_input(handle, emb, w_ih, b_ih, table, stream=None):

@@ -5,11 +5,17 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/dtree.h"
 #include "dt_launch.h"
+
+// dt_build_noalloc's scratch (see scratch_on below): file scope, one copy per
+// device, held until the process ends.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -44,6 +50,7 @@ struct dt_handle {
     int ksplit_f;  // of its recurrent part alone (folded input projection)
     dt::NodeLds lds;
     Layout lay;
+    Layout lay_na;  // dt_build_noalloc's use of the static scratch (no weight-tile copy)
     std::string err;
     // timing
     int tlevel = 0;
@@ -78,7 +85,8 @@ float tail_scale(const dt_config& c) {
     return 1.4426950408889634f / (c.temperature > 0.f ? c.temperature : 1.f);
 }
 
-Layout plan_layout(const dt_config& c, int nseg, int ksplit) {  // ksplit: the larger of the two
+// ksplit: the larger of the two; wtiles: room for the weights in operand tiles
+Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true) {
     Layout l{};
     const size_t B = c.B, L = c.L, M = c.M, S = (size_t)c.n + 1, H = c.H;
     size_t off = 0;
@@ -107,7 +115,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit) {  // ksplit: the l
     l.nval = take(B * 64 * 4);
     l.tail = take(B * L * 4);                          // full-vocabulary mode: tail_lse per row
     l.tail_part = take(B * L * (size_t)nseg * 2 * 4);  // its per-segment (m, s) sums
-    l.wpack = take(c.dtype == DT_BF16 ? (size_t)3 * H * (c.E + c.H) * 2 : 0);  // weights in operand tiles
+    l.wpack = take(wtiles && c.dtype == DT_BF16 ? (size_t)3 * H * (c.E + c.H) * 2 : 0);  // weights in operand tiles
     l.total = off;
     return l;
 }
@@ -121,6 +129,40 @@ bool misaligned(const void* p) { return p && ((uintptr_t)p % 16) != 0; }
 dt_status pending_error(dt_handle* h) {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DT_OK : hip_fail(h, e, "HIP error pending from earlier asynchronous work");
+}
+
+// dt_build_noalloc's scratch: a file-scope device array, one copy on each GPU
+// the library runs on, held until the process ends.  On the host, `scratch`
+// names a stand-in, not a device address: host code uses only the address
+// that hipGetSymbolAddress returns for each device (kept in g_scratch).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The scratch address on `stream`'s device, which must be the calling
+// thread's current device (looked up once per device, with it current).
+dt_status scratch_on(dt_handle* h, hipStream_t stream, void** out) {
+    int cur = -1, dev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(h, e, "hipGetDevice");
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamGetDevice");
+    if (dev != cur)
+        return fail(h, DT_ERR_INVALID_ARG, "dt_build_noalloc: the stream is on device %d, the current device is %d",
+                    dev, cur);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(h, DT_ERR_UNSUPPORTED, "dt_build_noalloc: device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(h, e, "hipGetSymbolAddress(scratch)");
+        if (!p || (uintptr_t)p % kAlign)
+            return fail(h, DT_ERR_HIP, "dt_build_noalloc: scratch address %p is not %zu-byte aligned", p, kAlign);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return DT_OK;
 }
 
 dt_status check_ws(dt_handle* h, void* ws, size_t bytes) {
@@ -235,6 +277,7 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     h->ksplit_f = dt::gru_ksplit(c.B, 0, c.H, (int)c.dtype);
     h->lds = lds;
     h->lay = plan_layout(c, h->nseg, std::max(h->ksplit, h->ksplit_f));
+    h->lay_na = plan_layout(c, h->nseg, h->ksplit, /*wtiles=*/false);
     *out = h;
     return DT_OK;
 }
@@ -415,12 +458,13 @@ dt_status dt_accept_greedy(dt_handle* h, const int32_t* tokens, const int32_t* p
 
 namespace {
 // table: the folded input projection [V, 3H] (dt_build_folded; emb, W_ih and
-// b_ih are then unused), or NULL.
+// b_ih are then unused), or NULL.  noalloc: the workspace is the device's
+// static scratch (ws is ignored) and the weights are read in place.
 dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, const void* base, const void* emb,
                    const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
                    const void* C, const float* h0, int32_t* tokens, int32_t* parents, int32_t* depths,
                    float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream,
-                   const float* table = nullptr) {
+                   const float* table = nullptr, bool noalloc = false) {
     if (!h) return DT_ERR_INVALID_ARG;
     const dt_config& c = h->cfg;
     if (c.B == 0) return DT_OK;
@@ -435,11 +479,18 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     if (misaligned(base) || misaligned(emb) || misaligned(W_ih) || misaligned(W_hh) || misaligned(C) ||
         misaligned(h0) || misaligned(b_ih) || misaligned(b_hh))
         return fail(h, DT_ERR_INVALID_ARG, "dt_build: matrices must be 16-byte aligned");
-    dt_status s = check_ws(h, ws, ws_bytes);
-    if (s || (s = pending_error(h))) return s;
     hipStream_t st = (hipStream_t)stream;
+    dt_status s = DT_OK;
+    if (noalloc) {
+        if (h->lay_na.total > kScratchBytes)
+            return fail(h, DT_ERR_UNSUPPORTED, "dt_build_noalloc: needs %zu bytes of scratch, the maximum is %zu",
+                        h->lay_na.total, kScratchBytes);
+        if ((s = pending_error(h)) || (s = scratch_on(h, st, &ws))) return s;
+    } else if ((s = check_ws(h, ws, ws_bytes)) || (s = pending_error(h))) {
+        return s;
+    }
     char* w = (char*)ws;
-    const Layout& L = h->lay;
+    const Layout& L = noalloc ? h->lay_na : h->lay;
 
     std::vector<Marker>* call = nullptr;
     if (h->tlevel > 0 && (int)h->calls.size() < h->tcapacity) {
@@ -509,7 +560,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     g.B = c.B; g.E = table ? 0 : c.E; g.H = c.H;  // folded: the recurrent part alone
     g.ksplit = a.ksplit;
     g.dtype = (int)c.dtype;
-    g.wpack = c.dtype == DT_BF16 ? (uint16_t*)(w + L.wpack) : nullptr;
+    g.wpack = c.dtype == DT_BF16 && !noalloc ? (uint16_t*)(w + L.wpack) : nullptr;  // NULL: read in place
 
     if (marginal) {  // no contraction between the steps: one launch runs all n
         DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
@@ -542,6 +593,14 @@ dt_status dt_build(dt_handle* h, void* ws, size_t ws_bytes, const void* base, co
                    float* scores, uint8_t* mask, int32_t* count, uint32_t* flags, void* stream) {
     return build_impl(false, h, ws, ws_bytes, base, emb, W_ih, W_hh, b_ih, b_hh, C, h0, tokens, parents,
                       depths, scores, mask, count, flags, stream);
+}
+
+dt_status dt_build_noalloc(dt_handle* h, const void* base, const void* emb, const void* W_ih, const void* W_hh,
+                           const void* b_ih, const void* b_hh, const void* C, const float* h0, int32_t* tokens,
+                           int32_t* parents, int32_t* depths, float* scores, uint8_t* mask, int32_t* count,
+                           uint32_t* flags, void* stream) {
+    return build_impl(false, h, nullptr, 0, base, emb, W_ih, W_hh, b_ih, b_hh, C, h0, tokens, parents, depths,
+                      scores, mask, count, flags, stream, nullptr, /*noalloc=*/true);
 }
 
 dt_status dt_build_folded(dt_handle* h, void* ws, size_t ws_bytes, const void* base, const float* table,

@@ -152,6 +152,27 @@ dt_status dt_build(dt_handle *h, void *workspace, size_t ws_bytes, const void *b
                    int32_t *count, uint32_t *flags, void *stream);
 
 /*
+ * dt_build_noalloc -- dt_build for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same inputs, outputs and results as dt_build, bit for
+ * bit; no workspace argument and no allocation of any kind: the scratch is a
+ * static device array of the library, one per GPU (32 MiB), kept until the
+ * process ends.  The weights are read in place (no operand-tile copy).
+ *  - Configurations whose scratch need exceeds 32 MiB return
+ *    DT_ERR_UNSUPPORTED before anything is enqueued (the Qwen3-4B and 8B
+ *    shapes at B = 64 fit; the B = 256, n = 64 stress shape does not).
+ *  - `stream` must belong to the calling thread's current device.
+ *  - Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *    one GPU (other streams, other threads, other handles) race.  Calls
+ *    ordered on one stream do not.  Nothing in the scratch needs clearing:
+ *    each call writes what it reads.
+ */
+dt_status dt_build_noalloc(dt_handle *h, const void *base_logits, const void *emb, const void *W_ih,
+                           const void *W_hh, const void *b_ih, const void *b_hh, const void *C,
+                           const float *h0, int32_t *tokens, int32_t *parents, int32_t *depths,
+                           float *scores, uint8_t *mask, int32_t *count, uint32_t *flags, void *stream);
+
+/*
  * dt_build_marginal -- the same best-first builder with DDTree's factorized
  * scores: every node's children distribution is the log-softmax of the base
  * logits over the top-M slice of its block position (no GRU, no

@@ -93,6 +93,10 @@ int main() {
                    fi, fu32, nullptr) == DT_ERR_WORKSPACE);
     CHECK(dt_build(h, (char*)fake + 16, need, fake, fake, fake, fake, nullptr, nullptr, fake, nullptr, fi, fi, fi,
                    ff, fu8, fi, fu32, nullptr) == DT_ERR_WORKSPACE);  // workspace alignment
+    CHECK(dt_build_noalloc(h, nullptr, fake, fake, fake, nullptr, nullptr, fake, nullptr, fi, fi, fi, ff, fu8, fi,
+                           fu32, nullptr) == DT_ERR_INVALID_ARG);
+    CHECK(dt_build_noalloc(h, fake, fake, fake, fake, nullptr, nullptr, fake, (const float*)odd, fi, fi, fi, ff, fu8,
+                           fi, fu32, nullptr) == DT_ERR_INVALID_ARG);
     CHECK(dt_build_marginal(h, fake, need, nullptr, fi, fi, fi, ff, fu8, fi, fu32, nullptr) == DT_ERR_INVALID_ARG);
     CHECK(dt_build_marginal(h, fake, need, odd, fi, fi, fi, ff, fu8, fi, fu32, nullptr) == DT_ERR_INVALID_ARG);
     CHECK(dt_build_folded(h, fake, need, fake, nullptr, fake, nullptr, fake, nullptr, fi, fi, fi, ff, fu8, fi, fu32,
@@ -126,6 +130,15 @@ int main() {
     CHECK(dt_timing_read(h, 4, nullptr, 0, &nout) == DT_OK && nout == 0);
     dt_destroy(h);
 
+    // dt_build_noalloc: a configuration whose scratch exceeds the static
+    // array is rejected before any HIP call
+    const dt_config big = cfg(256, 16, 151936, 2560, 1024, 64, 64);
+    CHECK(dt_create(&big, &h) == DT_OK);
+    CHECK(dt_build_noalloc(h, fake, fake, fake, fake, nullptr, nullptr, fake, nullptr, fi, fi, fi, ff, fu8, fi, fu32,
+                           nullptr) == DT_ERR_UNSUPPORTED);
+    CHECK(strstr(dt_last_error(h), "scratch") != nullptr);
+    dt_destroy(h);
+
     // B = 0: nothing to enqueue, every pointer may be NULL
     const dt_config z = cfg(0, 4, 100, 32, 32, 8, 6);
     CHECK(dt_create(&z, &h) == DT_OK);
@@ -133,6 +146,8 @@ int main() {
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == DT_OK);
     CHECK(dt_build_marginal(h, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                             nullptr) == DT_OK);
+    CHECK(dt_build_noalloc(h, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == DT_OK);
     CHECK(dt_topm(h, nullptr, 0, nullptr, nullptr, nullptr, nullptr) == DT_OK);
     CHECK(dt_topm_tail(h, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr) == DT_OK);
     CHECK(dt_accept_greedy(h, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) == DT_OK);
