@@ -3,9 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen3_4b_batched]
 
 A step is one dt_build call: top-M select over the full vocabulary, the whole
-best-first conditional expansion (n pops, n-1 GRU contractions) and the tree +
+best-first conditional expansion (n pops and their GRU updates) and the tree +
 mask emit, for B independent requests on synthetic Zipf-shaped inputs already
-resident in HBM.  Prints ONE JSON line:
+resident in HBM.  dt_build runs its default expansion (the fused launches where
+they apply); a second handle forced to the stepped expansion (contraction and
+node step as separate kernels) gives the per-kernel figures.  Prints ONE JSON
+line:
 
   value       tree builds per second (B * K / wall time of the K timed steps)
   roofline    the top-M select kernel (the dominant HBM stream): algorithmic
@@ -17,8 +20,9 @@ resident in HBM.  Prints ONE JSON line:
               on one core on a bounded sample; host core count and CPU model
   parity      the timed trees compared with the oracle's, request by request
 Extra keys: per-round time percentiles from per-call HIP events, per-stage
-times (a separate pass with per-kernel events), the GRU contraction's MFMA rate
-against the bf16 dense peak, and latency figures.
+times (a separate pass with per-kernel events), the fused expansion launches,
+the stepped expansion's GRU contraction (MFMA rate against the bf16 dense peak)
+and gathers, and latency figures.
 """
 from __future__ import annotations
 
@@ -157,6 +161,25 @@ def parse():
     return p.parse_args()
 
 
+def fused_summary(st, sst, fused, n, stepped_us, stepped_same, np):
+    """The expansion's share of a round: the fused launches (default path) and
+    the stepped path's contraction + node-step kernels on the same inputs."""
+    d = {"mode": "fused" if fused else "stepped",
+         "stepped_us_per_round": round(stepped_us, 1),
+         "stepped_trees_equal_to_timed": stepped_same,
+         "stepped_kernels_us_per_round": round(float(np.mean(sst["gru_gemm_total"]) + np.mean(sst["node_total"])) * 1e3, 1)
+         if sst["gru_gemm_total"] and sst["node_total"] else None}
+    if fused and st["fused_each"]:
+        each = [x * 1e3 for x in st["fused_each"]]
+        d.update({"launches_per_round": len(each) // max(len(st["fused_total"]), 1),
+                  "fused_kernels_us_per_round": round(float(np.mean(st["fused_total"])) * 1e3, 1),
+                  "fused_launch_us": {"mean": round(float(np.mean(each)), 2),
+                                      "p10": round(percentile(each, 10), 2),
+                                      "median": round(percentile(each, 50), 2),
+                                      "p90": round(percentile(each, 90), 2)}})
+    return d
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -184,11 +207,12 @@ def main():
           flush=True)
 
     bld = dtree.Builder(B, L, V, E, H, M, n, cfg["T"], cfg["dtype"], 1e-5, device=dev)
+    fused = bld.fused
     stream = torch.cuda.current_stream()
 
-    def step(out=None):
-        return bld.build(t["base"], t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"],
-                         t["h0"], out=out)
+    def step(out=None, b=bld):
+        return b.build(t["base"], t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"],
+                       t["h0"], out=out)
 
     out = step()
     for _ in range(args.warmup):
@@ -227,9 +251,33 @@ def main():
     torch.cuda.synchronize()
     st = {name: dtree.dt_timing_read(bld.handle, i) for i, name in
           ((0, "topm_select"), (1, "topm_merge"), (2, "gru_gemm_total"), (3, "node_total"),
-           (4, "call"), (5, "gru_gemm_each"))}
+           (4, "call"), (5, "gru_gemm_each"), (7, "fused_total"), (8, "fused_each"))}
     dtree.dt_timing_enable(bld.handle, 0, 0)
-    gemm_each = float(np.mean(st["gru_gemm_each"])) if st["gru_gemm_each"] else float("nan")
+
+    # ---- the stepped expansion on the same inputs (its own handle): round
+    # time, and per-kernel events of its contraction and node-step kernels
+    sbld = dtree.Builder(B, L, V, E, H, M, n, cfg["T"], cfg["dtype"], 1e-5, device=dev,
+                         expand=dtree.DT_EXPAND_STEPPED) if fused else bld
+    sout = step(b=sbld) if fused else out
+    for _ in range(3):
+        step(sout, b=sbld)
+    torch.cuda.synchronize()
+    s0 = time.perf_counter()
+    for _ in range(args.stage_steps):
+        step(sout, b=sbld)
+    torch.cuda.synchronize()
+    stepped_us = (time.perf_counter() - s0) * 1e6 / max(args.stage_steps, 1)
+    dtree.dt_timing_enable(sbld.handle, 2, args.stage_steps)
+    for _ in range(args.stage_steps):
+        step(sout, b=sbld)
+    torch.cuda.synchronize()
+    sst = {name: dtree.dt_timing_read(sbld.handle, i) for i, name in
+           ((2, "gru_gemm_total"), (3, "node_total"), (5, "gru_gemm_each"))}
+    dtree.dt_timing_enable(sbld.handle, 0, 0)
+    stepped_same = bool(torch.equal(sout["tokens"], out["tokens"]) and torch.equal(sout["parents"], out["parents"]))
+    if fused:
+        sbld.close()
+    gemm_each = float(np.mean(sst["gru_gemm_each"])) if sst["gru_gemm_each"] else float("nan")
     gemm_flop = 2.0 * B * 3 * H * (E + H)
     gemm_weight_bytes = 3 * H * (E + H) * esz
     peak_mfma = MFMA_BF16_PEAK_TFS if esz == 2 else MFMA_FP32_PEAK_TFS
@@ -289,8 +337,12 @@ def main():
         torch.cuda.synchronize()
         h256 = {"workload": "qwen3_4b_head256: H=256, C [V, 256], otherwise as the main workload",
                 "us_per_round": round(h_us, 1), "tree_builds_per_s": round(B / (h_us * 1e-6), 1),
-                "gru_gemm_each_us": round(float(np.mean(dtree.dt_timing_read(hb.handle, 5))) * 1e3, 2),
-                "node_step_each_us": round(float(np.mean(dtree.dt_timing_read(hb.handle, 3))) * 1e3 / n, 2)}
+                "expansion": "fused" if hb.fused else "stepped"}
+        if hb.fused:
+            h256["fused_launch_each_us"] = round(float(np.mean(dtree.dt_timing_read(hb.handle, 8))) * 1e3, 2)
+        else:
+            h256["gru_gemm_each_us"] = round(float(np.mean(dtree.dt_timing_read(hb.handle, 5))) * 1e3, 2)
+            h256["node_step_each_us"] = round(float(np.mean(dtree.dt_timing_read(hb.handle, 3))) * 1e3 / n, 2)
         hb.close()
         del t256
 
@@ -398,7 +450,7 @@ def main():
     # embedding row per request; per round also the lower bound that reads
     # each (request, depth) slice of C once (slots 0 .. min(count, n-1) are
     # expanded, slot k from the slice of position depth(k))
-    node_each = float(np.mean(st["node_total"])) / n if st["node_total"] else float("nan")
+    node_each = float(np.mean(sst["node_total"])) / n if sst["node_total"] else float("nan")
     gather_bytes = B * (M * H + E) * esz
     dep = out["depths"].cpu().numpy()
     uniq = sum(len(set(dep[b, :min(int(cnt[b]), n - 1) + 1].tolist())) for b in range(B))
@@ -436,7 +488,7 @@ def main():
             "frac_of_copy": round(achieved_gbs / copy_gbs, 4),
         },
         "roofline_gather": {
-            "kernel": "node_step_kernel (the gathers of one expansion step)",
+            "kernel": "node_step_kernel (the gathers of one expansion step; stepped expansion)",
             "bound": "hbm",
             "limited_by": "latency: a dependent round trip for the candidate tokens, then 64 random "
                           "2 KiB rows per request",
@@ -450,7 +502,7 @@ def main():
             "round_bytes_unique_slices": uniq * M * H * esz + B * (n - 1) * E * esz,
         },
         "roofline_gru": {
-            "kernel": "gru_gemm_bf16_kernel (one expansion step)",
+            "kernel": "gru_gates_bf16_kernel (one expansion step; stepped expansion)",
             "bound": "hbm" if gemm_flop / gemm_weight_bytes < 312 else "mfma",
             "achieved_tflops": round(gemm_tfs, 2),
             "mfma_peak_tflops": peak_mfma,
@@ -465,6 +517,7 @@ def main():
             "counters": gru_counter_figures(gemm_each) if args.config == "qwen3_4b_batched" else None,
         },
         "stages_ms_mean": {k: round(float(np.mean(v)), 5) for k, v in st.items() if v},
+        "expansion": fused_summary(st, sst, fused, n, stepped_us, stepped_same, np),
         # (null: each row is one segment, so no merge kernel runs)
         "topm_merge_ms_mean": round(float(np.mean(merge_ms)), 5) if merge_ms else None,
         "call_ms_events_mean": round(float(np.mean(call_ms)), 5),

@@ -11,6 +11,7 @@ _lock = threading.Lock()
 _lib = None
 
 DT_F32, DT_BF16 = 0, 1
+DT_EXPAND_AUTO, DT_EXPAND_STEPPED, DT_EXPAND_FUSED = 0, 1, 2
 _STATUS = {0: "DT_OK", -1: "DT_ERR_INVALID_ARG", -2: "DT_ERR_UNSUPPORTED", -3: "DT_ERR_WORKSPACE",
            -4: "DT_ERR_HIP"}
 
@@ -24,7 +25,8 @@ class DtreeError(RuntimeError):
 class dt_config(C.Structure):
     _fields_ = [("B", C.c_int32), ("L", C.c_int32), ("V", C.c_int32), ("E", C.c_int32),
                 ("H", C.c_int32), ("M", C.c_int32), ("n", C.c_int32), ("temperature", C.c_float),
-                ("dtype", C.c_int), ("near_tie_eps", C.c_float), ("full_vocab", C.c_int32)]
+                ("dtype", C.c_int), ("near_tie_eps", C.c_float), ("full_vocab", C.c_int32),
+                ("expand", C.c_int32)]
 
 
 def lib_path() -> str:
@@ -48,6 +50,8 @@ def load_library():
         lib.dt_destroy.restype = None
         lib.dt_workspace_bytes.argtypes = [H]
         lib.dt_workspace_bytes.restype = C.c_size_t
+        lib.dt_expand_mode.argtypes = [H]
+        lib.dt_expand_mode.restype = C.c_int32
         lib.dt_status_string.argtypes = [C.c_int]
         lib.dt_status_string.restype = C.c_char_p
         lib.dt_last_error.argtypes = [H]
@@ -102,11 +106,12 @@ def dt_last_error(handle=None) -> str:
     return load_library().dt_last_error(handle).decode(errors="replace")
 
 
-def dt_create(B, L, V, E, H, M, n, temperature=0.0, dtype=DT_BF16, near_tie_eps=1e-5, full_vocab=False):
+def dt_create(B, L, V, E, H, M, n, temperature=0.0, dtype=DT_BF16, near_tie_eps=1e-5, full_vocab=False,
+              expand=DT_EXPAND_AUTO):
     """Returns an opaque handle (host only; no GPU needed)."""
     lib = load_library()
     cfg = dt_config(B, L, V, E, H, M, n, float(temperature), int(dtype), float(near_tie_eps),
-                    int(bool(full_vocab)))
+                    int(bool(full_vocab)), int(expand))
     h = C.c_void_p()
     _check(lib.dt_create(C.byref(cfg), C.byref(h)), None)
     return h
@@ -118,6 +123,10 @@ def dt_destroy(handle):
 
 def dt_workspace_bytes(handle) -> int:
     return int(load_library().dt_workspace_bytes(handle))
+
+
+def dt_expand_mode(handle) -> int:
+    return int(load_library().dt_expand_mode(handle))
 
 
 def _p(t):
@@ -220,17 +229,22 @@ class Builder:
     """
 
     def __init__(self, B, L, V, E, H, M, n, temperature=0.0, dtype="bf16", near_tie_eps=1e-5,
-                 device=None, full_vocab=False):
+                 device=None, full_vocab=False, expand=DT_EXPAND_AUTO):
         import torch
         self.cfg = dict(B=B, L=L, V=V, E=E, H=H, M=M, n=n, temperature=float(temperature),
-                        near_tie_eps=float(near_tie_eps), full_vocab=bool(full_vocab))
+                        near_tie_eps=float(near_tie_eps), full_vocab=bool(full_vocab), expand=int(expand))
         self.dtype_name = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.handle = dt_create(B, L, V, E, H, M, n, temperature,
-                                DT_BF16 if dtype == "bf16" else DT_F32, near_tie_eps, full_vocab)
+                                DT_BF16 if dtype == "bf16" else DT_F32, near_tie_eps, full_vocab, expand)
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         nbytes = dt_workspace_bytes(self.handle)
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+
+    @property
+    def fused(self) -> bool:
+        """True when dt_build runs the fused expansion for this configuration."""
+        return dt_expand_mode(self.handle) == DT_EXPAND_FUSED
 
     def close(self):
         if getattr(self, "handle", None) is not None:

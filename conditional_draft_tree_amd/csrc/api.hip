@@ -29,6 +29,8 @@ thread_local char g_create_error[512] = "";
 struct Layout {
     size_t partial, tidx, tval, hstate, hsplit, gpart, gru_tok, gru_par, child_tok, child_lp, ckey, queue, nidx, nval,
         rstate, xpack, hpack, hprev, tail, tail_part, wpack;
+    // fused expansion only (sizes 0 otherwise)
+    size_t p_gi, p_gh, p_hstate, p_exp, p_done, p_active, p_xpack1, p_hpack1, p_xtok, p_hslot;
     size_t total;
 };
 
@@ -49,6 +51,8 @@ struct dt_handle {
     int ksplit;    // K ranges of the gate contraction
     int ksplit_f;  // of its recurrent part alone (folded input projection)
     dt::NodeLds lds;
+    dt::PipePlan pp;  // fused expansion plan (pp.ng = 0: stepped)
+    int pipe_T;       // launches of a fused call
     Layout lay;
     Layout lay_na;  // dt_build_noalloc's use of the static scratch (no weight-tile copy)
     std::string err;
@@ -85,8 +89,10 @@ float tail_scale(const dt_config& c) {
     return 1.4426950408889634f / (c.temperature > 0.f ? c.temperature : 1.f);
 }
 
-// ksplit: the larger of the two; wtiles: room for the weights in operand tiles
-Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true) {
+// ksplit: the larger of the two; wtiles: room for the weights in operand tiles;
+// pp: the fused expansion's plan (pp.ng = 0: none), pT its launches per call
+Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true, dt::PipePlan pp = {},
+                   int pT = 0) {
     Layout l{};
     const size_t B = c.B, L = c.L, M = c.M, S = (size_t)c.n + 1, H = c.H;
     size_t off = 0;
@@ -116,6 +122,18 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true)
     l.tail = take(B * L * 4);                          // full-vocabulary mode: tail_lse per row
     l.tail_part = take(B * L * (size_t)nseg * 2 * 4);  // its per-segment (m, s) sums
     l.wpack = take(wtiles && c.dtype == DT_BF16 ? (size_t)3 * H * (c.E + c.H) * 2 : 0);  // weights in operand tiles
+    const bool fp = pp.ng > 0;
+    const size_t pks = fp ? (size_t)pp.ksplit : 0;
+    l.p_gi = take(2 * pks * B * 3 * H * 4);           // x-part gate sums by launch parity
+    l.p_gh = take(B * S * pks * 3 * H * 4);           // h-part gate sums per slot
+    l.p_hstate = take(fp ? B * S * H * 4 : 0);        // binary32 state per slot
+    l.p_exp = take(fp ? B * S * 4 : 0);               // launch that expanded each slot
+    l.p_done = take(fp ? (size_t)pT * 4 : 0);         // per-launch counters
+    l.p_active = take(fp ? (size_t)2 * pT * 4 : 0);
+    l.p_xpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * c.E * 2 : 0);  // parity-1 activations
+    l.p_hpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
+    l.p_xtok = take(fp ? 2 * B * 4 : 0);
+    l.p_hslot = take(fp ? 2 * B * 4 : 0);
     l.total = off;
     return l;
 }
@@ -249,6 +267,8 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
         return fail(nullptr, DT_ERR_INVALID_ARG, "temperature and near_tie_eps must be >= 0");
     if (c.full_vocab != 0 && c.full_vocab != 1)
         return fail(nullptr, DT_ERR_INVALID_ARG, "full_vocab must be 0 or 1 (got %d)", (int)c.full_vocab);
+    if (c.expand < DT_EXPAND_AUTO || c.expand > DT_EXPAND_FUSED)
+        return fail(nullptr, DT_ERR_INVALID_ARG, "expand must be 0, 1 or 2 (got %d)", (int)c.expand);
     if (c.M > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "M=%d > 64 (one candidate per lane)", c.M);
     if (c.n > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "n=%d > 64 (queue of one wave)", c.n);
     if (c.L > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "L=%d > 64", c.L);
@@ -276,7 +296,18 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     h->ksplit = dt::gru_ksplit(c.B, c.E, c.H, (int)c.dtype);
     h->ksplit_f = dt::gru_ksplit(c.B, 0, c.H, (int)c.dtype);
     h->lds = lds;
-    h->lay = plan_layout(c, h->nseg, std::max(h->ksplit, h->ksplit_f));
+    h->pp = dt::PipePlan{};
+    h->pipe_T = 0;
+    if (c.dtype == DT_BF16 && c.expand != DT_EXPAND_STEPPED) {
+        h->pp = dt::pipe_plan(c.B, c.L, c.E, c.H, c.M, c.n);
+        h->pipe_T = c.n + 2;
+    }
+    if (c.expand == DT_EXPAND_FUSED && h->pp.ng == 0) {
+        delete h;
+        return fail(nullptr, DT_ERR_UNSUPPORTED,
+                    "fused expansion needs bf16, 1 <= B <= 64, H <= 1024 and E, H multiples of 32");
+    }
+    h->lay = plan_layout(c, h->nseg, std::max(h->ksplit, h->ksplit_f), true, h->pp, h->pipe_T);
     h->lay_na = plan_layout(c, h->nseg, h->ksplit, /*wtiles=*/false);
     *out = h;
     return DT_OK;
@@ -289,6 +320,11 @@ void dt_destroy(dt_handle* h) {
 }
 
 size_t dt_workspace_bytes(const dt_handle* h) { return h ? h->lay.total : 0; }
+
+int32_t dt_expand_mode(const dt_handle* h) {
+    if (!h) return -1;
+    return h->pp.ng > 0 ? DT_EXPAND_FUSED : DT_EXPAND_STEPPED;
+}
 
 dt_status dt_timing_enable(dt_handle* h, int level, int capacity) {
     if (!h) return DT_ERR_INVALID_ARG;
@@ -303,7 +339,7 @@ dt_status dt_timing_enable(dt_handle* h, int level, int capacity) {
 
 dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out) {
     if (!h || !n_out || (max > 0 && !ms)) return h ? fail(h, DT_ERR_INVALID_ARG, "null output") : DT_ERR_INVALID_ARG;
-    if (stage < 0 || stage > 6) return fail(h, DT_ERR_INVALID_ARG, "stage must be 0..6");
+    if (stage < 0 || stage > 8) return fail(h, DT_ERR_INVALID_ARG, "stage must be 0..8");
     int n = 0;
     for (const auto& call : h->calls) {
         float sum = 0.f;
@@ -312,12 +348,13 @@ dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out
             const char tag = call[i].tag;
             bool hit = (stage == 0 && tag == 'T') || (stage == 1 && tag == 'M') ||
                        (stage == 2 && tag == 'G') || (stage == 3 && tag == 'N') ||
-                       (stage == 5 && tag == 'G') || (stage == 6 && tag == 'A');
+                       (stage == 5 && tag == 'G') || (stage == 6 && tag == 'A') ||
+                       ((stage == 7 || stage == 8) && tag == 'P');
             if (!hit) continue;
             float t = 0.f;
             hipError_t e = hipEventElapsedTime(&t, call[i - 1].ev, call[i].ev);
             if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
-            if (stage == 5) {
+            if (stage == 5 || stage == 8) {
                 if (n < max) ms[n] = t;
                 ++n;
             } else {
@@ -332,7 +369,7 @@ dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out
             sum = t;
             any = true;
         }
-        if (stage != 5 && any) {
+        if (stage != 5 && stage != 8 && any) {
             if (n < max) ms[n] = sum;
             ++n;
         }
@@ -565,6 +602,40 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     if (marginal) {  // no contraction between the steps: one launch runs all n
         DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
         DT_TRY(dt::launch_marginal_build(a, h->lds, st, ev), "factorized expansion launch");
+        DT_TRY(mark(h, call, 1, 'E', st), "timing event");
+        return DT_OK;
+    }
+    if (!table && !noalloc && h->pp.ng > 0) {  // fused expansion: n + 2 launches
+        dt::PipeArgs pa{};
+        pa.B = c.B; pa.L = c.L; pa.V = c.V; pa.E = c.E; pa.H = c.H; pa.M = c.M; pa.n = c.n;
+        pa.T = h->pipe_T;
+        pa.ng = h->pp.ng; pa.ksplit = h->pp.ksplit; pa.xwaves = h->pp.xwaves;
+        pa.temp = c.temperature; pa.eps = c.near_tie_eps;
+        pa.C = C; pa.h0 = h0; pa.tidx = tidx; pa.tval = tval; pa.tail = tail;
+        pa.emb = emb; pa.W_ih = W_ih; pa.W_hh = W_hh; pa.b_ih = b_ih; pa.b_hh = b_hh;
+        pa.xpack[0] = (uint16_t*)(w + L.xpack);
+        pa.xpack[1] = (uint16_t*)(w + L.p_xpack1);
+        pa.hpack[0] = (uint16_t*)(w + L.hpack);
+        pa.hpack[1] = (uint16_t*)(w + L.p_hpack1);
+        pa.xtok[0] = (int32_t*)(w + L.p_xtok);
+        pa.xtok[1] = pa.xtok[0] + c.B;
+        pa.hslot[0] = (int32_t*)(w + L.p_hslot);
+        pa.hslot[1] = pa.hslot[0] + c.B;
+        pa.gi = (float*)(w + L.p_gi);
+        pa.gh = (float*)(w + L.p_gh);
+        pa.hstate = (float*)(w + L.p_hstate);
+        pa.exp_at = (int32_t*)(w + L.p_exp);
+        pa.done = (unsigned*)(w + L.p_done);
+        pa.active = (int32_t*)(w + L.p_active);
+        pa.wpack = (uint16_t*)(w + L.wpack);
+        pa.child_tok = a.child_tok; pa.child_lp = a.child_lp; pa.ckey = a.ckey; pa.queue = a.queue;
+        pa.rstate = a.rstate; pa.nidx = a.nidx; pa.nval = a.nval;
+        pa.tokens = tokens; pa.parents = parents; pa.depths = depths; pa.scores = scores;
+        pa.mask = mask; pa.count = count; pa.flags = flags;
+        for (int t = 0; t < h->pipe_T; ++t) {
+            DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
+            DT_TRY(dt::launch_pipe_step(pa, h->pp, h->lds, t, st, ev), "fused expansion launch");
+        }
         DT_TRY(mark(h, call, 1, 'E', st), "timing event");
         return DT_OK;
     }

@@ -158,6 +158,68 @@ hipError_t launch_node_step(const NodeArgs& a, const NodeLds& lp, int step, hipS
 // every request, one workgroup per request looping over them.
 hipError_t launch_marginal_build(const NodeArgs& a, const NodeLds& lp, hipStream_t stream, LaunchEvents ev = {});
 
+// ---- fused pipelined expansion (expand.hip, bf16) ----------------------------
+// One launch per expansion step runs two kinds of workgroups side by side:
+// `ng` contraction workgroups (16 hidden units x one of `ksplit` K ranges
+// each) and one node workgroup per request.  The contraction of launch t
+// takes, per request, an x row (the embedding of the token whose input
+// projection the request needs next: a prediction of its next expansion, or
+// the node it has to expand) and an h row (the state of the node it expanded
+// at launch t - 1), so the node workgroups of launch t expand with what
+// launch t - 1 contracted.  See expand.hip.
+struct PipeArgs {
+    int B, L, V, E, H, M, n;
+    int T;                // launches per call
+    int ng, ksplit, xwaves;
+    float temp, eps;
+    const void* C;
+    const float* h0;
+    const int32_t* tidx;  // [B, L, M] top-M tables
+    const float* tval;
+    const float* tail;    // [B, L] full-vocabulary mode, or NULL
+    const void* emb;
+    const void* W_ih;
+    const void* W_hh;
+    const void* b_ih;
+    const void* b_hh;
+    // workspace
+    uint16_t* xpack[2];   // contraction activations by launch parity (pack_index_x / _h)
+    uint16_t* hpack[2];
+    int32_t* xtok[2];     // [B] token of launch t's x row (parity t & 1), -1 = none
+    int32_t* hslot[2];    // [B] slot whose state is launch t's h row, -1 = none
+    float* gi;            // [2][ksplit][B][3][H] x-part gate sums by launch parity
+    float* gh;            // [B][n+1][ksplit][3][H] h-part gate sums per slot
+    float* hstate;        // [B][n+1][H] binary32 state per slot (slot 0 = h0)
+    int32_t* exp_at;      // [B][n+1] launch that expanded the slot
+    unsigned* done;       // [T] contraction workgroups finished, per launch
+    int32_t* active;      // [2][T] launch t's contraction has a row; some request waits for it
+    uint16_t* wpack;      // the weights in operand tiles (written by launch 1)
+    int32_t* child_tok;   // [B, n+1, 64]
+    float* child_lp;
+    u64* ckey;            // [B, n+1, 64] unsorted child keys
+    u64* queue;           // [B, 64]
+    int32_t* rstate;      // [B, kStateWords]
+    int32_t* nidx;        // [B, 64] candidates of the slot to expand
+    float* nval;
+    // outputs
+    int32_t* tokens;
+    int32_t* parents;
+    int32_t* depths;
+    float* scores;
+    uint8_t* mask;
+    int32_t* count;
+    uint32_t* flags;
+};
+// Launch geometry of the fused expansion for a configuration, or ng = 0 when
+// it does not apply (binary32, the factorized mode, too many requests).
+struct PipePlan {
+    int ng, ksplit, xwaves, rb;
+    size_t lds;  // dynamic LDS bytes
+};
+PipePlan pipe_plan(int B, int L, int E, int H, int M, int n);
+hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, int t, hipStream_t stream,
+                            LaunchEvents ev = {});
+
 // Conditional children distribution of one node per row (dt_correct).
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,
                           const int32_t* pos, int32_t* tok_sorted, float* lp_sorted, int B, int L,

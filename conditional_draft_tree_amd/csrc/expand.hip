@@ -22,8 +22,11 @@
 //   4. stage slot s+1 for the next GRU step;
 //   5. after the last step, emit the ancestor-only mask.
 // Queue key: (score desc, depth asc, parent slot asc, rank asc).
+#include <algorithm>
+
 #include "dt_device.h"
 #include "dt_launch.h"
+#include "gate_tile.h"
 
 namespace dt {
 
@@ -249,7 +252,7 @@ __device__ __forceinline__ void node_step_body(const NodeArgs& a, const NodeLds&
     constexpr int NW = NT / kWave;
     constexpr int RW = kMaxM / NW;                    // gathered rows per wave
     constexpr int kStageV = kMaxM * kMaxN / (4 * NT);  // 16-byte vectors of table / child list per thread
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // (16-byte vector accesses)
     float* hs = lds + lp.hs;
     float* zs = lds + lp.zs;
     float* s_sc = lds + lp.sc;
@@ -817,6 +820,614 @@ __global__ __launch_bounds__(kCorrThreads) void correct_kernel(const int32_t* ti
     }
 }
 
+// ============================================================================
+// Fused pipelined expansion (bf16).  One launch per expansion step; its grid
+// holds `ng` contraction workgroups (blocks 0 .. ng-1) and one node workgroup
+// per request (blocks ng .. ng+B-1), all of 512 threads, on separate CUs.
+//
+// The GRU update of node v needs gi(v) = W_ih . Emb[tok(v)] (its token's input
+// projection) and gh(p) = W_hh . h(p) (its parent's recurrent projection).
+// Launch t's contraction computes, per request, gi of one token (x row) and
+// gh of the node that request expanded at launch t - 1 (h row, kept per slot
+// in the workspace).  Its node workgroup meanwhile expands the node popped at
+// t - 1 with what earlier launches contracted, so the contraction is off the
+// expansion's dependency chain.  The x row of launch t + 1 is chosen by the
+// node workgroup of launch t: after its pop, the queue's best candidate is
+// the next pop unless the node expanded at t + 1 has a better child, so that
+// candidate's token is contracted ahead (a prediction); when a pop takes the
+// newest child instead, the popped node's own token is contracted at t + 1
+// and the request waits one launch (it expands at t + 2).  Every launch after
+// the first expands at most one node per request, so a call runs n + 2
+// launches; a request that has used its one spare launch and is not ready
+// waits inside the launch for that launch's contraction (a counter the
+// contraction workgroups raise; bounded spin) instead of idling.  Results are
+// the stepped path's, up to binary32 rounding order of the gate sums.
+// ============================================================================
+
+constexpr int kPipeThreads = 512;
+constexpr int kMaxB = 64;  // requests of a fused call
+constexpr int kRedRow = 20;  // floats per row of the contraction's sums in LDS (16 units + padding)
+constexpr int kPipeWaves = kPipeThreads / kWave;    // 8
+constexpr int kPipeRows = kMaxM / kPipeWaves;       // 8 gathered rows per wave
+constexpr unsigned kPipeSpinLimit = 1u << 18;       // bounded wait for a launch's contraction (~0.3 s)
+constexpr uint32_t kPipeTimeoutFlag = 0x80000000u;  // flags bit: such a wait timed out
+// dynamic LDS a fused launch may take: a CU's 160 KB less the static
+// variables of the node role (and headroom)
+constexpr size_t kPipeMaxDynLds = 160 * 1024 - 256;
+
+// Agent-scope loads (coherent across XCDs) of the gate sums that a waiting
+// node workgroup reads in the launch that computes them.
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __uint_as_float(__hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Contraction role: 32 hidden units x one K range of launch t's rows (the
+// 32-unit tile of gate_tile.h: the activations staged in LDS once per
+// workgroup).  Its x waves' sums are the x part of gates (r, z, n), its h
+// waves' sums the h part; the two halves of each are added in LDS (first
+// half first) and stored: gi by launch parity, gh by the slot of the state.
+template <int WM, int RB>
+__device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) {
+    if (t == 0) {  // no rows yet; clear this call's per-launch counters and flags
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < a.T; i += kPipeThreads) {
+                a.done[i] = 0u;
+                a.active[i] = 0;
+                a.active[a.T + i] = 0;
+            }
+        return;
+    }
+    const int groups = a.H / 32;
+    const int ug = (int)blockIdx.x % groups, ks = (int)blockIdx.x / groups;
+    const int par = t & 1, S = a.n + 1;
+    // this launch's flags: some row needs the contraction (launch 1 always
+    // has rows); some request waits for its sums in this launch, so they are
+    // published (release) and the workgroup counted -- otherwise they are
+    // read from launch t + 1 on, after the launch boundary, and plain stores
+    // suffice.  Their loads overlap the contraction, which runs either way
+    // (its inputs are always in bounds; without rows nothing is stored).
+    const int act = a.active[t], publish = a.active[a.T + t];
+    __shared__ int s_hsl[kMaxB];  // each row's state slot (ordered by the tile's barrier)
+    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = a.hslot[par][threadIdx.x];
+    GruGatesArgs g{};
+    g.xpack = a.xpack[par];
+    g.hpack = a.hpack[par];
+    g.W_ih = a.W_ih;
+    g.W_hh = a.W_hh;
+    g.B = a.B;
+    g.E = a.E;
+    g.H = a.H;
+    g.ksplit = a.ksplit;
+    g.dtype = 1;
+    g.wpack = a.wpack;
+    g.wmode = WM;
+    gate::f32x4 acc[RB][3];
+    gate::tile32_lds<WM, RB>(g, ug, ks, a.ksplit, reinterpret_cast<gate::u32x4*>(lds), acc);
+    __syncthreads();  // every wave is done with the staged activations
+    // the waves' sums into LDS as [wave][rb][slot][row of 16][unit of 16],
+    // rows padded to kRedRow floats (the four row groups of a write fall in
+    // different banks); MFMA output lane l holds unit l % 16 of rows
+    // 4 (l / 16) + e
+    const int wave = (int)threadIdx.x / kWave, lane = lane_id();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                lds[(((wave * RB + rb) * 3 + sl) * 16 + (lane >> 4) * 4 + e) * kRedRow + (lane & 15)] = acc[rb][sl][e];
+    __syncthreads();
+    if (t == 1 || act != 0) {
+        // outputs: (kind, slot, row, 4 consecutive units) per 16-byte store; a
+        // wave covers 8 rows x 32 units (128 contiguous bytes per row).  The
+        // halves of a kind (waves 4 u + 2 kind + 0, 1) are added first half first.
+        for (int idx = (int)threadIdx.x; idx < 2 * 3 * a.B * 8; idx += kPipeThreads) {
+            const int u4 = idx & 7, r = idx >> 3;
+            const int row = r % a.B, ksl = r / a.B, sl = ksl % 3, kind = ksl / 3;
+            const int u = u4 >> 2, rb = row >> 4, r16 = row & 15, c16 = (u4 & 3) * 4;
+            const int w0 = u * 4 + kind * 2;
+            const gate::f32x4 v0 =
+                *reinterpret_cast<const gate::f32x4*>(lds + (((w0 * RB + rb) * 3 + sl) * 16 + r16) * kRedRow + c16);
+            const gate::f32x4 v1 = *reinterpret_cast<const gate::f32x4*>(
+                lds + ((((w0 + 1) * RB + rb) * 3 + sl) * 16 + r16) * kRedRow + c16);
+            const gate::f32x4 sum = v0 + v1;
+            const int unit = ug * 32 + u4 * 4;
+            if (kind == 0) {
+                *reinterpret_cast<gate::f32x4*>(a.gi + (((size_t)(par * a.ksplit + ks) * a.B + row) * 3 + sl) * a.H +
+                                                unit) = sum;
+            } else {
+                const int hsl = s_hsl[row];
+                if (hsl >= 0 && hsl < S)
+                    *reinterpret_cast<gate::f32x4*>(
+                        a.gh + ((((size_t)row * S + hsl) * a.ksplit + ks) * 3 + sl) * a.H + unit) = sum;
+            }
+        }
+    }
+    if (publish) {
+        // every store of the workgroup has reached the L2; thread 0 writes the
+        // L2 back (agent-scope release) and counts the workgroup
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_fetch_add(a.done + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Node role: request b's step at launch t.
+enum PipeMode { kRoot, kExpand, kWait, kTrivial, kIdle, kDone };
+
+__device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, int t, float* lds) {
+    constexpr int NT = kPipeThreads, RW = kPipeRows;
+    constexpr int P = 8;                    // bf16 elements per 16-byte vector
+    constexpr int kChunk = 2 * kWave * P;   // K elements of a gathered chunk
+    constexpr int kStageV = kMaxM * kMaxN / (4 * NT);  // 16-byte vectors of table / child list per thread
+    float* hs = lds + lp.hs;
+    float* zs = lds + lp.zs;
+    float* s_sc = lds + lp.sc;
+    int* s_par = (int*)(lds + lp.par);
+    int32_t* s_tidx = (int32_t*)(lds + lp.tidx);
+    float* s_tval = lds + lp.tval;
+    int32_t* s_ctok = (int32_t*)(lds + lp.ctok);
+    float* s_clp = lds + lp.clp;
+    int32_t* s_exp = (int32_t*)(lds + lp.bytes / 4);  // [n+1] launch that expanded each slot
+    __shared__ int s_dec[4];  // x-row token and h-row slot of the next launch, mode
+
+    const int b = (int)blockIdx.x - a.ng;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int S = a.n + 1, H = a.H, M = a.M, LM = a.L * a.M;
+    const size_t slot0 = (size_t)b * S;
+    const int pt = t & 1, pn = (t + 1) & 1;  // this launch's parity; the next's (= the previous one's)
+    const int KS = a.ksplit;
+
+    // ---- round trip 1 (every address valid in every mode)
+    const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
+    const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
+    const u64 q_m = a.queue[(size_t)b * kWave + lane];
+    const int xt_prev = a.xtok[pn][b];  // launch t-1's x row
+    const int xt_cur = a.xtok[pt][b];   // this launch's x row
+    const int jl = min(lane, M - 1);
+    const int32_t* ip = t == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
+    const float* vp = t == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
+    const int my_tok = min(max(ip[jl], 0), a.V - 1);
+    const float my_val = vp[jl];
+    // this thread's state elements k1 and k1 + NT (H <= 2 NT)
+    const int k1 = (int)threadIdx.x, k2 = k1 + NT;
+    const int kc1 = k1 < H ? k1 : 0, kc2 = k2 < H ? k2 : 0;
+    float gi[2][kMaxKsplit][3];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+            const size_t base = (((size_t)(pn * KS + min(s2, KS - 1)) * a.B + b) * 3 + g) * H;
+            gi[0][s2][g] = a.gi[base + kc1];
+            gi[1][s2][g] = a.gi[base + kc2];
+        }
+    float bias[2][6];
+#pragma unroll
+    for (int g = 0; g < 6; ++g) {
+        const void* bp = g < 3 ? a.b_ih : a.b_hh;
+        const bf16_t* src = bp ? (const bf16_t*)bp : (const bf16_t*)a.tidx;  // any valid address
+        const float v1 = load1<bf16_t>(src + (size_t)(g % 3) * H + kc1);
+        const float v2 = load1<bf16_t>(src + (size_t)(g % 3) * H + kc2);
+        bias[0][g] = bp ? v1 : 0.f;
+        bias[1][g] = bp ? v2 : 0.f;
+    }
+    float h0v[2] = {0.f, 0.f};
+    {
+        const float* h0p = a.h0 ? a.h0 + (size_t)b * H : a.tval;
+        const float v1 = h0p[kc1], v2 = h0p[kc2];
+        h0v[0] = a.h0 ? v1 : 0.f;
+        h0v[1] = a.h0 ? v2 : 0.f;
+    }
+    float tail_l = -INFINITY;
+    {
+        const float* tp = a.tail ? a.tail + (size_t)b * a.L : a.tval;
+        const float v = tp[min(lane, a.L - 1)];
+        tail_l = a.tail ? v : -INFINITY;
+    }
+    // top-M table, sorted child lists, scores, parents and expansion launches
+    // of every slot (rows of slots not yet filled are never read)
+    const bool tvec = (LM & 3) == 0;
+    i32x4 r_ti[kStageV], r_ct[kStageV];
+    f32x4 r_tv[kStageV], r_cl[kStageV];
+    const int32_t* ti = a.tidx + (size_t)b * LM;
+    const float* tv = a.tval + (size_t)b * LM;
+    const int32_t* kt = a.child_tok + slot0 * kMaxM;
+    const float* kl = a.child_lp + slot0 * kMaxM;
+    const int nkid = a.n * kMaxM;
+#pragma unroll
+    for (int u = 0; u < kStageV; ++u) {
+        const int e = ((int)threadIdx.x + u * NT) * 4;
+        const bool te = tvec && e < LM, ke = t > 0 && e < nkid;
+        r_ti[u] = te ? *reinterpret_cast<const i32x4*>(ti + e) : i32x4{0, 0, 0, 0};
+        r_tv[u] = te ? *reinterpret_cast<const f32x4*>(tv + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+        r_ct[u] = ke ? *reinterpret_cast<const i32x4*>(kt + e) : i32x4{0, 0, 0, 0};
+        r_cl[u] = ke ? *reinterpret_cast<const f32x4*>(kl + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float r_sc = 0.f;
+    int r_par = -1, r_exp = 0;
+    if (t > 0 && (int)threadIdx.x < S) {
+        r_sc = a.scores[slot0 + threadIdx.x];
+        r_par = a.parents[slot0 + threadIdx.x];
+        r_exp = a.exp_at[slot0 + threadIdx.x];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the request's state and this launch's mode (uniform)
+    const int cnt = t == 0 ? 0 : rs0[0];
+    const int cur = t == 0 ? 0 : (rs0[1] < 0 ? -1 : min(rs0[1], a.n));
+    int qs = t == 0 ? 0 : rs0[2];
+    uint32_t flag = t == 0 ? 0u : (uint32_t)rs0[3];
+    const int unsorted = t == 0 || rs1[0] < 0 || rs1[0] >= a.n ? -1 : rs1[0];
+    const int ctok = t == 0 ? -1 : rs1[1];
+    const int cpar = t == 0 ? -1 : min(max(rs1[2], 0), a.n);
+    const int cdepth = t == 0 ? 0 : rs1[3];
+    u64 q = t == 0 ? 0ull : q_m;
+    // a node to expand (its GRU inputs may not be ready yet): its correction
+    // rows are gathered at once, whatever the readiness turns out to be
+    const bool cand = t > 0 && cnt < a.n && cur >= 0 && cdepth < a.L;
+
+    // ---- round trip 2: the gathered correction rows, the parent's gh, state
+    // and expansion launch
+    u32x4 cv[RW][2];
+    auto gather = [&](int k0) {
+        const int ka = min(k0 + lane * P, H - P), kb = min(k0 + (kWave + lane) * P, H - P);
+#pragma unroll
+        for (int jj = 0; jj < RW; ++jj) {
+            const int tk = __builtin_amdgcn_readlane(my_tok, wave * RW + jj);
+            const bf16_t* row = (const bf16_t*)a.C + (size_t)tk * H;
+            cv[jj][0] = *reinterpret_cast<const u32x4*>(row + ka);
+            cv[jj][1] = *reinterpret_cast<const u32x4*>(row + kb);
+        }
+    };
+    if (t == 0 || cand) gather(0);
+    const int cp = t == 0 ? 0 : cpar;
+    const int pexp = a.exp_at[slot0 + cp];
+    float gh[2][kMaxKsplit][3];
+    float hp[2];
+    {
+        const float* ghp = a.gh + (slot0 + cp) * (size_t)KS * 3 * H;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const size_t o = ((size_t)min(s2, KS - 1) * 3 + g) * H;
+                gh[0][s2][g] = ghp[o + kc1];
+                gh[1][s2][g] = ghp[o + kc2];
+            }
+        const float* hpp = a.hstate + (slot0 + cp) * H;
+        hp[0] = hpp[kc1];
+        hp[1] = hpp[kc2];
+    }
+    const u64 prev_keys = a.ckey[(slot0 + (unsorted >= 0 ? unsorted : 0)) * kMaxM + lane];
+    // this launch's mode (uniform over the workgroup)
+    int mode;
+    if (t == 0) mode = kRoot;
+    else if (cnt >= a.n || cur < 0) mode = kDone;
+    else if (cdepth >= a.L) mode = kTrivial;
+    else if (xt_prev == ctok && pexp <= t - 2) mode = kExpand;  // gi and the parent's gh are ready
+    else if (a.n - cnt <= a.T - 1 - t) mode = kIdle;            // a spare launch is left: expand at t + 1
+    else mode = kWait;                                           // none left: take this launch's
+    const bool grow = mode == kRoot || mode == kExpand || mode == kWait;
+
+    // ---- stage into LDS
+#pragma unroll
+    for (int u = 0; u < kStageV; ++u) {
+        const int e = ((int)threadIdx.x + u * NT) * 4;
+        if (tvec && e < LM) {
+            *reinterpret_cast<i32x4*>(s_tidx + e) = r_ti[u];
+            *reinterpret_cast<f32x4*>(s_tval + e) = r_tv[u];
+        }
+        if (e < nkid) {
+            *reinterpret_cast<i32x4*>(s_ctok + e) = r_ct[u];
+            *reinterpret_cast<f32x4*>(s_clp + e) = r_cl[u];
+        }
+    }
+    if (!tvec)
+        for (int e = threadIdx.x; e < LM; e += NT) {
+            s_tidx[e] = ti[e];
+            s_tval[e] = tv[e];
+        }
+    if ((int)threadIdx.x < S) {
+        s_sc[threadIdx.x] = threadIdx.x == 0 ? 0.f : r_sc;
+        s_par[threadIdx.x] = threadIdx.x == 0 ? -1 : r_par;
+        s_exp[threadIdx.x] = r_exp;
+    }
+
+    // ---- wait for this launch's contraction (bounded), then take its sums
+    if (mode == kWait) {
+        if (threadIdx.x == 0) {
+            unsigned spins = 0;
+            while (__hip_atomic_load(a.done + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.ng &&
+                   ++spins < kPipeSpinLimit)
+                __builtin_amdgcn_s_sleep(2);
+            s_dec[3] = spins >= kPipeSpinLimit;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // (lines of the sums cached earlier are stale)
+        }
+        __syncthreads();
+        if (s_dec[3]) flag |= kPipeTimeoutFlag;
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const size_t base = (((size_t)(pt * KS + min(s2, KS - 1)) * a.B + b) * 3 + g) * H;
+                gi[0][s2][g] = ld_agent(a.gi + base + kc1);
+                gi[1][s2][g] = ld_agent(a.gi + base + kc2);
+                const float* ghp = a.gh + (slot0 + cp) * (size_t)KS * 3 * H + ((size_t)min(s2, KS - 1) * 3 + g) * H;
+                gh[0][s2][g] = ld_agent(ghp + kc1);
+                gh[1][s2][g] = ld_agent(ghp + kc2);
+            }
+    }
+
+    // ---- the expanded node's state: GRU cell (the root takes h0)
+    if (grow) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kk = u == 0 ? k1 : k2;
+            if (kk >= H) continue;
+            float hv = h0v[u];
+            if (mode != kRoot) {
+                float sr = 0.f, sz = 0.f, snx = 0.f, snh = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+                    if (s2 < KS) {
+                        sr += gi[u][s2][0];
+                        sz += gi[u][s2][1];
+                        snx += gi[u][s2][2];
+                    }
+                float hr = 0.f, hz = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+                    if (s2 < KS) {
+                        hr += gh[u][s2][0];
+                        hz += gh[u][s2][1];
+                        snh += gh[u][s2][2];
+                    }
+                hv = gru_cell_b(sr + hr, sz + hz, snx, snh, bias[u][0], bias[u][1], bias[u][2], bias[u][3],
+                                bias[u][4], bias[u][5], hp[u]);
+            }
+            hs[kk] = hv;
+            a.hstate[(slot0 + (mode == kRoot ? 0 : cur)) * H + kk] = hv;
+        }
+    }
+    __syncthreads();
+
+    // the previously expanded slot's children, sorted for the sibling pushes
+    // of this and later launches (wave 1, while the gathers are in flight)
+    if (wave == 1 && unsorted >= 0) {
+        const u64 kids = wave_sort_desc(prev_keys);
+        if (lane < M) {
+            a.child_tok[(slot0 + unsorted) * kMaxM + lane] = child_tok_of(kids);
+            a.child_lp[(slot0 + unsorted) * kMaxM + lane] = child_lp_of(kids);
+            s_ctok[unsorted * kMaxM + lane] = child_tok_of(kids);
+            s_clp[unsorted * kMaxM + lane] = child_lp_of(kids);
+        }
+    }
+
+    // ---- correction dots of the expanded node's children
+    if (grow) {
+        float acc[RW];
+#pragma unroll
+        for (int jj = 0; jj < RW; ++jj) acc[jj] = 0.f;
+        for (int k0 = 0; k0 < H; k0 += kChunk) {
+            if (k0 > 0) gather(k0);
+            const int ka = k0 + lane * P, kb = k0 + (kWave + lane) * P;
+            float ha[P], hb[P];
+#pragma unroll
+            for (int i2 = 0; i2 < P; ++i2) {
+                ha[i2] = ka < H ? hs[ka + i2] : 0.f;
+                hb[i2] = kb < H ? hs[kb + i2] : 0.f;
+            }
+#pragma unroll
+            for (int jj = 0; jj < RW; ++jj) {
+                acc[jj] += Row<bf16_t>::dot(cv[jj][0], ha);
+                acc[jj] += Row<bf16_t>::dot(cv[jj][1], hb);
+            }
+        }
+        const float lo[4] = {acc[0], acc[1], acc[2], acc[3]};
+        const float hi[4] = {acc[4], acc[5], acc[6], acc[7]};
+        const float d0 = wave_rowsum4(lo), d1 = wave_rowsum4(hi);
+        if ((lane & 15) == 0) {
+            zs[wave * RW + (lane >> 4)] = d0;
+            zs[wave * RW + 4 + (lane >> 4)] = d1;
+        }
+    }
+    __syncthreads();
+
+    // ---- queue (wave 0): push the expanded node's best child, pop the next
+    // node, choose the next launch's contraction rows
+    const int ecur = mode == kRoot ? 0 : cur;  // the slot expanded (or popped trivially) now
+    u64 ckey = 0ull, best = 0ull, second = 0ull;
+    int new_cnt = cnt, new_cur = cur, v_par = -1, pd = 0, pr = 0, ptok = -1;
+    float psc = 0.f;
+    int xtok_next = -1, hslot_next = grow ? ecur : -1;
+    bool wait_next = false;  // launch t + 1 will find the popped node not ready and no launch to spare
+    const bool pops = mode == kRoot || mode == kExpand || mode == kWait || mode == kTrivial;
+    if (wave == 0) {
+        if (grow) {
+            const float tz = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(tail_l), min(mode == kRoot ? 0 : cdepth, a.L - 1)));
+            ckey = child_keys_r(my_val, zs[lane], my_tok, M, a.temp, tz);
+            a.ckey[(slot0 + ecur) * kMaxM + lane] = ckey;  // sorted at the next launch
+            best = wave_max_u64(ckey);
+            second = wave_max_u64(ckey == best ? 0ull : ckey);
+            const int edepth = mode == kRoot ? 0 : cdepth;
+            const u64 key = queue_key(s_sc[ecur] + child_lp_of(best), edepth + 1, ecur, 0);
+            if (lane == qs) q = key;
+            ++qs;
+        }
+        // token of a queued candidate: the expanded node's own children come
+        // from registers (ranks 0 and 1), the others from the sorted lists
+        auto cand_tok = [&](u64 k) {
+            const int p = qk_parent(k), r = qk_rank(k);
+            if (grow && p == ecur) return r == 0 ? child_tok_of(best) : child_tok_of(second);
+            return s_ctok[p * kMaxM + min(r, kMaxM - 1)];
+        };
+        if (pops && qs > 0) {
+            const u64 top = wave_max_u64(q);
+            pd = qk_depth(top);
+            v_par = qk_parent(top);
+            pr = qk_rank(top);
+            psc = qk_score(top);
+            ptok = cand_tok(top);
+            const int v = cnt + 1;
+            new_cnt = v;
+            new_cur = v;
+            // remove the popped entry, push its next-ranked sibling
+            const int holder = (int)__builtin_ctzll(__ballot(q == top));
+            const u64 last = bcast_u64(q, qs - 1);
+            if (lane == holder) q = last;
+            if (lane == qs - 1) q = 0ull;
+            --qs;
+            if (pr + 1 < M) {
+                const float sib_lp = (grow && v_par == ecur) ? child_lp_of(second)
+                                                             : s_clp[v_par * kMaxM + min(pr + 1, kMaxM - 1)];
+                const u64 key = queue_key(s_sc[v_par] + sib_lp, pd, v_par, pr + 1);
+                if (lane == qs) q = key;
+                ++qs;
+            }
+            {  // near tie: the popped score vs every candidate left
+                const float gap = psc - qk_score(q);
+                if (__ballot(lane < qs && gap > 0.f && gap < a.eps)) flag |= 1u;
+            }
+            if (lane == 0) {
+                a.tokens[slot0 + v] = ptok;
+                a.parents[slot0 + v] = v_par;
+                a.depths[slot0 + v] = pd;
+                a.scores[slot0 + v] = psc;
+                s_sc[v] = psc;
+                s_par[v] = v_par;
+            }
+            if (pd < a.L) {  // hand over the popped node's candidates
+                const int jm = min(lane, M - 1);
+                a.nidx[(size_t)b * kWave + lane] = s_tidx[pd * M + jm];
+                a.nval[(size_t)b * kWave + lane] = s_tval[pd * M + jm];
+            }
+            // the next launch's x row: the popped node's token when it cannot
+            // expand at t + 1, else the token of the queue's best candidate
+            // (the likely pop of launch t + 1)
+            if (v >= a.n) {
+                xtok_next = -1;
+            } else {
+                const int vexp = v_par == ecur && grow ? t : s_exp[v_par];
+                const bool ready_next = pd >= a.L || (t > 0 && ptok == xt_cur && vexp <= t - 1);
+                if (ready_next) xtok_next = qs > 0 ? cand_tok(wave_max_u64(q)) : -1;
+                else xtok_next = ptok;
+                // (the mode test of launch t + 1, decided here: not ready, and
+                // no idle launch left)
+                wait_next = !ready_next && !(a.n - v <= a.T - 2 - t);
+            }
+        } else if (pops) {  // the candidate tree is exhausted
+            new_cur = -1;
+        } else if (mode == kIdle) {
+            // cur expands at t + 1: contract the likely pop after it
+            xtok_next = qs > 0 ? cand_tok(wave_max_u64(q)) : -1;
+        }
+        if (lane == 0) {
+            s_dec[0] = xtok_next;
+            s_dec[1] = hslot_next;
+        }
+    }
+    __syncthreads();
+
+    if (wave != 0) {
+        // ---- the next launch's activations (waves 1 .. 7): the x row (waves
+        // 1 .. 3) and the expanded node's state in three exact bf16 parts
+        // (waves 4 .. 7)
+        const int xn = s_dec[0], hn = s_dec[1];
+        if (wave < 4) {
+            if (xn < 0) return;
+            const int nv = a.E >> 3;
+            for (int i = (wave - 1) * kWave + lane; i < nv; i += 3 * kWave) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + (size_t)xn * a.E + i * 8);
+                *reinterpret_cast<u32x4*>(a.xpack[pn] + pack_index_x(b, i * 8, a.E)) = v;
+            }
+        } else {
+            if (hn < 0) return;
+            const int nv = H >> 3;
+            for (int i = (wave - 4) * kWave + lane; i < nv; i += 4 * kWave) {
+                const int k = i * 8;
+                uint32_t w[3][4] = {};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t p3[3];
+                    split3_bf16(hs[k + e], p3);
+#pragma unroll
+                    for (int qq = 0; qq < 3; ++qq) w[qq][e >> 1] |= p3[qq] << (16 * (e & 1));
+                }
+#pragma unroll
+                for (int qq = 0; qq < 3; ++qq)
+                    *reinterpret_cast<u32x4*>(a.hpack[pn] + pack_index_h(b, qq, k, H)) =
+                        u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]};
+            }
+        }
+        return;
+    }
+
+    // ---- wave 0: the request's record for the next launch, outputs
+    if (t == 0) {  // the empty tree around the root
+        for (int i = lane; i < S; i += kWave) {
+            if (i == 0) {
+                a.tokens[slot0] = -1;
+                a.parents[slot0] = -1;
+                a.depths[slot0] = 0;
+                a.scores[slot0] = 0.f;
+            } else if (i >= 2 || new_cnt < 1) {  // slot 1 is this launch's pop
+                a.tokens[slot0 + i] = -1;
+                a.parents[slot0 + i] = -1;
+                a.depths[slot0 + i] = -1;
+                a.scores[slot0 + i] = -INFINITY;
+            }
+        }
+        if (lane == 0) a.xtok[pt][b] = -1;  // (the parity launch 1 reads as "previous")
+    }
+    a.queue[(size_t)b * kWave + lane] = q;
+    if (lane == 0) {
+        if (grow) a.exp_at[slot0 + ecur] = t;
+        a.xtok[pn][b] = xtok_next;
+        a.hslot[pn][b] = hslot_next;
+        if ((xtok_next >= 0 || hslot_next >= 0) && t + 1 < a.T) a.active[t + 1] = 1;
+        if (wait_next && t + 1 < a.T) a.active[a.T + t + 1] = 1;  // its contraction publishes
+        const int nd = new_cur == cur && !pops ? cdepth : pd;
+        const int ntok = new_cur == cur && !pops ? ctok : ptok;
+        const int npar = new_cur == cur && !pops ? cpar : v_par;
+        int32_t* rs = a.rstate + (size_t)b * kStateWords;
+        *reinterpret_cast<i32x4*>(rs) = i32x4{new_cnt, new_cur, qs, (int)flag};
+        *reinterpret_cast<i32x4*>(rs + 4) = i32x4{grow ? ecur : -1, ntok, npar < 0 ? 0 : npar, nd};
+        a.count[b] = new_cnt;
+        a.flags[b] = flag;
+    }
+
+    // ---- ancestor-only mask, at the call's last launch
+    if (t == a.T - 1) {
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        for (int i = lane; i < S; i += kWave) {
+            uint8_t* row = a.mask + ((size_t)b * S + i) * S;
+            u64 bits_lo = 0ull;
+            bool bit64 = false;
+            if (i <= new_cnt) {
+                for (int j = i; j >= 0; j = j == 0 ? -1 : s_par[j]) {
+                    if (j < 64) bits_lo |= 1ull << j;
+                    else bit64 = true;
+                }
+            }
+            for (int j = 0; j < S; ++j)
+                row[j] = (uint8_t)(j < 64 ? ((bits_lo >> j) & 1ull) : (bit64 ? 1 : 0));
+        }
+    }
+}
+
+template <int WM, int RB>
+__global__ __launch_bounds__(kPipeThreads) void pipe_kernel(PipeArgs a, NodeLds lp, int t) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // (16-byte vector accesses)
+    if ((int)blockIdx.x < a.ng) pipe_gate<WM, RB>(a, t, lds);
+    else pipe_node(a, lp, t, lds);
+}
+
 }  // namespace
 
 template <typename T>
@@ -860,6 +1471,50 @@ hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C,
         correct_kernel<float><<<B, kCorrThreads, 0, stream>>>(tidx, tval, (const float*)C, h, pos,
                                                               tok_sorted, lp_sorted, L, H, M, temp);
     return hipGetLastError();
+}
+
+
+PipePlan pipe_plan(int B, int L, int E, int H, int M, int n) {
+    PipePlan p{};
+    if (B < 1 || B > 64 || H > 2 * kPipeThreads || H % 32 || E % 32) return p;  // ng = 0: not applicable
+    // contraction workgroups of 32 units x one K range, and the requests'
+    // node workgroups, together at most one per CU
+    const int groups = H / 32;
+    if (groups + B > 256) return p;
+    p.ksplit = std::min(kMaxKsplit, std::max(1, (256 - B) / groups));
+    p.ng = groups * p.ksplit;
+    p.rb = gate::row_blocks(B);
+    p.xwaves = 0;
+    if (!gate::t32_fits(E / 32, H / 32, p.ksplit, p.rb)) return PipePlan{};  // one weight batch per wave
+    const NodeLds lp = node_lds_plan(L, M, n, H);
+    const size_t node = lp.bytes + (((size_t)n + 1) * 4 + 15) / 16 * 16;  // + the slots' expansion launches
+    const size_t red = (size_t)kPipeWaves * p.rb * 3 * 16 * kRedRow * 4;  // the waves' sums
+    const size_t gates = std::max(gate::t32_act_bytes(E / 32, H / 32, p.ksplit, p.rb), red);
+    p.lds = std::max(node, gates);
+    if (p.lds > kPipeMaxDynLds) return PipePlan{};  // does not fit one CU's LDS
+    return p;
+}
+
+hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, int t, hipStream_t stream,
+                            LaunchEvents ev) {
+    if (a.B == 0) return hipSuccess;
+    const dim3 grid(pp.ng + a.B), block(kPipeThreads);
+    const unsigned shm = (unsigned)pp.lds;
+    const int wm = t == 1 ? 1 : 2;  // launch 1 copies the weights into operand tiles, the later ones read them
+#define DT_PIPE(WM, RB)                                                                                    \
+    if (wm == WM && pp.rb == RB) {                                                                         \
+        static unsigned granted = 0;  /* dynamic LDS bytes allowed so far (grows only) */                \
+        if (shm > granted) {                                                                               \
+            const hipError_t e = hipFuncSetAttribute((const void*)pipe_kernel<WM, RB>,                      \
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm); \
+            if (e != hipSuccess) return e;                                                                 \
+            granted = shm;                                                                                 \
+        }                                                                                                  \
+        return launch_kernel(pipe_kernel<WM, RB>, grid, block, shm, stream, ev, a, lp, t);                 \
+    }
+    DT_PIPE(1, 4) DT_PIPE(2, 4) DT_PIPE(1, 2) DT_PIPE(2, 2) DT_PIPE(1, 1) DT_PIPE(2, 1)
+#undef DT_PIPE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dt

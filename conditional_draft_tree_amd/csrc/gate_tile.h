@@ -1,0 +1,402 @@
+// gate_tile.h -- the GRU gate contraction of one workgroup tile: 16 hidden
+// units x RB x 16 rows x one of `ksplit` K ranges, on bf16 MFMA with binary32
+// accumulation.  Shared by the stepped contraction kernel (gru.hip) and the
+// fused expansion kernel (expand.hip).  Internal; not part of the C ABI.
+//
+// A wave's accumulators: x waves (the token embedding) add into gates
+// (r, z, n) = slots 0, 1, 2; h waves (the state) into (r, z, n) = slots 0,
+// 1, 3 -- slot 2 holds the candidate gate's x part and slot 3 its h part,
+// which the reset gate scales.
+#pragma once
+
+#include "dt_device.h"
+#include "dt_launch.h"
+
+namespace dt {
+namespace gate {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowBlocks = 4;  // up to 4 x 16 rows per workgroup
+// 16-row blocks a workgroup covers: fewer when the batch is small, so that
+// no activation loads are spent on rows past B
+inline int row_blocks(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : kRowBlocks; }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kWaves8 = 8;
+constexpr int kMaxXChunks = 6;  // x chunks per wave and batch
+constexpr int kMaxHChunks = 2;  // h chunks per wave and batch
+// 16-byte loads per lane of an x chunk, and of an h chunk (three activation
+// parts), with rb row blocks
+constexpr int x_chunk_loads(int rb) { return 3 + rb; }
+constexpr int h_chunk_loads(int rb) { return 3 + 3 * rb; }
+
+// Work split.  K is cut into 32-wide chunks: nE chunks of the x part then
+// nH of the h part (three bf16 parts each, so three times the MFMAs and the
+// activation loads).  Each tile of 16 hidden units is covered by ksplit
+// workgroups of 8 waves; in every workgroup the first WX waves take x chunks
+// and the others h chunks, so that every workgroup loads about the same
+// bytes (the bytes a CU loads set the contraction's time).  WX minimizes
+// the larger per-wave load of the two kinds.  A wave issues every load of
+// its chunks (weights and activations) before its first MFMA: one memory
+// round trip.
+inline int x_waves(int nE, int nH, int ksplit, int rb) {
+    if (nH == 0) return kWaves8;
+    if (nE == 0) return 0;
+    int best = 1;
+    long long best_cost = -1;
+    for (int wx = 1; wx < kWaves8; ++wx) {
+        const int nx = ksplit * wx, nh = ksplit * (kWaves8 - wx);
+        const long long cost = max((long long)((nE + nx - 1) / nx) * x_chunk_loads(rb),
+                                   (long long)((nH + nh - 1) / nh) * h_chunk_loads(rb));
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = wx;
+        }
+    }
+    return best;
+}
+// [begin, end) of the chunks of wave w (0 <= w < 8) of K range ks, with wx
+// x waves per workgroup
+__device__ __forceinline__ void wave_chunks(int nE, int nH, int ksplit, int wx, int ks, int w, int& cb, int& ce) {
+    if (w < wx) {
+        const int n = ksplit * wx, i = ks * wx + w;
+        cb = (int)((long long)i * nE / n);
+        ce = (int)((long long)(i + 1) * nE / n);
+    } else {
+        const int n = ksplit * (kWaves8 - wx), i = ks * (kWaves8 - wx) + (w - wx);
+        cb = nE + (int)((long long)i * nH / n);
+        ce = nE + (int)((long long)(i + 1) * nH / n);
+    }
+}
+
+// The accumulators of this wave (8 waves per workgroup) for tile (unit tile
+// ut, row group rg, K range ks).  WM: weight source (0: W_ih / W_hh; 1:
+// those, and write the packed copy; 2: the packed copy), a template parameter
+// so that each variant keeps one address path and no dead store code.  RB:
+// 16-row blocks per workgroup.
+template <int WM, int RB>
+__device__ __forceinline__ void tile_accumulate(const GruGatesArgs& a, int ut, int rg, int ks, f32x4 (&acc)[RB][4]) {
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const int unit = ut * 16 + (lane & 15);
+    const int kq = (lane >> 4) * 8;  // MFMA operand layout: lane l supplies row/column
+                                     // l % 16 with K values 8 * (l / 16) .. + 8
+    const int nE = a.E / 32, nH = a.H / 32;
+    int cbeg, cend;
+    wave_chunks(nE, nH, a.ksplit, a.xwaves, ks, wave, cbeg, cend);
+
+    const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
+    const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
+    const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;  // one gate's rows
+    // packed weights: the 1 KB operand tile (16 units x 32 K) of unit tile ut,
+    // gate g and chunk c (x chunks, then h chunks) is contiguous; lane l's
+    // 16 bytes sit at l * 16 in it (see pack_index_w)
+    constexpr bool wread = WM == 2, wwrite = WM == 1;
+    const size_t wgate = (size_t)(nE + nH) * 512;  // one gate of one unit tile
+    // per-lane base and strides (gate, chunk) of the weight loads, either layout
+    const bf16_t* wpl = (const bf16_t*)a.wpack + pack_index_w(ut, 0, 0, nE + nH) + lane * 8;
+    const bf16_t* wxb = wread ? wpl : wi + kq;
+    const bf16_t* whb = wread ? wpl + (size_t)nE * 512 : wh + kq;
+    const size_t wxg = wread ? wgate : gi, whg = wread ? wgate : gh, wcs = wread ? 512 : 32;
+    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    // packed activations: lane l reads row l % 16 of its row block at K offset
+    // 8 * (l / 16) of a chunk; a wave's read is one contiguous 1 KB block.
+    // Rows past B read the last row (their sums are not stored).
+    const bf16_t* xblk[RB];
+    const bf16_t* hblk[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = min(rg * 64 + rb * 16 + (lane & 15), a.B - 1);
+        xblk[rb] = (const bf16_t*)a.xpack + pack_index_x(r, 0, a.E) + kq;
+        hblk[rb] = (const bf16_t*)a.hpack + pack_index_h(r, 0, 0, a.H) + kq;
+    }
+    const size_t xstep = 16 * 32;                  // one chunk of one block
+    const size_t hpart = (size_t)nH * 16 * 32;     // one part of one block
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (cbeg < nE) {
+        // x part: batches of up to kMaxXChunks chunks, all loads of a batch at once
+        for (int cb = cbeg; cb < cend; cb += kMaxXChunks) {
+            const int n = min(kMaxXChunks, cend - cb);
+            bf16x8 w[kMaxXChunks][3], x[kMaxXChunks][RB];
+#pragma unroll
+            for (int i = 0; i < kMaxXChunks; ++i) {
+                const size_t c = (size_t)(cb + min(i, n - 1));  // clamped: always in bounds
+#pragma unroll
+                for (int g = 0; g < 3; ++g) {  // chunks past n: zero weights (no branch, see below)
+                    const bf16x8 v = load_bf16x8(wxb + g * wxg + c * wcs);
+                    w[i][g] = i < n ? v : zero;
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
+            }
+            // MFMAs for every chunk slot, unconditionally, and no scheduling
+            // across this point: loads sunk next to their MFMAs would wait
+            // one by one (loads complete in order)
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (wwrite) {  // the round's first contraction leaves the packed copy
+#pragma unroll
+                for (int i = 0; i < kMaxXChunks; ++i)
+                    if (i < n)
+#pragma unroll
+                        for (int g = 0; g < 3; ++g)
+                            *reinterpret_cast<u32x4*>((bf16_t*)wpl + g * wgate + (size_t)(cb + i) * 512) =
+                                __builtin_bit_cast(u32x4, w[i][g]);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxXChunks; ++i) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    acc[rb][0] = mfma(x[i][rb], w[i][0], acc[rb][0]);
+                    acc[rb][1] = mfma(x[i][rb], w[i][1], acc[rb][1]);
+                    acc[rb][2] = mfma(x[i][rb], w[i][2], acc[rb][2]);
+                }
+            }
+        }
+    } else {
+        // h part (three exact bf16 parts per state element)
+        for (int cb = cbeg; cb < cend; cb += kMaxHChunks) {
+            const int n = min(kMaxHChunks, cend - cb);
+            bf16x8 w[kMaxHChunks][3], hp[kMaxHChunks][RB][3];
+#pragma unroll
+            for (int i = 0; i < kMaxHChunks; ++i) {
+                const size_t c = (size_t)(cb + min(i, n - 1) - nE);
+#pragma unroll
+                for (int g = 0; g < 3; ++g) {
+                    const bf16x8 v = load_bf16x8(whb + g * whg + c * wcs);
+                    w[i][g] = i < n ? v : zero;
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        hp[i][rb][q] = load_bf16x8(hblk[rb] + q * hpart + c * xstep);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (wwrite) {
+#pragma unroll
+                for (int i = 0; i < kMaxHChunks; ++i)
+                    if (i < n)
+#pragma unroll
+                        for (int g = 0; g < 3; ++g)
+                            *reinterpret_cast<u32x4*>((bf16_t*)wpl + g * wgate + (size_t)(cb + i) * 512) =
+                                __builtin_bit_cast(u32x4, w[i][g]);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxHChunks; ++i) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) {
+                        acc[rb][0] = mfma(hp[i][rb][q], w[i][0], acc[rb][0]);
+                        acc[rb][1] = mfma(hp[i][rb][q], w[i][1], acc[rb][1]);
+                        acc[rb][3] = mfma(hp[i][rb][q], w[i][2], acc[rb][3]);
+                    }
+            }
+        }
+    }
+
+}
+
+// ---- 32-unit tiles with the activations staged in LDS -----------------------
+// A workgroup of 8 waves owns 32 hidden units (unit tiles 2 ug and 2 ug + 1)
+// and K range ks of KS: x chunks [xb, xe) and h chunks [hb, he) (equal
+// shares of nE and of nH).  It copies the range's packed activations (RB row
+// blocks; three parts per h chunk) into LDS once for all its waves, so each
+// activation byte crosses the memory system once per 32 units rather than
+// once per 16.  Wave w takes unit tile w / 4 and, by (w / 2) % 2 and w % 2,
+// the first or second half of the x chunks or of the h chunks: the weights of
+// its chunks are loaded into registers in one batch, issued with the
+// activation copy (one memory round trip), and the activation operands are
+// read from LDS.  Accumulator slots 0, 1, 2 hold gates r, z, n of the wave's
+// kind (x or h), so the x part and the h part stay apart.
+//
+// Chunks per wave: at most t32_xbatch(RB) x chunks or t32_hbatch(RB) h
+// chunks (weights in registers: fewer row blocks leave room for more);
+// t32_fits() is the host's check of a configuration.
+__host__ __device__ constexpr int t32_xbatch(int rb) { return rb == 4 ? 8 : 12; }
+__host__ __device__ constexpr int t32_hbatch(int rb) { return rb == 4 ? 4 : 6; }
+
+// [b, e) of share i of n equal shares of [0, total)
+__host__ __device__ inline void share(int total, int n, int i, int& b, int& e) {
+    b = (int)((long long)i * total / n);
+    e = (int)((long long)(i + 1) * total / n);
+}
+inline bool t32_fits(int nE, int nH, int KS, int rb) {
+    const int nx = (nE + KS - 1) / KS, nh = (nH + KS - 1) / KS;  // largest shares
+    return (nx + 1) / 2 <= t32_xbatch(rb) && (nh + 1) / 2 <= t32_hbatch(rb);
+}
+// Bytes of LDS one workgroup's staged activations take (the largest share).
+inline size_t t32_act_bytes(int nE, int nH, int KS, int rb) {
+    const int nx = (nE + KS - 1) / KS, nh = (nH + KS - 1) / KS;
+    return (size_t)rb * (nx + 3 * nh) * 1024;
+}
+
+// Operand-tile order: lane l of an MFMA operand read takes row l % 16 and K
+// offset 8 (l / 16) of a 1 KB block, i.e. 16-byte vector 4 (l % 16) + l / 16
+// of the block in memory.  The copy puts that vector at position l, so the
+// operand reads are lane-linear in LDS (no bank conflicts).
+__device__ __forceinline__ int t32_src_vector(int p) { return (p & 15) * 4 + (p >> 4); }
+
+template <int WM, int RB>
+__device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ks, int KS, u32x4* sact,
+                                           f32x4 (&acc)[RB][3]) {
+    constexpr int XB = t32_xbatch(RB), HB = t32_hbatch(RB);
+    // (the wave's role and chunk range are wave-uniform: scalar registers)
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
+    const int u = wave >> 2, kind = (wave >> 1) & 1, half = wave & 1;
+    const int ut = ug * 2 + u;
+    const int kq = (lane >> 4) * 8;
+    const int nE = a.E / 32, nH = a.H / 32, nC = nE + nH;
+    int xb, xe, hb, he;
+    share(nE, KS, ks, xb, xe);
+    share(nH, KS, ks, hb, he);
+    const int nxw = xe - xb, nhw = he - hb;
+    // this wave's chunks, numbered within its kind; cg: the kind's first
+    // chunk in the packed weights
+    const int kb = kind ? hb : xb, kn = kind ? nhw : nxw;
+    const int cb = kb + (half ? kn / 2 : 0), n = half ? kn - kn / 2 : kn / 2;
+    const int cg = kind ? nE : 0;
+
+    // ---- weights of the wave's chunks: a wave-uniform base plus a fixed
+    // per-lane byte offset per load
+    const size_t wgate = (size_t)nC * 512;
+    bf16_t* wpl = (bf16_t*)a.wpack + pack_index_w(ut, 0, 0, nC) + lane * 8;
+    const char* wpk = (const char*)a.wpack + pack_index_w(ut, 0, 0, nC) * 2;
+    const int Kk = kind ? a.H : a.E;  // row length of the kind's weight matrix
+    const char* wsrc = (const char*)(kind ? a.W_hh : a.W_ih) + (size_t)ut * 16 * Kk * 2;
+    const unsigned loff = WM == 2 ? (unsigned)lane * 16u : (unsigned)(((lane & 15) * Kk + kq) * 2);
+    // (fully unrolled with constant trip counts: the array stays in registers;
+    // past n, chunk n - 1 is loaded again and its MFMAs are skipped)
+    bf16x8 w[XB][3];
+    auto wload = [&](int i, int g) {
+        const int c = cb + min(i, n - 1);
+        const char* base = WM == 2 ? wpk + (g * wgate + (size_t)(cg + c) * 512) * 2
+                                   : wsrc + ((size_t)g * a.H * Kk + (size_t)c * 32) * 2;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + loff));
+    };
+    if (n > 0 && kind == 0) {
+#pragma unroll
+        for (int i = 0; i < XB; ++i)
+#pragma unroll
+            for (int g = 0; g < 3; ++g) w[i][g] = wload(i, g);
+    } else if (n > 0) {
+#pragma unroll
+        for (int i = 0; i < HB; ++i)
+#pragma unroll
+            for (int g = 0; g < 3; ++g) w[i][g] = wload(i, g);
+    }
+
+    // ---- copy the activations of the range into LDS: x blocks [rb][c], then
+    // h blocks [rb * 3 + q][c], 1 KB each; wave w copies blocks w, w + 8, ...
+    // with global_load_lds_dwordx4 (lane l's 16 bytes land at block + 16 l,
+    // no registers held), and waits for its copies before the barrier
+    const int nbx = RB * nxw, nblk = nbx + RB * 3 * nhw;
+    const u32x4* xp = reinterpret_cast<const u32x4*>(a.xpack);
+    const u32x4* hp = reinterpret_cast<const u32x4*>(a.hpack);
+    const int sv = t32_src_vector(lane);
+    for (int blk = wave; blk < nblk; blk += kWaves8) {
+        const u32x4* src;
+        if (blk < nbx) {
+            int rb = 0, c = blk;
+            while (c >= nxw) {
+                c -= nxw;
+                ++rb;
+            }
+            src = xp + ((size_t)rb * nE + xb + c) * 64;
+        } else {
+            int rq = 0, c = blk - nbx;
+            while (c >= nhw) {
+                c -= nhw;
+                ++rq;
+            }
+            src = hp + ((size_t)rq * nH + hb + c) * 64;
+        }
+        __builtin_amdgcn_global_load_lds(src + sv, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16,
+                                         0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int g = 0; g < 3; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (n <= 0) return;
+    if constexpr (WM == 1) {  // the call's first contraction leaves the packed copy
+#pragma unroll
+        for (int i = 0; i < XB; ++i)
+            if (i < n)  // (uniform)
+#pragma unroll
+                for (int g = 0; g < 3; ++g)
+                    *reinterpret_cast<u32x4*>(wpl + g * wgate + (size_t)(cg + cb + i) * 512) =
+                        __builtin_bit_cast(u32x4, w[i][g]);
+    }
+    // x waves read their operand fragments from LDS one chunk ahead (two
+    // buffers): the MFMAs of chunk i run while chunk i + 1's reads are in
+    // flight.  h waves (three times the fragments per chunk) read a chunk's
+    // fragments together, then run its MFMAs.  The scheduling barrier per
+    // chunk keeps the compiler from hoisting every chunk's reads (their
+    // fragments would all be held in registers).
+    if (kind == 0) {
+        bf16x8 f[2][RB];
+        auto rd = [&](bf16x8 (&d)[RB], int i) {
+            const int c = cb + i - xb;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) d[rb] = __builtin_bit_cast(bf16x8, sact[(rb * nxw + c) * 64 + lane]);
+        };
+        rd(f[0], 0);
+#pragma unroll
+        for (int i = 0; i < XB; ++i) {
+            if (i < n) {  // (uniform)
+                if (i + 1 < n) rd(f[(i + 1) & 1], i + 1);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    acc[rb][0] = mfma(f[i & 1][rb], w[i][0], acc[rb][0]);
+                    acc[rb][1] = mfma(f[i & 1][rb], w[i][1], acc[rb][1]);
+                    acc[rb][2] = mfma(f[i & 1][rb], w[i][2], acc[rb][2]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        const int nvx = nbx * 64;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            if (i < n) {  // (uniform)
+                const int c = cb + i - hb;
+                bf16x8 f[RB][3];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        f[rb][q] = __builtin_bit_cast(bf16x8, sact[nvx + ((rb * 3 + q) * nhw + c) * 64 + lane]);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) {
+                        acc[rb][0] = mfma(f[rb][q], w[i][0], acc[rb][0]);
+                        acc[rb][1] = mfma(f[rb][q], w[i][1], acc[rb][1]);
+                        acc[rb][2] = mfma(f[rb][q], w[i][2], acc[rb][2]);
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+}  // namespace gate
+}  // namespace dt

@@ -21,74 +21,20 @@
 // partial buffer, so the consumer needs no dependent load.
 #include "dt_device.h"
 #include "dt_launch.h"
+#include "gate_tile.h"
 
 namespace dt {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kRowBlocks = 4;  // up to 4 x 16 rows per workgroup
-// 16-row blocks a workgroup covers: fewer when the batch is small, so that
-// no activation loads are spent on rows past B
-inline int row_blocks(int B) { return B <= 16 ? 1 : B <= 32 ? 2 : kRowBlocks; }
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-constexpr int kWaves8 = 8;
-constexpr int kMaxXChunks = 6;  // x chunks per wave and batch
-constexpr int kMaxHChunks = 2;  // h chunks per wave and batch
-// 16-byte loads per lane of an x chunk, and of an h chunk (three activation
-// parts), with rb row blocks
-constexpr int x_chunk_loads(int rb) { return 3 + rb; }
-constexpr int h_chunk_loads(int rb) { return 3 + 3 * rb; }
-
-// Work split.  K is cut into 32-wide chunks: nE chunks of the x part then
-// nH of the h part (three bf16 parts each, so three times the MFMAs and the
-// activation loads).  Each tile of 16 hidden units is covered by ksplit
-// workgroups of 8 waves; in every workgroup the first WX waves take x chunks
-// and the others h chunks, so that every workgroup loads about the same
-// bytes (the bytes a CU loads set the contraction's time).  WX minimizes
-// the larger per-wave load of the two kinds.  A wave issues every load of
-// its chunks (weights and activations) before its first MFMA: one memory
-// round trip.
-inline int x_waves(int nE, int nH, int ksplit, int rb) {
-    if (nH == 0) return kWaves8;
-    if (nE == 0) return 0;
-    int best = 1;
-    long long best_cost = -1;
-    for (int wx = 1; wx < kWaves8; ++wx) {
-        const int nx = ksplit * wx, nh = ksplit * (kWaves8 - wx);
-        const long long cost = max((long long)((nE + nx - 1) / nx) * x_chunk_loads(rb),
-                                   (long long)((nH + nh - 1) / nh) * h_chunk_loads(rb));
-        if (best_cost < 0 || cost < best_cost) {
-            best_cost = cost;
-            best = wx;
-        }
-    }
-    return best;
-}
-// [begin, end) of the chunks of wave w (0 <= w < 8) of K range ks, with wx
-// x waves per workgroup
-__device__ __forceinline__ void wave_chunks(int nE, int nH, int ksplit, int wx, int ks, int w, int& cb, int& ce) {
-    if (w < wx) {
-        const int n = ksplit * wx, i = ks * wx + w;
-        cb = (int)((long long)i * nE / n);
-        ce = (int)((long long)(i + 1) * nE / n);
-    } else {
-        const int n = ksplit * (kWaves8 - wx), i = ks * (kWaves8 - wx) + (w - wx);
-        cb = nE + (int)((long long)i * nH / n);
-        ce = nE + (int)((long long)(i + 1) * nH / n);
-    }
-}
+using gate::bf16x8;
+using gate::f32x4;
+using gate::u32x4;
+using gate::kWaves8;
+using gate::row_blocks;
+using gate::x_waves;
+using gate::kMaxXChunks;
+using gate::kMaxHChunks;
 
 // WM: weight source (0: W_ih / W_hh; 1: those, and write the packed copy; 2:
 // the packed copy), a template parameter so that each variant keeps one
@@ -100,128 +46,8 @@ __global__ __launch_bounds__(kWaves8 * 64) void gru_gates_bf16_kernel(GruGatesAr
     __shared__ f32x4 red[kWaves8][RB * 4][kWave];
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const int ut = blockIdx.x, rg = blockIdx.y, ks = blockIdx.z;
-    const int unit = ut * 16 + (lane & 15);
-    const int kq = (lane >> 4) * 8;  // MFMA operand layout: lane l supplies row/column
-                                     // l % 16 with K values 8 * (l / 16) .. + 8
-    const int nE = a.E / 32, nH = a.H / 32;
-    int cbeg, cend;
-    wave_chunks(nE, nH, a.ksplit, a.xwaves, ks, wave, cbeg, cend);
-
-    const bf16_t* wi = (const bf16_t*)a.W_ih + (size_t)unit * a.E;
-    const bf16_t* wh = (const bf16_t*)a.W_hh + (size_t)unit * a.H;
-    const size_t gi = (size_t)a.H * a.E, gh = (size_t)a.H * a.H;  // one gate's rows
-    // packed weights: the 1 KB operand tile (16 units x 32 K) of unit tile ut,
-    // gate g and chunk c (x chunks, then h chunks) is contiguous; lane l's
-    // 16 bytes sit at l * 16 in it (see pack_index_w)
-    constexpr bool wread = WM == 2, wwrite = WM == 1;
-    const size_t wgate = (size_t)(nE + nH) * 512;  // one gate of one unit tile
-    // per-lane base and strides (gate, chunk) of the weight loads, either layout
-    const bf16_t* wpl = (const bf16_t*)a.wpack + pack_index_w(ut, 0, 0, nE + nH) + lane * 8;
-    const bf16_t* wxb = wread ? wpl : wi + kq;
-    const bf16_t* whb = wread ? wpl + (size_t)nE * 512 : wh + kq;
-    const size_t wxg = wread ? wgate : gi, whg = wread ? wgate : gh, wcs = wread ? 512 : 32;
-    const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    // packed activations: lane l reads row l % 16 of its row block at K offset
-    // 8 * (l / 16) of a chunk; a wave's read is one contiguous 1 KB block.
-    // Rows past B read the last row (their sums are not stored).
-    const bf16_t* xblk[RB];
-    const bf16_t* hblk[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r = min(rg * 64 + rb * 16 + (lane & 15), a.B - 1);
-        xblk[rb] = (const bf16_t*)a.xpack + pack_index_x(r, 0, a.E) + kq;
-        hblk[rb] = (const bf16_t*)a.hpack + pack_index_h(r, 0, 0, a.H) + kq;
-    }
-    const size_t xstep = 16 * 32;                  // one chunk of one block
-    const size_t hpart = (size_t)nH * 16 * 32;     // one part of one block
-
     f32x4 acc[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (cbeg < nE) {
-        // x part: batches of up to kMaxXChunks chunks, all loads of a batch at once
-        for (int cb = cbeg; cb < cend; cb += kMaxXChunks) {
-            const int n = min(kMaxXChunks, cend - cb);
-            bf16x8 w[kMaxXChunks][3], x[kMaxXChunks][RB];
-#pragma unroll
-            for (int i = 0; i < kMaxXChunks; ++i) {
-                const size_t c = (size_t)(cb + min(i, n - 1));  // clamped: always in bounds
-#pragma unroll
-                for (int g = 0; g < 3; ++g) {  // chunks past n: zero weights (no branch, see below)
-                    const bf16x8 v = load_bf16x8(wxb + g * wxg + c * wcs);
-                    w[i][g] = i < n ? v : zero;
-                }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) x[i][rb] = load_bf16x8(xblk[rb] + c * xstep);
-            }
-            // MFMAs for every chunk slot, unconditionally, and no scheduling
-            // across this point: loads sunk next to their MFMAs would wait
-            // one by one (loads complete in order)
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (wwrite) {  // the round's first contraction leaves the packed copy
-#pragma unroll
-                for (int i = 0; i < kMaxXChunks; ++i)
-                    if (i < n)
-#pragma unroll
-                        for (int g = 0; g < 3; ++g)
-                            *reinterpret_cast<u32x4*>((bf16_t*)wpl + g * wgate + (size_t)(cb + i) * 512) =
-                                __builtin_bit_cast(u32x4, w[i][g]);
-            }
-#pragma unroll
-            for (int i = 0; i < kMaxXChunks; ++i) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    acc[rb][0] = mfma(x[i][rb], w[i][0], acc[rb][0]);
-                    acc[rb][1] = mfma(x[i][rb], w[i][1], acc[rb][1]);
-                    acc[rb][2] = mfma(x[i][rb], w[i][2], acc[rb][2]);
-                }
-            }
-        }
-    } else {
-        // h part (three exact bf16 parts per state element)
-        for (int cb = cbeg; cb < cend; cb += kMaxHChunks) {
-            const int n = min(kMaxHChunks, cend - cb);
-            bf16x8 w[kMaxHChunks][3], hp[kMaxHChunks][RB][3];
-#pragma unroll
-            for (int i = 0; i < kMaxHChunks; ++i) {
-                const size_t c = (size_t)(cb + min(i, n - 1) - nE);
-#pragma unroll
-                for (int g = 0; g < 3; ++g) {
-                    const bf16x8 v = load_bf16x8(whb + g * whg + c * wcs);
-                    w[i][g] = i < n ? v : zero;
-                }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int q = 0; q < 3; ++q)
-                        hp[i][rb][q] = load_bf16x8(hblk[rb] + q * hpart + c * xstep);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (wwrite) {
-#pragma unroll
-                for (int i = 0; i < kMaxHChunks; ++i)
-                    if (i < n)
-#pragma unroll
-                        for (int g = 0; g < 3; ++g)
-                            *reinterpret_cast<u32x4*>((bf16_t*)wpl + g * wgate + (size_t)(cb + i) * 512) =
-                                __builtin_bit_cast(u32x4, w[i][g]);
-            }
-#pragma unroll
-            for (int i = 0; i < kMaxHChunks; ++i) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int q = 0; q < 3; ++q) {
-                        acc[rb][0] = mfma(hp[i][rb][q], w[i][0], acc[rb][0]);
-                        acc[rb][1] = mfma(hp[i][rb][q], w[i][1], acc[rb][1]);
-                        acc[rb][3] = mfma(hp[i][rb][q], w[i][2], acc[rb][3]);
-                    }
-            }
-        }
-    }
+    gate::tile_accumulate<WM, RB>(a, ut, rg, ks, acc);
 
     // the 8 waves' sums added in wave order (one LDS round trip); all 512
     // threads write the workgroup's partial sums

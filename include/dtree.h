@@ -70,14 +70,24 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *                leave the softmax scope open: [captcha] "Key findings",
  *                "Methodology -- deep read").  Applies to dt_build and
  *                dt_build_marginal.
+ *   expand       how dt_build runs the expansion steps (same trees either
+ *                way, up to binary32 rounding order of the GRU gate sums):
+ *                DT_EXPAND_AUTO (0) fused where supported, else stepped;
+ *                DT_EXPAND_STEPPED (1) two launches per step, the batched
+ *                GRU contraction then the node step; DT_EXPAND_FUSED (2) one
+ *                launch per step in which the contraction of the rows the
+ *                requests need next runs beside the node steps (bf16, B <= 64,
+ *                H <= 1024; otherwise dt_create returns DT_ERR_UNSUPPORTED).
  * A request's expansion state lives in one workgroup's LDS: configurations with
  * 4 H + 8 L M + 512 n bytes (plus ~0.8 KiB) above 64 KiB are DT_ERR_UNSUPPORTED. */
+typedef enum { DT_EXPAND_AUTO = 0, DT_EXPAND_STEPPED = 1, DT_EXPAND_FUSED = 2 } dt_expand;
 typedef struct {
     int32_t B, L, V, E, H, M, n;
     float temperature;
     dt_dtype dtype;
     float near_tie_eps;
     int32_t full_vocab;
+    int32_t expand;
 } dt_config;
 
 typedef struct dt_handle dt_handle; /* opaque: configuration, launch plan, timing events */
@@ -91,6 +101,11 @@ void dt_destroy(dt_handle *h);
 /* Device workspace bytes dt_build needs for this handle (caller allocates,
  * 256-byte aligned).  dt_topm and dt_gru_step need no more than this. */
 size_t dt_workspace_bytes(const dt_handle *h);
+
+/* The expansion dt_build runs for this handle: DT_EXPAND_FUSED or
+ * DT_EXPAND_STEPPED (DT_EXPAND_AUTO resolved from the configuration); -1 for a
+ * NULL handle.  Host only. */
+int32_t dt_expand_mode(const dt_handle *h);
 
 const char *dt_status_string(dt_status s);
 /* Last error message of `h` (or of the last failed dt_create when h is NULL). */
@@ -142,7 +157,9 @@ const char *dt_last_error(const dt_handle *h);
  *                       eps are such a pop, and the last pop's comparison
  *                       covers the final node set: every decision whose
  *                       outcome rounding could change sets this one bit.
- *                       Other bits are 0.
+ *                       Bit 31: (fused expansion) a wait for a launch's
+ *                       contraction gave up after its bounded spin; the tree
+ *                       is then not valid.  Other bits are 0.
  * workspace: device buffer of at least dt_workspace_bytes(h) bytes.
  */
 dt_status dt_build(dt_handle *h, void *workspace, size_t ws_bytes, const void *base_logits,
@@ -313,6 +330,8 @@ dt_status dt_accept_greedy(dt_handle *h, const int32_t *tokens, const int32_t *p
  *   stage 4  the whole call
  *   stage 5  GRU gate contraction, every launch separately (level 2)
  *   stage 6  the dt_accept_greedy kernel (one launch per call)
+ *   stage 7  fused expansion launches of the call, summed  (level 2)
+ *   stage 8  fused expansion, every launch separately      (level 2)
  * Timing calls are host-side and need the handle's device to be current.
  */
 dt_status dt_timing_enable(dt_handle *h, int level, int capacity);

@@ -194,7 +194,35 @@ def test_timing_argument_checks():
     assert lib.dt_timing_enable(h, 0, 0) == 0
     n = C.c_int(0)
     assert lib.dt_timing_read(h, 9, None, 0, C.byref(n)) == -1
-    assert lib.dt_timing_read(h, 7, None, 0, C.byref(n)) == -1
+    assert lib.dt_timing_read(h, 9, None, 0, C.byref(n)) == -1
+    assert lib.dt_timing_read(h, -1, None, 0, C.byref(n)) == -1
+    assert lib.dt_timing_read(h, 8, None, 0, C.byref(n)) == 0 and n.value == 0
     assert lib.dt_timing_read(h, 0, None, 0, C.byref(n)) == 0 and n.value == 0
     assert lib.dt_timing_read(h, 6, None, 0, C.byref(n)) == 0 and n.value == 0
     dtree.dt_destroy(h)
+
+
+def test_expand_mode_is_validated():
+    lib = dtree.load_library()
+    out = C.c_void_p()
+    bad = dt_config(2, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_BF16, 1e-5, 0, 3)
+    assert lib.dt_create(C.byref(bad), C.byref(out)) == -1 and not out.value
+    assert "expand" in dtree.dt_last_error(None)
+    # the fused expansion is bf16 with at most 64 requests and H <= 1024
+    for kw in (dict(dtype=dtree.DT_F32), dict(B=65), dict(H=2048)):
+        with pytest.raises(ValueError, match="UNSUPPORTED"):
+            make(expand=dtree.DT_EXPAND_FUSED, **kw)
+    # the mode dt_build runs: auto resolves to fused where it applies
+    for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_FUSED), (dtree.DT_EXPAND_STEPPED, dtree.DT_EXPAND_STEPPED),
+                    (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_FUSED)):
+        h = make(expand=e)
+        assert dtree.dt_expand_mode(h) == want
+        dtree.dt_destroy(h)
+    for kw in (dict(dtype=dtree.DT_F32), dict(B=65), dict(H=2048)):
+        h = make(**kw)
+        assert dtree.dt_expand_mode(h) == dtree.DT_EXPAND_STEPPED
+        dtree.dt_destroy(h)
+    assert lib.dt_expand_mode(None) == -1
+    # the fused expansion's workspace holds its per-slot gate sums besides the stepped path's
+    assert dtree.dt_workspace_bytes(make(expand=dtree.DT_EXPAND_FUSED)) > \
+        dtree.dt_workspace_bytes(make(expand=dtree.DT_EXPAND_STEPPED))

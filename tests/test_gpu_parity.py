@@ -45,7 +45,14 @@ def inputs(name, variant="default", over=()):
 
 def builder(cfg, eps=1e-5):
     return dtree.Builder(cfg["B"], cfg["L"], cfg["V"], cfg["E"], cfg["H"], cfg["M"], cfg["n"],
-                         cfg["T"], cfg["dtype"], eps, device=DEV, full_vocab=cfg.get("full_vocab", False))
+                         cfg["T"], cfg["dtype"], eps, device=DEV, full_vocab=cfg.get("full_vocab", False),
+                         expand=cfg.get("expand", dtree.DT_EXPAND_AUTO))
+
+
+# dt_build's two ways of running the expansion: "auto" takes the fused
+# launches wherever they apply (bf16, B <= 64, H <= 1024), "stepped" forces two
+# launches per step; the whole-build tests run both where both apply
+EXPAND = {"auto": dtree.DT_EXPAND_AUTO, "stepped": dtree.DT_EXPAND_STEPPED}
 
 
 # The "strong" variant (h0 ~ N(0, 1), C scaled by 10) makes corrected logits
@@ -83,7 +90,8 @@ def build_and_compare(cfg, inp, requests=None, threads=THREADS, eps=1e-5, tol=SC
     B = cfg["B"]
     reqs = list(range(B)) if requests is None else list(requests)
     say(f"  build B={B} V={cfg['V']} L={cfg['L']} E={cfg['E']} H={cfg['H']} M={cfg['M']} "
-        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']} eps={eps} full_vocab={cfg.get('full_vocab', False)}")
+        f"n={cfg['n']} {cfg['dtype']} T={cfg['T']} eps={eps} full_vocab={cfg.get('full_vocab', False)} "
+        f"expand={cfg.get('expand', 0)}")
     bld = builder(cfg, eps)
     got = run_build(bld, S.to_torch(inp, DEV))
     for b in range(B):
@@ -227,14 +235,15 @@ def test_build_bf16_ragged(variant):
                       **(STRONG if variant == "strong" else {}))
 
 
+@pytest.mark.parametrize("mode", list(EXPAND))
 @pytest.mark.parametrize("B", [16, 17, 32, 33])
-def test_build_bf16_row_blocks(B):
+def test_build_bf16_row_blocks(B, mode):
     # whole builds at the contraction's row-block boundaries: one 16-row block
     # per workgroup up to 16 rows, two up to 32, four above (ragged tails at
     # 17 and 33)
     cfg = dict(B=B, V=5003, L=16, E=256, H=128, M=64, n=16, dtype="bf16", alpha=1.5, T=0.0)
     inp = S.make_inputs(cfg, seed=11, variant="strong")
-    build_and_compare(cfg, inp, requests=range(B), **STRONG)
+    build_and_compare(dict(cfg, expand=EXPAND[mode]), inp, requests=range(B), **STRONG)
 
 
 @pytest.mark.parametrize("dtype,H,E,variant", [("bf16", 2048, 64, "strong"), ("bf16", 4096, 96, "default"),
@@ -247,13 +256,16 @@ def test_build_wide_state(dtype, H, E, variant):
     build_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
 
 
-def test_build_qwen3_4b_single():
+@pytest.mark.parametrize("mode", list(EXPAND))
+def test_build_qwen3_4b_single(mode):
     cfg, inp = inputs("qwen3_4b_single")
-    build_and_compare(cfg, inp)
+    build_and_compare(dict(cfg, expand=EXPAND[mode]), inp)
 
 
-def test_build_qwen3_4b_batched_and_rerun_identical():
+@pytest.mark.parametrize("mode", list(EXPAND))
+def test_build_qwen3_4b_batched_and_rerun_identical(mode):
     cfg, inp = inputs("qwen3_4b_batched")
+    cfg = dict(cfg, expand=EXPAND[mode])
     got, _, _ = build_and_compare(cfg, inp)  # all 64 requests
     bld = builder(cfg)
     again = run_build(bld, S.to_torch(inp, DEV))
@@ -262,14 +274,16 @@ def test_build_qwen3_4b_batched_and_rerun_identical():
         np.testing.assert_array_equal(got[k], again[k], err_msg=f"rerun differs in {k}")
 
 
-def test_build_qwen3_4b_batched_strong_correction():
+@pytest.mark.parametrize("mode", list(EXPAND))
+def test_build_qwen3_4b_batched_strong_correction(mode):
     cfg, inp = inputs("qwen3_4b_batched", "strong")
-    build_and_compare(cfg, inp, **STRONG)
+    build_and_compare(dict(cfg, expand=EXPAND[mode]), inp, **STRONG)
 
 
-def test_build_qwen3_8b():
+@pytest.mark.parametrize("mode", list(EXPAND))
+def test_build_qwen3_8b(mode):
     cfg, inp = inputs("qwen3_8b")
-    build_and_compare(cfg, inp)  # all 32 requests
+    build_and_compare(dict(cfg, expand=EXPAND[mode]), inp)  # all 32 requests
 
 
 def test_build_stress():
@@ -574,9 +588,10 @@ def test_full_vocab_bf16_ragged():
     build_and_compare(cfg, inp)
 
 
-def test_full_vocab_qwen3_4b_batched():
+@pytest.mark.parametrize("mode", list(EXPAND))
+def test_full_vocab_qwen3_4b_batched(mode):
     cfg, inp = inputs("qwen3_4b_batched")
-    cfg = dict(cfg, full_vocab=True)
+    cfg = dict(cfg, full_vocab=True, expand=EXPAND[mode])
     build_and_compare(cfg, inp)  # all 64 requests
 
 
@@ -590,14 +605,16 @@ def test_full_vocab_marginal_matches_oracle():
 
 # ---- the 256-wide correction head ---------------------------------------------------
 
-def test_build_head256():
+@pytest.mark.parametrize("mode", list(EXPAND))
+def test_build_head256(mode):
     cfg, inp = inputs("qwen3_4b_head256")
-    build_and_compare(cfg, inp)  # all 64 requests
+    build_and_compare(dict(cfg, expand=EXPAND[mode]), inp)  # all 64 requests
 
 
+@pytest.mark.parametrize("mode", list(EXPAND))
 @pytest.mark.parametrize("variant", ["default", "strong"])
-def test_build_head256_small(variant):
-    cfg = dict(B=9, V=5003, L=16, E=256, H=256, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0)
+def test_build_head256_small(variant, mode):
+    cfg = dict(B=9, V=5003, L=16, E=256, H=256, M=64, n=16, dtype="bf16", alpha=1.1, T=0.0, expand=EXPAND[mode])
     inp = S.make_inputs(cfg, seed=17, variant=variant)
     build_and_compare(cfg, inp, **(STRONG if variant == "strong" else {}))
 
@@ -725,13 +742,15 @@ def test_build_side_stream_and_graph_replay():
 
 # ------------------------------------------------------- the position limit --
 
-@pytest.mark.parametrize("mode", ["standard", "marginal", "full_vocab"])
+@pytest.mark.parametrize("mode", ["standard", "stepped", "marginal", "full_vocab"])
 def test_build_max_positions(mode):
     # L = 64 positions (the limit): depths up to n in the queue keys, the whole
     # L x M table staged per step, every row's tail (full-vocabulary mode);
-    # very peaked logits (Zipf alpha = 6) grow chains n nodes deep
+    # very peaked logits (Zipf alpha = 6) grow chains n nodes deep (in the
+    # fused expansion nearly every pop takes the newest child: waits)
     cfg = dict(B=5, V=4099, L=64, E=64, H=96, M=32, n=32, dtype="bf16", alpha=6.0, T=0.0,
-               full_vocab=mode == "full_vocab")
+               full_vocab=mode == "full_vocab",
+               expand=EXPAND["stepped"] if mode == "stepped" else EXPAND["auto"])
     inp = S.make_inputs(cfg, seed=11)
     if mode == "marginal":
         got = marginal_and_compare(cfg, inp, requests=range(cfg["B"]))

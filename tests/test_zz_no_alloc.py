@@ -21,8 +21,10 @@ KEYS = ("tokens", "parents", "depths", "scores", "mask", "count", "flags")
 
 
 def _builder(cfg, B):
+    # dt_build_noalloc runs the stepped expansion; dt_build of the same handle
+    # is made to run it too, so the two are compared bit for bit
     return dtree.Builder(B, cfg["L"], cfg["V"], cfg["E"], cfg["H"], cfg["M"], cfg["n"], cfg["T"], cfg["dtype"],
-                         1e-5, device=DEV)
+                         1e-5, device=DEV, expand=dtree.DT_EXPAND_STEPPED)
 
 
 def _noalloc(bld, t):
