@@ -123,9 +123,8 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true,
     l.tail_part = take(B * L * (size_t)nseg * 2 * 4);  // its per-segment (m, s) sums
     l.wpack = take(wtiles && c.dtype == DT_BF16 ? (size_t)3 * H * (c.E + c.H) * 2 : 0);  // weights in operand tiles
     const bool fp = pp.ng > 0;
-    const size_t pks = fp ? (size_t)pp.ksplit : 0;
-    l.p_gi = take(2 * pks * B * 3 * H * 4);           // x-part gate sums by launch parity
-    l.p_gh = take(B * S * pks * 3 * H * 4);           // h-part gate sums per slot
+    l.p_gi = take(fp ? 2 * (size_t)pp.ksx * B * 3 * H * 4 : 0);  // x-part gate sums by launch parity
+    l.p_gh = take(fp ? B * S * (size_t)pp.ksh * 3 * H * 4 : 0);  // h-part gate sums per slot
     l.p_hstate = take(fp ? B * S * H * 4 : 0);        // binary32 state per slot
     l.p_exp = take(fp ? B * S * 4 : 0);               // launch that expanded each slot
     l.p_done = take(fp ? (size_t)pT * 4 : 0);         // per-launch counters
@@ -609,7 +608,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         dt::PipeArgs pa{};
         pa.B = c.B; pa.L = c.L; pa.V = c.V; pa.E = c.E; pa.H = c.H; pa.M = c.M; pa.n = c.n;
         pa.T = h->pipe_T;
-        pa.ng = h->pp.ng; pa.ksplit = h->pp.ksplit; pa.xwaves = h->pp.xwaves;
+        pa.ng = h->pp.ng; pa.ksx = h->pp.ksx; pa.ksh = h->pp.ksh;
         pa.temp = c.temperature; pa.eps = c.near_tie_eps;
         pa.C = C; pa.h0 = h0; pa.tidx = tidx; pa.tval = tval; pa.tail = tail;
         pa.emb = emb; pa.W_ih = W_ih; pa.W_hh = W_hh; pa.b_ih = b_ih; pa.b_hh = b_hh;

@@ -170,7 +170,8 @@ hipError_t launch_marginal_build(const NodeArgs& a, const NodeLds& lp, hipStream
 struct PipeArgs {
     int B, L, V, E, H, M, n;
     int T;                // launches per call
-    int ng, ksplit, xwaves;
+    int ng;               // contraction workgroups (blocks 0 .. ng - 1)
+    int ksx, ksh;         // partial sums of a gate's x part, of its h part
     float temp, eps;
     const void* C;
     const float* h0;
@@ -187,8 +188,8 @@ struct PipeArgs {
     uint16_t* hpack[2];
     int32_t* xtok[2];     // [B] token of launch t's x row (parity t & 1), -1 = none
     int32_t* hslot[2];    // [B] slot whose state is launch t's h row, -1 = none
-    float* gi;            // [2][ksplit][B][3][H] x-part gate sums by launch parity
-    float* gh;            // [B][n+1][ksplit][3][H] h-part gate sums per slot
+    float* gi;            // [2][ksx][B][3][H] x-part gate sums by launch parity
+    float* gh;            // [B][n+1][ksh][3][H] h-part gate sums per slot
     float* hstate;        // [B][n+1][H] binary32 state per slot (slot 0 = h0)
     int32_t* exp_at;      // [B][n+1] launch that expanded the slot
     unsigned* done;       // [T] contraction workgroups finished, per launch
@@ -213,7 +214,7 @@ struct PipeArgs {
 // Launch geometry of the fused expansion for a configuration, or ng = 0 when
 // it does not apply (binary32, the factorized mode, too many requests).
 struct PipePlan {
-    int ng, ksplit, xwaves, rb;
+    int ng, ksx, ksh, rb;
     size_t lds;  // dynamic LDS bytes
 };
 PipePlan pipe_plan(int B, int L, int E, int H, int M, int n);

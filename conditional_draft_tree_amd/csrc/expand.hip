@@ -845,8 +845,8 @@ __global__ __launch_bounds__(kCorrThreads) void correct_kernel(const int32_t* ti
 // ============================================================================
 
 constexpr int kPipeThreads = 512;
-constexpr int kMaxB = 64;  // requests of a fused call
-constexpr int kRedRow = 20;  // floats per row of the contraction's sums in LDS (16 units + padding)
+constexpr int kMaxB = 64;      // requests of a fused call
+constexpr int kPipeMaxKs = 3;  // partial sums per kind (x part, h part) of a gate sum
 constexpr int kPipeWaves = kPipeThreads / kWave;    // 8
 constexpr int kPipeRows = kMaxM / kPipeWaves;       // 8 gathered rows per wave
 constexpr unsigned kPipeSpinLimit = 1u << 18;       // bounded wait for a launch's contraction (~0.3 s)
@@ -854,6 +854,13 @@ constexpr uint32_t kPipeTimeoutFlag = 0x80000000u;  // flags bit: such a wait ti
 // dynamic LDS a fused launch may take: a CU's 160 KB less the static
 // variables of the node role (and headroom)
 constexpr size_t kPipeMaxDynLds = 160 * 1024 - 256;
+
+// Buffer p[i] of a launch-parity pair, by selection: indexing the kernel
+// argument's array with a run-time index would copy the argument to scratch.
+template <typename P>
+__device__ __forceinline__ P by_parity(P const (&p)[2], int i) {
+    return i ? p[1] : p[0];
+}
 
 // Agent-scope loads (coherent across XCDs) of the gate sums that a waiting
 // node workgroup reads in the launch that computes them.
@@ -878,7 +885,8 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
         return;
     }
     const int groups = a.H / 32;
-    const int ug = (int)blockIdx.x % groups, ks = (int)blockIdx.x / groups;
+    const int ug = (int)blockIdx.x % groups, kw = (int)blockIdx.x / groups;
+    const int kind = kw >= a.ksx, ksub = kind ? kw - a.ksx : kw, nsub = kind ? a.ksh : a.ksx;
     const int par = t & 1, S = a.n + 1;
     // this launch's flags: some row needs the contraction (launch 1 always
     // has rows); some request waits for its sums in this launch, so they are
@@ -888,58 +896,59 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
     // (its inputs are always in bounds; without rows nothing is stored).
     const int act = a.active[t], publish = a.active[a.T + t];
     __shared__ int s_hsl[kMaxB];  // each row's state slot (ordered by the tile's barrier)
-    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = a.hslot[par][threadIdx.x];
+    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = by_parity(a.hslot, par)[threadIdx.x];
     GruGatesArgs g{};
-    g.xpack = a.xpack[par];
-    g.hpack = a.hpack[par];
+    g.xpack = by_parity(a.xpack, par);
+    g.hpack = by_parity(a.hpack, par);
     g.W_ih = a.W_ih;
     g.W_hh = a.W_hh;
     g.B = a.B;
     g.E = a.E;
     g.H = a.H;
-    g.ksplit = a.ksplit;
+    g.ksplit = 1;  // (unused by this tile)
     g.dtype = 1;
     g.wpack = a.wpack;
     g.wmode = WM;
     gate::f32x4 acc[RB][3];
-    gate::tile32_lds<WM, RB>(g, ug, ks, a.ksplit, reinterpret_cast<gate::u32x4*>(lds), acc);
+    gate::tile32_lds<WM, RB>(g, ug, kind, ksub, nsub, reinterpret_cast<gate::u32x4*>(lds), acc);
     __syncthreads();  // every wave is done with the staged activations
-    // the waves' sums into LDS as [wave][rb][slot][row of 16][unit of 16],
-    // rows padded to kRedRow floats (the four row groups of a write fall in
-    // different banks); MFMA output lane l holds unit l % 16 of rows
-    // 4 (l / 16) + e
-    const int wave = (int)threadIdx.x / kWave, lane = lane_id();
+    // the four quarters of each unit tile (waves 4 u + 0 .. 3) are added in
+    // order: quarters 1 .. 3 leave their sums in LDS ([u][quarter - 1][rb * 3
+    // + slot][lane]), quarter 0 adds them to its own and stores.  Lane l holds
+    // units 4 (l / 16) .. + 3 of row l % 16 of each row block.
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
+    const int u = wave / gate::kT32Quarters, qt = wave % gate::kT32Quarters;
+    gate::f32x4* red = reinterpret_cast<gate::f32x4*>(lds);
+    if (qt != 0) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int sl = 0; sl < 3; ++sl)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                lds[(((wave * RB + rb) * 3 + sl) * 16 + (lane >> 4) * 4 + e) * kRedRow + (lane & 15)] = acc[rb][sl][e];
+            for (int sl = 0; sl < 3; ++sl)
+                red[(((u * 3 + qt - 1) * RB + rb) * 3 + sl) * kWave + lane] = acc[rb][sl];
+    }
     __syncthreads();
-    if (t == 1 || act != 0) {
-        // outputs: (kind, slot, row, 4 consecutive units) per 16-byte store; a
-        // wave covers 8 rows x 32 units (128 contiguous bytes per row).  The
-        // halves of a kind (waves 4 u + 2 kind + 0, 1) are added first half first.
-        for (int idx = (int)threadIdx.x; idx < 2 * 3 * a.B * 8; idx += kPipeThreads) {
-            const int u4 = idx & 7, r = idx >> 3;
-            const int row = r % a.B, ksl = r / a.B, sl = ksl % 3, kind = ksl / 3;
-            const int u = u4 >> 2, rb = row >> 4, r16 = row & 15, c16 = (u4 & 3) * 4;
-            const int w0 = u * 4 + kind * 2;
-            const gate::f32x4 v0 =
-                *reinterpret_cast<const gate::f32x4*>(lds + (((w0 * RB + rb) * 3 + sl) * 16 + r16) * kRedRow + c16);
-            const gate::f32x4 v1 = *reinterpret_cast<const gate::f32x4*>(
-                lds + ((((w0 + 1) * RB + rb) * 3 + sl) * 16 + r16) * kRedRow + c16);
-            const gate::f32x4 sum = v0 + v1;
-            const int unit = ug * 32 + u4 * 4;
-            if (kind == 0) {
-                *reinterpret_cast<gate::f32x4*>(a.gi + (((size_t)(par * a.ksplit + ks) * a.B + row) * 3 + sl) * a.H +
-                                                unit) = sum;
-            } else {
-                const int hsl = s_hsl[row];
-                if (hsl >= 0 && hsl < S)
-                    *reinterpret_cast<gate::f32x4*>(
-                        a.gh + ((((size_t)row * S + hsl) * a.ksplit + ks) * 3 + sl) * a.H + unit) = sum;
+    if (qt == 0 && (t == 1 || act != 0)) {
+        // (the fields are read into values first: selecting between fields of
+        // the kernel argument would copy the argument to scratch)
+        float* const gi = a.gi;
+        float* const gh = a.gh;
+        const int B = a.B, H = a.H, ksx = a.ksx, ksh = a.ksh;
+        const int unit = ug * 32 + u * 16 + (lane >> 4) * 4;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = rb * 16 + (lane & 15);
+            const int hsl = kind ? s_hsl[min(row, B - 1)] : 0;
+            const bool ok = row < B && (kind == 0 || (hsl >= 0 && hsl < S));
+#pragma unroll
+            for (int sl = 0; sl < 3; ++sl) {
+                gate::f32x4 sum = acc[rb][sl];
+#pragma unroll
+                for (int q = 0; q < gate::kT32Quarters - 1; ++q)
+                    sum += red[(((u * 3 + q) * RB + rb) * 3 + sl) * kWave + lane];
+                if (!ok) continue;
+                float* dst = kind == 0 ? gi + (((size_t)(par * ksx + ksub) * B + row) * 3 + sl) * H + unit
+                                       : gh + ((((size_t)row * S + hsl) * ksh + ksub) * 3 + sl) * H + unit;
+                *reinterpret_cast<gate::f32x4*>(dst) = sum;
             }
         }
     }
@@ -980,14 +989,14 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     const int S = a.n + 1, H = a.H, M = a.M, LM = a.L * a.M;
     const size_t slot0 = (size_t)b * S;
     const int pt = t & 1, pn = (t + 1) & 1;  // this launch's parity; the next's (= the previous one's)
-    const int KS = a.ksplit;
+    const int KSX = a.ksx, KSH = a.ksh;  // partial sums of the x part and of the h part
 
     // ---- round trip 1 (every address valid in every mode)
     const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
     const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
     const u64 q_m = a.queue[(size_t)b * kWave + lane];
-    const int xt_prev = a.xtok[pn][b];  // launch t-1's x row
-    const int xt_cur = a.xtok[pt][b];   // this launch's x row
+    const int xt_prev = by_parity(a.xtok, pn)[b];  // launch t-1's x row
+    const int xt_cur = by_parity(a.xtok, pt)[b];   // this launch's x row
     const int jl = min(lane, M - 1);
     const int32_t* ip = t == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
     const float* vp = t == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
@@ -996,20 +1005,24 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     // this thread's state elements k1 and k1 + NT (H <= 2 NT)
     const int k1 = (int)threadIdx.x, k2 = k1 + NT;
     const int kc1 = k1 < H ? k1 : 0, kc2 = k2 < H ? k2 : 0;
-    float gi[2][kMaxKsplit][3];
+    float gi[2][kPipeMaxKs][3];
 #pragma unroll
-    for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+    for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
 #pragma unroll
         for (int g = 0; g < 3; ++g) {
-            const size_t base = (((size_t)(pn * KS + min(s2, KS - 1)) * a.B + b) * 3 + g) * H;
+            const size_t base = (((size_t)(pn * KSX + min(s2, KSX - 1)) * a.B + b) * 3 + g) * H;
             gi[0][s2][g] = a.gi[base + kc1];
             gi[1][s2][g] = a.gi[base + kc2];
         }
+    // (loads without branches, from a stand-in address when a pointer is
+    // NULL, so that every path issues the same loads: the in-order load
+    // counters then let round trip 2 wait for exactly what it needs)
     float bias[2][6];
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
         const void* bp = g < 3 ? a.b_ih : a.b_hh;
-        const bf16_t* src = bp ? (const bf16_t*)bp : (const bf16_t*)a.tidx;  // any valid address
+        // stand-in: W_ih, [3H, E] with E >= 1, holds at least 3H elements
+        const bf16_t* src = bp ? (const bf16_t*)bp : (const bf16_t*)a.W_ih;
         const float v1 = load1<bf16_t>(src + (size_t)(g % 3) * H + kc1);
         const float v2 = load1<bf16_t>(src + (size_t)(g % 3) * H + kc2);
         bias[0][g] = bp ? v1 : 0.f;
@@ -1017,7 +1030,8 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     }
     float h0v[2] = {0.f, 0.f};
     {
-        const float* h0p = a.h0 ? a.h0 + (size_t)b * H : a.tval;
+        // stand-in: the per-slot states, [B][n + 1][H], hold row b
+        const float* h0p = (a.h0 ? a.h0 : a.hstate) + (size_t)b * H;
         const float v1 = h0p[kc1], v2 = h0p[kc2];
         h0v[0] = a.h0 ? v1 : 0.f;
         h0v[1] = a.h0 ? v2 : 0.f;
@@ -1064,14 +1078,16 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     const int unsorted = t == 0 || rs1[0] < 0 || rs1[0] >= a.n ? -1 : rs1[0];
     const int ctok = t == 0 ? -1 : rs1[1];
     const int cpar = t == 0 ? -1 : min(max(rs1[2], 0), a.n);
-    const int cdepth = t == 0 ? 0 : rs1[3];
+    const int cdepth = t == 0 ? 0 : (rs1[3] & 0xffff);
+    // launch that expanded cur's parent (recorded at cur's pop)
+    const int pexp = t == 0 ? 0 : (int)((unsigned)rs1[3] >> 16);
     u64 q = t == 0 ? 0ull : q_m;
     // a node to expand (its GRU inputs may not be ready yet): its correction
     // rows are gathered at once, whatever the readiness turns out to be
     const bool cand = t > 0 && cnt < a.n && cur >= 0 && cdepth < a.L;
 
-    // ---- round trip 2: the gathered correction rows, the parent's gh, state
-    // and expansion launch
+    // ---- round trip 2: the gathered correction rows (first: the critical
+    // path runs through them), the parent's gh and state, the unsorted keys
     u32x4 cv[RW][2];
     auto gather = [&](int k0) {
         const int ka = min(k0 + lane * P, H - P), kb = min(k0 + (kWave + lane) * P, H - P);
@@ -1085,19 +1101,18 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     };
     if (t == 0 || cand) gather(0);
     const int cp = t == 0 ? 0 : cpar;
-    const int pexp = a.exp_at[slot0 + cp];
-    float gh[2][kMaxKsplit][3];
+    float gh[2][kPipeMaxKs][3];
     float hp[2];
+    const float* ghp = a.gh + (slot0 + cp) * (size_t)KSH * 3 * H;
+#pragma unroll
+    for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
+#pragma unroll
+        for (int g = 0; g < 3; ++g) {
+            const size_t o = ((size_t)min(s2, KSH - 1) * 3 + g) * H;
+            gh[0][s2][g] = ghp[o + kc1];
+            gh[1][s2][g] = ghp[o + kc2];
+        }
     {
-        const float* ghp = a.gh + (slot0 + cp) * (size_t)KS * 3 * H;
-#pragma unroll
-        for (int s2 = 0; s2 < kMaxKsplit; ++s2)
-#pragma unroll
-            for (int g = 0; g < 3; ++g) {
-                const size_t o = ((size_t)min(s2, KS - 1) * 3 + g) * H;
-                gh[0][s2][g] = ghp[o + kc1];
-                gh[1][s2][g] = ghp[o + kc2];
-            }
         const float* hpp = a.hstate + (slot0 + cp) * H;
         hp[0] = hpp[kc1];
         hp[1] = hpp[kc2];
@@ -1150,16 +1165,20 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         __syncthreads();
         if (s_dec[3]) flag |= kPipeTimeoutFlag;
 #pragma unroll
-        for (int s2 = 0; s2 < kMaxKsplit; ++s2)
+        for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
-                const size_t base = (((size_t)(pt * KS + min(s2, KS - 1)) * a.B + b) * 3 + g) * H;
+                const size_t base = (((size_t)(pt * KSX + min(s2, KSX - 1)) * a.B + b) * 3 + g) * H;
                 gi[0][s2][g] = ld_agent(a.gi + base + kc1);
                 gi[1][s2][g] = ld_agent(a.gi + base + kc2);
-                const float* ghp = a.gh + (slot0 + cp) * (size_t)KS * 3 * H + ((size_t)min(s2, KS - 1) * 3 + g) * H;
-                gh[0][s2][g] = ld_agent(ghp + kc1);
-                gh[1][s2][g] = ld_agent(ghp + kc2);
+                const size_t o = ((size_t)min(s2, KSH - 1) * 3 + g) * H;
+                gh[0][s2][g] = ld_agent(ghp + o + kc1);
+                gh[1][s2][g] = ld_agent(ghp + o + kc2);
             }
+        // complete the reloads here (vmcnt(0) alone): after this branch the
+        // cell then waits only for the loads it uses on either path, not for
+        // the gathered rows issued after them on the other path
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 
     // ---- the expanded node's state: GRU cell (the root takes h0)
@@ -1172,16 +1191,16 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             if (mode != kRoot) {
                 float sr = 0.f, sz = 0.f, snx = 0.f, snh = 0.f;
 #pragma unroll
-                for (int s2 = 0; s2 < kMaxKsplit; ++s2)
-                    if (s2 < KS) {
+                for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
+                    if (s2 < KSX) {
                         sr += gi[u][s2][0];
                         sz += gi[u][s2][1];
                         snx += gi[u][s2][2];
                     }
                 float hr = 0.f, hz = 0.f;
 #pragma unroll
-                for (int s2 = 0; s2 < kMaxKsplit; ++s2)
-                    if (s2 < KS) {
+                for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
+                    if (s2 < KSH) {
                         hr += gh[u][s2][0];
                         hz += gh[u][s2][1];
                         snh += gh[u][s2][2];
@@ -1245,6 +1264,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     float psc = 0.f;
     int xtok_next = -1, hslot_next = grow ? ecur : -1;
     bool wait_next = false;  // launch t + 1 will find the popped node not ready and no launch to spare
+    int vexp_rec = 0;        // launch that expanded the popped node's parent
     const bool pops = mode == kRoot || mode == kExpand || mode == kWait || mode == kTrivial;
     if (wave == 0) {
         if (grow) {
@@ -1313,6 +1333,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                 xtok_next = -1;
             } else {
                 const int vexp = v_par == ecur && grow ? t : s_exp[v_par];
+                vexp_rec = vexp;
                 const bool ready_next = pd >= a.L || (t > 0 && ptok == xt_cur && vexp <= t - 1);
                 if (ready_next) xtok_next = qs > 0 ? cand_tok(wave_max_u64(q)) : -1;
                 else xtok_next = ptok;
@@ -1343,7 +1364,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             const int nv = a.E >> 3;
             for (int i = (wave - 1) * kWave + lane; i < nv; i += 3 * kWave) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + (size_t)xn * a.E + i * 8);
-                *reinterpret_cast<u32x4*>(a.xpack[pn] + pack_index_x(b, i * 8, a.E)) = v;
+                *reinterpret_cast<u32x4*>(by_parity(a.xpack, pn) + pack_index_x(b, i * 8, a.E)) = v;
             }
         } else {
             if (hn < 0) return;
@@ -1360,7 +1381,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                 }
 #pragma unroll
                 for (int qq = 0; qq < 3; ++qq)
-                    *reinterpret_cast<u32x4*>(a.hpack[pn] + pack_index_h(b, qq, k, H)) =
+                    *reinterpret_cast<u32x4*>(by_parity(a.hpack, pn) + pack_index_h(b, qq, k, H)) =
                         u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]};
             }
         }
@@ -1382,16 +1403,16 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                 a.scores[slot0 + i] = -INFINITY;
             }
         }
-        if (lane == 0) a.xtok[pt][b] = -1;  // (the parity launch 1 reads as "previous")
+        if (lane == 0) by_parity(a.xtok, pt)[b] = -1;  // (the parity launch 1 reads as "previous")
     }
     a.queue[(size_t)b * kWave + lane] = q;
     if (lane == 0) {
         if (grow) a.exp_at[slot0 + ecur] = t;
-        a.xtok[pn][b] = xtok_next;
-        a.hslot[pn][b] = hslot_next;
+        by_parity(a.xtok, pn)[b] = xtok_next;
+        by_parity(a.hslot, pn)[b] = hslot_next;
         if ((xtok_next >= 0 || hslot_next >= 0) && t + 1 < a.T) a.active[t + 1] = 1;
         if (wait_next && t + 1 < a.T) a.active[a.T + t + 1] = 1;  // its contraction publishes
-        const int nd = new_cur == cur && !pops ? cdepth : pd;
+        const int nd = new_cur == cur && !pops ? (rs1[3] & 0xffff) | (pexp << 16) : pd | (vexp_rec << 16);
         const int ntok = new_cur == cur && !pops ? ctok : ptok;
         const int npar = new_cur == cur && !pops ? cpar : v_par;
         int32_t* rs = a.rstate + (size_t)b * kStateWords;
@@ -1477,19 +1498,20 @@ hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C,
 PipePlan pipe_plan(int B, int L, int E, int H, int M, int n) {
     PipePlan p{};
     if (B < 1 || B > 64 || H > 2 * kPipeThreads || H % 32 || E % 32) return p;  // ng = 0: not applicable
-    // contraction workgroups of 32 units x one K range, and the requests'
-    // node workgroups, together at most one per CU
+    // contraction workgroups of 32 units x one share of the x part or of the
+    // h part, and the requests' node workgroups, together at most one per CU
     const int groups = H / 32;
-    if (groups + B > 256) return p;
-    p.ksplit = std::min(kMaxKsplit, std::max(1, (256 - B) / groups));
-    p.ng = groups * p.ksplit;
+    const int per = std::min(2 * kPipeMaxKs, (256 - B) / groups);  // shares per 32 units
+    if (per < 2) return p;
+    p.ksh = per / 2;
+    p.ksx = per - p.ksh;
+    p.ng = groups * per;
     p.rb = gate::row_blocks(B);
-    p.xwaves = 0;
-    if (!gate::t32_fits(E / 32, H / 32, p.ksplit, p.rb)) return PipePlan{};  // one weight batch per wave
+    if (!gate::t32_fits(E / 32, H / 32, p.ksx, p.ksh, p.rb)) return PipePlan{};  // one weight batch per wave
     const NodeLds lp = node_lds_plan(L, M, n, H);
     const size_t node = lp.bytes + (((size_t)n + 1) * 4 + 15) / 16 * 16;  // + the slots' expansion launches
-    const size_t red = (size_t)kPipeWaves * p.rb * 3 * 16 * kRedRow * 4;  // the waves' sums
-    const size_t gates = std::max(gate::t32_act_bytes(E / 32, H / 32, p.ksplit, p.rb), red);
+    const size_t red = (size_t)2 * (gate::kT32Quarters - 1) * p.rb * 3 * kWave * 16;  // quarters 1 .. 3's sums
+    const size_t gates = std::max(gate::t32_act_bytes(E / 32, H / 32, p.ksx, p.ksh, p.rb), red);
     p.lds = std::max(node, gates);
     if (p.lds > kPipeMaxDynLds) return PipePlan{};  // does not fit one CU's LDS
     return p;

@@ -213,36 +213,41 @@ __device__ __forceinline__ void tile_accumulate(const GruGatesArgs& a, int ut, i
 
 // ---- 32-unit tiles with the activations staged in LDS -----------------------
 // A workgroup of 8 waves owns 32 hidden units (unit tiles 2 ug and 2 ug + 1)
-// and K range ks of KS: x chunks [xb, xe) and h chunks [hb, he) (equal
-// shares of nE and of nH).  It copies the range's packed activations (RB row
-// blocks; three parts per h chunk) into LDS once for all its waves, so each
-// activation byte crosses the memory system once per 32 units rather than
-// once per 16.  Wave w takes unit tile w / 4 and, by (w / 2) % 2 and w % 2,
-// the first or second half of the x chunks or of the h chunks: the weights of
-// its chunks are loaded into registers in one batch, issued with the
-// activation copy (one memory round trip), and the activation operands are
-// read from LDS.  Accumulator slots 0, 1, 2 hold gates r, z, n of the wave's
-// kind (x or h), so the x part and the h part stay apart.
+// and one kind of the contraction's K range: x (the embedding part, nE
+// chunks) or h (the state part, nH chunks), share ksub of nsub equal shares
+// of that kind.  Workgroups of one kind only: the consumer adds nsub partial
+// sums per kind rather than one per K range of either kind.  The workgroup
+// copies its share's packed activations (RB row blocks; three parts per h
+// chunk) into LDS once for all its waves, so each activation byte crosses
+// the memory system once per 32 units.  Wave w takes unit tile w / 4 and
+// quarter w % 4 of the share's chunks: the weights of its chunks are loaded
+// into registers in one batch, issued with the activation copy (one memory
+// round trip), and the activation operands are read from LDS.  Accumulator
+// slots 0, 1, 2 hold gates r, z, n of the kind.  The weights are the MFMA's
+// first operand: output lane l holds units 4 (l / 16) .. + 3 of the unit
+// tile for row l % 16 of each row block (16 contiguous bytes per row).
 //
 // Chunks per wave: at most t32_xbatch(RB) x chunks or t32_hbatch(RB) h
 // chunks (weights in registers: fewer row blocks leave room for more);
 // t32_fits() is the host's check of a configuration.
 __host__ __device__ constexpr int t32_xbatch(int rb) { return rb == 4 ? 8 : 12; }
 __host__ __device__ constexpr int t32_hbatch(int rb) { return rb == 4 ? 4 : 6; }
+constexpr int kT32Quarters = 4;  // waves per unit tile
 
 // [b, e) of share i of n equal shares of [0, total)
 __host__ __device__ inline void share(int total, int n, int i, int& b, int& e) {
     b = (int)((long long)i * total / n);
     e = (int)((long long)(i + 1) * total / n);
 }
-inline bool t32_fits(int nE, int nH, int KS, int rb) {
-    const int nx = (nE + KS - 1) / KS, nh = (nH + KS - 1) / KS;  // largest shares
-    return (nx + 1) / 2 <= t32_xbatch(rb) && (nh + 1) / 2 <= t32_hbatch(rb);
+inline bool t32_fits(int nE, int nH, int ksx, int ksh, int rb) {
+    const int nx = (nE + ksx - 1) / ksx, nh = (nH + ksh - 1) / ksh;  // largest shares
+    return (nx + kT32Quarters - 1) / kT32Quarters <= t32_xbatch(rb) &&
+           (nh + kT32Quarters - 1) / kT32Quarters <= t32_hbatch(rb);
 }
 // Bytes of LDS one workgroup's staged activations take (the largest share).
-inline size_t t32_act_bytes(int nE, int nH, int KS, int rb) {
-    const int nx = (nE + KS - 1) / KS, nh = (nH + KS - 1) / KS;
-    return (size_t)rb * (nx + 3 * nh) * 1024;
+inline size_t t32_act_bytes(int nE, int nH, int ksx, int ksh, int rb) {
+    const int nx = (nE + ksx - 1) / ksx, nh = (nH + ksh - 1) / ksh;
+    return (size_t)rb * (nx > 3 * nh ? nx : 3 * nh) * 1024;
 }
 
 // Operand-tile order: lane l of an MFMA operand read takes row l % 16 and K
@@ -252,24 +257,24 @@ inline size_t t32_act_bytes(int nE, int nH, int KS, int rb) {
 __device__ __forceinline__ int t32_src_vector(int p) { return (p & 15) * 4 + (p >> 4); }
 
 template <int WM, int RB>
-__device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ks, int KS, u32x4* sact,
+__device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int kind, int ksub, int nsub, u32x4* sact,
                                            f32x4 (&acc)[RB][3]) {
     constexpr int XB = t32_xbatch(RB), HB = t32_hbatch(RB);
     // (the wave's role and chunk range are wave-uniform: scalar registers)
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
-    const int u = wave >> 2, kind = (wave >> 1) & 1, half = wave & 1;
+    const int u = wave / kT32Quarters, qt = wave % kT32Quarters;
     const int ut = ug * 2 + u;
     const int kq = (lane >> 4) * 8;
     const int nE = a.E / 32, nH = a.H / 32, nC = nE + nH;
-    int xb, xe, hb, he;
-    share(nE, KS, ks, xb, xe);
-    share(nH, KS, ks, hb, he);
-    const int nxw = xe - xb, nhw = he - hb;
-    // this wave's chunks, numbered within its kind; cg: the kind's first
-    // chunk in the packed weights
-    const int kb = kind ? hb : xb, kn = kind ? nhw : nxw;
-    const int cb = kb + (half ? kn / 2 : 0), n = half ? kn - kn / 2 : kn / 2;
-    const int cg = kind ? nE : 0;
+    // the workgroup's share [sb, se) of its kind's chunks, and the wave's
+    // quarter of it [cb, cb + n) (chunks numbered within the kind)
+    int sb, se;
+    share(kind ? nH : nE, nsub, ksub, sb, se);
+    const int nsh = se - sb;
+    int qb, qe;
+    share(nsh, kT32Quarters, qt, qb, qe);
+    const int cb = sb + qb, n = qe - qb;
+    const int cg = kind ? nE : 0;  // the kind's first chunk in the packed weights
 
     // ---- weights of the wave's chunks: a wave-uniform base plus a fixed
     // per-lane byte offset per load
@@ -300,31 +305,22 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ks
             for (int g = 0; g < 3; ++g) w[i][g] = wload(i, g);
     }
 
-    // ---- copy the activations of the range into LDS: x blocks [rb][c], then
-    // h blocks [rb * 3 + q][c], 1 KB each; wave w copies blocks w, w + 8, ...
+    // ---- copy the share's activations into LDS: x blocks [rb][c], or h
+    // blocks [rb * 3 + q][c], 1 KB each; wave w copies blocks w, w + 8, ...
     // with global_load_lds_dwordx4 (lane l's 16 bytes land at block + 16 l,
     // no registers held), and waits for its copies before the barrier
-    const int nbx = RB * nxw, nblk = nbx + RB * 3 * nhw;
-    const u32x4* xp = reinterpret_cast<const u32x4*>(a.xpack);
-    const u32x4* hp = reinterpret_cast<const u32x4*>(a.hpack);
+    const int nper = kind ? 3 * RB : RB;  // block rows (rb, or rb and part)
+    const int nblk = nper * nsh;
+    const u32x4* src0 = reinterpret_cast<const u32x4*>(kind ? a.hpack : a.xpack);
+    const int nrow = kind ? nH : nE;      // chunks per block row in the packed layout
     const int sv = t32_src_vector(lane);
     for (int blk = wave; blk < nblk; blk += kWaves8) {
-        const u32x4* src;
-        if (blk < nbx) {
-            int rb = 0, c = blk;
-            while (c >= nxw) {
-                c -= nxw;
-                ++rb;
-            }
-            src = xp + ((size_t)rb * nE + xb + c) * 64;
-        } else {
-            int rq = 0, c = blk - nbx;
-            while (c >= nhw) {
-                c -= nhw;
-                ++rq;
-            }
-            src = hp + ((size_t)rq * nH + hb + c) * 64;
+        int r = 0, c = blk;
+        while (c >= nsh) {
+            c -= nsh;
+            ++r;
         }
+        const u32x4* src = src0 + ((size_t)r * nrow + sb + c) * 64;
         __builtin_amdgcn_global_load_lds(src + sv, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16,
                                          0, 0);
     }
@@ -354,9 +350,9 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ks
     if (kind == 0) {
         bf16x8 f[2][RB];
         auto rd = [&](bf16x8 (&d)[RB], int i) {
-            const int c = cb + i - xb;
+            const int c = cb + i - sb;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) d[rb] = __builtin_bit_cast(bf16x8, sact[(rb * nxw + c) * 64 + lane]);
+            for (int rb = 0; rb < RB; ++rb) d[rb] = __builtin_bit_cast(bf16x8, sact[(rb * nsh + c) * 64 + lane]);
         };
         rd(f[0], 0);
 #pragma unroll
@@ -365,32 +361,31 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ks
                 if (i + 1 < n) rd(f[(i + 1) & 1], i + 1);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    acc[rb][0] = mfma(f[i & 1][rb], w[i][0], acc[rb][0]);
-                    acc[rb][1] = mfma(f[i & 1][rb], w[i][1], acc[rb][1]);
-                    acc[rb][2] = mfma(f[i & 1][rb], w[i][2], acc[rb][2]);
+                    acc[rb][0] = mfma(w[i][0], f[i & 1][rb], acc[rb][0]);
+                    acc[rb][1] = mfma(w[i][1], f[i & 1][rb], acc[rb][1]);
+                    acc[rb][2] = mfma(w[i][2], f[i & 1][rb], acc[rb][2]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        const int nvx = nbx * 64;
 #pragma unroll
         for (int i = 0; i < HB; ++i) {
             if (i < n) {  // (uniform)
-                const int c = cb + i - hb;
+                const int c = cb + i - sb;
                 bf16x8 f[RB][3];
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int q = 0; q < 3; ++q)
-                        f[rb][q] = __builtin_bit_cast(bf16x8, sact[nvx + ((rb * 3 + q) * nhw + c) * 64 + lane]);
+                        f[rb][q] = __builtin_bit_cast(bf16x8, sact[((rb * 3 + q) * nsh + c) * 64 + lane]);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int q = 0; q < 3; ++q) {
-                        acc[rb][0] = mfma(f[rb][q], w[i][0], acc[rb][0]);
-                        acc[rb][1] = mfma(f[rb][q], w[i][1], acc[rb][1]);
-                        acc[rb][2] = mfma(f[rb][q], w[i][2], acc[rb][2]);
+                        acc[rb][0] = mfma(w[i][0], f[rb][q], acc[rb][0]);
+                        acc[rb][1] = mfma(w[i][1], f[rb][q], acc[rb][1]);
+                        acc[rb][2] = mfma(w[i][2], f[rb][q], acc[rb][2]);
                     }
             }
             __builtin_amdgcn_sched_barrier(0);
