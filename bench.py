@@ -219,15 +219,22 @@ def main():
         step(out)
     torch.cuda.synchronize()
 
-    # ---- timed steps (level-1 events: around the top-M kernels and at the
-    # end of each call, so every round's duration is measured on the stream)
-    dtree.dt_timing_enable(bld.handle, 1, args.steps)
+    # ---- timed steps: no timing events (an event recorded after a kernel
+    # delays the next one's start by a few microseconds)
     torch.cuda.synchronize()
     start = time.perf_counter()
     for _ in range(args.steps):
         step(out)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - start
+
+    # ---- the same steps again with level-1 events (around the top-M kernels
+    # and at the end of each call): per-round durations on the stream and the
+    # select kernel's own time
+    dtree.dt_timing_enable(bld.handle, 1, args.steps)
+    for _ in range(args.steps):
+        step(out)
+    torch.cuda.synchronize()
     sel_ms = dtree.dt_timing_read(bld.handle, 0)
     merge_ms = dtree.dt_timing_read(bld.handle, 1)
     call_ms = dtree.dt_timing_read(bld.handle, 4)
@@ -521,8 +528,8 @@ def main():
         # (null: each row is one segment, so no merge kernel runs)
         "topm_merge_ms_mean": round(float(np.mean(merge_ms)), 5) if merge_ms else None,
         "call_ms_events_mean": round(float(np.mean(call_ms)), 5),
-        # per-round durations from the events each timed call records on the
-        # library's stream (first kernel's begin to the call's end)
+        # per-round durations from the events each call of the second pass
+        # records on the library's stream (first kernel's begin to the call's end)
         "us_per_round_events": {"p10": round(percentile(round_us, 10), 1),
                                 "median": round(percentile(round_us, 50), 1),
                                 "p90": round(percentile(round_us, 90), 1),

@@ -194,7 +194,7 @@ struct PipeArgs {
     int32_t* exp_at;      // [B][n+1] launch that expanded the slot
     unsigned* done;       // [T] contraction workgroups finished, per launch
     int32_t* active;      // [2][T] launch t's contraction has a row; some request waits for it
-    uint16_t* wpack;      // the weights in operand tiles (written by launch 1)
+    uint16_t* wpack;      // the weights in operand tiles (written by launch 0)
     int32_t* child_tok;   // [B, n+1, 64]
     float* child_lp;
     u64* ckey;            // [B, n+1, 64] unsorted child keys

@@ -875,18 +875,28 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 // half first) and stored: gi by launch parity, gh by the slot of the state.
 template <int WM, int RB>
 __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) {
-    if (t == 0) {  // no rows yet; clear this call's per-launch counters and flags
+    const int groups = a.H / 32;
+    const int ug = (int)blockIdx.x % groups, kw = (int)blockIdx.x / groups;
+    const int kind = kw >= a.ksx, ksub = kind ? kw - a.ksx : kw, nsub = kind ? a.ksh : a.ksx;
+    if (t == 0) {
+        // no rows yet: clear this call's per-launch counters and flags, and
+        // lay this workgroup's weights out in operand tiles for the later
+        // launches (beside the root expansions)
         if (blockIdx.x == 0)
             for (int i = threadIdx.x; i < a.T; i += kPipeThreads) {
                 a.done[i] = 0u;
                 a.active[i] = 0;
                 a.active[a.T + i] = 0;
             }
+        GruGatesArgs g{};
+        g.W_ih = a.W_ih;
+        g.W_hh = a.W_hh;
+        g.E = a.E;
+        g.H = a.H;
+        g.wpack = a.wpack;
+        gate::t32_pack_weights(g, ug, kind, ksub, nsub);
         return;
     }
-    const int groups = a.H / 32;
-    const int ug = (int)blockIdx.x % groups, kw = (int)blockIdx.x / groups;
-    const int kind = kw >= a.ksx, ksub = kind ? kw - a.ksx : kw, nsub = kind ? a.ksh : a.ksx;
     const int par = t & 1, S = a.n + 1;
     // this launch's flags: some row needs the contraction (launch 1 always
     // has rows); some request waits for its sums in this launch, so they are
@@ -1099,7 +1109,6 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             cv[jj][1] = *reinterpret_cast<const u32x4*>(row + kb);
         }
     };
-    if (t == 0 || cand) gather(0);
     const int cp = t == 0 ? 0 : cpar;
     float gh[2][kPipeMaxKs][3];
     float hp[2];
@@ -1118,6 +1127,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         hp[1] = hpp[kc2];
     }
     const u64 prev_keys = a.ckey[(slot0 + (unsorted >= 0 ? unsorted : 0)) * kMaxM + lane];
+    if (t == 0 || cand) gather(0);
     // this launch's mode (uniform over the workgroup)
     int mode;
     if (t == 0) mode = kRoot;
@@ -1522,7 +1532,7 @@ hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds
     if (a.B == 0) return hipSuccess;
     const dim3 grid(pp.ng + a.B), block(kPipeThreads);
     const unsigned shm = (unsigned)pp.lds;
-    const int wm = t == 1 ? 1 : 2;  // launch 1 copies the weights into operand tiles, the later ones read them
+    const int wm = 2;  // (launch 0 lays the weights out in operand tiles; the later ones read them)
 #define DT_PIPE(WM, RB)                                                                                    \
     if (wm == WM && pp.rb == RB) {                                                                         \
         static unsigned granted = 0;  /* dynamic LDS bytes allowed so far (grows only) */                \
@@ -1534,7 +1544,7 @@ hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds
         }                                                                                                  \
         return launch_kernel(pipe_kernel<WM, RB>, grid, block, shm, stream, ev, a, lp, t);                 \
     }
-    DT_PIPE(1, 4) DT_PIPE(2, 4) DT_PIPE(1, 2) DT_PIPE(2, 2) DT_PIPE(1, 1) DT_PIPE(2, 1)
+    DT_PIPE(2, 4) DT_PIPE(2, 2) DT_PIPE(2, 1)
 #undef DT_PIPE
     return hipErrorInvalidValue;
 }

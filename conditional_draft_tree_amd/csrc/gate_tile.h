@@ -393,5 +393,27 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ki
     }
 }
 
+// The weights of a workgroup's share (both unit tiles, the four quarters)
+// copied from W_ih / W_hh into the operand-tile layout of pack_index_w: the
+// same chunks tile32_lds<2, RB> of that workgroup reads afterwards.
+__device__ __forceinline__ void t32_pack_weights(const GruGatesArgs& a, int ug, int kind, int ksub, int nsub) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
+    const int u = wave / kT32Quarters, qt = wave % kT32Quarters;
+    const int ut = ug * 2 + u;
+    const int nE = a.E / 32, nH = a.H / 32, nC = nE + nH;
+    int sb, se, qb, qe;
+    share(kind ? nH : nE, nsub, ksub, sb, se);
+    share(se - sb, kT32Quarters, qt, qb, qe);
+    const int cg = kind ? nE : 0, Kk = kind ? a.H : a.E;
+    const bf16_t* src = (const bf16_t*)(kind ? a.W_hh : a.W_ih) + ((size_t)ut * 16 + (lane & 15)) * Kk + (lane >> 4) * 8;
+    bf16_t* dst = (bf16_t*)a.wpack + pack_index_w(ut, 0, 0, nC) + lane * 8;
+    const size_t wgate = (size_t)nC * 512;
+    for (int c = sb + qb; c < sb + qe; ++c)
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+            *reinterpret_cast<u32x4*>(dst + g * wgate + (size_t)(cg + c) * 512) =
+                *reinterpret_cast<const u32x4*>(src + (size_t)g * a.H * Kk + (size_t)c * 32);
+}
+
 }  // namespace gate
 }  // namespace dt
