@@ -897,6 +897,9 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
         gate::t32_pack_weights(g, ug, kind, ksub, nsub);
         return;
     }
+    // after the last launch nothing expands: its sums are read only by requests
+    // waiting in it (published then)
+    if (t == a.T - 1 && a.active[a.T + t] == 0) return;
     const int par = t & 1, S = a.n + 1;
     // this launch's flags: some row needs the contraction (launch 1 always
     // has rows); some request waits for its sums in this launch, so they are
@@ -905,8 +908,10 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
     // suffice.  Their loads overlap the contraction, which runs either way
     // (its inputs are always in bounds; without rows nothing is stored).
     const int act = a.active[t], publish = a.active[a.T + t];
-    __shared__ int s_hsl[kMaxB];  // each row's state slot (ordered by the tile's barrier)
-    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = by_parity(a.hslot, par)[threadIdx.x];
+    // each row's state slot: loaded now, stored into LDS after the tile
+    // (a store would wait for the load here)
+    __shared__ int s_hsl[kMaxB];
+    const int hsl_r = (int)threadIdx.x < a.B ? by_parity(a.hslot, par)[threadIdx.x] : -1;
     GruGatesArgs g{};
     g.xpack = by_parity(a.xpack, par);
     g.hpack = by_parity(a.hpack, par);
@@ -923,21 +928,20 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
     gate::tile32_lds<WM, RB>(g, ug, kind, ksub, nsub, reinterpret_cast<gate::u32x4*>(lds), acc);
     __syncthreads();  // every wave is done with the staged activations
     // the four quarters of each unit tile (waves 4 u + 0 .. 3) are added in
-    // order: quarters 1 .. 3 leave their sums in LDS ([u][quarter - 1][rb * 3
-    // + slot][lane]), quarter 0 adds them to its own and stores.  Lane l holds
-    // units 4 (l / 16) .. + 3 of row l % 16 of each row block.
+    // order, quarter 0 first: every wave leaves its sums in LDS ([wave][rb *
+    // 3 + slot][lane]); wave 4 u + q then adds up and stores the slot vectors
+    // j = q, q + 4, ... of the unit tile.  Lane l holds units 4 (l / 16) .. +
+    // 3 of row l % 16 of each row block.
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
     const int u = wave / gate::kT32Quarters, qt = wave % gate::kT32Quarters;
     gate::f32x4* red = reinterpret_cast<gate::f32x4*>(lds);
-    if (qt != 0) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int sl = 0; sl < 3; ++sl)
-                red[(((u * 3 + qt - 1) * RB + rb) * 3 + sl) * kWave + lane] = acc[rb][sl];
-    }
+        for (int sl = 0; sl < 3; ++sl) red[(wave * RB * 3 + rb * 3 + sl) * kWave + lane] = acc[rb][sl];
+    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = hsl_r;
     __syncthreads();
-    if (qt == 0 && (t == 1 || act != 0)) {
+    if (t == 1 || act != 0) {
         // (the fields are read into values first: selecting between fields of
         // the kernel argument would copy the argument to scratch)
         float* const gi = a.gi;
@@ -945,21 +949,20 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
         const int B = a.B, H = a.H, ksx = a.ksx, ksh = a.ksh;
         const int unit = ug * 32 + u * 16 + (lane >> 4) * 4;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
+        for (int j0 = 0; j0 < RB * 3; j0 += gate::kT32Quarters) {
+            const int j = j0 + qt;  // (wave-uniform)
+            if (j >= RB * 3) break;
+            const int rb = j / 3, sl = j % 3;
+            gate::f32x4 sum = red[((u * gate::kT32Quarters) * RB * 3 + j) * kWave + lane];
+#pragma unroll
+            for (int q = 1; q < gate::kT32Quarters; ++q)
+                sum += red[((u * gate::kT32Quarters + q) * RB * 3 + j) * kWave + lane];
             const int row = rb * 16 + (lane & 15);
             const int hsl = kind ? s_hsl[min(row, B - 1)] : 0;
-            const bool ok = row < B && (kind == 0 || (hsl >= 0 && hsl < S));
-#pragma unroll
-            for (int sl = 0; sl < 3; ++sl) {
-                gate::f32x4 sum = acc[rb][sl];
-#pragma unroll
-                for (int q = 0; q < gate::kT32Quarters - 1; ++q)
-                    sum += red[(((u * 3 + q) * RB + rb) * 3 + sl) * kWave + lane];
-                if (!ok) continue;
-                float* dst = kind == 0 ? gi + (((size_t)(par * ksx + ksub) * B + row) * 3 + sl) * H + unit
-                                       : gh + ((((size_t)row * S + hsl) * ksh + ksub) * 3 + sl) * H + unit;
-                *reinterpret_cast<gate::f32x4*>(dst) = sum;
-            }
+            if (row >= B || (kind && (hsl < 0 || hsl >= S))) continue;
+            float* dst = kind == 0 ? gi + (((size_t)(par * ksx + ksub) * B + row) * 3 + sl) * H + unit
+                                   : gh + ((((size_t)row * S + hsl) * ksh + ksub) * 3 + sl) * H + unit;
+            *reinterpret_cast<gate::f32x4*>(dst) = sum;
         }
     }
     if (publish) {
@@ -1520,7 +1523,7 @@ PipePlan pipe_plan(int B, int L, int E, int H, int M, int n) {
     if (!gate::t32_fits(E / 32, H / 32, p.ksx, p.ksh, p.rb)) return PipePlan{};  // one weight batch per wave
     const NodeLds lp = node_lds_plan(L, M, n, H);
     const size_t node = lp.bytes + (((size_t)n + 1) * 4 + 15) / 16 * 16;  // + the slots' expansion launches
-    const size_t red = (size_t)2 * (gate::kT32Quarters - 1) * p.rb * 3 * kWave * 16;  // quarters 1 .. 3's sums
+    const size_t red = (size_t)kPipeWaves * p.rb * 3 * kWave * 16;  // the waves' sums
     const size_t gates = std::max(gate::t32_act_bytes(E / 32, H / 32, p.ksx, p.ksh, p.rb), red);
     p.lds = std::max(node, gates);
     if (p.lds > kPipeMaxDynLds) return PipePlan{};  // does not fit one CU's LDS

@@ -291,7 +291,9 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ki
         const int c = cb + min(i, n - 1);
         const char* base = WM == 2 ? wpk + (g * wgate + (size_t)(cg + c) * 512) * 2
                                    : wsrc + ((size_t)g * a.H * Kk + (size_t)c * 32) * 2;
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + loff));
+        // (each weight byte is read once per launch: non-temporal, so the
+        // stream does not evict what the node workgroups keep in the L2)
+        return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + loff)));
     };
     if (n > 0 && kind == 0) {
 #pragma unroll
