@@ -19,10 +19,12 @@ line:
               single-threaded oracle call per request on a thread pool), and
               on one core on a bounded sample; host core count and CPU model
   parity      the timed trees compared with the oracle's, request by request
-Extra keys: per-round time percentiles from per-call HIP events, per-stage
-times (a separate pass with per-kernel events), the fused expansion launches,
-the stepped expansion's GRU contraction (MFMA rate against the bf16 dense peak)
-and gathers, and latency figures.
+Extra keys: per-round time percentiles from per-call HIP events (a second
+pass over the same steps), per-stage times (a pass with per-kernel events),
+the fused expansion launch's roofline (the GRU contraction's flops and the
+weights + gathers bytes per launch over its mean duration, with its MFMA
+counters), the stepped expansion's GRU contraction (MFMA rate against the bf16
+dense peak) and gathers, and latency figures.
 """
 from __future__ import annotations
 
@@ -59,28 +61,33 @@ def topm_traffic():
     return int(m.group(1)) if h.hexdigest() == m.group(2) else None
 
 
-def gru_counters():
-    """(MFMA MOPs, MFMA busy SIMD-cycles) per benchmarked contraction launch from
-    the committed counter summary, or None when the contraction's sources have
-    changed since the counters were taken."""
+def mfma_counters(prefix, files):
+    """(MFMA MOPs, MFMA busy SIMD-cycles) per benchmarked launch of a
+    contraction from the committed counter summary (line `prefix_mfma_...`),
+    or None when the kernel's sources have changed since they were taken."""
     import hashlib
     import re
     try:
         text = open(os.path.join(ROOT, "profiles", "gru_contraction_qwen3_4b_batched_mfma.md")).read()
     except OSError:
         return None
-    m = re.search(r"gru_mfma_mops_bf16=(\d+) gru_mfma_busy_cycles=(\d+) source_sha256=([0-9a-f]{64})", text)
+    m = re.search(prefix + r"_mfma_mops_bf16=(\d+) " + prefix +
+                  r"_mfma_busy_cycles=(\d+) source_sha256=([0-9a-f]{64})", text)
     if not m:
         return None
     h = hashlib.sha256()
-    for f in ("gru.hip", "dt_device.h", "dt_launch.h"):
+    for f in files:
         with open(os.path.join(ROOT, "conditional_draft_tree_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return (int(m.group(1)), int(m.group(2))) if h.hexdigest() == m.group(3) else None
 
 
-def gru_counter_figures(mean_ms):
-    c = gru_counters()
+# the sources each contraction kernel is built from (the counters' hash)
+GRU_SOURCES = ("gru.hip", "gate_tile.h", "dt_device.h", "dt_launch.h")
+FUSED_SOURCES = ("expand.hip", "gate_tile.h", "dt_device.h", "dt_launch.h")
+
+
+def counter_figures(c, mean_ms):
     if c is None or not mean_ms == mean_ms:
         return None
     mops, busy = c
@@ -159,6 +166,36 @@ def parse():
     p.add_argument("--copy-calib", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
+
+
+def fused_roofline(st, fused, B, L, E, H, M, n, esz, config, np):
+    """The fused expansion launch (both roles): per launch that contracts
+    (t = 1 .. T - 2), the GRU gate contraction's algorithmic flops
+    2 B 3H (E + H) and bytes read (the weights once, 3H (E + H) elements, and
+    the node steps' gathers, B (M H + E) elements), over the launch's mean
+    duration from the events each launch records."""
+    if not fused or not st["fused_each"] or not st["fused_total"]:
+        return None
+    calls = len(st["fused_total"])
+    each = np.array(st["fused_each"], dtype=np.float64).reshape(calls, -1)
+    T = each.shape[1]
+    mid_ms = float(np.mean(each[:, 1:T - 1]))
+    flop = 2.0 * B * 3 * H * (E + H)
+    nbytes = (3 * H * (E + H) + B * (M * H + E)) * esz
+    tfs = flop / (mid_ms * 1e-3) / 1e12
+    gbs = nbytes / (mid_ms * 1e-3) / 1e9
+    return {"kernel": "pipe_kernel (one fused expansion launch: contraction and node steps)",
+            "bound": "hbm" if flop / nbytes < 312 else "mfma",
+            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": nbytes,
+            "flop_per_launch": flop, "achieved_tflops": round(tfs, 2),
+            "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 5),
+            "mean_launch_ms": round(mid_ms, 5), "launches_per_round": T,
+            "root_launch_ms": round(float(np.mean(each[:, 0])), 5),
+            "last_launch_ms": round(float(np.mean(each[:, T - 1])), 5),
+            "counters": counter_figures(mfma_counters("fused", FUSED_SOURCES), mid_ms)
+            if config == "qwen3_4b_batched" else None}
 
 
 def fused_summary(st, sst, fused, n, stepped_us, stepped_same, np):
@@ -521,8 +558,10 @@ def main():
             # from the committed rocprofv3 counters of the same launch shape:
             # MFMA ops actually issued (512 flops per MOP) and MFMA busy cycles
             # over the launch (1024 SIMDs at 2.4 GHz), at this run's mean time
-            "counters": gru_counter_figures(gemm_each) if args.config == "qwen3_4b_batched" else None,
+            "counters": counter_figures(mfma_counters("gru", GRU_SOURCES), gemm_each)
+            if args.config == "qwen3_4b_batched" else None,
         },
+        "roofline_fused": fused_roofline(st, fused, B, L, E, H, M, n, esz, args.config, np),
         "stages_ms_mean": {k: round(float(np.mean(v)), 5) for k, v in st.items() if v},
         "expansion": fused_summary(st, sst, fused, n, stepped_us, stepped_same, np),
         # (null: each row is one segment, so no merge kernel runs)

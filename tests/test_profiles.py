@@ -62,3 +62,19 @@ def test_contraction_mfma_counters_match_the_kernel_structure():
     assert int(shown.group(1)) == mops
     assert abs(float(shown.group(2)) - 512 * mops / 1e9) < 1e-3
     assert abs(float(shown.group(3)) - 2 * 64 * 3 * 1024 * (2560 + 1024) / 1e9) < 1e-3
+
+
+def test_fused_contraction_mfma_counters_match_the_kernel_structure():
+    # SQ_INSTS_VALU_MFMA_MOPS_BF16 of the benchmarked fused launches (their
+    # contraction workgroups): every (16-unit tile, 32-wide chunk) pair once,
+    # 4 row blocks, 3 gates; the x part (E / 32 chunks) one MFMA per block and
+    # gate, the h part (H / 32 chunks) three (the state's three bf16 parts)
+    text = read("gru_contraction_qwen3_4b_batched_mfma.md")
+    m = re.search(r"fused_mfma_mops_bf16=(\d+) fused_mfma_busy_cycles=(\d+) source_sha256=[0-9a-f]{64}", text)
+    assert m
+    mops, busy = int(m.group(1)), int(m.group(2))
+    tiles, rb, gates = 1024 // 16, 4, 3
+    x_mfma = tiles * (2560 // 32) * gates * rb
+    h_mfma = tiles * (1024 // 32) * 3 * gates * rb
+    assert mops == (x_mfma + h_mfma) * 32
+    assert busy == (x_mfma + h_mfma) * 16
