@@ -72,7 +72,8 @@ __device__ __forceinline__ u64 child_key(float lp, int tok) {
 // traffic, no waits).  Lane semantics (checked on the device): row_shl:n
 // reads lane i+n, row_shr:n reads lane i-n within a 16-lane row;
 // permlane16_swap(v, v) = {row-even copies, row-odd copies} and
-// permlane32_swap(v, v) = {lower-half copies, upper-half copies}.
+// permlane32_swap(v, v) = {lower-half copies, upper-half copies}; row_ror:n
+// rotates a 16-lane row by n lanes.
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
@@ -87,10 +88,8 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
         const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false);
         const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
         return (lane & 4) ? dn : up;
-    } else if constexpr (J == 8) {
-        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x108, 0xF, 0xF, false);
-        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
-        return (lane & 8) ? dn : up;
+    } else if constexpr (J == 8) {  // a rotation by 8 within the row: lane i ^ 8
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
     } else if constexpr (J == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
         return (lane & 16) ? r[0] : r[1];
@@ -132,36 +131,49 @@ __device__ __forceinline__ u64 bcast_u64(u64 v, int src) {
     return ((u64)hi << 32) | lo;
 }
 
-// Butterfly sum over the 64 lanes: the order is fixed and, addition being
-// commutative, every lane ends with the same bits.
-__device__ __forceinline__ float wave_sum(float v) {
-    v += xor_lane_f<32>(v);
-    v += xor_lane_f<16>(v);
-    v += xor_lane_f<8>(v);
-    v += xor_lane_f<4>(v);
-    v += xor_lane_f<2>(v);
-    v += xor_lane_f<1>(v);
+// All-reduce over the 64 lanes in the lane-distance order 32, 16, 8, 4, 2, 1
+// (the xor butterfly).  At distances 32 and 16 both results of a swap hold
+// the pair's two values, so a symmetric op takes them without a lane select;
+// at distance 4 a rotation by 4 within the row stands in for the xor partner
+// (after the distance-8 step lanes i and i ^ 8 hold the same value, and the
+// rotation reads one of lanes i ^ 4, i ^ 12).  Every lane ends with the same
+// bits, and with the bits of the plain butterfly: each step combines the same
+// two values, in either order.
+template <typename F>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, F op) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = op(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(b[0], b[1]);
+    v = op(v, xor_lane<8>(v));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = op(v, xor_lane<2>(v));
+    v = op(v, xor_lane<1>(v));
     return v;
 }
+__device__ __forceinline__ float wave_sum(float v) {
+    return __uint_as_float(wave_allreduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+    }));
+}
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, xor_lane_f<32>(v));
-    v = fmaxf(v, xor_lane_f<16>(v));
-    v = fmaxf(v, xor_lane_f<8>(v));
-    v = fmaxf(v, xor_lane_f<4>(v));
-    v = fmaxf(v, xor_lane_f<2>(v));
-    v = fmaxf(v, xor_lane_f<1>(v));
-    return v;
+    return __uint_as_float(wave_allreduce(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    }));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return wave_allreduce(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
 }
 __device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
 __device__ __forceinline__ u64 umin64(u64 a, u64 b) { return a > b ? b : a; }
+// Largest 64-bit key over the 64 lanes: the largest high word, and when more
+// than one lane holds it, the largest low word among those lanes.
 __device__ __forceinline__ u64 wave_max_u64(u64 v) {
-    v = umax64(v, xor_lane_u64<32>(v));
-    v = umax64(v, xor_lane_u64<16>(v));
-    v = umax64(v, xor_lane_u64<8>(v));
-    v = umax64(v, xor_lane_u64<4>(v));
-    v = umax64(v, xor_lane_u64<2>(v));
-    v = umax64(v, xor_lane_u64<1>(v));
-    return v;
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    const u64 tied = __ballot(hi == mh);
+    if (__builtin_popcountll(tied) == 1) return bcast_u64(v, (int)__builtin_ctzll(tied));  // (uniform)
+    return ((u64)mh << 32) | wave_max_u32(hi == mh ? (uint32_t)v : 0u);
 }
 
 // One compare-exchange stage of a bitonic network at lane distance J:

@@ -898,8 +898,12 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
         return;
     }
     // after the last launch nothing expands: its sums are read only by requests
-    // waiting in it (published then)
-    if (t == a.T - 1 && a.active[a.T + t] == 0) return;
+    // waiting in it (published then).  (The flag is read in this branch only,
+    // by a load of its own: a plain load would be shared with the one below
+    // and waited for here, at the start of every launch.)
+    if (t == a.T - 1 &&
+        __hip_atomic_load(a.active + a.T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        return;
     const int par = t & 1, S = a.n + 1;
     // this launch's flags: some row needs the contraction (launch 1 always
     // has rows); some request waits for its sums in this launch, so they are
@@ -1239,6 +1243,16 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         }
     }
 
+    // the queue's two best entries before this launch's pushes (wave 0, while
+    // the gathers are in flight): a pop takes the first or the expanded
+    // node's best child, and the next best is among the two, that child and
+    // the popped entry's sibling
+    u64 qa = 0ull, qb = 0ull;
+    if (wave == 0) {
+        qa = wave_max_u64(q);
+        qb = wave_max_u64(q == qa ? 0ull : q);
+    }
+
     // ---- correction dots of the expanded node's children
     if (grow) {
         float acc[RW];
@@ -1270,7 +1284,10 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     __syncthreads();
 
     // ---- queue (wave 0): push the expanded node's best child, pop the next
-    // node, choose the next launch's contraction rows
+    // node, choose the next launch's contraction rows.  The pop is the larger
+    // of qa and that child (keys are unique); what a pop of qa reads is
+    // fetched before the children are known, and the queue is left as a push
+    // and a swap-remove of the popped entry would leave it.
     const int ecur = mode == kRoot ? 0 : cur;  // the slot expanded (or popped trivially) now
     u64 ckey = 0ull, best = 0ull, second = 0ull;
     int new_cnt = cnt, new_cur = cur, v_par = -1, pd = 0, pr = 0, ptok = -1;
@@ -1280,47 +1297,81 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     int vexp_rec = 0;        // launch that expanded the popped node's parent
     const bool pops = mode == kRoot || mode == kExpand || mode == kWait || mode == kTrivial;
     if (wave == 0) {
+        const int edepth = mode == kRoot ? 0 : cdepth;
+        // qa and qb: parent, rank, depth; their tokens, qa's sibling and the
+        // rows a pop of qa hands over (LDS reads issued ahead; an empty entry
+        // reads slot n's rows, unused)
+        const int pa = min(qk_parent(qa), a.n), ra = qk_rank(qa), da = qk_depth(qa);
+        const int pb = min(qk_parent(qb), a.n), rb = qk_rank(qb);
+        const int jm = min(lane, M - 1);
+        const int tok_qa = s_ctok[pa * kMaxM + min(ra, kMaxM - 1)];
+        const int tok_qb = s_ctok[pb * kMaxM + min(rb, kMaxM - 1)];
+        const int tok_sb = s_ctok[pa * kMaxM + min(ra + 1, kMaxM - 1)];
+        const float lp_sb = s_clp[pa * kMaxM + min(ra + 1, kMaxM - 1)];
+        const float sc_pa = s_sc[pa];
+        const int exp_pa = s_exp[pa];
+        const float sc_e = s_sc[ecur];
+        const int rowa = min(edepth + 1, a.L - 1) * M + jm, rowb = min(da, a.L - 1) * M + jm;
+        const int hi_a = s_tidx[rowa], hi_b = s_tidx[rowb];
+        const float hv_a = s_tval[rowa], hv_b = s_tval[rowb];
+        u64 kbest = 0ull;
         if (grow) {
             const float tz = __int_as_float(
-                __builtin_amdgcn_readlane(__float_as_int(tail_l), min(mode == kRoot ? 0 : cdepth, a.L - 1)));
+                __builtin_amdgcn_readlane(__float_as_int(tail_l), min(edepth, a.L - 1)));
             ckey = child_keys_r(my_val, zs[lane], my_tok, M, a.temp, tz);
             a.ckey[(slot0 + ecur) * kMaxM + lane] = ckey;  // sorted at the next launch
             best = wave_max_u64(ckey);
             second = wave_max_u64(ckey == best ? 0ull : ckey);
-            const int edepth = mode == kRoot ? 0 : cdepth;
-            const u64 key = queue_key(s_sc[ecur] + child_lp_of(best), edepth + 1, ecur, 0);
-            if (lane == qs) q = key;
-            ++qs;
+            kbest = queue_key(sc_e + child_lp_of(best), edepth + 1, ecur, 0);
         }
-        // token of a queued candidate: the expanded node's own children come
-        // from registers (ranks 0 and 1), the others from the sorted lists
-        auto cand_tok = [&](u64 k) {
-            const int p = qk_parent(k), r = qk_rank(k);
-            if (grow && p == ecur) return r == 0 ? child_tok_of(best) : child_tok_of(second);
-            return s_ctok[p * kMaxM + min(r, kMaxM - 1)];
-        };
-        if (pops && qs > 0) {
-            const u64 top = wave_max_u64(q);
+        const int qs0 = qs;  // entries before this launch's pushes
+        if (pops && (grow || qs0 > 0)) {
+            const bool take_a = grow && kbest > qa;  // the expanded node's best child is popped
+            const u64 top = take_a ? kbest : qa;
             pd = qk_depth(top);
             v_par = qk_parent(top);
             pr = qk_rank(top);
             psc = qk_score(top);
-            ptok = cand_tok(top);
+            ptok = take_a ? child_tok_of(best) : tok_qa;
             const int v = cnt + 1;
             new_cnt = v;
             new_cur = v;
-            // remove the popped entry, push its next-ranked sibling
-            const int holder = (int)__builtin_ctzll(__ballot(q == top));
-            const u64 last = bcast_u64(q, qs - 1);
-            if (lane == holder) q = last;
-            if (lane == qs - 1) q = 0ull;
-            --qs;
-            if (pr + 1 < M) {
-                const float sib_lp = (grow && v_par == ecur) ? child_lp_of(second)
-                                                             : s_clp[v_par * kMaxM + min(pr + 1, kMaxM - 1)];
-                const u64 key = queue_key(s_sc[v_par] + sib_lp, pd, v_par, pr + 1);
-                if (lane == qs) q = key;
-                ++qs;
+            // the popped entry's next-ranked sibling, and the best entry left
+            const bool sib = pr + 1 < M;
+            u64 ksib = 0ull, nb;
+            int ntok;
+            if (take_a) {  // kbest never enters the queue; its sibling takes lane qs0
+                if (sib) ksib = queue_key(sc_e + child_lp_of(second), pd, ecur, 1);
+                if (sib && lane == qs0) q = ksib;
+                qs = qs0 + (sib ? 1 : 0);
+                nb = qa;
+                ntok = tok_qa;
+                if (ksib > nb) {
+                    nb = ksib;
+                    ntok = child_tok_of(second);
+                }
+            } else {  // qa's lane takes the last entry (kbest when pushed)
+                const int holder = (int)__builtin_ctzll(__ballot(q == qa));
+                const int last = grow ? qs0 : qs0 - 1;
+                const u64 klast = grow ? kbest : bcast_u64(q, last);
+                if (lane == holder) q = klast;
+                if (lane == last) q = 0ull;
+                qs = last;
+                if (sib) {
+                    ksib = queue_key(sc_pa + lp_sb, pd, v_par, pr + 1);
+                    if (lane == qs) q = ksib;
+                    ++qs;
+                }
+                nb = qb;
+                ntok = tok_qb;
+                if (kbest > nb) {
+                    nb = kbest;
+                    ntok = child_tok_of(best);
+                }
+                if (ksib > nb) {
+                    nb = ksib;
+                    ntok = tok_sb;
+                }
             }
             {  // near tie: the popped score vs every candidate left
                 const float gap = psc - qk_score(q);
@@ -1335,20 +1386,19 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                 s_par[v] = v_par;
             }
             if (pd < a.L) {  // hand over the popped node's candidates
-                const int jm = min(lane, M - 1);
-                a.nidx[(size_t)b * kWave + lane] = s_tidx[pd * M + jm];
-                a.nval[(size_t)b * kWave + lane] = s_tval[pd * M + jm];
+                a.nidx[(size_t)b * kWave + lane] = take_a ? hi_a : hi_b;
+                a.nval[(size_t)b * kWave + lane] = take_a ? hv_a : hv_b;
             }
             // the next launch's x row: the popped node's token when it cannot
-            // expand at t + 1, else the token of the queue's best candidate
-            // (the likely pop of launch t + 1)
+            // expand at t + 1, else the token of the best entry left (the
+            // likely pop of launch t + 1)
             if (v >= a.n) {
                 xtok_next = -1;
             } else {
-                const int vexp = v_par == ecur && grow ? t : s_exp[v_par];
+                const int vexp = take_a ? t : exp_pa;
                 vexp_rec = vexp;
                 const bool ready_next = pd >= a.L || (t > 0 && ptok == xt_cur && vexp <= t - 1);
-                if (ready_next) xtok_next = qs > 0 ? cand_tok(wave_max_u64(q)) : -1;
+                if (ready_next) xtok_next = nb != 0ull ? ntok : -1;
                 else xtok_next = ptok;
                 // (the mode test of launch t + 1, decided here: not ready, and
                 // no idle launch left)
@@ -1358,7 +1408,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             new_cur = -1;
         } else if (mode == kIdle) {
             // cur expands at t + 1: contract the likely pop after it
-            xtok_next = qs > 0 ? cand_tok(wave_max_u64(q)) : -1;
+            xtok_next = qa != 0ull ? tok_qa : -1;
         }
         if (lane == 0) {
             s_dec[0] = xtok_next;
