@@ -11,7 +11,7 @@ _lock = threading.Lock()
 _lib = None
 
 DT_F32, DT_BF16 = 0, 1
-DT_EXPAND_AUTO, DT_EXPAND_STEPPED, DT_EXPAND_FUSED = 0, 1, 2
+DT_EXPAND_AUTO, DT_EXPAND_STEPPED, DT_EXPAND_FUSED, DT_EXPAND_PERSISTENT = 0, 1, 2, 3
 _STATUS = {0: "DT_OK", -1: "DT_ERR_INVALID_ARG", -2: "DT_ERR_UNSUPPORTED", -3: "DT_ERR_WORKSPACE",
            -4: "DT_ERR_HIP"}
 
@@ -243,8 +243,15 @@ class Builder:
 
     @property
     def fused(self) -> bool:
-        """True when dt_build runs the fused expansion for this configuration."""
-        return dt_expand_mode(self.handle) == DT_EXPAND_FUSED
+        """True when dt_build runs the fused expansion (per-step launches or the
+        persistent launch) for this configuration."""
+        return dt_expand_mode(self.handle) in (DT_EXPAND_FUSED, DT_EXPAND_PERSISTENT)
+
+    @property
+    def expand_mode(self) -> int:
+        """dt_expand_mode of the handle: what the last build ran (before any,
+        what the configuration selects)."""
+        return dt_expand_mode(self.handle)
 
     def close(self):
         if getattr(self, "handle", None) is not None:

@@ -53,6 +53,8 @@ struct dt_handle {
     dt::NodeLds lds;
     dt::PipePlan pp;  // fused expansion plan (pp.ng = 0: stepped)
     int pipe_T;       // launches of a fused call
+    int pers = -1;    // the device holds the persistent grid: 1 yes, 0 no, -1 not checked yet
+    int32_t last_mode;  // expansion of the last dt_build call (before any: the configured one)
     Layout lay;
     Layout lay_na;  // dt_build_noalloc's use of the static scratch (no weight-tile copy)
     std::string err;
@@ -127,7 +129,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true,
     l.p_gh = take(fp ? B * S * (size_t)pp.ksh * 3 * H * 4 : 0);  // h-part gate sums per slot
     l.p_hstate = take(fp ? B * S * H * 4 : 0);        // binary32 state per slot
     l.p_exp = take(fp ? B * S * 4 : 0);               // launch that expanded each slot
-    l.p_done = take(fp ? (size_t)pT * 4 : 0);         // per-launch counters
+    l.p_done = take(fp ? ((size_t)pT + pp.ng + B + 1) * 4 : 0);  // per-launch counters, per-workgroup flags, error word
     l.p_active = take(fp ? (size_t)2 * pT * 4 : 0);
     l.p_xpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * c.E * 2 : 0);  // parity-1 activations
     l.p_hpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
@@ -266,8 +268,8 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
         return fail(nullptr, DT_ERR_INVALID_ARG, "temperature and near_tie_eps must be >= 0");
     if (c.full_vocab != 0 && c.full_vocab != 1)
         return fail(nullptr, DT_ERR_INVALID_ARG, "full_vocab must be 0 or 1 (got %d)", (int)c.full_vocab);
-    if (c.expand < DT_EXPAND_AUTO || c.expand > DT_EXPAND_FUSED)
-        return fail(nullptr, DT_ERR_INVALID_ARG, "expand must be 0, 1 or 2 (got %d)", (int)c.expand);
+    if (c.expand < DT_EXPAND_AUTO || c.expand > DT_EXPAND_PERSISTENT)
+        return fail(nullptr, DT_ERR_INVALID_ARG, "expand must be 0, 1, 2 or 3 (got %d)", (int)c.expand);
     if (c.M > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "M=%d > 64 (one candidate per lane)", c.M);
     if (c.n > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "n=%d > 64 (queue of one wave)", c.n);
     if (c.L > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "L=%d > 64", c.L);
@@ -301,11 +303,13 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
         h->pp = dt::pipe_plan(c.B, c.L, c.E, c.H, c.M, c.n);
         h->pipe_T = c.n + 2;
     }
-    if (c.expand == DT_EXPAND_FUSED && h->pp.ng == 0) {
+    if ((c.expand == DT_EXPAND_FUSED || c.expand == DT_EXPAND_PERSISTENT) && h->pp.ng == 0) {
         delete h;
         return fail(nullptr, DT_ERR_UNSUPPORTED,
                     "fused expansion needs bf16, 1 <= B <= 64, H <= 1024 and E, H multiples of 32");
     }
+    h->last_mode = h->pp.ng == 0 ? DT_EXPAND_STEPPED
+                   : c.expand == DT_EXPAND_FUSED ? DT_EXPAND_FUSED : DT_EXPAND_PERSISTENT;
     h->lay = plan_layout(c, h->nseg, std::max(h->ksplit, h->ksplit_f), true, h->pp, h->pipe_T);
     h->lay_na = plan_layout(c, h->nseg, h->ksplit, /*wtiles=*/false);
     *out = h;
@@ -322,7 +326,7 @@ size_t dt_workspace_bytes(const dt_handle* h) { return h ? h->lay.total : 0; }
 
 int32_t dt_expand_mode(const dt_handle* h) {
     if (!h) return -1;
-    return h->pp.ng > 0 ? DT_EXPAND_FUSED : DT_EXPAND_STEPPED;
+    return h->last_mode;
 }
 
 dt_status dt_timing_enable(dt_handle* h, int level, int capacity) {
@@ -625,15 +629,38 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         pa.hstate = (float*)(w + L.p_hstate);
         pa.exp_at = (int32_t*)(w + L.p_exp);
         pa.done = (unsigned*)(w + L.p_done);
+        pa.gflag = pa.done + pa.T;
+        pa.nflag = pa.gflag + pa.ng;
+        pa.perr = pa.nflag + pa.B;
         pa.active = (int32_t*)(w + L.p_active);
         pa.wpack = (uint16_t*)(w + L.wpack);
         pa.child_tok = a.child_tok; pa.child_lp = a.child_lp; pa.ckey = a.ckey; pa.queue = a.queue;
         pa.rstate = a.rstate; pa.nidx = a.nidx; pa.nval = a.nval;
         pa.tokens = tokens; pa.parents = parents; pa.depths = depths; pa.scores = scores;
         pa.mask = mask; pa.count = count; pa.flags = flags;
-        for (int t = 0; t < h->pipe_T; ++t) {
+        // the persistent launch, where the device holds its grid and the
+        // stream is not being captured; else one launch per step
+        bool pers = false;
+        if (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT) {
+            if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B) ? 1 : 0;
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
+            pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
+            if (c.expand == DT_EXPAND_PERSISTENT && !pers)
+                return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
+                                                       ? "persistent expansion: the stream is being captured"
+                                                       : "persistent expansion: the device cannot hold the grid "
+                                                         "(%d workgroups) at once", h->pp.ng + c.B);
+        }
+        h->last_mode = pers ? DT_EXPAND_PERSISTENT : DT_EXPAND_FUSED;
+        if (pers) {
             DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
-            DT_TRY(dt::launch_pipe_step(pa, h->pp, h->lds, t, st, ev), "fused expansion launch");
+            DT_TRY(dt::launch_pers_build(pa, h->pp, h->lds, st, ev), "persistent expansion launch");
+        } else {
+            for (int t = 0; t < h->pipe_T; ++t) {
+                DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
+                DT_TRY(dt::launch_pipe_step(pa, h->pp, h->lds, t, st, ev), "fused expansion launch");
+            }
         }
         DT_TRY(mark(h, call, 1, 'E', st), "timing event");
         return DT_OK;

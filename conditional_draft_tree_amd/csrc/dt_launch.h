@@ -193,6 +193,9 @@ struct PipeArgs {
     float* hstate;        // [B][n+1][H] binary32 state per slot (slot 0 = h0)
     int32_t* exp_at;      // [B][n+1] launch that expanded the slot
     unsigned* done;       // [T] contraction workgroups finished, per launch
+    unsigned* gflag;      // [ng] persistent launch: last step each contraction workgroup finished
+    unsigned* nflag;      // [B] persistent launch: steps each node workgroup finished
+    unsigned* perr;       // a wait of the persistent launch ran out (nonzero)
     int32_t* active;      // [2][T] launch t's contraction has a row; some request waits for it
     uint16_t* wpack;      // the weights in operand tiles (written by launch 0)
     int32_t* child_tok;   // [B, n+1, 64]
@@ -220,6 +223,14 @@ struct PipePlan {
 PipePlan pipe_plan(int B, int L, int E, int H, int M, int n);
 hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, int t, hipStream_t stream,
                             LaunchEvents ev = {});
+// The same expansion as one cooperative launch of the same grid: every step of
+// the call, the workgroups kept resident and handing over through counters
+// (see expand.hip).  pers_supported: the device can hold the whole grid at
+// once (checked once per plan); launch_pers_build zeroes the call's counters
+// and launches.
+bool pers_supported(const PipePlan& pp, int B);
+hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
+                             LaunchEvents ev = {});
 
 // Conditional children distribution of one node per row (dt_correct).
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,

@@ -867,6 +867,138 @@ __device__ __forceinline__ P by_parity(P const (&p)[2], int i) {
 __device__ __forceinline__ float ld_agent(const float* p) {
     return __uint_as_float(__hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+__device__ __forceinline__ int ld_agent_i(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_i(int32_t* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- hand-over inside one launch (the persistent launch, and a request that
+// waits for its launch's contraction).  Each XCD has its own L2, written back
+// to memory only at the end of a kernel.  Data that another XCD reads in the
+// same launch is therefore stored with the device-scope cache policy (sc1:
+// written through to the device-coherent level) and read with it (sc1 loads,
+// and the sc1 copy into LDS), and once the stores are complete (vmcnt(0)) the
+// workgroup's own flag word is set to the step it finished: no L2 writeback
+// or invalidation is needed, what a workgroup keeps for itself stays cached,
+// and no two workgroups update one word (same-address atomics from every
+// workgroup serialize).
+constexpr int kCpolSc1 = 16;  // cache-policy operand of buffer and LDS-copy builtins: sc1
+// Buffer resource over a buffer whose offsets fit 32 bits (uniform base)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void st_through(__amdgpu_buffer_rsrc_t r, size_t byte_off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kCpolSc1);
+}
+// Wait (wave 0, bounded) until every flag f[0 .. n) (n <= 256) is at least
+// target -- lane l reads flags l, l + 64, ... with device-coherent loads --
+// then the workgroup barrier.  A wait that runs out, or finds that another
+// wait ran out, raises *perr and returns: every workgroup still runs to its
+// end.
+// poll_flags: the same wait by one wave, without the barrier.
+__device__ __forceinline__ void poll_flags(const unsigned* f, int n, unsigned target, unsigned* perr) {
+    const int l = lane_id();
+    unsigned spins = 0;
+    for (;;) {
+        bool ok = true;  // (the loads issued together)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = min(l + i * kWave, n - 1);
+            ok &= __hip_atomic_load(f + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
+        }
+        if (__ballot(!ok) == 0ull) break;
+        if ((++spins & 63u) == 0u &&
+            (spins >= kPipeSpinLimit || __hip_atomic_load(perr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            if (l == 0) __hip_atomic_fetch_or(perr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+__device__ __forceinline__ void wait_flags(const unsigned* f, int n, unsigned target, unsigned* perr) {
+    if (threadIdx.x < kWave) poll_flags(f, n, target, perr);
+    __syncthreads();
+}
+__device__ __forceinline__ void set_flag(unsigned* f, unsigned v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The four quarters of each unit tile (waves 4 u + 0 .. 3) added in order,
+// quarter 0 first, and stored (when `store`): every wave leaves its sums in
+// LDS ([wave][rb * 3 + slot][lane]); wave 4 u + q then adds up and stores the
+// slot vectors j = q, q + 4, ... of the unit tile.  Lane l holds units 4 (l /
+// 16) .. + 3 of row l % 16 of each row block.  gi by launch parity, gh by the
+// slot of the state (hsl_r: thread i < B holds row i's slot, loaded before
+// the tile and put into LDS here, after it).  COH: the stores are written
+// through (read by other workgroups in the same launch).
+template <int RB, bool COH>
+__device__ __forceinline__ void gate_sums(const PipeArgs& a, int t, int ug, int kind, int ksub, int hsl_r, bool store,
+                                          gate::f32x4 (&acc)[RB][3], float* lds, int* s_hsl) {
+    __syncthreads();  // every wave is done with the staged activations
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
+    const int u = wave / gate::kT32Quarters, qt = wave % gate::kT32Quarters;
+    gate::f32x4* red = reinterpret_cast<gate::f32x4*>(lds);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) red[(wave * RB * 3 + rb * 3 + sl) * kWave + lane] = acc[rb][sl];
+    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = hsl_r;
+    __syncthreads();
+    if (!store) return;
+    // (the fields are read into values first: selecting between fields of
+    // the kernel argument would copy the argument to scratch)
+    float* const gi = a.gi;
+    float* const gh = a.gh;
+    const int B = a.B, H = a.H, ksx = a.ksx, ksh = a.ksh, S = a.n + 1, par = t & 1;
+    const int unit = ug * 32 + u * 16 + (lane >> 4) * 4;
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(kind == 0 ? (const void*)gi : (const void*)gh);
+#pragma unroll
+    for (int j0 = 0; j0 < RB * 3; j0 += gate::kT32Quarters) {
+        const int j = j0 + qt;  // (wave-uniform)
+        if (j >= RB * 3) break;
+        const int rb = j / 3, sl = j % 3;
+        gate::f32x4 sum = red[((u * gate::kT32Quarters) * RB * 3 + j) * kWave + lane];
+#pragma unroll
+        for (int q = 1; q < gate::kT32Quarters; ++q)
+            sum += red[((u * gate::kT32Quarters + q) * RB * 3 + j) * kWave + lane];
+        const int row = rb * 16 + (lane & 15);
+        const int hsl = kind ? s_hsl[min(row, B - 1)] : 0;
+        if (row >= B || (kind && (hsl < 0 || hsl >= S))) continue;
+        const size_t off = kind == 0 ? (((size_t)(par * ksx + ksub) * B + row) * 3 + sl) * H + unit
+                                     : ((((size_t)row * S + hsl) * ksh + ksub) * 3 + sl) * H + unit;
+        if constexpr (COH) st_through(rs, off * 4, __builtin_bit_cast(u32x4, sum));
+        else *reinterpret_cast<gate::f32x4*>((kind == 0 ? gi : gh) + off) = sum;
+    }
+}
+
+// A node workgroup's record between the steps of the persistent launch, in
+// LDS after the slots' expansion steps: queue, unsorted child keys, handed-over
+// candidates, state words, the two x-row tokens.
+struct PersLds {
+    u64* q;
+    u64* ckey;
+    int32_t* nidx;
+    float* nval;
+    int32_t* rs;
+    int32_t* xt;
+};
+constexpr size_t kPersLdsBytes = 64 * 8 * 2 + 64 * 4 * 2 + kStateWords * 4 + 16;
+__host__ __device__ inline size_t pers_lds_offset(const NodeLds& lp, int n) {
+    return lp.bytes + (((size_t)n + 1) * 4 + 15) / 16 * 16;  // (bytes; after s_exp)
+}
+__device__ __forceinline__ PersLds pers_lds(float* lds, const NodeLds& lp, int n) {
+    char* p = reinterpret_cast<char*>(lds) + pers_lds_offset(lp, n);
+    PersLds r;
+    r.q = reinterpret_cast<u64*>(p);
+    r.ckey = r.q + 64;
+    r.nidx = reinterpret_cast<int32_t*>(r.ckey + 64);
+    r.nval = reinterpret_cast<float*>(r.nidx + 64);
+    r.rs = reinterpret_cast<int32_t*>(r.nval + 64);
+    r.xt = r.rs + kStateWords;
+    return r;
+}
 
 // Contraction role: 32 hidden units x one K range of launch t's rows (the
 // 32-unit tile of gate_tile.h: the activations staged in LDS once per
@@ -904,7 +1036,7 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
     if (t == a.T - 1 &&
         __hip_atomic_load(a.active + a.T + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
         return;
-    const int par = t & 1, S = a.n + 1;
+    const int par = t & 1;
     // this launch's flags: some row needs the contraction (launch 1 always
     // has rows); some request waits for its sums in this launch, so they are
     // published (release) and the workgroup counted -- otherwise they are
@@ -930,45 +1062,7 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
     g.wmode = WM;
     gate::f32x4 acc[RB][3];
     gate::tile32_lds<WM, RB>(g, ug, kind, ksub, nsub, reinterpret_cast<gate::u32x4*>(lds), acc);
-    __syncthreads();  // every wave is done with the staged activations
-    // the four quarters of each unit tile (waves 4 u + 0 .. 3) are added in
-    // order, quarter 0 first: every wave leaves its sums in LDS ([wave][rb *
-    // 3 + slot][lane]); wave 4 u + q then adds up and stores the slot vectors
-    // j = q, q + 4, ... of the unit tile.  Lane l holds units 4 (l / 16) .. +
-    // 3 of row l % 16 of each row block.
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
-    const int u = wave / gate::kT32Quarters, qt = wave % gate::kT32Quarters;
-    gate::f32x4* red = reinterpret_cast<gate::f32x4*>(lds);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int sl = 0; sl < 3; ++sl) red[(wave * RB * 3 + rb * 3 + sl) * kWave + lane] = acc[rb][sl];
-    if ((int)threadIdx.x < a.B) s_hsl[threadIdx.x] = hsl_r;
-    __syncthreads();
-    if (t == 1 || act != 0) {
-        // (the fields are read into values first: selecting between fields of
-        // the kernel argument would copy the argument to scratch)
-        float* const gi = a.gi;
-        float* const gh = a.gh;
-        const int B = a.B, H = a.H, ksx = a.ksx, ksh = a.ksh;
-        const int unit = ug * 32 + u * 16 + (lane >> 4) * 4;
-#pragma unroll
-        for (int j0 = 0; j0 < RB * 3; j0 += gate::kT32Quarters) {
-            const int j = j0 + qt;  // (wave-uniform)
-            if (j >= RB * 3) break;
-            const int rb = j / 3, sl = j % 3;
-            gate::f32x4 sum = red[((u * gate::kT32Quarters) * RB * 3 + j) * kWave + lane];
-#pragma unroll
-            for (int q = 1; q < gate::kT32Quarters; ++q)
-                sum += red[((u * gate::kT32Quarters + q) * RB * 3 + j) * kWave + lane];
-            const int row = rb * 16 + (lane & 15);
-            const int hsl = kind ? s_hsl[min(row, B - 1)] : 0;
-            if (row >= B || (kind && (hsl < 0 || hsl >= S))) continue;
-            float* dst = kind == 0 ? gi + (((size_t)(par * ksx + ksub) * B + row) * 3 + sl) * H + unit
-                                   : gh + ((((size_t)row * S + hsl) * ksh + ksub) * 3 + sl) * H + unit;
-            *reinterpret_cast<gate::f32x4*>(dst) = sum;
-        }
-    }
+    gate_sums<RB, false>(a, t, ug, kind, ksub, hsl_r, t == 1 || act != 0, acc, lds, s_hsl);
     if (publish) {
         // every store of the workgroup has reached the L2; thread 0 writes the
         // L2 back (agent-scope release) and counts the workgroup
@@ -981,10 +1075,57 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
     }
 }
 
-// Node role: request b's step at launch t.
+// Contraction role of the persistent launch: the workgroup's weights are
+// loaded into registers once, then every step t = 1 .. T - 1 waits for the
+// node workgroups' step t - 1 (their activations), contracts and counts
+// itself.  The last step runs only if some request waits in it.
+template <int KIND, int RB>
+__device__ __forceinline__ void pers_gate_loop(const PipeArgs& a, GruGatesArgs& g, const gate::T32Wave& r, int ug,
+                                               int ksub, float* lds) {
+    __shared__ int s_hsl[kMaxB];
+    gate::bf16x8 w[gate::t32_xbatch(RB)][3];
+    gate::t32_load_weights<KIND, false, RB>(g, r, w);
+    for (int t = 1; t < a.T; ++t) {
+        wait_flags(a.nflag, a.B, (unsigned)t, a.perr);  // every node workgroup finished step t - 1
+        if (t == a.T - 1 && ld_agent_i(a.active + a.T + t) == 0) break;
+        const int par = t & 1;
+        const int hsl_r = (int)threadIdx.x < a.B ? ld_agent_i(by_parity(a.hslot, par) + threadIdx.x) : -1;
+        g.xpack = by_parity(a.xpack, par);
+        g.hpack = by_parity(a.hpack, par);
+        gate::f32x4 acc[RB][3];
+        gate::t32_contract<KIND, false, RB, kCpolSc1>(g, r, reinterpret_cast<gate::u32x4*>(lds), w, acc);
+        gate_sums<RB, true>(a, t, ug, KIND, ksub, hsl_r, true, acc, lds, s_hsl);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sums are written through
+        __syncthreads();
+        if (threadIdx.x == 0) set_flag(a.gflag + blockIdx.x, (unsigned)t);
+    }
+}
+template <int RB>
+__device__ __forceinline__ void pers_gate(const PipeArgs& a, float* lds) {
+    const int groups = a.H / 32;
+    const int ug = (int)blockIdx.x % groups, kw = (int)blockIdx.x / groups;
+    const int kind = kw >= a.ksx, ksub = kind ? kw - a.ksx : kw, nsub = kind ? a.ksh : a.ksx;
+    GruGatesArgs g{};
+    g.W_ih = a.W_ih;
+    g.W_hh = a.W_hh;
+    g.B = a.B;
+    g.E = a.E;
+    g.H = a.H;
+    g.ksplit = 1;
+    g.dtype = 1;
+    const gate::T32Wave r = gate::t32_wave(g, ug, kind, ksub, nsub);
+    if (kind == 0) pers_gate_loop<0, RB>(a, g, r, ug, ksub, lds);
+    else pers_gate_loop<1, RB>(a, g, r, ug, ksub, lds);
+}
+
+// Node role: request b's step at launch t.  PERS: step t of the persistent
+// launch -- it first waits for the contraction of step t - 1, reads the gate
+// sums and writes the next step's rows coherently, and counts itself at the
+// end (its own records stay in its XCD's caches).
 enum PipeMode { kRoot, kExpand, kWait, kTrivial, kIdle, kDone };
 
-__device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, int t, float* lds) {
+template <bool PERS>
+__device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, int t, float* lds, int tid) {
     constexpr int NT = kPipeThreads, RW = kPipeRows;
     constexpr int P = 8;                    // bf16 elements per 16-byte vector
     constexpr int kChunk = 2 * kWave * P;   // K elements of a gathered chunk
@@ -999,38 +1140,62 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     float* s_clp = lds + lp.clp;
     int32_t* s_exp = (int32_t*)(lds + lp.bytes / 4);  // [n+1] launch that expanded each slot
     __shared__ int s_dec[4];  // x-row token and h-row slot of the next launch, mode
+    // persistent launch: the request's record from step to step, in LDS (the
+    // top-M table, child lists, scores, parents and expansion steps stay in
+    // their LDS arrays)
+    PersLds ps = pers_lds(lds, lp, a.n);
 
     const int b = (int)blockIdx.x - a.ng;
-    const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int S = a.n + 1, H = a.H, M = a.M, LM = a.L * a.M;
     const size_t slot0 = (size_t)b * S;
     const int pt = t & 1, pn = (t + 1) & 1;  // this launch's parity; the next's (= the previous one's)
     const int KSX = a.ksx, KSH = a.ksh;  // partial sums of the x part and of the h part
-
-    // ---- round trip 1 (every address valid in every mode)
-    const i32x4 rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
-    const i32x4 rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
-    const u64 q_m = a.queue[(size_t)b * kWave + lane];
-    const int xt_prev = by_parity(a.xtok, pn)[b];  // launch t-1's x row
-    const int xt_cur = by_parity(a.xtok, pt)[b];   // this launch's x row
+    // (a gate sum of the persistent launch: written through by another XCD)
+    auto ld_sum = [](const float* p) { return PERS ? ld_agent(p) : *p; };
+    // ---- round trip 1 (every address valid in every mode); the persistent
+    // launch takes the request's record from LDS
+    i32x4 rs0, rs1;
+    u64 q_m;
+    int xt_prev, xt_cur;  // launch t-1's x row, this launch's
     const int jl = min(lane, M - 1);
-    const int32_t* ip = t == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
-    const float* vp = t == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
-    const int my_tok = min(max(ip[jl], 0), a.V - 1);
-    const float my_val = vp[jl];
+    int my_tok;
+    float my_val;
+    if constexpr (PERS) {
+        rs0 = *reinterpret_cast<const i32x4*>(ps.rs);
+        rs1 = *reinterpret_cast<const i32x4*>(ps.rs + 4);
+        q_m = ps.q[lane];
+        xt_prev = ps.xt[pn];
+        xt_cur = ps.xt[pt];
+        my_tok = min(max(ps.nidx[jl], 0), a.V - 1);  // (step 0: the root's, put there before the steps)
+        my_val = ps.nval[jl];
+    } else {
+        rs0 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords);
+        rs1 = *reinterpret_cast<const i32x4*>(a.rstate + (size_t)b * kStateWords + 4);
+        q_m = a.queue[(size_t)b * kWave + lane];
+        xt_prev = by_parity(a.xtok, pn)[b];
+        xt_cur = by_parity(a.xtok, pt)[b];
+        const int32_t* ip = t == 0 ? a.tidx + (size_t)b * LM : a.nidx + (size_t)b * kWave;
+        const float* vp = t == 0 ? a.tval + (size_t)b * LM : a.nval + (size_t)b * kWave;
+        my_tok = min(max(ip[jl], 0), a.V - 1);
+        my_val = vp[jl];
+    }
     // this thread's state elements k1 and k1 + NT (H <= 2 NT)
-    const int k1 = (int)threadIdx.x, k2 = k1 + NT;
+    const int k1 = tid, k2 = k1 + NT;
     const int kc1 = k1 < H ? k1 : 0, kc2 = k2 < H ? k2 : 0;
     float gi[2][kPipeMaxKs][3];
+    auto load_gi = [&]() {
 #pragma unroll
-    for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
+        for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
 #pragma unroll
-        for (int g = 0; g < 3; ++g) {
-            const size_t base = (((size_t)(pn * KSX + min(s2, KSX - 1)) * a.B + b) * 3 + g) * H;
-            gi[0][s2][g] = a.gi[base + kc1];
-            gi[1][s2][g] = a.gi[base + kc2];
-        }
+            for (int g = 0; g < 3; ++g) {
+                const size_t base = (((size_t)(pn * KSX + min(s2, KSX - 1)) * a.B + b) * 3 + g) * H;
+                gi[0][s2][g] = ld_sum(a.gi + base + kc1);
+                gi[1][s2][g] = ld_sum(a.gi + base + kc2);
+            }
+    };
+    if constexpr (!PERS) load_gi();
     // (loads without branches, from a stand-in address when a pointer is
     // NULL, so that every path issues the same loads: the in-order load
     // counters then let round trip 2 wait for exactly what it needs)
@@ -1071,8 +1236,8 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     const int nkid = a.n * kMaxM;
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
-        const int e = ((int)threadIdx.x + u * NT) * 4;
-        const bool te = tvec && e < LM, ke = t > 0 && e < nkid;
+        const int e = (tid + u * NT) * 4;
+        const bool te = tvec && e < LM && (!PERS || t == 0), ke = !PERS && t > 0 && e < nkid;
         r_ti[u] = te ? *reinterpret_cast<const i32x4*>(ti + e) : i32x4{0, 0, 0, 0};
         r_tv[u] = te ? *reinterpret_cast<const f32x4*>(tv + e) : f32x4{0.f, 0.f, 0.f, 0.f};
         r_ct[u] = ke ? *reinterpret_cast<const i32x4*>(kt + e) : i32x4{0, 0, 0, 0};
@@ -1080,10 +1245,10 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     }
     float r_sc = 0.f;
     int r_par = -1, r_exp = 0;
-    if (t > 0 && (int)threadIdx.x < S) {
-        r_sc = a.scores[slot0 + threadIdx.x];
-        r_par = a.parents[slot0 + threadIdx.x];
-        r_exp = a.exp_at[slot0 + threadIdx.x];
+    if (!PERS && t > 0 && tid < S) {
+        r_sc = a.scores[slot0 + tid];
+        r_par = a.parents[slot0 + tid];
+        r_exp = a.exp_at[slot0 + tid];
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -1120,21 +1285,33 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     float gh[2][kPipeMaxKs][3];
     float hp[2];
     const float* ghp = a.gh + (slot0 + cp) * (size_t)KSH * 3 * H;
+    auto load_gh = [&]() {
 #pragma unroll
-    for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
+        for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
 #pragma unroll
-        for (int g = 0; g < 3; ++g) {
-            const size_t o = ((size_t)min(s2, KSH - 1) * 3 + g) * H;
-            gh[0][s2][g] = ghp[o + kc1];
-            gh[1][s2][g] = ghp[o + kc2];
-        }
+            for (int g = 0; g < 3; ++g) {
+                const size_t o = ((size_t)min(s2, KSH - 1) * 3 + g) * H;
+                gh[0][s2][g] = ld_sum(ghp + o + kc1);
+                gh[1][s2][g] = ld_sum(ghp + o + kc2);
+            }
+    };
+    if constexpr (!PERS) load_gh();
     {
         const float* hpp = a.hstate + (slot0 + cp) * H;
         hp[0] = hpp[kc1];
         hp[1] = hpp[kc2];
     }
-    const u64 prev_keys = a.ckey[(slot0 + (unsorted >= 0 ? unsorted : 0)) * kMaxM + lane];
+    const u64 prev_keys = PERS ? ps.ckey[lane] : a.ckey[(slot0 + (unsorted >= 0 ? unsorted : 0)) * kMaxM + lane];
     if (t == 0 || cand) gather(0);
+    if constexpr (PERS) {
+        // with the gathers in flight: wait for the contraction of step t - 1
+        // (its sums, and the end of its reads of the activation buffers that
+        // this step rewrites; step 1 reads no sums and writes buffers no
+        // contraction has read), then read its sums
+        if (t >= 2) wait_flags(a.gflag, a.ng, (unsigned)(t - 1), a.perr);
+        load_gi();
+        load_gh();
+    }
     // this launch's mode (uniform over the workgroup)
     int mode;
     if (t == 0) mode = kRoot;
@@ -1145,42 +1322,47 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     else mode = kWait;                                           // none left: take this launch's
     const bool grow = mode == kRoot || mode == kExpand || mode == kWait;
 
-    // ---- stage into LDS
+    // ---- stage into LDS (the persistent launch: once, at step 0)
+    const bool stage = !PERS || t == 0;
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
-        const int e = ((int)threadIdx.x + u * NT) * 4;
-        if (tvec && e < LM) {
+        const int e = (tid + u * NT) * 4;
+        if (stage && tvec && e < LM) {
             *reinterpret_cast<i32x4*>(s_tidx + e) = r_ti[u];
             *reinterpret_cast<f32x4*>(s_tval + e) = r_tv[u];
         }
-        if (e < nkid) {
+        if (!PERS && e < nkid) {
             *reinterpret_cast<i32x4*>(s_ctok + e) = r_ct[u];
             *reinterpret_cast<f32x4*>(s_clp + e) = r_cl[u];
         }
     }
-    if (!tvec)
-        for (int e = threadIdx.x; e < LM; e += NT) {
+    if (stage && !tvec)
+        for (int e = tid; e < LM; e += NT) {
             s_tidx[e] = ti[e];
             s_tval[e] = tv[e];
         }
-    if ((int)threadIdx.x < S) {
-        s_sc[threadIdx.x] = threadIdx.x == 0 ? 0.f : r_sc;
-        s_par[threadIdx.x] = threadIdx.x == 0 ? -1 : r_par;
-        s_exp[threadIdx.x] = r_exp;
+    if (stage && tid < S) {
+        s_sc[tid] = tid == 0 ? 0.f : r_sc;
+        s_par[tid] = tid == 0 ? -1 : r_par;
+        s_exp[tid] = r_exp;
     }
 
     // ---- wait for this launch's contraction (bounded), then take its sums
     if (mode == kWait) {
-        if (threadIdx.x == 0) {
-            unsigned spins = 0;
-            while (__hip_atomic_load(a.done + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.ng &&
-                   ++spins < kPipeSpinLimit)
-                __builtin_amdgcn_s_sleep(2);
-            s_dec[3] = spins >= kPipeSpinLimit;
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // (lines of the sums cached earlier are stale)
+        if constexpr (PERS) {  // every contraction workgroup finished step t
+            wait_flags(a.gflag, a.ng, (unsigned)t, a.perr);
+        } else {
+            if (tid == 0) {
+                unsigned spins = 0;
+                while (__hip_atomic_load(a.done + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)a.ng &&
+                       ++spins < kPipeSpinLimit)
+                    __builtin_amdgcn_s_sleep(2);
+                s_dec[3] = spins >= kPipeSpinLimit;
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // (lines of the sums cached earlier are stale)
+            }
+            __syncthreads();
+            if (s_dec[3]) flag |= kPipeTimeoutFlag;
         }
-        __syncthreads();
-        if (s_dec[3]) flag |= kPipeTimeoutFlag;
 #pragma unroll
         for (int s2 = 0; s2 < kPipeMaxKs; ++s2)
 #pragma unroll
@@ -1319,7 +1501,8 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             const float tz = __int_as_float(
                 __builtin_amdgcn_readlane(__float_as_int(tail_l), min(edepth, a.L - 1)));
             ckey = child_keys_r(my_val, zs[lane], my_tok, M, a.temp, tz);
-            a.ckey[(slot0 + ecur) * kMaxM + lane] = ckey;  // sorted at the next launch
+            if constexpr (PERS) ps.ckey[lane] = ckey;  // sorted at the next step
+            else a.ckey[(slot0 + ecur) * kMaxM + lane] = ckey;  // sorted at the next launch
             best = wave_max_u64(ckey);
             second = wave_max_u64(ckey == best ? 0ull : ckey);
             kbest = queue_key(sc_e + child_lp_of(best), edepth + 1, ecur, 0);
@@ -1386,8 +1569,13 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                 s_par[v] = v_par;
             }
             if (pd < a.L) {  // hand over the popped node's candidates
-                a.nidx[(size_t)b * kWave + lane] = take_a ? hi_a : hi_b;
-                a.nval[(size_t)b * kWave + lane] = take_a ? hv_a : hv_b;
+                if constexpr (PERS) {
+                    ps.nidx[lane] = take_a ? hi_a : hi_b;
+                    ps.nval[lane] = take_a ? hv_a : hv_b;
+                } else {
+                    a.nidx[(size_t)b * kWave + lane] = take_a ? hi_a : hi_b;
+                    a.nval[(size_t)b * kWave + lane] = take_a ? hv_a : hv_b;
+                }
             }
             // the next launch's x row: the popped node's token when it cannot
             // expand at t + 1, else the token of the best entry left (the
@@ -1423,14 +1611,25 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         // (waves 4 .. 7)
         const int xn = s_dec[0], hn = s_dec[1];
         if (wave < 4) {
-            if (xn < 0) return;
-            const int nv = a.E >> 3;
-            for (int i = (wave - 1) * kWave + lane; i < nv; i += 3 * kWave) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + (size_t)xn * a.E + i * 8);
-                *reinterpret_cast<u32x4*>(by_parity(a.xpack, pn) + pack_index_x(b, i * 8, a.E)) = v;
+            if (xn < 0) {
+                if constexpr (!PERS) return;
+            } else {
+                uint16_t* const xp = by_parity(a.xpack, pn);
+                const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(xp);
+                const int nv = a.E >> 3;
+                for (int i = (wave - 1) * kWave + lane; i < nv; i += 3 * kWave) {
+                    const u32x4 v =
+                        *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + (size_t)xn * a.E + i * 8);
+                    const size_t o = pack_index_x(b, i * 8, a.E);
+                    if constexpr (PERS) st_through(rx, o * 2, v);
+                    else *reinterpret_cast<u32x4*>(xp + o) = v;
+                }
             }
+        } else if (hn < 0) {
+            if constexpr (!PERS) return;
         } else {
-            if (hn < 0) return;
+            uint16_t* const hq = by_parity(a.hpack, pn);
+            const __amdgpu_buffer_rsrc_t rh = coherent_rsrc(hq);
             const int nv = H >> 3;
             for (int i = (wave - 4) * kWave + lane; i < nv; i += 4 * kWave) {
                 const int k = i * 8;
@@ -1443,65 +1642,90 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                     for (int qq = 0; qq < 3; ++qq) w[qq][e >> 1] |= p3[qq] << (16 * (e & 1));
                 }
 #pragma unroll
-                for (int qq = 0; qq < 3; ++qq)
-                    *reinterpret_cast<u32x4*>(by_parity(a.hpack, pn) + pack_index_h(b, qq, k, H)) =
-                        u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]};
-            }
-        }
-        return;
-    }
-
-    // ---- wave 0: the request's record for the next launch, outputs
-    if (t == 0) {  // the empty tree around the root
-        for (int i = lane; i < S; i += kWave) {
-            if (i == 0) {
-                a.tokens[slot0] = -1;
-                a.parents[slot0] = -1;
-                a.depths[slot0] = 0;
-                a.scores[slot0] = 0.f;
-            } else if (i >= 2 || new_cnt < 1) {  // slot 1 is this launch's pop
-                a.tokens[slot0 + i] = -1;
-                a.parents[slot0 + i] = -1;
-                a.depths[slot0 + i] = -1;
-                a.scores[slot0 + i] = -INFINITY;
-            }
-        }
-        if (lane == 0) by_parity(a.xtok, pt)[b] = -1;  // (the parity launch 1 reads as "previous")
-    }
-    a.queue[(size_t)b * kWave + lane] = q;
-    if (lane == 0) {
-        if (grow) a.exp_at[slot0 + ecur] = t;
-        by_parity(a.xtok, pn)[b] = xtok_next;
-        by_parity(a.hslot, pn)[b] = hslot_next;
-        if ((xtok_next >= 0 || hslot_next >= 0) && t + 1 < a.T) a.active[t + 1] = 1;
-        if (wait_next && t + 1 < a.T) a.active[a.T + t + 1] = 1;  // its contraction publishes
-        const int nd = new_cur == cur && !pops ? (rs1[3] & 0xffff) | (pexp << 16) : pd | (vexp_rec << 16);
-        const int ntok = new_cur == cur && !pops ? ctok : ptok;
-        const int npar = new_cur == cur && !pops ? cpar : v_par;
-        int32_t* rs = a.rstate + (size_t)b * kStateWords;
-        *reinterpret_cast<i32x4*>(rs) = i32x4{new_cnt, new_cur, qs, (int)flag};
-        *reinterpret_cast<i32x4*>(rs + 4) = i32x4{grow ? ecur : -1, ntok, npar < 0 ? 0 : npar, nd};
-        a.count[b] = new_cnt;
-        a.flags[b] = flag;
-    }
-
-    // ---- ancestor-only mask, at the call's last launch
-    if (t == a.T - 1) {
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-        for (int i = lane; i < S; i += kWave) {
-            uint8_t* row = a.mask + ((size_t)b * S + i) * S;
-            u64 bits_lo = 0ull;
-            bool bit64 = false;
-            if (i <= new_cnt) {
-                for (int j = i; j >= 0; j = j == 0 ? -1 : s_par[j]) {
-                    if (j < 64) bits_lo |= 1ull << j;
-                    else bit64 = true;
+                for (int qq = 0; qq < 3; ++qq) {
+                    const u32x4 v = u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]};
+                    const size_t o = pack_index_h(b, qq, k, H);
+                    if constexpr (PERS) st_through(rh, o * 2, v);
+                    else *reinterpret_cast<u32x4*>(hq + o) = v;
                 }
             }
-            for (int j = 0; j < S; ++j)
-                row[j] = (uint8_t)(j < 64 ? ((bits_lo >> j) & 1ull) : (bit64 ? 1 : 0));
         }
+        if constexpr (!PERS) return;
+    } else {
+        // ---- wave 0: the request's record for the next launch, outputs
+        if (t == 0) {  // the empty tree around the root
+            for (int i = lane; i < S; i += kWave) {
+                if (i == 0) {
+                    a.tokens[slot0] = -1;
+                    a.parents[slot0] = -1;
+                    a.depths[slot0] = 0;
+                    a.scores[slot0] = 0.f;
+                } else if (i >= 2 || new_cnt < 1) {  // slot 1 is this launch's pop
+                    a.tokens[slot0 + i] = -1;
+                    a.parents[slot0 + i] = -1;
+                    a.depths[slot0 + i] = -1;
+                    a.scores[slot0 + i] = -INFINITY;
+                }
+            }
+            if (lane == 0) {  // (the parity launch 1 reads as "previous")
+                if constexpr (PERS) ps.xt[pt] = -1;
+                else by_parity(a.xtok, pt)[b] = -1;
+            }
+        }
+        if constexpr (PERS) ps.q[lane] = q;
+        else a.queue[(size_t)b * kWave + lane] = q;
+        if (lane == 0) {
+            if constexpr (PERS) {
+                if (grow) s_exp[ecur] = t;
+                ps.xt[pn] = xtok_next;
+            } else {
+                if (grow) a.exp_at[slot0 + ecur] = t;
+                by_parity(a.xtok, pn)[b] = xtok_next;
+            }
+            if constexpr (PERS) {  // (read by the contraction workgroups in this launch)
+                st_agent_i(by_parity(a.hslot, pn) + b, hslot_next);
+                if (wait_next && t + 1 < a.T) st_agent_i(a.active + a.T + t + 1, 1);  // its contraction runs
+                if (t == a.T - 1 && __hip_atomic_load(a.perr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                    flag |= kPipeTimeoutFlag;  // some wait of the launch ran out
+            } else {
+                by_parity(a.hslot, pn)[b] = hslot_next;
+                if ((xtok_next >= 0 || hslot_next >= 0) && t + 1 < a.T) a.active[t + 1] = 1;
+                if (wait_next && t + 1 < a.T) a.active[a.T + t + 1] = 1;  // its contraction publishes
+            }
+            const int nd = new_cur == cur && !pops ? (rs1[3] & 0xffff) | (pexp << 16) : pd | (vexp_rec << 16);
+            const int ntok = new_cur == cur && !pops ? ctok : ptok;
+            const int npar = new_cur == cur && !pops ? cpar : v_par;
+            int32_t* rs = PERS ? ps.rs : a.rstate + (size_t)b * kStateWords;
+            *reinterpret_cast<i32x4*>(rs) = i32x4{new_cnt, new_cur, qs, (int)flag};
+            *reinterpret_cast<i32x4*>(rs + 4) = i32x4{grow ? ecur : -1, ntok, npar < 0 ? 0 : npar, nd};
+            a.count[b] = new_cnt;
+            a.flags[b] = flag;
+        }
+
+        // ---- ancestor-only mask, at the call's last launch
+        if (t == a.T - 1) {
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+            for (int i = lane; i < S; i += kWave) {
+                uint8_t* row = a.mask + ((size_t)b * S + i) * S;
+                u64 bits_lo = 0ull;
+                bool bit64 = false;
+                if (i <= new_cnt) {
+                    for (int j = i; j >= 0; j = j == 0 ? -1 : s_par[j]) {
+                        if (j < 64) bits_lo |= 1ull << j;
+                        else bit64 = true;
+                    }
+                }
+                for (int j = 0; j < S; ++j)
+                    row[j] = (uint8_t)(j < 64 ? ((bits_lo >> j) & 1ull) : (bit64 ? 1 : 0));
+            }
+        }
+    }
+    if constexpr (PERS) {
+        // the step's coherent stores are complete: count the workgroup
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) set_flag(a.nflag + b, (unsigned)(t + 1));
     }
 }
 
@@ -1509,7 +1733,47 @@ template <int WM, int RB>
 __global__ __launch_bounds__(kPipeThreads) void pipe_kernel(PipeArgs a, NodeLds lp, int t) {
     extern __shared__ __attribute__((aligned(16))) float lds[];  // (16-byte vector accesses)
     if ((int)blockIdx.x < a.ng) pipe_gate<WM, RB>(a, t, lds);
-    else pipe_node(a, lp, t, lds);
+    else pipe_node<false>(a, lp, t, lds, (int)threadIdx.x);
+}
+
+// The persistent launch: the same grid and roles, every step of the call.
+// A contraction workgroup keeps its weights in registers; a node workgroup
+// keeps its request's records in its XCD's caches.  Step t's contraction
+// waits for the node workgroups' step t - 1 and the node workgroups' step t
+// for step t - 1's contraction (and a waiting request for step t's), so the
+// two roles run one step apart, as the launches do.  Co-residency of the
+// grid is guaranteed by the cooperative launch; every wait is bounded.
+template <int RB>
+__global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds lp) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // (16-byte vector accesses)
+    if ((int)blockIdx.x < a.ng) {
+        pers_gate<RB>(a, lds);
+    } else {
+        {  // the root's candidates, where every step reads the node's
+            const int b = (int)blockIdx.x - a.ng, LM = a.L * a.M;
+            const PersLds ps = pers_lds(lds, lp, a.n);
+            if ((int)threadIdx.x < a.M) {
+                ps.nidx[threadIdx.x] = a.tidx[(size_t)b * LM + threadIdx.x];
+                ps.nval[threadIdx.x] = a.tval[(size_t)b * LM + threadIdx.x];
+            }
+            __syncthreads();
+        }
+        for (int t = 0; t < a.T; ++t) {
+            // (the thread index through an opaque copy in each step: what is
+            // derived from it, such as the per-lane addresses, is then
+            // computed in the step and not held across the steps)
+            int tid = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            pipe_node<true>(a, lp, t, lds, tid);
+        }
+    }
+}
+
+// The persistent launch's flags, cleared before it starts: gflag [ng], nflag
+// [B] and the error word (one run of words), active [2T].
+__global__ void pers_clear_kernel(unsigned* flags, int nflags, int32_t* active, int T) {
+    for (int i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0u;
+    for (int i = threadIdx.x; i < 2 * T; i += blockDim.x) active[i] = 0;
 }
 
 }  // namespace
@@ -1572,7 +1836,7 @@ PipePlan pipe_plan(int B, int L, int E, int H, int M, int n) {
     p.rb = gate::row_blocks(B);
     if (!gate::t32_fits(E / 32, H / 32, p.ksx, p.ksh, p.rb)) return PipePlan{};  // one weight batch per wave
     const NodeLds lp = node_lds_plan(L, M, n, H);
-    const size_t node = lp.bytes + (((size_t)n + 1) * 4 + 15) / 16 * 16;  // + the slots' expansion launches
+    const size_t node = pers_lds_offset(lp, n) + kPersLdsBytes;  // + the slots' expansion launches, the record
     const size_t red = (size_t)kPipeWaves * p.rb * 3 * kWave * 16;  // the waves' sums
     const size_t gates = std::max(gate::t32_act_bytes(E / 32, H / 32, p.ksx, p.ksh, p.rb), red);
     p.lds = std::max(node, gates);
@@ -1600,6 +1864,64 @@ hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds
     DT_PIPE(2, 4) DT_PIPE(2, 2) DT_PIPE(2, 1)
 #undef DT_PIPE
     return hipErrorInvalidValue;
+}
+
+// LDS grant and co-residency of the persistent kernel for a plan (once per
+// distinct plan: the first call sets the kernel's dynamic-LDS limit)
+template <int RB>
+static hipError_t pers_prepare(const PipePlan& pp, int B, bool* fits) {
+    static unsigned granted = 0;  // dynamic LDS bytes allowed so far (grows only)
+    const unsigned shm = (unsigned)pp.lds;
+    if (shm > granted) {
+        const hipError_t e =
+            hipFuncSetAttribute((const void*)pers_kernel<RB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+        granted = shm;
+    }
+    int dev = 0, coop = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pers_kernel<RB>, kPipeThreads, shm);
+    if (e != hipSuccess) return e;
+    *fits = coop != 0 && (long long)per_cu * cus >= (long long)pp.ng + B;
+    return hipSuccess;
+}
+
+bool pers_supported(const PipePlan& pp, int B) {
+    if (pp.ng == 0 || B < 1) return false;
+    bool fits = false;
+    hipError_t e = hipErrorInvalidValue;
+    if (pp.rb == 4) e = pers_prepare<4>(pp, B, &fits);
+    else if (pp.rb == 2) e = pers_prepare<2>(pp, B, &fits);
+    else if (pp.rb == 1) e = pers_prepare<1>(pp, B, &fits);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // (a failed query leaves nothing pending)
+        return false;
+    }
+    return fits;
+}
+
+hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
+                             LaunchEvents ev) {
+    if (a.B == 0) return hipSuccess;
+    // (done, gflag, nflag and perr are one run of words in the workspace)
+    hipLaunchKernelGGL(pers_clear_kernel, dim3(1), dim3(256), 0, stream, a.gflag, pp.ng + a.B + 1, a.active, a.T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
+    PipeArgs args = a;
+    NodeLds lds = lp;
+    void* params[] = {&args, &lds};
+    const dim3 grid(pp.ng + a.B), block(kPipeThreads);
+    const void* fn = pp.rb == 4 ? (const void*)pers_kernel<4>
+                   : pp.rb == 2 ? (const void*)pers_kernel<2>
+                                : (const void*)pers_kernel<1>;
+    e = hipLaunchCooperativeKernel(fn, grid, block, params, (unsigned)pp.lds, stream);
+    if (e != hipSuccess) return e;
+    if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return e;
+    return hipSuccess;
 }
 
 }  // namespace dt

@@ -256,75 +256,88 @@ inline size_t t32_act_bytes(int nE, int nH, int ksx, int ksh, int rb) {
 // operand reads are lane-linear in LDS (no bank conflicts).
 __device__ __forceinline__ int t32_src_vector(int p) { return (p & 15) * 4 + (p >> 4); }
 
-template <int WM, int RB>
-__device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int kind, int ksub, int nsub, u32x4* sact,
-                                           f32x4 (&acc)[RB][3]) {
-    constexpr int XB = t32_xbatch(RB), HB = t32_hbatch(RB);
-    // (the wave's role and chunk range are wave-uniform: scalar registers)
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = lane_id();
-    const int u = wave / kT32Quarters, qt = wave % kT32Quarters;
-    const int ut = ug * 2 + u;
-    const int kq = (lane >> 4) * 8;
-    const int nE = a.E / 32, nH = a.H / 32, nC = nE + nH;
-    // the workgroup's share [sb, se) of its kind's chunks, and the wave's
-    // quarter of it [cb, cb + n) (chunks numbered within the kind)
-    int sb, se;
-    share(kind ? nH : nE, nsub, ksub, sb, se);
-    const int nsh = se - sb;
-    int qb, qe;
-    share(nsh, kT32Quarters, qt, qb, qe);
-    const int cb = sb + qb, n = qe - qb;
-    const int cg = kind ? nE : 0;  // the kind's first chunk in the packed weights
+// A wave's place in the 32-unit tile: unit tile, quarter, and its chunks
+// [cb, cb + n) of the workgroup's share [sb, sb + nsh) of its kind's chunks
+// (chunks numbered within the kind).  (Wave-uniform: scalar registers.)
+struct T32Wave {
+    int lane, wave, u, qt, ut, kq, nE, nH, nC, sb, nsh, cb, n, cg;
+};
+__device__ __forceinline__ T32Wave t32_wave(const GruGatesArgs& a, int ug, int kind, int ksub, int nsub) {
+    T32Wave r;
+    r.wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    r.lane = lane_id();
+    r.u = r.wave / kT32Quarters;
+    r.qt = r.wave % kT32Quarters;
+    r.ut = ug * 2 + r.u;
+    r.kq = (r.lane >> 4) * 8;
+    r.nE = a.E / 32;
+    r.nH = a.H / 32;
+    r.nC = r.nE + r.nH;
+    int se, qb, qe;
+    share(kind ? r.nH : r.nE, nsub, ksub, r.sb, se);
+    r.nsh = se - r.sb;
+    share(r.nsh, kT32Quarters, r.qt, qb, qe);
+    r.cb = r.sb + qb;
+    r.n = qe - qb;
+    r.cg = kind ? r.nE : 0;  // the kind's first chunk in the packed weights
+    return r;
+}
 
-    // ---- weights of the wave's chunks: a wave-uniform base plus a fixed
-    // per-lane byte offset per load
-    const size_t wgate = (size_t)nC * 512;
-    bf16_t* wpl = (bf16_t*)a.wpack + pack_index_w(ut, 0, 0, nC) + lane * 8;
-    const char* wpk = (const char*)a.wpack + pack_index_w(ut, 0, 0, nC) * 2;
+// The weights of the wave's chunks into registers: from the operand-tile copy
+// (PACKED) or from W_ih / W_hh in place.  A wave-uniform base plus a fixed
+// per-lane byte offset per load; fully unrolled with constant trip counts (the
+// array stays in registers); past n, chunk n - 1 is loaded again (its MFMAs
+// are skipped).
+template <int KIND, bool PACKED, int RB>
+__device__ __forceinline__ void t32_load_weights(const GruGatesArgs& a, const T32Wave& r,
+                                                 bf16x8 (&w)[t32_xbatch(RB)][3]) {
+    constexpr int kind = KIND, NB = KIND ? t32_hbatch(RB) : t32_xbatch(RB);
+    const size_t wgate = (size_t)r.nC * 512;
+    const char* wpk = (const char*)a.wpack + pack_index_w(r.ut, 0, 0, r.nC) * 2;
     const int Kk = kind ? a.H : a.E;  // row length of the kind's weight matrix
-    const char* wsrc = (const char*)(kind ? a.W_hh : a.W_ih) + (size_t)ut * 16 * Kk * 2;
-    const unsigned loff = WM == 2 ? (unsigned)lane * 16u : (unsigned)(((lane & 15) * Kk + kq) * 2);
-    // (fully unrolled with constant trip counts: the array stays in registers;
-    // past n, chunk n - 1 is loaded again and its MFMAs are skipped)
-    bf16x8 w[XB][3];
+    const char* wsrc = (const char*)(kind ? a.W_hh : a.W_ih) + (size_t)r.ut * 16 * Kk * 2;
+    const unsigned loff = PACKED ? (unsigned)r.lane * 16u : (unsigned)(((r.lane & 15) * Kk + r.kq) * 2);
     auto wload = [&](int i, int g) {
-        const int c = cb + min(i, n - 1);
-        const char* base = WM == 2 ? wpk + (g * wgate + (size_t)(cg + c) * 512) * 2
-                                   : wsrc + ((size_t)g * a.H * Kk + (size_t)c * 32) * 2;
+        const int c = r.cb + min(i, r.n - 1);
+        const char* base = PACKED ? wpk + (g * wgate + (size_t)(r.cg + c) * 512) * 2
+                                  : wsrc + ((size_t)g * a.H * Kk + (size_t)c * 32) * 2;
         // (each weight byte is read once per launch: non-temporal, so the
         // stream does not evict what the node workgroups keep in the L2)
         return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + loff)));
     };
-    if (n > 0 && kind == 0) {
+    if (r.n > 0) {
 #pragma unroll
-        for (int i = 0; i < XB; ++i)
-#pragma unroll
-            for (int g = 0; g < 3; ++g) w[i][g] = wload(i, g);
-    } else if (n > 0) {
-#pragma unroll
-        for (int i = 0; i < HB; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int g = 0; g < 3; ++g) w[i][g] = wload(i, g);
     }
+}
 
-    // ---- copy the share's activations into LDS: x blocks [rb][c], or h
-    // blocks [rb * 3 + q][c], 1 KB each; wave w copies blocks w, w + 8, ...
-    // with global_load_lds_dwordx4 (lane l's 16 bytes land at block + 16 l,
-    // no registers held), and waits for its copies before the barrier
+// Copy the share's activations into LDS (x blocks [rb][c], or h blocks
+// [rb * 3 + q][c], 1 KB each; wave w copies blocks w, w + 8, ... with
+// global_load_lds_dwordx4: lane l's 16 bytes land at block + 16 l, no
+// registers held; cache policy CPOL), wait for them, and contract them with
+// the wave's weights.  PACK: also store the weights into the operand-tile copy
+// (the call's first contraction).
+template <int KIND, bool PACK, int RB, int CPOL>
+__device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wave& r, u32x4* sact,
+                                             const bf16x8 (&w)[t32_xbatch(RB)][3], f32x4 (&acc)[RB][3]) {
+    constexpr int kind = KIND, XB = t32_xbatch(RB), HB = t32_hbatch(RB);
+    const int lane = r.lane, nsh = r.nsh, sb = r.sb, cb = r.cb, n = r.n;
     const int nper = kind ? 3 * RB : RB;  // block rows (rb, or rb and part)
     const int nblk = nper * nsh;
     const u32x4* src0 = reinterpret_cast<const u32x4*>(kind ? a.hpack : a.xpack);
-    const int nrow = kind ? nH : nE;      // chunks per block row in the packed layout
+    const int nrow = kind ? r.nH : r.nE;  // chunks per block row in the packed layout
     const int sv = t32_src_vector(lane);
-    for (int blk = wave; blk < nblk; blk += kWaves8) {
-        int r = 0, c = blk;
+    for (int blk = r.wave; blk < nblk; blk += kWaves8) {
+        int rr = 0, c = blk;
         while (c >= nsh) {
             c -= nsh;
-            ++r;
+            ++rr;
         }
-        const u32x4* src = src0 + ((size_t)r * nrow + sb + c) * 64;
+        const u32x4* src = src0 + ((size_t)rr * nrow + sb + c) * 64;
         __builtin_amdgcn_global_load_lds(src + sv, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16,
-                                         0, 0);
+                                         0, CPOL);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -334,13 +347,15 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ki
 #pragma unroll
         for (int g = 0; g < 3; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (n <= 0) return;
-    if constexpr (WM == 1) {  // the call's first contraction leaves the packed copy
+    if constexpr (PACK) {
+        const size_t wgate = (size_t)r.nC * 512;
+        bf16_t* wpl = (bf16_t*)a.wpack + pack_index_w(r.ut, 0, 0, r.nC) + lane * 8;
 #pragma unroll
-        for (int i = 0; i < XB; ++i)
+        for (int i = 0; i < (KIND ? HB : XB); ++i)
             if (i < n)  // (uniform)
 #pragma unroll
                 for (int g = 0; g < 3; ++g)
-                    *reinterpret_cast<u32x4*>(wpl + g * wgate + (size_t)(cg + cb + i) * 512) =
+                    *reinterpret_cast<u32x4*>(wpl + g * wgate + (size_t)(r.cg + cb + i) * 512) =
                         __builtin_bit_cast(u32x4, w[i][g]);
     }
     // x waves read their operand fragments from LDS one chunk ahead (two
@@ -349,7 +364,7 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ki
     // fragments together, then run its MFMAs.  The scheduling barrier per
     // chunk keeps the compiler from hoisting every chunk's reads (their
     // fragments would all be held in registers).
-    if (kind == 0) {
+    if constexpr (KIND == 0) {
         bf16x8 f[2][RB];
         auto rd = [&](bf16x8 (&d)[RB], int i) {
             const int c = cb + i - sb;
@@ -392,6 +407,23 @@ __device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int ki
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+}
+
+// One 32-unit tile contraction: the weights (WM 2: from the operand-tile
+// copy; WM 1: in place, leaving that copy) issued with the activation copy
+// (one memory round trip), then the MFMAs.
+template <int WM, int RB>
+__device__ __forceinline__ void tile32_lds(const GruGatesArgs& a, int ug, int kind, int ksub, int nsub, u32x4* sact,
+                                           f32x4 (&acc)[RB][3]) {
+    const T32Wave r = t32_wave(a, ug, kind, ksub, nsub);
+    bf16x8 w[t32_xbatch(RB)][3];
+    if (kind == 0) {
+        t32_load_weights<0, WM == 2, RB>(a, r, w);
+        t32_contract<0, WM == 1, RB, 0>(a, r, sact, w, acc);
+    } else {
+        t32_load_weights<1, WM == 2, RB>(a, r, w);
+        t32_contract<1, WM == 1, RB, 0>(a, r, sact, w, acc);
     }
 }
 

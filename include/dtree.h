@@ -72,15 +72,23 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *                dt_build_marginal.
  *   expand       how dt_build runs the expansion steps (same trees either
  *                way, up to binary32 rounding order of the GRU gate sums):
- *                DT_EXPAND_AUTO (0) fused where supported, else stepped;
+ *                DT_EXPAND_AUTO (0) persistent where the device and stream
+ *                allow it, else fused where supported, else stepped;
  *                DT_EXPAND_STEPPED (1) two launches per step, the batched
  *                GRU contraction then the node step; DT_EXPAND_FUSED (2) one
  *                launch per step in which the contraction of the rows the
  *                requests need next runs beside the node steps (bf16, B <= 64,
- *                H <= 1024; otherwise dt_create returns DT_ERR_UNSUPPORTED).
+ *                H <= 1024; otherwise dt_create returns DT_ERR_UNSUPPORTED);
+ *                DT_EXPAND_PERSISTENT (3) the fused steps in one cooperative
+ *                launch whose workgroups stay resident (the contraction keeps
+ *                its weights in registers) and hand over through counters
+ *                (same conditions; dt_build returns DT_ERR_UNSUPPORTED when
+ *                the device cannot hold the whole grid at once or the stream
+ *                is being captured).  The same trees, bit for bit, as
+ *                DT_EXPAND_FUSED.
  * A request's expansion state lives in one workgroup's LDS: configurations with
  * 4 H + 8 L M + 512 n bytes (plus ~0.8 KiB) above 64 KiB are DT_ERR_UNSUPPORTED. */
-typedef enum { DT_EXPAND_AUTO = 0, DT_EXPAND_STEPPED = 1, DT_EXPAND_FUSED = 2 } dt_expand;
+typedef enum { DT_EXPAND_AUTO = 0, DT_EXPAND_STEPPED = 1, DT_EXPAND_FUSED = 2, DT_EXPAND_PERSISTENT = 3 } dt_expand;
 typedef struct {
     int32_t B, L, V, E, H, M, n;
     float temperature;
@@ -102,9 +110,11 @@ void dt_destroy(dt_handle *h);
  * 256-byte aligned).  dt_topm and dt_gru_step need no more than this. */
 size_t dt_workspace_bytes(const dt_handle *h);
 
-/* The expansion dt_build runs for this handle: DT_EXPAND_FUSED or
- * DT_EXPAND_STEPPED (DT_EXPAND_AUTO resolved from the configuration); -1 for a
- * NULL handle.  Host only. */
+/* The expansion dt_build runs for this handle: DT_EXPAND_PERSISTENT,
+ * DT_EXPAND_FUSED or DT_EXPAND_STEPPED -- the one its last dt_build call ran,
+ * or before any call the one the configuration selects (DT_EXPAND_AUTO with a
+ * fused plan: DT_EXPAND_PERSISTENT, which a call may turn into
+ * DT_EXPAND_FUSED, see dt_config.expand); -1 for a NULL handle.  Host only. */
 int32_t dt_expand_mode(const dt_handle *h);
 
 const char *dt_status_string(dt_status s);
@@ -331,7 +341,8 @@ dt_status dt_accept_greedy(dt_handle *h, const int32_t *tokens, const int32_t *p
  *   stage 5  GRU gate contraction, every launch separately (level 2)
  *   stage 6  the dt_accept_greedy kernel (one launch per call)
  *   stage 7  fused expansion launches of the call, summed  (level 2)
- *   stage 8  fused expansion, every launch separately      (level 2)
+ *   stage 8  fused expansion, every launch separately      (level 2; the
+ *            persistent expansion is one launch per call)
  * Timing calls are host-side and need the handle's device to be current.
  */
 dt_status dt_timing_enable(dt_handle *h, int level, int capacity);

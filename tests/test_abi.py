@@ -205,16 +205,23 @@ def test_timing_argument_checks():
 def test_expand_mode_is_validated():
     lib = dtree.load_library()
     out = C.c_void_p()
-    bad = dt_config(2, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_BF16, 1e-5, 0, 3)
-    assert lib.dt_create(C.byref(bad), C.byref(out)) == -1 and not out.value
-    assert "expand" in dtree.dt_last_error(None)
-    # the fused expansion is bf16 with at most 64 requests and H <= 1024
-    for kw in (dict(dtype=dtree.DT_F32), dict(B=65), dict(H=2048)):
-        with pytest.raises(ValueError, match="UNSUPPORTED"):
-            make(expand=dtree.DT_EXPAND_FUSED, **kw)
-    # the mode dt_build runs: auto resolves to fused where it applies
-    for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_FUSED), (dtree.DT_EXPAND_STEPPED, dtree.DT_EXPAND_STEPPED),
-                    (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_FUSED)):
+    for e in (4, -1):
+        bad = dt_config(2, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_BF16, 1e-5, 0, e)
+        assert lib.dt_create(C.byref(bad), C.byref(out)) == -1 and not out.value
+        assert "expand" in dtree.dt_last_error(None)
+    # the fused expansion (per-step launches or persistent) is bf16 with at
+    # most 64 requests and H <= 1024
+    for e in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT):
+        for kw in (dict(dtype=dtree.DT_F32), dict(B=65), dict(H=2048)):
+            with pytest.raises(ValueError, match="UNSUPPORTED"):
+                make(expand=e, **kw)
+    # the mode dt_build runs, before any call: auto selects the persistent
+    # launch where the fused expansion applies (a call may fall back to the
+    # per-step launches)
+    for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_PERSISTENT),
+                    (dtree.DT_EXPAND_STEPPED, dtree.DT_EXPAND_STEPPED),
+                    (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_FUSED),
+                    (dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_PERSISTENT)):
         h = make(expand=e)
         assert dtree.dt_expand_mode(h) == want
         dtree.dt_destroy(h)

@@ -49,10 +49,13 @@ def builder(cfg, eps=1e-5):
                          expand=cfg.get("expand", dtree.DT_EXPAND_AUTO))
 
 
-# dt_build's two ways of running the expansion: "auto" takes the fused
-# launches wherever they apply (bf16, B <= 64, H <= 1024), "stepped" forces two
-# launches per step; the whole-build tests run both where both apply
-EXPAND = {"auto": dtree.DT_EXPAND_AUTO, "stepped": dtree.DT_EXPAND_STEPPED}
+# dt_build's ways of running the expansion: "auto" takes the persistent launch
+# wherever it applies (bf16, B <= 64, H <= 1024, a device that holds the
+# grid), "fused" forces one launch per step of the same pipeline, "stepped" two
+# launches per step; the whole-build tests run each where it applies
+EXPAND = {"auto": dtree.DT_EXPAND_AUTO, "fused": dtree.DT_EXPAND_FUSED, "stepped": dtree.DT_EXPAND_STEPPED}
+MODE_NAME = {dtree.DT_EXPAND_STEPPED: "stepped", dtree.DT_EXPAND_FUSED: "fused",
+             dtree.DT_EXPAND_PERSISTENT: "persistent"}
 
 
 # The "strong" variant (h0 ~ N(0, 1), C scaled by 10) makes corrected logits
@@ -94,6 +97,10 @@ def build_and_compare(cfg, inp, requests=None, threads=THREADS, eps=1e-5, tol=SC
         f"expand={cfg.get('expand', 0)}")
     bld = builder(cfg, eps)
     got = run_build(bld, S.to_torch(inp, DEV))
+    ran = bld.expand_mode
+    say(f"  expansion ran: {MODE_NAME.get(ran, ran)}")
+    if cfg.get("expand", dtree.DT_EXPAND_AUTO) != dtree.DT_EXPAND_AUTO:
+        assert ran == cfg["expand"], (ran, cfg["expand"])
     for b in range(B):
         check_valid_tree(got, b, cfg["n"], cfg["L"])
     refs = oracle.build_batch(inp, cfg["M"], cfg["n"], cfg["T"], eps=eps, requests=reqs,
@@ -683,6 +690,36 @@ def test_folded_qwen3_4b_batched():
     folded_and_compare(cfg, inp)  # all 64 requests
 
 
+# ------------------------------------- persistent vs per-step fused launches --
+
+@pytest.mark.parametrize("name,over", [("qwen3_4b_batched", ()), ("qwen3_4b_batched", (("B", 1),)),
+                                       # peaked logits: deep chains, requests waiting inside a step
+                                       ("qwen3_4b_batched", (("B", 8), ("alpha", 6.0)))])
+def test_persistent_equals_per_step_launches(name, over):
+    # The persistent launch runs the per-step launches' arithmetic in the same
+    # order: every output equal bit for bit, twice in a row on one handle
+    # (counters and flags start afresh in each call).
+    cfg, inp = inputs(name, over=over)
+    t = S.to_torch(inp, DEV)
+    got = {}
+    for mode in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT):
+        bld = builder(dict(cfg, expand=mode))
+        outs = []
+        for _ in range(2):
+            outs.append({k: v.cpu().clone() for k, v in bld.build(t["base"], t["emb"], t["w_ih"], t["w_hh"],
+                                                                  t["b_ih"], t["b_hh"], t["C"], t["h0"]).items()})
+            torch.cuda.synchronize()
+        assert bld.expand_mode == mode
+        for k in outs[0]:
+            assert torch.equal(_i32(outs[0][k]), _i32(outs[1][k])), f"{MODE_NAME[mode]}: second call differs in {k}"
+        got[mode] = outs[0]
+        bld.close()
+    for k in got[dtree.DT_EXPAND_FUSED]:
+        assert torch.equal(_i32(got[dtree.DT_EXPAND_FUSED][k]), _i32(got[dtree.DT_EXPAND_PERSISTENT][k])), \
+            f"persistent differs from per-step launches in {k}"
+    assert int(got[dtree.DT_EXPAND_PERSISTENT]["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
+
+
 # ------------------------------------------------ streams and graph replay --
 
 def _i32(t):
@@ -742,7 +779,7 @@ def test_build_side_stream_and_graph_replay():
 
 # ------------------------------------------------------- the position limit --
 
-@pytest.mark.parametrize("mode", ["standard", "stepped", "marginal", "full_vocab"])
+@pytest.mark.parametrize("mode", ["standard", "fused", "stepped", "marginal", "full_vocab"])
 def test_build_max_positions(mode):
     # L = 64 positions (the limit): depths up to n in the queue keys, the whole
     # L x M table staged per step, every row's tail (full-vocabulary mode);
@@ -750,7 +787,7 @@ def test_build_max_positions(mode):
     # fused expansion nearly every pop takes the newest child: waits)
     cfg = dict(B=5, V=4099, L=64, E=64, H=96, M=32, n=32, dtype="bf16", alpha=6.0, T=0.0,
                full_vocab=mode == "full_vocab",
-               expand=EXPAND["stepped"] if mode == "stepped" else EXPAND["auto"])
+               expand=EXPAND[mode] if mode in ("stepped", "fused") else EXPAND["auto"])
     inp = S.make_inputs(cfg, seed=11)
     if mode == "marginal":
         got = marginal_and_compare(cfg, inp, requests=range(cfg["B"]))
