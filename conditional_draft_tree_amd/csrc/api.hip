@@ -129,7 +129,7 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true,
     l.p_gh = take(fp ? B * S * (size_t)pp.ksh * 3 * H * 4 : 0);  // h-part gate sums per slot
     l.p_hstate = take(fp ? B * S * H * 4 : 0);        // binary32 state per slot
     l.p_exp = take(fp ? B * S * 4 : 0);               // launch that expanded each slot
-    l.p_done = take(fp ? ((size_t)pT + pp.ng + B + 1) * 4 : 0);  // per-launch counters, per-workgroup flags, error word
+    l.p_done = take(fp ? ((size_t)pT + pp.ng + 6 * B + 1) * 4 : 0);  // per-launch counters, flags, error word
     l.p_active = take(fp ? (size_t)2 * pT * 4 : 0);
     l.p_xpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * c.E * 2 : 0);  // parity-1 activations
     l.p_hpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
@@ -630,8 +630,9 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         pa.exp_at = (int32_t*)(w + L.p_exp);
         pa.done = (unsigned*)(w + L.p_done);
         pa.gflag = pa.done + pa.T;
-        pa.nflag = pa.gflag + pa.ng;
-        pa.perr = pa.nflag + pa.B;
+        pa.hflag = pa.gflag + pa.ng;
+        pa.xflag = pa.hflag + 4 * pa.B;
+        pa.perr = pa.xflag + 2 * pa.B;
         pa.active = (int32_t*)(w + L.p_active);
         pa.wpack = (uint16_t*)(w + L.wpack);
         pa.child_tok = a.child_tok; pa.child_lp = a.child_lp; pa.ckey = a.ckey; pa.queue = a.queue;
@@ -642,7 +643,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         // stream is not being captured; else one launch per step
         bool pers = false;
         if (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT) {
-            if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B) ? 1 : 0;
+            if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B, c.V) ? 1 : 0;
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
             pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
@@ -650,7 +651,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
                 return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
                                                        ? "persistent expansion: the stream is being captured"
                                                        : "persistent expansion: the device cannot hold the grid "
-                                                         "(%d workgroups) at once", h->pp.ng + c.B);
+                                                         "(%d workgroups) at once, or V > 262143", h->pp.ng + c.B);
         }
         h->last_mode = pers ? DT_EXPAND_PERSISTENT : DT_EXPAND_FUSED;
         if (pers) {

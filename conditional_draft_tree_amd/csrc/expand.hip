@@ -924,6 +924,42 @@ __device__ __forceinline__ void wait_flags(const unsigned* f, int n, unsigned ta
 __device__ __forceinline__ void set_flag(unsigned* f, unsigned v) {
     __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A node workgroup's x flag for the contraction of step s (one word per
+// request and step parity): s (bits 19 ..), whether the request waits in
+// step s (bit 18) and the token of step s's x row + 1 (bits 0 .. 17; 0:
+// none).  The word of step s is >= xflag_word(s, -1, false); the word of step
+// s - 2 in the same slot is below it.
+constexpr int kXflagStep = 19;
+constexpr int kPersMaxV = (1 << 18) - 1;  // tokens the x flag can carry
+__host__ __device__ constexpr unsigned xflag_word(int step, int tok, bool wait) {
+    return ((unsigned)step << kXflagStep) | ((wait ? 1u : 0u) << 18) | (unsigned)(tok + 1);
+}
+// Wait (wave 0, bounded) for the B x flags of step s, then put the tokens into
+// s_tok[0 .. 64) (0 where none, and past B) and whether any request waits
+// into *s_any; then the workgroup barrier.
+__device__ __forceinline__ void wait_xflags(const unsigned* f, int B, int V, int s, unsigned* perr, int32_t* s_tok,
+                                            int* s_any) {
+    if (threadIdx.x < kWave) {
+        const int l = (int)threadIdx.x;
+        const unsigned target = xflag_word(s, -1, false);
+        unsigned v = target, spins = 0;
+        for (;;) {
+            v = l < B ? __hip_atomic_load(f + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : target;
+            if (__ballot(v < target) == 0ull) break;
+            if ((++spins & 63u) == 0u &&
+                (spins >= kPipeSpinLimit || __hip_atomic_load(perr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                if (l == 0) __hip_atomic_fetch_or(perr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const int tok1 = (int)(v & ((1u << 18) - 1u));
+        s_tok[l] = l < B && tok1 > 0 ? min(tok1 - 1, V - 1) : 0;  // (a row without an x row reads token 0)
+        const bool any = __ballot(l < B && ((v >> 18) & 1u)) != 0ull;
+        if (l == 0) *s_any = any;
+    }
+    __syncthreads();
+}
 
 // The four quarters of each unit tile (waves 4 u + 0 .. 3) added in order,
 // quarter 0 first, and stored (when `store`): every wave leaves its sums in
@@ -1077,23 +1113,32 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
 
 // Contraction role of the persistent launch: the workgroup's weights are
 // loaded into registers once, then every step t = 1 .. T - 1 waits for the
-// node workgroups' step t - 1 (their activations), contracts and counts
-// itself.  The last step runs only if some request waits in it.
+// node workgroups' rows of step t - 1 -- an x workgroup for their x tokens
+// (it reads the embedding rows itself), an h workgroup for their h rows --,
+// contracts and raises its flag.  The last step runs only if some request
+// waits in it.
 template <int KIND, int RB>
 __device__ __forceinline__ void pers_gate_loop(const PipeArgs& a, GruGatesArgs& g, const gate::T32Wave& r, int ug,
                                                int ksub, float* lds) {
     __shared__ int s_hsl[kMaxB];
+    __shared__ int32_t s_tok[kWave];  // x rows' tokens (row blocks of 16)
+    __shared__ int s_any;             // some request waits in this step
     gate::bf16x8 w[gate::t32_xbatch(RB)][3];
     gate::t32_load_weights<KIND, false, RB>(g, r, w);
     for (int t = 1; t < a.T; ++t) {
-        wait_flags(a.nflag, a.B, (unsigned)t, a.perr);  // every node workgroup finished step t - 1
-        if (t == a.T - 1 && ld_agent_i(a.active + a.T + t) == 0) break;
         const int par = t & 1;
-        const int hsl_r = (int)threadIdx.x < a.B ? ld_agent_i(by_parity(a.hslot, par) + threadIdx.x) : -1;
-        g.xpack = by_parity(a.xpack, par);
-        g.hpack = by_parity(a.hpack, par);
+        // (the wait bits of the last step travel with the x tokens)
+        if (KIND == 0 || t == a.T - 1) wait_xflags(a.xflag + par * a.B, a.B, a.V, t, a.perr, s_tok, &s_any);
+        if (KIND == 1) wait_flags(a.hflag, 4 * a.B, (unsigned)t, a.perr);
+        if (t == a.T - 1 && !s_any) break;
+        int hsl_r = -1;
+        if (KIND == 1) {
+            hsl_r = (int)threadIdx.x < a.B ? ld_agent_i(by_parity(a.hslot, par) + threadIdx.x) : -1;
+            g.hpack = by_parity(a.hpack, par);
+        }
         gate::f32x4 acc[RB][3];
-        gate::t32_contract<KIND, false, RB, kCpolSc1>(g, r, reinterpret_cast<gate::u32x4*>(lds), w, acc);
+        gate::t32_contract<KIND, false, RB, kCpolSc1, KIND == 0>(g, r, reinterpret_cast<gate::u32x4*>(lds), w, acc,
+                                                                 s_tok);
         gate_sums<RB, true>(a, t, ug, KIND, ksub, hsl_r, true, acc, lds, s_hsl);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sums are written through
         __syncthreads();
@@ -1106,6 +1151,7 @@ __device__ __forceinline__ void pers_gate(const PipeArgs& a, float* lds) {
     const int ug = (int)blockIdx.x % groups, kw = (int)blockIdx.x / groups;
     const int kind = kw >= a.ksx, ksub = kind ? kw - a.ksx : kw, nsub = kind ? a.ksh : a.ksx;
     GruGatesArgs g{};
+    g.x = a.emb;
     g.W_ih = a.W_ih;
     g.W_hh = a.W_hh;
     g.B = a.B;
@@ -1116,6 +1162,35 @@ __device__ __forceinline__ void pers_gate(const PipeArgs& a, float* lds) {
     const gate::T32Wave r = gate::t32_wave(g, ug, kind, ksub, nsub);
     if (kind == 0) pers_gate_loop<0, RB>(a, g, r, ug, ksub, lds);
     else pers_gate_loop<1, RB>(a, g, r, ug, ksub, lds);
+}
+
+// The state hs ([H] binary32 in LDS) in three exact bf16 parts, as request
+// b's h row of the contraction of launch parity pn (pack_index_h): wave w of
+// four takes the 8-element vectors w * 64 + lane, + 256, ...  COH: written
+// through (read by other workgroups in the same launch).
+template <bool COH>
+__device__ __forceinline__ void pack_state(const PipeArgs& a, const float* hs, int b, int pn, int w, int lane) {
+    const int H = a.H, nv = H >> 3;
+    uint16_t* const hq = by_parity(a.hpack, pn);
+    const __amdgpu_buffer_rsrc_t rh = coherent_rsrc(hq);
+    for (int i = w * kWave + lane; i < nv; i += 4 * kWave) {
+        const int k = i * 8;
+        uint32_t v[3][4] = {};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t p3[3];
+            split3_bf16(hs[k + e], p3);
+#pragma unroll
+            for (int qq = 0; qq < 3; ++qq) v[qq][e >> 1] |= p3[qq] << (16 * (e & 1));
+        }
+#pragma unroll
+        for (int qq = 0; qq < 3; ++qq) {
+            const u32x4 x = u32x4{v[qq][0], v[qq][1], v[qq][2], v[qq][3]};
+            const size_t o = pack_index_h(b, qq, k, H);
+            if constexpr (COH) st_through(rh, o * 2, x);
+            else *reinterpret_cast<u32x4*>(hq + o) = x;
+        }
+    }
 }
 
 // Node role: request b's step at launch t.  PERS: step t of the persistent
@@ -1321,6 +1396,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     else if (a.n - cnt <= a.T - 1 - t) mode = kIdle;            // a spare launch is left: expand at t + 1
     else mode = kWait;                                           // none left: take this launch's
     const bool grow = mode == kRoot || mode == kExpand || mode == kWait;
+    const int ecur = mode == kRoot ? 0 : cur;  // the slot expanded (or popped trivially) now
 
     // ---- stage into LDS (the persistent launch: once, at step 0)
     const bool stage = !PERS || t == 0;
@@ -1414,8 +1490,9 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     __syncthreads();
 
     // the previously expanded slot's children, sorted for the sibling pushes
-    // of this and later launches (wave 1, while the gathers are in flight)
-    if (wave == 1 && unsorted >= 0) {
+    // of this and later launches (wave 1, while the gathers are in flight;
+    // the persistent launch sorts them at the end of the step that made them)
+    if (!PERS && wave == 1 && unsorted >= 0) {
         const u64 kids = wave_sort_desc(prev_keys);
         if (lane < M) {
             a.child_tok[(slot0 + unsorted) * kMaxM + lane] = child_tok_of(kids);
@@ -1470,7 +1547,6 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     // of qa and that child (keys are unique); what a pop of qa reads is
     // fetched before the children are known, and the queue is left as a push
     // and a swap-remove of the popped entry would leave it.
-    const int ecur = mode == kRoot ? 0 : cur;  // the slot expanded (or popped trivially) now
     u64 ckey = 0ull, best = 0ull, second = 0ull;
     int new_cnt = cnt, new_cur = cur, v_par = -1, pd = 0, pr = 0, ptok = -1;
     float psc = 0.f;
@@ -1478,6 +1554,17 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     bool wait_next = false;  // launch t + 1 will find the popped node not ready and no launch to spare
     int vexp_rec = 0;        // launch that expanded the popped node's parent
     const bool pops = mode == kRoot || mode == kExpand || mode == kWait || mode == kTrivial;
+    if (PERS && wave >= 4) {
+        // persistent launch: the next step's h row (this state in three exact
+        // bf16 parts, waves 4 .. 7, while wave 0 runs the queue), written
+        // through, then each wave raises its flag: the state contraction of
+        // step t + 1 starts on these, not on the end of the step
+        const int hn = grow ? ecur : -1;
+        if (wave == 4 && lane == 0) st_agent_i(by_parity(a.hslot, pn) + b, hn);
+        if (hn >= 0) pack_state<true>(a, hs, b, pn, wave - 4, lane);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) set_flag(a.hflag + b * 4 + (wave - 4), (unsigned)(t + 1));
+    }
     if (wave == 0) {
         const int edepth = mode == kRoot ? 0 : cdepth;
         // qa and qb: parent, rank, depth; their tokens, qa's sibling and the
@@ -1602,55 +1689,46 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             s_dec[0] = xtok_next;
             s_dec[1] = hslot_next;
         }
+        if constexpr (PERS) {
+            // the next step's x row (the contraction reads its embedding row
+            // by this token) and whether the request waits in it, in the flag
+            // word itself (one store, nothing to complete first)
+            if (lane == 0)
+                set_flag(a.xflag + pn * a.B + b, xflag_word(t + 1, xtok_next, wait_next && t + 1 < a.T));
+        }
     }
     __syncthreads();
 
     if (wave != 0) {
-        // ---- the next launch's activations (waves 1 .. 7): the x row (waves
-        // 1 .. 3) and the expanded node's state in three exact bf16 parts
-        // (waves 4 .. 7)
-        const int xn = s_dec[0], hn = s_dec[1];
-        if (wave < 4) {
-            if (xn < 0) {
-                if constexpr (!PERS) return;
-            } else {
-                uint16_t* const xp = by_parity(a.xpack, pn);
-                const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(xp);
-                const int nv = a.E >> 3;
-                for (int i = (wave - 1) * kWave + lane; i < nv; i += 3 * kWave) {
-                    const u32x4 v =
-                        *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + (size_t)xn * a.E + i * 8);
-                    const size_t o = pack_index_x(b, i * 8, a.E);
-                    if constexpr (PERS) st_through(rx, o * 2, v);
-                    else *reinterpret_cast<u32x4*>(xp + o) = v;
+        if constexpr (PERS) {
+            // this step's children, sorted for the sibling pushes of the
+            // later steps (wave 1)
+            if (wave == 1 && grow) {
+                const u64 kids = wave_sort_desc(ps.ckey[lane]);
+                if (lane < M) {
+                    s_ctok[ecur * kMaxM + lane] = child_tok_of(kids);
+                    s_clp[ecur * kMaxM + lane] = child_lp_of(kids);
                 }
             }
-        } else if (hn < 0) {
-            if constexpr (!PERS) return;
         } else {
-            uint16_t* const hq = by_parity(a.hpack, pn);
-            const __amdgpu_buffer_rsrc_t rh = coherent_rsrc(hq);
-            const int nv = H >> 3;
-            for (int i = (wave - 4) * kWave + lane; i < nv; i += 4 * kWave) {
-                const int k = i * 8;
-                uint32_t w[3][4] = {};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uint32_t p3[3];
-                    split3_bf16(hs[k + e], p3);
-#pragma unroll
-                    for (int qq = 0; qq < 3; ++qq) w[qq][e >> 1] |= p3[qq] << (16 * (e & 1));
+            // ---- the next launch's activations (waves 1 .. 7): the x row
+            // (waves 1 .. 3) and the expanded node's state in three exact
+            // bf16 parts (waves 4 .. 7)
+            const int xn = s_dec[0], hn = s_dec[1];
+            if (wave < 4) {
+                if (xn < 0) return;
+                uint16_t* const xp = by_parity(a.xpack, pn);
+                const int nv = a.E >> 3;
+                const size_t row = (size_t)min(xn, a.V - 1) * a.E;  // (a token of the request's tables: < V)
+                for (int i = (wave - 1) * kWave + lane; i < nv; i += 3 * kWave) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>((const bf16_t*)a.emb + row + i * 8);
+                    *reinterpret_cast<u32x4*>(xp + pack_index_x(b, i * 8, a.E)) = v;
                 }
-#pragma unroll
-                for (int qq = 0; qq < 3; ++qq) {
-                    const u32x4 v = u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]};
-                    const size_t o = pack_index_h(b, qq, k, H);
-                    if constexpr (PERS) st_through(rh, o * 2, v);
-                    else *reinterpret_cast<u32x4*>(hq + o) = v;
-                }
+            } else if (hn >= 0) {
+                pack_state<false>(a, hs, b, pn, wave - 4, lane);
             }
+            return;
         }
-        if constexpr (!PERS) return;
     } else {
         // ---- wave 0: the request's record for the next launch, outputs
         if (t == 0) {  // the empty tree around the root
@@ -1682,9 +1760,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                 if (grow) a.exp_at[slot0 + ecur] = t;
                 by_parity(a.xtok, pn)[b] = xtok_next;
             }
-            if constexpr (PERS) {  // (read by the contraction workgroups in this launch)
-                st_agent_i(by_parity(a.hslot, pn) + b, hslot_next);
-                if (wait_next && t + 1 < a.T) st_agent_i(a.active + a.T + t + 1, 1);  // its contraction runs
+            if constexpr (PERS) {  // (its rows and flags went out after the cell and the queue)
                 if (t == a.T - 1 && __hip_atomic_load(a.perr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                     flag |= kPipeTimeoutFlag;  // some wait of the launch ran out
             } else {
@@ -1721,12 +1797,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             }
         }
     }
-    if constexpr (PERS) {
-        // the step's coherent stores are complete: count the workgroup
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) set_flag(a.nflag + b, (unsigned)(t + 1));
-    }
+    if constexpr (PERS) __syncthreads();  // (the next step reuses the LDS)
 }
 
 template <int WM, int RB>
@@ -1769,8 +1840,8 @@ __global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds 
     }
 }
 
-// The persistent launch's flags, cleared before it starts: gflag [ng], nflag
-// [B] and the error word (one run of words), active [2T].
+// The persistent launch's flags, cleared before it starts: gflag [ng], hflag
+// [B][4], xflag [2][B] and the error word (one run of words), active [2T].
 __global__ void pers_clear_kernel(unsigned* flags, int nflags, int32_t* active, int T) {
     for (int i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0u;
     for (int i = threadIdx.x; i < 2 * T; i += blockDim.x) active[i] = 0;
@@ -1889,8 +1960,8 @@ static hipError_t pers_prepare(const PipePlan& pp, int B, bool* fits) {
     return hipSuccess;
 }
 
-bool pers_supported(const PipePlan& pp, int B) {
-    if (pp.ng == 0 || B < 1) return false;
+bool pers_supported(const PipePlan& pp, int B, int V) {
+    if (pp.ng == 0 || B < 1 || V > kPersMaxV) return false;
     bool fits = false;
     hipError_t e = hipErrorInvalidValue;
     if (pp.rb == 4) e = pers_prepare<4>(pp, B, &fits);
@@ -1906,8 +1977,8 @@ bool pers_supported(const PipePlan& pp, int B) {
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
                              LaunchEvents ev) {
     if (a.B == 0) return hipSuccess;
-    // (done, gflag, nflag and perr are one run of words in the workspace)
-    hipLaunchKernelGGL(pers_clear_kernel, dim3(1), dim3(256), 0, stream, a.gflag, pp.ng + a.B + 1, a.active, a.T);
+    // (gflag, hflag, xflag and perr are one run of words in the workspace)
+    hipLaunchKernelGGL(pers_clear_kernel, dim3(1), dim3(256), 0, stream, a.gflag, pp.ng + 6 * a.B + 1, a.active, a.T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;

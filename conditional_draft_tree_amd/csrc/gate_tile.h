@@ -318,10 +318,13 @@ __device__ __forceinline__ void t32_load_weights(const GruGatesArgs& a, const T3
 // global_load_lds_dwordx4: lane l's 16 bytes land at block + 16 l, no
 // registers held; cache policy CPOL), wait for them, and contract them with
 // the wave's weights.  PACK: also store the weights into the operand-tile copy
-// (the call's first contraction).
-template <int KIND, bool PACK, int RB, int CPOL>
+// (the call's first contraction).  XTOK (x part): the rows are read from the
+// embedding table a.x at the tokens xtok[row] (row < 16 RB, valid tokens)
+// instead of from the packed copy.
+template <int KIND, bool PACK, int RB, int CPOL, bool XTOK = false>
 __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wave& r, u32x4* sact,
-                                             const bf16x8 (&w)[t32_xbatch(RB)][3], f32x4 (&acc)[RB][3]) {
+                                             const bf16x8 (&w)[t32_xbatch(RB)][3], f32x4 (&acc)[RB][3],
+                                             const int32_t* xtok = nullptr) {
     constexpr int kind = KIND, XB = t32_xbatch(RB), HB = t32_hbatch(RB);
     const int lane = r.lane, nsh = r.nsh, sb = r.sb, cb = r.cb, n = r.n;
     const int nper = kind ? 3 * RB : RB;  // block rows (rb, or rb and part)
@@ -335,9 +338,17 @@ __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wav
             c -= nsh;
             ++rr;
         }
-        const u32x4* src = src0 + ((size_t)rr * nrow + sb + c) * 64;
-        __builtin_amdgcn_global_load_lds(src + sv, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16,
-                                         0, CPOL);
+        const u32x4* src;
+        if constexpr (KIND == 0 && XTOK) {
+            // lane l: row l % 16 of the row block, 8 elements at K offset 8 (l / 16)
+            const int tok = xtok[rr * 16 + (lane & 15)];
+            src = reinterpret_cast<const u32x4*>((const bf16_t*)a.x + (size_t)tok * a.E + (sb + c) * 32 +
+                                                 (lane >> 4) * 8);
+        } else {
+            src = src0 + ((size_t)rr * nrow + sb + c) * 64 + sv;
+        }
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16, 0,
+                                         KIND == 0 && XTOK ? 0 : CPOL);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
