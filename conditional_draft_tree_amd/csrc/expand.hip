@@ -867,6 +867,11 @@ __device__ __forceinline__ P by_parity(P const (&p)[2], int i) {
 __device__ __forceinline__ float ld_agent(const float* p) {
     return __uint_as_float(__hip_atomic_load((unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+__device__ __forceinline__ float2 ld_agent2(const float* p) {  // (8-byte aligned)
+    const unsigned long long v =
+        __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
 __device__ __forceinline__ int ld_agent_i(const int32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1203,7 +1208,7 @@ template <bool PERS>
 __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, int t, float* lds, int tid) {
     constexpr int NT = kPipeThreads, RW = kPipeRows;
     constexpr int P = 8;                    // bf16 elements per 16-byte vector
-    constexpr int kChunk = 2 * kWave * P;   // K elements of a gathered chunk
+
     constexpr int kStageV = kMaxM * kMaxN / (4 * NT);  // 16-byte vectors of table / child list per thread
     float* hs = lds + lp.hs;
     float* zs = lds + lp.zs;
@@ -1227,8 +1232,9 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     const size_t slot0 = (size_t)b * S;
     const int pt = t & 1, pn = (t + 1) & 1;  // this launch's parity; the next's (= the previous one's)
     const int KSX = a.ksx, KSH = a.ksh;  // partial sums of the x part and of the h part
-    // (a gate sum of the persistent launch: written through by another XCD)
-    auto ld_sum = [](const float* p) { return PERS ? ld_agent(p) : *p; };
+    // (two adjacent gate sums; the persistent launch's are written through by
+    // another XCD)
+    auto ld_sum2 = [](const float* p) { return PERS ? ld_agent2(p) : *reinterpret_cast<const float2*>(p); };
     // ---- round trip 1 (every address valid in every mode); the persistent
     // launch takes the request's record from LDS
     i32x4 rs0, rs1;
@@ -1256,9 +1262,9 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         my_tok = min(max(ip[jl], 0), a.V - 1);
         my_val = vp[jl];
     }
-    // this thread's state elements k1 and k1 + NT (H <= 2 NT)
-    const int k1 = tid, k2 = k1 + NT;
-    const int kc1 = k1 < H ? k1 : 0, kc2 = k2 < H ? k2 : 0;
+    // this thread's state elements k1 = 2 tid and k2 = k1 + 1 (H even, H <= 2 NT)
+    const int k1 = 2 * tid, k2 = k1 + 1;
+    const int kc1 = k1 < H ? k1 : 0;  // (pair loads: elements kc1, kc1 + 1)
     float gi[2][kPipeMaxKs][3];
     auto load_gi = [&]() {
 #pragma unroll
@@ -1266,8 +1272,9 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const size_t base = (((size_t)(pn * KSX + min(s2, KSX - 1)) * a.B + b) * 3 + g) * H;
-                gi[0][s2][g] = ld_sum(a.gi + base + kc1);
-                gi[1][s2][g] = ld_sum(a.gi + base + kc2);
+                const float2 v = ld_sum2(a.gi + base + kc1);
+                gi[0][s2][g] = v.x;
+                gi[1][s2][g] = v.y;
             }
     };
     if constexpr (!PERS) load_gi();
@@ -1280,18 +1287,17 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         const void* bp = g < 3 ? a.b_ih : a.b_hh;
         // stand-in: W_ih, [3H, E] with E >= 1, holds at least 3H elements
         const bf16_t* src = bp ? (const bf16_t*)bp : (const bf16_t*)a.W_ih;
-        const float v1 = load1<bf16_t>(src + (size_t)(g % 3) * H + kc1);
-        const float v2 = load1<bf16_t>(src + (size_t)(g % 3) * H + kc2);
-        bias[0][g] = bp ? v1 : 0.f;
-        bias[1][g] = bp ? v2 : 0.f;
+        const uint32_t two = *reinterpret_cast<const uint32_t*>(src + (size_t)(g % 3) * H + kc1);
+        bias[0][g] = bp ? __uint_as_float(two << 16) : 0.f;
+        bias[1][g] = bp ? __uint_as_float(two & 0xFFFF0000u) : 0.f;
     }
     float h0v[2] = {0.f, 0.f};
     {
         // stand-in: the per-slot states, [B][n + 1][H], hold row b
         const float* h0p = (a.h0 ? a.h0 : a.hstate) + (size_t)b * H;
-        const float v1 = h0p[kc1], v2 = h0p[kc2];
-        h0v[0] = a.h0 ? v1 : 0.f;
-        h0v[1] = a.h0 ? v2 : 0.f;
+        const float2 v = *reinterpret_cast<const float2*>(h0p + kc1);
+        h0v[0] = a.h0 ? v.x : 0.f;
+        h0v[1] = a.h0 ? v.y : 0.f;
     }
     float tail_l = -INFINITY;
     {
@@ -1366,15 +1372,16 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const size_t o = ((size_t)min(s2, KSH - 1) * 3 + g) * H;
-                gh[0][s2][g] = ld_sum(ghp + o + kc1);
-                gh[1][s2][g] = ld_sum(ghp + o + kc2);
+                const float2 v = ld_sum2(ghp + o + kc1);
+                gh[0][s2][g] = v.x;
+                gh[1][s2][g] = v.y;
             }
     };
     if constexpr (!PERS) load_gh();
     {
-        const float* hpp = a.hstate + (slot0 + cp) * H;
-        hp[0] = hpp[kc1];
-        hp[1] = hpp[kc2];
+        const float2 v = *reinterpret_cast<const float2*>(a.hstate + (slot0 + cp) * H + kc1);
+        hp[0] = v.x;
+        hp[1] = v.y;
     }
     const u64 prev_keys = PERS ? ps.ckey[lane] : a.ckey[(slot0 + (unsorted >= 0 ? unsorted : 0)) * kMaxM + lane];
     if (t == 0 || cand) gather(0);
@@ -1444,11 +1451,13 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const size_t base = (((size_t)(pt * KSX + min(s2, KSX - 1)) * a.B + b) * 3 + g) * H;
-                gi[0][s2][g] = ld_agent(a.gi + base + kc1);
-                gi[1][s2][g] = ld_agent(a.gi + base + kc2);
+                const float2 v = ld_agent2(a.gi + base + kc1);
+                gi[0][s2][g] = v.x;
+                gi[1][s2][g] = v.y;
                 const size_t o = ((size_t)min(s2, KSH - 1) * 3 + g) * H;
-                gh[0][s2][g] = ld_agent(ghp + o + kc1);
-                gh[1][s2][g] = ld_agent(ghp + o + kc2);
+                const float2 w2 = ld_agent2(ghp + o + kc1);
+                gh[0][s2][g] = w2.x;
+                gh[1][s2][g] = w2.y;
             }
         // complete the reloads here (vmcnt(0) alone): after this branch the
         // cell then waits only for the loads it uses on either path, not for
@@ -1517,14 +1526,22 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         float acc[RW];
 #pragma unroll
         for (int jj = 0; jj < RW; ++jj) acc[jj] = 0.f;
-        for (int k0 = 0; k0 < H; k0 += kChunk) {
-            if (k0 > 0) gather(k0);
-            const int ka = k0 + lane * P, kb = k0 + (kWave + lane) * P;
+        {  // one chunk: the fused plan has H <= kChunk
+            const int ka = lane * P, kb = (kWave + lane) * P;
+            // (H is a multiple of 32: a lane's 8 elements are all in range or
+            // all past H, where its gathered vector repeats another's)
             float ha[P], hb[P];
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(hs + min(ka, H - P));
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(hs + min(ka, H - P) + 4);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(hs + min(kb, H - P));
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(hs + min(kb, H - P) + 4);
+            const bool ia = ka < H, ib = kb < H;
 #pragma unroll
-            for (int i2 = 0; i2 < P; ++i2) {
-                ha[i2] = ka < H ? hs[ka + i2] : 0.f;
-                hb[i2] = kb < H ? hs[kb + i2] : 0.f;
+            for (int i2 = 0; i2 < 4; ++i2) {
+                ha[i2] = ia ? a0[i2] : 0.f;
+                ha[4 + i2] = ia ? a1[i2] : 0.f;
+                hb[i2] = ib ? b0[i2] : 0.f;
+                hb[4 + i2] = ib ? b1[i2] : 0.f;
             }
 #pragma unroll
             for (int jj = 0; jj < RW; ++jj) {
