@@ -643,7 +643,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         // stream is not being captured; else one launch per step
         bool pers = false;
         if (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT) {
-            if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B, c.V) ? 1 : 0;
+            if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B, c.V, c.E) ? 1 : 0;
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
             pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
@@ -651,7 +651,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
                 return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
                                                        ? "persistent expansion: the stream is being captured"
                                                        : "persistent expansion: the device cannot hold the grid "
-                                                         "(%d workgroups) at once, or V > 262143", h->pp.ng + c.B);
+                                                         "(%d workgroups) at once, or V > 262143 or V E >= 2^31", h->pp.ng + c.B);
         }
         h->last_mode = pers ? DT_EXPAND_PERSISTENT : DT_EXPAND_FUSED;
         if (pers) {

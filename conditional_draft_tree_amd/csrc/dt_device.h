@@ -282,16 +282,19 @@ __device__ __forceinline__ float gru_from_partials(const float* partial, int ksp
     return gru_cell(t[0], t[1], t[2], t[3], b_ih, b_hh, dtype, H, k, hprev);
 }
 
-// x = p[0] + p[1] + p[2] exactly, each part a bf16 (bits returned): every
-// subtraction below is exact, and the last remainder has at most 8
-// significant bits.
+// x = p[0] + p[1] + p[2] exactly, each part a bf16 (bits returned): the
+// first two parts are x and the first remainder cut to their leading 8
+// significant bits (the high half of the word), every subtraction is exact,
+// and the last remainder has at most 8 significant bits (as long as it is not
+// below bf16's subnormal range: |x| >= 2^-110 or x = 0).
 __device__ __forceinline__ void split3_bf16(float x, uint32_t p[3]) {
-    float r = x;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        p[s] = f32_to_bf16_rne(r);
-        r = r - bf16_to_f32(p[s]);
-    }
+    const uint32_t b0 = __float_as_uint(x) & 0xFFFF0000u;
+    const float r1 = x - __uint_as_float(b0);
+    const uint32_t b1 = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(b1);
+    p[0] = b0 >> 16;
+    p[1] = b1 >> 16;
+    p[2] = __float_as_uint(r2) >> 16;
 }
 
 }  // namespace dt

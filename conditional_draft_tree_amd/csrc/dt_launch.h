@@ -194,7 +194,7 @@ struct PipeArgs {
     int32_t* exp_at;      // [B][n+1] launch that expanded the slot
     unsigned* done;       // [T] contraction workgroups finished, per launch
     unsigned* gflag;      // [ng] persistent launch: last step each contraction workgroup finished
-    unsigned* hflag;      // [B][4] persistent launch: steps whose h row each node wave has written
+    unsigned* hflag;      // [2][B] persistent launch: step and h-row slot per node workgroup (hflag_word)
     unsigned* xflag;      // [2][B] persistent launch: x token, wait bit and step per node workgroup
     unsigned* perr;       // a wait of the persistent launch ran out (nonzero)
     int32_t* active;      // [2][T] launch t's contraction has a row; some request waits for it
@@ -227,9 +227,10 @@ hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds
 // The same expansion as one cooperative launch of the same grid: every step of
 // the call, the workgroups kept resident and handing over through counters
 // (see expand.hip).  pers_supported: the device can hold the whole grid at
-// once and V is small enough for a token in a flag word (checked once per
-// plan); launch_pers_build zeroes the call's flags and launches.
-bool pers_supported(const PipePlan& pp, int B, int V);
+// once, V is small enough for a token in a flag word and V E for a 32-bit
+// row offset (checked once per plan); launch_pers_build zeroes the call's
+// flags and launches.
+bool pers_supported(const PipePlan& pp, int B, int V, int E);
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
                              LaunchEvents ev = {});
 

@@ -881,14 +881,18 @@ __device__ __forceinline__ void st_agent_i(int32_t* p, int v) {
 
 // ---- hand-over inside one launch (the persistent launch, and a request that
 // waits for its launch's contraction).  Each XCD has its own L2, written back
-// to memory only at the end of a kernel.  Data that another XCD reads in the
-// same launch is therefore stored with the device-scope cache policy (sc1:
-// written through to the device-coherent level) and read with it (sc1 loads,
-// and the sc1 copy into LDS), and once the stores are complete (vmcnt(0)) the
-// workgroup's own flag word is set to the step it finished: no L2 writeback
-// or invalidation is needed, what a workgroup keeps for itself stays cached,
-// and no two workgroups update one word (same-address atomics from every
-// workgroup serialize).
+// to memory only at the end of a kernel (and invalidated at the start of
+// one).  Data that another XCD reads in the same launch is therefore stored
+// with the device-scope cache policy (sc1: written through to the
+// device-coherent level), and once the stores are complete (vmcnt(0)) the
+// workgroup's own flag word is set to the step it finished.  The reader uses
+// sc1 loads where its XCD may hold an older copy of the line (the gate sums,
+// rewritten every other step); data written once per launch and read only
+// after its flag (a slot's state) is read through the caches, provided that
+// nothing reads it before it is written.  No L2 writeback or invalidation is
+// needed, what a workgroup keeps for itself stays cached, and no two
+// workgroups update one word (same-address atomics from every workgroup
+// serialize).
 constexpr int kCpolSc1 = 16;  // cache-policy operand of buffer and LDS-copy builtins: sc1
 // Buffer resource over a buffer whose offsets fit 32 bits (uniform base)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
@@ -896,6 +900,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base
 }
 __device__ __forceinline__ void st_through(__amdgpu_buffer_rsrc_t r, size_t byte_off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void st_through2(__amdgpu_buffer_rsrc_t r, size_t byte_off, float x, float y) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x), __float_as_uint(y)}, r, (int)byte_off, 0,
+                                          kCpolSc1);
 }
 // Wait (wave 0, bounded) until every flag f[0 .. n) (n <= 256) is at least
 // target -- lane l reads flags l, l + 64, ... with device-coherent loads --
@@ -939,11 +948,12 @@ constexpr int kPersMaxV = (1 << 18) - 1;  // tokens the x flag can carry
 __host__ __device__ constexpr unsigned xflag_word(int step, int tok, bool wait) {
     return ((unsigned)step << kXflagStep) | ((wait ? 1u : 0u) << 18) | (unsigned)(tok + 1);
 }
-// Wait (wave 0, bounded) for the B x flags of step s, then put the tokens into
-// s_tok[0 .. 64) (0 where none, and past B) and whether any request waits
-// into *s_any; then the workgroup barrier.
-__device__ __forceinline__ void wait_xflags(const unsigned* f, int B, int V, int s, unsigned* perr, int32_t* s_tok,
-                                            int* s_any) {
+// Wait (wave 0, bounded) for the B x flags of step s, then put the x rows'
+// offsets in the embedding table (token * E; token 0 where none, and past B)
+// into s_roff[0 .. 64) unless it is NULL, and whether any request waits into
+// *s_any; then the workgroup barrier.
+__device__ __forceinline__ void wait_xflags(const unsigned* f, int B, int V, int E, int s, unsigned* perr,
+                                            int32_t* s_roff, int* s_any) {
     if (threadIdx.x < kWave) {
         const int l = (int)threadIdx.x;
         const unsigned target = xflag_word(s, -1, false);
@@ -959,9 +969,42 @@ __device__ __forceinline__ void wait_xflags(const unsigned* f, int B, int V, int
             __builtin_amdgcn_s_sleep(1);
         }
         const int tok1 = (int)(v & ((1u << 18) - 1u));
-        s_tok[l] = l < B && tok1 > 0 ? min(tok1 - 1, V - 1) : 0;  // (a row without an x row reads token 0)
+        if (s_roff) s_roff[l] = (l < B && tok1 > 0 ? min(tok1 - 1, V - 1) : 0) * E;  // (no x row: token 0)
         const bool any = __ballot(l < B && ((v >> 18) & 1u)) != 0ull;
         if (l == 0) *s_any = any;
+    }
+    __syncthreads();
+}
+// A node workgroup's h flag for the contraction of step s (one word per
+// request and step parity): s (bits 8 ..) and the slot whose state is the h
+// row of step s, + 1 (bits 0 .. 7; 0: none).
+__host__ __device__ constexpr unsigned hflag_word(int step, int slot) {
+    return ((unsigned)step << 8) | (unsigned)(slot + 1);
+}
+// Wait (wave 0, bounded) for the B h flags of step s, then put each row's
+// slot into s_slot[0 .. 64) (-1 where none, and past B) and the offset of its
+// state among the per-slot states [B][S][H] into s_roff (row 0's first slot
+// where none); then the workgroup barrier.
+__device__ __forceinline__ void wait_hflags(const unsigned* f, int B, int S, int H, int s, unsigned* perr,
+                                            int32_t* s_roff, int32_t* s_slot) {
+    if (threadIdx.x < kWave) {
+        const int l = (int)threadIdx.x;
+        const unsigned target = hflag_word(s, -1);
+        unsigned v = target, spins = 0;
+        for (;;) {
+            v = l < B ? __hip_atomic_load(f + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : target;
+            if (__ballot(v < target) == 0ull) break;
+            if ((++spins & 63u) == 0u &&
+                (spins >= kPipeSpinLimit || __hip_atomic_load(perr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                if (l == 0) __hip_atomic_fetch_or(perr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const int sl = l < B ? (int)(v & 255u) - 1 : -1;
+        const bool ok = sl >= 0 && sl < S;
+        s_slot[l] = ok ? sl : -1;
+        s_roff[l] = ok ? (l * S + sl) * H : 0;
     }
     __syncthreads();
 }
@@ -1119,31 +1162,32 @@ __device__ __forceinline__ void pipe_gate(const PipeArgs& a, int t, float* lds) 
 // Contraction role of the persistent launch: the workgroup's weights are
 // loaded into registers once, then every step t = 1 .. T - 1 waits for the
 // node workgroups' rows of step t - 1 -- an x workgroup for their x tokens
-// (it reads the embedding rows itself), an h workgroup for their h rows --,
-// contracts and raises its flag.  The last step runs only if some request
-// waits in it.
+// (it reads the embedding rows itself), an h workgroup for the slots of their
+// states (it reads the binary32 states and splits them itself) --, contracts
+// and raises its flag.  The last step runs only if some request waits in it.
+// Both read their rows through the caches: the embedding table is never
+// written, and a slot's state is written once per launch (written through,
+// before the flag that names it) and read only after.
 template <int KIND, int RB>
 __device__ __forceinline__ void pers_gate_loop(const PipeArgs& a, GruGatesArgs& g, const gate::T32Wave& r, int ug,
                                                int ksub, float* lds) {
     __shared__ int s_hsl[kMaxB];
-    __shared__ int32_t s_tok[kWave];  // x rows' tokens (row blocks of 16)
-    __shared__ int s_any;             // some request waits in this step
+    __shared__ int32_t s_roff[kWave];  // the rows' offsets (row blocks of 16)
+    __shared__ int32_t s_slot[kWave];  // h rows: the slot of each row's state
+    __shared__ int s_any;              // some request waits in this step
     gate::bf16x8 w[gate::t32_xbatch(RB)][3];
     gate::t32_load_weights<KIND, false, RB>(g, r, w);
     for (int t = 1; t < a.T; ++t) {
         const int par = t & 1;
         // (the wait bits of the last step travel with the x tokens)
-        if (KIND == 0 || t == a.T - 1) wait_xflags(a.xflag + par * a.B, a.B, a.V, t, a.perr, s_tok, &s_any);
-        if (KIND == 1) wait_flags(a.hflag, 4 * a.B, (unsigned)t, a.perr);
+        if (KIND == 0 || t == a.T - 1)
+            wait_xflags(a.xflag + par * a.B, a.B, a.V, a.E, t, a.perr, KIND == 0 ? s_roff : nullptr, &s_any);
+        if (KIND == 1) wait_hflags(a.hflag + par * a.B, a.B, a.n + 1, a.H, t, a.perr, s_roff, s_slot);
         if (t == a.T - 1 && !s_any) break;
-        int hsl_r = -1;
-        if (KIND == 1) {
-            hsl_r = (int)threadIdx.x < a.B ? ld_agent_i(by_parity(a.hslot, par) + threadIdx.x) : -1;
-            g.hpack = by_parity(a.hpack, par);
-        }
+        const int hsl_r = KIND == 1 && (int)threadIdx.x < a.B ? s_slot[threadIdx.x] : -1;
         gate::f32x4 acc[RB][3];
-        gate::t32_contract<KIND, false, RB, kCpolSc1, KIND == 0>(g, r, reinterpret_cast<gate::u32x4*>(lds), w, acc,
-                                                                 s_tok);
+        gate::t32_contract<KIND, false, RB, 0, true>(g, r, reinterpret_cast<gate::u32x4*>(lds), w, acc, s_roff,
+                                                     a.hstate);
         gate_sums<RB, true>(a, t, ug, KIND, ksub, hsl_r, true, acc, lds, s_hsl);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sums are written through
         __syncthreads();
@@ -1171,13 +1215,10 @@ __device__ __forceinline__ void pers_gate(const PipeArgs& a, float* lds) {
 
 // The state hs ([H] binary32 in LDS) in three exact bf16 parts, as request
 // b's h row of the contraction of launch parity pn (pack_index_h): wave w of
-// four takes the 8-element vectors w * 64 + lane, + 256, ...  COH: written
-// through (read by other workgroups in the same launch).
-template <bool COH>
+// four takes the 8-element vectors w * 64 + lane, + 256, ...
 __device__ __forceinline__ void pack_state(const PipeArgs& a, const float* hs, int b, int pn, int w, int lane) {
     const int H = a.H, nv = H >> 3;
     uint16_t* const hq = by_parity(a.hpack, pn);
-    const __amdgpu_buffer_rsrc_t rh = coherent_rsrc(hq);
     for (int i = w * kWave + lane; i < nv; i += 4 * kWave) {
         const int k = i * 8;
         uint32_t v[3][4] = {};
@@ -1191,17 +1232,16 @@ __device__ __forceinline__ void pack_state(const PipeArgs& a, const float* hs, i
 #pragma unroll
         for (int qq = 0; qq < 3; ++qq) {
             const u32x4 x = u32x4{v[qq][0], v[qq][1], v[qq][2], v[qq][3]};
-            const size_t o = pack_index_h(b, qq, k, H);
-            if constexpr (COH) st_through(rh, o * 2, x);
-            else *reinterpret_cast<u32x4*>(hq + o) = x;
+            *reinterpret_cast<u32x4*>(hq + pack_index_h(b, qq, k, H)) = x;
         }
     }
 }
 
 // Node role: request b's step at launch t.  PERS: step t of the persistent
-// launch -- it first waits for the contraction of step t - 1, reads the gate
-// sums and writes the next step's rows coherently, and counts itself at the
-// end (its own records stay in its XCD's caches).
+// launch -- it first waits for the contraction of step t - 1 and reads the
+// gate sums, writes the new state through and names its slot in the h flag,
+// and the next x row's token in the x flag (its own records stay in LDS and
+// its XCD's caches).
 enum PipeMode { kRoot, kExpand, kWait, kTrivial, kIdle, kDone };
 
 template <bool PERS>
@@ -1293,8 +1333,11 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     }
     float h0v[2] = {0.f, 0.f};
     {
-        // stand-in: the per-slot states, [B][n + 1][H], hold row b
-        const float* h0p = (a.h0 ? a.h0 : a.hstate) + (size_t)b * H;
+        // stand-in: W_ih, [3H, E] bf16 with E >= 1, holds 2H floats (not the
+        // per-slot states: the persistent launch's contraction reads those
+        // through the caches, and nothing may cache a state before it is
+        // written)
+        const float* h0p = a.h0 ? a.h0 + (size_t)b * H : (const float*)a.W_ih;
         const float2 v = *reinterpret_cast<const float2*>(h0p + kc1);
         h0v[0] = a.h0 ? v.x : 0.f;
         h0v[1] = a.h0 ? v.y : 0.f;
@@ -1466,6 +1509,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     }
 
     // ---- the expanded node's state: GRU cell (the root takes h0)
+    float hv2[2] = {0.f, 0.f};
     if (grow) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1493,8 +1537,12 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                                 bias[u][4], bias[u][5], hp[u]);
             }
             hs[kk] = hv;
-            a.hstate[(slot0 + (mode == kRoot ? 0 : cur)) * H + kk] = hv;
+            if constexpr (PERS) hv2[u] = hv;
+            else a.hstate[(slot0 + (mode == kRoot ? 0 : cur)) * H + kk] = hv;
         }
+        // (the persistent launch: written through, read by the contraction
+        // of step t + 1 once the h flag names the slot)
+        if (PERS && k1 < H) st_through2(coherent_rsrc(a.hstate), ((slot0 + ecur) * H + k1) * 4, hv2[0], hv2[1]);
     }
     __syncthreads();
 
@@ -1557,6 +1605,9 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             zs[wave * RW + 4 + (lane >> 4)] = d1;
         }
     }
+    // (persistent launch: every wave's stores of the state are complete
+    // before its h flag goes out)
+    if constexpr (PERS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     // ---- queue (wave 0): push the expanded node's best child, pop the next
@@ -1571,16 +1622,11 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     bool wait_next = false;  // launch t + 1 will find the popped node not ready and no launch to spare
     int vexp_rec = 0;        // launch that expanded the popped node's parent
     const bool pops = mode == kRoot || mode == kExpand || mode == kWait || mode == kTrivial;
-    if (PERS && wave >= 4) {
-        // persistent launch: the next step's h row (this state in three exact
-        // bf16 parts, waves 4 .. 7, while wave 0 runs the queue), written
-        // through, then each wave raises its flag: the state contraction of
-        // step t + 1 starts on these, not on the end of the step
-        const int hn = grow ? ecur : -1;
-        if (wave == 4 && lane == 0) st_agent_i(by_parity(a.hslot, pn) + b, hn);
-        if (hn >= 0) pack_state<true>(a, hs, b, pn, wave - 4, lane);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (lane == 0) set_flag(a.hflag + b * 4 + (wave - 4), (unsigned)(t + 1));
+    if (PERS && wave == 4 && lane == 0) {
+        // persistent launch: the next step's h row is this state (its slot
+        // in the flag word; the state contraction of step t + 1 starts on it,
+        // not on the end of the step)
+        set_flag(a.hflag + pn * a.B + b, hflag_word(t + 1, grow ? ecur : -1));
     }
     if (wave == 0) {
         const int edepth = mode == kRoot ? 0 : cdepth;
@@ -1742,7 +1788,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
                     *reinterpret_cast<u32x4*>(xp + pack_index_x(b, i * 8, a.E)) = v;
                 }
             } else if (hn >= 0) {
-                pack_state<false>(a, hs, b, pn, wave - 4, lane);
+                pack_state(a, hs, b, pn, wave - 4, lane);
             }
             return;
         }
@@ -1858,7 +1904,8 @@ __global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds 
 }
 
 // The persistent launch's flags, cleared before it starts: gflag [ng], hflag
-// [B][4], xflag [2][B] and the error word (one run of words), active [2T].
+// [2][B] (in room for 4 B words), xflag [2][B] and the error word (one run of
+// words), active [2T].
 __global__ void pers_clear_kernel(unsigned* flags, int nflags, int32_t* active, int T) {
     for (int i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0u;
     for (int i = threadIdx.x; i < 2 * T; i += blockDim.x) active[i] = 0;
@@ -1977,8 +2024,9 @@ static hipError_t pers_prepare(const PipePlan& pp, int B, bool* fits) {
     return hipSuccess;
 }
 
-bool pers_supported(const PipePlan& pp, int B, int V) {
-    if (pp.ng == 0 || B < 1 || V > kPersMaxV) return false;
+bool pers_supported(const PipePlan& pp, int B, int V, int E) {
+    // (the x rows' offsets in the embedding table are 32-bit)
+    if (pp.ng == 0 || B < 1 || V > kPersMaxV || (long long)V * E > 0x7fffffffLL) return false;
     bool fits = false;
     hipError_t e = hipErrorInvalidValue;
     if (pp.rb == 4) e = pers_prepare<4>(pp, B, &fits);

@@ -250,11 +250,19 @@ inline size_t t32_act_bytes(int nE, int nH, int ksx, int ksh, int rb) {
     return (size_t)rb * (nx > 3 * nh ? nx : 3 * nh) * 1024;
 }
 
-// Operand-tile order: lane l of an MFMA operand read takes row l % 16 and K
-// offset 8 (l / 16) of a 1 KB block, i.e. 16-byte vector 4 (l % 16) + l / 16
-// of the block in memory.  The copy puts that vector at position l, so the
-// operand reads are lane-linear in LDS (no bank conflicts).
-__device__ __forceinline__ int t32_src_vector(int p) { return (p & 15) * 4 + (p >> 4); }
+// Operand-tile order: lane l of an MFMA operand read takes row m = l % 16 and
+// K group g = l / 16 (8 elements at K offset 8 g) of a 1 KB block, in memory
+// 16-byte vector 4 m + g of the block.  In LDS the vector (m, g) sits at
+// position t32_lds_pos(m, g) = 4 m + ((g - m / 4) mod 4): copy lane p then
+// takes row p / 4 and K group (p + p / 16) mod 4, so that lanes 4 i .. 4 i + 3
+// read one row's 64 contiguous bytes (one cache line for four lanes, where
+// the operand order would touch four lines), and the operand reads of 16
+// lanes (one g, rows 0 .. 15) still fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int t32_lds_pos(int m, int g) { return 4 * m + ((g - (m >> 2)) & 3); }
+// The K group copy lane p takes (of row p / 4); the vector it reads in the
+// packed layout.
+__device__ __forceinline__ int t32_copy_group(int p) { return ((p & 3) + (p >> 4)) & 3; }
+__device__ __forceinline__ int t32_src_vector(int p) { return 4 * (p >> 2) + t32_copy_group(p); }
 
 // A wave's place in the 32-unit tile: unit tile, quarter, and its chunks
 // [cb, cb + n) of the workgroup's share [sb, sb + nsh) of its kind's chunks
@@ -318,13 +326,14 @@ __device__ __forceinline__ void t32_load_weights(const GruGatesArgs& a, const T3
 // global_load_lds_dwordx4: lane l's 16 bytes land at block + 16 l, no
 // registers held; cache policy CPOL), wait for them, and contract them with
 // the wave's weights.  PACK: also store the weights into the operand-tile copy
-// (the call's first contraction).  XTOK (x part): the rows are read from the
-// embedding table a.x at the tokens xtok[row] (row < 16 RB, valid tokens)
-// instead of from the packed copy.
-template <int KIND, bool PACK, int RB, int CPOL, bool XTOK = false>
+// (the call's first contraction).  ROWS (persistent launch): row i < 16 RB
+// of the activations starts at element roff[i] (LDS) of the embedding table
+// a.x (x part, bf16) or of the binary32 states hbase (h part, which is split
+// into its three bf16 parts here), instead of the packed copies.
+template <int KIND, bool PACK, int RB, int CPOL, bool ROWS = false>
 __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wave& r, u32x4* sact,
                                              const bf16x8 (&w)[t32_xbatch(RB)][3], f32x4 (&acc)[RB][3],
-                                             const int32_t* xtok = nullptr) {
+                                             const int32_t* roff = nullptr, const float* hbase = nullptr) {
     constexpr int kind = KIND, XB = t32_xbatch(RB), HB = t32_hbatch(RB);
     const int lane = r.lane, nsh = r.nsh, sb = r.sb, cb = r.cb, n = r.n;
     const int nper = kind ? 3 * RB : RB;  // block rows (rb, or rb and part)
@@ -332,23 +341,81 @@ __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wav
     const u32x4* src0 = reinterpret_cast<const u32x4*>(kind ? a.hpack : a.xpack);
     const int nrow = kind ? r.nH : r.nE;  // chunks per block row in the packed layout
     const int sv = t32_src_vector(lane);
-    for (int blk = r.wave; blk < nblk; blk += kWaves8) {
-        int rr = 0, c = blk;
-        while (c >= nsh) {
-            c -= nsh;
-            ++rr;
+    if constexpr (ROWS && KIND == 0) {
+        // lane p of a block: row p / 4 of the row block, K group
+        // t32_copy_group(p) of the chunk (the copy order, see above)
+        const bf16_t* xrow[RB];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+            xrow[rr] = (const bf16_t*)a.x + (unsigned)roff[rr * 16 + (lane >> 2)] + sb * 32 + t32_copy_group(lane) * 8;
+        for (int blk = r.wave; blk < nblk; blk += kWaves8) {
+            int rr = 0, c = blk;
+            while (c >= nsh) {
+                c -= nsh;
+                ++rr;
+            }
+            const bf16_t* src = rr == 0 ? xrow[0] : rr == 1 ? xrow[min(1, RB - 1)] : rr == 2 ? xrow[min(2, RB - 1)]
+                                                                                          : xrow[RB - 1];
+            __builtin_amdgcn_global_load_lds(src + c * 32, (__attribute__((address_space(3))) void*)(sact + blk * 64),
+                                             16, 0, 0);
         }
-        const u32x4* src;
-        if constexpr (KIND == 0 && XTOK) {
-            // lane l: row l % 16 of the row block, 8 elements at K offset 8 (l / 16)
-            const int tok = xtok[rr * 16 + (lane & 15)];
-            src = reinterpret_cast<const u32x4*>((const bf16_t*)a.x + (size_t)tok * a.E + (sb + c) * 32 +
-                                                 (lane >> 4) * 8);
-        } else {
-            src = src0 + ((size_t)rr * nrow + sb + c) * 64 + sv;
+    } else if constexpr (ROWS && KIND == 1) {
+        // the (row block, chunk) blocks of the share: lane p reads row m = p / 4's
+        // states 4 j .. 4 j + 3 and 16 + 4 j .. 16 + 4 j + 3 (j = p % 4: four
+        // lanes read 64 contiguous bytes per load) and writes their three
+        // parts, 8 bytes each, into the blocks (rb * 3 + q, c) at the halves j %
+        // 2 of vectors (m, j / 2) and (m, 2 + j / 2)
+        // (batches of kHB blocks per wave: every load of a batch is issued
+        // before the first is used -- no branch between them, so that none is
+        // moved down to its use; past the last block a wave repeats it,
+        // writing the same values again)
+        constexpr int kHB = 6;
+        const int nrb = RB * nsh;
+        for (int i0 = r.wave; i0 < nrb; i0 += kHB * kWaves8) {
+            f32x4 v[kHB][2];
+#pragma unroll
+            for (int j = 0; j < kHB; ++j) {
+                const int i = min(i0 + j * kWaves8, nrb - 1);
+                const int rr = i / nsh, c = i - rr * nsh;
+                const float* src = hbase + (unsigned)roff[rr * 16 + (lane >> 2)] + (sb + c) * 32 + (lane & 3) * 4;
+                v[j][0] = *reinterpret_cast<const f32x4*>(src);
+                v[j][1] = *reinterpret_cast<const f32x4*>(src + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kHB; ++j) {
+                const int i = min(i0 + j * kWaves8, nrb - 1);
+                const int rr = i / nsh, c = i - rr * nsh;
+                uint32_t pq[3][4] = {};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t p3[3];
+                    split3_bf16(v[j][e >> 2][e & 3], p3);
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) pq[q][e >> 1] |= p3[q] << (16 * (e & 1));
+                }
+                const int m = lane >> 2, jj = lane & 3;
+                const int pa = t32_lds_pos(m, jj >> 1), pb = t32_lds_pos(m, 2 + (jj >> 1));
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    uint32_t* blk = reinterpret_cast<uint32_t*>(sact + ((rr * 3 + q) * nsh + c) * 64);
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<u32x2*>(blk + pa * 4 + (jj & 1) * 2) = u32x2{pq[q][0], pq[q][1]};
+                    *reinterpret_cast<u32x2*>(blk + pb * 4 + (jj & 1) * 2) = u32x2{pq[q][2], pq[q][3]};
+                }
+            }
         }
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16, 0,
-                                         KIND == 0 && XTOK ? 0 : CPOL);
+    } else {
+        for (int blk = r.wave; blk < nblk; blk += kWaves8) {
+            int rr = 0, c = blk;
+            while (c >= nsh) {
+                c -= nsh;
+                ++rr;
+            }
+            const u32x4* src = src0 + ((size_t)rr * nrow + sb + c) * 64 + sv;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sact + blk * 64), 16, 0,
+                                             CPOL);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -377,10 +444,11 @@ __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wav
     // fragments would all be held in registers).
     if constexpr (KIND == 0) {
         bf16x8 f[2][RB];
+        const int lp = t32_lds_pos(lane & 15, lane >> 4);
         auto rd = [&](bf16x8 (&d)[RB], int i) {
             const int c = cb + i - sb;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) d[rb] = __builtin_bit_cast(bf16x8, sact[(rb * nsh + c) * 64 + lane]);
+            for (int rb = 0; rb < RB; ++rb) d[rb] = __builtin_bit_cast(bf16x8, sact[(rb * nsh + c) * 64 + lp]);
         };
         rd(f[0], 0);
 #pragma unroll
@@ -397,6 +465,7 @@ __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wav
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
+        const int lp = t32_lds_pos(lane & 15, lane >> 4);
 #pragma unroll
         for (int i = 0; i < HB; ++i) {
             if (i < n) {  // (uniform)
@@ -406,7 +475,7 @@ __device__ __forceinline__ void t32_contract(const GruGatesArgs& a, const T32Wav
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int q = 0; q < 3; ++q)
-                        f[rb][q] = __builtin_bit_cast(bf16x8, sact[((rb * 3 + q) * nsh + c) * 64 + lane]);
+                        f[rb][q] = __builtin_bit_cast(bf16x8, sact[((rb * 3 + q) * nsh + c) * 64 + lp]);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
