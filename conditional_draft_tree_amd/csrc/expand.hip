@@ -912,27 +912,39 @@ __device__ __forceinline__ void st_through2(__amdgpu_buffer_rsrc_t r, size_t byt
 // wait ran out, raises *perr and returns: every workgroup still runs to its
 // end.
 // poll_flags: the same wait by one wave, without the barrier.
-__device__ __forceinline__ void poll_flags(const unsigned* f, int n, unsigned target, unsigned* perr) {
+// The flags' first loads, issued ahead of a wait (lane l: flags l, l + 64,
+// ..., the last flag again past n; no branch, so that a later wait counts
+// exactly the loads issued after these).
+struct FlagPeek {
+    unsigned v[4];
+};
+__device__ __forceinline__ FlagPeek peek_flags(const unsigned* f, int n) {
     const int l = lane_id();
+    FlagPeek p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        p.v[i] = __hip_atomic_load(f + min(l + i * kWave, n - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return p;
+}
+__device__ __forceinline__ void poll_flags(const unsigned* f, int n, unsigned target, unsigned* perr,
+                                           FlagPeek p = FlagPeek{{0u, 0u, 0u, 0u}}) {
     unsigned spins = 0;
     for (;;) {
-        bool ok = true;  // (the loads issued together)
+        bool ok = true;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = min(l + i * kWave, n - 1);
-            ok &= __hip_atomic_load(f + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target;
-        }
+        for (int i = 0; i < 4; ++i) ok &= p.v[i] >= target;
         if (__ballot(!ok) == 0ull) break;
         if ((++spins & 63u) == 0u &&
             (spins >= kPipeSpinLimit || __hip_atomic_load(perr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-            if (l == 0) __hip_atomic_fetch_or(perr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane_id() == 0) __hip_atomic_fetch_or(perr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
         __builtin_amdgcn_s_sleep(1);
+        p = peek_flags(f, n);  // (the loads issued together)
     }
 }
 __device__ __forceinline__ void wait_flags(const unsigned* f, int n, unsigned target, unsigned* perr) {
-    if (threadIdx.x < kWave) poll_flags(f, n, target, perr);
+    if (threadIdx.x < kWave) poll_flags(f, n, target, perr, peek_flags(f, n));
     __syncthreads();
 }
 __device__ __forceinline__ void set_flag(unsigned* f, unsigned v) {
@@ -1059,7 +1071,8 @@ __device__ __forceinline__ void gate_sums(const PipeArgs& a, int t, int ug, int 
 
 // A node workgroup's record between the steps of the persistent launch, in
 // LDS after the slots' expansion steps: queue, unsorted child keys, handed-over
-// candidates, state words, the two x-row tokens.
+// candidates, state words, the two x-row tokens; then the gate biases b_ih,
+// b_hh as binary32 [6][H] (staged at step 0).
 struct PersLds {
     u64* q;
     u64* ckey;
@@ -1067,8 +1080,11 @@ struct PersLds {
     float* nval;
     int32_t* rs;
     int32_t* xt;
+    float* bias;
 };
-constexpr size_t kPersLdsBytes = 64 * 8 * 2 + 64 * 4 * 2 + kStateWords * 4 + 16;
+__host__ __device__ constexpr size_t pers_lds_bytes(int H) {
+    return 64 * 8 * 2 + 64 * 4 * 2 + kStateWords * 4 + 16 + (size_t)6 * H * 4;
+}
 __host__ __device__ inline size_t pers_lds_offset(const NodeLds& lp, int n) {
     return lp.bytes + (((size_t)n + 1) * 4 + 15) / 16 * 16;  // (bytes; after s_exp)
 }
@@ -1081,6 +1097,7 @@ __device__ __forceinline__ PersLds pers_lds(float* lds, const NodeLds& lp, int n
     r.nval = reinterpret_cast<float*>(r.nidx + 64);
     r.rs = reinterpret_cast<int32_t*>(r.nval + 64);
     r.xt = r.rs + kStateWords;
+    r.bias = reinterpret_cast<float*>(r.xt + 4);
     return r;
 }
 
@@ -1268,6 +1285,10 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     const int b = (int)blockIdx.x - a.ng;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    // persistent launch: the first loads of the wait for the contraction of
+    // step t - 1, issued before the step's own (their round trip overlaps them)
+    FlagPeek peek{{0u, 0u, 0u, 0u}};
+    if (PERS && t >= 2 && wave == 0) peek = peek_flags(a.gflag, a.ng);
     const int S = a.n + 1, H = a.H, M = a.M, LM = a.L * a.M;
     const size_t slot0 = (size_t)b * S;
     const int pt = t & 1, pn = (t + 1) & 1;  // this launch's parity; the next's (= the previous one's)
@@ -1321,9 +1342,11 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     // (loads without branches, from a stand-in address when a pointer is
     // NULL, so that every path issues the same loads: the in-order load
     // counters then let round trip 2 wait for exactly what it needs)
+    // (the persistent launch keeps the biases in LDS and reads h0 in the cell)
     float bias[2][6];
 #pragma unroll
     for (int g = 0; g < 6; ++g) {
+        if constexpr (PERS) break;
         const void* bp = g < 3 ? a.b_ih : a.b_hh;
         // stand-in: W_ih, [3H, E] with E >= 1, holds at least 3H elements
         const bf16_t* src = bp ? (const bf16_t*)bp : (const bf16_t*)a.W_ih;
@@ -1332,7 +1355,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         bias[1][g] = bp ? __uint_as_float(two & 0xFFFF0000u) : 0.f;
     }
     float h0v[2] = {0.f, 0.f};
-    {
+    if (!PERS) {
         // stand-in: W_ih, [3H, E] bf16 with E >= 1, holds 2H floats (not the
         // per-slot states: the persistent launch's contraction reads those
         // through the caches, and nothing may cache a state before it is
@@ -1361,7 +1384,8 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
         const int e = (tid + u * NT) * 4;
-        const bool te = tvec && e < LM && (!PERS || t == 0), ke = !PERS && t > 0 && e < nkid;
+        // (the persistent launch copies the table at step 0 without these)
+        const bool te = !PERS && tvec && e < LM, ke = !PERS && t > 0 && e < nkid;
         r_ti[u] = te ? *reinterpret_cast<const i32x4*>(ti + e) : i32x4{0, 0, 0, 0};
         r_tv[u] = te ? *reinterpret_cast<const f32x4*>(tv + e) : f32x4{0.f, 0.f, 0.f, 0.f};
         r_ct[u] = ke ? *reinterpret_cast<const i32x4*>(kt + e) : i32x4{0, 0, 0, 0};
@@ -1432,8 +1456,20 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
         // with the gathers in flight: wait for the contraction of step t - 1
         // (its sums, and the end of its reads of the activation buffers that
         // this step rewrites; step 1 reads no sums and writes buffers no
-        // contraction has read), then read its sums
-        if (t >= 2) wait_flags(a.gflag, a.ng, (unsigned)(t - 1), a.perr);
+        // contraction has read), then read its sums.  Meanwhile wave 1 sorts
+        // the children of the slot grown at step t - 1, for the sibling
+        // pushes of this and later steps.
+        if (t >= 2 || unsorted >= 0) {
+            if (t >= 2 && wave == 0) poll_flags(a.gflag, a.ng, (unsigned)(t - 1), a.perr, peek);
+            if (wave == 1 && unsorted >= 0) {
+                const u64 kids = wave_sort_desc(prev_keys);
+                if (lane < M) {
+                    s_ctok[unsorted * kMaxM + lane] = child_tok_of(kids);
+                    s_clp[unsorted * kMaxM + lane] = child_lp_of(kids);
+                }
+            }
+            __syncthreads();
+        }
         load_gi();
         load_gh();
     }
@@ -1449,11 +1485,12 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     const int ecur = mode == kRoot ? 0 : cur;  // the slot expanded (or popped trivially) now
 
     // ---- stage into LDS (the persistent launch: once, at step 0)
-    const bool stage = !PERS || t == 0;
+    // (the persistent launch stages the table before its first step)
+    const bool stage = !PERS;
 #pragma unroll
     for (int u = 0; u < kStageV; ++u) {
         const int e = (tid + u * NT) * 4;
-        if (stage && tvec && e < LM) {
+        if (!PERS && tvec && e < LM) {
             *reinterpret_cast<i32x4*>(s_tidx + e) = r_ti[u];
             *reinterpret_cast<f32x4*>(s_tval + e) = r_tv[u];
         }
@@ -1516,6 +1553,11 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
             const int kk = u == 0 ? k1 : k2;
             if (kk >= H) continue;
             float hv = h0v[u];
+            if (PERS && mode == kRoot) hv = a.h0 ? a.h0[(size_t)b * H + kk] : 0.f;
+            if (PERS && mode != kRoot) {
+#pragma unroll
+                for (int g = 0; g < 6; ++g) bias[u][g] = ps.bias[g * H + kk];
+            }
             if (mode != kRoot) {
                 float sr = 0.f, sz = 0.f, snx = 0.f, snh = 0.f;
 #pragma unroll
@@ -1548,7 +1590,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
 
     // the previously expanded slot's children, sorted for the sibling pushes
     // of this and later launches (wave 1, while the gathers are in flight;
-    // the persistent launch sorts them at the end of the step that made them)
+    // the persistent launch sorts them during its wait for the contraction)
     if (!PERS && wave == 1 && unsorted >= 0) {
         const u64 kids = wave_sort_desc(prev_keys);
         if (lane < M) {
@@ -1763,17 +1805,7 @@ __device__ __forceinline__ void pipe_node(const PipeArgs& a, const NodeLds& lp, 
     __syncthreads();
 
     if (wave != 0) {
-        if constexpr (PERS) {
-            // this step's children, sorted for the sibling pushes of the
-            // later steps (wave 1)
-            if (wave == 1 && grow) {
-                const u64 kids = wave_sort_desc(ps.ckey[lane]);
-                if (lane < M) {
-                    s_ctok[ecur * kMaxM + lane] = child_tok_of(kids);
-                    s_clp[ecur * kMaxM + lane] = child_lp_of(kids);
-                }
-            }
-        } else {
+        if constexpr (!PERS) {
             // ---- the next launch's activations (waves 1 .. 7): the x row
             // (waves 1 .. 3) and the expanded node's state in three exact
             // bf16 parts (waves 4 .. 7)
@@ -1883,12 +1915,46 @@ __global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds 
     if ((int)blockIdx.x < a.ng) {
         pers_gate<RB>(a, lds);
     } else {
-        {  // the root's candidates, where every step reads the node's
-            const int b = (int)blockIdx.x - a.ng, LM = a.L * a.M;
+        {  // the root's candidates, where every step reads the node's; the
+            // request's top-M table and the gate biases (binary32)
+            const int b = (int)blockIdx.x - a.ng, LM = a.L * a.M, H = a.H, tid = (int)threadIdx.x;
             const PersLds ps = pers_lds(lds, lp, a.n);
-            if ((int)threadIdx.x < a.M) {
-                ps.nidx[threadIdx.x] = a.tidx[(size_t)b * LM + threadIdx.x];
-                ps.nval[threadIdx.x] = a.tval[(size_t)b * LM + threadIdx.x];
+            if (tid < a.M) {
+                ps.nidx[tid] = a.tidx[(size_t)b * LM + tid];
+                ps.nval[tid] = a.tval[(size_t)b * LM + tid];
+            }
+            const int32_t* ti = a.tidx + (size_t)b * LM;
+            const float* tv = a.tval + (size_t)b * LM;
+            int32_t* s_tidx = (int32_t*)(lds + lp.tidx);
+            float* s_tval = lds + lp.tval;
+            if ((LM & 3) == 0) {
+                for (int e = tid * 4; e < LM; e += 4 * kPipeThreads) {
+                    *reinterpret_cast<i32x4*>(s_tidx + e) = *reinterpret_cast<const i32x4*>(ti + e);
+                    *reinterpret_cast<f32x4*>(s_tval + e) = *reinterpret_cast<const f32x4*>(tv + e);
+                }
+            } else {
+                for (int e = tid; e < LM; e += kPipeThreads) {
+                    s_tidx[e] = ti[e];
+                    s_tval[e] = tv[e];
+                }
+            }
+            // the slots' scores, parents and expansion steps (slot 0: the root)
+            for (int i = tid; i <= a.n; i += kPipeThreads) {
+                lds[lp.sc + i] = 0.f;
+                reinterpret_cast<int*>(lds + lp.par)[i] = -1;
+                reinterpret_cast<int32_t*>(lds + lp.bytes / 4)[i] = 0;
+            }
+            // (8 bf16 per thread and load; H % 32 == 0)
+            for (int e = tid * 8; e < 6 * H; e += 8 * kPipeThreads) {
+                const bf16_t* bp = (const bf16_t*)(e < 3 * H ? a.b_ih : a.b_hh);
+                const int o = e < 3 * H ? e : e - 3 * H;
+                const u32x4 v = bp ? *reinterpret_cast<const u32x4*>(bp + o) : u32x4{0u, 0u, 0u, 0u};
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ps.bias[e + 2 * i] = __uint_as_float(w[i] << 16);
+                    ps.bias[e + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                }
             }
             __syncthreads();
         }
@@ -1971,7 +2037,7 @@ PipePlan pipe_plan(int B, int L, int E, int H, int M, int n) {
     p.rb = gate::row_blocks(B);
     if (!gate::t32_fits(E / 32, H / 32, p.ksx, p.ksh, p.rb)) return PipePlan{};  // one weight batch per wave
     const NodeLds lp = node_lds_plan(L, M, n, H);
-    const size_t node = pers_lds_offset(lp, n) + kPersLdsBytes;  // + the slots' expansion launches, the record
+    const size_t node = pers_lds_offset(lp, n) + pers_lds_bytes(H);  // + the slots' expansion launches, the record
     const size_t red = (size_t)kPipeWaves * p.rb * 3 * kWave * 16;  // the waves' sums
     const size_t gates = std::max(gate::t32_act_bytes(E / 32, H / 32, p.ksx, p.ksh, p.rb), red);
     p.lds = std::max(node, gates);
