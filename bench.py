@@ -176,7 +176,8 @@ def expansion_roofline(st, mode, B, L, E, H, M, n, esz, config, np):
     3H (E + H) elements, and per expansion the gathered correction rows and
     the embedding row, n B (M H + E) elements; flops: the gate contraction of
     the T - 2 steps that contract, 2 B 3H (E + H) each.  Over the launch's
-    mean duration from the events each launch records."""
+    mean duration, which each launch records with the device clock (its first
+    workgroup's start to its last one's end; the library's stage 8)."""
     if mode != "persistent" or not st["fused_each"]:
         return None
     T = n + 2

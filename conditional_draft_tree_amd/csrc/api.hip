@@ -38,9 +38,12 @@ struct Marker {
     // 'K'/'T' begin/end of the top-M select kernel, 'M' after the top-M merge,
     // 'g'/'G' begin/end of a gate contraction, 'n'/'N' of a node step, 'E'
     // end of the call; 'a'/'A' begin/end of a dt_accept_greedy kernel.  A
-    // stage's time is the span from the preceding marker.
+    // stage's time is the span from the preceding marker, or, where `clock`
+    // >= 0 (the persistent expansion), the device-clock span that the launch
+    // wrote into slot `clock` of the handle's clock buffer.
     char tag;
     hipEvent_t ev;
+    int clock = -1;
 };
 
 }  // namespace
@@ -64,6 +67,8 @@ struct dt_handle {
     std::vector<std::vector<Marker>> calls;
     std::vector<hipEvent_t> pool;
     size_t pool_used = 0;
+    unsigned long long* tclock = nullptr;  // [capacity][2] device clock of persistent launches (level 2)
+    int tclock_cap = 0;
 };
 
 namespace {
@@ -319,6 +324,7 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
 void dt_destroy(dt_handle* h) {
     if (!h) return;
     for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+    if (h->tclock) (void)hipFree(h->tclock);
     delete h;
 }
 
@@ -337,12 +343,35 @@ dt_status dt_timing_enable(dt_handle* h, int level, int capacity) {
     h->pool_used = 0;
     h->tlevel = level;
     h->tcapacity = level ? capacity : 0;
+    // the device-clock slots of the persistent expansion (level 2)
+    if (level == 2 && capacity > h->tclock_cap) {
+        if (h->tclock) (void)hipFree(h->tclock);
+        h->tclock = nullptr;
+        h->tclock_cap = 0;
+        const hipError_t e = hipMalloc((void**)&h->tclock, (size_t)capacity * 2 * sizeof(unsigned long long));
+        if (e != hipSuccess) {
+            h->tlevel = 0;
+            h->tcapacity = 0;
+            return hip_fail(h, e, "timing clock buffer");
+        }
+        h->tclock_cap = capacity;
+    }
     return DT_OK;
 }
 
 dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out) {
     if (!h || !n_out || (max > 0 && !ms)) return h ? fail(h, DT_ERR_INVALID_ARG, "null output") : DT_ERR_INVALID_ARG;
     if (stage < 0 || stage > 8) return fail(h, DT_ERR_INVALID_ARG, "stage must be 0..8");
+    // the persistent launches' device-clock spans, when any call recorded one
+    std::vector<unsigned long long> clk;
+    for (const auto& call : h->calls)
+        for (const Marker& m : call)
+            if (m.clock >= 0 && clk.empty()) {
+                clk.resize((size_t)h->tclock_cap * 2);
+                const hipError_t e = hipMemcpy(clk.data(), h->tclock, clk.size() * sizeof(unsigned long long),
+                                               hipMemcpyDeviceToHost);
+                if (e != hipSuccess) return hip_fail(h, e, "timing clock read");
+            }
     int n = 0;
     for (const auto& call : h->calls) {
         float sum = 0.f;
@@ -355,8 +384,13 @@ dt_status dt_timing_read(dt_handle* h, int stage, float* ms, int max, int* n_out
                        ((stage == 7 || stage == 8) && tag == 'P');
             if (!hit) continue;
             float t = 0.f;
-            hipError_t e = hipEventElapsedTime(&t, call[i - 1].ev, call[i].ev);
-            if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
+            if (call[i].clock >= 0) {  // (the device's constant 100 MHz clock)
+                const unsigned long long t0 = clk[2 * call[i].clock], t1 = clk[2 * call[i].clock + 1];
+                t = t1 > t0 ? (float)((double)(t1 - t0) * 1e-5) : 0.f;
+            } else {
+                hipError_t e = hipEventElapsedTime(&t, call[i - 1].ev, call[i].ev);
+                if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
+            }
             if (stage == 5 || stage == 8) {
                 if (n < max) ms[n] = t;
                 ++n;
@@ -656,6 +690,14 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         h->last_mode = pers ? DT_EXPAND_PERSISTENT : DT_EXPAND_FUSED;
         if (pers) {
             DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
+            // (timed: the launch also writes its device-clock span, which is
+            // the stage's time; the events would span the cooperative
+            // launch's hand-over as well)
+            const int slot = (int)h->calls.size() - 1;
+            if (ev.stop && h->tclock && slot < h->tclock_cap) {
+                pa.tclock = h->tclock + 2 * (size_t)slot;
+                call->back().clock = slot;
+            }
             DT_TRY(dt::launch_pers_build(pa, h->pp, h->lds, st, ev), "persistent expansion launch");
         } else {
             for (int t = 0; t < h->pipe_T; ++t) {

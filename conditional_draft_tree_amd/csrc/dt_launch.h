@@ -197,6 +197,8 @@ struct PipeArgs {
     unsigned* hflag;      // [2][B] persistent launch: step and h-row slot per node workgroup (hflag_word)
     unsigned* xflag;      // [2][B] persistent launch: x token, wait bit and step per node workgroup
     unsigned* perr;       // a wait of the persistent launch ran out (nonzero)
+    unsigned long long* tclock;  // [2] persistent launch: device clock at its first workgroup's start and
+                                 // its last one's end (min / max; NULL: not timed)
     int32_t* active;      // [2][T] launch t's contraction has a row; some request waits for it
     uint16_t* wpack;      // the weights in operand tiles (written by launch 0)
     int32_t* child_tok;   // [B, n+1, 64]

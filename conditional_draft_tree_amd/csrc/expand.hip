@@ -1912,6 +1912,8 @@ __global__ __launch_bounds__(kPipeThreads) void pipe_kernel(PipeArgs a, NodeLds 
 template <int RB>
 __global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds lp) {
     extern __shared__ __attribute__((aligned(16))) float lds[];  // (16-byte vector accesses)
+    if (a.tclock && threadIdx.x == 0)
+        __hip_atomic_fetch_min(a.tclock, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int)blockIdx.x < a.ng) {
         pers_gate<RB>(a, lds);
     } else {
@@ -1967,14 +1969,20 @@ __global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds 
             pipe_node<true>(a, lp, t, lds, tid);
         }
     }
+    if (a.tclock) {
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_max(a.tclock + 1, wall_clock64(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // The persistent launch's flags, cleared before it starts: gflag [ng], hflag
 // [2][B] (in room for 4 B words), xflag [2][B] and the error word (one run of
-// words), active [2T].
-__global__ void pers_clear_kernel(unsigned* flags, int nflags, int32_t* active, int T) {
+// words), active [2T]; its clock pair when timed.
+__global__ void pers_clear_kernel(unsigned* flags, int nflags, int32_t* active, int T, unsigned long long* tclock) {
     for (int i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0u;
     for (int i = threadIdx.x; i < 2 * T; i += blockDim.x) active[i] = 0;
+    if (tclock && threadIdx.x < 2) tclock[threadIdx.x] = threadIdx.x ? 0ull : ~0ull;
 }
 
 }  // namespace
@@ -2109,7 +2117,8 @@ hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLd
                              LaunchEvents ev) {
     if (a.B == 0) return hipSuccess;
     // (gflag, hflag, xflag and perr are one run of words in the workspace)
-    hipLaunchKernelGGL(pers_clear_kernel, dim3(1), dim3(256), 0, stream, a.gflag, pp.ng + 6 * a.B + 1, a.active, a.T);
+    hipLaunchKernelGGL(pers_clear_kernel, dim3(1), dim3(256), 0, stream, a.gflag, pp.ng + 6 * a.B + 1, a.active, a.T,
+                       a.tclock);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;

@@ -342,7 +342,10 @@ dt_status dt_accept_greedy(dt_handle *h, const int32_t *tokens, const int32_t *p
  *   stage 6  the dt_accept_greedy kernel (one launch per call)
  *   stage 7  fused expansion launches of the call, summed  (level 2)
  *   stage 8  fused expansion, every launch separately      (level 2; the
- *            persistent expansion is one launch per call)
+ *            persistent expansion is one launch per call, timed by the
+ *            device's constant 100 MHz clock from its first workgroup's
+ *            start to its last one's end: events around a cooperative
+ *            launch would also span its hand-over between queues)
  * Timing calls are host-side and need the handle's device to be current.
  */
 dt_status dt_timing_enable(dt_handle *h, int level, int capacity);

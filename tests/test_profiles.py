@@ -19,12 +19,41 @@ def test_select_trace_mean_agrees_with_the_launch_events():
     # own launch-recorded events, both quoted in the same summary
     text = read("kernels_qwen3_4b_batched.md")
     trace = float(re.search(r"Top-M select of the benchmarked workload[^:]*: \d+ calls, mean ([0-9.]+) us", text).group(1))
-    events = float(re.search(r"HIP events that each launch records ([0-9.]+) us", text).group(1))
+    events = float(re.search(r"top-M select mean kernel time from the HIP events that each launch records ([0-9.]+) us",
+                             text).group(1))
     assert abs(trace - events) / events < 0.05, (trace, events)
 
 
+def test_persistent_trace_mean_agrees_with_the_launch_clock():
+    # the kernel-trace mean of the persistent expansion launches and the
+    # bench's own figure (the device-clock span each launch records)
+    text = read("kernels_qwen3_4b_batched.md")
+    trace = float(re.search(r"Persistent expansion of the benchmarked workload \(.*?\): \d+ launches, mean ([0-9.]+) us",
+                            text).group(1))
+    clock = float(re.search(r"persistent expansion mean kernel time from the device clock that each launch records "
+                            r"([0-9.]+) us", text).group(1))
+    assert abs(trace - clock) / clock < 0.05, (trace, clock)
+
+
+def test_persistent_traffic_line_is_consistent():
+    text = read("hbm_traffic_qwen3_4b_batched_pmc.md")
+    shown = re.search(r"(\d+) bytes fetched and (\d+) written per launch, (\d+) in all, against (\d+) algorithmic "
+                      r"\(([0-9.]+)x\)", text)
+    stored = re.search(r"pers_traffic_bytes=(\d+) source_sha256=[0-9a-f]{64}", text)
+    assert shown and stored
+    fetched, written, total, alg = (int(shown.group(i)) for i in range(1, 5))
+    ratio = float(shown.group(5))
+    assert abs(fetched + written - total) <= 1 and int(stored.group(1)) == total
+    assert abs(total / alg - ratio) < 1e-3
+    # the weights once and, per expansion, the gathered correction rows and the embedding row
+    B, L, E, H, M, n = 64, 16, 2560, 1024, 64, 16
+    assert alg == (3 * H * (E + H) + n * B * (M * H + E)) * 2
+    # the algorithmic bytes are all there; the rest is bounded (activations, sums, states)
+    assert 1.0 < ratio < 3.0
+
+
 def test_select_traffic_line_is_consistent():
-    text = read("topm_select_qwen3_4b_batched_pmc.md")
+    text = read("hbm_traffic_qwen3_4b_batched_pmc.md")
     shown = re.search(r"\): (\d+) bytes per launch against (\d+) algorithmic \(([0-9.]+)x\)", text)
     stored = re.search(r"topm_traffic_bytes=(\d+) source_sha256=[0-9a-f]{64}", text)
     assert shown and stored
@@ -64,17 +93,18 @@ def test_contraction_mfma_counters_match_the_kernel_structure():
     assert abs(float(shown.group(3)) - 2 * 64 * 3 * 1024 * (2560 + 1024) / 1e9) < 1e-3
 
 
-def test_fused_contraction_mfma_counters_match_the_kernel_structure():
-    # SQ_INSTS_VALU_MFMA_MOPS_BF16 of the benchmarked fused launches (their
-    # contraction workgroups): every (16-unit tile, 32-wide chunk) pair once,
-    # 4 row blocks, 3 gates; the x part (E / 32 chunks) one MFMA per block and
-    # gate, the h part (H / 32 chunks) three (the state's three bf16 parts)
+def test_persistent_contraction_mfma_counters_match_the_kernel_structure():
+    # SQ_INSTS_VALU_MFMA_MOPS_BF16 of the benchmarked persistent launches
+    # (their contraction workgroups): per contracting step every (16-unit
+    # tile, 32-wide chunk) pair once, 4 row blocks, 3 gates; the x part
+    # (E / 32 chunks) one MFMA per block and gate, the h part (H / 32 chunks)
+    # three (the state's three bf16 parts).  Steps 1 .. n always contract,
+    # step n + 1 only when some request waits in it.
     text = read("gru_contraction_qwen3_4b_batched_mfma.md")
-    m = re.search(r"fused_mfma_mops_bf16=(\d+) fused_mfma_busy_cycles=(\d+) source_sha256=[0-9a-f]{64}", text)
+    m = re.search(r"pers_mfma_mops_bf16=(\d+) pers_mfma_busy_cycles=(\d+) source_sha256=[0-9a-f]{64}", text)
     assert m
     mops, busy = int(m.group(1)), int(m.group(2))
-    tiles, rb, gates = 1024 // 16, 4, 3
-    x_mfma = tiles * (2560 // 32) * gates * rb
-    h_mfma = tiles * (1024 // 32) * 3 * gates * rb
-    assert mops == (x_mfma + h_mfma) * 32
-    assert busy == (x_mfma + h_mfma) * 16
+    tiles, rb, gates, n = 1024 // 16, 4, 3, 16
+    step = tiles * (2560 // 32) * gates * rb + tiles * (1024 // 32) * 3 * gates * rb
+    assert mops % (step * 32) == 0 and mops // (step * 32) in (n, n + 1)
+    assert busy * 2 == mops  # 16 busy cycles per 32-MOP MFMA
