@@ -578,13 +578,44 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         if (e != hipSuccess) return hip_fail(h, e, what);  \
     } while (0)
 
+    // the expansion's mode, decided before anything is enqueued: the
+    // persistent launch where the device holds its grid and the stream is
+    // not being captured, else one launch per step (fused), or the stepped
+    // launches.  The persistent launch's flags and clock pair are set by the
+    // top-M select (no launch of their own between the two).
+    const bool fused = !marginal && !table && !noalloc && h->pp.ng > 0;
+    bool pers = false;
+    if (fused && (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT)) {
+        if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B, c.V, c.E) ? 1 : 0;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
+        pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
+        if (c.expand == DT_EXPAND_PERSISTENT && !pers)
+            return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
+                                                   ? "persistent expansion: the stream is being captured"
+                                                   : "persistent expansion: the device cannot hold the grid "
+                                                     "(%d workgroups) at once, or V > 262143 or V E >= 2^31", h->pp.ng + c.B);
+    }
+    dt::TopmSide side{};
+    const int pslot = (int)h->calls.size() - 1;  // this call's clock pair, when timed
+    unsigned long long* pclock = nullptr;
+    if (pers) {
+        side.zero = (unsigned*)(w + L.p_done) + h->pipe_T;  // from gflag on
+        side.nzero = dt::pers_flag_words(h->pp, c.B);
+        // (timed: the launch writes its device-clock span, which is the
+        // stage's time; the events would span the cooperative launch's
+        // hand-over as well)
+        if (call && h->tlevel >= 2 && h->tclock && pslot < h->tclock_cap) pclock = h->tclock + 2 * (size_t)pslot;
+        side.clock = pclock;
+    }
+
     int32_t* tidx = (int32_t*)(w + L.tidx);
     float* tval = (float*)(w + L.tval);
     dt::LaunchEvents ev{};
     DT_TRY(kernel_marks(h, call, 1, 'K', 'T', &ev), "timing event");
     float* tail = c.full_vocab ? (float*)(w + L.tail) : nullptr;
     DT_TRY(dt::launch_topm(base, (int)c.dtype, c.B * c.L, c.V, h->nseg, (u64*)(w + L.partial), c.M,
-                           tidx, tval, st, ev, tail_scale(c), tail, (float*)(w + L.tail_part)),
+                           tidx, tval, st, ev, tail_scale(c), tail, (float*)(w + L.tail_part), side),
            "top-M launch");
     if (h->nseg > 1) DT_TRY(mark(h, call, 1, 'M', st), "timing event");  // after the merge kernel
 
@@ -642,7 +673,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         DT_TRY(mark(h, call, 1, 'E', st), "timing event");
         return DT_OK;
     }
-    if (!table && !noalloc && h->pp.ng > 0) {  // fused expansion: n + 2 launches
+    if (fused) {  // fused expansion: n + 2 launches
         dt::PipeArgs pa{};
         pa.B = c.B; pa.L = c.L; pa.V = c.V; pa.E = c.E; pa.H = c.H; pa.M = c.M; pa.n = c.n;
         pa.T = h->pipe_T;
@@ -673,30 +704,12 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         pa.rstate = a.rstate; pa.nidx = a.nidx; pa.nval = a.nval;
         pa.tokens = tokens; pa.parents = parents; pa.depths = depths; pa.scores = scores;
         pa.mask = mask; pa.count = count; pa.flags = flags;
-        // the persistent launch, where the device holds its grid and the
-        // stream is not being captured; else one launch per step
-        bool pers = false;
-        if (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT) {
-            if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B, c.V, c.E) ? 1 : 0;
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
-            pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
-            if (c.expand == DT_EXPAND_PERSISTENT && !pers)
-                return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
-                                                       ? "persistent expansion: the stream is being captured"
-                                                       : "persistent expansion: the device cannot hold the grid "
-                                                         "(%d workgroups) at once, or V > 262143 or V E >= 2^31", h->pp.ng + c.B);
-        }
         h->last_mode = pers ? DT_EXPAND_PERSISTENT : DT_EXPAND_FUSED;
         if (pers) {
             DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
-            // (timed: the launch also writes its device-clock span, which is
-            // the stage's time; the events would span the cooperative
-            // launch's hand-over as well)
-            const int slot = (int)h->calls.size() - 1;
-            if (ev.stop && h->tclock && slot < h->tclock_cap) {
-                pa.tclock = h->tclock + 2 * (size_t)slot;
-                call->back().clock = slot;
+            if (pclock) {  // (set up before the top-M select)
+                pa.tclock = pclock;
+                call->back().clock = pslot;
             }
             DT_TRY(dt::launch_pers_build(pa, h->pp, h->lds, st, ev), "persistent expansion launch");
         } else {

@@ -37,9 +37,19 @@ int topm_segments(int rows, int V);
 // exp(x / T) over the row's logits outside its top M (-inf if none), with
 // tail_c = log2(e) / T (T = 1 when T = 0); tail_part is rows*nseg*2 floats
 // of scratch.
+// side: words that the next kernel on the stream needs zeroed and a clock
+// pair it needs set to (max, 0) (the persistent expansion's flags and its
+// device-clock span), written by the select's first workgroup beside its row
+// so that no launch of their own runs between the two kernels.
+struct TopmSide {
+    unsigned* zero = nullptr;  // [nzero] (NULL: none)
+    int nzero = 0;
+    unsigned long long* clock = nullptr;  // [2] (NULL: none)
+};
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial, int M,
                        int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev = {},
-                       float tail_c = 0.f, float* tail_out = nullptr, float* tail_part = nullptr);
+                       float tail_c = 0.f, float* tail_out = nullptr, float* tail_part = nullptr,
+                       TopmSide side = {});
 
 // ---- GRU gate contraction (gru.hip) -----------------------------------------
 // bf16 path: the activations come packed for the MFMA operands (see
@@ -230,9 +240,12 @@ hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds
 // the call, the workgroups kept resident and handing over through counters
 // (see expand.hip).  pers_supported: the device can hold the whole grid at
 // once, V is small enough for a token in a flag word and V E for a 32-bit
-// row offset (checked once per plan); launch_pers_build zeroes the call's
-// flags and launches.
+// row offset (checked once per plan); launch_pers_build launches it.  The
+// call's flags, the pers_flag_words(pp, B) words from a.gflag on, must be
+// zero when it starts, and its clock pair (when timed) at (max, 0): the
+// top-M select before it sets them (TopmSide).
 bool pers_supported(const PipePlan& pp, int B, int V, int E);
+inline int pers_flag_words(const PipePlan& pp, int B) { return pp.ng + 6 * B + 1; }
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
                              LaunchEvents ev = {});
 

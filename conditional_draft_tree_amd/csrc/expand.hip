@@ -1976,15 +1976,6 @@ __global__ __launch_bounds__(kPipeThreads) void pers_kernel(PipeArgs a, NodeLds 
     }
 }
 
-// The persistent launch's flags, cleared before it starts: gflag [ng], hflag
-// [2][B] (in room for 4 B words), xflag [2][B] and the error word (one run of
-// words), active [2T]; its clock pair when timed.
-__global__ void pers_clear_kernel(unsigned* flags, int nflags, int32_t* active, int T, unsigned long long* tclock) {
-    for (int i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0u;
-    for (int i = threadIdx.x; i < 2 * T; i += blockDim.x) active[i] = 0;
-    if (tclock && threadIdx.x < 2) tclock[threadIdx.x] = threadIdx.x ? 0ull : ~0ull;
-}
-
 }  // namespace
 
 template <typename T>
@@ -2116,11 +2107,10 @@ bool pers_supported(const PipePlan& pp, int B, int V, int E) {
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
                              LaunchEvents ev) {
     if (a.B == 0) return hipSuccess;
-    // (gflag, hflag, xflag and perr are one run of words in the workspace)
-    hipLaunchKernelGGL(pers_clear_kernel, dim3(1), dim3(256), 0, stream, a.gflag, pp.ng + 6 * a.B + 1, a.active, a.T,
-                       a.tclock);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // (its flags -- gflag [ng], hflag [2][B] in room for 4 B words, xflag
+    // [2][B] and the error word, one run of words -- and its clock pair were
+    // set by the top-M select before it)
+    hipError_t e;
     if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
     PipeArgs args = a;
     NodeLds lds = lp;

@@ -301,7 +301,8 @@ __device__ __forceinline__ void drain_stash(WaveTop& w, TailAcc& ta, u64* buf, S
 // the top M (idx, val) directly (and with TAIL the row's tail_lse to
 // tail_out[row]) and no merge kernel runs; with several, each segment leaves
 // its list in `partial` (and its tail sum (m, s), list excluded, in
-// tail_part[row * nseg + segment]).
+// tail_part[row * nseg + segment]).  Workgroup (0, 0) also does the side job
+// (TopmSide: a run of words zeroed, a clock pair set).
 template <typename T, bool kVec, bool TAIL>
 __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __restrict__ base, int V,
                                                                     int nseg, int seg,
@@ -309,7 +310,8 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
                                                                     int32_t* __restrict__ idx,
                                                                     float* __restrict__ val, float tail_c,
                                                                     float* __restrict__ tail_out,
-                                                                    float2* __restrict__ tail_part) {
+                                                                    float2* __restrict__ tail_part,
+                                                                    TopmSide side) {
     __shared__ u64 sbuf[kWaves][kWave];
     __shared__ u32x4 svec[kWaves][kStash];
     __shared__ int sidx[kWaves][kStash];
@@ -323,6 +325,10 @@ __global__ __launch_bounds__(kTopmThreads) void topm_partial_kernel(const T* __r
     u64* buf = sbuf[wave];
     if (threadIdx.x == 0) s_thr.max64 = 0u;
     if (threadIdx.x < kWaves) s_thr.q16[threadIdx.x] = 0u;
+    if (row == 0 && s == 0) {  // the side job (see TopmSide)
+        for (int i = threadIdx.x; i < side.nzero; i += kTopmThreads) side.zero[i] = 0u;
+        if (side.clock && threadIdx.x < 2) side.clock[threadIdx.x] = threadIdx.x ? 0ull : ~0ull;
+    }
     __syncthreads();
 
     WaveTop w;
@@ -535,7 +541,7 @@ int topm_segments(int rows, int V) {
 
 hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u64* partial,
                        int M, int32_t* idx, float* val, hipStream_t stream, LaunchEvents ev, float tail_c,
-                       float* tail_out, float* tail_part) {
+                       float* tail_out, float* tail_part, TopmSide side) {
     if (rows == 0) return hipSuccess;
     const size_t esz = dtype == 1 ? 2 : 4;
     const int per_vec = 16 / (int)esz;
@@ -547,7 +553,7 @@ hipError_t launch_topm(const void* base, int dtype, int rows, int V, int nseg, u
     hipError_t e;
 #define DT_TOPM(Ty, kV, TL) \
     launch_kernel(topm_partial_kernel<Ty, kV, TL>, grid, block, 0, stream, ev, (const Ty*)base, V, nseg, seg, \
-                  partial, M, idx, val, tail_c, tail_out, tp)
+                  partial, M, idx, val, tail_c, tail_out, tp, side)
     if (tail_out) {
         if (dtype == 1) e = vec ? DT_TOPM(bf16_t, true, true) : DT_TOPM(bf16_t, false, true);
         else e = vec ? DT_TOPM(float, true, true) : DT_TOPM(float, false, true);
