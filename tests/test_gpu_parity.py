@@ -720,6 +720,30 @@ def test_persistent_equals_per_step_launches(name, over):
     assert int(got[dtree.DT_EXPAND_PERSISTENT]["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
 
 
+@pytest.mark.parametrize("mode", [dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT])
+def test_expansion_ignores_workspace_contents(mode):
+    # Nothing a call reads from its workspace survives from before it: with
+    # every byte set to 0xFF first (flag words that read as every step done,
+    # tokens and slots past their ranges) the trees equal those of a call on
+    # a fresh workspace bit for bit.  The persistent launch's flags are zeroed
+    # by the top-M select before it, the per-step launches' counters by
+    # their first launch.
+    cfg, inp = inputs("qwen3_4b_batched", over=(("B", 8),))
+    t = S.to_torch(inp, DEV)
+    bld = builder(dict(cfg, expand=mode))
+    args = (t["base"], t["emb"], t["w_ih"], t["w_hh"], t["b_ih"], t["b_hh"], t["C"], t["h0"])
+    ref = {k: v.cpu().clone() for k, v in bld.build(*args).items()}
+    torch.cuda.synchronize()
+    bld.workspace.fill_(255)
+    got = {k: v.cpu().clone() for k, v in bld.build(*args).items()}
+    torch.cuda.synchronize()
+    assert bld.expand_mode == mode
+    for k in ref:
+        assert torch.equal(_i32(ref[k]), _i32(got[k])), f"{MODE_NAME[mode]}: differs in {k} after 0xFF"
+    assert int(got["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
+    bld.close()
+
+
 # ------------------------------------------------ streams and graph replay --
 
 def _i32(t):
