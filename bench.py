@@ -171,18 +171,20 @@ def parse():
 
 
 def expansion_roofline(st, mode, B, L, E, H, M, n, esz, config, np):
-    """The persistent expansion launch (one per call: every step of both
-    roles).  Algorithmic bytes per launch: the GRU weights once,
-    3H (E + H) elements, and per expansion the gathered correction rows and
-    the embedding row, n B (M H + E) elements; flops: the gate contraction of
-    the T - 2 steps that contract, 2 B 3H (E + H) each.  Over the launch's
-    mean duration, which each launch records with the device clock (its first
-    workgroup's start to its last one's end; the library's stage 8)."""
+    """The persistent expansion (one launch per call, every step of both
+    roles; more than 64 requests: one launch per slice of 64).  Algorithmic
+    bytes per call: the GRU weights once per launch, 3H (E + H) elements, and
+    per expansion the gathered correction rows and the embedding row,
+    n B (M H + E) elements; flops: the gate contraction of the T - 2 steps
+    that contract, 2 B 3H (E + H) each.  Over the call's mean expansion time,
+    which the launches record with the device clock (the first workgroup's
+    start to the last one's end; the library's stage 8)."""
     if mode != "persistent" or not st["fused_each"]:
         return None
     T = n + 2
+    nsl = -(-B // 64)
     ms = float(np.mean(st["fused_each"]))
-    nbytes = (3 * H * (E + H) + n * B * (M * H + E)) * esz
+    nbytes = (nsl * 3 * H * (E + H) + n * B * (M * H + E)) * esz
     flop = (T - 2) * 2.0 * B * 3 * H * (E + H)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tfs = flop / (ms * 1e-3) / 1e12
@@ -197,7 +199,7 @@ def expansion_roofline(st, mode, B, L, E, H, M, n, esz, config, np):
             "flop_per_launch": flop, "achieved_tflops": round(tfs, 2),
             "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 5),
             "mean_launch_ms": round(ms, 5), "launches": len(st["fused_each"]),
-            "step_us": round(ms * 1e3 / T, 2),
+            "slices": nsl, "step_us": round(ms * 1e3 / (nsl * T), 2),
             "counters": counter_figures(mfma_counters("pers", FUSED_SOURCES), ms)
             if config == "qwen3_4b_batched" else None}
 
@@ -332,7 +334,7 @@ def main():
     # ---- the same pipeline as one launch per step (its own handle), where
     # the default runs it persistent: round time, per-launch time, trees
     per_step = None
-    if mode == "persistent":
+    if mode == "persistent" and B <= 64:  # (one launch per step holds at most 64 requests)
         pbld = dtree.Builder(B, L, V, E, H, M, n, cfg["T"], cfg["dtype"], 1e-5, device=dev,
                              expand=dtree.DT_EXPAND_FUSED)
         pout = step(b=pbld)

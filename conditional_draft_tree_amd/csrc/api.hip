@@ -134,7 +134,9 @@ Layout plan_layout(const dt_config& c, int nseg, int ksplit, bool wtiles = true,
     l.p_gh = take(fp ? B * S * (size_t)pp.ksh * 3 * H * 4 : 0);  // h-part gate sums per slot
     l.p_hstate = take(fp ? B * S * H * 4 : 0);        // binary32 state per slot
     l.p_exp = take(fp ? B * S * 4 : 0);               // launch that expanded each slot
-    l.p_done = take(fp ? ((size_t)pT + pp.ng + 6 * B + 1) * 4 : 0);  // per-launch counters, flags, error word
+    // per-launch counters, then each slice's flags and error word
+    l.p_done = take(fp ? ((size_t)pT + (size_t)dt::pers_slices(c.B) * dt::pers_flag_words(pp, dt::pers_slice_b(c.B))) * 4
+                       : 0);
     l.p_active = take(fp ? (size_t)2 * pT * 4 : 0);
     l.p_xpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * c.E * 2 : 0);  // parity-1 activations
     l.p_hpack1 = take(fp ? (size_t)dt::pack_rows(c.B) * 3 * H * 2 : 0);
@@ -304,14 +306,22 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     h->lds = lds;
     h->pp = dt::PipePlan{};
     h->pipe_T = 0;
-    if (c.dtype == DT_BF16 && c.expand != DT_EXPAND_STEPPED) {
-        h->pp = dt::pipe_plan(c.B, c.L, c.E, c.H, c.M, c.n);
+    if (c.expand == DT_EXPAND_FUSED && c.B > dt::kPipeSliceB) {
+        delete h;
+        return fail(nullptr, DT_ERR_UNSUPPORTED, "one launch per step needs B <= %d", dt::kPipeSliceB);
+    }
+    // more requests than one grid holds: the persistent launch in slices (with
+    // the plan of one) only when asked for -- on deep chains its requests wait
+    // inside the steps, and the slices run one after another
+    if (c.dtype == DT_BF16 && c.expand != DT_EXPAND_STEPPED &&
+        (c.B <= dt::kPipeSliceB || c.expand == DT_EXPAND_PERSISTENT)) {
+        h->pp = dt::pipe_plan(dt::pers_slice_b(c.B), c.L, c.E, c.H, c.M, c.n);
         h->pipe_T = c.n + 2;
     }
     if ((c.expand == DT_EXPAND_FUSED || c.expand == DT_EXPAND_PERSISTENT) && h->pp.ng == 0) {
         delete h;
         return fail(nullptr, DT_ERR_UNSUPPORTED,
-                    "fused expansion needs bf16, 1 <= B <= 64, H <= 1024 and E, H multiples of 32");
+                    "fused expansion needs bf16, H <= 1024 and E, H multiples of 32");
     }
     h->last_mode = h->pp.ng == 0 ? DT_EXPAND_STEPPED
                    : c.expand == DT_EXPAND_FUSED ? DT_EXPAND_FUSED : DT_EXPAND_PERSISTENT;
@@ -583,10 +593,11 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     // not being captured, else one launch per step (fused), or the stepped
     // launches.  The persistent launch's flags and clock pair are set by the
     // top-M select (no launch of their own between the two).
-    const bool fused = !marginal && !table && !noalloc && h->pp.ng > 0;
+    const int nsl = dt::pers_slices(c.B), bsl = dt::pers_slice_b(c.B);
+    bool fused = !marginal && !table && !noalloc && h->pp.ng > 0;
     bool pers = false;
     if (fused && (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT)) {
-        if (h->pers < 0) h->pers = dt::pers_supported(h->pp, c.B, c.V, c.E) ? 1 : 0;
+        if (h->pers < 0) h->pers = dt::pers_supported(h->pp, bsl, c.V, c.E) ? 1 : 0;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
         pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
@@ -594,14 +605,15 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
             return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
                                                    ? "persistent expansion: the stream is being captured"
                                                    : "persistent expansion: the device cannot hold the grid "
-                                                     "(%d workgroups) at once, or V > 262143 or V E >= 2^31", h->pp.ng + c.B);
+                                                     "(%d workgroups) at once, or V > 262143 or V E >= 2^31", h->pp.ng + bsl);
     }
+    if (nsl > 1 && !pers) fused = false;  // (more requests than one launch step holds: stepped)
     dt::TopmSide side{};
     const int pslot = (int)h->calls.size() - 1;  // this call's clock pair, when timed
     unsigned long long* pclock = nullptr;
     if (pers) {
         side.zero = (unsigned*)(w + L.p_done) + h->pipe_T;  // from gflag on
-        side.nzero = dt::pers_flag_words(h->pp, c.B);
+        side.nzero = nsl * dt::pers_flag_words(h->pp, bsl);  // (every slice's)
         // (timed: the launch writes its device-clock span, which is the
         // stage's time; the events would span the cooperative launch's
         // hand-over as well)
@@ -711,7 +723,42 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
                 pa.tclock = pclock;
                 call->back().clock = pslot;
             }
-            DT_TRY(dt::launch_pers_build(pa, h->pp, h->lds, st, ev), "persistent expansion launch");
+            // one launch per slice of requests, each on its own flag words;
+            // the events (when timed) span them all
+            const int S = c.n + 1, LM = c.L * c.M, H = c.H, fw = dt::pers_flag_words(h->pp, bsl);
+            for (int sl = 0; sl < nsl; ++sl) {
+                const int b0 = sl * bsl;
+                const size_t r = (size_t)b0;
+                dt::PipeArgs ps = pa;
+                ps.B = std::min(bsl, c.B - b0);
+                if (h0) ps.h0 = h0 + r * H;
+                ps.tidx = tidx + r * LM;
+                ps.tval = tval + r * LM;
+                if (tail) ps.tail = tail + r * c.L;
+                ps.gh = pa.gh + r * S * h->pp.ksh * 3 * H;
+                ps.hstate = pa.hstate + r * S * H;
+                ps.exp_at = pa.exp_at + r * S;
+                ps.gflag = pa.gflag + (size_t)sl * fw;
+                ps.hflag = ps.gflag + ps.ng;
+                ps.xflag = ps.hflag + 4 * bsl;
+                ps.perr = ps.xflag + 2 * bsl;
+                ps.child_tok = pa.child_tok + r * S * 64;
+                ps.child_lp = pa.child_lp + r * S * 64;
+                ps.ckey = pa.ckey + r * S * 64;
+                ps.queue = pa.queue + r * 64;
+                ps.rstate = pa.rstate + r * dt::kStateWords;
+                ps.nidx = pa.nidx + r * 64;
+                ps.nval = pa.nval + r * 64;
+                ps.tokens = tokens + r * S;
+                ps.parents = parents + r * S;
+                ps.depths = depths + r * S;
+                ps.scores = scores + r * S;
+                ps.mask = mask + r * S * S;
+                ps.count = count + r;
+                ps.flags = flags + r;
+                dt::LaunchEvents es{sl == 0 ? ev.start : nullptr, sl == nsl - 1 ? ev.stop : nullptr};
+                DT_TRY(dt::launch_pers_build(ps, h->pp, h->lds, st, es), "persistent expansion launch");
+            }
         } else {
             for (int t = 0; t < h->pipe_T; ++t) {
                 DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
@@ -721,6 +768,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         DT_TRY(mark(h, call, 1, 'E', st), "timing event");
         return DT_OK;
     }
+    if (!noalloc && !table) h->last_mode = DT_EXPAND_STEPPED;  // (a persistent plan that could not run)
     DT_TRY(kernel_marks(h, call, 2, 'n', 'N', &ev), "timing event");
     DT_TRY(dt::launch_node_step(a, h->lds, 0, st, ev), "node step launch");
     for (int step = 1; step < c.n; ++step) {

@@ -244,8 +244,14 @@ hipError_t launch_pipe_step(const PipeArgs& a, const PipePlan& pp, const NodeLds
 // call's flags, the pers_flag_words(pp, B) words from a.gflag on, must be
 // zero when it starts, and its clock pair (when timed) at (max, 0): the
 // top-M select before it sets them (TopmSide).
+// More requests than one grid holds (B > kPipeSliceB) run as consecutive
+// launches of kPipeSliceB requests each (the last one takes the rest), every
+// launch with its own run of flag words; the plan is that of kPipeSliceB.
+constexpr int kPipeSliceB = 64;
 bool pers_supported(const PipePlan& pp, int B, int V, int E);
 inline int pers_flag_words(const PipePlan& pp, int B) { return pp.ng + 6 * B + 1; }
+inline int pers_slices(int B) { return (B + kPipeSliceB - 1) / kPipeSliceB; }
+inline int pers_slice_b(int B) { return B < kPipeSliceB ? B : kPipeSliceB; }
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
                              LaunchEvents ev = {});
 

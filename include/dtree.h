@@ -73,19 +73,23 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *   expand       how dt_build runs the expansion steps (same trees either
  *                way, up to binary32 rounding order of the GRU gate sums):
  *                DT_EXPAND_AUTO (0) persistent where the device and stream
- *                allow it, else fused where supported, else stepped;
- *                DT_EXPAND_STEPPED (1) two launches per step, the batched
- *                GRU contraction then the node step; DT_EXPAND_FUSED (2) one
- *                launch per step in which the contraction of the rows the
- *                requests need next runs beside the node steps (bf16, B <= 64,
- *                H <= 1024; otherwise dt_create returns DT_ERR_UNSUPPORTED);
- *                DT_EXPAND_PERSISTENT (3) the fused steps in one cooperative
- *                launch whose workgroups stay resident (the contraction keeps
- *                its weights in registers) and hand over through counters
- *                (same conditions; dt_build returns DT_ERR_UNSUPPORTED when
- *                the device cannot hold the whole grid at once or the stream
- *                is being captured).  The same trees, bit for bit, as
- *                DT_EXPAND_FUSED.
+ *                allow it and B <= 64, else fused where supported, else
+ *                stepped; DT_EXPAND_STEPPED (1) two launches per step, the
+ *                batched GRU contraction then the node step; DT_EXPAND_FUSED
+ *                (2) one launch per step in which the contraction of the rows
+ *                the requests need next runs beside the node steps (bf16,
+ *                B <= 64, H <= 1024; otherwise dt_create returns
+ *                DT_ERR_UNSUPPORTED); DT_EXPAND_PERSISTENT (3) the fused
+ *                steps in one cooperative launch whose workgroups stay
+ *                resident (the contraction keeps its weights in registers)
+ *                and hand over through counters (bf16, H <= 1024; more than
+ *                64 requests run as consecutive launches of 64 -- faster than
+ *                stepped on shallow trees, slower on deep chains, where
+ *                requests wait inside the steps; dt_build returns
+ *                DT_ERR_UNSUPPORTED when the device cannot hold a launch's
+ *                grid at once or the stream is being captured).  The same
+ *                trees, bit for bit, as DT_EXPAND_FUSED, and for each slice
+ *                of 64 requests as a call on those requests alone.
  * A request's expansion state lives in one workgroup's LDS: configurations with
  * 4 H + 8 L M + 512 n bytes (plus ~0.8 KiB) above 64 KiB are DT_ERR_UNSUPPORTED. */
 typedef enum { DT_EXPAND_AUTO = 0, DT_EXPAND_STEPPED = 1, DT_EXPAND_FUSED = 2, DT_EXPAND_PERSISTENT = 3 } dt_expand;

@@ -209,12 +209,15 @@ def test_expand_mode_is_validated():
         bad = dt_config(2, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_BF16, 1e-5, 0, e)
         assert lib.dt_create(C.byref(bad), C.byref(out)) == -1 and not out.value
         assert "expand" in dtree.dt_last_error(None)
-    # the fused expansion (per-step launches or persistent) is bf16 with at
-    # most 64 requests and H <= 1024
+    # the fused expansion (per-step launches or persistent) is bf16 with
+    # H <= 1024; one launch per step holds at most 64 requests, the persistent
+    # launch takes more in slices of 64
     for e in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT):
-        for kw in (dict(dtype=dtree.DT_F32), dict(B=65), dict(H=2048)):
+        for kw in (dict(dtype=dtree.DT_F32), dict(H=2048)):
             with pytest.raises(ValueError, match="UNSUPPORTED"):
                 make(expand=e, **kw)
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        make(expand=dtree.DT_EXPAND_FUSED, B=65)
     # the mode dt_build runs, before any call: auto selects the persistent
     # launch where the fused expansion applies (a call may fall back to the
     # per-step launches)
@@ -225,10 +228,22 @@ def test_expand_mode_is_validated():
         h = make(expand=e)
         assert dtree.dt_expand_mode(h) == want
         dtree.dt_destroy(h)
-    for kw in (dict(dtype=dtree.DT_F32), dict(B=65), dict(H=2048)):
+    for kw in (dict(dtype=dtree.DT_F32), dict(H=2048)):
         h = make(**kw)
         assert dtree.dt_expand_mode(h) == dtree.DT_EXPAND_STEPPED
         dtree.dt_destroy(h)
+    # more than 64 requests: stepped unless the persistent launch (in slices
+    # of 64) is asked for
+    for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_STEPPED),
+                    (dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_PERSISTENT)):
+        h = make(expand=e, B=65)
+        assert dtree.dt_expand_mode(h) == want
+        dtree.dt_destroy(h)
+    # the stress shape (B = 256, n = 64) fits the persistent plan: four launches
+    h = dtree.dt_create(256, 16, 151936, 2560, 1024, 64, 64, 0.0, dtree.DT_BF16, 1e-5,
+                        expand=dtree.DT_EXPAND_PERSISTENT)
+    assert dtree.dt_expand_mode(h) == dtree.DT_EXPAND_PERSISTENT
+    dtree.dt_destroy(h)
     assert lib.dt_expand_mode(None) == -1
     # the fused expansion's workspace holds its per-slot gate sums besides the stepped path's
     assert dtree.dt_workspace_bytes(make(expand=dtree.DT_EXPAND_FUSED)) > \

@@ -50,8 +50,8 @@ def builder(cfg, eps=1e-5):
 
 
 # dt_build's ways of running the expansion: "auto" takes the persistent launch
-# wherever it applies (bf16, B <= 64, H <= 1024, a device that holds the
-# grid), "fused" forces one launch per step of the same pipeline, "stepped" two
+# wherever it applies (bf16, H <= 1024, a device that holds the grid; more
+# than 64 requests in launches of 64), "fused" forces one launch per step of the same pipeline, "stepped" two
 # launches per step; the whole-build tests run each where it applies
 EXPAND = {"auto": dtree.DT_EXPAND_AUTO, "fused": dtree.DT_EXPAND_FUSED, "stepped": dtree.DT_EXPAND_STEPPED}
 MODE_NAME = {dtree.DT_EXPAND_STEPPED: "stepped", dtree.DT_EXPAND_FUSED: "fused",
@@ -718,6 +718,31 @@ def test_persistent_equals_per_step_launches(name, over):
         assert torch.equal(_i32(got[dtree.DT_EXPAND_FUSED][k]), _i32(got[dtree.DT_EXPAND_PERSISTENT][k])), \
             f"persistent differs from per-step launches in {k}"
     assert int(got[dtree.DT_EXPAND_PERSISTENT]["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
+
+
+def test_persistent_in_slices_beyond_one_grid():
+    # B = 100 requests: two persistent launches (64 requests, then 36), each
+    # on its own flag words.  Every request against the oracle; each slice's
+    # outputs equal, bit for bit, those of a build of its requests alone (one
+    # launch), twice in a row on one handle.
+    cfg, inp = inputs("qwen3_4b_batched", over=(("B", 100),))
+    cfg = dict(cfg, expand=dtree.DT_EXPAND_PERSISTENT)
+    got, _, _ = build_and_compare(cfg, inp)
+    t = S.to_torch(inp, DEV)
+    bld = builder(cfg)
+    again = run_build(bld, t)
+    bld.close()
+    for k in got:
+        assert np.array_equal(got[k], again[k]), f"second call differs in {k}"
+    for b0, b1 in ((0, 64), (64, 100)):
+        sub = dict(inp, base=inp["base"][b0:b1], h0=inp["h0"][b0:b1] if inp["h0"] is not None else None)
+        bld = builder(dict(cfg, B=b1 - b0))
+        one = run_build(bld, S.to_torch(sub, DEV))
+        assert bld.expand_mode == dtree.DT_EXPAND_PERSISTENT
+        bld.close()
+        for k in one:
+            assert np.array_equal(one[k], got[k][b0:b1]), f"requests {b0}..{b1 - 1} differ in {k}"
+    assert int(got["flags"].view(np.int32).min()) >= 0, "a wait ran out"
 
 
 @pytest.mark.parametrize("mode", [dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT])
