@@ -720,12 +720,13 @@ def test_persistent_equals_per_step_launches(name, over):
     assert int(got[dtree.DT_EXPAND_PERSISTENT]["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
 
 
-def test_persistent_in_slices_beyond_one_grid():
-    # B = 100 requests: two persistent launches (64 requests, then 36), each
-    # on its own flag words.  Every request against the oracle; each slice's
-    # outputs equal, bit for bit, those of a build of its requests alone (one
-    # launch), twice in a row on one handle.
-    cfg, inp = inputs("qwen3_4b_batched", over=(("B", 100),))
+@pytest.mark.parametrize("B", [65, 100])
+def test_persistent_in_slices_beyond_one_grid(B):
+    # More than 64 requests: two persistent launches (64 requests, then the
+    # rest: 1 or 36), each on its own flag words.  Every request against the
+    # oracle, twice in a row on one handle; each slice's outputs equal, bit
+    # for bit, those of a build of its requests alone (one launch).
+    cfg, inp = inputs("qwen3_4b_batched", over=(("B", B),))
     cfg = dict(cfg, expand=dtree.DT_EXPAND_PERSISTENT)
     got, _, _ = build_and_compare(cfg, inp)
     t = S.to_torch(inp, DEV)
@@ -734,7 +735,7 @@ def test_persistent_in_slices_beyond_one_grid():
     bld.close()
     for k in got:
         assert np.array_equal(got[k], again[k]), f"second call differs in {k}"
-    for b0, b1 in ((0, 64), (64, 100)):
+    for b0, b1 in ((0, 64), (64, B)):
         sub = dict(inp, base=inp["base"][b0:b1], h0=inp["h0"][b0:b1] if inp["h0"] is not None else None)
         bld = builder(dict(cfg, B=b1 - b0))
         one = run_build(bld, S.to_torch(sub, DEV))
