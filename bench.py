@@ -285,8 +285,9 @@ def main():
     call_ms = dtree.dt_timing_read(bld.handle, 4)
     dtree.dt_timing_enable(bld.handle, 0, 0)
 
-    mode = {dtree.DT_EXPAND_PERSISTENT: "persistent", dtree.DT_EXPAND_FUSED: "fused",
-            dtree.DT_EXPAND_STEPPED: "stepped"}[bld.expand_mode]
+    mode = {dtree.DT_EXPAND_PERSISTENT: "persistent", dtree.DT_EXPAND_RESIDENT: "persistent",
+            dtree.DT_EXPAND_FUSED: "fused", dtree.DT_EXPAND_STEPPED: "stepped"}[bld.expand_mode]
+    launch = {dtree.DT_EXPAND_PERSISTENT: "cooperative", dtree.DT_EXPAND_RESIDENT: "plain"}.get(bld.expand_mode)
     ms_per_step = elapsed * 1e3 / args.steps
     value = B * args.steps / elapsed
     round_us = [m * 1e3 for m in call_ms]
@@ -356,6 +357,23 @@ def main():
                     "launch_us_mean": round(float(np.mean(p_each)) * 1e3, 2) if p_each else None,
                     "trees_equal_bit_for_bit": all(bool(torch.equal(pout[k], out[k])) for k in out)}
         pbld.close()
+    # ---- the same persistent kernel as a cooperative launch (its own handle),
+    # where the default launches it plainly: round time, trees
+    coop_leg = None
+    if launch == "plain":
+        cbld = dtree.Builder(B, L, V, E, H, M, n, cfg["T"], cfg["dtype"], 1e-5, device=dev,
+                             expand=dtree.DT_EXPAND_PERSISTENT)
+        cout = step(b=cbld)
+        for _ in range(3):
+            step(cout, b=cbld)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(args.stage_steps):
+            step(cout, b=cbld)
+        torch.cuda.synchronize()
+        coop_leg = {"us_per_round": round((time.perf_counter() - c0) * 1e6 / max(args.stage_steps, 1), 1),
+                    "trees_equal_bit_for_bit": all(bool(torch.equal(cout[k], out[k])) for k in out)}
+        cbld.close()
     gemm_each = float(np.mean(sst["gru_gemm_each"])) if sst["gru_gemm_each"] else float("nan")
     gemm_flop = 2.0 * B * 3 * H * (E + H)
     gemm_weight_bytes = 3 * H * (E + H) * esz
@@ -416,8 +434,8 @@ def main():
         torch.cuda.synchronize()
         h256 = {"workload": "qwen3_4b_head256: H=256, C [V, 256], otherwise as the main workload",
                 "us_per_round": round(h_us, 1), "tree_builds_per_s": round(B / (h_us * 1e-6), 1),
-                "expansion": {dtree.DT_EXPAND_PERSISTENT: "persistent", dtree.DT_EXPAND_FUSED: "fused",
-                              dtree.DT_EXPAND_STEPPED: "stepped"}[hb.expand_mode]}
+                "expansion": {dtree.DT_EXPAND_PERSISTENT: "persistent", dtree.DT_EXPAND_RESIDENT: "persistent",
+                              dtree.DT_EXPAND_FUSED: "fused", dtree.DT_EXPAND_STEPPED: "stepped"}[hb.expand_mode]}
         if hb.fused:
             h256["expansion_launch_us"] = round(float(np.mean(dtree.dt_timing_read(hb.handle, 8))) * 1e3, 2)
         else:
@@ -598,7 +616,8 @@ def main():
             if args.config == "qwen3_4b_batched" else None,
         },
         "stages_ms_mean": {k: round(float(np.mean(v)), 5) for k, v in st.items() if v},
-        "expansion": fused_summary(st, sst, mode, n, stepped_us, stepped_same, per_step, np),
+        "expansion": dict(fused_summary(st, sst, mode, n, stepped_us, stepped_same, per_step, np),
+                          launch=launch, cooperative_launch=coop_leg),
         # (null: each row is one segment, so no merge kernel runs)
         "topm_merge_ms_mean": round(float(np.mean(merge_ms)), 5) if merge_ms else None,
         "call_ms_events_mean": round(float(np.mean(call_ms)), 5),

@@ -11,7 +11,7 @@ _lock = threading.Lock()
 _lib = None
 
 DT_F32, DT_BF16 = 0, 1
-DT_EXPAND_AUTO, DT_EXPAND_STEPPED, DT_EXPAND_FUSED, DT_EXPAND_PERSISTENT = 0, 1, 2, 3
+DT_EXPAND_AUTO, DT_EXPAND_STEPPED, DT_EXPAND_FUSED, DT_EXPAND_PERSISTENT, DT_EXPAND_RESIDENT = 0, 1, 2, 3, 4
 _STATUS = {0: "DT_OK", -1: "DT_ERR_INVALID_ARG", -2: "DT_ERR_UNSUPPORTED", -3: "DT_ERR_WORKSPACE",
            -4: "DT_ERR_HIP"}
 
@@ -245,7 +245,7 @@ class Builder:
     def fused(self) -> bool:
         """True when dt_build runs the fused expansion (per-step launches or the
         persistent launch) for this configuration."""
-        return dt_expand_mode(self.handle) in (DT_EXPAND_FUSED, DT_EXPAND_PERSISTENT)
+        return dt_expand_mode(self.handle) in (DT_EXPAND_FUSED, DT_EXPAND_PERSISTENT, DT_EXPAND_RESIDENT)
 
     @property
     def expand_mode(self) -> int:

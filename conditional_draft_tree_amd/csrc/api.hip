@@ -275,7 +275,7 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
         return fail(nullptr, DT_ERR_INVALID_ARG, "temperature and near_tie_eps must be >= 0");
     if (c.full_vocab != 0 && c.full_vocab != 1)
         return fail(nullptr, DT_ERR_INVALID_ARG, "full_vocab must be 0 or 1 (got %d)", (int)c.full_vocab);
-    if (c.expand < DT_EXPAND_AUTO || c.expand > DT_EXPAND_PERSISTENT)
+    if (c.expand < DT_EXPAND_AUTO || c.expand > DT_EXPAND_RESIDENT)
         return fail(nullptr, DT_ERR_INVALID_ARG, "expand must be 0, 1, 2 or 3 (got %d)", (int)c.expand);
     if (c.M > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "M=%d > 64 (one candidate per lane)", c.M);
     if (c.n > 64) return fail(nullptr, DT_ERR_UNSUPPORTED, "n=%d > 64 (queue of one wave)", c.n);
@@ -314,17 +314,20 @@ dt_status dt_create(const dt_config* cfg, dt_handle** out) {
     // the plan of one) only when asked for -- on deep chains its requests wait
     // inside the steps, and the slices run one after another
     if (c.dtype == DT_BF16 && c.expand != DT_EXPAND_STEPPED &&
-        (c.B <= dt::kPipeSliceB || c.expand == DT_EXPAND_PERSISTENT)) {
+        (c.B <= dt::kPipeSliceB || c.expand == DT_EXPAND_PERSISTENT || c.expand == DT_EXPAND_RESIDENT)) {
         h->pp = dt::pipe_plan(dt::pers_slice_b(c.B), c.L, c.E, c.H, c.M, c.n);
         h->pipe_T = c.n + 2;
     }
-    if ((c.expand == DT_EXPAND_FUSED || c.expand == DT_EXPAND_PERSISTENT) && h->pp.ng == 0) {
+    if ((c.expand == DT_EXPAND_FUSED || c.expand == DT_EXPAND_PERSISTENT || c.expand == DT_EXPAND_RESIDENT) &&
+        h->pp.ng == 0) {
         delete h;
         return fail(nullptr, DT_ERR_UNSUPPORTED,
                     "fused expansion needs bf16, H <= 1024 and E, H multiples of 32");
     }
-    h->last_mode = h->pp.ng == 0 ? DT_EXPAND_STEPPED
-                   : c.expand == DT_EXPAND_FUSED ? DT_EXPAND_FUSED : DT_EXPAND_PERSISTENT;
+    h->last_mode = h->pp.ng == 0                   ? DT_EXPAND_STEPPED
+                   : c.expand == DT_EXPAND_FUSED      ? DT_EXPAND_FUSED
+                   : c.expand == DT_EXPAND_PERSISTENT ? DT_EXPAND_PERSISTENT
+                                                      : DT_EXPAND_RESIDENT;
     h->lay = plan_layout(c, h->nseg, std::max(h->ksplit, h->ksplit_f), true, h->pp, h->pipe_T);
     h->lay_na = plan_layout(c, h->nseg, h->ksplit, /*wtiles=*/false);
     *out = h;
@@ -596,12 +599,16 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
     const int nsl = dt::pers_slices(c.B), bsl = dt::pers_slice_b(c.B);
     bool fused = !marginal && !table && !noalloc && h->pp.ng > 0;
     bool pers = false;
-    if (fused && (c.expand == DT_EXPAND_AUTO || c.expand == DT_EXPAND_PERSISTENT)) {
+    // (the cooperative launch only where asked for; otherwise a plain launch
+    // of the same grid, whose co-residency rests on the occupancy check)
+    const bool coop = c.expand == DT_EXPAND_PERSISTENT;
+    const bool want_pers = c.expand == DT_EXPAND_PERSISTENT || c.expand == DT_EXPAND_RESIDENT;
+    if (fused && (c.expand == DT_EXPAND_AUTO || want_pers)) {
         if (h->pers < 0) h->pers = dt::pers_supported(h->pp, bsl, c.V, c.E) ? 1 : 0;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         DT_TRY(hipStreamIsCapturing(st, &cs), "stream capture query");
         pers = h->pers == 1 && cs == hipStreamCaptureStatusNone;
-        if (c.expand == DT_EXPAND_PERSISTENT && !pers)
+        if (want_pers && !pers)
             return fail(h, DT_ERR_UNSUPPORTED, h->pers == 1
                                                    ? "persistent expansion: the stream is being captured"
                                                    : "persistent expansion: the device cannot hold the grid "
@@ -716,7 +723,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
         pa.rstate = a.rstate; pa.nidx = a.nidx; pa.nval = a.nval;
         pa.tokens = tokens; pa.parents = parents; pa.depths = depths; pa.scores = scores;
         pa.mask = mask; pa.count = count; pa.flags = flags;
-        h->last_mode = pers ? DT_EXPAND_PERSISTENT : DT_EXPAND_FUSED;
+        h->last_mode = pers ? (coop ? DT_EXPAND_PERSISTENT : DT_EXPAND_RESIDENT) : DT_EXPAND_FUSED;
         if (pers) {
             DT_TRY(kernel_marks(h, call, 2, 'p', 'P', &ev), "timing event");
             if (pclock) {  // (set up before the top-M select)
@@ -757,7 +764,7 @@ dt_status build_impl(bool marginal, dt_handle* h, void* ws, size_t ws_bytes, con
                 ps.count = count + r;
                 ps.flags = flags + r;
                 dt::LaunchEvents es{sl == 0 ? ev.start : nullptr, sl == nsl - 1 ? ev.stop : nullptr};
-                DT_TRY(dt::launch_pers_build(ps, h->pp, h->lds, st, es), "persistent expansion launch");
+                DT_TRY(dt::launch_pers_build(ps, h->pp, h->lds, st, es, coop), "persistent expansion launch");
             }
         } else {
             for (int t = 0; t < h->pipe_T; ++t) {

@@ -252,8 +252,11 @@ bool pers_supported(const PipePlan& pp, int B, int V, int E);
 inline int pers_flag_words(const PipePlan& pp, int B) { return pp.ng + 6 * B + 1; }
 inline int pers_slices(int B) { return (B + kPipeSliceB - 1) / kPipeSliceB; }
 inline int pers_slice_b(int B) { return B < kPipeSliceB ? B : kPipeSliceB; }
+// coop: a cooperative launch (the runtime guarantees the grid's
+// co-residency); otherwise a plain launch of the same grid, resident by the
+// occupancy check alone (every wait is bounded either way).
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
-                             LaunchEvents ev = {});
+                             LaunchEvents ev = {}, bool coop = true);
 
 // Conditional children distribution of one node per row (dt_correct).
 hipError_t launch_correct(const int32_t* tidx, const float* tval, const void* C, const float* h,

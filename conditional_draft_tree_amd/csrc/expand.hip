@@ -2105,7 +2105,7 @@ bool pers_supported(const PipePlan& pp, int B, int V, int E) {
 }
 
 hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLds& lp, hipStream_t stream,
-                             LaunchEvents ev) {
+                             LaunchEvents ev, bool coop) {
     if (a.B == 0) return hipSuccess;
     // (its flags -- gflag [ng], hflag [2][B] in room for 4 B words, xflag
     // [2][B] and the error word, one run of words -- and its clock pair were
@@ -2119,7 +2119,8 @@ hipError_t launch_pers_build(const PipeArgs& a, const PipePlan& pp, const NodeLd
     const void* fn = pp.rb == 4 ? (const void*)pers_kernel<4>
                    : pp.rb == 2 ? (const void*)pers_kernel<2>
                                 : (const void*)pers_kernel<1>;
-    e = hipLaunchCooperativeKernel(fn, grid, block, params, (unsigned)pp.lds, stream);
+    e = coop ? hipLaunchCooperativeKernel(fn, grid, block, params, (unsigned)pp.lds, stream)
+             : hipLaunchKernel(fn, grid, block, params, (unsigned)pp.lds, stream);
     if (e != hipSuccess) return e;
     if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return e;
     return hipSuccess;

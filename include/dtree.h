@@ -72,9 +72,9 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *                dt_build_marginal.
  *   expand       how dt_build runs the expansion steps (same trees either
  *                way, up to binary32 rounding order of the GRU gate sums):
- *                DT_EXPAND_AUTO (0) persistent where the device and stream
- *                allow it and B <= 64, else fused where supported, else
- *                stepped; DT_EXPAND_STEPPED (1) two launches per step, the
+ *                DT_EXPAND_AUTO (0) resident (below) where the device and
+ *                stream allow it and B <= 64, else fused where supported,
+ *                else stepped; DT_EXPAND_STEPPED (1) two launches per step, the
  *                batched GRU contraction then the node step; DT_EXPAND_FUSED
  *                (2) one launch per step in which the contraction of the rows
  *                the requests need next runs beside the node steps (bf16,
@@ -89,10 +89,25 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *                DT_ERR_UNSUPPORTED when the device cannot hold a launch's
  *                grid at once or the stream is being captured).  The same
  *                trees, bit for bit, as DT_EXPAND_FUSED, and for each slice
- *                of 64 requests as a call on those requests alone.
+ *                of 64 requests as a call on those requests alone;
+ *                DT_EXPAND_RESIDENT (4) the same kernel as a plain launch:
+ *                the grid is resident by the occupancy check alone, not by
+ *                the runtime's guarantee, and the call saves the cooperative
+ *                launch's hand-over (about 20 us).  For a device the call
+ *                does not share with long-running work: should another
+ *                queue's kernels hold CUs for longer than the bounded waits
+ *                (about 2^18 polls), the launch ends with flags bit 31 set
+ *                for its requests rather than waiting longer.  The same
+ *                trees, bit for bit, as DT_EXPAND_PERSISTENT.
  * A request's expansion state lives in one workgroup's LDS: configurations with
  * 4 H + 8 L M + 512 n bytes (plus ~0.8 KiB) above 64 KiB are DT_ERR_UNSUPPORTED. */
-typedef enum { DT_EXPAND_AUTO = 0, DT_EXPAND_STEPPED = 1, DT_EXPAND_FUSED = 2, DT_EXPAND_PERSISTENT = 3 } dt_expand;
+typedef enum {
+    DT_EXPAND_AUTO = 0,
+    DT_EXPAND_STEPPED = 1,
+    DT_EXPAND_FUSED = 2,
+    DT_EXPAND_PERSISTENT = 3,
+    DT_EXPAND_RESIDENT = 4
+} dt_expand;
 typedef struct {
     int32_t B, L, V, E, H, M, n;
     float temperature;
@@ -114,11 +129,12 @@ void dt_destroy(dt_handle *h);
  * 256-byte aligned).  dt_topm and dt_gru_step need no more than this. */
 size_t dt_workspace_bytes(const dt_handle *h);
 
-/* The expansion dt_build runs for this handle: DT_EXPAND_PERSISTENT,
- * DT_EXPAND_FUSED or DT_EXPAND_STEPPED -- the one its last dt_build call ran,
- * or before any call the one the configuration selects (DT_EXPAND_AUTO with a
- * fused plan: DT_EXPAND_PERSISTENT, which a call may turn into
- * DT_EXPAND_FUSED, see dt_config.expand); -1 for a NULL handle.  Host only. */
+/* The expansion dt_build runs for this handle: DT_EXPAND_RESIDENT,
+ * DT_EXPAND_PERSISTENT, DT_EXPAND_FUSED or DT_EXPAND_STEPPED -- the one its
+ * last dt_build call ran, or before any call the one the configuration
+ * selects (DT_EXPAND_AUTO with a fused plan: DT_EXPAND_RESIDENT, which a call
+ * may turn into DT_EXPAND_FUSED, see dt_config.expand); -1 for a NULL handle.
+ * Host only. */
 int32_t dt_expand_mode(const dt_handle *h);
 
 const char *dt_status_string(dt_status s);

@@ -205,14 +205,14 @@ def test_timing_argument_checks():
 def test_expand_mode_is_validated():
     lib = dtree.load_library()
     out = C.c_void_p()
-    for e in (4, -1):
+    for e in (5, -1):
         bad = dt_config(2, 4, 100, 32, 32, 8, 4, 0.0, dtree.DT_BF16, 1e-5, 0, e)
         assert lib.dt_create(C.byref(bad), C.byref(out)) == -1 and not out.value
         assert "expand" in dtree.dt_last_error(None)
     # the fused expansion (per-step launches or persistent) is bf16 with
     # H <= 1024; one launch per step holds at most 64 requests, the persistent
     # launch takes more in slices of 64
-    for e in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT):
+    for e in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_RESIDENT):
         for kw in (dict(dtype=dtree.DT_F32), dict(H=2048)):
             with pytest.raises(ValueError, match="UNSUPPORTED"):
                 make(expand=e, **kw)
@@ -221,7 +221,8 @@ def test_expand_mode_is_validated():
     # the mode dt_build runs, before any call: auto selects the persistent
     # launch where the fused expansion applies (a call may fall back to the
     # per-step launches)
-    for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_PERSISTENT),
+    for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_RESIDENT),
+                    (dtree.DT_EXPAND_RESIDENT, dtree.DT_EXPAND_RESIDENT),
                     (dtree.DT_EXPAND_STEPPED, dtree.DT_EXPAND_STEPPED),
                     (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_FUSED),
                     (dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_PERSISTENT)):
@@ -235,7 +236,8 @@ def test_expand_mode_is_validated():
     # more than 64 requests: stepped unless the persistent launch (in slices
     # of 64) is asked for
     for e, want in ((dtree.DT_EXPAND_AUTO, dtree.DT_EXPAND_STEPPED),
-                    (dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_PERSISTENT)):
+                    (dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_PERSISTENT),
+                    (dtree.DT_EXPAND_RESIDENT, dtree.DT_EXPAND_RESIDENT)):
         h = make(expand=e, B=65)
         assert dtree.dt_expand_mode(h) == want
         dtree.dt_destroy(h)

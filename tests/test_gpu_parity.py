@@ -49,13 +49,13 @@ def builder(cfg, eps=1e-5):
                          expand=cfg.get("expand", dtree.DT_EXPAND_AUTO))
 
 
-# dt_build's ways of running the expansion: "auto" takes the persistent launch
-# wherever it applies (bf16, H <= 1024, a device that holds the grid; more
-# than 64 requests in launches of 64), "fused" forces one launch per step of the same pipeline, "stepped" two
+# dt_build's ways of running the expansion: "auto" takes the persistent kernel
+# as a plain launch wherever it applies (bf16, B <= 64, H <= 1024, a device
+# that holds the grid), "fused" forces one launch per step of the same pipeline, "stepped" two
 # launches per step; the whole-build tests run each where it applies
 EXPAND = {"auto": dtree.DT_EXPAND_AUTO, "fused": dtree.DT_EXPAND_FUSED, "stepped": dtree.DT_EXPAND_STEPPED}
 MODE_NAME = {dtree.DT_EXPAND_STEPPED: "stepped", dtree.DT_EXPAND_FUSED: "fused",
-             dtree.DT_EXPAND_PERSISTENT: "persistent"}
+             dtree.DT_EXPAND_PERSISTENT: "persistent", dtree.DT_EXPAND_RESIDENT: "resident"}
 
 
 # The "strong" variant (h0 ~ N(0, 1), C scaled by 10) makes corrected logits
@@ -702,7 +702,7 @@ def test_persistent_equals_per_step_launches(name, over):
     cfg, inp = inputs(name, over=over)
     t = S.to_torch(inp, DEV)
     got = {}
-    for mode in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT):
+    for mode in (dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_RESIDENT):
         bld = builder(dict(cfg, expand=mode))
         outs = []
         for _ in range(2):
@@ -714,20 +714,22 @@ def test_persistent_equals_per_step_launches(name, over):
             assert torch.equal(_i32(outs[0][k]), _i32(outs[1][k])), f"{MODE_NAME[mode]}: second call differs in {k}"
         got[mode] = outs[0]
         bld.close()
-    for k in got[dtree.DT_EXPAND_FUSED]:
-        assert torch.equal(_i32(got[dtree.DT_EXPAND_FUSED][k]), _i32(got[dtree.DT_EXPAND_PERSISTENT][k])), \
-            f"persistent differs from per-step launches in {k}"
-    assert int(got[dtree.DT_EXPAND_PERSISTENT]["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
+    for mode in (dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_RESIDENT):
+        for k in got[dtree.DT_EXPAND_FUSED]:
+            assert torch.equal(_i32(got[dtree.DT_EXPAND_FUSED][k]), _i32(got[mode][k])), \
+                f"{MODE_NAME[mode]} differs from per-step launches in {k}"
+        assert int(got[mode]["flags"].view(torch.int32).min()) >= 0, "a wait ran out"
 
 
-@pytest.mark.parametrize("B", [65, 100])
-def test_persistent_in_slices_beyond_one_grid(B):
+@pytest.mark.parametrize("B,mode", [(65, dtree.DT_EXPAND_PERSISTENT), (100, dtree.DT_EXPAND_PERSISTENT),
+                                    (100, dtree.DT_EXPAND_RESIDENT)])
+def test_persistent_in_slices_beyond_one_grid(B, mode):
     # More than 64 requests: two persistent launches (64 requests, then the
     # rest: 1 or 36), each on its own flag words.  Every request against the
     # oracle, twice in a row on one handle; each slice's outputs equal, bit
     # for bit, those of a build of its requests alone (one launch).
     cfg, inp = inputs("qwen3_4b_batched", over=(("B", B),))
-    cfg = dict(cfg, expand=dtree.DT_EXPAND_PERSISTENT)
+    cfg = dict(cfg, expand=mode)
     got, _, _ = build_and_compare(cfg, inp)
     t = S.to_torch(inp, DEV)
     bld = builder(cfg)
@@ -739,14 +741,14 @@ def test_persistent_in_slices_beyond_one_grid(B):
         sub = dict(inp, base=inp["base"][b0:b1], h0=inp["h0"][b0:b1] if inp["h0"] is not None else None)
         bld = builder(dict(cfg, B=b1 - b0))
         one = run_build(bld, S.to_torch(sub, DEV))
-        assert bld.expand_mode == dtree.DT_EXPAND_PERSISTENT
+        assert bld.expand_mode == mode
         bld.close()
         for k in one:
             assert np.array_equal(one[k], got[k][b0:b1]), f"requests {b0}..{b1 - 1} differ in {k}"
     assert int(got["flags"].view(np.int32).min()) >= 0, "a wait ran out"
 
 
-@pytest.mark.parametrize("mode", [dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT])
+@pytest.mark.parametrize("mode", [dtree.DT_EXPAND_FUSED, dtree.DT_EXPAND_PERSISTENT, dtree.DT_EXPAND_RESIDENT])
 def test_expansion_ignores_workspace_contents(mode):
     # Nothing a call reads from its workspace survives from before it: with
     # every byte set to 0xFF first (flag words that read as every step done,
